@@ -1,0 +1,342 @@
+"""Pins for the oracle's codec (GAAC page, §3.1 codec, §3.3 slots, App. B FP8, App. D storage).
+
+Nothing here compares the oracle with itself: round trips over every bit pattern, hand-derived
+golden bytes, closed-form sizes, brute-force mode choice and calibration computed a different
+way, and the page's storage arithmetic.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _tiles_from_patterns(pat, T, D):
+    n = T * D
+    pad = (-len(pat)) % n
+    pat = np.concatenate([pat, pat[:pad]])
+    return pat.reshape(-1, T, D)
+
+
+def _roundtrip(orc, p, tiles, b3, b4, is_v=0):
+    data, is_raw, esc, modes = orc.encode_tiles(p, tiles, b3, b4, is_v)
+    back, status = orc.decode_tiles(p, data, is_raw, is_v, b3, b4)
+    assert (status == 0).all()
+    assert np.array_equal(back, tiles)
+    return data, is_raw, esc, modes
+
+
+# ---- exhaustive round trips (every sign/exponent/mantissa bit survives, §3.1) -------------
+
+@pytest.mark.parametrize("G", [8, 16])
+def test_bf16_every_pattern_roundtrips(orc, G):
+    p = orc.Params(orc.BF16, 64, 128, G)
+    rng = np.random.default_rng(11)
+    allp = np.arange(65536, dtype=np.uint16)
+    arrangements = [allp, rng.permutation(allp), allp.reshape(-1, 2)[:, ::-1].ravel()]
+    for pat in arrangements:
+        tiles = _tiles_from_patterns(pat, p.T, p.D)
+        n = tiles.shape[0]
+        for b3, b4 in [(rng.integers(0, 249, (n, p.D)), rng.integers(0, 241, (n, p.D))),
+                       (np.zeros((n, p.D)), np.zeros((n, p.D))),
+                       (np.full((n, p.D), 248), np.full((n, p.D), 240))]:
+            _roundtrip(orc, p, tiles, b3.astype(np.uint8), b4.astype(np.uint8), is_v=int(rng.integers(2)))
+
+
+def test_bf16_every_pattern_in_narrow_groups(orc):
+    """Each pattern repeated G times down one channel: every group is narrow at a base equal
+    to its exponent (b3 = e); ±0, subnormals, Inf and NaN payloads included."""
+    p = orc.Params(orc.BF16, 16, 128, 16)
+    allp = np.arange(65536, dtype=np.uint16)
+    tiles = np.repeat(allp.reshape(-1, 1, 128), 16, axis=1)       # [512][16][128]
+    e = (tiles[:, 0, :] >> 7) & 0xFF
+    b3 = np.minimum(e, 248).astype(np.uint8)
+    b4 = np.minimum(e, 240).astype(np.uint8)
+    data, is_raw, esc, modes = _roundtrip(orc, p, tiles, b3, b4)
+    assert (is_raw == 0).all()
+    # exponents above 248 do not fit a base of 248 plus 3 bits only when e > 255: never
+    assert modes[:, 0].sum() == tiles.shape[0] * 128
+    assert (esc == 0).all()
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_fp8_every_pattern_roundtrips(orc, fmt):
+    F = 5 if fmt == 1 else 4
+    p = orc.Params(fmt, 64, 128, 16)
+    rng = np.random.default_rng(5)
+    allp = np.arange(256, dtype=np.uint16)
+    for pat in (np.tile(allp, 32), rng.permutation(np.tile(allp, 32)), np.repeat(allp, 32)):
+        tiles = pat.reshape(1, 64, 128)
+        for _ in range(4):
+            b3 = rng.integers(0, (1 << F) - 8 + 1, (1, 128)).astype(np.uint8)
+            b4 = rng.integers(0, max((1 << F) - 16, 0) + 1, (1, 128)).astype(np.uint8)
+            _roundtrip(orc, p, tiles, b3, b4, is_v=int(rng.integers(2)))
+
+
+# ---- golden bytes derived by hand from the format -----------------------------------------
+
+@pytest.mark.parametrize("name", ["tile_t16_d2_narrow_wide", "tile_t16_d2_raw_group"])
+def test_golden_tile_bytes(orc, name):
+    d = json.load(open(os.path.join(GOLDEN, name + ".json")))
+    p = orc.Params(**d["params"])
+    T, D = p.T, p.D
+    x = np.zeros((T, D), np.uint16)
+    for t in range(T):
+        if name.endswith("narrow_wide"):
+            x[t, 0] = ((t % 2) << 15) | ((120 + t % 8) << 7) | t
+            x[t, 1] = ((t % 2) << 15) | ((120 + t) << 7) | (16 + t)
+        else:
+            x[t, 0] = ((8 * t + 7) << 7) | t
+            x[t, 1] = 127 << 7
+    b3 = np.array(d["b3"], np.uint8)
+    b4 = np.array(d["b4"], np.uint8)
+    data, is_raw, esc, modes = orc.encode_tiles(p, x[None], b3, b4, 0)
+    lay = orc.layout(p)
+    assert lay["stride"] == d["stride"]
+    want = bytes.fromhex(d["expected_hex"].replace(" ", ""))
+    assert is_raw[0] == 0
+    assert bytes(data[0, :lay["stride"]]) == want
+    back, st = orc.decode_tiles(p, data, is_raw, 0, b3, b4)
+    assert st[0] == 0 and np.array_equal(back[0], x)
+
+
+def test_raw_fallback_layout(orc):
+    """esc_cap = 0 and one wide group: the tile stays in native form, K token-major and V
+    channel-major (§3.3: oversized blocks remain BF16)."""
+    p = orc.Params(orc.BF16, 16, 32, 16, esc_cap=0)
+    rng = np.random.default_rng(1)
+    x = (rng.integers(0, 1 << 16, (16, 32))).astype(np.uint16)
+    x[:, 0] = (np.arange(16) * 9 + 10).astype(np.uint16) << 7      # exponent spread 135 -> raw group
+    b3 = np.full(32, 10, np.uint8)
+    b4 = np.full(32, 10, np.uint8)
+    for is_v in (0, 1):
+        data, is_raw, esc, modes = orc.encode_tiles(p, x[None], b3, b4, is_v)
+        assert is_raw[0] == 1
+        words = data[0, :16 * 32 * 2].view(np.uint16)
+        want = x.T.ravel() if is_v else x.ravel()
+        assert np.array_equal(words, want)
+
+
+def test_narrow_only_tile_never_falls_back_even_at_zero_cap(orc):
+    p = orc.Params(orc.BF16, 64, 128, 16, esc_cap=0)
+    x = np.full((64, 128), 127 << 7, np.uint16) | np.arange(64 * 128, dtype=np.uint16).reshape(64, 128) % 128
+    b3 = np.full(128, 125, np.uint8)
+    data, is_raw, esc, modes = _roundtrip(orc, p, x[None], b3, b3)
+    assert is_raw[0] == 0 and esc[0] == 0
+
+
+def test_all_distinct_exponents_tile_is_raw(orc):
+    """A tile whose groups all need raw mode overflows the default escape capacity."""
+    p = orc.Params(orc.BF16, 64, 128, 16)
+    t = np.arange(64)[:, None]
+    x = np.broadcast_to(((t * 4) % 256) << 7, (64, 128)).astype(np.uint16)
+    data, is_raw, esc, modes = _roundtrip(orc, p, x[None], np.zeros(128, np.uint8), np.zeros(128, np.uint8))
+    assert is_raw[0] == 1 and modes[0, 2] == 512
+
+
+# ---- closed-form sizes and the page's storage figure --------------------------------------
+
+@pytest.mark.parametrize("fmt,m", [(0, 7), (1, 2), (2, 3)])
+@pytest.mark.parametrize("T,D,G", [(64, 128, 16), (16, 128, 16), (64, 64, 16), (16, 128, 8)])
+def test_section_sizes_closed_form(orc, fmt, m, T, D, G):
+    p = orc.Params(fmt, T, D, G)
+    lay = orc.layout(p)
+    NG = T * D // G
+    assert lay["n_groups"] == NG
+    assert lay["tag_bytes"] == 2 * ((NG + 31) // 32) * 4
+    assert lay["code_bytes"] == 3 * T * D // 8
+    assert lay["sm_bytes"] == (1 + m) * T * D // 8
+    a16 = lambda v: (v + 15) // 16 * 16
+    assert lay["stride"] == a16(lay["tag_bytes"]) + a16(lay["code_bytes"]) + a16(lay["sm_bytes"]) + T * D // 16
+
+
+def test_page_storage_figure_3016_bytes(orc):
+    """App. D: a 16-token tile of a 128-dim (half-)head averages 3,016 B including tags, codes,
+    escape slot and block-table entry.  With G = 8 this layout gives 64 + 768 + 2048 + 128 = 3008
+    bytes of slot plus an 8-byte table entry."""
+    lay = orc.layout(orc.Params(orc.BF16, 16, 128, 8))
+    assert lay["stride"] == 3008
+    assert lay["stride"] + 8 == 3016
+    # the page's 3,016 B is itself rounded (11.783 bits x 2048 elements = 3016.45 B)
+    assert abs(3016 * 8 / (16 * 128) - 11.783) < 2.5e-3
+
+
+def test_escape_bytes_closed_form_and_ratio_bound(orc):
+    """Used escape bytes = sum over groups of (w-3)*G/8; an all-narrow tile reaches the
+    ratio bound 16 / (11 + 2/G)."""
+    cfg = synth.config(2)
+    g = synth.LayerGen(cfg)
+    k, v = g.tokens(512)
+    for G in (8, 16):
+        p = orc.Params(orc.BF16, 64, 128, G)
+        b3, b4 = orc.calibrate_layer(p, k[:256], v[:256])
+        tiles = k.reshape(8, 64, 8, 128).transpose(0, 2, 1, 3).reshape(-1, 64, 128)
+        bb3 = np.tile(b3[0], (8, 1))
+        bb4 = np.tile(b4[0], (8, 1))
+        data, is_raw, esc, modes = _roundtrip(orc, p, tiles, bb3, bb4)
+        assert (is_raw == 0).all()
+        want = (modes[:, 1] * (4 - 3) * G + modes[:, 2] * (8 - 3) * G + 7) // 8
+        assert np.array_equal(esc, want)
+    p = orc.Params(orc.BF16, 64, 128, 16)
+    x = (np.full((64, 128), 100, np.uint16) << 7) | (np.arange(64 * 128) % 128).astype(np.uint16).reshape(64, 128)
+    seq = orc.Sequence(p, 1, (np.full((2, 1, 128), 100, np.uint8), np.full((2, 1, 128), 100, np.uint8)))
+    seq.append(x[:, None, :], x[:, None, :])
+    st = orc.stats(p, [seq])
+    assert abs(st["codec_ratio"] - 16 / (11 + 2 / 16)) < 1e-12
+
+
+# ---- mode choice by brute force (§3.1: narrowest width whose offsets fit) -----------------
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_mode_is_narrowest_fitting(orc, fmt):
+    F, MB = {0: (8, 7), 1: (5, 2), 2: (4, 3)}[fmt]
+    p = orc.Params(fmt, 16, 32, 16, esc_cap=512)   # 32 groups per tile, room for any escapes
+    lay = orc.layout(p)
+    rng = np.random.default_rng(fmt + 3)
+    emax = (1 << F) - 1
+    cases = []
+    for _ in range(600):
+        mn = int(rng.integers(0, emax + 1))
+        mx = int(rng.integers(mn, min(emax, mn + int(rng.choice([3, 7, 8, 15, 16, 40]))) + 1))
+        b3 = int(rng.integers(max(0, mn - 9), min(emax - 7, mn + 2) + 1)) if mn <= emax - 7 else emax - 7
+        b4 = int(rng.integers(max(0, mn - 17), max(0, min(emax - 15, mn + 2)) + 1)) if F > 4 else 0
+        cases.append((mn, mx, b3, b4))
+    for i in range(0, len(cases), 32):
+        chunk = cases[i:i + 32]
+        x = np.zeros((16, 32), np.uint16)
+        b3a = np.zeros(32, np.uint8)
+        b4a = np.zeros(32, np.uint8)
+        for c, (mn, mx, b3, b4) in enumerate(chunk):
+            es = np.linspace(mn, mx, 16).round().astype(np.int64)
+            es[0], es[-1] = mn, mx
+            x[:, c] = (es << MB).astype(np.uint16)
+            b3a[c], b4a[c] = b3, b4
+        data, is_raw, esc, modes = orc.encode_tiles(p, x[None], b3a, b4a, 0)
+        assert is_raw[0] == 0
+        raw = data[0]
+        for c, (mn, mx, b3, b4) in enumerate(chunk):
+            q = c                               # token group 0
+            E = (raw[lay["tag_off"] + q // 8] >> (q % 8)) & 1
+            R = (raw[lay["tag_off"] + lay["plane_bytes"] + q // 8] >> (q % 8)) & 1
+            tag = int(E) + int(R)
+            # brute force: try windows in width order, check every element offset
+            es = x[:, c].astype(np.int64) >> MB
+            want = 2
+            for mode, (w, base) in enumerate([(3, b3), (4, b4)]):
+                if mode == 1 and F <= 4:
+                    continue
+                if all(0 <= e - base < (1 << w) for e in es):
+                    want = mode
+                    break
+            assert tag == want, (fmt, mn, mx, b3, b4)
+
+
+# ---- calibration (§3.1 windows of 8 and 16; lower-median tie-break is this library's reading)
+
+def _calib_bruteforce(x_col_exps, F, w):
+    """Count elements inside [b, b+2^w-1] directly from the data for every start b."""
+    best, starts = -1, []
+    for b in range(0, (1 << F) - (1 << w) + 1):
+        cnt = int(np.sum((x_col_exps >= b) & (x_col_exps <= b + (1 << w) - 1)))
+        if cnt > best:
+            best, starts = cnt, [b]
+        elif cnt == best:
+            starts.append(b)
+    return starts[(len(starts) - 1) // 2]
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_calibration_bruteforce(orc, fmt):
+    F, MB = {0: (8, 7), 1: (5, 2), 2: (4, 3)}[fmt]
+    p = orc.Params(fmt, 64, 32, 16)
+    rng = np.random.default_rng(21 + fmt)
+    center = rng.integers(0, 1 << F, 32)
+    spread = rng.integers(0, 6, 32)
+    es = np.clip(center + np.round(rng.standard_normal((97, 32)) * spread), 0, (1 << F) - 1).astype(np.int64)
+    x = ((es << MB) | rng.integers(0, 1 << MB, es.shape)).astype(np.uint16)
+    b3, b4 = orc.calibrate(p, x)
+    for c in range(32):
+        assert b3[c] == _calib_bruteforce(es[:, c], F, 3)
+        if F > 4:
+            assert b4[c] == _calib_bruteforce(es[:, c], F, 4)
+
+
+def test_calibration_constructed_histograms(orc):
+    p = orc.Params(orc.BF16, 64, 4, 16)
+    MB = 7
+    cols = []
+    cols.append(np.full(40, 130))                        # spike at 130: ties b in [123,130] / [115,130]
+    cols.append(np.arange(0, 256, 1)[:40] * 0 + np.repeat([100, 101, 102, 103, 104, 105, 106, 107], 5))  # flat 100..107
+    cols.append(np.concatenate([np.full(20, 50), np.full(20, 200)]))  # bimodal, equal halves
+    cols.append(np.concatenate([np.full(39, 255), [0]]))  # top edge
+    es = np.stack(cols, axis=1).astype(np.int64)
+    x = (es << MB).astype(np.uint16)
+    b3, b4 = orc.calibrate(p, x)
+    # spike: windows [b, b+7] containing 130: b = 123..130 (8 ties) -> lower median index 3 -> 126
+    assert b3[0] == 126
+    # [b, b+15] containing 130: b = 115..130 (16 ties) -> index 7 -> 122
+    assert b4[0] == 122
+    # flat 100..107: only b = 100 covers all 40 for w=3; for w=4: b = 92..100 (9 ties) -> index 4 -> 96
+    assert b3[1] == 100 and b4[1] == 96
+    # bimodal: any window covers one mode; ties: [43..50] and [193..200] (16) -> index 7 -> 50
+    assert b3[2] == 50
+    # w=4: [35..50] and [185..200] (32 ties) -> index 15 -> 50
+    assert b4[2] == 50
+    # top edge: w=3 windows must end at 255: b = 248 only
+    assert b3[3] == 248 and b4[3] == 240
+
+
+def test_calibration_empty_histogram(orc):
+    p = orc.Params(orc.BF16, 64, 4, 16)
+    b3, b4 = orc.calibrate(p, np.zeros((0, 4), np.uint16))
+    assert (b3 == 124).all() and (b4 == 120).all()
+
+
+# ---- corrupt input is rejected --------------------------------------------------------------
+
+def test_decoder_rejects_reserved_tag_and_escape_overrun(orc):
+    p = orc.Params(orc.BF16, 16, 32, 16, esc_cap=16)
+    lay = orc.layout(p)
+    x = np.full((16, 32), 120 << 7, np.uint16)
+    b = np.full(32, 120, np.uint8)
+    data, is_raw, esc, modes = orc.encode_tiles(p, x[None], b, b, 0)
+    bad = data.copy()
+    bad[0, lay["tag_off"] + lay["plane_bytes"]] |= 1       # R without E
+    _, st = orc.decode_tiles(p, bad, is_raw, 0, b, b)
+    assert st[0] == -5
+    bad = data.copy()
+    bad[0, lay["tag_off"]: lay["tag_off"] + 4] = 0xFF        # 32 raw groups need 160 B > 16
+    bad[0, lay["tag_off"] + lay["plane_bytes"]: lay["tag_off"] + lay["plane_bytes"] + 4] = 0xFF
+    _, st = orc.decode_tiles(p, bad, is_raw, 0, b, b)
+    assert st[0] == -5
+    pe = orc.Params(orc.E4M3, 16, 32, 16, esc_cap=16)
+    le = orc.layout(pe)
+    xe = np.full((16, 32), 5 << 3, np.uint16)
+    be = np.full(32, 3, np.uint8)
+    d2, r2, _, _ = orc.encode_tiles(pe, xe[None], be, be, 0)
+    d2[0, le["tag_off"]] |= 1                                # wide tag in E4M3
+    _, st = orc.decode_tiles(pe, d2, r2, 0, be, be)
+    assert st[0] == -5
+
+
+# ---- the codec on the synthetic workloads --------------------------------------------------
+
+def test_cfg0_cache_roundtrip_and_ratio_band(orc):
+    cfg = synth.config(0)
+    g, seqs = synth.sequence_tokens(cfg)
+    k, v = seqs[0]
+    p = orc.Params(orc.BF16, cfg.T, cfg.D, cfg.G)
+    bases = orc.calibrate_layer(p, k[:cfg.n_cal], v[:cfg.n_cal])
+    s = orc.Sequence(p, cfg.Hkv, bases)
+    for i in range(0, k.shape[0], 100):       # ragged appends cross block boundaries
+        s.append(k[i:i + 100], v[i:i + 100])
+    kd, vd = s.decoded()
+    assert np.array_equal(kd, k) and np.array_equal(vd, v)
+    st = orc.stats(p, [s])
+    # context, not parity: the page reports 1.405-1.407x on model KV (§4.2)
+    assert 1.38 < st["codec_ratio"] < 1.44
+    assert st["mode_share"][2] < 0.02
