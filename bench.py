@@ -1,0 +1,274 @@
+"""Decode-step benchmark of the lossless compressed-KV attention path on one MI355X.
+
+Workload (default): the 64K-token Qwen3-8B-like layer -- 1 sequence, 8 KV heads, 32 query heads,
+head_dim 128, 65,536 context tokens, 64-token blocks, 16-token exponent groups, synthetic BF16
+K/V with per-head log-normal channel scales and 4 outlier key channels per head.
+
+One timed step = one decode step of one layer: append the new token (encoding the block when it
+fills), run the split-K attention kernel over every cached token, merge the splits.  Steps
+rotate over --layers independent layer caches so each step reads its layer cold from HBM (the
+compressed layer, ~190 MB, would otherwise sit in the 256 MB last-level cache).  The same steps
+run on an uncompressed BF16 cache with the same table, layout and kernel structure (the speedup
+baseline).  The attention kernel alone is timed with HIP events on the stream it runs on.
+
+Prints one JSON line (rank 0, N = 1).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode-attention µs/step + effective HBM GB/s at 64K ctx; lossless ratio"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--splits", type=int, default=128)
+    ap.add_argument("--layers", type=int, default=8, help="layer caches rotated through (cold-cache protocol)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--sweep", type=str, default="", help="comma-separated split counts to time (extra)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import decode_attention_calibrate_amd as K
+    import synth
+
+    torch.cuda.set_device(0)
+    cfg = synth.config(2)
+    T, D, Hkv, Hq = cfg.T, cfg.D, cfg.Hkv, cfg.Hq
+    L0 = cfg.context[0]
+    S = args.splits
+    n_layers = args.layers
+    log(f"[bench] generating {L0} tokens x {Hkv} heads x {D}")
+    g, toks = synth.sequence_tokens(cfg)
+    k0, v0 = toks[0]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    kd, vd = dev(k0[None]), dev(v0[None])
+    steps_total = args.warmup + args.steps
+    per_layer = (steps_total + n_layers - 1) // n_layers + 1
+    kn, vn = g.tokens(per_layer * n_layers)
+    k_new = dev(kn.reshape(n_layers, per_layer, 1, 1, Hkv, D))
+    v_new = dev(vn.reshape(n_layers, per_layer, 1, 1, Hkv, D))
+    q = dev(synth.queries(cfg))
+    max_blocks = (L0 + per_layer) // T + 2
+    n_tiles = max_blocks * 2 * Hkv
+
+    def make(compressed):
+        c = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=1,
+                      max_blocks_per_seq=max_blocks, num_comp_slots=n_tiles if compressed else 0,
+                      num_raw_slots=256 if compressed else n_tiles, compressed=compressed, perm_seed=7)
+        c.calibrate(dev(k0[:cfg.n_cal]), dev(v0[:cfg.n_cal]))
+        c.append([0], kd, vd)
+        return c
+
+    log(f"[bench] building {n_layers} compressed + {n_layers} uncompressed layer caches")
+    comp = [make(True) for _ in range(n_layers)]
+    raw = [make(False) for _ in range(n_layers)]
+    torch.cuda.synchronize()
+    flags, st = comp[0].status()
+    if flags:
+        raise RuntimeError(f"cache status flags {flags}")
+
+    # ---- byte accounting (algorithmic bytes one attention launch must read) ----
+    TD = T * D
+    n_grp = TD // 16
+    payload_per_comp_tile = (2 * n_grp + 3 * TD + 8 * TD) // 8          # TAG + CODE + SM, without escapes
+    comp_kv_bytes = st["comp_tiles"] * payload_per_comp_tile + st["esc_bytes"] + st["raw_tiles"] * TD * 2
+    raw_kv_bytes = (st["comp_tiles"] + st["raw_tiles"]) * TD * 2
+    codec_ratio = raw_kv_bytes / comp_kv_bytes
+    resident = st["comp_tiles"] * comp[0].slot_stride + st["raw_tiles"] * TD * 2 + 4 * (st["comp_tiles"] + st["raw_tiles"])
+    resident_ratio = raw_kv_bytes / resident
+    q_bytes = Hq * D * 2
+    table_bytes = 4 * (st["comp_tiles"] + st["raw_tiles"])
+    log(f"[bench] codec ratio {codec_ratio:.4f}, resident ratio {resident_ratio:.4f}, tiles {st}")
+
+    wsc = comp[0].workspace(1, S)
+    out = torch.empty((1, Hq, D), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(caches, n_steps, record, splits=S, ws=wsc, start=0):
+        """n_steps decode steps starting at global step `start` (layer = step % n_layers)."""
+        ev = []
+        for i in range(n_steps):
+            step = start + i
+            li = step % n_layers
+            c = caches[li]
+            pos = step // n_layers
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+            if record:
+                e[0].record(stream)
+            c.append([0], k_new[li, pos], v_new[li, pos])
+            if record:
+                e[1].record(stream)
+            c.attention_partials([0], q, cfg.scale, splits, ws)
+            if record:
+                e[2].record(stream)
+            c.attention_combine(1, splits, ws, out)
+            if record:
+                e[3].record(stream)
+                ev.append(e)
+        return ev
+
+    def timed(caches, start):
+        run(caches, args.warmup, False, start=start)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        ev = run(caches, args.steps, True, start=start + args.warmup)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t0.elapsed_time(t1)
+        step_us = np.array([a.elapsed_time(d) * 1e3 for a, b, c, d in ev])
+        attn_us = np.array([b.elapsed_time(c) * 1e3 for a, b, c, d in ev])
+        app_us = np.array([a.elapsed_time(b) * 1e3 for a, b, c, d in ev])
+        comb_us = np.array([c.elapsed_time(d) * 1e3 for a, b, c, d in ev])
+        return total_ms, step_us, attn_us, app_us, comb_us
+
+    log(f"[bench] timing {args.steps} compressed steps (S={S})")
+    c_total, c_step, c_attn, c_app, c_comb = timed(comp, 0)
+    log(f"[bench] timing {args.steps} uncompressed steps")
+    r_total, r_step, r_attn, r_app, r_comb = timed(raw, 0)
+
+    sweep = {}
+    for s_ in [int(x) for x in args.sweep.split(",") if x]:
+        ws_ = comp[0].workspace(1, s_)
+        for name, caches in (("comp", comp), ("raw", raw)):
+            times = []
+            for i in range(40):
+                a_ = torch.cuda.Event(enable_timing=True)
+                b_ = torch.cuda.Event(enable_timing=True)
+                a_.record(stream)
+                caches[i % n_layers].attention_partials([0], q, cfg.scale, s_, ws_)
+                b_.record(stream)
+                times.append((a_, b_))
+            torch.cuda.synchronize()
+            sweep.setdefault(str(s_), {})[name] = float(np.median([a_.elapsed_time(b_) * 1e3 for a_, b_ in times[8:]]))
+        log(f"[bench] sweep S={s_}: {sweep[str(s_)]}")
+
+    # block-completing append (encode of 2*Hkv tiles), measured on its own
+    enc_us = None
+    try:
+        c = comp[0]
+        n_now = c.seq_length(0)
+        fill = (-n_now) % T
+        if fill == 0:
+            fill = T
+        kf, vf = g.tokens(fill)
+        kfd, vfd = dev(kf[None]), dev(vf[None])
+        if fill > 1:
+            c.append([0], kfd[:, :fill - 1].contiguous(), vfd[:, :fill - 1].contiguous())
+        a_ = torch.cuda.Event(enable_timing=True)
+        b_ = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a_.record(stream)
+        c.append([0], kfd[:, fill - 1:].contiguous(), vfd[:, fill - 1:].contiguous())
+        b_.record(stream)
+        torch.cuda.synchronize()
+        enc_us = a_.elapsed_time(b_) * 1e3
+    except Exception as ex:  # measurement only
+        log(f"[bench] encode timing skipped: {ex}")
+
+    attn_c = float(np.mean(c_attn))
+    attn_r = float(np.mean(r_attn))
+    bytes_c = comp_kv_bytes + q_bytes + table_bytes
+    bytes_r = raw_kv_bytes + q_bytes + table_bytes
+    achieved = bytes_c / (attn_c * 1e-6) / 1e9
+    value_us = c_total * 1e3 / args.steps
+    result = {
+        "metric": METRIC,
+        "value": round(value_us, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(c_total / args.steps, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded log-normal channel scales, 4 outlier key channels/head; no model weights)",
+        "config": {"workload": "qwen3-8b-like-64k-decode", "n_seqs": 1, "kv_heads": Hkv, "q_heads": Hq,
+                   "head_dim": D, "context": L0, "block_tokens": T, "group_tokens": 16, "n_splits": S,
+                   "layers_rotated": n_layers},
+        "step_us": {"median": float(np.median(c_step)), "p10": float(np.percentile(c_step, 10)),
+                    "p90": float(np.percentile(c_step, 90))},
+        "attention_us": {"compressed": attn_c, "uncompressed": attn_r,
+                         "compressed_median": float(np.median(c_attn)), "uncompressed_median": float(np.median(r_attn))},
+        "append_us": {"compressed_median": float(np.median(c_app)), "uncompressed_median": float(np.median(r_app)),
+                      "block_encode_append": enc_us},
+        "combine_us": float(np.median(c_comb)),
+        "uncompressed_step_us": round(r_total * 1e3 / args.steps, 3),
+        "speedup_step": round(r_total / c_total, 4),
+        "speedup_attention": round(attn_r / attn_c, 4),
+        "effective_GBps": round(achieved, 1),
+        "logical_GBps": round(bytes_r / (attn_c * 1e-6) / 1e9, 1),
+        "uncompressed_GBps": round(bytes_r / (attn_r * 1e-6) / 1e9, 1),
+        "codec_ratio": round(codec_ratio, 4),
+        "resident_ratio": round(resident_ratio, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "attn_comp_kernel<4>", "bytes_per_launch": bytes_c},
+        "sweep_attention_us": sweep or None,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(cfg, k0, v0)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, k0, v0):
+    """The oracle as it stands, on the host: rebuild every tile of the layer from its stored form
+    and evaluate exact fp64 attention for all 32 query heads -- one full decode step."""
+    import oracle
+    import synth
+    p = oracle.Params(oracle.BF16, cfg.T, cfg.D, cfg.G)
+    threads = oracle._threads(None)
+    log(f"[bench] cpu baseline: oracle encode (untimed), then decode + fp64 attention on {threads} threads")
+    bases = oracle.calibrate_layer(p, k0[:cfg.n_cal], v0[:cfg.n_cal])
+    s = oracle.Sequence(p, cfg.Hkv, bases)
+    s.append(k0, v0)
+    q = synth.queries(cfg)[0]
+    t0 = time.perf_counter()
+    kd, vd = s.decoded()
+    t1 = time.perf_counter()
+    oracle.attention(oracle.BF16, q, kd, vd, cfg.scale)
+    t2 = time.perf_counter()
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round((t2 - t0) * 1e6, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"one full decode step of the 64K layer: rebuild all {len(s.tiles) * 2 * cfg.Hkv} tiles "
+                      f"({(t1 - t0):.2f} s) + exact fp64 attention, 32 heads ({(t2 - t1):.2f} s)",
+            "cpu_model": cpu_model, "nproc": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+"""KVCache: one layer of lossless compressed (or uncompressed) paged KV cache on one GPU.
+
+A thin wrapper over the C ABI: it allocates the device buffers as torch tensors, passes
+pointers, sizes and the current HIP stream, and raises on error codes.  All computation runs
+in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _elem(t: torch.Tensor, what: str) -> torch.Tensor:
+    if not t.is_cuda or not t.is_contiguous() or t.element_size() != 2:
+        raise ValueError(f"{what} must be a contiguous 2-byte (BF16 bits) CUDA tensor")
+    return t
+
+
+class KVCache:
+    def __init__(self, *, num_kv_heads: int, num_q_heads: int, head_dim: int, block_tokens: int,
+                 max_seqs: int, max_blocks_per_seq: int, num_comp_slots: int, num_raw_slots: int,
+                 compressed: bool = True, group_tokens: int = 16, esc_cap_bytes: int = -1, dtype: int = L.BF16,
+                 device: str | torch.device = "cuda", perm_seed: int = 0):
+        self.lib = L.load()
+        self.device = torch.device(device)
+        self.params = L.Params(dtype, num_kv_heads, num_q_heads, head_dim, block_tokens, group_tokens, esc_cap_bytes,
+                               1 if compressed else 0, max_seqs, max_blocks_per_seq, num_comp_slots, num_raw_slots)
+        sizes = (ctypes.c_size_t * L.NUM_BUFFERS)()
+        stride = ctypes.c_size_t()
+        L.check(self.lib.kv_buffer_sizes(ctypes.byref(self.params), sizes, ctypes.byref(stride)))
+        self.slot_stride = stride.value
+        self.T, self.D, self.Hkv, self.Hq = block_tokens, head_dim, num_kv_heads, num_q_heads
+        self.compressed = bool(compressed)
+        self.buffers = {}
+        for name, sz in zip(L.BUFFER_NAMES, sizes):
+            self.buffers[name] = torch.empty(max(int(sz), 16), dtype=torch.uint8, device=self.device)
+        self._bufs = L.Buffers(*[_ptr(self.buffers[n]) if sizes[i] else None for i, n in enumerate(L.BUFFER_NAMES)])
+        h = ctypes.c_void_p()
+        L.check(self.lib.kv_cache_create(ctypes.byref(self.params), ctypes.byref(self._bufs), perm_seed,
+                                         self._stream(), ctypes.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            self.lib.kv_cache_destroy(h)
+            self.handle = None
+
+    def _stream(self):
+        return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+
+    # ---- the four calls of the method ----
+    def _shape(self, t: torch.Tensor, what: str, lead: int):
+        if t.dim() != lead + 2 or tuple(t.shape[lead:]) != (self.Hkv, self.D) or t.device != self.device:
+            raise ValueError(f"{what} must have shape [...{lead} dims...][{self.Hkv}][{self.D}] on {self.device}")
+
+    def calibrate(self, k: torch.Tensor, v: torch.Tensor):
+        """k, v: [n][Hkv][D] element bits."""
+        _elem(k, "k"), _elem(v, "v")
+        self._shape(k, "k", 1), self._shape(v, "v", 1)
+        if k.shape != v.shape:
+            raise ValueError("k and v differ in shape")
+        L.check(self.lib.kv_calibrate(self.handle, _ptr(k), _ptr(v), k.shape[0], self._stream()))
+
+    def append(self, seq_ids, k: torch.Tensor, v: torch.Tensor):
+        """k, v: [n_seqs][n_tokens][Hkv][D] element bits."""
+        _elem(k, "k"), _elem(v, "v")
+        self._shape(k, "k", 2), self._shape(v, "v", 2)
+        if k.shape[0] != len(seq_ids) or k.shape != v.shape:
+            raise ValueError("k, v must be [n_seqs][n_tokens][Hkv][D] with n_seqs = len(seq_ids)")
+        ids = (ctypes.c_int32 * len(seq_ids))(*seq_ids)
+        L.check(self.lib.kv_encode_append(self.handle, ids, len(seq_ids), _ptr(k), _ptr(v), k.shape[1],
+                                          self._stream()))
+
+    def decode_blocks(self, seq: int, first: int, n: int, out=None):
+        if out is None:
+            k = torch.empty((n * self.T, self.Hkv, self.D), dtype=torch.int16, device=self.device)
+            v = torch.empty_like(k)
+        else:
+            k, v = out
+            for t in (k, v):
+                _elem(t, "out")
+                if tuple(t.shape) != (n * self.T, self.Hkv, self.D):
+                    raise ValueError("decode_blocks outputs must be [n*T][Hkv][D]")
+        L.check(self.lib.kv_decode_blocks(self.handle, seq, first, n, _ptr(k), _ptr(v), self._stream()))
+        return k, v
+
+    def workspace(self, n_seqs: int, n_splits: int) -> torch.Tensor:
+        nb = self.lib.kv_attention_workspace_bytes(ctypes.byref(self.params), n_seqs, n_splits)
+        return torch.empty(max(nb, 16), dtype=torch.uint8, device=self.device)
+
+    def attention(self, seq_ids, q: torch.Tensor, scale: float, n_splits: int, ws=None, out=None) -> torch.Tensor:
+        """q: [n_seqs][Hq][D] BF16 bits -> out [n_seqs][Hq][D] BF16 bits."""
+        n = len(seq_ids)
+        self._check_q(q, n)
+        if ws is None:
+            ws = self.workspace(n, n_splits)
+        if out is None:
+            out = torch.empty((n, self.Hq, self.D), dtype=torch.int16, device=self.device)
+        self._check_out(out, n)
+        ids = (ctypes.c_int32 * n)(*seq_ids)
+        L.check(self.lib.kv_decode_attention(self.handle, ids, n, _ptr(q), float(scale), n_splits, _ptr(ws),
+                                             ws.numel(), _ptr(out), self._stream()))
+        return out
+
+    def _check_q(self, q: torch.Tensor, n: int):
+        _elem(q, "q")
+        if tuple(q.shape) != (n, self.Hq, self.D) or q.device != self.device:
+            raise ValueError(f"q must be [{n}][{self.Hq}][{self.D}] on {self.device}")
+
+    def _check_out(self, out: torch.Tensor, n: int):
+        _elem(out, "out")
+        if tuple(out.shape) != (n, self.Hq, self.D) or out.device != self.device:
+            raise ValueError(f"out must be [{n}][{self.Hq}][{self.D}] on {self.device}")
+
+    def attention_partials(self, seq_ids, q: torch.Tensor, scale: float, n_splits: int, ws: torch.Tensor):
+        self._check_q(q, len(seq_ids))
+        ids = (ctypes.c_int32 * len(seq_ids))(*seq_ids)
+        L.check(self.lib.kv_attention_partials(self.handle, ids, len(seq_ids), _ptr(q), float(scale), n_splits,
+                                               _ptr(ws), ws.numel(), self._stream()))
+
+    def attention_combine(self, n_seqs: int, n_splits: int, ws: torch.Tensor, out: torch.Tensor):
+        self._check_out(out, n_seqs)
+        L.check(self.lib.kv_attention_combine(self.handle, n_seqs, n_splits, _ptr(ws), ws.numel(), _ptr(out),
+                                              self._stream()))
+        return out
+
+    # ---- bookkeeping ----
+    def release(self, seq: int):
+        L.check(self.lib.kv_release_seq(self.handle, seq, self._stream()))
+
+    def seq_length(self, seq: int) -> int:
+        n = ctypes.c_int32()
+        L.check(self.lib.kv_seq_length(self.handle, seq, ctypes.byref(n)))
+        return n.value
+
+    def status(self):
+        flags = ctypes.c_uint32()
+        st = L.Stats()
+        L.check(self.lib.kv_get_status(self.handle, ctypes.byref(flags), ctypes.byref(st), self._stream()))
+        return flags.value, dict(comp_tiles=st.comp_tiles, raw_tiles=st.raw_tiles, groups=list(st.groups),
+                                 esc_bytes=st.esc_bytes, comp_free=st.comp_free, raw_free=st.raw_free)
+
+    # ---- raw views of the device state (tests) ----
+    def table(self) -> torch.Tensor:
+        return self.buffers["block_table"].view(torch.int32)
+
+    def bases(self) -> torch.Tensor:
+        return self.buffers["bases"][: 4 * self.Hkv * self.D].view(2, 2, self.Hkv, self.D)

@@ -1,0 +1,365 @@
+// api.cpp -- the C ABI declared in include/kvc.h: argument validation, the host mirror of
+// sequence lengths, and kernel launches.  No compute happens here and there is no CPU path:
+// every step of the method runs in the HIP kernels.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kvc.h"
+#include "kvc_internal.h"
+
+using kvc::DevBufs;
+using kvc::Geo;
+using kvc::SeqList;
+
+struct kvc_cache {
+  kvc_params p;
+  Geo G;
+  DevBufs B;
+  std::vector<int32_t> len;  // tokens per sequence (host mirror)
+  bool calibrated = false;
+  long long blocks = 0;      // finished blocks over all sequences
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(int err, const char* what) {
+  if (err == 0) return KVC_OK;
+  g_err = std::string(what) + ": " + hipGetErrorString((hipError_t)err);
+  return KVC_EHIP;
+}
+
+int esc_cap_of(const kvc_params& p) { return p.esc_cap_bytes < 0 ? p.block_tokens * p.head_dim / 16 : p.esc_cap_bytes; }
+
+int check_params(const kvc_params* p) {
+  if (!p) return fail(KVC_EINVAL, "params is NULL");
+  if (p->dtype < 0 || p->dtype > 2) return fail(KVC_EINVAL, "dtype must be KVC_BF16, KVC_FP8_E5M2 or KVC_FP8_E4M3");
+  if (p->num_kv_heads < 1 || p->num_q_heads < 1) return fail(KVC_EINVAL, "head counts must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads != 0) return fail(KVC_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
+  if (p->num_q_heads / p->num_kv_heads > 16) return fail(KVC_EINVAL, "at most 16 query heads per KV head");
+  if (p->head_dim != 64 && p->head_dim != 128) return fail(KVC_EINVAL, "head_dim must be 64 or 128");
+  if (p->block_tokens < 16 || p->block_tokens % 16 != 0) return fail(KVC_EINVAL, "block_tokens must be a multiple of 16");
+  if (p->group_tokens < 1 || p->block_tokens % p->group_tokens != 0)
+    return fail(KVC_EINVAL, "group_tokens must divide block_tokens");
+  const int cap = esc_cap_of(*p);
+  if (cap < 0 || cap % 16 != 0 || cap > 2032) return fail(KVC_EINVAL, "esc_cap_bytes must be a multiple of 16, <= 2032");
+  if (p->compressed != 0 && p->compressed != 1) return fail(KVC_EINVAL, "compressed must be 0 or 1");
+  if (p->max_seqs < 1 || p->max_blocks_per_seq < 1) return fail(KVC_EINVAL, "max_seqs and max_blocks_per_seq >= 1");
+  if (p->num_raw_slots < 0 || p->num_comp_slots < 0) return fail(KVC_EINVAL, "slot counts must be >= 0");
+  if (p->num_raw_slots >= (1 << 24) || p->num_comp_slots >= (1 << 24)) return fail(KVC_EINVAL, "slot counts < 2^24");
+  if (p->compressed && p->num_comp_slots < 1) return fail(KVC_EINVAL, "a compressed cache needs compressed slots");
+  if (!p->compressed && p->num_raw_slots < 1) return fail(KVC_EINVAL, "an uncompressed cache needs raw slots");
+  // valid requests the kernels of this build do not implement
+  if (p->dtype != KVC_BF16) return fail(KVC_EUNSUPPORTED, "FP8 caches are not implemented by these kernels");
+  if (p->group_tokens != kvc::kGroup) return fail(KVC_EUNSUPPORTED, "these kernels implement 16-token groups");
+  if (p->block_tokens > 64) return fail(KVC_EUNSUPPORTED, "these kernels implement block_tokens <= 64");
+  if (cap > 512) return fail(KVC_EUNSUPPORTED, "these kernels implement esc_cap_bytes <= 512");
+  return KVC_OK;
+}
+
+int align16(int x) { return (x + 15) / 16 * 16; }
+
+Geo make_geo(const kvc_params& p) {
+  Geo G;
+  memset(&G, 0, sizeof(G));
+  G.T = p.block_tokens;
+  G.D = p.head_dim;
+  G.Hkv = p.num_kv_heads;
+  G.Hq = p.num_q_heads;
+  G.g = p.num_q_heads / p.num_kv_heads;
+  G.NT = G.T / kvc::kGroup;
+  G.NG = G.NT * G.D;
+  G.NP = G.NG / 2;
+  G.PW = (G.NG + 31) / 32;
+  G.tag_off = 0;
+  G.code_off = align16(2 * G.PW * 4);
+  G.sm_off = G.code_off + align16(G.T * G.D * 3 / 8);
+  G.esc_off = G.sm_off + align16(G.T * G.D);
+  G.esc_cap = esc_cap_of(p);
+  G.stride = G.esc_off + G.esc_cap;
+  G.raw_elems = G.T * G.D;
+  G.max_seqs = p.max_seqs;
+  G.max_blocks = p.max_blocks_per_seq;
+  G.n_comp = p.compressed ? p.num_comp_slots : 0;
+  G.n_raw = p.num_raw_slots;
+  G.compressed = p.compressed;
+  return G;
+}
+
+void sizes_of(const kvc_params& p, const Geo& G, size_t out[KVC_NUM_BUFFERS]) {
+  out[0] = (size_t)G.n_comp * G.stride;
+  out[1] = (size_t)G.n_raw * G.raw_elems * 2;
+  out[2] = (size_t)p.max_seqs * 2 * G.Hkv * G.raw_elems * 2;
+  out[3] = (size_t)4 * G.Hkv * G.D;
+  out[4] = (size_t)p.max_seqs * p.max_blocks_per_seq * 2 * G.Hkv * 4;
+  out[5] = (size_t)G.n_comp * 4;
+  out[6] = (size_t)G.n_raw * 4;
+  out[7] = sizeof(kvc::Counters) <= 128 ? 128 : sizeof(kvc::Counters);
+}
+
+uint64_t splitmix64(uint64_t& s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+std::vector<int32_t> permutation(int n, uint64_t seed) {
+  std::vector<int32_t> v(n);
+  for (int i = 0; i < n; ++i) v[i] = i;
+  uint64_t s = seed;
+  for (int i = n - 1; i > 0; --i) {
+    const int k = (int)(splitmix64(s) % (uint64_t)(i + 1));
+    std::swap(v[i], v[k]);
+  }
+  return v;
+}
+
+int check_seq_ids(const kvc_cache* c, const int32_t* ids, int n) {
+  if (!ids || n < 1) return fail(KVC_EINVAL, "seq_ids must list at least one sequence");
+  std::vector<char> seen(c->p.max_seqs, 0);
+  for (int i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= c->p.max_seqs) return fail(KVC_EINVAL, "sequence id out of range");
+    if (seen[ids[i]]) return fail(KVC_EINVAL, "sequence ids must be distinct");
+    seen[ids[i]] = 1;
+  }
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_buffer_sizes(const kvc_params* params, size_t* out_bytes, size_t* slot_stride) {
+  const int rc = check_params(params);
+  if (rc != KVC_OK) return rc;
+  if (!out_bytes) return fail(KVC_EINVAL, "out_bytes is NULL");
+  const Geo G = make_geo(*params);
+  sizes_of(*params, G, out_bytes);
+  if (slot_stride) *slot_stride = (size_t)G.stride;
+  return KVC_OK;
+}
+
+int kv_cache_create(const kvc_params* params, const kvc_buffers* buffers, uint64_t perm_seed, void* stream,
+                    kvc_cache** out) {
+  int rc = check_params(params);
+  if (rc != KVC_OK) return rc;
+  if (!buffers || !out) return fail(KVC_EINVAL, "buffers and out must not be NULL");
+  *out = nullptr;
+  const Geo G = make_geo(*params);
+  size_t sz[KVC_NUM_BUFFERS];
+  sizes_of(*params, G, sz);
+  void* const ptrs[KVC_NUM_BUFFERS] = {buffers->comp_pool, buffers->raw_pool, buffers->tail, buffers->bases,
+                                       buffers->block_table, buffers->comp_free, buffers->raw_free,
+                                       buffers->counters};
+  for (int i = 0; i < KVC_NUM_BUFFERS; ++i) {
+    if (sz[i] > 0 && !ptrs[i]) return fail(KVC_EINVAL, "a required device buffer is NULL");
+    if (ptrs[i] && ((uintptr_t)ptrs[i] & 15u)) return fail(KVC_EINVAL, "device buffers must be 16-byte aligned");
+  }
+  kvc_cache* c = new (std::nothrow) kvc_cache;
+  if (!c) return fail(KVC_EINVAL, "out of host memory");
+  c->p = *params;
+  c->G = G;
+  c->B.comp_pool = (uint8_t*)buffers->comp_pool;
+  c->B.raw_pool = (uint16_t*)buffers->raw_pool;
+  c->B.tail = (uint16_t*)buffers->tail;
+  c->B.bases = (uint8_t*)buffers->bases;
+  c->B.table = (uint32_t*)buffers->block_table;
+  c->B.comp_free = (int32_t*)buffers->comp_free;
+  c->B.raw_free = (int32_t*)buffers->raw_free;
+  c->B.counters = (kvc::Counters*)buffers->counters;
+  c->len.assign(params->max_seqs, 0);
+  hipStream_t st = (hipStream_t)stream;
+  if (G.n_comp > 0) {
+    const std::vector<int32_t> perm = permutation(G.n_comp, perm_seed);
+    rc = hip_fail((int)hipMemcpyAsync(c->B.comp_free, perm.data(), perm.size() * 4, hipMemcpyHostToDevice, st),
+                  "copy compressed free stack");
+    if (rc == KVC_OK) rc = hip_fail((int)hipStreamSynchronize(st), "synchronise");
+  }
+  if (rc == KVC_OK && G.n_raw > 0) {
+    const std::vector<int32_t> perm = permutation(G.n_raw, perm_seed ^ 0x5A5A5A5A5A5A5A5Aull);
+    rc = hip_fail((int)hipMemcpyAsync(c->B.raw_free, perm.data(), perm.size() * 4, hipMemcpyHostToDevice, st),
+                  "copy raw free stack");
+    if (rc == KVC_OK) rc = hip_fail((int)hipStreamSynchronize(st), "synchronise");
+  }
+  if (rc == KVC_OK) rc = hip_fail(kvc::launch_init(G, c->B, nullptr, nullptr, stream), "launch init");
+  if (rc == KVC_OK) rc = hip_fail((int)hipStreamSynchronize(st), "synchronise");
+  if (rc != KVC_OK) {
+    delete c;
+    return rc;
+  }
+  *out = c;
+  return KVC_OK;
+}
+
+void kv_cache_destroy(kvc_cache* cache) { delete cache; }
+
+int kv_calibrate(kvc_cache* c, const void* k_dev, const void* v_dev, int32_t n_tokens, void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  if (!k_dev || !v_dev || n_tokens < 1) return fail(KVC_EINVAL, "calibration needs K and V with n_tokens >= 1");
+  if (c->blocks > 0) return fail(KVC_ESTATE, "calibration must precede the first finished block");
+  const int rc = hip_fail(kvc::launch_calibrate(c->G, c->B, (const uint16_t*)k_dev, (const uint16_t*)v_dev,
+                                                n_tokens, stream),
+                          "launch calibrate");
+  if (rc == KVC_OK) c->calibrated = true;
+  return rc;
+}
+
+int kv_encode_append(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* k_dev, const void* v_dev,
+                     int32_t n_tokens, void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  int rc = check_seq_ids(c, seq_ids_host, n_seqs);
+  if (rc != KVC_OK) return rc;
+  if (!k_dev || !v_dev || n_tokens < 1) return fail(KVC_EINVAL, "append needs K and V with n_tokens >= 1");
+  const int T = c->G.T;
+  long long new_blocks = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const long long L1 = (long long)c->len[seq_ids_host[i]] + n_tokens;
+    if (L1 / T > c->p.max_blocks_per_seq) return fail(KVC_ENOSLOT, "sequence would exceed max_blocks_per_seq");
+    if (L1 > INT32_MAX) return fail(KVC_EINVAL, "sequence too long");
+    new_blocks += L1 / T - c->len[seq_ids_host[i]] / T;
+  }
+  if (new_blocks > 0 && c->p.compressed && !c->calibrated)
+    return fail(KVC_ESTATE, "kv_calibrate must run before the first block is encoded");
+  const size_t row = (size_t)c->G.Hkv * c->G.D;
+  for (int s0 = 0; s0 < n_seqs; s0 += kvc::kMaxSeqsPerLaunch) {
+    SeqList S;
+    S.n = std::min(kvc::kMaxSeqsPerLaunch, n_seqs - s0);
+    int max_new = 0;
+    for (int i = 0; i < S.n; ++i) {
+      const int id = seq_ids_host[s0 + i];
+      S.ids[i] = id;
+      S.lens[i] = c->len[id];
+      max_new = std::max(max_new, (c->len[id] + n_tokens) / T - c->len[id] / T);
+    }
+    const uint16_t* k = (const uint16_t*)k_dev + (size_t)s0 * n_tokens * row;
+    const uint16_t* v = (const uint16_t*)v_dev + (size_t)s0 * n_tokens * row;
+    rc = hip_fail(kvc::launch_append(c->G, c->B, S, k, v, n_tokens, max_new, stream), "launch append");
+    if (rc != KVC_OK) return rc;
+  }
+  for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] += n_tokens;
+  c->blocks += new_blocks;
+  return KVC_OK;
+}
+
+int kv_decode_blocks(kvc_cache* c, int32_t seq, int32_t first_block, int32_t n_blocks, void* k_out_dev,
+                     void* v_out_dev, void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  if (seq < 0 || seq >= c->p.max_seqs) return fail(KVC_EINVAL, "sequence id out of range");
+  if (!k_out_dev || !v_out_dev || first_block < 0 || n_blocks < 1) return fail(KVC_EINVAL, "bad block range");
+  if (first_block + n_blocks > c->len[seq] / c->G.T) return fail(KVC_EINVAL, "blocks past the finished blocks");
+  return hip_fail(kvc::launch_decode_blocks(c->G, c->B, seq, first_block, n_blocks, (uint16_t*)k_out_dev,
+                                            (uint16_t*)v_out_dev, stream),
+                  "launch decode_blocks");
+}
+
+size_t kv_attention_workspace_bytes(const kvc_params* p, int32_t n_seqs, int32_t n_splits) {
+  if (!p || n_seqs < 1 || n_splits < 1) return 0;
+  return (size_t)n_seqs * p->num_q_heads * n_splits * ((size_t)p->head_dim + 2) * 4;
+}
+
+int kv_attention_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev, float scale,
+                          int32_t n_splits, void* ws_dev, size_t ws_bytes, void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  int rc = check_seq_ids(c, seq_ids_host, n_seqs);
+  if (rc != KVC_OK) return rc;
+  if (!q_dev || !ws_dev) return fail(KVC_EINVAL, "q and workspace must not be NULL");
+  if (n_splits < 1 || n_splits > 1024) return fail(KVC_EINVAL, "n_splits must be in 1..1024");
+  if (ws_bytes < kv_attention_workspace_bytes(&c->p, n_seqs, n_splits))
+    return fail(KVC_ESMALLWS, "workspace smaller than kv_attention_workspace_bytes()");
+  if (((uintptr_t)ws_dev & 15u) || ((uintptr_t)q_dev & 15u)) return fail(KVC_EINVAL, "q and workspace must be 16-byte aligned");
+  for (int i = 0; i < n_seqs; ++i)
+    if (c->len[seq_ids_host[i]] < 1) return fail(KVC_EINVAL, "every listed sequence needs at least one token");
+  const Geo& G = c->G;
+  float* acc = (float*)ws_dev;
+  float* ml = acc + (size_t)n_seqs * G.Hq * n_splits * G.D;
+  for (int s0 = 0; s0 < n_seqs; s0 += kvc::kMaxSeqsPerLaunch) {
+    SeqList S;
+    S.n = std::min(kvc::kMaxSeqsPerLaunch, n_seqs - s0);
+    for (int i = 0; i < S.n; ++i) {
+      S.ids[i] = seq_ids_host[s0 + i];
+      S.lens[i] = c->len[S.ids[i]];
+    }
+    rc = hip_fail(kvc::launch_attention_partials(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale,
+                                                 n_splits, acc + (size_t)s0 * G.Hq * n_splits * G.D,
+                                                 ml + (size_t)s0 * G.Hq * n_splits * 2, stream),
+                  "launch attention");
+    if (rc != KVC_OK) return rc;
+  }
+  return KVC_OK;
+}
+
+int kv_attention_combine(kvc_cache* c, int32_t n_seqs, int32_t n_splits, const void* ws_dev, size_t ws_bytes,
+                         void* out_dev, void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  if (n_seqs < 1 || n_splits < 1 || n_splits > 1024) return fail(KVC_EINVAL, "bad n_seqs or n_splits");
+  if (!ws_dev || !out_dev) return fail(KVC_EINVAL, "workspace and out must not be NULL");
+  if (ws_bytes < kv_attention_workspace_bytes(&c->p, n_seqs, n_splits))
+    return fail(KVC_ESMALLWS, "workspace smaller than kv_attention_workspace_bytes()");
+  const Geo& G = c->G;
+  const float* acc = (const float*)ws_dev;
+  const float* ml = acc + (size_t)n_seqs * G.Hq * n_splits * G.D;
+  return hip_fail(kvc::launch_combine(G, n_seqs, n_splits, acc, ml, (uint16_t*)out_dev, stream), "launch combine");
+}
+
+int kv_decode_attention(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev, float scale,
+                        int32_t n_splits, void* ws_dev, size_t ws_bytes, void* out_dev, void* stream) {
+  if (!out_dev) return fail(KVC_EINVAL, "out must not be NULL");
+  const int rc = kv_attention_partials(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, stream);
+  if (rc != KVC_OK) return rc;
+  return kv_attention_combine(c, n_seqs, n_splits, ws_dev, ws_bytes, out_dev, stream);
+}
+
+int kv_release_seq(kvc_cache* c, int32_t seq, void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  if (seq < 0 || seq >= c->p.max_seqs) return fail(KVC_EINVAL, "sequence id out of range");
+  const int nb = c->len[seq] / c->G.T;
+  const int rc = hip_fail(kvc::launch_release(c->G, c->B, seq, nb, stream), "launch release");
+  if (rc == KVC_OK) {
+    c->blocks -= nb;
+    c->len[seq] = 0;
+  }
+  return rc;
+}
+
+int kv_seq_length(const kvc_cache* c, int32_t seq, int32_t* length) {
+  if (!c || !length) return fail(KVC_EINVAL, "cache and length must not be NULL");
+  if (seq < 0 || seq >= c->p.max_seqs) return fail(KVC_EINVAL, "sequence id out of range");
+  *length = c->len[seq];
+  return KVC_OK;
+}
+
+int kv_get_status(kvc_cache* c, uint32_t* flags, kvc_stats* stats, void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  kvc::Counters h;
+  hipStream_t st = (hipStream_t)stream;
+  int rc = hip_fail((int)hipMemcpyAsync(&h, c->B.counters, sizeof(h), hipMemcpyDeviceToHost, st), "read counters");
+  if (rc == KVC_OK) rc = hip_fail((int)hipStreamSynchronize(st), "synchronise");
+  if (rc != KVC_OK) return rc;
+  if (flags) *flags = h.status;
+  if (stats) {
+    stats->comp_tiles = h.comp_tiles;
+    stats->raw_tiles = h.raw_tiles;
+    for (int i = 0; i < 3; ++i) stats->groups[i] = h.groups[i];
+    stats->esc_bytes = h.esc_bytes;
+    stats->comp_free = h.comp_top;
+    stats->raw_free = h.raw_top;
+  }
+  return KVC_OK;
+}
+
+const char* kv_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

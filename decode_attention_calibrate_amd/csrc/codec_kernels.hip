@@ -1,0 +1,465 @@
+// codec_kernels.hip -- cache initialisation, window calibration, block encode (append), tail
+// update, slot release and block decode for the lossless KV codec of the page "GAAC: Lossless
+// KV Compression for Bandwidth-Efficient LLM Inference on Personal Devices" (§3.1 codec,
+// §3.3 fill-then-finalize blocks in fixed-capacity slots with a block table).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "codec_dev.h"
+#include "kvc_internal.h"
+
+namespace kvc {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int block_sum(int v, int* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  int s = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+  return s;
+}
+
+__device__ __forceinline__ int block_max(int v, int* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  int s = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) s = max(s, red[i]);
+  return s;
+}
+
+// Exclusive prefix sum over the block (thread order); *total receives the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  __syncthreads();
+  if (lane == 63) red[w] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
+    if (i < w) before += red[i];
+    all += red[i];
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+__global__ void init_kernel(Geo G, DevBufs B) {
+  const size_t n_table = (size_t)G.max_seqs * G.max_blocks * 2 * G.Hkv;
+  const size_t n_bases = (size_t)4 * G.Hkv * G.D;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_table; i += stride) B.table[i] = kUnallocated;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_bases; i += stride) B.bases[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    Counters* c = B.counters;
+    c->comp_top = G.compressed ? G.n_comp : 0;
+    c->raw_top = G.n_raw;
+    c->status = 0;
+    c->pad = 0;
+    c->comp_tiles = c->raw_tiles = 0;
+    c->groups[0] = c->groups[1] = c->groups[2] = 0;
+    c->esc_bytes = 0;
+  }
+}
+
+// One block per (channel, kv-head, K|V): histogram of the 8-bit exponent over the calibration
+// tokens, then the 8- and 16-wide windows with the largest count (ties: lower median start).
+__global__ void calibrate_kernel(Geo G, DevBufs B, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                 int n) {
+  __shared__ int hist[256];
+  __shared__ int red[8];
+  const int c = blockIdx.x, h = blockIdx.y, kv = blockIdx.z, tid = threadIdx.x;
+  hist[tid] = 0;
+  __syncthreads();
+  const uint16_t* src = kv ? v : k;
+  for (int t = tid; t < n; t += kThreads) {
+    const uint32_t x = src[((size_t)t * G.Hkv + h) * G.D + c];
+    atomicAdd(&hist[(x >> 7) & 0xFF], 1);
+  }
+  __syncthreads();
+  for (int w = 3; w <= 4; ++w) {
+    const int width = 1 << w, nb = 256 - width + 1;
+    int cov = -1;
+    if (tid < nb) {
+      cov = 0;
+      for (int e = tid; e < tid + width; ++e) cov += hist[e];
+    }
+    const int best = block_max(cov, red);
+    const int flag = (tid < nb && cov == best) ? 1 : 0;
+    int count;
+    const int rank = block_exclusive_scan(flag, red, &count);
+    if (flag && rank == (count - 1) / 2) B.bases[(((size_t)kv * 2 + (w - 3)) * G.Hkv + h) * G.D + c] = (uint8_t)tid;
+    __syncthreads();
+  }
+}
+
+// Mode of a group from its exponent range and the channel's bases: 0 narrow, 1 wide, 2 raw.
+__device__ __forceinline__ int choose_mode(uint32_t mn, uint32_t mx, uint32_t b3, uint32_t b4) {
+  if (b3 <= mn && mx <= b3 + 7) return 0;
+  if (b4 <= mn && mx <= b4 + 15) return 1;
+  return 2;
+}
+
+struct PairInfo {
+  int mode[2];
+  uint32_t base[2];
+};
+
+__device__ __forceinline__ PairInfo pair_info(const Geo& G, const uint16_t* tile, const uint8_t* b3, const uint8_t* b4,
+                                              int pr) {
+  PairInfo P;
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int q = 2 * pr + gi, tg = q / G.D, c = q % G.D;
+    uint32_t mn = 255, mx = 0;
+    for (int tau = 0; tau < kGroup; ++tau) {
+      const uint32_t e = (tile[(tg * kGroup + tau) * G.D + c] >> 7) & 0xFF;
+      mn = min(mn, e);
+      mx = max(mx, e);
+    }
+    P.mode[gi] = choose_mode(mn, mx, b3[c], b4[c]);
+    P.base[gi] = P.mode[gi] == 0 ? b3[c] : (P.mode[gi] == 1 ? b4[c] : 0u);
+  }
+  return P;
+}
+
+__device__ __forceinline__ int mode_planes(int m) { return m == 0 ? 0 : (m == 1 ? 1 : 5); }
+
+// One block per newly full block of one (sequence, K|V, head): gathers its T tokens from the
+// old tail and the appended tokens, encodes it (or stores it raw), pops a slot and writes the
+// block-table entry.
+__global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqList S, const uint16_t* __restrict__ kin,
+                                                          const uint16_t* __restrict__ vin, int n_tok) {
+  extern __shared__ uint32_t smem[];
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);                  // [T][D] logical
+  uint32_t* tagw = smem + (G.raw_elems / 2);                            // [2][PW]
+  __shared__ int red[8];
+  __shared__ int sh_slot, sh_raw;
+  __shared__ unsigned long long sh_modes[3];
+
+  const int si = blockIdx.y, kv = blockIdx.z / G.Hkv, h = blockIdx.z % G.Hkv;
+  const int seq = S.ids[si], L0 = S.lens[si];
+  const int first_blk = L0 / G.T, last_full = (L0 + n_tok) / G.T;
+  const int b = first_blk + blockIdx.x;
+  if (b >= last_full) return;
+  const int tid = threadIdx.x, D = G.D, T = G.T;
+  const uint16_t* in = kv ? vin : kin;
+  const uint16_t* tail = B.tail + tail_offset(G, seq, kv, h);
+  const int tail_base = first_blk * T;
+
+  for (int i = tid; i < G.raw_elems; i += kThreads) {
+    const int t = i / D, c = i % D, p = b * T + t;
+    uint16_t x;
+    if (p < L0) {
+      const int tt = p - tail_base;
+      x = kv ? tail[c * T + tt] : tail[tt * D + c];
+    } else {
+      x = in[(((size_t)si * n_tok + (p - L0)) * G.Hkv + h) * D + c];
+    }
+    tile[i] = x;
+  }
+  for (int i = tid; i < 2 * G.PW; i += kThreads) tagw[i] = 0;
+  if (tid < 3) sh_modes[tid] = 0;
+  __syncthreads();
+
+  const size_t entry_idx = table_index(G, seq, b, kv, h);
+  int is_raw = 1, total = 0;
+  const uint8_t* b3 = B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
+  const uint8_t* b4 = B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;
+  const int ppt = (G.NP + kThreads - 1) / kThreads;  // pairs per thread (consecutive)
+  const int pr0 = tid * ppt;
+  int my_before = 0;
+  if (G.compressed) {
+    int my_planes = 0;
+    int cnt[3] = {0, 0, 0};
+    for (int k = 0; k < ppt; ++k) {
+      const int pr = pr0 + k;
+      if (pr >= G.NP) break;
+      const PairInfo P = pair_info(G, tile, b3, b4, pr);
+      my_planes += mode_planes(P.mode[0]) + mode_planes(P.mode[1]);
+      cnt[P.mode[0]]++;
+      cnt[P.mode[1]]++;
+    }
+    my_before = block_exclusive_scan(my_planes, red, &total);
+    is_raw = (2 * total > G.esc_cap) ? 1 : 0;
+    for (int m = 0; m < 3; ++m) {
+      const int s = block_sum(cnt[m], red);
+      if (tid == 0) sh_modes[m] = (unsigned long long)s;
+    }
+  }
+
+  if (tid == 0) {
+    Counters* C = B.counters;
+    int slot = -1, raw = is_raw;
+    if (!raw) {
+      const int idx = atomicSub(&C->comp_top, 1) - 1;
+      if (idx >= 0) {
+        slot = B.comp_free[idx];
+      } else {
+        atomicAdd(&C->comp_top, 1);
+        atomicOr(&C->status, 1u);
+        raw = 1;
+      }
+    }
+    if (raw) {
+      const int idx = atomicSub(&C->raw_top, 1) - 1;
+      if (idx >= 0) {
+        slot = B.raw_free[idx];
+      } else {
+        atomicAdd(&C->raw_top, 1);
+        atomicOr(&C->status, 2u);
+      }
+    }
+    sh_slot = slot;
+    sh_raw = raw;
+    if (slot >= 0) {
+      if (raw) {
+        atomicAdd(&C->raw_tiles, 1ull);
+      } else {
+        atomicAdd(&C->comp_tiles, 1ull);
+        atomicAdd(&C->groups[0], sh_modes[0]);
+        atomicAdd(&C->groups[1], sh_modes[1]);
+        atomicAdd(&C->groups[2], sh_modes[2]);
+        atomicAdd(&C->esc_bytes, (unsigned long long)(2 * total));
+      }
+    }
+  }
+  __syncthreads();
+  const int slot = sh_slot, raw = sh_raw;
+  if (slot < 0) {
+    if (tid == 0) B.table[entry_idx] = kUnallocated;
+    return;
+  }
+
+  if (raw) {
+    uint16_t* dst = B.raw_pool + (size_t)slot * G.raw_elems;
+    for (int i = tid; i < G.raw_elems; i += kThreads) {
+      if (kv) {
+        const int c = i / T, t = i % T;
+        dst[i] = tile[t * D + c];
+      } else {
+        dst[i] = tile[i];
+      }
+    }
+    if (tid == 0) B.table[entry_idx] = (uint32_t)slot | 0x80000000u;
+    return;
+  }
+
+  uint8_t* dst = B.comp_pool + (size_t)slot * G.stride;
+  int P = my_before;
+  for (int k = 0; k < ppt; ++k) {
+    const int pr = pr0 + k;
+    if (pr >= G.NP) break;
+    const PairInfo PI = pair_info(G, tile, b3, b4, pr);
+    uint32_t W[3] = {0u, 0u, 0u};
+    uint32_t smw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) smw[i] = 0;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int q = 2 * pr + gi, tg = q / D, c = q % D;
+      const int np = mode_planes(PI.mode[gi]);
+      uint32_t planes[5] = {0u, 0u, 0u, 0u, 0u};
+      for (int tau = 0; tau < kGroup; ++tau) {
+        const uint32_t x = tile[(tg * kGroup + tau) * D + c];
+        const uint32_t o = ((x >> 7) & 0xFF) - PI.base[gi];
+        const int r = gi * kGroup + tau, lk = r & 3, s = r >> 2;
+        const uint32_t code = o & 7u;
+        for (int bb = 0; bb < 3; ++bb) {
+          const int xs = 3 * s + bb;
+          W[xs >> 3] |= ((code >> bb) & 1u) << (8 * lk + (xs & 7));
+        }
+        smw[r >> 2] |= (((x >> 8) & 0x80u) | (x & 0x7Fu)) << (8 * (r & 3));
+        for (int p = 0; p < np; ++p) planes[p] |= ((o >> (3 + p)) & 1u) << tau;
+      }
+      uint16_t* esc16 = reinterpret_cast<uint16_t*>(dst + G.esc_off);
+      for (int p = 0; p < np; ++p) esc16[P + p] = (uint16_t)planes[p];
+      P += np;
+      if (PI.mode[gi] >= 1) atomicOr(&tagw[q >> 5], 1u << (q & 31));
+      if (PI.mode[gi] == 2) atomicOr(&tagw[G.PW + (q >> 5)], 1u << (q & 31));
+    }
+    uint32_t* code = reinterpret_cast<uint32_t*>(dst + G.code_off + 12 * pr);
+    code[0] = W[0];
+    code[1] = W[1];
+    code[2] = W[2];
+    uint4* smd = reinterpret_cast<uint4*>(dst + G.sm_off + 32 * pr);
+    smd[0] = make_uint4(smw[0], smw[1], smw[2], smw[3]);
+    smd[1] = make_uint4(smw[4], smw[5], smw[6], smw[7]);
+  }
+  // zero the unused escape bytes [2*total, esc_cap)
+  {
+    const int used = 2 * total;
+    if ((used & 3) && tid == 0) reinterpret_cast<uint16_t*>(dst + G.esc_off)[total] = 0;
+    const int w0 = (used + 3) >> 2;
+    uint32_t* esc32 = reinterpret_cast<uint32_t*>(dst + G.esc_off);
+    for (int i = w0 + tid; i < (G.esc_cap >> 2); i += kThreads) esc32[i] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < 2 * G.PW; i += kThreads) reinterpret_cast<uint32_t*>(dst + G.tag_off)[i] = tagw[i];
+  if (tid == 0) {
+    const uint32_t units = (uint32_t)((2 * total + 15) >> 4);
+    B.table[entry_idx] = (uint32_t)slot | (units << 24);
+  }
+}
+
+// Writes the appended tokens that do not complete a block into the sequence's tail.
+__global__ void tail_kernel(Geo G, DevBufs B, SeqList S, const uint16_t* __restrict__ kin,
+                            const uint16_t* __restrict__ vin, int n_tok) {
+  const int si = blockIdx.x, kv = blockIdx.y / G.Hkv, h = blockIdx.y % G.Hkv;
+  const int seq = S.ids[si], L0 = S.lens[si];
+  const int new_full = (L0 + n_tok) / G.T;
+  const int p0 = max(L0, new_full * G.T), p1 = L0 + n_tok;
+  const int D = G.D, T = G.T;
+  const uint16_t* in = kv ? vin : kin;
+  uint16_t* tail = B.tail + tail_offset(G, seq, kv, h);
+  for (int i = threadIdx.x; i < (p1 - p0) * D; i += blockDim.x) {
+    const int p = p0 + i / D, c = i % D, tt = p - new_full * T;
+    const uint16_t x = in[(((size_t)si * n_tok + (p - L0)) * G.Hkv + h) * D + c];
+    if (kv) tail[c * T + tt] = x;
+    else tail[tt * D + c] = x;
+  }
+}
+
+__global__ void release_kernel(Geo G, DevBufs B, int seq, int n_blocks) {
+  const int n = n_blocks * 2 * G.Hkv;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const size_t idx = (size_t)seq * G.max_blocks * 2 * G.Hkv + i;
+    const uint32_t e = B.table[idx];
+    if (e == kUnallocated) continue;
+    const int slot = (int)(e & 0x00FFFFFFu);
+    if (e & 0x80000000u) {
+      const int t = atomicAdd(&B.counters->raw_top, 1);
+      B.raw_free[t] = slot;
+    } else {
+      const int t = atomicAdd(&B.counters->comp_top, 1);
+      B.comp_free[t] = slot;
+    }
+    B.table[idx] = kUnallocated;
+  }
+}
+
+// One block per (block, K|V, head): rebuilds the tile into [n*T][Hkv][D].
+__global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs B, int seq, int first,
+                                                                  uint16_t* __restrict__ kout,
+                                                                  uint16_t* __restrict__ vout) {
+  const int bi = blockIdx.x, kv = blockIdx.y / G.Hkv, h = blockIdx.y % G.Hkv;
+  const int b = first + bi, D = G.D, T = G.T, tid = threadIdx.x;
+  uint16_t* out = kv ? vout : kout;
+  const uint32_t e = B.table[table_index(G, seq, b, kv, h)];
+  auto out_at = [&](int t, int c) -> uint16_t* { return out + (((size_t)bi * T + t) * G.Hkv + h) * D + c; };
+  if (e == kUnallocated) {
+    for (int i = tid; i < G.raw_elems; i += kThreads) *out_at(i / D, i % D) = 0;
+    if (tid == 0) atomicOr(&B.counters->status, 4u);
+    return;
+  }
+  const int slot = (int)(e & 0x00FFFFFFu);
+  if (e & 0x80000000u) {
+    const uint16_t* src = B.raw_pool + (size_t)slot * G.raw_elems;
+    for (int i = tid; i < G.raw_elems; i += kThreads) {
+      const int t = i / D, c = i % D;
+      *out_at(t, c) = kv ? src[c * T + t] : src[i];
+    }
+    return;
+  }
+  const uint8_t* tile = B.comp_pool + (size_t)slot * G.stride;
+  const uint32_t* tagE = reinterpret_cast<const uint32_t*>(tile + G.tag_off);
+  const uint32_t* tagR = tagE + G.PW;
+  const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(tile + G.esc_off);
+  const uint8_t* b3 = B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
+  const uint8_t* b4 = B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;
+  const int max_plane = G.esc_cap / 2;
+  for (int pr = tid; pr < G.NP; pr += kThreads) {
+    const int q0 = 2 * pr, w = q0 >> 5, bit = q0 & 31;
+    uint32_t Pw = 0;
+    for (int i = 0; i < w; ++i) Pw += __popc(tagE[i]) + 4u * __popc(tagR[i]);
+    const uint32_t Ew = tagE[w], Rw = tagR[w];
+    uint32_t P = planes_before(Ew, Rw, Pw, bit);
+    const uint4 s0 = *reinterpret_cast<const uint4*>(tile + G.sm_off + 32 * pr);
+    const uint4 s1 = *reinterpret_cast<const uint4*>(tile + G.sm_off + 32 * pr + 16);
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(tile + G.code_off + 12 * pr);
+    const uint32_t W0 = cw[0], W1 = cw[1], W2 = cw[2];
+    const int tg = q0 / D, c0 = q0 % D;
+    uint32_t outs[2][2][4];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const uint32_t E = (Ew >> (bit + gi)) & 1u, R = (Rw >> (bit + gi)) & 1u;
+      if (R && !E) atomicOr(&B.counters->status, 8u);
+      const int mode = (int)(E + R);
+      const int c = c0 + gi;
+      const uint32_t base = mode == 0 ? b3[c] : (mode == 1 ? b4[c] : 0u);
+      uint32_t plane0 = 0, pl[4] = {0u, 0u, 0u, 0u};
+      int nextra = 0;
+      if (E && (int)P < max_plane) plane0 = esc16[P];
+      if (R) {
+        nextra = 4;
+        for (int p = 0; p < 4; ++p) pl[p] = ((int)P + 1 + p < max_plane) ? esc16[P + 1 + p] : 0u;
+      }
+      const uint32_t smv[4] = {gi ? s1.x : s0.x, gi ? s1.y : s0.y, gi ? s1.z : s0.z, gi ? s1.w : s0.w};
+      if (gi == 0) rebuild_group<0>(smv, W0, W1, W2, base, plane0, pl, nextra, outs[0][0], outs[0][1]);
+      else rebuild_group<1>(smv, W0, W1, W2, base, plane0, pl, nextra, outs[1][0], outs[1][1]);
+      P += E + 4u * R;
+    }
+    for (int j = 0; j < 4; ++j) {
+      const int t = tg * kGroup + 4 * j;
+      // (c0, c1) pairs per token
+      *reinterpret_cast<uint32_t*>(out_at(t + 0, c0)) = perm_b32(outs[1][0][j], outs[0][0][j], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(out_at(t + 2, c0)) = perm_b32(outs[1][0][j], outs[0][0][j], 0x07060302u);
+      *reinterpret_cast<uint32_t*>(out_at(t + 1, c0)) = perm_b32(outs[1][1][j], outs[0][1][j], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(out_at(t + 3, c0)) = perm_b32(outs[1][1][j], outs[0][1][j], 0x07060302u);
+    }
+  }
+}
+
+}  // namespace
+
+int launch_init(const Geo& G, const DevBufs& B, const int32_t*, const int32_t*, void* stream) {
+  hipLaunchKernelGGL(init_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream, G, B);
+  return (int)hipGetLastError();
+}
+
+int launch_calibrate(const Geo& G, const DevBufs& B, const uint16_t* k, const uint16_t* v, int n, void* stream) {
+  hipLaunchKernelGGL(calibrate_kernel, dim3(G.D, G.Hkv, 2), dim3(kThreads), 0, (hipStream_t)stream, G, B, k, v, n);
+  return (int)hipGetLastError();
+}
+
+int launch_append(const Geo& G, const DevBufs& B, const SeqList& S, const uint16_t* k, const uint16_t* v,
+                  int n_tokens, int max_new_blocks, void* stream) {
+  if (max_new_blocks > 0) {
+    const size_t lds = (size_t)G.raw_elems * 2 + (size_t)2 * G.PW * 4;
+    hipLaunchKernelGGL(encode_kernel, dim3(max_new_blocks, S.n, 2 * G.Hkv), dim3(kThreads), lds,
+                       (hipStream_t)stream, G, B, S, k, v, n_tokens);
+    const int err = (int)hipGetLastError();
+    if (err) return err;
+  }
+  hipLaunchKernelGGL(tail_kernel, dim3(S.n, 2 * G.Hkv), dim3(256), 0, (hipStream_t)stream, G, B, S, k, v, n_tokens);
+  return (int)hipGetLastError();
+}
+
+int launch_release(const Geo& G, const DevBufs& B, int seq, int n_blocks, void* stream) {
+  if (n_blocks <= 0) return 0;
+  const int n = n_blocks * 2 * G.Hkv;
+  hipLaunchKernelGGL(release_kernel, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, G, B, seq, n_blocks);
+  return (int)hipGetLastError();
+}
+
+int launch_decode_blocks(const Geo& G, const DevBufs& B, int seq, int first, int n, uint16_t* k_out,
+                         uint16_t* v_out, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(decode_blocks_kernel, dim3(n, 2 * G.Hkv), dim3(kThreads), 0, (hipStream_t)stream, G, B, seq,
+                     first, k_out, v_out);
+  return (int)hipGetLastError();
+}
+
+}  // namespace kvc

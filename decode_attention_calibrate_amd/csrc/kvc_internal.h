@@ -1,0 +1,85 @@
+// kvc_internal.h -- geometry, kernel argument blocks and launcher declarations shared by the
+// C-ABI host code (api.cpp) and the HIP kernels.  Not part of the public ABI.
+//
+// Compressed tile layout (FORMAT v1, this library's byte layout for the codec of the page
+// "GAAC: Lossless KV Compression for Bandwidth-Efficient LLM Inference on Personal Devices",
+// §3.1 codec, App. D stored pieces).  One tile = T tokens x D channels of one (K|V, kv-head):
+//   group q = tg*D + c = tokens tg*16 .. tg*16+15 of channel c; element n = 16q + tau;
+//   TAG  : plane E (mode >= 1) then plane R (mode == 2), PW = NG/32 little-endian words each;
+//   CODE : 3-bit offset codes; 12-byte units of 32 elements (one pair of groups); element
+//          r of a unit lives in byte lane r%4, slot r/4 of a 24-bit lane stream spread over
+//          the unit's three words (byte lane k of word w = stream bits 8w..8w+7);
+//   SM   : BF16 sign/mantissa byte (s << 7) | m per element, element order;
+//   ESC  : for every group with mode >= 1, in q order, (w - 3) 16-bit planes holding bit 3+p
+//          of the 16 offsets (bit tau = token tau); zero up to esc_cap;
+//   RAW  : tiles that overflow esc_cap (and every tile of an uncompressed cache) are stored
+//          as native elements, K token-major [t][c], V channel-major [c][t].
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvc {
+
+constexpr int kGroup = 16;          // tokens per exponent group handled by these kernels
+constexpr int kMaxSeqsPerLaunch = 64;
+constexpr uint32_t kUnallocated = 0xFFFFFFFFu;
+
+struct Geo {
+  int T, D, Hkv, Hq, g;             // block tokens, head dim, KV heads, query heads, Hq/Hkv
+  int NT, NG, NP, PW;               // token groups per tile, groups, group pairs, tag words
+  int tag_off, code_off, sm_off, esc_off, stride;  // compressed tile offsets (bytes)
+  int esc_cap;                      // escape capacity (bytes)
+  int raw_elems;                    // T*D
+  int max_seqs, max_blocks;
+  int n_comp, n_raw;
+  int compressed;
+};
+
+// counters buffer (128 bytes)
+struct Counters {
+  int32_t comp_top, raw_top;
+  uint32_t status, pad;
+  unsigned long long comp_tiles, raw_tiles, groups[3], esc_bytes;
+};
+
+struct DevBufs {
+  uint8_t* comp_pool;
+  uint16_t* raw_pool;
+  uint16_t* tail;
+  uint8_t* bases;        // [2][2][Hkv][D]
+  uint32_t* table;       // [max_seqs][max_blocks][2][Hkv]
+  int32_t* comp_free;
+  int32_t* raw_free;
+  Counters* counters;
+};
+
+struct SeqList {
+  int n;
+  int ids[kMaxSeqsPerLaunch];
+  int lens[kMaxSeqsPerLaunch];     // token count (attention) or token count before append
+};
+
+// table entry helpers
+__host__ __device__ inline size_t table_index(const Geo& G, int seq, int blk, int kv, int h) {
+  return (((size_t)seq * G.max_blocks + blk) * 2 + kv) * G.Hkv + h;
+}
+__host__ __device__ inline size_t tail_offset(const Geo& G, int seq, int kv, int h) {
+  return (((size_t)seq * 2 + kv) * G.Hkv + h) * (size_t)G.raw_elems;
+}
+
+// ---- launchers (defined in the .hip files; return hipError_t as int) ----
+int launch_init(const Geo& G, const DevBufs& B, const int32_t* comp_perm_dev, const int32_t* raw_perm_dev,
+                void* stream);
+int launch_calibrate(const Geo& G, const DevBufs& B, const uint16_t* k, const uint16_t* v, int n_tokens,
+                     void* stream);
+int launch_append(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* k, const uint16_t* v,
+                  int n_tokens, int max_new_blocks, void* stream);
+int launch_release(const Geo& G, const DevBufs& B, int seq, int n_blocks, void* stream);
+int launch_decode_blocks(const Geo& G, const DevBufs& B, int seq, int first, int n, uint16_t* k_out,
+                         uint16_t* v_out, void* stream);
+int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale,
+                              int n_splits, float* ws_acc, float* ws_ml, void* stream);
+int launch_combine(const Geo& G, int n_seqs, int n_splits, const float* ws_acc, const float* ws_ml, uint16_t* out,
+                   void* stream);
+
+}  // namespace kvc

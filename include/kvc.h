@@ -1,0 +1,185 @@
+/*
+ * kvc.h -- C ABI of a lossless compressed-KV decode-attention library for AMD MI355X (gfx950).
+ *
+ * The method is the one of the page "GAAC: Lossless KV Compression for Bandwidth-Efficient LLM
+ * Inference on Personal Devices" (paperlayer.ai summary of arXiv:2610.38210v1):
+ *   - §3.1: BF16 (or FP8, App. B) exponents are stored as a calibrated per-(head, channel)
+ *     base plus a small offset; each group of tokens of one channel picks a 3-bit, 4-bit or raw
+ *     exponent mode; values outside the window widen the whole group; sign and mantissa bits
+ *     are stored unchanged, so every value is rebuilt bit for bit.
+ *   - §3.2: decode attention reads the compressed tiles and rebuilds them on chip, with the
+ *     compressed blocks, the raw blocks and the uncompressed tail in one softmax.
+ *   - §3.3 / Figure 3: new tokens accumulate in an uncompressed tail; a full block is encoded
+ *     once into a fixed-capacity slot, or kept raw if its encoding does not fit; a block table
+ *     records each block's storage mode and location.
+ * The byte layout of a compressed tile ("FORMAT v1") is this library's own; the page prints none.
+ *
+ * Conventions for every entry point:
+ *   - Plain C: no C++ types or exceptions cross this boundary.  Every call returns KVC_OK (0)
+ *     or a negative KVC_E* code and never aborts; kv_last_error() gives a message.
+ *   - "dev" pointers are device memory owned by the caller (e.g. torch tensors on one GPU).
+ *     The library never allocates or frees device memory; it allocates only the small host
+ *     object behind kvc_cache.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the default stream).  Work is only
+ *     enqueued; nothing synchronises except kv_cache_create and kv_get_status.
+ *   - Argument errors are found on the host before anything is enqueued.  Conditions found on
+ *     the device (a pool ran out, a missing block) set sticky bits read by kv_get_status.
+ *   - One kvc_cache is one layer of KV cache, used from one host thread and one stream at a time.
+ *   - Element tensors hold raw bit patterns: BF16 as 16-bit words, FP8 as bytes.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KVC_BF16 = 0, KVC_FP8_E5M2 = 1, KVC_FP8_E4M3 = 2 } kvc_dtype;
+
+enum {
+  KVC_OK = 0,
+  KVC_EINVAL = -1,        /* bad argument                                               */
+  KVC_ENOSLOT = -2,       /* not enough free slots / table room for the request         */
+  KVC_EUNSUPPORTED = -3,  /* valid request this build's kernels do not implement        */
+  KVC_EHIP = -4,          /* a HIP runtime call failed                                  */
+  KVC_ECORRUPT = -5,      /* corrupt stored data (reserved tag, escape overrun)         */
+  KVC_ESTATE = -6,        /* call not valid in the cache's current state                */
+  KVC_ESMALLWS = -7       /* workspace smaller than kv_attention_workspace_bytes()      */
+};
+
+/* Sticky device status bits (kv_get_status). */
+enum {
+  KVC_STATUS_COMP_EXHAUSTED = 1u << 0, /* a compressed slot was needed and none was free     */
+  KVC_STATUS_RAW_EXHAUSTED = 1u << 1,  /* a raw slot was needed and none was free            */
+  KVC_STATUS_MISSING_BLOCK = 1u << 2,  /* attention met an unallocated block (skipped)       */
+  KVC_STATUS_CORRUPT = 1u << 3         /* a reserved tag pair was met while decoding         */
+};
+
+typedef struct {
+  int32_t dtype;              /* kvc_dtype                                                   */
+  int32_t num_kv_heads;       /* Hkv                                                         */
+  int32_t num_q_heads;        /* Hq; Hq % Hkv == 0, Hq / Hkv <= 16 (query head hq reads KV
+                                 head hq / (Hq / Hkv))                                       */
+  int32_t head_dim;           /* D in {64, 128}                                              */
+  int32_t block_tokens;       /* T: tokens per block/tile, multiple of 16, 16..256           */
+  int32_t group_tokens;       /* G: tokens per exponent group (16 in this build)             */
+  int32_t esc_cap_bytes;      /* escape capacity per tile, multiple of 16, <= 2032;
+                                 < 0 selects T*D/16                                          */
+  int32_t compressed;         /* 1: blocks are encoded; 0: every block is stored raw (the
+                                 uncompressed baseline cache, same table and layout)         */
+  int32_t max_seqs;           /* sequence ids are 0 .. max_seqs-1                            */
+  int32_t max_blocks_per_seq; /* finished blocks a sequence may hold                         */
+  int32_t num_comp_slots;     /* compressed slot pool size (ignored when compressed == 0)    */
+  int32_t num_raw_slots;      /* raw slot pool size                                          */
+} kvc_params;
+
+/* Device buffers, all owned by the caller; sizes from kv_buffer_sizes (same order). */
+typedef struct {
+  void* comp_pool;   /* [num_comp_slots][slot_stride] bytes: compressed tiles               */
+  void* raw_pool;    /* [num_raw_slots][T*D] elements: raw tiles, K token-major [t][c],
+                        V channel-major [c][t]                                              */
+  void* tail;        /* [max_seqs][2 (K,V)][Hkv][T*D] elements, raw-tile layout             */
+  void* bases;       /* [2 (K,V)][2 (narrow b3, wide b4)][Hkv][D] uint8 calibrated bases    */
+  void* block_table; /* [max_seqs][max_blocks_per_seq][2 (K,V)][Hkv] uint32 entries:
+                        0xFFFFFFFF = unallocated; else bit 31 = raw, bits 24..30 = escape
+                        bytes used in 16-byte units, bits 0..23 = slot index                */
+  void* comp_free;   /* [num_comp_slots] int32 free stack of compressed slots               */
+  void* raw_free;    /* [num_raw_slots] int32 free stack of raw slots                       */
+  void* counters;    /* 128 bytes: int32 stack tops, uint32 status, uint64 statistics       */
+} kvc_buffers;
+
+#define KVC_NUM_BUFFERS 8
+
+typedef struct {
+  uint64_t comp_tiles;    /* tiles stored compressed                                        */
+  uint64_t raw_tiles;     /* tiles stored raw (escape overflow or compressed == 0)          */
+  uint64_t groups[3];     /* groups per mode: narrow, wide, raw (compressed tiles only)      */
+  uint64_t esc_bytes;     /* escape bytes used by compressed tiles                          */
+  int32_t comp_free;      /* free compressed slots                                          */
+  int32_t raw_free;       /* free raw slots                                                 */
+} kvc_stats;
+
+typedef struct kvc_cache kvc_cache; /* opaque host object */
+
+/* Byte size of every kvc_buffers field for these parameters (out_bytes[KVC_NUM_BUFFERS]),
+ * plus the compressed slot stride.  Host only; no GPU needed. */
+int kv_buffer_sizes(const kvc_params* params, size_t* out_bytes, size_t* slot_stride);
+
+/* Validates the parameters and buffers, initialises the block table (all unallocated), the
+ * free stacks (a permutation of the slot ids seeded by perm_seed), the counters and the bases
+ * (zero), then synchronises the stream.  *out receives a host object the caller frees with
+ * kv_cache_destroy.  The buffers must stay valid for the cache's lifetime. */
+int kv_cache_create(const kvc_params* params, const kvc_buffers* buffers, uint64_t perm_seed, void* stream,
+                    kvc_cache** out);
+void kv_cache_destroy(kvc_cache* cache);
+
+/* Window calibration (GAAC page §3.1: per-head-channel windows of 8 and 16 exponents chosen
+ * from calibration data).  k_dev, v_dev: [n_tokens][Hkv][D] elements (typically the first
+ * tokens of one sequence).  For each (K|V, head, channel) the narrow base b3 is the start of
+ * the 8-wide exponent window holding the most calibration exponents and b4 the same for the
+ * 16-wide window; ties take the lower median of the tied starts.  Must precede the first
+ * block encode (KVC_ESTATE otherwise) and may not be repeated once blocks exist. */
+int kv_calibrate(kvc_cache* cache, const void* k_dev, const void* v_dev, int32_t n_tokens, void* stream);
+
+/* Appends n_tokens tokens to each listed sequence (GAAC page §3.3, fill-then-finalize).
+ * k_dev, v_dev: [n_seqs][n_tokens][Hkv][D] elements.  Tokens go to the sequence's tail; each
+ * block that becomes full is encoded once into a compressed slot, or stored raw when its
+ * escape planes exceed the capacity (or when compressed == 0), and its table entry is written.
+ * n_tokens == 1 is a decode step; larger values are a bulk (prefill) append.  seq_ids_host:
+ * host array of n_seqs distinct ids.  KVC_ENOSLOT if a sequence would exceed
+ * max_blocks_per_seq; pool exhaustion is detected on the device (status bits). */
+int kv_encode_append(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs, const void* k_dev,
+                     const void* v_dev, int32_t n_tokens, void* stream);
+
+/* Rebuilds finished blocks first_block .. first_block+n_blocks-1 of one sequence into plain
+ * element tensors k_out_dev, v_out_dev: [n_blocks*T][Hkv][D] (GAAC page §3.2 reconstruction,
+ * bit for bit).  Unallocated blocks come out as zeros and set KVC_STATUS_MISSING_BLOCK. */
+int kv_decode_blocks(kvc_cache* cache, int32_t seq, int32_t first_block, int32_t n_blocks, void* k_out_dev,
+                     void* v_out_dev, void* stream);
+
+/* Bytes of workspace kv_decode_attention needs for n_seqs sequences and n_splits splits:
+ * fp32 partial outputs [n_seqs][Hq][n_splits][D] and (max, sum) pairs [n_seqs][Hq][n_splits][2]. */
+size_t kv_attention_workspace_bytes(const kvc_params* params, int32_t n_seqs, int32_t n_splits);
+
+/* One decode-attention step (GAAC page §3.2) for each listed sequence:
+ *   out[s][hq][c] = sum_t softmax_t(scale * q[s][hq] . k_t) v_t[c]
+ * over every token of the sequence (finished blocks, compressed or raw, and the tail), with
+ * query head hq reading KV head hq / (Hq / Hkv).  q_dev: [n_seqs][Hq][D] BF16; out_dev:
+ * [n_seqs][Hq][D] BF16 (round-to-nearest-even of an fp32 result).  The context of each
+ * sequence is split into n_splits contiguous ranges of 64 tokens processed in parallel
+ * (1 <= n_splits <= 1024); their partial results are merged by log-sum-exp.  Every listed
+ * sequence must hold at least one token (KVC_EINVAL otherwise). */
+int kv_decode_attention(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
+                        float scale, int32_t n_splits, void* ws_dev, size_t ws_bytes, void* out_dev, void* stream);
+
+/* The two halves of kv_decode_attention, for callers that schedule or time them apart:
+ * kv_attention_partials runs the split kernel and leaves, for every (sequence, query head,
+ * split), the unnormalised partial output, the running maximum (base-2 units) and the sum of
+ * weights in the workspace; kv_attention_combine merges the splits of those n_seqs sequences
+ * (log-sum-exp) into out.  Same arguments and checks as kv_decode_attention. */
+int kv_attention_partials(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
+                          float scale, int32_t n_splits, void* ws_dev, size_t ws_bytes, void* stream);
+int kv_attention_combine(kvc_cache* cache, int32_t n_seqs, int32_t n_splits, const void* ws_dev, size_t ws_bytes,
+                         void* out_dev, void* stream);
+
+/* Returns every slot of a sequence to the free stacks and empties it (enqueued). */
+int kv_release_seq(kvc_cache* cache, int32_t seq, void* stream);
+
+/* Current token count of a sequence (host mirror; no GPU access). */
+int kv_seq_length(const kvc_cache* cache, int32_t seq, int32_t* length);
+
+/* Synchronises the stream, then reports the sticky status bits and statistics.  Either output
+ * pointer may be NULL. */
+int kv_get_status(kvc_cache* cache, uint32_t* flags, kvc_stats* stats, void* stream);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -78,7 +78,13 @@ def lib():
 
 
 def _threads(n):
-    return int(n) if n else (os.cpu_count() or 1)
+    """Thread count: explicit n, else OMP_NUM_THREADS, else min(cpu count, 16)."""
+    if n:
+        return int(n)
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    return min(os.cpu_count() or 1, 16)
 
 
 @dataclass(frozen=True)
