@@ -30,6 +30,8 @@ class KVCache:
                  device: str | torch.device = "cuda", perm_seed: int = 0):
         self.lib = L.load()
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.params = L.Params(dtype, num_kv_heads, num_q_heads, head_dim, block_tokens, group_tokens, esc_cap_bytes,
                                1 if compressed else 0, max_seqs, max_blocks_per_seq, num_comp_slots, num_raw_slots)
         sizes = (ctypes.c_size_t * L.NUM_BUFFERS)()
