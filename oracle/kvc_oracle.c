@@ -34,9 +34,12 @@
  *   SM          sign and mantissa, (1+MB)-bit field (s << MB) | m per element:
  *               BF16 one byte per element; E5M2 3-bit fields in the CODE unit layout;
  *               E4M3 4-bit fields, element n in bits 4n..4n+3 (LSB-first).
- *   ESC         for each group with mode >= 1 in increasing q: (w - 3) bit planes of G bits,
- *               plane p holding bit 3+p of every offset (bit tau = token tau).  Planes are
- *               consecutive in an LSB-first bit stream; unused bytes up to esc_cap are zero.
+ *   ESC         for each group with mode >= 1 in increasing q, in an LSB-first bit stream:
+ *               first one bit plane of G bits holding bit 3 of every offset (bit tau = token
+ *               tau); then, for a raw group, the remaining F-4 bits of each offset: for BF16
+ *               (F = 8) as one 4-bit field per element (offset bits 4..7 of token tau at
+ *               bits 4*tau .. 4*tau+3), for F = 5 as one more plane (bit 4).  A group thus
+ *               uses (w - 3) * G bits.  Unused bytes up to esc_cap are zero.
  *   sections    TAG | CODE | SM | ESC, each starting 16-byte aligned; slot stride = sum of
  *               the four 16-aligned section sizes (ESC counted at esc_cap).
  *   fallback    if the escape planes need more than esc_cap bytes, the tile is RAW: native
@@ -244,7 +247,12 @@ int orc_encode_tile(const orc_params* p, const uint16_t* x, const uint8_t* b3, c
       uint32_t o = f_exp(&L, v) - base;
       for (int b = 0; b < 3; ++b) put_bit(code, unit_bit(n, 3, b), (o & 7u) >> b);
       put_sm(&L, sm, n, (f_sign(&L, v) << L.MB) | f_man(&L, v));
-      for (int pl = 0; pl < w - 3; ++pl) put_bit(esc, (P + pl) * G + tau, o >> (3 + pl));
+      if (w > 3) put_bit(esc, P * G + tau, o >> 3);
+      if (w == 8) {
+        for (int b = 0; b < 4; ++b) put_bit(esc, (P + 1) * G + 4L * tau + b, o >> (4 + b));
+      } else if (w == 5) {
+        put_bit(esc, (P + 1) * G + tau, o >> 4);
+      }
     }
     P += w - 3;
   }
@@ -288,7 +296,12 @@ int orc_decode_tile(const orc_params* p, const uint8_t* in, int32_t is_raw, int3
       long n = (long)q * G + tau;
       uint32_t o = 0;
       for (int b = 0; b < 3; ++b) o |= get_bit(code, unit_bit(n, 3, b)) << b;
-      for (int pl = 0; pl < w - 3; ++pl) o |= get_bit(esc, (P + pl) * G + tau) << (3 + pl);
+      if (w > 3) o |= get_bit(esc, P * G + tau) << 3;
+      if (w == 8) {
+        for (int b = 0; b < 4; ++b) o |= get_bit(esc, (P + 1) * G + 4L * tau + b) << (4 + b);
+      } else if (w == 5) {
+        o |= get_bit(esc, (P + 1) * G + tau) << 4;
+      }
       uint32_t e = base + o;
       if (e >= (1u << L.F)) return ORC_ECORRUPT;
       uint32_t field = get_sm(&L, sm, n);
