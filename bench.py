@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=8, help="layer caches rotated through (cold-cache protocol)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep", type=str, default="", help="comma-separated split counts to time (extra)")
+    ap.add_argument("--probe", action="store_true", help="also time plain HBM copy / read kernels (torch)")
     return ap.parse_args()
 
 
@@ -192,6 +193,8 @@ def main():
     except Exception as ex:  # measurement only
         log(f"[bench] encode timing skipped: {ex}")
 
+    probe = hbm_probe(torch, stream) if args.probe else None
+
     attn_c = float(np.mean(c_attn))
     attn_r = float(np.mean(r_attn))
     bytes_c = comp_kv_bytes + q_bytes + table_bytes
@@ -233,10 +236,38 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "attn_comp_kernel<4>", "bytes_per_launch": bytes_c},
         "sweep_attention_us": sweep or None,
+        "hbm_probe": probe,
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, k0, v0)
     print(json.dumps(result), flush=True)
+
+
+def hbm_probe(torch, stream, nbytes=2 << 30, reps=10):
+    """Plain streaming kernels of known size on the same GPU: a device copy (reads and writes
+    nbytes) and a read-only reduction over nbytes.  Their rates bound what any HBM-bound kernel
+    can reach here, and the copy is the reference for scaling FETCH_SIZE/WRITE_SIZE counters."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                            ("read", lambda: src.sum(dtype=torch.float32), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a_ = torch.cuda.Event(enable_timing=True)
+            b_ = torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            fn()
+            b_.record(stream)
+            ts.append((a_, b_))
+        torch.cuda.synchronize()
+        us = float(np.median([a_.elapsed_time(b_) * 1e3 for a_, b_ in ts]))
+        out[name] = {"us": us, "bytes": moved, "GBps": round(moved / (us * 1e-6) / 1e9, 1)}
+    log(f"[bench] hbm probe: {out}")
+    del src, dst
+    return out
 
 
 def cpu_baseline(cfg, k0, v0):

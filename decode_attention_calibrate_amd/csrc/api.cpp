@@ -64,7 +64,8 @@ int check_params(const kvc_params* p) {
   // valid requests the kernels of this build do not implement
   if (p->dtype != KVC_BF16) return fail(KVC_EUNSUPPORTED, "FP8 caches are not implemented by these kernels");
   if (p->group_tokens != kvc::kGroup) return fail(KVC_EUNSUPPORTED, "these kernels implement 16-token groups");
-  if (p->block_tokens > 64) return fail(KVC_EUNSUPPORTED, "these kernels implement block_tokens <= 64");
+  if (p->block_tokens != 16 && p->block_tokens != 32 && p->block_tokens != 64)
+    return fail(KVC_EUNSUPPORTED, "these kernels implement block_tokens 16, 32 or 64");
   if (cap > 512) return fail(KVC_EUNSUPPORTED, "these kernels implement esc_cap_bytes <= 512");
   return KVC_OK;
 }

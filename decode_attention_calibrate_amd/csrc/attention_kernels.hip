@@ -10,17 +10,19 @@
 //   grid = (split, kv-head, sequence).  A split walks a contiguous range of 64-token
 //   super-blocks.  Lane l = n + 16j: j (0..3) selects the 16-token group t0+16j..t0+16j+15 of the
 //   super-block, n (0..15) a query head (QK output), a channel pair (rebuild, PV) or an MFMA row.
-//   QK   : v_mfma_f32_16x16x32_bf16 with A = K rows from LDS (16 tokens x 32 channels) and
-//          B = the g query heads (columns n < g used).  Row m of MFMA rb is token
-//          16(m/4) + 4rb + m%4, so lane n + 16j ends up holding the scores of head n for its own
-//          token group j.
+//   QK   : v_mfma_f32_16x16x32_bf16 with A = K rows (16 tokens x 32 channels) and B = the g query
+//          heads (columns n < g used).  Row m of MFMA rb is token 16(m/4) + 4rb + m%4, so lane
+//          n + 16j ends up holding the scores of head n for its own token group j.
 //   PV   : the same MFMA with A = P (rows = heads, k = 8 tokens of group j per lane) and B = V
 //          (k = the same 8 tokens, columns = 16 channels).  A group owner's rebuilt V values are
 //          already B operands, so V never touches LDS; P is split into a bf16 high part and a bf16
 //          low part (two MFMAs) so the probabilities keep ~16 mantissa bits.
 //   K    : group owners rebuild 16 tokens x 2 channels and write them to an XOR-swizzled LDS
 //          tile [64 tokens][D] (16-byte chunks, chunk ^ ((row & 3) | ((row >> 2) & 4))) that the
-//          QK A-operand reads conflict-free.
+//          QK A-operand reads without bank conflicts.
+//   Pipeline: the V bytes of super-block i load while its K is rebuilt and scored, and the K
+//          bytes of super-block i+1 load while its V is rebuilt and accumulated, so one half
+//          super-block of HBM reads is always in flight per wave.
 //   Softmax: online, fp32, base-2 (scores pre-multiplied by scale*log2(e)); per-split outputs
 //          (acc, max, sum) go to the workspace and combine_kernel merges them.
 #include <hip/hip_runtime.h>
@@ -53,6 +55,19 @@ struct AttnArgs {
   int n_splits;
 };
 
+// Compile-time geometry of a compressed tile (FORMAT v1) for head_dim 32*NR and T = TT tokens.
+template <int NR, int TT>
+struct TG {
+  static constexpr int D = 32 * NR;
+  static constexpr int NT = TT / 16;
+  static constexpr int NG = NT * D;
+  static constexpr int PW = NG / 32;
+  static constexpr int CODE_OFF = (2 * PW * 4 + 15) / 16 * 16;
+  static constexpr int SM_OFF = CODE_OFF + (TT * D * 3 / 8 + 15) / 16 * 16;
+  static constexpr int ESC_OFF = SM_OFF + (TT * D + 15) / 16 * 16;
+  static constexpr int RAW = TT * D;  // elements of a raw tile
+};
+
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
@@ -67,147 +82,177 @@ __device__ __forceinline__ uint32_t ld32(const void* p) { return *reinterpret_ca
 
 __device__ __forceinline__ int swz(int row) { return (row & 3) | ((row >> 2) & 4); }
 
+// Inclusive prefix sum over the 16 lanes of a DPP row.
+__device__ __forceinline__ uint32_t row_scan16(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  return v;
+}
+
 // Where the 16-token group starting at token t of one (sequence, K|V, head) lives.
-struct Src {
+struct TileRef {
   int kind;              // SRC_COMP, SRC_RAW (raw tile or tail), SRC_NONE
   int tg;                // token group inside the tile
   int valid;             // valid tokens in the group (0..16)
-  uint32_t esc_units;    // escape bytes / 16 (compressed)
-  const uint8_t* comp;   // compressed tile (never null: clamped to slot 0 when unused)
-  const uint16_t* raw;   // raw tile or tail tile
+  int escu;              // escape bytes / 16 (compressed)
+  const uint8_t* comp;   // compressed tile (clamped to slot 0 when unused: always dereferenceable)
+  const uint16_t* raw;   // raw tile or tail tile (always dereferenceable)
 };
 
-__device__ __forceinline__ Src resolve(const Geo& G, const DevBufs& B, int seq, int L, int t, int kv, int h,
-                                       uint32_t entry) {
-  Src s;
-  s.kind = SRC_NONE;
-  s.tg = 0;
-  s.valid = 0;
-  s.esc_units = 0;
-  s.comp = B.comp_pool;
-  s.raw = B.tail;
-  const int n_full = L / G.T;
-  if (t >= L) return s;
-  if (t < n_full * G.T) {
-    s.tg = (t % G.T) >> 4;
+template <int TT>
+__device__ __forceinline__ uint32_t load_entry(const AttnArgs& a, int seq, int L, int t, int kv, int h) {
+  const int n_full = L / TT;
+  if (t >= n_full * TT) return kUnallocated;
+  return a.B.table[table_index(a.G, seq, t / TT, kv, h)];
+}
+
+template <int NR, int TT>
+__device__ __forceinline__ TileRef tile_ref(const AttnArgs& a, int seq, int L, int t, int kv, int h, uint32_t entry,
+                                            uint32_t& flags) {
+  TileRef r;
+  r.kind = SRC_NONE;
+  r.tg = (t % TT) >> 4;
+  r.valid = 0;
+  r.escu = 0;
+  r.comp = a.B.comp_pool;
+  r.raw = a.B.tail;
+  const int n_full = L / TT;
+  if (t >= L) {
+    r.tg = 0;
+    return r;
+  }
+  if (t < n_full * TT) {
     if (entry == kUnallocated) {
-      atomicOr(&B.counters->status, 4u);
-      return s;
+      flags |= 4u;
+      return r;
     }
     const uint32_t slot = entry & 0x00FFFFFFu;
-    s.valid = 16;
+    r.valid = 16;
     if (entry & 0x80000000u) {
-      s.kind = SRC_RAW;
-      s.raw = B.raw_pool + (size_t)slot * G.raw_elems;
+      r.kind = SRC_RAW;
+      r.raw = a.B.raw_pool + (size_t)slot * TG<NR, TT>::RAW;
     } else {
-      s.kind = SRC_COMP;
-      s.comp = B.comp_pool + (size_t)slot * G.stride;
-      s.esc_units = (entry >> 24) & 0x7Fu;
+      r.kind = SRC_COMP;
+      r.comp = a.B.comp_pool + (size_t)slot * (uint32_t)a.G.stride;
+      r.escu = (int)((entry >> 24) & 0x7Fu);
     }
   } else {
-    s.kind = SRC_RAW;
-    s.tg = (t - n_full * G.T) >> 4;
-    s.valid = min(16, L - t);
-    s.raw = B.tail + tail_offset(G, seq, kv, h);
+    r.kind = SRC_RAW;
+    r.tg = (t - n_full * TT) >> 4;
+    r.valid = min(16, L - t);
+    r.raw = a.B.tail + tail_offset(a.G, seq, kv, h);
   }
-  return s;
+  return r;
 }
 
-__device__ __forceinline__ uint32_t load_entry(const Geo& G, const DevBufs& B, int seq, int L, int t, int kv, int h) {
-  const int n_full = L / G.T;
-  if (t >= L || t >= n_full * G.T) return kUnallocated;
-  return B.table[table_index(G, seq, t / G.T, kv, h)];
-}
-
-// Compressed-tile registers of one lane for one super-block: tag words, escape bytes,
-// sign/mantissa and code words of its NR group pairs.
+// Compressed bytes of one tile (K or V) held by one lane: tag words (lanes n < PW), escape
+// bytes (lanes n < escu, two 16-byte pieces), and sign/mantissa + code words of its NR pairs.
 template <int NR>
-struct CompRegs {
+struct CRegs {
   uint32_t tE, tR;
   uint4 esc0, esc1;
   uint4 sm[NR][2];
   uint32_t cd[NR][3];
 };
 
-template <int NR>
-__device__ __forceinline__ void load_comp(const Geo& G, const Src& s, int n, CompRegs<NR>& r) {
-  const uint8_t* t = s.comp;
-  r.tE = 0;
-  r.tR = 0;
-  if (n < G.PW) {
-    r.tE = ld32(t + G.tag_off + 4 * n);
-    r.tR = ld32(t + G.tag_off + 4 * (G.PW + n));
+template <int NR, int TT>
+__device__ __forceinline__ void load_tile(const TileRef& r, int n, CRegs<NR>& c) {
+  using Q = TG<NR, TT>;
+  const uint8_t* t = r.comp;
+  c.tE = c.tR = 0;
+  if (n < Q::PW) {
+    c.tE = ld32(t + 4 * n);
+    c.tR = ld32(t + 4 * (Q::PW + n));
   }
-  r.esc0 = make_uint4(0, 0, 0, 0);
-  r.esc1 = make_uint4(0, 0, 0, 0);
-  if (n < (int)s.esc_units) r.esc0 = ld128(t + G.esc_off + 16 * n);
-  if (n + 16 < (int)s.esc_units) r.esc1 = ld128(t + G.esc_off + 16 * (n + 16));
+  c.esc0 = c.esc1 = make_uint4(0, 0, 0, 0);
+  if (n < r.escu) c.esc0 = ld128(t + Q::ESC_OFF + 16 * n);
+  if (n + 16 < r.escu) c.esc1 = ld128(t + Q::ESC_OFF + 16 * (n + 16));
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    const int pr = s.tg * (G.D / 2) + 16 * i + n;
-    r.sm[i][0] = ld128(t + G.sm_off + 32 * pr);
-    r.sm[i][1] = ld128(t + G.sm_off + 32 * pr + 16);
-    const uint8_t* c = t + G.code_off + 12 * pr;
-    r.cd[i][0] = ld32(c);
-    r.cd[i][1] = ld32(c + 4);
-    r.cd[i][2] = ld32(c + 8);
+    const int pr = r.tg * (Q::D / 2) + 16 * i + n;
+    c.sm[i][0] = ld128(t + Q::SM_OFF + 32 * pr);
+    c.sm[i][1] = ld128(t + Q::SM_OFF + 32 * pr + 16);
+    const uint8_t* cp = t + Q::CODE_OFF + 12 * pr;
+    c.cd[i][0] = ld32(cp);
+    c.cd[i][1] = ld32(cp + 4);
+    c.cd[i][2] = ld32(cp + 8);
   }
 }
 
-// Stage the escape bytes of lane group j into LDS and compute the exclusive plane prefix of
-// each tag word (held by lane 16j + w).
+// Stage the escape bytes of this lane group's tile into its LDS area; return the exclusive
+// escape-plane prefix of tag word n (a wide group has 1 plane, a raw group 5).
 template <int NR>
-__device__ __forceinline__ uint32_t stage_escape(const CompRegs<NR>& r, const Src& s, int n, uint8_t* esc_lds) {
-  if (s.kind == SRC_COMP) {
-    if (n < (int)s.esc_units) *reinterpret_cast<uint4*>(esc_lds + 16 * n) = r.esc0;
-    if (n + 16 < (int)s.esc_units) *reinterpret_cast<uint4*>(esc_lds + 16 * (n + 16)) = r.esc1;
+__device__ __forceinline__ uint32_t stage_escape(const CRegs<NR>& c, const TileRef& r, int n, uint8_t* esc_lds) {
+  if (r.kind == SRC_COMP) {
+    if (n < r.escu) *reinterpret_cast<uint4*>(esc_lds + 16 * n) = c.esc0;
+    if (n + 16 < r.escu) *reinterpret_cast<uint4*>(esc_lds + 16 * (n + 16)) = c.esc1;
   }
-  const uint32_t cnt = __popc(r.tE) + 4u * __popc(r.tR);
-  uint32_t incl = cnt;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    const uint32_t v = __shfl_up(incl, o, 16);
-    if (n >= o) incl += v;
-  }
-  return incl - cnt;
+  const uint32_t cnt = __popc(c.tE) + 4u * __popc(c.tR);
+  return row_scan16(cnt) - cnt;
 }
 
-// Rebuild the pair of round i for lane n of lane group j.  bases: b3[c0], b3[c1], b4[c0], b4[c1].
+// Escape spread table: entry v holds bit 3 set in byte k for every set bit k of v (the
+// plane bits of four tokens moved to exponent bit 3 of their byte lanes).  Lives at LDS
+// offset 0 of every attention workgroup.
+__shared__ uint32_t esc_lut[16];
+
+__device__ __forceinline__ void init_esc_lut() {
+  if (threadIdx.x < 16) esc_lut[threadIdx.x] = spread4(threadIdx.x) << 3;
+}
+
+// Rebuild the two groups of round i for lane n of lane group j.  bases packs b3[c0], b3[c1],
+// b4[c0], b4[c1]; below = (1 << 2n) - 1.  Output o[gi][0][q] = BF16 of tokens (4q, 4q+2),
+// o[gi][1][q] = (4q+1, 4q+3), low half first.
 template <int NR>
-__device__ __forceinline__ void rebuild_pair(const Geo& G, const CompRegs<NR>& r, int i, int j, int tg, uint32_t pfx,
-                                             uint32_t bases, const uint16_t* esc16, int max_plane, uint32_t* status,
-                                             uint32_t outs[2][2][4]) {
-  const int w = tg * (G.D / 32) + i;            // tag word of this pair (same word for both groups)
-  const int bit = (2 * (16 * i + (threadIdx.x & 15))) & 31;
-  const uint32_t Ew = __shfl(r.tE, 16 * j + w);
-  const uint32_t Rw = __shfl(r.tR, 16 * j + w);
-  const uint32_t Pw = __shfl(pfx, 16 * j + w);
-  uint32_t P = planes_before(Ew, Rw, Pw, bit);
+__device__ __forceinline__ void rebuild_round(const CRegs<NR>& c, int i, int j, int n, int tg, uint32_t pfx,
+                                              uint32_t bases, const uint16_t* esc16, uint32_t below, uint32_t& bad,
+                                              uint32_t o[2][2][4]) {
+  const int w = tg * NR + i;  // tag word holding both groups of this pair
+  const uint32_t Ew = (uint32_t)__shfl((int)c.tE, 16 * j + w);
+  const uint32_t Rw = (uint32_t)__shfl((int)c.tR, 16 * j + w);
+  const uint32_t Pw = (uint32_t)__shfl((int)pfx, 16 * j + w);
+  bad |= Rw & ~Ew;
+  const uint32_t P0 = Pw + __popc(Ew & below) + 4u * __popc(Rw & below);
+  const uint32_t e2 = (Ew >> (2 * n)) & 3u, r2 = (Rw >> (2 * n)) & 3u;
+  const uint32_t W0 = c.cd[i][0], W1 = c.cd[i][1], W2 = c.cd[i][2];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
-    const uint32_t E = (Ew >> (bit + gi)) & 1u, R = (Rw >> (bit + gi)) & 1u;
-    if (R && !E) atomicOr(status, 8u);
+    const uint32_t E = (e2 >> gi) & 1u, R = (r2 >> gi) & 1u;
+    const uint32_t P = gi ? P0 + (e2 & 1u) + 4u * (r2 & 1u) : P0;
     const uint32_t b3 = (bases >> (8 * gi)) & 0xFFu, b4 = (bases >> (16 + 8 * gi)) & 0xFFu;
-    const uint32_t base = R ? 0u : (E ? b4 : b3);
-    const int p0 = min((int)P, max_plane);
-    const uint32_t plane0 = E ? (uint32_t)esc16[p0] : 0u;
-    uint32_t pl[4] = {0u, 0u, 0u, 0u};
-    int nextra = 0;
-    if (R) {
-      nextra = 4;
+    const uint32_t H = perm_b32(0u, R ? 0u : (E ? b4 : b3), 0x00000000u);  // base in all four bytes
+    const uint32_t plane0 = (uint32_t)esc16[P] & (0u - E);                  // read always, keep if escaped
+    const uint4 s4 = c.sm[i][gi];
+    const uint32_t smv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-      for (int p = 0; p < 4; ++p) pl[p] = esc16[min((int)P + 1 + p, max_plane)];
+    for (int q = 0; q < 4; ++q) {
+      uint32_t cs;
+      if (gi == 0) {
+        cs = q == 0 ? code_slot<0>(W0, W1, W2) : q == 1 ? code_slot<1>(W0, W1, W2)
+           : q == 2 ? code_slot<2>(W0, W1, W2) : code_slot<3>(W0, W1, W2);
+      } else {
+        cs = q == 0 ? code_slot<4>(W0, W1, W2) : q == 1 ? code_slot<5>(W0, W1, W2)
+           : q == 2 ? code_slot<6>(W0, W1, W2) : code_slot<7>(W0, W1, W2);
+      }
+      const uint32_t Ev = H + cs + esc_lut[(plane0 >> (4 * q)) & 0xFu];
+      o[gi][0][q] = bitsel(0x7F807F80u, Ev << 7, perm_b32(smv[q], smv[q], 0x02020000u));
+      o[gi][1][q] = bitsel(0x7F807F80u, Ev >> 1, perm_b32(smv[q], smv[q], 0x03030101u));
     }
-    const uint4 sv = r.sm[i][gi];
-    const uint32_t smv[4] = {sv.x, sv.y, sv.z, sv.w};
-    if (gi == 0) rebuild_group<0>(smv, r.cd[i][0], r.cd[i][1], r.cd[i][2], base, plane0, pl, nextra, outs[0][0], outs[0][1]);
-    else rebuild_group<1>(smv, r.cd[i][0], r.cd[i][1], r.cd[i][2], base, plane0, pl, nextra, outs[1][0], outs[1][1]);
-    P += E + 4u * R;
+    if (R) {  // raw group (rare): base 0, add offset bits 4..7 into the exponent field
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t X = raw_high_nibbles(esc16[P + 1 + q]);
+        o[gi][0][q] |= (X << 7) & 0x7F807F80u;
+        o[gi][1][q] |= (X >> 1) & 0x7F807F80u;
+      }
+    }
   }
 }
 
 // Online-softmax state update for one super-block.  s[16]: this lane's 16 scores (already in
-// base-2 units, masked to -inf); returns the probabilities in p and the rescale factor.
+// base-2 units, masked to -inf); they are replaced by probabilities; returns the rescale factor.
 __device__ __forceinline__ float softmax_update(float s[16], float& m, float& l) {
   float mx = s[0];
 #pragma unroll
@@ -216,11 +261,11 @@ __device__ __forceinline__ float softmax_update(float s[16], float& m, float& l)
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float m_new = fmaxf(m, mx);
   const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-  const float alpha = exp2f(m - m_use);
+  const float alpha = __builtin_amdgcn_exp2f(m - m_use);
   float sum = 0.0f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    s[k] = exp2f(s[k] - m_use);
+    s[k] = __builtin_amdgcn_exp2f(s[k] - m_use);
     sum += s[k];
   }
   l = l * alpha + sum;
@@ -271,7 +316,7 @@ __device__ __forceinline__ void write_partial(const AttnArgs& a, int si, int h, 
   for (int r = 0; r < 4; ++r) {
     const int head = 4 * j + r;
     if (head < G.g) {
-      float* dst = a.ws_acc + (((size_t)si * G.Hq + h * G.g + head) * S + split) * G.D;
+      float* dst = a.ws_acc + (((size_t)si * G.Hq + h * G.g + head) * S + split) * (32 * NR);
 #pragma unroll
       for (int i = 0; i < NR; ++i)
         *reinterpret_cast<float2*>(dst + 32 * i + 2 * n) = make_float2(acc[i][0][r], acc[i][1][r]);
@@ -284,58 +329,55 @@ __device__ __forceinline__ void write_partial(const AttnArgs& a, int si, int h, 
   }
 }
 
-// Natural-order raw V words for channel c and tokens tg*16 + 8e .. +8 (masked past valid).
-__device__ __forceinline__ uint4 raw_v_operand(const Geo& G, const Src& s, int c, int e) {
-  uint4 v = ld128(s.raw + (size_t)c * G.T + s.tg * 16 + 8 * e);
-  const int keep = s.valid - 8 * e;  // tokens of this 8-token half still valid
-  if (keep < 8) {
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// Zero the bf16 lanes of a natural-order 8-token V operand past `keep` valid tokens.
+__device__ __forceinline__ uint4 mask_tokens(uint4 v, int keep) {
+  if (keep >= 8) return v;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t m = (2 * k < keep ? 0x0000FFFFu : 0u) | (2 * k + 1 < keep ? 0xFFFF0000u : 0u);
-      w[k] &= m;
-    }
-    v = make_uint4(w[0], w[1], w[2], w[3]);
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t m = (2 * k < keep ? 0x0000FFFFu : 0u) | (2 * k + 1 < keep ? 0xFFFF0000u : 0u);
+    w[k] &= m;
   }
-  return v;
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
+
+// First token of lane group j's 16-token group in super-block sb.
+__device__ __forceinline__ int group_token(int sb, int j) { return sb * kSB + 16 * j; }
 
 // ------------------------------------------------------------------------------------------
 // Compressed cache.
-template <int NR>
-__global__ void __launch_bounds__(kWave) attn_comp_kernel(AttnArgs a) {
-  constexpr int D = 32 * NR;
+template <int NR, int TT>
+__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_comp_kernel(AttnArgs a) {
+  using Q = TG<NR, TT>;
+  constexpr int D = Q::D;
   extern __shared__ uint4 lds4[];
-  uint8_t* klds = reinterpret_cast<uint8_t*>(lds4);              // [64][D] bf16, swizzled
-  uint8_t* esc_base = klds + kSB * D * 2;                         // [4][esc_cap]
   const Geo& G = a.G;
-  const DevBufs& B = a.B;
+  const int esc_room = max(G.esc_cap, 16);
+  uint8_t* klds = reinterpret_cast<uint8_t*>(lds4);              // [64][D] bf16, swizzled
+  uint8_t* esc_base = klds + kSB * D * 2;                         // [4][esc_room]
+  uint4* qlds = reinterpret_cast<uint4*>(esc_base + 4 * esc_room);  // [g][D/8] query chunks
+  uint32_t* blds = reinterpret_cast<uint32_t*>(qlds + G.g * (D / 8));  // [2][NR][16] packed bases
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, si = blockIdx.z;
   const int seq = a.S.ids[si], L = a.S.lens[si];
   const int nsb = (L + kSB - 1) / kSB;
   const int per = (nsb + a.n_splits - 1) / a.n_splits;
   const int sb0 = split * per, sb1 = min(nsb, sb0 + per);
-  const int esc_room = max(G.esc_cap, 16);                        // LDS bytes per lane group
   uint8_t* esc_lds = esc_base + j * esc_room;
   const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(esc_lds);
-  const int max_plane = esc_room / 2 - 1;
+  const uint32_t below = (1u << (2 * n)) - 1u;
+  uint32_t flags = 0, bad = 0;
+  init_esc_lut();
 
-  // query heads h*g + n as B operands: channels 32ks + 8j .. +8
-  uint4 qb[NR];
-#pragma unroll
-  for (int ks = 0; ks < NR; ++ks)
-    qb[ks] = (n < G.g) ? ld128(a.q + ((size_t)si * G.Hq + h * G.g + n) * D + 32 * ks + 8 * j) : make_uint4(0, 0, 0, 0);
-  // calibrated bases of this lane's channel pairs (c0 = 32i + 2n), K and V
-  uint32_t kbase[NR], vbase[NR];
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int c0 = 32 * i + 2 * n;
-    const uint8_t* bk = B.bases + (size_t)h * D;
-    const uint8_t* bv = B.bases + ((size_t)2 * G.Hkv + h) * D;
-    const size_t wide = (size_t)G.Hkv * D;
-    kbase[i] = bk[c0] | (bk[c0 + 1] << 8) | (bk[wide + c0] << 16) | (bk[wide + c0 + 1] << 24);
-    vbase[i] = bv[c0] | (bv[c0 + 1] << 8) | (bv[wide + c0] << 16) | (bv[wide + c0 + 1] << 24);
+  // query heads h*g .. h*g+g-1 and the calibrated bases of every lane's channel pairs go to
+  // LDS once (keeps the per-lane register budget at two waves per SIMD)
+  for (int k = lane; k < G.g * (D / 8); k += kWave)
+    qlds[k] = ld128(a.q + ((size_t)si * G.Hq + h * G.g) * D + 8 * k);
+  for (int k = lane; k < 2 * NR * 16; k += kWave) {
+    const int kv = k / (NR * 16), i = (k / 16) % NR, nn = k % 16, c0 = 32 * i + 2 * nn;
+    const uint8_t* b3 = a.B.bases + ((size_t)(2 * kv) * G.Hkv + h) * D;
+    const uint8_t* b4 = b3 + (size_t)G.Hkv * D;
+    blds[k] = b3[c0] | (b3[c0 + 1] << 8) | (b4[c0] << 16) | (b4[c0 + 1] << 24);
   }
 
   float m = -INFINITY, l = 0.0f;
@@ -343,130 +385,177 @@ __global__ void __launch_bounds__(kWave) attn_comp_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < NR; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint32_t eK = 0, eV = 0;
   if (sb0 < sb1) {
-    eK = load_entry(G, B, seq, L, sb0 * kSB + 16 * j, 0, h);
-    eV = load_entry(G, B, seq, L, sb0 * kSB + 16 * j, 1, h);
-  }
-  for (int sb = sb0; sb < sb1; ++sb) {
-    const int t_j = sb * kSB + 16 * j;
-    const Src sK = resolve(G, B, seq, L, t_j, 0, h, eK);
-    const Src sV = resolve(G, B, seq, L, t_j, 1, h, eV);
-    CompRegs<NR> rK, rV;
-    load_comp<NR>(G, sK, n, rK);
-    load_comp<NR>(G, sV, n, rV);
-    if (sb + 1 < sb1) {
-      eK = load_entry(G, B, seq, L, t_j + kSB, 0, h);
-      eV = load_entry(G, B, seq, L, t_j + kSB, 1, h);
-    }
+    CRegs<NR> cK, cV;
+    TileRef rK, rV;
+    uint32_t eK = load_entry<TT>(a, seq, L, group_token(sb0, j), 0, h);
+    uint32_t eV = load_entry<TT>(a, seq, L, group_token(sb0, j), 1, h);
+    rK = tile_ref<NR, TT>(a, seq, L, group_token(sb0, j), 0, h, eK, flags);
+    load_tile<NR, TT>(rK, n, cK);
+    for (int sb = sb0; sb < sb1; ++sb) {
+      // V bytes of this super-block load while K is rebuilt and scored
+      rV = tile_ref<NR, TT>(a, seq, L, group_token(sb, j), 1, h, eV, flags);
+      load_tile<NR, TT>(rV, n, cV);
+      if (sb + 1 < sb1) {
+        eK = load_entry<TT>(a, seq, L, group_token(sb + 1, j), 0, h);
+        eV = load_entry<TT>(a, seq, L, group_token(sb + 1, j), 1, h);
+      }
 
-    // ---- K: rebuild into the LDS tile ----
-    __syncthreads();
-    const uint32_t pfxK = stage_escape<NR>(rK, sK, n, esc_lds);
-    __syncthreads();
-    if (sK.kind == SRC_COMP) {
+      // ---- K: rebuild into the LDS tile ----
+      __syncthreads();
+      const uint32_t pfxK = stage_escape<NR>(cK, rK, n, esc_lds);
+      __syncthreads();
+      if (rK.kind == SRC_COMP) {
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        uint32_t o[2][2][4];
-        rebuild_pair<NR>(G, rK, i, j, sK.tg, pfxK, kbase[i], esc16, max_plane, &B.counters->status, o);
-        const int chunk = 4 * i + (n >> 2), off = 4 * (n & 3);
+        for (int i = 0; i < NR; ++i) {
+          uint32_t o[2][2][4];
+          rebuild_round<NR>(cK, i, j, n, rK.tg, pfxK, blds[i * 16 + n], esc16, below, bad, o);
+          // transpose to token-major rows with 16-bit stores: row 16j + 4q + k, channels c0, c0+1
+          const int chunk = 4 * i + (n >> 2), off = 4 * (n & 3);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r0 = 16 * j + 4 * jj;
-          const uint32_t w0 = perm_b32(o[1][0][jj], o[0][0][jj], 0x05040100u);
-          const uint32_t w2 = perm_b32(o[1][0][jj], o[0][0][jj], 0x07060302u);
-          const uint32_t w1 = perm_b32(o[1][1][jj], o[0][1][jj], 0x05040100u);
-          const uint32_t w3 = perm_b32(o[1][1][jj], o[0][1][jj], 0x07060302u);
-          *reinterpret_cast<uint32_t*>(klds + (r0 + 0) * 2 * D + ((chunk ^ swz(r0 + 0)) << 4) + off) = w0;
-          *reinterpret_cast<uint32_t*>(klds + (r0 + 1) * 2 * D + ((chunk ^ swz(r0 + 1)) << 4) + off) = w1;
-          *reinterpret_cast<uint32_t*>(klds + (r0 + 2) * 2 * D + ((chunk ^ swz(r0 + 2)) << 4) + off) = w2;
-          *reinterpret_cast<uint32_t*>(klds + (r0 + 3) * 2 * D + ((chunk ^ swz(r0 + 3)) << 4) + off) = w3;
+          for (int k = 0; k < 4; ++k) {
+            const int rk = 16 * j + k;  // row of quad 0; quad q adds 4q rows (same swizzle)
+            uint8_t* p = klds + rk * 2 * D + ((chunk ^ swz(rk)) << 4) + off;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+              for (int gi = 0; gi < 2; ++gi) {
+                const uint32_t v = o[gi][k & 1][q];
+                *reinterpret_cast<uint16_t*>(p + q * 4 * 2 * D + 2 * gi) = (uint16_t)((k & 2) ? (v >> 16) : v);
+              }
+            }
+          }
+        }
+      } else if (rK.kind == SRC_RAW) {
+        for (int k = n; k < 16 * (D / 8); k += 16) {
+          const int rr = k / (D / 8), chunk = k % (D / 8), row = 16 * j + rr;
+          uint4 v = ld128(rK.raw + (size_t)(rK.tg * 16 + rr) * D + 8 * chunk);
+          if (rr >= rK.valid) v = make_uint4(0, 0, 0, 0);
+          *reinterpret_cast<uint4*>(klds + row * 2 * D + ((chunk ^ swz(row)) << 4)) = v;
         }
       }
-    } else if (sK.kind == SRC_RAW) {
-      // raw K tile / tail: token-major rows, copied 16 bytes at a time
-      for (int k = n; k < 16 * (D / 8); k += 16) {
-        const int rr = k / (D / 8), chunk = k % (D / 8), row = 16 * j + rr;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (rr < sK.valid) v = ld128(sK.raw + (size_t)(sK.tg * 16 + rr) * D + 8 * chunk);
-        *reinterpret_cast<uint4*>(klds + row * 2 * D + ((chunk ^ swz(row)) << 4)) = v;
-      }
-    }
-    __syncthreads();
+      __syncthreads();
 
-    // ---- QK ----
-    float s[16];
+      // ---- QK and softmax ----
+      const int valid = min(rK.valid, rV.valid);
+      f32x4_t cc[4];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-      const int row = 16 * (n >> 2) + 4 * rb + (n & 3);
+      for (int rb = 0; rb < 4; ++rb) cc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NR; ++ks) {
-        const uint4 av = *reinterpret_cast<const uint4*>(klds + row * 2 * D + (((4 * ks + j) ^ swz(row)) << 4));
-        c = mfma16(av, qb[ks], c);
-      }
+        uint4 qv = qlds[min(n, G.g - 1) * (D / 8) + 4 * ks + j];
+        if (n >= G.g) qv = make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[4 * rb + r] = (4 * rb + r < sK.valid && 4 * rb + r < sV.valid) ? c[r] * a.sl2 : -INFINITY;
-    }
-    const float alpha = softmax_update(s, m, l);
-    rescale_acc<NR>(acc, alpha, j);
-    uint4 phi[2], plo[2];
-    pack_p<true>(s, phi, plo);
-
-    // ---- V: rebuild straight into B operands ----
-    __syncthreads();
-    const uint32_t pfxV = stage_escape<NR>(rV, sV, n, esc_lds);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      uint4 bv[2][2];
-      if (sV.kind == SRC_COMP) {
-        uint32_t o[2][2][4];
-        rebuild_pair<NR>(G, rV, i, j, sV.tg, pfxV, vbase[i], esc16, max_plane, &B.counters->status, o);
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          bv[x][0] = make_uint4(o[x][0][0], o[x][1][0], o[x][0][1], o[x][1][1]);
-          bv[x][1] = make_uint4(o[x][0][2], o[x][1][2], o[x][0][3], o[x][1][3]);
+        for (int rb = 0; rb < 4; ++rb) {
+          const int row = 16 * (n >> 2) + 4 * rb + (n & 3);
+          const uint4 av = *reinterpret_cast<const uint4*>(klds + row * 2 * D + (((4 * ks + j) ^ swz(row)) << 4));
+          cc[rb] = mfma16(av, qv, cc[rb]);
         }
-      } else if (sV.kind == SRC_RAW) {
+      }
+      float s[16];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[4 * rb + r] = (4 * rb + r < valid) ? cc[rb][r] * a.sl2 : -INFINITY;
+      const float alpha = softmax_update(s, m, l);
+      rescale_acc<NR>(acc, alpha, j);
+      uint4 phi[2], plo[2];
+      pack_p<true>(s, phi, plo);
+
+      // K bytes of the next super-block load while V is rebuilt and accumulated
+      if (sb + 1 < sb1) {
+        rK = tile_ref<NR, TT>(a, seq, L, group_token(sb + 1, j), 0, h, eK, flags);
+        load_tile<NR, TT>(rK, n, cK);
+      }
+
+      // ---- V: rebuild straight into B operands ----
+      __syncthreads();
+      const uint32_t pfxV = stage_escape<NR>(cV, rV, n, esc_lds);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        uint4 bv[2][2];
+        if (rV.kind == SRC_COMP) {
+          uint32_t o[2][2][4];
+          rebuild_round<NR>(cV, i, j, n, rV.tg, pfxV, blds[(NR + i) * 16 + n], esc16, below, bad, o);
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            bv[x][0] = make_uint4(o[x][0][0], o[x][1][0], o[x][0][1], o[x][1][1]);
+            bv[x][1] = make_uint4(o[x][0][2], o[x][1][2], o[x][0][3], o[x][1][3]);
+          }
+        } else if (rV.kind == SRC_RAW) {
+#pragma unroll
+          for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int ch = 32 * i + 2 * n + x;
+              const uint4 v = mask_tokens(ld128(rV.raw + (size_t)ch * TT + rV.tg * 16 + 8 * e), rV.valid - 8 * e);
+              bv[x][e] = make_uint4(perm_b32(v.y, v.x, 0x05040100u), perm_b32(v.y, v.x, 0x07060302u),
+                                    perm_b32(v.w, v.z, 0x05040100u), perm_b32(v.w, v.z, 0x07060302u));
+            }
+        } else {
+#pragma unroll
+          for (int x = 0; x < 2; ++x) bv[x][0] = bv[x][1] = make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const uint4 v = raw_v_operand(G, sV, 32 * i + 2 * n + x, e);
-            bv[x][e] = make_uint4(perm_b32(v.y, v.x, 0x05040100u), perm_b32(v.y, v.x, 0x07060302u),
-                                  perm_b32(v.w, v.z, 0x05040100u), perm_b32(v.w, v.z, 0x07060302u));
+            acc[i][x] = mfma16(phi[e], bv[x][e], acc[i][x]);
+            acc[i][x] = mfma16(plo[e], bv[x][e], acc[i][x]);
           }
-      } else {
-#pragma unroll
-        for (int x = 0; x < 2; ++x) bv[x][0] = bv[x][1] = make_uint4(0, 0, 0, 0);
       }
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          acc[i][x] = mfma16(phi[e], bv[x][e], acc[i][x]);
-          acc[i][x] = mfma16(plo[e], bv[x][e], acc[i][x]);
-        }
     }
   }
+  if (bad) flags |= 8u;
+  if (flags) atomicOr(&a.B.counters->status, flags);
   write_partial<NR>(a, si, h, split, m, l, acc);
 }
 
 // ------------------------------------------------------------------------------------------
 // Uncompressed cache (every tile raw): the speedup baseline.  K rows are loaded straight into
-// QK A operands and V straight into PV B operands; no LDS.
+// QK A operands and V straight into PV B operands (no LDS), with the same K/V phase pipelining.
 template <int NR>
-__global__ void __launch_bounds__(kWave) attn_raw_kernel(AttnArgs a) {
+struct RawK {
+  uint4 ka[4][NR];
+};
+template <int NR>
+struct RawV {
+  uint4 vb[NR][2][2];
+};
+
+template <int NR, int TT>
+__device__ __forceinline__ void raw_load_k(const TileRef& r, int n, int j, RawK<NR>& k) {
+  constexpr int D = 32 * NR;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int rr = 4 * rb + (n & 3);
+#pragma unroll
+    for (int ks = 0; ks < NR; ++ks) k.ka[rb][ks] = ld128(r.raw + (size_t)(r.tg * 16 + rr) * D + 32 * ks + 8 * j);
+  }
+}
+
+template <int NR, int TT>
+__device__ __forceinline__ void raw_load_v(const TileRef& r, int n, RawV<NR>& v) {
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) v.vb[i][x][e] = ld128(r.raw + (size_t)(32 * i + 2 * n + x) * TT + r.tg * 16 + 8 * e);
+}
+
+template <int NR, int TT>
+__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_raw_kernel(AttnArgs a) {
   constexpr int D = 32 * NR;
   const Geo& G = a.G;
-  const DevBufs& B = a.B;
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, si = blockIdx.z;
   const int seq = a.S.ids[si], L = a.S.lens[si];
   const int nsb = (L + kSB - 1) / kSB;
   const int per = (nsb + a.n_splits - 1) / a.n_splits;
   const int sb0 = split * per, sb1 = min(nsb, sb0 + per);
+  uint32_t flags = 0;
 
   uint4 qb[NR];
 #pragma unroll
@@ -478,100 +567,137 @@ __global__ void __launch_bounds__(kWave) attn_raw_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < NR; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint32_t eK = 0, eV = 0;
   if (sb0 < sb1) {
-    eK = load_entry(G, B, seq, L, sb0 * kSB + 16 * j, 0, h);
-    eV = load_entry(G, B, seq, L, sb0 * kSB + 16 * j, 1, h);
+    RawK<NR> ck;
+    RawV<NR> cv;
+    const int jr = n >> 2;  // token group of this lane's QK A-operand rows
+    uint32_t eK = load_entry<TT>(a, seq, L, group_token(sb0, jr), 0, h);
+    uint32_t eV = load_entry<TT>(a, seq, L, group_token(sb0, j), 1, h);
+    TileRef rK = tile_ref<NR, TT>(a, seq, L, group_token(sb0, jr), 0, h, eK, flags);
+    raw_load_k<NR, TT>(rK, n, j, ck);
+    for (int sb = sb0; sb < sb1; ++sb) {
+      const TileRef rV = tile_ref<NR, TT>(a, seq, L, group_token(sb, j), 1, h, eV, flags);
+      raw_load_v<NR, TT>(rV, n, cv);
+      if (sb + 1 < sb1) {
+        eK = load_entry<TT>(a, seq, L, group_token(sb + 1, jr), 0, h);
+        eV = load_entry<TT>(a, seq, L, group_token(sb + 1, j), 1, h);
+      }
+      // scores of this lane belong to token group j: its K validity comes from lane 4j
+      const int validKj = __shfl(rK.valid, 4 * j);
+      const int valid = min(validKj, rV.valid);
+      float s[16];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
+        const bool rowok = 4 * rb + (n & 3) < rK.valid;
+#pragma unroll
+        for (int ks = 0; ks < NR; ++ks) cc = mfma16(rowok ? ck.ka[rb][ks] : make_uint4(0, 0, 0, 0), qb[ks], cc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[4 * rb + r] = (4 * rb + r < valid) ? cc[r] * a.sl2 : -INFINITY;
+      }
+      const float alpha = softmax_update(s, m, l);
+      rescale_acc<NR>(acc, alpha, j);
+      uint4 phi[2], plo[2];
+      pack_p<false>(s, phi, plo);
+      if (sb + 1 < sb1) {
+        rK = tile_ref<NR, TT>(a, seq, L, group_token(sb + 1, jr), 0, h, eK, flags);
+        raw_load_k<NR, TT>(rK, n, j, ck);
+      }
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint4 v = mask_tokens(cv.vb[i][x][e], rV.valid - 8 * e);
+            acc[i][x] = mfma16(phi[e], v, acc[i][x]);
+            acc[i][x] = mfma16(plo[e], v, acc[i][x]);
+          }
+    }
   }
-  for (int sb = sb0; sb < sb1; ++sb) {
-    const int t_j = sb * kSB + 16 * j;
-    const Src sK = resolve(G, B, seq, L, t_j, 0, h, eK);
-    const Src sV = resolve(G, B, seq, L, t_j, 1, h, eV);
-    // K source of the token group this lane's MFMA rows come from (group n / 4)
-    const int jr = n >> 2;
-    const int kindR = __shfl(sK.kind, 16 * jr), tgR = __shfl(sK.tg, 16 * jr), validR = __shfl(sK.valid, 16 * jr);
-    const uint16_t* rawR = reinterpret_cast<const uint16_t*>(
-        __shfl((unsigned long long)reinterpret_cast<uintptr_t>(sK.raw), 16 * jr));
-    uint4 ka[4][NR];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int rr = 4 * rb + (n & 3);
-#pragma unroll
-      for (int ks = 0; ks < NR; ++ks)
-        ka[rb][ks] = (kindR == SRC_RAW && rr < validR) ? ld128(rawR + (size_t)(tgR * 16 + rr) * D + 32 * ks + 8 * j)
-                                                        : make_uint4(0, 0, 0, 0);
-    }
-    uint4 vb[NR][2][2];
-#pragma unroll
-    for (int i = 0; i < NR; ++i)
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          vb[i][x][e] = (sV.kind == SRC_RAW) ? raw_v_operand(G, sV, 32 * i + 2 * n + x, e) : make_uint4(0, 0, 0, 0);
-    if (sb + 1 < sb1) {
-      eK = load_entry(G, B, seq, L, t_j + kSB, 0, h);
-      eV = load_entry(G, B, seq, L, t_j + kSB, 1, h);
-    }
-
-    float s[16];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NR; ++ks) c = mfma16(ka[rb][ks], qb[ks], c);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[4 * rb + r] = (4 * rb + r < sK.valid && 4 * rb + r < sV.valid) ? c[r] * a.sl2 : -INFINITY;
-    }
-    const float alpha = softmax_update(s, m, l);
-    rescale_acc<NR>(acc, alpha, j);
-    uint4 phi[2], plo[2];
-    pack_p<false>(s, phi, plo);
-#pragma unroll
-    for (int i = 0; i < NR; ++i)
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          acc[i][x] = mfma16(phi[e], vb[i][x][e], acc[i][x]);
-          acc[i][x] = mfma16(plo[e], vb[i][x][e], acc[i][x]);
-        }
-  }
+  if (flags) atomicOr(&a.B.counters->status, flags);
   write_partial<NR>(a, si, h, split, m, l, acc);
 }
 
-// Log-sum-exp merge of the splits: one block per (query head, sequence), one thread per channel.
-__global__ void combine_kernel(int Hq, int D, int S, const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
-                               uint16_t* __restrict__ out) {
-  const int hq = blockIdx.x, si = blockIdx.y, c = threadIdx.x;
-  if (c >= D) return;
+// Log-sum-exp merge of the splits: one 256-thread block per (query head, sequence).  The split
+// weights are computed once into LDS; each thread then sums one channel over a subset of the
+// splits with independent loads, and the subsets are added in LDS.
+constexpr int kCombineThreads = 256;
+
+__global__ void __launch_bounds__(kCombineThreads) combine_kernel(int Hq, int D, int S,
+                                                                  const float* __restrict__ ws_acc,
+                                                                  const float* __restrict__ ws_ml,
+                                                                  uint16_t* __restrict__ out) {
+  __shared__ float w[1024];
+  __shared__ float red[kCombineThreads];
+  __shared__ float sh_M, sh_den;
+  const int hq = blockIdx.x, si = blockIdx.y, tid = threadIdx.x;
   const float* ml = ws_ml + ((size_t)si * Hq + hq) * S * 2;
   const float* acc = ws_acc + ((size_t)si * Hq + hq) * S * D;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s)
-    if (ml[2 * s + 1] > 0.0f) M = fmaxf(M, ml[2 * s]);
-  float num = 0.0f, den = 0.0f;
-  for (int s = 0; s < S; ++s) {
-    const float ls = ml[2 * s + 1];
-    if (ls > 0.0f) {
-      const float w = exp2f(ml[2 * s] - M);
-      num += w * acc[(size_t)s * D + c];
-      den += w * ls;
-    }
+  float mx = -INFINITY;
+  for (int s = tid; s < S; s += kCombineThreads) {
+    const float2 v = *reinterpret_cast<const float2*>(ml + 2 * s);
+    if (v.y > 0.0f) mx = fmaxf(mx, v.x);
   }
-  out[((size_t)si * Hq + hq) * D + c] = f32_to_bf16_rne(num / den);
+  red[tid] = mx;
+  __syncthreads();
+  for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  if (tid == 0) sh_M = red[0];
+  __syncthreads();
+  const float M = sh_M;
+  float den = 0.0f;
+  for (int s = tid; s < S; s += kCombineThreads) {
+    const float2 v = *reinterpret_cast<const float2*>(ml + 2 * s);
+    const float ws = v.y > 0.0f ? exp2f(v.x - M) : 0.0f;
+    w[s] = ws;
+    den += ws * v.y;
+  }
+  red[tid] = den;
+  __syncthreads();
+  for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) sh_den = red[0];
+  __syncthreads();
+  const int parts = kCombineThreads / D, c = tid % D, part = tid / D;
+  float num = 0.0f;
+#pragma unroll 8
+  for (int s = part; s < S; s += parts) num += w[s] * acc[(size_t)s * D + c];
+  __syncthreads();
+  red[tid] = num;
+  __syncthreads();
+  if (part == 0) {
+    float t = 0.0f;
+    for (int p = 0; p < parts; ++p) t += red[p * D + c];
+    out[((size_t)si * Hq + hq) * D + c] = f32_to_bf16_rne(t / sh_den);
+  }
+}
+
+template <int NR, int TT>
+int launch_attn(const AttnArgs& a, int n_seqs, void* stream) {
+  const dim3 grid(a.n_splits, a.G.Hkv, n_seqs);
+  if (a.G.compressed) {
+    const size_t lds = (size_t)kSB * (32 * NR) * 2 + (size_t)4 * max(a.G.esc_cap, 16) +
+                       (size_t)a.G.g * (32 * NR) * 2 + (size_t)2 * NR * 16 * 4;
+    hipLaunchKernelGGL((attn_comp_kernel<NR, TT>), grid, dim3(kWave), lds, (hipStream_t)stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_raw_kernel<NR, TT>), grid, dim3(kWave), 0, (hipStream_t)stream, a);
+  }
+  return (int)hipGetLastError();
 }
 
 template <int NR>
-int launch_attn_nr(const AttnArgs& a, int n_seqs, void* stream) {
-  const dim3 grid(a.n_splits, a.G.Hkv, n_seqs);
-  if (a.G.compressed) {
-    const size_t lds = (size_t)kSB * (32 * NR) * 2 + (size_t)4 * max(a.G.esc_cap, 16);
-    hipLaunchKernelGGL(attn_comp_kernel<NR>, grid, dim3(kWave), lds, (hipStream_t)stream, a);
-  } else {
-    hipLaunchKernelGGL(attn_raw_kernel<NR>, grid, dim3(kWave), 0, (hipStream_t)stream, a);
+int launch_attn_t(const AttnArgs& a, int n_seqs, void* stream) {
+  switch (a.G.T) {
+    case 16: return launch_attn<NR, 16>(a, n_seqs, stream);
+    case 32: return launch_attn<NR, 32>(a, n_seqs, stream);
+    case 64: return launch_attn<NR, 64>(a, n_seqs, stream);
+    default: return (int)hipErrorInvalidValue;
   }
-  return (int)hipGetLastError();
 }
 
 }  // namespace
@@ -587,13 +713,13 @@ int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& S, 
   a.ws_ml = ws_ml;
   a.sl2 = scale * 1.4426950408889634f;
   a.n_splits = n_splits;
-  return (G.D == 128) ? launch_attn_nr<4>(a, S.n, stream) : launch_attn_nr<2>(a, S.n, stream);
+  return (G.D == 128) ? launch_attn_t<4>(a, S.n, stream) : launch_attn_t<2>(a, S.n, stream);
 }
 
 int launch_combine(const Geo& G, int n_seqs, int n_splits, const float* ws_acc, const float* ws_ml, uint16_t* out,
                    void* stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(G.Hq, n_seqs), dim3(G.D), 0, (hipStream_t)stream, G.Hq, G.D, n_splits,
-                     ws_acc, ws_ml, out);
+  hipLaunchKernelGGL(combine_kernel, dim3(G.Hq, n_seqs), dim3(kCombineThreads), 0, (hipStream_t)stream, G.Hq, G.D,
+                     n_splits, ws_acc, ws_ml, out);
   return (int)hipGetLastError();
 }
 

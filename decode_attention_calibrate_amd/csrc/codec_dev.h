@@ -35,37 +35,48 @@ __device__ __forceinline__ uint32_t code_slot(uint32_t W0, uint32_t W1, uint32_t
   }
 }
 
+// 24-bit multiply (v_mul_u32_u24, full rate).  Written as asm so that the compiler cannot fold a
+// following shift into the constant and fall back to the quarter-rate 32-bit multiply.
+__device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_mul_u32_u24 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Four bits -> bit 0 of four bytes.
-__device__ __forceinline__ uint32_t spread4(uint32_t nib) { return __umul24(nib, 0x00204081u) & 0x01010101u; }
+__device__ __forceinline__ uint32_t spread4(uint32_t nib) { return mul_u24(nib, 0x00204081u) & 0x01010101u; }
+
+// Offset bits 4..7 of tokens 4q..4q+3 of a raw group, one per byte lane (bits 4..7 of each
+// byte), from the 16-bit escape unit holding their four 4-bit fields (token 4q in the low nibble).
+__device__ __forceinline__ uint32_t raw_high_nibbles(uint32_t u16) {
+  const uint32_t y = perm_b32(u16, u16, 0x01010000u);
+  return ((y << 4) & 0x00F000F0u) | (y & 0xF000F000u);
+}
 
 // Rebuild the 16 BF16 values of group GI (0 or 1) of a pair.
-//   sm[4]   : the group's sign/mantissa bytes, word j = tokens 4j..4j+3
+//   sm[4]   : the group's sign/mantissa bytes, word q = tokens 4q..4q+3
 //   W0..W2  : the pair's CODE unit
 //   base    : exponent base of the group's mode (b3, b4 or 0)
-//   plane0  : first escape plane (0 for narrow groups); pl[0..3] further planes of a raw group
-//   nextra  : number of further planes (0, or 4 for a BF16 raw group)
-// Output word j: o02 = BF16 of tokens (4j, 4j+2), o13 = tokens (4j+1, 4j+3), low half first.
+//   plane0  : escape plane of offset bit 3 (0 for narrow groups)
+//   X[4]    : offset bits 4..7 per byte lane (raw groups), else 0
+// Output word q: o02 = BF16 of tokens (4q, 4q+2), o13 = tokens (4q+1, 4q+3), low half first.
 template <int GI>
 __device__ __forceinline__ void rebuild_group(const uint32_t sm[4], uint32_t W0, uint32_t W1, uint32_t W2,
-                                              uint32_t base, uint32_t plane0, const uint32_t pl[4], int nextra,
+                                              uint32_t base, uint32_t plane0, const uint32_t X[4],
                                               uint32_t o02[4], uint32_t o13[4]) {
-  const uint32_t H = base * 0x01010101u;
+  const uint32_t H = perm_b32(base, base, 0u);  // base in all four bytes
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int q = 0; q < 4; ++q) {
     uint32_t cs;
-    if (j == 0) cs = code_slot<4 * GI + 0>(W0, W1, W2);
-    else if (j == 1) cs = code_slot<4 * GI + 1>(W0, W1, W2);
-    else if (j == 2) cs = code_slot<4 * GI + 2>(W0, W1, W2);
+    if (q == 0) cs = code_slot<4 * GI + 0>(W0, W1, W2);
+    else if (q == 1) cs = code_slot<4 * GI + 1>(W0, W1, W2);
+    else if (q == 2) cs = code_slot<4 * GI + 2>(W0, W1, W2);
     else cs = code_slot<4 * GI + 3>(W0, W1, W2);
-    uint32_t esc = spread4((plane0 >> (4 * j)) & 0xFu) << 3;
-    if (nextra) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) esc |= spread4((pl[p] >> (4 * j)) & 0xFu) << (4 + p);
-    }
-    const uint32_t E = H + cs + esc;
-    const uint32_t s = sm[j];
-    o02[j] = bitsel(0x7F807F80u, E << 7, perm_b32(s, s, 0x02020000u));
-    o13[j] = bitsel(0x7F807F80u, E >> 1, perm_b32(s, s, 0x03030101u));
+    const uint32_t esc = spread4((plane0 >> (4 * q)) & 0xFu);
+    const uint32_t E = H + cs + (esc << 3) + X[q];
+    const uint32_t s = sm[q];
+    o02[q] = bitsel(0x7F807F80u, E << 7, perm_b32(s, s, 0x02020000u));
+    o13[q] = bitsel(0x7F807F80u, E >> 1, perm_b32(s, s, 0x03030101u));
   }
 }
 

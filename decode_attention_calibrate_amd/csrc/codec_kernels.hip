@@ -271,7 +271,9 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
     for (int gi = 0; gi < 2; ++gi) {
       const int q = 2 * pr + gi, tg = q / D, c = q % D;
       const int np = mode_planes(PI.mode[gi]);
-      uint32_t planes[5] = {0u, 0u, 0u, 0u, 0u};
+      // escape units: [0] = plane of offset bit 3; raw groups add [1..4] = 4-bit fields of
+      // offset bits 4..7, token tau at bits 4*tau.. of the 64-bit little-endian run
+      uint32_t units[5] = {0u, 0u, 0u, 0u, 0u};
       for (int tau = 0; tau < kGroup; ++tau) {
         const uint32_t x = tile[(tg * kGroup + tau) * D + c];
         const uint32_t o = ((x >> 7) & 0xFF) - PI.base[gi];
@@ -282,10 +284,11 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
           W[xs >> 3] |= ((code >> bb) & 1u) << (8 * lk + (xs & 7));
         }
         smw[r >> 2] |= (((x >> 8) & 0x80u) | (x & 0x7Fu)) << (8 * (r & 3));
-        for (int p = 0; p < np; ++p) planes[p] |= ((o >> (3 + p)) & 1u) << tau;
+        units[0] |= ((o >> 3) & 1u) << tau;
+        units[1 + (tau >> 2)] |= ((o >> 4) & 0xFu) << (4 * (tau & 3));
       }
       uint16_t* esc16 = reinterpret_cast<uint16_t*>(dst + G.esc_off);
-      for (int p = 0; p < np; ++p) esc16[P + p] = (uint16_t)planes[p];
+      for (int p = 0; p < np; ++p) esc16[P + p] = (uint16_t)units[p];
       P += np;
       if (PI.mode[gi] >= 1) atomicOr(&tagw[q >> 5], 1u << (q & 31));
       if (PI.mode[gi] == 2) atomicOr(&tagw[G.PW + (q >> 5)], 1u << (q & 31));
@@ -399,16 +402,14 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
       const int mode = (int)(E + R);
       const int c = c0 + gi;
       const uint32_t base = mode == 0 ? b3[c] : (mode == 1 ? b4[c] : 0u);
-      uint32_t plane0 = 0, pl[4] = {0u, 0u, 0u, 0u};
-      int nextra = 0;
+      uint32_t plane0 = 0, X[4] = {0u, 0u, 0u, 0u};
       if (E && (int)P < max_plane) plane0 = esc16[P];
       if (R) {
-        nextra = 4;
-        for (int p = 0; p < 4; ++p) pl[p] = ((int)P + 1 + p < max_plane) ? esc16[P + 1 + p] : 0u;
+        for (int qq = 0; qq < 4; ++qq) X[qq] = ((int)P + 1 + qq < max_plane) ? raw_high_nibbles(esc16[P + 1 + qq]) : 0u;
       }
       const uint32_t smv[4] = {gi ? s1.x : s0.x, gi ? s1.y : s0.y, gi ? s1.z : s0.z, gi ? s1.w : s0.w};
-      if (gi == 0) rebuild_group<0>(smv, W0, W1, W2, base, plane0, pl, nextra, outs[0][0], outs[0][1]);
-      else rebuild_group<1>(smv, W0, W1, W2, base, plane0, pl, nextra, outs[1][0], outs[1][1]);
+      if (gi == 0) rebuild_group<0>(smv, W0, W1, W2, base, plane0, X, outs[0][0], outs[0][1]);
+      else rebuild_group<1>(smv, W0, W1, W2, base, plane0, X, outs[1][0], outs[1][1]);
       P += E + 4u * R;
     }
     for (int j = 0; j < 4; ++j) {

@@ -70,6 +70,7 @@ def test_slot_stride_matches_format(K, T, D):
     (dict(block_tokens=40), -1), (dict(esc_cap_bytes=24), -1), (dict(max_seqs=0), -1),
     (dict(num_comp_slots=0), -1), (dict(compressed=0, num_raw_slots=0), -1), (dict(dtype=7), -1),
     (dict(dtype=1), -3), (dict(dtype=2), -3), (dict(group_tokens=8), -3), (dict(block_tokens=128), -3),
+    (dict(block_tokens=48), -3),
 ])
 def test_parameter_validation(K, kw, code):
     rc, _, _, msg = _sizes(K, _params(K, **kw))
