@@ -16,7 +16,7 @@
  *     in a fixed-capacity escape area, and block-table entries.
  *   - App. B: the same codec applies to FP8 E5M2 / E4M3 caches.
  * The pages print no byte layout.  The layout below ("FORMAT v1") is this library's reading;
- * every choice is listed in the design doc.  The oracle writes each field bit by bit at the
+ * every choice is stated below.  The oracle writes each field bit by bit at the
  * position the format defines, with no blocking or fusion, so it can be checked by eye.
  *
  * FORMAT v1 for one tile = T tokens x D channels of one (K|V, kv-head), element = F exponent
