@@ -145,21 +145,23 @@ def main():
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
         t0.record(stream)
         ev = run(caches, args.steps, True, start=start + args.warmup)
         t1.record(stream)
+        host_us = (time.perf_counter() - h0) * 1e6 / args.steps  # enqueue time per step
         torch.cuda.synchronize()
         total_ms = t0.elapsed_time(t1)
         step_us = np.array([a.elapsed_time(d) * 1e3 for a, b, c, d in ev])
         attn_us = np.array([b.elapsed_time(c) * 1e3 for a, b, c, d in ev])
         app_us = np.array([a.elapsed_time(b) * 1e3 for a, b, c, d in ev])
         comb_us = np.array([c.elapsed_time(d) * 1e3 for a, b, c, d in ev])
-        return total_ms, step_us, attn_us, app_us, comb_us
+        return total_ms, step_us, attn_us, app_us, comb_us, host_us
 
     log(f"[bench] timing {args.steps} compressed steps (S={S})")
-    c_total, c_step, c_attn, c_app, c_comb = timed(comp, 0)
+    c_total, c_step, c_attn, c_app, c_comb, c_host = timed(comp, 0)
     log(f"[bench] timing {args.steps} uncompressed steps")
-    r_total, r_step, r_attn, r_app, r_comb = timed(raw, 0)
+    r_total, r_step, r_attn, r_app, r_comb, r_host = timed(raw, 0)
 
     sweep = {}
     for s_ in [int(x) for x in args.sweep.split(",") if x]:
@@ -233,6 +235,7 @@ def main():
         "append_us": {"compressed_median": float(np.median(c_app)), "uncompressed_median": float(np.median(r_app)),
                       "block_encode_append": enc_us},
         "combine_us": float(np.median(c_comb)),
+        "host_enqueue_us_per_step": {"compressed": round(c_host, 2), "uncompressed": round(r_host, 2)},
         "uncompressed_step_us": round(r_total * 1e3 / args.steps, 3),
         "speedup_step": round(r_total / c_total, 4),
         "speedup_attention": round(attn_r / attn_c, 4),

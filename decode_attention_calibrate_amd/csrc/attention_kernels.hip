@@ -341,6 +341,18 @@ __device__ __forceinline__ uint4 mask_tokens(uint4 v, int keep) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Super-blocks [sb0, sb1) of split `split`: the full 64-token super-blocks are dealt out as
+// evenly as possible (the first nfull % n_splits splits take one more), and the last split also
+// takes the partial last super-block, if any.  Its share of full ones is never above the others',
+// so a length just past a multiple of 64 * n_splits puts one extra super-block on a few splits
+// instead of on all of them.
+__device__ __forceinline__ void split_range(int L, int n_splits, int split, int& sb0, int& sb1) {
+  const int nfull = L / kSB, base = nfull / n_splits, rem = nfull % n_splits;
+  sb0 = split * base + min(split, rem);
+  sb1 = sb0 + base + (split < rem ? 1 : 0);
+  if (split == n_splits - 1 && (L % kSB)) sb1 += 1;
+}
+
 // First token of lane group j's 16-token group in super-block sb.
 __device__ __forceinline__ int group_token(int sb, int j) { return sb * kSB + 16 * j; }
 
@@ -360,9 +372,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, si = blockIdx.z;
   const int seq = a.S.ids[si], L = a.S.lens[si];
-  const int nsb = (L + kSB - 1) / kSB;
-  const int per = (nsb + a.n_splits - 1) / a.n_splits;
-  const int sb0 = split * per, sb1 = min(nsb, sb0 + per);
+  int sb0, sb1;
+  split_range(L, a.n_splits, split, sb0, sb1);
   uint8_t* esc_lds = esc_base + j * esc_room;
   const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(esc_lds);
   const uint32_t below = (1u << (2 * n)) - 1u;
@@ -410,7 +421,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
         for (int i = 0; i < NR; ++i) {
           uint32_t o[2][2][4];
           rebuild_round<NR>(cK, i, j, n, rK.tg, pfxK, blds[i * 16 + n], esc16, below, bad, o);
-          // transpose to token-major rows with 16-bit stores: row 16j + 4q + k, channels c0, c0+1
+          // transpose to token-major rows: token 16j + 4q + k gets the (c0, c0+1) word, taken
+          // from the low (k < 2) or high (k >= 2) halves of the two channels' token-pair words
           const int chunk = 4 * i + (n >> 2), off = 4 * (n & 3);
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -418,21 +430,39 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
             uint8_t* p = klds + rk * 2 * D + ((chunk ^ swz(rk)) << 4) + off;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-#pragma unroll
-              for (int gi = 0; gi < 2; ++gi) {
-                const uint32_t v = o[gi][k & 1][q];
-                *reinterpret_cast<uint16_t*>(p + q * 4 * 2 * D + 2 * gi) = (uint16_t)((k & 2) ? (v >> 16) : v);
-              }
+              const uint32_t w = perm_b32(o[1][k & 1][q], o[0][k & 1][q], (k & 2) ? 0x07060302u : 0x05040100u);
+              *reinterpret_cast<uint32_t*>(p + q * 4 * 2 * D) = w;
             }
           }
         }
-      } else if (rK.kind == SRC_RAW) {
-        for (int k = n; k < 16 * (D / 8); k += 16) {
-          const int rr = k / (D / 8), chunk = k % (D / 8), row = 16 * j + rr;
-          uint4 v = ld128(rK.raw + (size_t)(rK.tg * 16 + rr) * D + 8 * chunk);
-          if (rr >= rK.valid) v = make_uint4(0, 0, 0, 0);
-          *reinterpret_cast<uint4*>(klds + row * 2 * D + ((chunk ^ swz(row)) << 4)) = v;
+      }
+      // Raw K groups (raw tiles, the tail) go straight from memory into their LDS rows with
+      // LDS-DMA loads: one instruction fills RPI whole rows (64 lanes x 16 bytes), each lane
+      // fetching the row piece whose swizzled position is its own, so a group costs one memory
+      // round trip and no registers.  Rows past the valid tokens hold stale but finite-or-not
+      // data; their scores are masked before the softmax.
+      {
+        constexpr int RPI = 512 / D;  // rows per instruction
+        constexpr int LPR = D / 8;    // lanes (16-byte pieces) per row
+        bool dma = false;
+#pragma unroll 1
+        for (int g = 0; g < 4; ++g) {
+          if (__builtin_amdgcn_readlane(rK.kind, 16 * g) != SRC_RAW) continue;
+          const uint64_t rp = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)((uintptr_t)rK.raw >> 32), 16 * g) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)(uintptr_t)rK.raw, 16 * g);
+          const int tg_g = __builtin_amdgcn_readlane(rK.tg, 16 * g);
+          const uint16_t* raw_g = reinterpret_cast<const uint16_t*>(rp) + (size_t)tg_g * 16 * D;
+#pragma unroll 1
+          for (int i = 0; i < 16 / RPI; ++i) {
+            const int row = 16 * g + RPI * i + lane / LPR, pos = lane % LPR;
+            const int chunk = pos ^ swz(row);
+            __builtin_amdgcn_global_load_lds(raw_g + (size_t)(row - 16 * g) * D + 8 * chunk,
+                                             (__attribute__((address_space(3))) void*)(klds + (16 * g + RPI * i) * 2 * D),
+                                             16, 0, 0);
+          }
+          dma = true;
         }
+        if (dma) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the DMA has landed in LDS
       }
       __syncthreads();
 
@@ -552,9 +582,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, si = blockIdx.z;
   const int seq = a.S.ids[si], L = a.S.lens[si];
-  const int nsb = (L + kSB - 1) / kSB;
-  const int per = (nsb + a.n_splits - 1) / a.n_splits;
-  const int sb0 = split * per, sb1 = min(nsb, sb0 + per);
+  int sb0, sb1;
+  split_range(L, a.n_splits, split, sb0, sb1);
   uint32_t flags = 0;
 
   uint4 qb[NR];
@@ -619,35 +648,44 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   write_partial<NR>(a, si, h, split, m, l, acc);
 }
 
-// Log-sum-exp merge of the splits: one 256-thread block per (query head, sequence).  The split
-// weights are computed once into LDS; each thread then sums one channel over a subset of the
-// splits with independent loads, and the subsets are added in LDS.
+// Log-sum-exp merge of the splits.  One 256-thread block per (16-channel slice, query head,
+// sequence), so a decode step launches D/16 * Hq blocks.  Every block derives the split weights
+// w_s = exp2(m_s - M) (M = the largest running maximum among splits that saw a token) into LDS;
+// its threads then sum w_s * acc_s over disjoint subsets of the splits (4 channels per thread,
+// independent 16-byte loads), the subsets are added across lanes and waves, and the result is
+// divided by sum_s w_s * l_s and rounded to BF16.
 constexpr int kCombineThreads = 256;
+constexpr int kCombineCh = 16;  // channels per block
+
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const float t = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, t) : v + t;
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < kCombineThreads / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+  return r;
+}
 
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(int Hq, int D, int S,
                                                                   const float* __restrict__ ws_acc,
                                                                   const float* __restrict__ ws_ml,
                                                                   uint16_t* __restrict__ out) {
   __shared__ float w[1024];
-  __shared__ float red[kCombineThreads];
-  __shared__ float sh_M, sh_den;
-  const int hq = blockIdx.x, si = blockIdx.y, tid = threadIdx.x;
+  __shared__ float red[kCombineThreads / 64 * kCombineCh];
+  const int cb = blockIdx.x, hq = blockIdx.y, si = blockIdx.z, tid = threadIdx.x;
   const float* ml = ws_ml + ((size_t)si * Hq + hq) * S * 2;
-  const float* acc = ws_acc + ((size_t)si * Hq + hq) * S * D;
+  const float* acc = ws_acc + ((size_t)si * Hq + hq) * S * D + cb * kCombineCh;
   float mx = -INFINITY;
   for (int s = tid; s < S; s += kCombineThreads) {
     const float2 v = *reinterpret_cast<const float2*>(ml + 2 * s);
     if (v.y > 0.0f) mx = fmaxf(mx, v.x);
   }
-  red[tid] = mx;
-  __syncthreads();
-  for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  if (tid == 0) sh_M = red[0];
-  __syncthreads();
-  const float M = sh_M;
+  const float M = block_reduce(mx, red, true);
   float den = 0.0f;
   for (int s = tid; s < S; s += kCombineThreads) {
     const float2 v = *reinterpret_cast<const float2*>(ml + 2 * s);
@@ -655,25 +693,32 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(int Hq, int D,
     w[s] = ws;
     den += ws * v.y;
   }
-  red[tid] = den;
-  __syncthreads();
-  for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
+  den = block_reduce(den, red, false);  // its barriers also publish w[]
+  // thread = (split slice, channel quad): slice tid >> 2 of 64, channels 4 * (tid & 3) .. +3
+  const int quad = tid & 3, slice = tid >> 2;
+  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = slice; s < S; s += kCombineThreads / 4) {
+    const float ws = w[s];
+    const float4 v = *reinterpret_cast<const float4*>(acc + (size_t)s * D + 4 * quad);
+    sum.x += ws * v.x;
+    sum.y += ws * v.y;
+    sum.z += ws * v.z;
+    sum.w += ws * v.w;
   }
-  if (tid == 0) sh_den = red[0];
+  for (int o = 4; o < 64; o <<= 1) {  // add the 16 slices of this wave (lane bits 2..5)
+    sum.x += __shfl_xor(sum.x, o);
+    sum.y += __shfl_xor(sum.y, o);
+    sum.z += __shfl_xor(sum.z, o);
+    sum.w += __shfl_xor(sum.w, o);
+  }
   __syncthreads();
-  const int parts = kCombineThreads / D, c = tid % D, part = tid / D;
-  float num = 0.0f;
-#pragma unroll 8
-  for (int s = part; s < S; s += parts) num += w[s] * acc[(size_t)s * D + c];
+  const int lane = tid & 63, wv = tid >> 6;
+  if (lane < 4) *reinterpret_cast<float4*>(red + wv * kCombineCh + 4 * lane) = sum;
   __syncthreads();
-  red[tid] = num;
-  __syncthreads();
-  if (part == 0) {
+  if (tid < kCombineCh) {
     float t = 0.0f;
-    for (int p = 0; p < parts; ++p) t += red[p * D + c];
-    out[((size_t)si * Hq + hq) * D + c] = f32_to_bf16_rne(t / sh_den);
+    for (int i = 0; i < kCombineThreads / 64; ++i) t += red[i * kCombineCh + tid];
+    out[((size_t)si * Hq + hq) * D + cb * kCombineCh + tid] = f32_to_bf16_rne(t / den);
   }
 }
 
@@ -718,8 +763,8 @@ int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& S, 
 
 int launch_combine(const Geo& G, int n_seqs, int n_splits, const float* ws_acc, const float* ws_ml, uint16_t* out,
                    void* stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(G.Hq, n_seqs), dim3(kCombineThreads), 0, (hipStream_t)stream, G.Hq, G.D,
-                     n_splits, ws_acc, ws_ml, out);
+  hipLaunchKernelGGL(combine_kernel, dim3(G.D / kCombineCh, G.Hq, n_seqs), dim3(kCombineThreads), 0,
+                     (hipStream_t)stream, G.Hq, G.D, n_splits, ws_acc, ws_ml, out);
   return (int)hipGetLastError();
 }
 
