@@ -353,6 +353,24 @@ __device__ __forceinline__ void split_range(int L, int n_splits, int split, int&
   if (split == n_splits - 1 && (L % kSB)) sb1 += 1;
 }
 
+// Visit order of a split's super-blocks: the split holding the partial last super-block takes
+// it first, while its first full super-block's bytes are still in flight, instead of adding it
+// (raw tail data, a chain of dependent reads) to the end of the kernel's longest split.
+struct SbOrder {
+  int sb0, cnt, rot;
+  __device__ __forceinline__ SbOrder(int L, int n_splits, int split) {
+    int sb1;
+    split_range(L, n_splits, split, sb0, sb1);
+    cnt = sb1 - sb0;
+    rot = (split == n_splits - 1 && (L % kSB) && cnt > 1) ? cnt - 1 : 0;
+  }
+  __device__ __forceinline__ int at(int it) const {
+    int x = it + rot;
+    if (x >= cnt) x -= cnt;
+    return sb0 + x;
+  }
+};
+
 // First token of lane group j's 16-token group in super-block sb.
 __device__ __forceinline__ int group_token(int sb, int j) { return sb * kSB + 16 * j; }
 
@@ -372,8 +390,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, si = blockIdx.z;
   const int seq = a.S.ids[si], L = a.S.lens[si];
-  int sb0, sb1;
-  split_range(L, a.n_splits, split, sb0, sb1);
+  const SbOrder ord(L, a.n_splits, split);
   uint8_t* esc_lds = esc_base + j * esc_room;
   const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(esc_lds);
   const uint32_t below = (1u << (2 * n)) - 1u;
@@ -396,20 +413,21 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
   for (int i = 0; i < NR; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (sb0 < sb1) {
+  if (ord.cnt > 0) {
     CRegs<NR> cK, cV;
     TileRef rK, rV;
-    uint32_t eK = load_entry<TT>(a, seq, L, group_token(sb0, j), 0, h);
-    uint32_t eV = load_entry<TT>(a, seq, L, group_token(sb0, j), 1, h);
-    rK = tile_ref<NR, TT>(a, seq, L, group_token(sb0, j), 0, h, eK, flags);
+    uint32_t eK = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 0, h);
+    uint32_t eV = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 1, h);
+    rK = tile_ref<NR, TT>(a, seq, L, group_token(ord.at(0), j), 0, h, eK, flags);
     load_tile<NR, TT>(rK, n, cK);
-    for (int sb = sb0; sb < sb1; ++sb) {
+    for (int it = 0; it < ord.cnt; ++it) {
+      const int sb = ord.at(it);
       // V bytes of this super-block load while K is rebuilt and scored
       rV = tile_ref<NR, TT>(a, seq, L, group_token(sb, j), 1, h, eV, flags);
       load_tile<NR, TT>(rV, n, cV);
-      if (sb + 1 < sb1) {
-        eK = load_entry<TT>(a, seq, L, group_token(sb + 1, j), 0, h);
-        eV = load_entry<TT>(a, seq, L, group_token(sb + 1, j), 1, h);
+      if (it + 1 < ord.cnt) {
+        eK = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), j), 0, h);
+        eV = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), j), 1, h);
       }
 
       // ---- K: rebuild into the LDS tile ----
@@ -493,8 +511,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       pack_p<true>(s, phi, plo);
 
       // K bytes of the next super-block load while V is rebuilt and accumulated
-      if (sb + 1 < sb1) {
-        rK = tile_ref<NR, TT>(a, seq, L, group_token(sb + 1, j), 0, h, eK, flags);
+      if (it + 1 < ord.cnt) {
+        rK = tile_ref<NR, TT>(a, seq, L, group_token(ord.at(it + 1), j), 0, h, eK, flags);
         load_tile<NR, TT>(rK, n, cK);
       }
 
@@ -582,8 +600,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, si = blockIdx.z;
   const int seq = a.S.ids[si], L = a.S.lens[si];
-  int sb0, sb1;
-  split_range(L, a.n_splits, split, sb0, sb1);
+  const SbOrder ord(L, a.n_splits, split);
   uint32_t flags = 0;
 
   uint4 qb[NR];
@@ -596,20 +613,21 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
   for (int i = 0; i < NR; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (sb0 < sb1) {
+  if (ord.cnt > 0) {
     RawK<NR> ck;
     RawV<NR> cv;
     const int jr = n >> 2;  // token group of this lane's QK A-operand rows
-    uint32_t eK = load_entry<TT>(a, seq, L, group_token(sb0, jr), 0, h);
-    uint32_t eV = load_entry<TT>(a, seq, L, group_token(sb0, j), 1, h);
-    TileRef rK = tile_ref<NR, TT>(a, seq, L, group_token(sb0, jr), 0, h, eK, flags);
+    uint32_t eK = load_entry<TT>(a, seq, L, group_token(ord.at(0), jr), 0, h);
+    uint32_t eV = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 1, h);
+    TileRef rK = tile_ref<NR, TT>(a, seq, L, group_token(ord.at(0), jr), 0, h, eK, flags);
     raw_load_k<NR, TT>(rK, n, j, ck);
-    for (int sb = sb0; sb < sb1; ++sb) {
+    for (int it = 0; it < ord.cnt; ++it) {
+      const int sb = ord.at(it);
       const TileRef rV = tile_ref<NR, TT>(a, seq, L, group_token(sb, j), 1, h, eV, flags);
       raw_load_v<NR, TT>(rV, n, cv);
-      if (sb + 1 < sb1) {
-        eK = load_entry<TT>(a, seq, L, group_token(sb + 1, jr), 0, h);
-        eV = load_entry<TT>(a, seq, L, group_token(sb + 1, j), 1, h);
+      if (it + 1 < ord.cnt) {
+        eK = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), jr), 0, h);
+        eV = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), j), 1, h);
       }
       // scores of this lane belong to token group j: its K validity comes from lane 4j
       const int validKj = __shfl(rK.valid, 4 * j);
@@ -628,8 +646,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       rescale_acc<NR>(acc, alpha, j);
       uint4 phi[2], plo[2];
       pack_p<false>(s, phi, plo);
-      if (sb + 1 < sb1) {
-        rK = tile_ref<NR, TT>(a, seq, L, group_token(sb + 1, jr), 0, h, eK, flags);
+      if (it + 1 < ord.cnt) {
+        rK = tile_ref<NR, TT>(a, seq, L, group_token(ord.at(it + 1), jr), 0, h, eK, flags);
         raw_load_k<NR, TT>(rK, n, j, ck);
       }
 #pragma unroll
