@@ -17,9 +17,10 @@ def _ptr(t: torch.Tensor) -> int:
     return t.data_ptr()
 
 
-def _elem(t: torch.Tensor, what: str) -> torch.Tensor:
-    if not t.is_cuda or not t.is_contiguous() or t.element_size() != 2:
-        raise ValueError(f"{what} must be a contiguous 2-byte (BF16 bits) CUDA tensor")
+def _elem(t: torch.Tensor, what: str, nbytes: int = 2) -> torch.Tensor:
+    if not t.is_cuda or not t.is_contiguous() or t.element_size() != nbytes:
+        kind = "2-byte (BF16 bits)" if nbytes == 2 else "1-byte (FP8 bits)"
+        raise ValueError(f"{what} must be a contiguous {kind} CUDA tensor")
     return t
 
 
@@ -39,6 +40,8 @@ class KVCache:
         L.check(self.lib.kv_buffer_sizes(ctypes.byref(self.params), sizes, ctypes.byref(stride)))
         self.slot_stride = stride.value
         self.T, self.D, self.Hkv, self.Hq = block_tokens, head_dim, num_kv_heads, num_q_heads
+        self.dtype = dtype
+        self.EB = 2 if dtype == L.BF16 else 1  # bytes per cached element
         self.compressed = bool(compressed)
         self.buffers = {}
         for name, sz in zip(L.BUFFER_NAMES, sizes):
@@ -65,7 +68,7 @@ class KVCache:
 
     def calibrate(self, k: torch.Tensor, v: torch.Tensor):
         """k, v: [n][Hkv][D] element bits."""
-        _elem(k, "k"), _elem(v, "v")
+        _elem(k, "k", self.EB), _elem(v, "v", self.EB)
         self._shape(k, "k", 1), self._shape(v, "v", 1)
         if k.shape != v.shape:
             raise ValueError("k and v differ in shape")
@@ -73,7 +76,7 @@ class KVCache:
 
     def append(self, seq_ids, k: torch.Tensor, v: torch.Tensor):
         """k, v: [n_seqs][n_tokens][Hkv][D] element bits."""
-        _elem(k, "k"), _elem(v, "v")
+        _elem(k, "k", self.EB), _elem(v, "v", self.EB)
         self._shape(k, "k", 2), self._shape(v, "v", 2)
         if k.shape[0] != len(seq_ids) or k.shape != v.shape:
             raise ValueError("k, v must be [n_seqs][n_tokens][Hkv][D] with n_seqs = len(seq_ids)")
@@ -83,12 +86,13 @@ class KVCache:
 
     def decode_blocks(self, seq: int, first: int, n: int, out=None):
         if out is None:
-            k = torch.empty((n * self.T, self.Hkv, self.D), dtype=torch.int16, device=self.device)
+            k = torch.empty((n * self.T, self.Hkv, self.D), dtype=torch.int16 if self.EB == 2 else torch.uint8,
+                            device=self.device)
             v = torch.empty_like(k)
         else:
             k, v = out
             for t in (k, v):
-                _elem(t, "out")
+                _elem(t, "out", self.EB)
                 if tuple(t.shape) != (n * self.T, self.Hkv, self.D):
                     raise ValueError("decode_blocks outputs must be [n*T][Hkv][D]")
         L.check(self.lib.kv_decode_blocks(self.handle, seq, first, n, _ptr(k), _ptr(v), self._stream()))

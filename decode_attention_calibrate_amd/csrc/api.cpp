@@ -62,7 +62,6 @@ int check_params(const kvc_params* p) {
   if (p->compressed && p->num_comp_slots < 1) return fail(KVC_EINVAL, "a compressed cache needs compressed slots");
   if (!p->compressed && p->num_raw_slots < 1) return fail(KVC_EINVAL, "an uncompressed cache needs raw slots");
   // valid requests the kernels of this build do not implement
-  if (p->dtype != KVC_BF16) return fail(KVC_EUNSUPPORTED, "FP8 caches are not implemented by these kernels");
   if (p->group_tokens != kvc::kGroup) return fail(KVC_EUNSUPPORTED, "these kernels implement 16-token groups");
   if (p->block_tokens != 16 && p->block_tokens != 32 && p->block_tokens != 64)
     return fail(KVC_EUNSUPPORTED, "these kernels implement block_tokens 16, 32 or 64");
@@ -75,6 +74,11 @@ int align16(int x) { return (x + 15) / 16 * 16; }
 Geo make_geo(const kvc_params& p) {
   Geo G;
   memset(&G, 0, sizeof(G));
+  G.fmt = p.dtype;
+  G.F = p.dtype == KVC_BF16 ? 8 : (p.dtype == KVC_FP8_E5M2 ? 5 : 4);
+  G.MB = p.dtype == KVC_BF16 ? 7 : (p.dtype == KVC_FP8_E5M2 ? 2 : 3);
+  G.EB = p.dtype == KVC_BF16 ? 2 : 1;
+  G.sm_pair = 4 * (1 + G.MB);
   G.T = p.block_tokens;
   G.D = p.head_dim;
   G.Hkv = p.num_kv_heads;
@@ -87,7 +91,7 @@ Geo make_geo(const kvc_params& p) {
   G.tag_off = 0;
   G.code_off = align16(2 * G.PW * 4);
   G.sm_off = G.code_off + align16(G.T * G.D * 3 / 8);
-  G.esc_off = G.sm_off + align16(G.T * G.D);
+  G.esc_off = G.sm_off + align16(G.T * G.D * (1 + G.MB) / 8);
   G.esc_cap = esc_cap_of(p);
   G.stride = G.esc_off + G.esc_cap;
   G.raw_elems = G.T * G.D;
@@ -101,8 +105,8 @@ Geo make_geo(const kvc_params& p) {
 
 void sizes_of(const kvc_params& p, const Geo& G, size_t out[KVC_NUM_BUFFERS]) {
   out[0] = (size_t)G.n_comp * G.stride;
-  out[1] = (size_t)G.n_raw * G.raw_elems * 2;
-  out[2] = (size_t)p.max_seqs * 2 * G.Hkv * G.raw_elems * 2;
+  out[1] = (size_t)G.n_raw * G.raw_elems * G.EB;
+  out[2] = (size_t)p.max_seqs * 2 * G.Hkv * G.raw_elems * G.EB;
   out[3] = (size_t)4 * G.Hkv * G.D;
   out[4] = (size_t)p.max_seqs * p.max_blocks_per_seq * 2 * G.Hkv * 4;
   out[5] = (size_t)G.n_comp * 4;
@@ -211,8 +215,7 @@ int kv_calibrate(kvc_cache* c, const void* k_dev, const void* v_dev, int32_t n_t
   if (!c) return fail(KVC_EINVAL, "cache is NULL");
   if (!k_dev || !v_dev || n_tokens < 1) return fail(KVC_EINVAL, "calibration needs K and V with n_tokens >= 1");
   if (c->blocks > 0) return fail(KVC_ESTATE, "calibration must precede the first finished block");
-  const int rc = hip_fail(kvc::launch_calibrate(c->G, c->B, (const uint16_t*)k_dev, (const uint16_t*)v_dev,
-                                                n_tokens, stream),
+  const int rc = hip_fail(kvc::launch_calibrate(c->G, c->B, k_dev, v_dev, n_tokens, stream),
                           "launch calibrate");
   if (rc == KVC_OK) c->calibrated = true;
   return rc;
@@ -245,8 +248,8 @@ int kv_encode_append(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, 
       S.lens[i] = c->len[id];
       max_new = std::max(max_new, (c->len[id] + n_tokens) / T - c->len[id] / T);
     }
-    const uint16_t* k = (const uint16_t*)k_dev + (size_t)s0 * n_tokens * row;
-    const uint16_t* v = (const uint16_t*)v_dev + (size_t)s0 * n_tokens * row;
+    const uint8_t* k = (const uint8_t*)k_dev + (size_t)s0 * n_tokens * row * c->G.EB;
+    const uint8_t* v = (const uint8_t*)v_dev + (size_t)s0 * n_tokens * row * c->G.EB;
     rc = hip_fail(kvc::launch_append(c->G, c->B, S, k, v, n_tokens, max_new, stream), "launch append");
     if (rc != KVC_OK) return rc;
   }
@@ -261,8 +264,7 @@ int kv_decode_blocks(kvc_cache* c, int32_t seq, int32_t first_block, int32_t n_b
   if (seq < 0 || seq >= c->p.max_seqs) return fail(KVC_EINVAL, "sequence id out of range");
   if (!k_out_dev || !v_out_dev || first_block < 0 || n_blocks < 1) return fail(KVC_EINVAL, "bad block range");
   if (first_block + n_blocks > c->len[seq] / c->G.T) return fail(KVC_EINVAL, "blocks past the finished blocks");
-  return hip_fail(kvc::launch_decode_blocks(c->G, c->B, seq, first_block, n_blocks, (uint16_t*)k_out_dev,
-                                            (uint16_t*)v_out_dev, stream),
+  return hip_fail(kvc::launch_decode_blocks(c->G, c->B, seq, first_block, n_blocks, k_out_dev, v_out_dev, stream),
                   "launch decode_blocks");
 }
 
@@ -281,6 +283,7 @@ int kv_attention_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_s
   if (ws_bytes < kv_attention_workspace_bytes(&c->p, n_seqs, n_splits))
     return fail(KVC_ESMALLWS, "workspace smaller than kv_attention_workspace_bytes()");
   if (((uintptr_t)ws_dev & 15u) || ((uintptr_t)q_dev & 15u)) return fail(KVC_EINVAL, "q and workspace must be 16-byte aligned");
+  if (c->G.fmt != KVC_BF16) return fail(KVC_EUNSUPPORTED, "decode attention over FP8 caches is not implemented yet");
   for (int i = 0; i < n_seqs; ++i)
     if (c->len[seq_ids_host[i]] < 1) return fail(KVC_EINVAL, "every listed sequence needs at least one token");
   const Geo& G = c->G;

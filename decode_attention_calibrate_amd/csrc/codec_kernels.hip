@@ -14,6 +14,20 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Element bits at index i of a BF16 (EB = 2) or FP8 (EB = 1) element array.
+__device__ __forceinline__ uint32_t elem_at(const void* p, size_t i, int EB) {
+  return EB == 2 ? (uint32_t)reinterpret_cast<const uint16_t*>(p)[i] : (uint32_t)reinterpret_cast<const uint8_t*>(p)[i];
+}
+__device__ __forceinline__ void elem_put(void* p, size_t i, int EB, uint32_t x) {
+  if (EB == 2) reinterpret_cast<uint16_t*>(p)[i] = (uint16_t)x;
+  else reinterpret_cast<uint8_t*>(p)[i] = (uint8_t)x;
+}
+__device__ __forceinline__ uint32_t exp_of(const Geo& G, uint32_t x) { return (x >> G.MB) & ((1u << G.F) - 1u); }
+// (sign << MB) | mantissa
+__device__ __forceinline__ uint32_t sm_of(const Geo& G, uint32_t x) {
+  return ((x >> (G.MB + G.F)) << G.MB) | (x & ((1u << G.MB) - 1u));
+}
+
 __device__ __forceinline__ int block_sum(int v, int* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -74,23 +88,21 @@ __global__ void init_kernel(Geo G, DevBufs B) {
   }
 }
 
-// One block per (channel, kv-head, K|V): histogram of the 8-bit exponent over the calibration
-// tokens, then the 8- and 16-wide windows with the largest count (ties: lower median start).
-__global__ void calibrate_kernel(Geo G, DevBufs B, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                 int n) {
+// One block per (channel, kv-head, K|V): histogram of the F-bit exponent field over the
+// calibration tokens, then the 8- and 16-wide windows with the largest count (ties: lower median
+// start).  A format whose exponent field is only 4 bits wide (E4M3) has no 16-wide window; its
+// b4 stays 0.
+__global__ void calibrate_kernel(Geo G, DevBufs B, const void* __restrict__ k, const void* __restrict__ v, int n) {
   __shared__ int hist[256];
   __shared__ int red[8];
   const int c = blockIdx.x, h = blockIdx.y, kv = blockIdx.z, tid = threadIdx.x;
   hist[tid] = 0;
   __syncthreads();
-  const uint16_t* src = kv ? v : k;
-  for (int t = tid; t < n; t += kThreads) {
-    const uint32_t x = src[((size_t)t * G.Hkv + h) * G.D + c];
-    atomicAdd(&hist[(x >> 7) & 0xFF], 1);
-  }
+  const void* src = kv ? v : k;
+  for (int t = tid; t < n; t += kThreads) atomicAdd(&hist[exp_of(G, elem_at(src, ((size_t)t * G.Hkv + h) * G.D + c, G.EB))], 1);
   __syncthreads();
-  for (int w = 3; w <= 4; ++w) {
-    const int width = 1 << w, nb = 256 - width + 1;
+  for (int w = 3; w <= 4 && w < G.F; ++w) {
+    const int width = 1 << w, nb = (1 << G.F) - width + 1;
     int cov = -1;
     if (tid < nb) {
       cov = 0;
@@ -106,9 +118,9 @@ __global__ void calibrate_kernel(Geo G, DevBufs B, const uint16_t* __restrict__ 
 }
 
 // Mode of a group from its exponent range and the channel's bases: 0 narrow, 1 wide, 2 raw.
-__device__ __forceinline__ int choose_mode(uint32_t mn, uint32_t mx, uint32_t b3, uint32_t b4) {
+__device__ __forceinline__ int choose_mode(uint32_t mn, uint32_t mx, uint32_t b3, uint32_t b4, bool has_wide) {
   if (b3 <= mn && mx <= b3 + 7) return 0;
-  if (b4 <= mn && mx <= b4 + 15) return 1;
+  if (has_wide && b4 <= mn && mx <= b4 + 15) return 1;
   return 2;
 }
 
@@ -125,23 +137,25 @@ __device__ __forceinline__ PairInfo pair_info(const Geo& G, const uint16_t* tile
     const int q = 2 * pr + gi, tg = q / G.D, c = q % G.D;
     uint32_t mn = 255, mx = 0;
     for (int tau = 0; tau < kGroup; ++tau) {
-      const uint32_t e = (tile[(tg * kGroup + tau) * G.D + c] >> 7) & 0xFF;
+      const uint32_t e = exp_of(G, tile[(tg * kGroup + tau) * G.D + c]);
       mn = min(mn, e);
       mx = max(mx, e);
     }
-    P.mode[gi] = choose_mode(mn, mx, b3[c], b4[c]);
+    P.mode[gi] = choose_mode(mn, mx, b3[c], b4[c], G.F > 4);
     P.base[gi] = P.mode[gi] == 0 ? b3[c] : (P.mode[gi] == 1 ? b4[c] : 0u);
   }
   return P;
 }
 
-__device__ __forceinline__ int mode_planes(int m) { return m == 0 ? 0 : (m == 1 ? 1 : 5); }
+// 16-bit escape units of a group: none (narrow), one plane (wide), F - 3 units (raw: bit 3,
+// then BF16 bits 4..7 as four units of nibbles, E5M2 bit 4 as one more plane).
+__device__ __forceinline__ int mode_planes(const Geo& G, int m) { return m == 0 ? 0 : (m == 1 ? 1 : G.F - 3); }
 
 // One block per newly full block of one (sequence, K|V, head): gathers its T tokens from the
 // old tail and the appended tokens, encodes it (or stores it raw), pops a slot and writes the
 // block-table entry.
-__global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqList S, const uint16_t* __restrict__ kin,
-                                                          const uint16_t* __restrict__ vin, int n_tok) {
+__global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqList S, const void* __restrict__ kin,
+                                                          const void* __restrict__ vin, int n_tok) {
   extern __shared__ uint32_t smem[];
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);                  // [T][D] logical
   uint32_t* tagw = smem + (G.raw_elems / 2);                            // [2][PW]
@@ -155,20 +169,20 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
   const int b = first_blk + blockIdx.x;
   if (b >= last_full) return;
   const int tid = threadIdx.x, D = G.D, T = G.T;
-  const uint16_t* in = kv ? vin : kin;
-  const uint16_t* tail = B.tail + tail_offset(G, seq, kv, h);
+  const void* in = kv ? vin : kin;
+  const uint8_t* tail = reinterpret_cast<const uint8_t*>(B.tail) + tail_offset(G, seq, kv, h) * G.EB;
   const int tail_base = first_blk * T;
 
   for (int i = tid; i < G.raw_elems; i += kThreads) {
     const int t = i / D, c = i % D, p = b * T + t;
-    uint16_t x;
+    uint32_t x;
     if (p < L0) {
       const int tt = p - tail_base;
-      x = kv ? tail[c * T + tt] : tail[tt * D + c];
+      x = elem_at(tail, kv ? (size_t)c * T + tt : (size_t)tt * D + c, G.EB);
     } else {
-      x = in[(((size_t)si * n_tok + (p - L0)) * G.Hkv + h) * D + c];
+      x = elem_at(in, (((size_t)si * n_tok + (p - L0)) * G.Hkv + h) * D + c, G.EB);
     }
-    tile[i] = x;
+    tile[i] = (uint16_t)x;
   }
   for (int i = tid; i < 2 * G.PW; i += kThreads) tagw[i] = 0;
   if (tid < 3) sh_modes[tid] = 0;
@@ -188,7 +202,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
       const int pr = pr0 + k;
       if (pr >= G.NP) break;
       const PairInfo P = pair_info(G, tile, b3, b4, pr);
-      my_planes += mode_planes(P.mode[0]) + mode_planes(P.mode[1]);
+      my_planes += mode_planes(G, P.mode[0]) + mode_planes(G, P.mode[1]);
       cnt[P.mode[0]]++;
       cnt[P.mode[1]]++;
     }
@@ -244,13 +258,13 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
   }
 
   if (raw) {
-    uint16_t* dst = B.raw_pool + (size_t)slot * G.raw_elems;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
     for (int i = tid; i < G.raw_elems; i += kThreads) {
       if (kv) {
         const int c = i / T, t = i % T;
-        dst[i] = tile[t * D + c];
+        elem_put(dst, i, G.EB, tile[t * D + c]);
       } else {
-        dst[i] = tile[i];
+        elem_put(dst, i, G.EB, tile[i]);
       }
     }
     if (tid == 0) B.table[entry_idx] = (uint32_t)slot | 0x80000000u;
@@ -264,28 +278,32 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
     if (pr >= G.NP) break;
     const PairInfo PI = pair_info(G, tile, b3, b4, pr);
     uint32_t W[3] = {0u, 0u, 0u};
-    uint32_t smw[8];
+    uint32_t smw[8];  // SM words of the pair: BF16 8 (bytes), E5M2 3 (unit layout), E4M3 4 (nibbles)
 #pragma unroll
     for (int i = 0; i < 8; ++i) smw[i] = 0;
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       const int q = 2 * pr + gi, tg = q / D, c = q % D;
-      const int np = mode_planes(PI.mode[gi]);
-      // escape units: [0] = plane of offset bit 3; raw groups add [1..4] = 4-bit fields of
-      // offset bits 4..7, token tau at bits 4*tau.. of the 64-bit little-endian run
+      const int np = mode_planes(G, PI.mode[gi]);
+      // escape units: [0] = plane of offset bit 3; a raw BF16 group adds [1..4] = 4-bit fields
+      // of offset bits 4..7 (token tau at bits 4*tau.. of the 64-bit little-endian run), a raw
+      // E5M2 group adds [1] = plane of offset bit 4
       uint32_t units[5] = {0u, 0u, 0u, 0u, 0u};
       for (int tau = 0; tau < kGroup; ++tau) {
         const uint32_t x = tile[(tg * kGroup + tau) * D + c];
-        const uint32_t o = ((x >> 7) & 0xFF) - PI.base[gi];
+        const uint32_t o = exp_of(G, x) - PI.base[gi];
         const int r = gi * kGroup + tau, lk = r & 3, s = r >> 2;
-        const uint32_t code = o & 7u;
+        const uint32_t code = o & 7u, f = sm_of(G, x);
         for (int bb = 0; bb < 3; ++bb) {
           const int xs = 3 * s + bb;
           W[xs >> 3] |= ((code >> bb) & 1u) << (8 * lk + (xs & 7));
+          if (G.MB == 2) smw[xs >> 3] |= ((f >> bb) & 1u) << (8 * lk + (xs & 7));
         }
-        smw[r >> 2] |= (((x >> 8) & 0x80u) | (x & 0x7Fu)) << (8 * (r & 3));
+        if (G.MB == 7) smw[r >> 2] |= f << (8 * (r & 3));
+        if (G.MB == 3) smw[r >> 3] |= f << (4 * (r & 7));
         units[0] |= ((o >> 3) & 1u) << tau;
-        units[1 + (tau >> 2)] |= ((o >> 4) & 0xFu) << (4 * (tau & 3));
+        if (G.F == 8) units[1 + (tau >> 2)] |= ((o >> 4) & 0xFu) << (4 * (tau & 3));
+        if (G.F == 5) units[1] |= ((o >> 4) & 1u) << tau;
       }
       uint16_t* esc16 = reinterpret_cast<uint16_t*>(dst + G.esc_off);
       for (int p = 0; p < np; ++p) esc16[P + p] = (uint16_t)units[p];
@@ -297,9 +315,8 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
     code[0] = W[0];
     code[1] = W[1];
     code[2] = W[2];
-    uint4* smd = reinterpret_cast<uint4*>(dst + G.sm_off + 32 * pr);
-    smd[0] = make_uint4(smw[0], smw[1], smw[2], smw[3]);
-    smd[1] = make_uint4(smw[4], smw[5], smw[6], smw[7]);
+    uint32_t* smd = reinterpret_cast<uint32_t*>(dst + G.sm_off + G.sm_pair * pr);
+    for (int i = 0; i < G.sm_pair / 4; ++i) smd[i] = smw[i];
   }
   // zero the unused escape bytes [2*total, esc_cap)
   {
@@ -318,20 +335,19 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
 }
 
 // Writes the appended tokens that do not complete a block into the sequence's tail.
-__global__ void tail_kernel(Geo G, DevBufs B, SeqList S, const uint16_t* __restrict__ kin,
-                            const uint16_t* __restrict__ vin, int n_tok) {
+__global__ void tail_kernel(Geo G, DevBufs B, SeqList S, const void* __restrict__ kin, const void* __restrict__ vin,
+                            int n_tok) {
   const int si = blockIdx.x, kv = blockIdx.y / G.Hkv, h = blockIdx.y % G.Hkv;
   const int seq = S.ids[si], L0 = S.lens[si];
   const int new_full = (L0 + n_tok) / G.T;
   const int p0 = max(L0, new_full * G.T), p1 = L0 + n_tok;
   const int D = G.D, T = G.T;
-  const uint16_t* in = kv ? vin : kin;
-  uint16_t* tail = B.tail + tail_offset(G, seq, kv, h);
+  const void* in = kv ? vin : kin;
+  uint8_t* tail = reinterpret_cast<uint8_t*>(B.tail) + tail_offset(G, seq, kv, h) * G.EB;
   for (int i = threadIdx.x; i < (p1 - p0) * D; i += blockDim.x) {
     const int p = p0 + i / D, c = i % D, tt = p - new_full * T;
-    const uint16_t x = in[(((size_t)si * n_tok + (p - L0)) * G.Hkv + h) * D + c];
-    if (kv) tail[c * T + tt] = x;
-    else tail[tt * D + c] = x;
+    const uint32_t x = elem_at(in, (((size_t)si * n_tok + (p - L0)) * G.Hkv + h) * D + c, G.EB);
+    elem_put(tail, kv ? (size_t)c * T + tt : (size_t)tt * D + c, G.EB, x);
   }
 }
 
@@ -353,30 +369,93 @@ __global__ void release_kernel(Geo G, DevBufs B, int seq, int n_blocks) {
   }
 }
 
+// FP8 tiles, one element at a time: every group's mode and first escape unit go to LDS (a block
+// scan of the unit counts), then each thread rebuilds elements from their 3-bit code, escape
+// bits and sign/mantissa field.  (BF16 tiles take the four-token SWAR path below.)
+__device__ void decode_fp8_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
+                                const uint8_t* b4, uint8_t* out, int bi, int h) {
+  __shared__ uint16_t gP[1024];
+  __shared__ uint8_t gm[1024];
+  __shared__ int red[8];
+  const int tid = threadIdx.x, D = G.D, T = G.T;
+  const uint32_t* tagE = reinterpret_cast<const uint32_t*>(tile + G.tag_off);
+  const uint32_t* tagR = tagE + G.PW;
+  const int per = (G.NG + kThreads - 1) / kThreads, q0 = tid * per;
+  int cnt = 0;
+  for (int q = q0; q < min(G.NG, q0 + per); ++q) {
+    const uint32_t E = (tagE[q >> 5] >> (q & 31)) & 1u, R = (tagR[q >> 5] >> (q & 31)) & 1u;
+    const int mode = (int)(E + R);
+    if ((R && !E) || (mode == 1 && G.F <= 4)) atomicOr(&B.counters->status, 8u);
+    gm[q] = (uint8_t)mode;
+    cnt += mode_planes(G, mode);
+  }
+  int total;
+  int P = block_exclusive_scan(cnt, red, &total);
+  for (int q = q0; q < min(G.NG, q0 + per); ++q) {
+    gP[q] = (uint16_t)P;
+    P += mode_planes(G, gm[q]);
+  }
+  __syncthreads();
+  const uint8_t* code = tile + G.code_off;
+  const uint8_t* sm = tile + G.sm_off;
+  const uint8_t* esc = tile + G.esc_off;
+  const int max_bit = 8 * G.esc_cap;
+  auto bit = [](const uint8_t* buf, int b) -> uint32_t { return (buf[b >> 3] >> (b & 7)) & 1u; };
+  auto ebit = [&](int b) -> uint32_t { return b < max_bit ? bit(esc, b) : 0u; };
+  for (int i = tid; i < G.raw_elems; i += kThreads) {
+    const int t = i / D, c = i % D, tg = t / kGroup, tau = t % kGroup;
+    const int q = tg * D + c, n = q * kGroup + tau;
+    const int mode = gm[q];
+    const int Pq = gP[q];
+    // 3-bit fields in the 32-element unit layout: element r of unit u in byte lane r%4, slot r/4
+    const int u = n >> 5, r = n & 31, lk = r & 3, sl = r >> 2;
+    uint32_t o = 0, f = 0;
+    for (int bb = 0; bb < 3; ++bb) {
+      const int x = 3 * sl + bb, byte = 12 * u + 4 * (x >> 3) + lk;
+      o |= ((code[byte] >> (x & 7)) & 1u) << bb;
+      if (G.MB == 2) f |= ((sm[byte] >> (x & 7)) & 1u) << bb;
+    }
+    if (G.MB == 3) f = (sm[n >> 1] >> (4 * (n & 1))) & 0xFu;
+    if (mode >= 1) o |= ebit(Pq * kGroup + tau) << 3;
+    if (mode == 2 && G.F == 5) o |= ebit((Pq + 1) * kGroup + tau) << 4;
+    const uint32_t base = mode == 0 ? b3[c] : (mode == 1 ? b4[c] : 0u);
+    if (base + o >= (1u << G.F)) atomicOr(&B.counters->status, 8u);  // corrupt offset
+    const uint32_t e = (base + o) & ((1u << G.F) - 1u);
+    const uint32_t x = ((f >> G.MB) << 7) | (e << G.MB) | (f & ((1u << G.MB) - 1u));
+    out[(((size_t)bi * T + t) * G.Hkv + h) * D + c] = (uint8_t)x;
+  }
+}
+
 // One block per (block, K|V, head): rebuilds the tile into [n*T][Hkv][D].
 __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs B, int seq, int first,
-                                                                  uint16_t* __restrict__ kout,
-                                                                  uint16_t* __restrict__ vout) {
+                                                                  void* __restrict__ kout, void* __restrict__ vout) {
   const int bi = blockIdx.x, kv = blockIdx.y / G.Hkv, h = blockIdx.y % G.Hkv;
   const int b = first + bi, D = G.D, T = G.T, tid = threadIdx.x;
-  uint16_t* out = kv ? vout : kout;
+  void* outv = kv ? vout : kout;
   const uint32_t e = B.table[table_index(G, seq, b, kv, h)];
-  auto out_at = [&](int t, int c) -> uint16_t* { return out + (((size_t)bi * T + t) * G.Hkv + h) * D + c; };
+  auto out_idx = [&](int t, int c) -> size_t { return (((size_t)bi * T + t) * G.Hkv + h) * D + c; };
   if (e == kUnallocated) {
-    for (int i = tid; i < G.raw_elems; i += kThreads) *out_at(i / D, i % D) = 0;
+    for (int i = tid; i < G.raw_elems; i += kThreads) elem_put(outv, out_idx(i / D, i % D), G.EB, 0u);
     if (tid == 0) atomicOr(&B.counters->status, 4u);
     return;
   }
   const int slot = (int)(e & 0x00FFFFFFu);
   if (e & 0x80000000u) {
-    const uint16_t* src = B.raw_pool + (size_t)slot * G.raw_elems;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
     for (int i = tid; i < G.raw_elems; i += kThreads) {
       const int t = i / D, c = i % D;
-      *out_at(t, c) = kv ? src[c * T + t] : src[i];
+      elem_put(outv, out_idx(t, c), G.EB, elem_at(src, kv ? (size_t)c * T + t : (size_t)i, G.EB));
     }
     return;
   }
   const uint8_t* tile = B.comp_pool + (size_t)slot * G.stride;
+  if (G.EB == 1) {
+    decode_fp8_tile(G, B, tile, B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
+                    B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, reinterpret_cast<uint8_t*>(outv), bi, h);
+    return;
+  }
+  uint16_t* out = reinterpret_cast<uint16_t*>(outv);
+  auto out_at = [&](int t, int c) -> uint16_t* { return out + out_idx(t, c); };
   const uint32_t* tagE = reinterpret_cast<const uint32_t*>(tile + G.tag_off);
   const uint32_t* tagR = tagE + G.PW;
   const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(tile + G.esc_off);
@@ -430,13 +509,13 @@ int launch_init(const Geo& G, const DevBufs& B, const int32_t*, const int32_t*, 
   return (int)hipGetLastError();
 }
 
-int launch_calibrate(const Geo& G, const DevBufs& B, const uint16_t* k, const uint16_t* v, int n, void* stream) {
+int launch_calibrate(const Geo& G, const DevBufs& B, const void* k, const void* v, int n, void* stream) {
   hipLaunchKernelGGL(calibrate_kernel, dim3(G.D, G.Hkv, 2), dim3(kThreads), 0, (hipStream_t)stream, G, B, k, v, n);
   return (int)hipGetLastError();
 }
 
-int launch_append(const Geo& G, const DevBufs& B, const SeqList& S, const uint16_t* k, const uint16_t* v,
-                  int n_tokens, int max_new_blocks, void* stream) {
+int launch_append(const Geo& G, const DevBufs& B, const SeqList& S, const void* k, const void* v, int n_tokens,
+                  int max_new_blocks, void* stream) {
   if (max_new_blocks > 0) {
     const size_t lds = (size_t)G.raw_elems * 2 + (size_t)2 * G.PW * 4;
     hipLaunchKernelGGL(encode_kernel, dim3(max_new_blocks, S.n, 2 * G.Hkv), dim3(kThreads), lds,
@@ -455,8 +534,8 @@ int launch_release(const Geo& G, const DevBufs& B, int seq, int n_blocks, void* 
   return (int)hipGetLastError();
 }
 
-int launch_decode_blocks(const Geo& G, const DevBufs& B, int seq, int first, int n, uint16_t* k_out,
-                         uint16_t* v_out, void* stream) {
+int launch_decode_blocks(const Geo& G, const DevBufs& B, int seq, int first, int n, void* k_out, void* v_out,
+                         void* stream) {
   if (n <= 0) return 0;
   hipLaunchKernelGGL(decode_blocks_kernel, dim3(n, 2 * G.Hkv), dim3(kThreads), 0, (hipStream_t)stream, G, B, seq,
                      first, k_out, v_out);

@@ -9,9 +9,13 @@
 //   CODE : 3-bit offset codes; 12-byte units of 32 elements (one pair of groups); element
 //          r of a unit lives in byte lane r%4, slot r/4 of a 24-bit lane stream spread over
 //          the unit's three words (byte lane k of word w = stream bits 8w..8w+7);
-//   SM   : BF16 sign/mantissa byte (s << 7) | m per element, element order;
-//   ESC  : for every group with mode >= 1, in q order, (w - 3) 16-bit planes holding bit 3+p
-//          of the 16 offsets (bit tau = token tau); zero up to esc_cap;
+//   SM   : sign/mantissa field (s << MB) | m per element, element order: BF16 one byte each;
+//          E5M2 3-bit fields in the CODE unit layout (12 bytes per 32 elements); E4M3 4-bit
+//          fields, element n at bits 4n..4n+3 (16 bytes per 32 elements);
+//   ESC  : for every group with mode >= 1, in q order: a 16-bit plane with bit 3 of the 16
+//          offsets (bit tau = token tau); a raw BF16 group then adds the offset bits 4..7 as
+//          one 4-bit field per token (4 units), a raw E5M2 group one more plane (bit 4); zero
+//          up to esc_cap;
 //   RAW  : tiles that overflow esc_cap (and every tile of an uncompressed cache) are stored
 //          as native elements, K token-major [t][c], V channel-major [c][t].
 #pragma once
@@ -25,11 +29,14 @@ constexpr int kMaxSeqsPerLaunch = 64;
 constexpr uint32_t kUnallocated = 0xFFFFFFFFu;
 
 struct Geo {
+  int fmt;                          // 0 BF16, 1 FP8 E5M2, 2 FP8 E4M3 (kvc_dtype)
+  int F, MB, EB;                    // exponent bits, mantissa bits, bytes per element
+  int sm_pair;                      // SM bytes per pair of groups (32 elements)
   int T, D, Hkv, Hq, g;             // block tokens, head dim, KV heads, query heads, Hq/Hkv
   int NT, NG, NP, PW;               // token groups per tile, groups, group pairs, tag words
   int tag_off, code_off, sm_off, esc_off, stride;  // compressed tile offsets (bytes)
   int esc_cap;                      // escape capacity (bytes)
-  int raw_elems;                    // T*D
+  int raw_elems;                    // T*D (a raw tile or tail tile holds raw_elems * EB bytes)
   int max_seqs, max_blocks;
   int n_comp, n_raw;
   int compressed;
@@ -44,8 +51,8 @@ struct Counters {
 
 struct DevBufs {
   uint8_t* comp_pool;
-  uint16_t* raw_pool;
-  uint16_t* tail;
+  uint16_t* raw_pool;    // element storage: 16-bit words (BF16) or bytes (FP8, cast to uint8_t*)
+  uint16_t* tail;        // same
   uint8_t* bases;        // [2][2][Hkv][D]
   uint32_t* table;       // [max_seqs][max_blocks][2][Hkv]
   int32_t* comp_free;
@@ -70,13 +77,12 @@ __host__ __device__ inline size_t tail_offset(const Geo& G, int seq, int kv, int
 // ---- launchers (defined in the .hip files; return hipError_t as int) ----
 int launch_init(const Geo& G, const DevBufs& B, const int32_t* comp_perm_dev, const int32_t* raw_perm_dev,
                 void* stream);
-int launch_calibrate(const Geo& G, const DevBufs& B, const uint16_t* k, const uint16_t* v, int n_tokens,
-                     void* stream);
-int launch_append(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* k, const uint16_t* v,
-                  int n_tokens, int max_new_blocks, void* stream);
+int launch_calibrate(const Geo& G, const DevBufs& B, const void* k, const void* v, int n_tokens, void* stream);
+int launch_append(const Geo& G, const DevBufs& B, const SeqList& seqs, const void* k, const void* v, int n_tokens,
+                  int max_new_blocks, void* stream);
 int launch_release(const Geo& G, const DevBufs& B, int seq, int n_blocks, void* stream);
-int launch_decode_blocks(const Geo& G, const DevBufs& B, int seq, int first, int n, uint16_t* k_out,
-                         uint16_t* v_out, void* stream);
+int launch_decode_blocks(const Geo& G, const DevBufs& B, int seq, int first, int n, void* k_out, void* v_out,
+                         void* stream);
 int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale,
                               int n_splits, float* ws_acc, float* ws_ml, void* stream);
 int launch_combine(const Geo& G, int n_seqs, int n_splits, const float* ws_acc, const float* ws_ml, uint16_t* out,

@@ -9,11 +9,17 @@ import oracle
 import synth
 
 
-def dev(a: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda()
+def dev(a: np.ndarray, fmt: int = oracle.BF16) -> torch.Tensor:
+    """Element bits to the device: BF16 as 16-bit words, FP8 as bytes."""
+    if fmt == oracle.BF16:
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a).astype(np.uint8)).cuda()
 
 
 def host(t: torch.Tensor) -> np.ndarray:
+    """Device element bits back as uint16 (FP8 bytes widened)."""
+    if t.dtype == torch.uint8:
+        return t.cpu().numpy().astype(np.uint16)
     return t.cpu().numpy().view(np.uint16)
 
 
@@ -22,14 +28,14 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def new_cache(*, Hkv, Hq, D, T, max_seqs, max_blocks, comp_slots=None, raw_slots=None, compressed=True,
-              esc_cap=-1, perm_seed=0):
+              esc_cap=-1, perm_seed=0, fmt=oracle.BF16):
     from decode_attention_calibrate_amd import KVCache
     n_tiles = max_seqs * max_blocks * 2 * Hkv
     return KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=max_seqs,
                    max_blocks_per_seq=max_blocks,
                    num_comp_slots=(n_tiles if comp_slots is None else comp_slots) if compressed else 0,
                    num_raw_slots=(n_tiles if raw_slots is None else raw_slots), compressed=compressed,
-                   esc_cap_bytes=esc_cap, perm_seed=perm_seed)
+                   esc_cap_bytes=esc_cap, perm_seed=perm_seed, dtype=fmt)
 
 
 def row_rel_err(out_bits: np.ndarray, ref: np.ndarray) -> float:
@@ -45,7 +51,7 @@ def gpu_tile_bytes(cache, seq, blk, kv, h):
     assert e != 0xFFFFFFFF, "unallocated tile"
     slot = e & 0xFFFFFF
     if e >> 31:
-        n = cache.T * cache.D * 2
+        n = cache.T * cache.D * cache.EB
         return True, 0, cache.buffers["raw_pool"][slot * n:(slot + 1) * n].cpu().numpy()
     st = cache.slot_stride
     return False, (e >> 24) & 0x7F, cache.buffers["comp_pool"][slot * st:(slot + 1) * st].cpu().numpy()

@@ -50,16 +50,18 @@ def _sizes(K, p):
     return rc, list(sz), st.value, lib.kv_last_error().decode()
 
 
+@pytest.mark.parametrize("fmt", [oracle.BF16, oracle.E5M2, oracle.E4M3])
 @pytest.mark.parametrize("T,D", [(64, 128), (16, 128), (64, 64), (32, 128)])
-def test_slot_stride_matches_format(K, T, D):
+def test_slot_stride_matches_format(K, T, D, fmt):
     """The library's slot stride equals the stride of FORMAT v1 as the oracle lays it out."""
-    rc, sz, stride, _ = _sizes(K, _params(K, block_tokens=T, head_dim=D))
+    rc, sz, stride, _ = _sizes(K, _params(K, block_tokens=T, head_dim=D, dtype=fmt))
     assert rc == 0
-    lay = oracle.layout(oracle.Params(oracle.BF16, T, D, 16))
+    lay = oracle.layout(oracle.Params(fmt, T, D, 16))
+    eb = 2 if fmt == oracle.BF16 else 1
     assert stride == lay["stride"]
     assert sz[0] == 2048 * stride
-    assert sz[1] == 64 * T * D * 2
-    assert sz[2] == 2 * 2 * 8 * T * D * 2
+    assert sz[1] == 64 * T * D * eb == 64 * lay["raw_bytes"]
+    assert sz[2] == 2 * 2 * 8 * T * D * eb
     assert sz[3] == 4 * 8 * D
     assert sz[4] == 2 * 1024 * 2 * 8 * 4
     assert sz[5] == 2048 * 4 and sz[6] == 64 * 4 and sz[7] == 128
@@ -69,7 +71,7 @@ def test_slot_stride_matches_format(K, T, D):
     (dict(head_dim=96), -1), (dict(num_q_heads=12), -1), (dict(num_q_heads=8 * 17), -1),
     (dict(block_tokens=40), -1), (dict(esc_cap_bytes=24), -1), (dict(max_seqs=0), -1),
     (dict(num_comp_slots=0), -1), (dict(compressed=0, num_raw_slots=0), -1), (dict(dtype=7), -1),
-    (dict(dtype=1), -3), (dict(dtype=2), -3), (dict(group_tokens=8), -3), (dict(block_tokens=128), -3),
+    (dict(group_tokens=8), -3), (dict(block_tokens=128), -3),
     (dict(block_tokens=48), -3),
 ])
 def test_parameter_validation(K, kw, code):
