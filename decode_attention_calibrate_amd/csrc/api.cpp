@@ -283,7 +283,6 @@ int kv_attention_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_s
   if (ws_bytes < kv_attention_workspace_bytes(&c->p, n_seqs, n_splits))
     return fail(KVC_ESMALLWS, "workspace smaller than kv_attention_workspace_bytes()");
   if (((uintptr_t)ws_dev & 15u) || ((uintptr_t)q_dev & 15u)) return fail(KVC_EINVAL, "q and workspace must be 16-byte aligned");
-  if (c->G.fmt != KVC_BF16) return fail(KVC_EUNSUPPORTED, "decode attention over FP8 caches is not implemented yet");
   for (int i = 0; i < n_seqs; ++i)
     if (c->len[seq_ids_host[i]] < 1) return fail(KVC_EINVAL, "every listed sequence needs at least one token");
   const Geo& G = c->G;

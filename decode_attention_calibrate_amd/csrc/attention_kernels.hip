@@ -29,6 +29,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "codec_dev.h"
 #include "kvc_internal.h"
 
@@ -55,8 +57,21 @@ struct AttnArgs {
   int n_splits;
 };
 
-// Compile-time geometry of a compressed tile (FORMAT v1) for head_dim 32*NR and T = TT tokens.
-template <int NR, int TT>
+// Element format: 0 BF16, 1 FP8 E5M2, 2 FP8 E4M3 (kvc_dtype).
+template <int FMT>
+struct FmtT {
+  static constexpr int F = FMT == 0 ? 8 : (FMT == 1 ? 5 : 4);   // exponent bits
+  static constexpr int MB = FMT == 0 ? 7 : (FMT == 1 ? 2 : 3);  // mantissa bits
+  static constexpr int EB = FMT == 0 ? 2 : 1;                   // bytes per element
+  static constexpr int SMW = FMT == 0 ? 8 : (FMT == 1 ? 3 : 4); // SM words per pair of groups
+  // Rebuilt words of four tokens 4q..4q+3: BF16 pairs (4q, 4q+2), (4q+1, 4q+3) [interleaved];
+  // FP8 (converted to BF16) pairs (4q, 4q+1), (4q+2, 4q+3) [natural].
+  static constexpr bool NATURAL = FMT != 0;
+};
+
+// Compile-time geometry of a compressed tile (FORMAT v1) for head_dim 32*NR, T = TT tokens and
+// element format FMT.
+template <int NR, int TT, int FMT>
 struct TG {
   static constexpr int D = 32 * NR;
   static constexpr int NT = TT / 16;
@@ -64,9 +79,27 @@ struct TG {
   static constexpr int PW = NG / 32;
   static constexpr int CODE_OFF = (2 * PW * 4 + 15) / 16 * 16;
   static constexpr int SM_OFF = CODE_OFF + (TT * D * 3 / 8 + 15) / 16 * 16;
-  static constexpr int ESC_OFF = SM_OFF + (TT * D + 15) / 16 * 16;
+  static constexpr int ESC_OFF = SM_OFF + (TT * D * (1 + FmtT<FMT>::MB) / 8 + 15) / 16 * 16;
   static constexpr int RAW = TT * D;  // elements of a raw tile
 };
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two FP8 values (bytes 2*HI, 2*HI+1 of x) -> two BF16 (low half = the lower byte); exact.
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t x) {
+  if constexpr (FMT == 1) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(x, 1.0f, HI));
+  else return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI));
+}
+
+// Eight FP8 values (tokens or channels in order) -> an MFMA operand of eight BF16.
+template <int FMT>
+__device__ __forceinline__ uint4 fp8x8_to_operand(uint2 v) {
+  return make_uint4(fp8x2_to_bf16x2<FMT, false>(v.x), fp8x2_to_bf16x2<FMT, true>(v.x),
+                    fp8x2_to_bf16x2<FMT, false>(v.y), fp8x2_to_bf16x2<FMT, true>(v.y));
+}
+
+__device__ __forceinline__ uint2 ld64(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -98,7 +131,7 @@ struct TileRef {
   int valid;             // valid tokens in the group (0..16)
   int escu;              // escape bytes / 16 (compressed)
   const uint8_t* comp;   // compressed tile (clamped to slot 0 when unused: always dereferenceable)
-  const uint16_t* raw;   // raw tile or tail tile (always dereferenceable)
+  const uint8_t* raw;    // raw tile or tail tile, element bytes (always dereferenceable)
 };
 
 template <int TT>
@@ -108,7 +141,7 @@ __device__ __forceinline__ uint32_t load_entry(const AttnArgs& a, int seq, int L
   return a.B.table[table_index(a.G, seq, t / TT, kv, h)];
 }
 
-template <int NR, int TT>
+template <int NR, int TT, int FMT>
 __device__ __forceinline__ TileRef tile_ref(const AttnArgs& a, int seq, int L, int t, int kv, int h, uint32_t entry,
                                             uint32_t& flags) {
   TileRef r;
@@ -117,7 +150,7 @@ __device__ __forceinline__ TileRef tile_ref(const AttnArgs& a, int seq, int L, i
   r.valid = 0;
   r.escu = 0;
   r.comp = a.B.comp_pool;
-  r.raw = a.B.tail;
+  r.raw = reinterpret_cast<const uint8_t*>(a.B.tail);
   const int n_full = L / TT;
   if (t >= L) {
     r.tg = 0;
@@ -132,7 +165,7 @@ __device__ __forceinline__ TileRef tile_ref(const AttnArgs& a, int seq, int L, i
     r.valid = 16;
     if (entry & 0x80000000u) {
       r.kind = SRC_RAW;
-      r.raw = a.B.raw_pool + (size_t)slot * TG<NR, TT>::RAW;
+      r.raw = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * TG<NR, TT, FMT>::RAW * FmtT<FMT>::EB;
     } else {
       r.kind = SRC_COMP;
       r.comp = a.B.comp_pool + (size_t)slot * (uint32_t)a.G.stride;
@@ -142,24 +175,34 @@ __device__ __forceinline__ TileRef tile_ref(const AttnArgs& a, int seq, int L, i
     r.kind = SRC_RAW;
     r.tg = (t - n_full * TT) >> 4;
     r.valid = min(16, L - t);
-    r.raw = a.B.tail + tail_offset(a.G, seq, kv, h);
+    r.raw = reinterpret_cast<const uint8_t*>(a.B.tail) + tail_offset(a.G, seq, kv, h) * FmtT<FMT>::EB;
   }
   return r;
 }
 
 // Compressed bytes of one tile (K or V) held by one lane: tag words (lanes n < PW), escape
-// bytes (lanes n < escu, two 16-byte pieces), and sign/mantissa + code words of its NR pairs.
+// bytes (lanes n < escu, two 16-byte pieces), and sign/mantissa + code words of its NR pairs
+// (SM: 32 bytes per pair for BF16, 12 for E5M2, 16 for E4M3).
+template <int NR, int FMT>
+struct SmRegs {
+  uint32_t w[NR][FmtT<FMT>::SMW];
+};
 template <int NR>
+struct SmRegs<NR, 0> {  // BF16: two 16-byte pieces per pair (one per group)
+  uint4 v[NR][2];
+};
+
+template <int NR, int FMT>
 struct CRegs {
   uint32_t tE, tR;
   uint4 esc0, esc1;
-  uint4 sm[NR][2];
+  SmRegs<NR, FMT> sm;
   uint32_t cd[NR][3];
 };
 
-template <int NR, int TT>
-__device__ __forceinline__ void load_tile(const TileRef& r, int n, CRegs<NR>& c) {
-  using Q = TG<NR, TT>;
+template <int NR, int TT, int FMT>
+__device__ __forceinline__ void load_tile(const TileRef& r, int n, CRegs<NR, FMT>& c) {
+  using Q = TG<NR, TT, FMT>;
   const uint8_t* t = r.comp;
   c.tE = c.tR = 0;
   if (n < Q::PW) {
@@ -172,8 +215,16 @@ __device__ __forceinline__ void load_tile(const TileRef& r, int n, CRegs<NR>& c)
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     const int pr = r.tg * (Q::D / 2) + 16 * i + n;
-    c.sm[i][0] = ld128(t + Q::SM_OFF + 32 * pr);
-    c.sm[i][1] = ld128(t + Q::SM_OFF + 32 * pr + 16);
+    if constexpr (FMT == 0) {
+      c.sm.v[i][0] = ld128(t + Q::SM_OFF + 32 * pr);
+      c.sm.v[i][1] = ld128(t + Q::SM_OFF + 32 * pr + 16);
+    } else if constexpr (FMT == 1) {
+      const uint8_t* sp = t + Q::SM_OFF + 12 * pr;
+      c.sm.w[i][0] = ld32(sp); c.sm.w[i][1] = ld32(sp + 4); c.sm.w[i][2] = ld32(sp + 8);
+    } else {
+      const uint4 a = ld128(t + Q::SM_OFF + 16 * pr);
+      c.sm.w[i][0] = a.x; c.sm.w[i][1] = a.y; c.sm.w[i][2] = a.z; c.sm.w[i][3] = a.w;
+    }
     const uint8_t* cp = t + Q::CODE_OFF + 12 * pr;
     c.cd[i][0] = ld32(cp);
     c.cd[i][1] = ld32(cp + 4);
@@ -182,14 +233,15 @@ __device__ __forceinline__ void load_tile(const TileRef& r, int n, CRegs<NR>& c)
 }
 
 // Stage the escape bytes of this lane group's tile into its LDS area; return the exclusive
-// escape-plane prefix of tag word n (a wide group has 1 plane, a raw group 5).
-template <int NR>
-__device__ __forceinline__ uint32_t stage_escape(const CRegs<NR>& c, const TileRef& r, int n, uint8_t* esc_lds) {
+// escape-unit prefix of tag word n (a wide group has 1 unit, a raw group F - 3).
+template <int NR, int FMT>
+__device__ __forceinline__ uint32_t stage_escape(const CRegs<NR, FMT>& c, const TileRef& r, int n, uint8_t* esc_lds) {
   if (r.kind == SRC_COMP) {
     if (n < r.escu) *reinterpret_cast<uint4*>(esc_lds + 16 * n) = c.esc0;
     if (n + 16 < r.escu) *reinterpret_cast<uint4*>(esc_lds + 16 * (n + 16)) = c.esc1;
   }
-  const uint32_t cnt = __popc(c.tE) + 4u * __popc(c.tR);
+  // escape units per group: wide 1, raw F - 3 (the E plane counts 1 for both)
+  const uint32_t cnt = __popc(c.tE) + (uint32_t)(FmtT<FMT>::F - 4) * __popc(c.tR);
   return row_scan16(cnt) - cnt;
 }
 
@@ -203,49 +255,74 @@ __device__ __forceinline__ void init_esc_lut() {
 }
 
 // Rebuild the two groups of round i for lane n of lane group j.  bases packs b3[c0], b3[c1],
-// b4[c0], b4[c1]; below = (1 << 2n) - 1.  Output o[gi][0][q] = BF16 of tokens (4q, 4q+2),
-// o[gi][1][q] = (4q+1, 4q+3), low half first.
-template <int NR>
-__device__ __forceinline__ void rebuild_round(const CRegs<NR>& c, int i, int j, int n, int tg, uint32_t pfx,
+// b4[c0], b4[c1]; below = (1 << 2n) - 1.  Output, low half first: BF16 o[gi][0][q] = tokens
+// (4q, 4q+2), o[gi][1][q] = (4q+1, 4q+3); FP8 (converted exactly to BF16) o[gi][0][q] = tokens
+// (4q, 4q+1), o[gi][1][q] = (4q+2, 4q+3).
+template <int NR, int FMT>
+__device__ __forceinline__ void rebuild_round(const CRegs<NR, FMT>& c, int i, int j, int n, int tg, uint32_t pfx,
                                               uint32_t bases, const uint16_t* esc16, uint32_t below, uint32_t& bad,
                                               uint32_t o[2][2][4]) {
+  constexpr int RU = FmtT<FMT>::F - 3;  // escape units of a raw group
   const int w = tg * NR + i;  // tag word holding both groups of this pair
   const uint32_t Ew = (uint32_t)__shfl((int)c.tE, 16 * j + w);
   const uint32_t Rw = (uint32_t)__shfl((int)c.tR, 16 * j + w);
   const uint32_t Pw = (uint32_t)__shfl((int)pfx, 16 * j + w);
   bad |= Rw & ~Ew;
-  const uint32_t P0 = Pw + __popc(Ew & below) + 4u * __popc(Rw & below);
+  if constexpr (FMT == 2) bad |= Ew & ~Rw;  // no wide mode in a 4-bit exponent field
+  const uint32_t P0 = Pw + __popc(Ew & below) + (uint32_t)(RU - 1) * __popc(Rw & below);
   const uint32_t e2 = (Ew >> (2 * n)) & 3u, r2 = (Rw >> (2 * n)) & 3u;
   const uint32_t W0 = c.cd[i][0], W1 = c.cd[i][1], W2 = c.cd[i][2];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const uint32_t E = (e2 >> gi) & 1u, R = (r2 >> gi) & 1u;
-    const uint32_t P = gi ? P0 + (e2 & 1u) + 4u * (r2 & 1u) : P0;
+    const uint32_t P = gi ? P0 + (e2 & 1u) + (uint32_t)(RU - 1) * (r2 & 1u) : P0;
     const uint32_t b3 = (bases >> (8 * gi)) & 0xFFu, b4 = (bases >> (16 + 8 * gi)) & 0xFFu;
     const uint32_t H = perm_b32(0u, R ? 0u : (E ? b4 : b3), 0x00000000u);  // base in all four bytes
     const uint32_t plane0 = (uint32_t)esc16[P] & (0u - E);                  // read always, keep if escaped
-    const uint4 s4 = c.sm[i][gi];
-    const uint32_t smv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint32_t cs;
-      if (gi == 0) {
-        cs = q == 0 ? code_slot<0>(W0, W1, W2) : q == 1 ? code_slot<1>(W0, W1, W2)
-           : q == 2 ? code_slot<2>(W0, W1, W2) : code_slot<3>(W0, W1, W2);
-      } else {
-        cs = q == 0 ? code_slot<4>(W0, W1, W2) : q == 1 ? code_slot<5>(W0, W1, W2)
-           : q == 2 ? code_slot<6>(W0, W1, W2) : code_slot<7>(W0, W1, W2);
-      }
+      const int slot = 4 * gi + q;
+      const uint32_t cs = slot == 0 ? code_slot<0>(W0, W1, W2) : slot == 1 ? code_slot<1>(W0, W1, W2)
+                        : slot == 2 ? code_slot<2>(W0, W1, W2) : slot == 3 ? code_slot<3>(W0, W1, W2)
+                        : slot == 4 ? code_slot<4>(W0, W1, W2) : slot == 5 ? code_slot<5>(W0, W1, W2)
+                        : slot == 6 ? code_slot<6>(W0, W1, W2) : code_slot<7>(W0, W1, W2);
       const uint32_t Ev = H + cs + esc_lut[(plane0 >> (4 * q)) & 0xFu];
-      o[gi][0][q] = bitsel(0x7F807F80u, Ev << 7, perm_b32(smv[q], smv[q], 0x02020000u));
-      o[gi][1][q] = bitsel(0x7F807F80u, Ev >> 1, perm_b32(smv[q], smv[q], 0x03030101u));
+      if constexpr (FMT == 0) {
+        const uint4 s4 = c.sm.v[i][gi];
+        const uint32_t sv = q == 0 ? s4.x : q == 1 ? s4.y : q == 2 ? s4.z : s4.w;
+        o[gi][0][q] = bitsel(0x7F807F80u, Ev << 7, perm_b32(sv, sv, 0x02020000u));
+        o[gi][1][q] = bitsel(0x7F807F80u, Ev >> 1, perm_b32(sv, sv, 0x03030101u));
+      } else {
+        uint32_t Eq = Ev;
+        if constexpr (FMT == 1) {
+          if (R) Eq += esc_lut[((uint32_t)esc16[P + 1] >> (4 * q)) & 0xFu] << 1;  // raw: offset bit 4
+        }
+        uint32_t f, B;  // f: (sign << MB) | mantissa per byte lane; B: the four FP8 bytes
+        if constexpr (FMT == 1) {
+          const uint32_t S0 = c.sm.w[i][0], S1 = c.sm.w[i][1], S2 = c.sm.w[i][2];
+          f = slot == 0 ? code_slot<0>(S0, S1, S2) : slot == 1 ? code_slot<1>(S0, S1, S2)
+            : slot == 2 ? code_slot<2>(S0, S1, S2) : slot == 3 ? code_slot<3>(S0, S1, S2)
+            : slot == 4 ? code_slot<4>(S0, S1, S2) : slot == 5 ? code_slot<5>(S0, S1, S2)
+            : slot == 6 ? code_slot<6>(S0, S1, S2) : code_slot<7>(S0, S1, S2);
+          B = (Eq << 2) | (f & 0x03030303u) | ((f << 5) & 0x80808080u);
+        } else {
+          const uint32_t sw = c.sm.w[i][2 * gi + (q >> 1)];
+          const uint32_t y = perm_b32(sw, sw, (q & 1) ? 0x03030202u : 0x01010000u);
+          f = (y & 0x000F000Fu) | ((y >> 4) & 0x0F000F00u);
+          B = (Eq << 3) | (f & 0x07070707u) | ((f << 4) & 0x80808080u);
+        }
+        o[gi][0][q] = fp8x2_to_bf16x2<FMT, false>(B);
+        o[gi][1][q] = fp8x2_to_bf16x2<FMT, true>(B);
+      }
     }
-    if (R) {  // raw group (rare): base 0, add offset bits 4..7 into the exponent field
+    if constexpr (FMT == 0) {
+      if (R) {  // raw group (rare): base 0, add offset bits 4..7 into the exponent field
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t X = raw_high_nibbles(esc16[P + 1 + q]);
-        o[gi][0][q] |= (X << 7) & 0x7F807F80u;
-        o[gi][1][q] |= (X >> 1) & 0x7F807F80u;
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t X = raw_high_nibbles(esc16[P + 1 + q]);
+          o[gi][0][q] |= (X << 7) & 0x7F807F80u;
+          o[gi][1][q] |= (X >> 1) & 0x7F807F80u;
+        }
       }
     }
   }
@@ -376,9 +453,10 @@ __device__ __forceinline__ int group_token(int sb, int j) { return sb * kSB + 16
 
 // ------------------------------------------------------------------------------------------
 // Compressed cache.
-template <int NR, int TT>
+template <int NR, int TT, int FMT>
 __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_comp_kernel(AttnArgs a) {
-  using Q = TG<NR, TT>;
+  using Q = TG<NR, TT, FMT>;
+  constexpr bool NAT = FmtT<FMT>::NATURAL;
   constexpr int D = Q::D;
   extern __shared__ uint4 lds4[];
   const Geo& G = a.G;
@@ -414,17 +492,17 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   for (int i = 0; i < NR; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   if (ord.cnt > 0) {
-    CRegs<NR> cK, cV;
+    CRegs<NR, FMT> cK, cV;
     TileRef rK, rV;
     uint32_t eK = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 0, h);
     uint32_t eV = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 1, h);
-    rK = tile_ref<NR, TT>(a, seq, L, group_token(ord.at(0), j), 0, h, eK, flags);
-    load_tile<NR, TT>(rK, n, cK);
+    rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(0), j), 0, h, eK, flags);
+    load_tile<NR, TT, FMT>(rK, n, cK);
     for (int it = 0; it < ord.cnt; ++it) {
       const int sb = ord.at(it);
       // V bytes of this super-block load while K is rebuilt and scored
-      rV = tile_ref<NR, TT>(a, seq, L, group_token(sb, j), 1, h, eV, flags);
-      load_tile<NR, TT>(rV, n, cV);
+      rV = tile_ref<NR, TT, FMT>(a, seq, L, group_token(sb, j), 1, h, eV, flags);
+      load_tile<NR, TT, FMT>(rV, n, cV);
       if (it + 1 < ord.cnt) {
         eK = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), j), 0, h);
         eV = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), j), 1, h);
@@ -432,34 +510,54 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 
       // ---- K: rebuild into the LDS tile ----
       __syncthreads();
-      const uint32_t pfxK = stage_escape<NR>(cK, rK, n, esc_lds);
+      const uint32_t pfxK = stage_escape<NR, FMT>(cK, rK, n, esc_lds);
       __syncthreads();
       if (rK.kind == SRC_COMP) {
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
           uint32_t o[2][2][4];
-          rebuild_round<NR>(cK, i, j, n, rK.tg, pfxK, blds[i * 16 + n], esc16, below, bad, o);
+          rebuild_round<NR, FMT>(cK, i, j, n, rK.tg, pfxK, blds[i * 16 + n], esc16, below, bad, o);
           // transpose to token-major rows: token 16j + 4q + k gets the (c0, c0+1) word, taken
-          // from the low (k < 2) or high (k >= 2) halves of the two channels' token-pair words
+          // from one half of each of the two channels' token-pair words (BF16: word k & 1, half
+          // k >> 1; FP8: word k >> 1, half k & 1)
           const int chunk = 4 * i + (n >> 2), off = 4 * (n & 3);
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int rk = 16 * j + k;  // row of quad 0; quad q adds 4q rows (same swizzle)
             uint8_t* p = klds + rk * 2 * D + ((chunk ^ swz(rk)) << 4) + off;
+            const int wi = NAT ? (k >> 1) : (k & 1);
+            const uint32_t sel = (NAT ? (k & 1) : (k >> 1)) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint32_t w = perm_b32(o[1][k & 1][q], o[0][k & 1][q], (k & 2) ? 0x07060302u : 0x05040100u);
-              *reinterpret_cast<uint32_t*>(p + q * 4 * 2 * D) = w;
-            }
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<uint32_t*>(p + q * 4 * 2 * D) = perm_b32(o[1][wi][q], o[0][wi][q], sel);
           }
         }
       }
-      // Raw K groups (raw tiles, the tail) go straight from memory into their LDS rows with
+      // Raw K groups (raw tiles, the tail).  BF16: straight from memory into their LDS rows with
       // LDS-DMA loads: one instruction fills RPI whole rows (64 lanes x 16 bytes), each lane
       // fetching the row piece whose swizzled position is its own, so a group costs one memory
-      // round trip and no registers.  Rows past the valid tokens hold stale but finite-or-not
-      // data; their scores are masked before the softmax.
-      {
+      // round trip and no registers.  FP8: eight-element pieces through registers, converted
+      // to BF16 on the way.  Rows past the valid tokens hold stale but finite-or-not data;
+      // their scores are masked before the softmax.
+      if constexpr (FMT != 0) {
+        if (rK.kind == SRC_RAW) {
+          constexpr int NCH = D / 8;  // 8-element pieces per row; lane n takes pieces n, n+16, ...
+#pragma unroll
+          for (int m0 = 0; m0 < NCH; m0 += 4) {
+            uint2 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int k = n + 16 * (m0 + u), rr = k / NCH, chunk = k % NCH;
+              v[u] = ld64(rK.raw + (size_t)(rK.tg * 16 + rr) * D + 8 * chunk);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int k = n + 16 * (m0 + u), rr = k / NCH, chunk = k % NCH, row = 16 * j + rr;
+              *reinterpret_cast<uint4*>(klds + row * 2 * D + ((chunk ^ swz(row)) << 4)) = fp8x8_to_operand<FMT>(v[u]);
+            }
+          }
+        }
+      } else {
         constexpr int RPI = 512 / D;  // rows per instruction
         constexpr int LPR = D / 8;    // lanes (16-byte pieces) per row
         bool dma = false;
@@ -508,24 +606,24 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       const float alpha = softmax_update(s, m, l);
       rescale_acc<NR>(acc, alpha, j);
       uint4 phi[2], plo[2];
-      pack_p<true>(s, phi, plo);
+      pack_p<!NAT>(s, phi, plo);
 
       // K bytes of the next super-block load while V is rebuilt and accumulated
       if (it + 1 < ord.cnt) {
-        rK = tile_ref<NR, TT>(a, seq, L, group_token(ord.at(it + 1), j), 0, h, eK, flags);
-        load_tile<NR, TT>(rK, n, cK);
+        rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(it + 1), j), 0, h, eK, flags);
+        load_tile<NR, TT, FMT>(rK, n, cK);
       }
 
       // ---- V: rebuild straight into B operands ----
       __syncthreads();
-      const uint32_t pfxV = stage_escape<NR>(cV, rV, n, esc_lds);
+      const uint32_t pfxV = stage_escape<NR, FMT>(cV, rV, n, esc_lds);
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         uint4 bv[2][2];
         if (rV.kind == SRC_COMP) {
           uint32_t o[2][2][4];
-          rebuild_round<NR>(cV, i, j, n, rV.tg, pfxV, blds[(NR + i) * 16 + n], esc16, below, bad, o);
+          rebuild_round<NR, FMT>(cV, i, j, n, rV.tg, pfxV, blds[(NR + i) * 16 + n], esc16, below, bad, o);
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
             bv[x][0] = make_uint4(o[x][0][0], o[x][1][0], o[x][0][1], o[x][1][1]);
@@ -537,9 +635,14 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               const int ch = 32 * i + 2 * n + x;
-              const uint4 v = mask_tokens(ld128(rV.raw + (size_t)ch * TT + rV.tg * 16 + 8 * e), rV.valid - 8 * e);
-              bv[x][e] = make_uint4(perm_b32(v.y, v.x, 0x05040100u), perm_b32(v.y, v.x, 0x07060302u),
-                                    perm_b32(v.w, v.z, 0x05040100u), perm_b32(v.w, v.z, 0x07060302u));
+              const size_t off = (size_t)ch * TT + rV.tg * 16 + 8 * e;  // elements
+              if constexpr (FMT == 0) {  // natural order -> the interleaved order of P
+                const uint4 v = mask_tokens(ld128(reinterpret_cast<const uint16_t*>(rV.raw) + off), rV.valid - 8 * e);
+                bv[x][e] = make_uint4(perm_b32(v.y, v.x, 0x05040100u), perm_b32(v.y, v.x, 0x07060302u),
+                                      perm_b32(v.w, v.z, 0x05040100u), perm_b32(v.w, v.z, 0x07060302u));
+              } else {
+                bv[x][e] = mask_tokens(fp8x8_to_operand<FMT>(ld64(rV.raw + off)), rV.valid - 8 * e);
+              }
             }
         } else {
 #pragma unroll
@@ -563,37 +666,53 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 // ------------------------------------------------------------------------------------------
 // Uncompressed cache (every tile raw): the speedup baseline.  K rows are loaded straight into
 // QK A operands and V straight into PV B operands (no LDS), with the same K/V phase pipelining.
-template <int NR>
+// Operand pieces as loaded: eight BF16 (uint4) or eight FP8 (uint2, converted at use).
+template <int FMT>
+using Piece = typename std::conditional<FMT == 0, uint4, uint2>::type;
+
+template <int FMT>
+__device__ __forceinline__ Piece<FMT> ld_piece(const uint8_t* base, size_t elem) {
+  if constexpr (FMT == 0) return ld128(reinterpret_cast<const uint16_t*>(base) + elem);
+  else return ld64(base + elem);
+}
+template <int FMT>
+__device__ __forceinline__ uint4 operand(const Piece<FMT>& v) {
+  if constexpr (FMT == 0) return v;
+  else return fp8x8_to_operand<FMT>(v);
+}
+
+template <int NR, int FMT>
 struct RawK {
-  uint4 ka[4][NR];
+  Piece<FMT> ka[4][NR];
 };
-template <int NR>
+template <int NR, int FMT>
 struct RawV {
-  uint4 vb[NR][2][2];
+  Piece<FMT> vb[NR][2][2];
 };
 
-template <int NR, int TT>
-__device__ __forceinline__ void raw_load_k(const TileRef& r, int n, int j, RawK<NR>& k) {
+template <int NR, int TT, int FMT>
+__device__ __forceinline__ void raw_load_k(const TileRef& r, int n, int j, RawK<NR, FMT>& k) {
   constexpr int D = 32 * NR;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int rr = 4 * rb + (n & 3);
 #pragma unroll
-    for (int ks = 0; ks < NR; ++ks) k.ka[rb][ks] = ld128(r.raw + (size_t)(r.tg * 16 + rr) * D + 32 * ks + 8 * j);
+    for (int ks = 0; ks < NR; ++ks) k.ka[rb][ks] = ld_piece<FMT>(r.raw, (size_t)(r.tg * 16 + rr) * D + 32 * ks + 8 * j);
   }
 }
 
-template <int NR, int TT>
-__device__ __forceinline__ void raw_load_v(const TileRef& r, int n, RawV<NR>& v) {
+template <int NR, int TT, int FMT>
+__device__ __forceinline__ void raw_load_v(const TileRef& r, int n, RawV<NR, FMT>& v) {
 #pragma unroll
   for (int i = 0; i < NR; ++i)
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) v.vb[i][x][e] = ld128(r.raw + (size_t)(32 * i + 2 * n + x) * TT + r.tg * 16 + 8 * e);
+      for (int e = 0; e < 2; ++e)
+        v.vb[i][x][e] = ld_piece<FMT>(r.raw, (size_t)(32 * i + 2 * n + x) * TT + r.tg * 16 + 8 * e);
 }
 
-template <int NR, int TT>
+template <int NR, int TT, int FMT>
 __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_raw_kernel(AttnArgs a) {
   constexpr int D = 32 * NR;
   const Geo& G = a.G;
@@ -614,17 +733,17 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   for (int i = 0; i < NR; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   if (ord.cnt > 0) {
-    RawK<NR> ck;
-    RawV<NR> cv;
+    RawK<NR, FMT> ck;
+    RawV<NR, FMT> cv;
     const int jr = n >> 2;  // token group of this lane's QK A-operand rows
     uint32_t eK = load_entry<TT>(a, seq, L, group_token(ord.at(0), jr), 0, h);
     uint32_t eV = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 1, h);
-    TileRef rK = tile_ref<NR, TT>(a, seq, L, group_token(ord.at(0), jr), 0, h, eK, flags);
-    raw_load_k<NR, TT>(rK, n, j, ck);
+    TileRef rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(0), jr), 0, h, eK, flags);
+    raw_load_k<NR, TT, FMT>(rK, n, j, ck);
     for (int it = 0; it < ord.cnt; ++it) {
       const int sb = ord.at(it);
-      const TileRef rV = tile_ref<NR, TT>(a, seq, L, group_token(sb, j), 1, h, eV, flags);
-      raw_load_v<NR, TT>(rV, n, cv);
+      const TileRef rV = tile_ref<NR, TT, FMT>(a, seq, L, group_token(sb, j), 1, h, eV, flags);
+      raw_load_v<NR, TT, FMT>(rV, n, cv);
       if (it + 1 < ord.cnt) {
         eK = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), jr), 0, h);
         eV = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), j), 1, h);
@@ -638,7 +757,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
         f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
         const bool rowok = 4 * rb + (n & 3) < rK.valid;
 #pragma unroll
-        for (int ks = 0; ks < NR; ++ks) cc = mfma16(rowok ? ck.ka[rb][ks] : make_uint4(0, 0, 0, 0), qb[ks], cc);
+        for (int ks = 0; ks < NR; ++ks)
+          cc = mfma16(rowok ? operand<FMT>(ck.ka[rb][ks]) : make_uint4(0, 0, 0, 0), qb[ks], cc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[4 * rb + r] = (4 * rb + r < valid) ? cc[r] * a.sl2 : -INFINITY;
       }
@@ -647,8 +767,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       uint4 phi[2], plo[2];
       pack_p<false>(s, phi, plo);
       if (it + 1 < ord.cnt) {
-        rK = tile_ref<NR, TT>(a, seq, L, group_token(ord.at(it + 1), jr), 0, h, eK, flags);
-        raw_load_k<NR, TT>(rK, n, j, ck);
+        rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(it + 1), jr), 0, h, eK, flags);
+        raw_load_k<NR, TT, FMT>(rK, n, j, ck);
       }
 #pragma unroll
       for (int i = 0; i < NR; ++i)
@@ -656,7 +776,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
         for (int x = 0; x < 2; ++x)
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const uint4 v = mask_tokens(cv.vb[i][x][e], rV.valid - 8 * e);
+            const uint4 v = mask_tokens(operand<FMT>(cv.vb[i][x][e]), rV.valid - 8 * e);
             acc[i][x] = mfma16(phi[e], v, acc[i][x]);
             acc[i][x] = mfma16(plo[e], v, acc[i][x]);
           }
@@ -740,27 +860,32 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(int Hq, int D,
   }
 }
 
-template <int NR, int TT>
+template <int NR, int TT, int FMT>
 int launch_attn(const AttnArgs& a, int n_seqs, void* stream) {
   const dim3 grid(a.n_splits, a.G.Hkv, n_seqs);
   if (a.G.compressed) {
     const size_t lds = (size_t)kSB * (32 * NR) * 2 + (size_t)4 * max(a.G.esc_cap, 16) +
                        (size_t)a.G.g * (32 * NR) * 2 + (size_t)2 * NR * 16 * 4;
-    hipLaunchKernelGGL((attn_comp_kernel<NR, TT>), grid, dim3(kWave), lds, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((attn_comp_kernel<NR, TT, FMT>), grid, dim3(kWave), lds, (hipStream_t)stream, a);
   } else {
-    hipLaunchKernelGGL((attn_raw_kernel<NR, TT>), grid, dim3(kWave), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((attn_raw_kernel<NR, TT, FMT>), grid, dim3(kWave), 0, (hipStream_t)stream, a);
   }
   return (int)hipGetLastError();
 }
 
-template <int NR>
+template <int NR, int FMT>
 int launch_attn_t(const AttnArgs& a, int n_seqs, void* stream) {
   switch (a.G.T) {
-    case 16: return launch_attn<NR, 16>(a, n_seqs, stream);
-    case 32: return launch_attn<NR, 32>(a, n_seqs, stream);
-    case 64: return launch_attn<NR, 64>(a, n_seqs, stream);
+    case 16: return launch_attn<NR, 16, FMT>(a, n_seqs, stream);
+    case 32: return launch_attn<NR, 32, FMT>(a, n_seqs, stream);
+    case 64: return launch_attn<NR, 64, FMT>(a, n_seqs, stream);
     default: return (int)hipErrorInvalidValue;
   }
+}
+
+template <int FMT>
+int launch_attn_f(const AttnArgs& a, int n_seqs, void* stream) {
+  return (a.G.D == 128) ? launch_attn_t<4, FMT>(a, n_seqs, stream) : launch_attn_t<2, FMT>(a, n_seqs, stream);
 }
 
 }  // namespace
@@ -776,7 +901,12 @@ int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& S, 
   a.ws_ml = ws_ml;
   a.sl2 = scale * 1.4426950408889634f;
   a.n_splits = n_splits;
-  return (G.D == 128) ? launch_attn_t<4>(a, S.n, stream) : launch_attn_t<2>(a, S.n, stream);
+  switch (G.fmt) {
+    case 0: return launch_attn_f<0>(a, S.n, stream);
+    case 1: return launch_attn_f<1>(a, S.n, stream);
+    case 2: return launch_attn_f<2>(a, S.n, stream);
+    default: return (int)hipErrorInvalidValue;
+  }
 }
 
 int launch_combine(const Geo& G, int n_seqs, int n_splits, const float* ws_acc, const float* ws_ml, uint16_t* out,
