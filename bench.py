@@ -51,6 +51,11 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep", type=str, default="", help="comma-separated split counts to time (extra)")
     ap.add_argument("--probe", action="store_true", help="also time plain HBM copy / read kernels (torch)")
+    ap.add_argument("--extra", type=str, default="fp8,paged",
+                    help="comma list of extra workloads measured after the headline one: fp8 (the 64K layer in "
+                         "FP8 E5M2 and E4M3), paged (32-sequence paged serving mix); '' for none")
+    ap.add_argument("--extra-steps", type=int, default=48)
+    ap.add_argument("--paged-splits", type=int, default=16)
     return ap.parse_args()
 
 
@@ -251,9 +256,99 @@ def main():
         "sweep_attention_us": sweep or None,
         "hbm_probe": probe,
     }
+    extras = [x for x in args.extra.split(",") if x]
+    if extras:
+        del comp, raw
+        torch.cuda.empty_cache()
+    if "fp8" in extras:
+        result["fp8_64k"] = {name: extra_steps(torch, K, synth, synth.config(4, fmt), args, splits=S)
+                             for name, fmt in (("e5m2", synth.E5M2), ("e4m3", synth.E4M3))}
+    if "paged" in extras:
+        result["paged_mix"] = extra_steps(torch, K, synth, synth.config(3), args, splits=args.paged_splits, layers=2)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, k0, v0)
     print(json.dumps(result), flush=True)
+
+
+def extra_steps(torch, K, synth, cfg, args, splits, layers=4):
+    """Decode steps of another workload: every step appends one token to each sequence and runs
+    split attention plus the merge over all sequences, on `layers` rotated layer caches;
+    compressed and uncompressed caches timed the same way.  Returns per-kernel and per-step
+    medians, the codec ratio and the attention speedup.  Sequences of the paged mix take their
+    tokens from one 32K-token stream (prefixes of it), which keeps input generation short."""
+    T, D, Hkv, Hq, B = cfg.T, cfg.D, cfg.Hkv, cfg.Hq, cfg.n_seqs
+    fmt = cfg.fmt
+    lens = list(cfg.context)
+    g = synth.LayerGen(cfg)
+    pool_k, pool_v = g.tokens(max(lens))
+    if fmt == synth.BF16:
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    else:
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).astype(np.uint8)).cuda()
+    steps = args.extra_steps
+    warm = 4
+    per_layer = (steps + warm + layers - 1) // layers + 1
+    kn, vn = g.tokens(per_layer * layers * B)
+    k_new = dev(kn.reshape(layers, per_layer, B, 1, Hkv, D))
+    v_new = dev(vn.reshape(layers, per_layer, B, 1, Hkv, D))
+    q = dev(synth.queries(cfg)) if fmt == synth.BF16 else \
+        torch.from_numpy(np.ascontiguousarray(synth.queries(cfg)).view(np.int16)).cuda()
+    max_blocks = (max(lens) + per_layer) // T + 2
+    n_tiles = B * max_blocks * 2 * Hkv
+    ids = list(range(B))
+    log(f"[bench] {cfg.name}: building {layers} compressed + {layers} uncompressed layers ({sum(lens)} tokens each)")
+
+    def make(compressed):
+        c = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=B,
+                      max_blocks_per_seq=max_blocks, num_comp_slots=n_tiles if compressed else 0,
+                      num_raw_slots=1024 if compressed else n_tiles, compressed=compressed, perm_seed=11, dtype=fmt)
+        c.calibrate(dev(pool_k[:cfg.n_cal]), dev(pool_v[:cfg.n_cal]))
+        for sid, L in enumerate(lens):
+            c.append([sid], dev(pool_k[None, :L]), dev(pool_v[None, :L]))
+        return c
+
+    out = torch.empty((B, Hq, D), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {"workload": cfg.name, "n_seqs": B, "tokens": sum(lens), "block_tokens": T, "n_splits": splits,
+           "layers_rotated": layers, "steps": steps}
+    for name, compressed in (("compressed", True), ("uncompressed", False)):
+        caches = [make(compressed) for _ in range(layers)]
+        ws = caches[0].workspace(B, splits)
+        torch.cuda.synchronize()
+        if compressed:
+            flags, st = caches[0].status()
+            n_grp = T * D // 16
+            mb = {synth.BF16: 7, synth.E5M2: 2, synth.E4M3: 3}[fmt]
+            eb = 2 if fmt == synth.BF16 else 1
+            payload = (2 * n_grp + 3 * T * D + (1 + mb) * T * D) // 8
+            comp_bytes = st["comp_tiles"] * payload + st["esc_bytes"] + st["raw_tiles"] * T * D * eb
+            res["codec_ratio"] = round((st["comp_tiles"] + st["raw_tiles"]) * T * D * eb / comp_bytes, 4)
+            res["compressed_kv_bytes"] = comp_bytes
+        ev = []
+        for i in range(warm + steps):
+            li, pos = i % layers, i // layers
+            c = caches[li]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+            c.append(ids, k_new[li, pos], v_new[li, pos])
+            e[1].record(stream)
+            c.attention_partials(ids, q, cfg.scale, splits, ws)
+            e[2].record(stream)
+            c.attention_combine(B, splits, ws, out)
+            e[3].record(stream)
+            if i >= warm:
+                ev.append(e)
+        torch.cuda.synchronize()
+        med = lambda a, b: float(np.median([x[a].elapsed_time(x[b]) * 1e3 for x in ev]))
+        res[name] = {"attention_us": round(med(1, 2), 2), "append_us": round(med(0, 1), 2),
+                     "combine_us": round(med(2, 3), 2), "step_us": round(med(0, 3), 2)}
+        del caches, ws
+        torch.cuda.empty_cache()
+    res["speedup_attention"] = round(res["uncompressed"]["attention_us"] / res["compressed"]["attention_us"], 4)
+    res["speedup_step"] = round(res["uncompressed"]["step_us"] / res["compressed"]["step_us"], 4)
+    res["effective_GBps"] = round(res["compressed_kv_bytes"] / (res["compressed"]["attention_us"] * 1e-6) / 1e9, 1)
+    log(f"[bench] {cfg.name}: {res}")
+    return res
 
 
 def kernel_source_digest():
