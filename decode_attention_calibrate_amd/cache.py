@@ -132,10 +132,14 @@ class KVCache:
         L.check(self.lib.kv_attention_partials(self.handle, ids, len(seq_ids), _ptr(q), float(scale), n_splits,
                                                _ptr(ws), ws.numel(), self._stream()))
 
-    def attention_combine(self, n_seqs: int, n_splits: int, ws: torch.Tensor, out: torch.Tensor):
-        self._check_out(out, n_seqs)
-        L.check(self.lib.kv_attention_combine(self.handle, n_seqs, n_splits, _ptr(ws), ws.numel(), _ptr(out),
-                                              self._stream()))
+    def attention_combine(self, seq_ids, q: torch.Tensor, scale: float, n_splits: int, ws: torch.Tensor,
+                          out: torch.Tensor):
+        n = len(seq_ids)
+        self._check_q(q, n)
+        self._check_out(out, n)
+        ids = (ctypes.c_int32 * n)(*seq_ids)
+        L.check(self.lib.kv_attention_combine(self.handle, ids, n, _ptr(q), float(scale), n_splits, _ptr(ws),
+                                              ws.numel(), _ptr(out), self._stream()))
         return out
 
     # ---- bookkeeping ----

@@ -273,8 +273,9 @@ size_t kv_attention_workspace_bytes(const kvc_params* p, int32_t n_seqs, int32_t
   return (size_t)n_seqs * p->num_q_heads * n_splits * ((size_t)p->head_dim + 2) * 4;
 }
 
-int kv_attention_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev, float scale,
-                          int32_t n_splits, void* ws_dev, size_t ws_bytes, void* stream) {
+// Shared argument checks of the attention calls.
+static int check_attention_args(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
+                                int32_t n_splits, const void* ws_dev, size_t ws_bytes) {
   if (!c) return fail(KVC_EINVAL, "cache is NULL");
   int rc = check_seq_ids(c, seq_ids_host, n_seqs);
   if (rc != KVC_OK) return rc;
@@ -285,6 +286,13 @@ int kv_attention_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_s
   if (((uintptr_t)ws_dev & 15u) || ((uintptr_t)q_dev & 15u)) return fail(KVC_EINVAL, "q and workspace must be 16-byte aligned");
   for (int i = 0; i < n_seqs; ++i)
     if (c->len[seq_ids_host[i]] < 1) return fail(KVC_EINVAL, "every listed sequence needs at least one token");
+  return KVC_OK;
+}
+
+int kv_attention_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev, float scale,
+                          int32_t n_splits, void* ws_dev, size_t ws_bytes, void* stream) {
+  int rc = check_attention_args(c, seq_ids_host, n_seqs, q_dev, n_splits, ws_dev, ws_bytes);
+  if (rc != KVC_OK) return rc;
   const Geo& G = c->G;
   float* acc = (float*)ws_dev;
   float* ml = acc + (size_t)n_seqs * G.Hq * n_splits * G.D;
@@ -293,7 +301,7 @@ int kv_attention_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_s
     S.n = std::min(kvc::kMaxSeqsPerLaunch, n_seqs - s0);
     for (int i = 0; i < S.n; ++i) {
       S.ids[i] = seq_ids_host[s0 + i];
-      S.lens[i] = c->len[S.ids[i]];
+      S.lens[i] = c->len[S.ids[i]] / G.T * G.T;  // the finished blocks; the merge adds the tail
     }
     rc = hip_fail(kvc::launch_attention_partials(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale,
                                                  n_splits, acc + (size_t)s0 * G.Hq * n_splits * G.D,
@@ -304,17 +312,28 @@ int kv_attention_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_s
   return KVC_OK;
 }
 
-int kv_attention_combine(kvc_cache* c, int32_t n_seqs, int32_t n_splits, const void* ws_dev, size_t ws_bytes,
-                         void* out_dev, void* stream) {
-  if (!c) return fail(KVC_EINVAL, "cache is NULL");
-  if (n_seqs < 1 || n_splits < 1 || n_splits > 1024) return fail(KVC_EINVAL, "bad n_seqs or n_splits");
-  if (!ws_dev || !out_dev) return fail(KVC_EINVAL, "workspace and out must not be NULL");
-  if (ws_bytes < kv_attention_workspace_bytes(&c->p, n_seqs, n_splits))
-    return fail(KVC_ESMALLWS, "workspace smaller than kv_attention_workspace_bytes()");
+int kv_attention_combine(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev, float scale,
+                         int32_t n_splits, const void* ws_dev, size_t ws_bytes, void* out_dev, void* stream) {
+  int rc = check_attention_args(c, seq_ids_host, n_seqs, q_dev, n_splits, ws_dev, ws_bytes);
+  if (rc != KVC_OK) return rc;
+  if (!out_dev) return fail(KVC_EINVAL, "out must not be NULL");
   const Geo& G = c->G;
   const float* acc = (const float*)ws_dev;
   const float* ml = acc + (size_t)n_seqs * G.Hq * n_splits * G.D;
-  return hip_fail(kvc::launch_combine(G, n_seqs, n_splits, acc, ml, (uint16_t*)out_dev, stream), "launch combine");
+  for (int s0 = 0; s0 < n_seqs; s0 += kvc::kMaxSeqsPerLaunch) {
+    SeqList S;
+    S.n = std::min(kvc::kMaxSeqsPerLaunch, n_seqs - s0);
+    for (int i = 0; i < S.n; ++i) {
+      S.ids[i] = seq_ids_host[s0 + i];
+      S.lens[i] = c->len[S.ids[i]];
+    }
+    rc = hip_fail(kvc::launch_combine(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale, n_splits,
+                                      acc + (size_t)s0 * G.Hq * n_splits * G.D, ml + (size_t)s0 * G.Hq * n_splits * 2,
+                                      (uint16_t*)out_dev + (size_t)s0 * G.Hq * G.D, stream),
+                  "launch combine");
+    if (rc != KVC_OK) return rc;
+  }
+  return KVC_OK;
 }
 
 int kv_decode_attention(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev, float scale,
@@ -322,7 +341,7 @@ int kv_decode_attention(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seq
   if (!out_dev) return fail(KVC_EINVAL, "out must not be NULL");
   const int rc = kv_attention_partials(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, stream);
   if (rc != KVC_OK) return rc;
-  return kv_attention_combine(c, n_seqs, n_splits, ws_dev, ws_bytes, out_dev, stream);
+  return kv_attention_combine(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, out_dev, stream);
 }
 
 int kv_release_seq(kvc_cache* c, int32_t seq, void* stream) {

@@ -4,7 +4,8 @@
 // Method: page "GAAC: Lossless KV Compression for Bandwidth-Efficient LLM Inference on Personal
 // Devices", §3.2 -- the kernel reads compressed tiles and rebuilds only the values attention
 // needs on chip (no decompressed copy of the cache in HBM); compressed blocks, raw blocks and
-// the uncompressed tail share one softmax normalisation.
+// the uncompressed tail share one softmax normalisation.  The split kernels cover the finished
+// blocks; the merge kernel adds the tail.
 //
 // Work decomposition (one 64-lane wave per workgroup):
 //   grid = (split, kv-head, sequence).  A split walks a contiguous range of 64-token
@@ -126,56 +127,47 @@ __device__ __forceinline__ uint32_t row_scan16(uint32_t v) {
 
 // Where the 16-token group starting at token t of one (sequence, K|V, head) lives.
 struct TileRef {
-  int kind;              // SRC_COMP, SRC_RAW (raw tile or tail), SRC_NONE
+  int kind;              // SRC_COMP, SRC_RAW (raw tile), SRC_NONE
   int tg;                // token group inside the tile
-  int valid;             // valid tokens in the group (0..16)
   int escu;              // escape bytes / 16 (compressed)
-  const uint8_t* comp;   // compressed tile (clamped to slot 0 when unused: always dereferenceable)
-  const uint8_t* raw;    // raw tile or tail tile, element bytes (always dereferenceable)
+  const uint8_t* p;      // the compressed or raw tile; for SRC_NONE a dummy tile-sized area (the
+                         // tail buffer), so every load a kernel issues from it stays in bounds
+  __device__ __forceinline__ int valid() const { return kind == SRC_NONE ? 0 : 16; }
 };
 
+// L here is the token count of the finished blocks (a multiple of T): the tail is merged in
+// by combine_kernel.
 template <int TT>
 __device__ __forceinline__ uint32_t load_entry(const AttnArgs& a, int seq, int L, int t, int kv, int h) {
-  const int n_full = L / TT;
-  if (t >= n_full * TT) return kUnallocated;
+  if (t >= L) return kUnallocated;
   return a.B.table[table_index(a.G, seq, t / TT, kv, h)];
 }
 
+// Status bit 4 if any lane's group inside the finished blocks has no table entry.  Called in
+// wave-uniform control flow; the result is wave-uniform (kept in a scalar register).
+__device__ __forceinline__ uint32_t missing_flag(int L, int t, uint32_t entry) {
+  return __builtin_amdgcn_ballot_w64(t < L && entry == kUnallocated) ? 4u : 0u;
+}
+
 template <int NR, int TT, int FMT>
-__device__ __forceinline__ TileRef tile_ref(const AttnArgs& a, int seq, int L, int t, int kv, int h, uint32_t entry,
-                                            uint32_t& flags) {
+__device__ __forceinline__ TileRef tile_ref(const AttnArgs& a, int seq, int L, int t, int kv, int h, uint32_t entry) {
   TileRef r;
   r.kind = SRC_NONE;
   r.tg = (t % TT) >> 4;
-  r.valid = 0;
   r.escu = 0;
-  r.comp = a.B.comp_pool;
-  r.raw = reinterpret_cast<const uint8_t*>(a.B.tail);
-  const int n_full = L / TT;
-  if (t >= L) {
+  r.p = reinterpret_cast<const uint8_t*>(a.B.tail);
+  if (t >= L || entry == kUnallocated) {  // past the finished blocks, or missing (missing_flag)
     r.tg = 0;
     return r;
   }
-  if (t < n_full * TT) {
-    if (entry == kUnallocated) {
-      flags |= 4u;
-      return r;
-    }
-    const uint32_t slot = entry & 0x00FFFFFFu;
-    r.valid = 16;
-    if (entry & 0x80000000u) {
-      r.kind = SRC_RAW;
-      r.raw = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * TG<NR, TT, FMT>::RAW * FmtT<FMT>::EB;
-    } else {
-      r.kind = SRC_COMP;
-      r.comp = a.B.comp_pool + (size_t)slot * (uint32_t)a.G.stride;
-      r.escu = (int)((entry >> 24) & 0x7Fu);
-    }
-  } else {
+  const uint32_t slot = entry & 0x00FFFFFFu;
+  if (entry & 0x80000000u) {
     r.kind = SRC_RAW;
-    r.tg = (t - n_full * TT) >> 4;
-    r.valid = min(16, L - t);
-    r.raw = reinterpret_cast<const uint8_t*>(a.B.tail) + tail_offset(a.G, seq, kv, h) * FmtT<FMT>::EB;
+    r.p = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * TG<NR, TT, FMT>::RAW * FmtT<FMT>::EB;
+  } else {
+    r.kind = SRC_COMP;
+    r.p = a.B.comp_pool + (size_t)slot * (uint32_t)a.G.stride;
+    r.escu = (int)((entry >> 24) & 0x7Fu);
   }
   return r;
 }
@@ -203,7 +195,7 @@ struct CRegs {
 template <int NR, int TT, int FMT>
 __device__ __forceinline__ void load_tile(const TileRef& r, int n, CRegs<NR, FMT>& c) {
   using Q = TG<NR, TT, FMT>;
-  const uint8_t* t = r.comp;
+  const uint8_t* t = r.p;  // a raw or dummy tile is large enough for every load below
   c.tE = c.tR = 0;
   if (n < Q::PW) {
     c.tE = ld32(t + 4 * n);
@@ -418,9 +410,10 @@ __device__ __forceinline__ uint4 mask_tokens(uint4 v, int keep) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Super-blocks [sb0, sb1) of split `split`: the full 64-token super-blocks are dealt out as
-// evenly as possible (the first nfull % n_splits splits take one more), and the last split also
-// takes the partial last super-block, if any.  Its share of full ones is never above the others',
+// Super-blocks [sb0, sb1) of split `split` (L = tokens of the finished blocks): the full 64-token
+// super-blocks are dealt out as evenly as possible (the first nfull % n_splits splits take one
+// more), and the last split also takes the partial last super-block, if any (blocks of T < 64
+// tokens that do not fill one).  Its share of full ones is never above the others',
 // so a length just past a multiple of 64 * n_splits puts one extra super-block on a few splits
 // instead of on all of them.
 __device__ __forceinline__ void split_range(int L, int n_splits, int split, int& sb0, int& sb1) {
@@ -432,7 +425,7 @@ __device__ __forceinline__ void split_range(int L, int n_splits, int split, int&
 
 // Visit order of a split's super-blocks: the split holding the partial last super-block takes
 // it first, while its first full super-block's bytes are still in flight, instead of adding it
-// (raw tail data, a chain of dependent reads) to the end of the kernel's longest split.
+// to the end of the kernel's longest split.
 struct SbOrder {
   int sb0, cnt, rot;
   __device__ __forceinline__ SbOrder(int L, int n_splits, int split) {
@@ -496,12 +489,14 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
     TileRef rK, rV;
     uint32_t eK = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 0, h);
     uint32_t eV = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 1, h);
-    rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(0), j), 0, h, eK, flags);
+    rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(0), j), 0, h, eK);
+    flags |= missing_flag(L, group_token(ord.at(0), j), eK);
     load_tile<NR, TT, FMT>(rK, n, cK);
     for (int it = 0; it < ord.cnt; ++it) {
       const int sb = ord.at(it);
       // V bytes of this super-block load while K is rebuilt and scored
-      rV = tile_ref<NR, TT, FMT>(a, seq, L, group_token(sb, j), 1, h, eV, flags);
+      rV = tile_ref<NR, TT, FMT>(a, seq, L, group_token(sb, j), 1, h, eV);
+      flags |= missing_flag(L, group_token(sb, j), eV);
       load_tile<NR, TT, FMT>(rV, n, cV);
       if (it + 1 < ord.cnt) {
         eK = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), j), 0, h);
@@ -533,7 +528,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
           }
         }
       }
-      // Raw K groups (raw tiles, the tail).  BF16: straight from memory into their LDS rows with
+      // Raw K groups (raw tiles).  BF16: straight from memory into their LDS rows with
       // LDS-DMA loads: one instruction fills RPI whole rows (64 lanes x 16 bytes), each lane
       // fetching the row piece whose swizzled position is its own, so a group costs one memory
       // round trip and no registers.  FP8: eight-element pieces through registers, converted
@@ -548,7 +543,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const int k = n + 16 * (m0 + u), rr = k / NCH, chunk = k % NCH;
-              v[u] = ld64(rK.raw + (size_t)(rK.tg * 16 + rr) * D + 8 * chunk);
+              v[u] = ld64(rK.p + (size_t)(rK.tg * 16 + rr) * D + 8 * chunk);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -564,8 +559,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll 1
         for (int g = 0; g < 4; ++g) {
           if (__builtin_amdgcn_readlane(rK.kind, 16 * g) != SRC_RAW) continue;
-          const uint64_t rp = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)((uintptr_t)rK.raw >> 32), 16 * g) << 32) |
-                              (uint32_t)__builtin_amdgcn_readlane((int)(uintptr_t)rK.raw, 16 * g);
+          const uint64_t rp = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)((uintptr_t)rK.p >> 32), 16 * g) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)(uintptr_t)rK.p, 16 * g);
           const int tg_g = __builtin_amdgcn_readlane(rK.tg, 16 * g);
           const uint16_t* raw_g = reinterpret_cast<const uint16_t*>(rp) + (size_t)tg_g * 16 * D;
 #pragma unroll 1
@@ -583,7 +578,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       __syncthreads();
 
       // ---- QK and softmax ----
-      const int valid = min(rK.valid, rV.valid);
+      const int valid = min(rK.valid(), rV.valid());
       f32x4_t cc[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) cc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -610,7 +605,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 
       // K bytes of the next super-block load while V is rebuilt and accumulated
       if (it + 1 < ord.cnt) {
-        rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(it + 1), j), 0, h, eK, flags);
+        rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(it + 1), j), 0, h, eK);
+        flags |= missing_flag(L, group_token(ord.at(it + 1), j), eK);
         load_tile<NR, TT, FMT>(rK, n, cK);
       }
 
@@ -637,11 +633,11 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
               const int ch = 32 * i + 2 * n + x;
               const size_t off = (size_t)ch * TT + rV.tg * 16 + 8 * e;  // elements
               if constexpr (FMT == 0) {  // natural order -> the interleaved order of P
-                const uint4 v = mask_tokens(ld128(reinterpret_cast<const uint16_t*>(rV.raw) + off), rV.valid - 8 * e);
+                const uint4 v = mask_tokens(ld128(reinterpret_cast<const uint16_t*>(rV.p) + off), rV.valid() - 8 * e);
                 bv[x][e] = make_uint4(perm_b32(v.y, v.x, 0x05040100u), perm_b32(v.y, v.x, 0x07060302u),
                                       perm_b32(v.w, v.z, 0x05040100u), perm_b32(v.w, v.z, 0x07060302u));
               } else {
-                bv[x][e] = mask_tokens(fp8x8_to_operand<FMT>(ld64(rV.raw + off)), rV.valid - 8 * e);
+                bv[x][e] = mask_tokens(fp8x8_to_operand<FMT>(ld64(rV.p + off)), rV.valid() - 8 * e);
               }
             }
         } else {
@@ -697,7 +693,7 @@ __device__ __forceinline__ void raw_load_k(const TileRef& r, int n, int j, RawK<
   for (int rb = 0; rb < 4; ++rb) {
     const int rr = 4 * rb + (n & 3);
 #pragma unroll
-    for (int ks = 0; ks < NR; ++ks) k.ka[rb][ks] = ld_piece<FMT>(r.raw, (size_t)(r.tg * 16 + rr) * D + 32 * ks + 8 * j);
+    for (int ks = 0; ks < NR; ++ks) k.ka[rb][ks] = ld_piece<FMT>(r.p, (size_t)(r.tg * 16 + rr) * D + 32 * ks + 8 * j);
   }
 }
 
@@ -709,7 +705,7 @@ __device__ __forceinline__ void raw_load_v(const TileRef& r, int n, RawV<NR, FMT
     for (int x = 0; x < 2; ++x)
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        v.vb[i][x][e] = ld_piece<FMT>(r.raw, (size_t)(32 * i + 2 * n + x) * TT + r.tg * 16 + 8 * e);
+        v.vb[i][x][e] = ld_piece<FMT>(r.p, (size_t)(32 * i + 2 * n + x) * TT + r.tg * 16 + 8 * e);
 }
 
 template <int NR, int TT, int FMT>
@@ -738,24 +734,26 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
     const int jr = n >> 2;  // token group of this lane's QK A-operand rows
     uint32_t eK = load_entry<TT>(a, seq, L, group_token(ord.at(0), jr), 0, h);
     uint32_t eV = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 1, h);
-    TileRef rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(0), jr), 0, h, eK, flags);
+    TileRef rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(0), jr), 0, h, eK);
+    flags |= missing_flag(L, group_token(ord.at(0), jr), eK);
     raw_load_k<NR, TT, FMT>(rK, n, j, ck);
     for (int it = 0; it < ord.cnt; ++it) {
       const int sb = ord.at(it);
-      const TileRef rV = tile_ref<NR, TT, FMT>(a, seq, L, group_token(sb, j), 1, h, eV, flags);
+      const TileRef rV = tile_ref<NR, TT, FMT>(a, seq, L, group_token(sb, j), 1, h, eV);
+      flags |= missing_flag(L, group_token(sb, j), eV);
       raw_load_v<NR, TT, FMT>(rV, n, cv);
       if (it + 1 < ord.cnt) {
         eK = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), jr), 0, h);
         eV = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), j), 1, h);
       }
       // scores of this lane belong to token group j: its K validity comes from lane 4j
-      const int validKj = __shfl(rK.valid, 4 * j);
-      const int valid = min(validKj, rV.valid);
+      const int validKj = __shfl(rK.valid(), 4 * j);
+      const int valid = min(validKj, rV.valid());
       float s[16];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
-        const bool rowok = 4 * rb + (n & 3) < rK.valid;
+        const bool rowok = 4 * rb + (n & 3) < rK.valid();
 #pragma unroll
         for (int ks = 0; ks < NR; ++ks)
           cc = mfma16(rowok ? operand<FMT>(ck.ka[rb][ks]) : make_uint4(0, 0, 0, 0), qb[ks], cc);
@@ -767,7 +765,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       uint4 phi[2], plo[2];
       pack_p<false>(s, phi, plo);
       if (it + 1 < ord.cnt) {
-        rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(it + 1), jr), 0, h, eK, flags);
+        rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(it + 1), jr), 0, h, eK);
+        flags |= missing_flag(L, group_token(ord.at(it + 1), jr), eK);
         raw_load_k<NR, TT, FMT>(rK, n, j, ck);
       }
 #pragma unroll
@@ -776,7 +775,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
         for (int x = 0; x < 2; ++x)
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const uint4 v = mask_tokens(operand<FMT>(cv.vb[i][x][e]), rV.valid - 8 * e);
+            const uint4 v = mask_tokens(operand<FMT>(cv.vb[i][x][e]), rV.valid() - 8 * e);
             acc[i][x] = mfma16(phi[e], v, acc[i][x]);
             acc[i][x] = mfma16(plo[e], v, acc[i][x]);
           }
@@ -786,14 +785,36 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   write_partial<NR>(a, si, h, split, m, l, acc);
 }
 
-// Log-sum-exp merge of the splits.  One 256-thread block per (16-channel slice, query head,
-// sequence), so a decode step launches D/16 * Hq blocks.  Every block derives the split weights
-// w_s = exp2(m_s - M) (M = the largest running maximum among splits that saw a token) into LDS;
-// its threads then sum w_s * acc_s over disjoint subsets of the splits (4 channels per thread,
-// independent 16-byte loads), the subsets are added across lanes and waves, and the result is
-// divided by sum_s w_s * l_s and rounded to BF16.
+// Log-sum-exp merge of the splits, with the tail.  The split kernels cover the finished blocks;
+// the unfinished block (the tail, fewer than T tokens, stored raw) is attended here as one more
+// term of the same normalisation, so no split carries a partial block.  One 256-thread block per
+// (CH-channel slice, query head, sequence): CH = 16 when there are many splits to read (the
+// reads spread over D/16 blocks per head), CH = D when there are few (one block per head, so the
+// tail is scored once per head).
+//   * Every load is issued first, unconditionally (indices clamped into their buffers, unused
+//     values masked afterwards by selects) -- the splits' (max, sum) pairs, this slice's partial
+//     outputs, the tail's K rows and the query, the tail's V values for the slice -- so the block
+//     waits on one memory round trip.
+//   * Tail scores: thread (token tid/4, channel quarter tid%4) takes a 4-lane dot product, in
+//     fp32, of the BF16 query with the token's K row, pre-multiplied by scale*log2(e).
+//   * M = the largest of the split maxima (splits that saw a token) and the tail scores; the
+//     weights exp2(m_s - M), exp2(s_t - M) go to LDS; den = sum_s w_s l_s + sum_t w_t.
+//   * out = (sum_s w_s acc_s + sum_t w_t v_t) / den, rounded to BF16.
 constexpr int kCombineThreads = 256;
-constexpr int kCombineCh = 16;  // channels per block
+constexpr int kMaxSplits = 1024;
+constexpr int kTailTok = 64;        // tail tokens a block can hold (T <= 64)
+
+struct CombineArgs {
+  Geo G;
+  SeqList S;
+  const uint8_t* tail;
+  const uint16_t* q;
+  const float* ws_acc;
+  const float* ws_ml;
+  uint16_t* out;
+  float sl2;
+  int n_splits;
+};
 
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
   for (int o = 32; o > 0; o >>= 1) {
@@ -809,54 +830,150 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
   return r;
 }
 
-__global__ void __launch_bounds__(kCombineThreads) combine_kernel(int Hq, int D, int S,
-                                                                  const float* __restrict__ ws_acc,
-                                                                  const float* __restrict__ ws_ml,
-                                                                  uint16_t* __restrict__ out) {
-  __shared__ float w[1024];
-  __shared__ float red[kCombineThreads / 64 * kCombineCh];
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Eight consecutive tail elements as four BF16 pairs (BF16: 16 bytes; FP8: 8 bytes, converted).
+template <int FMT>
+__device__ __forceinline__ uint4 tail_oct(const uint8_t* p) {
+  if constexpr (FMT == 0) return *reinterpret_cast<const uint4*>(p);
+  else return fp8x8_to_operand<FMT>(*reinterpret_cast<const uint2*>(p));
+}
+// Four consecutive tail elements as two BF16 pairs.
+template <int FMT>
+__device__ __forceinline__ uint2 tail_quad(const uint8_t* p) {
+  if constexpr (FMT == 0) return *reinterpret_cast<const uint2*>(p);
+  else {
+    const uint32_t x = *reinterpret_cast<const uint32_t*>(p);
+    return make_uint2(fp8x2_to_bf16x2<FMT, false>(x), fp8x2_to_bf16x2<FMT, true>(x));
+  }
+}
+
+__device__ __forceinline__ float dot8(uint4 k, uint4 q) {
+  float d = bf16_lo(k.x) * bf16_lo(q.x) + bf16_hi(k.x) * bf16_hi(q.x);
+  d += bf16_lo(k.y) * bf16_lo(q.y) + bf16_hi(k.y) * bf16_hi(q.y);
+  d += bf16_lo(k.z) * bf16_lo(q.z) + bf16_hi(k.z) * bf16_hi(q.z);
+  d += bf16_lo(k.w) * bf16_lo(q.w) + bf16_hi(k.w) * bf16_hi(q.w);
+  return d;
+}
+
+// NR: head_dim / 32; CH: channels per block; UPT: partial outputs per thread (the launch picks
+// UPT * 1024 / CH >= n_splits).
+template <int NR, int FMT, int CH, int UPT>
+__global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a) {
+  constexpr int D = 32 * NR, EB = FmtT<FMT>::EB;
+  constexpr int NQ = CH / 4;                      // channel quads per block
+  constexpr int NSL = kCombineThreads / NQ;       // split slices
+  constexpr int MLPT = (UPT * NSL + kCombineThreads - 1) / kCombineThreads;  // (max, sum) pairs per thread
+  constexpr int KPL = D / 4;                      // tail K channels per lane (4 lanes per token)
+  constexpr int TPC = kCombineThreads / CH;       // tail V: threads per channel
+  constexpr int QPT = (kTailTok / 4) / TPC;       // tail V: token quads per thread
+  static_assert(NQ <= 32 && TPC <= 16 && QPT >= 1, "combine geometry");
+  __shared__ float w[UPT * NSL];
+  __shared__ float pt[kTailTok];
+  __shared__ float red[kCombineThreads / 64];
+  __shared__ float part[kCombineThreads / 64 * CH];
+  __shared__ float tsum[CH];
+  const Geo& G = a.G;
   const int cb = blockIdx.x, hq = blockIdx.y, si = blockIdx.z, tid = threadIdx.x;
-  const float* ml = ws_ml + ((size_t)si * Hq + hq) * S * 2;
-  const float* acc = ws_acc + ((size_t)si * Hq + hq) * S * D + cb * kCombineCh;
-  float mx = -INFINITY;
-  for (int s = tid; s < S; s += kCombineThreads) {
-    const float2 v = *reinterpret_cast<const float2*>(ml + 2 * s);
-    if (v.y > 0.0f) mx = fmaxf(mx, v.x);
+  const int S = a.n_splits, T = G.T;
+  const int seq = a.S.ids[si], L = a.S.lens[si], ntail = L % T, h = hq / G.g;
+  const float* ml = a.ws_ml + ((size_t)si * G.Hq + hq) * S * 2;
+  const float* acc = a.ws_acc + ((size_t)si * G.Hq + hq) * S * D + cb * CH;
+  const int quad = tid % NQ, slice = tid / NQ;    // partial outputs: channels 4*quad.., splits slice + NSL*u
+  const int tk = tid >> 2, kq4 = tid & 3;         // tail K: token tk, channels KPL*kq4 ..
+  const int cv = tid / TPC, tq0 = (tid % TPC) * QPT;  // tail V: channel cb*CH + cv, token quads tq0 ..
+
+  // ---- loads ----
+  float2 mv[MLPT];
+#pragma unroll
+  for (int u = 0; u < MLPT; ++u)
+    mv[u] = *reinterpret_cast<const float2*>(ml + 2 * min(tid + kCombineThreads * u, S - 1));
+  float4 av[UPT];
+#pragma unroll
+  for (int u = 0; u < UPT; ++u)
+    av[u] = *reinterpret_cast<const float4*>(acc + (size_t)min(slice + NSL * u, S - 1) * D + 4 * quad);
+  const uint8_t* tk_base = a.tail + tail_offset(G, seq, 0, h) * EB;  // K tail [t][c]
+  const uint8_t* tv_base = a.tail + tail_offset(G, seq, 1, h) * EB;  // V tail [c][t]
+  const uint16_t* qrow = a.q + ((size_t)si * G.Hq + hq) * D + KPL * kq4;
+  const int tkc = min(tk, T - 1);
+  uint4 kk[KPL / 8], qq[KPL / 8];
+#pragma unroll
+  for (int p = 0; p < KPL / 8; ++p) {
+    kk[p] = tail_oct<FMT>(tk_base + ((size_t)tkc * D + KPL * kq4 + 8 * p) * EB);
+    qq[p] = *reinterpret_cast<const uint4*>(qrow + 8 * p);
   }
+  uint2 vv[QPT];
+#pragma unroll
+  for (int u = 0; u < QPT; ++u)
+    vv[u] = tail_quad<FMT>(tv_base + ((size_t)(cb * CH + cv) * T + min(4 * (tq0 + u), T - 4)) * EB);
+
+  // ---- maximum ----
+  float dot = 0.0f;
+#pragma unroll
+  for (int p = 0; p < KPL / 8; ++p) dot += dot8(kk[p], qq[p]);
+  dot += __shfl_xor(dot, 1);
+  dot += __shfl_xor(dot, 2);
+  const bool kok = tk < ntail;
+  const float st = kok ? dot * a.sl2 : -INFINITY;
+  float mx = st;
+#pragma unroll
+  for (int u = 0; u < MLPT; ++u)
+    if (tid + kCombineThreads * u < S && mv[u].y > 0.0f) mx = fmaxf(mx, mv[u].x);
   const float M = block_reduce(mx, red, true);
+
+  // ---- weights and denominator ----
   float den = 0.0f;
-  for (int s = tid; s < S; s += kCombineThreads) {
-    const float2 v = *reinterpret_cast<const float2*>(ml + 2 * s);
-    const float ws = v.y > 0.0f ? exp2f(v.x - M) : 0.0f;
-    w[s] = ws;
-    den += ws * v.y;
+#pragma unroll
+  for (int u = 0; u < MLPT; ++u) {
+    const int s = tid + kCombineThreads * u;
+    const bool ok = s < S && mv[u].y > 0.0f;
+    const float ws = ok ? exp2f(mv[u].x - M) : 0.0f;
+    if (s < UPT * NSL) w[s] = ws;
+    den += ok ? ws * mv[u].y : 0.0f;
   }
-  den = block_reduce(den, red, false);  // its barriers also publish w[]
-  // thread = (split slice, channel quad): slice tid >> 2 of 64, channels 4 * (tid & 3) .. +3
-  const int quad = tid & 3, slice = tid >> 2;
+  if (kq4 == 0) {
+    const float p = kok ? exp2f(st - M) : 0.0f;
+    pt[tk] = p;
+    den += p;
+  }
+  den = block_reduce(den, red, false);  // its barriers also publish w[] and pt[]
+
+  // ---- weighted sums ----
   float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = slice; s < S; s += kCombineThreads / 4) {
-    const float ws = w[s];
-    const float4 v = *reinterpret_cast<const float4*>(acc + (size_t)s * D + 4 * quad);
-    sum.x += ws * v.x;
-    sum.y += ws * v.y;
-    sum.z += ws * v.z;
-    sum.w += ws * v.w;
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int s = slice + NSL * u;
+    const float ws = s < S ? w[s] : 0.0f;
+    sum.x += s < S ? ws * av[u].x : 0.0f;
+    sum.y += s < S ? ws * av[u].y : 0.0f;
+    sum.z += s < S ? ws * av[u].z : 0.0f;
+    sum.w += s < S ? ws * av[u].w : 0.0f;
   }
-  for (int o = 4; o < 64; o <<= 1) {  // add the 16 slices of this wave (lane bits 2..5)
+  for (int o = NQ; o < 64; o <<= 1) {  // add the slices of this wave
     sum.x += __shfl_xor(sum.x, o);
     sum.y += __shfl_xor(sum.y, o);
     sum.z += __shfl_xor(sum.z, o);
     sum.w += __shfl_xor(sum.w, o);
   }
-  __syncthreads();
+  float tv = 0.0f;
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) {
+    const int t0 = 4 * (tq0 + u);
+    const float v4[4] = {bf16_lo(vv[u].x), bf16_hi(vv[u].x), bf16_lo(vv[u].y), bf16_hi(vv[u].y)};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tv += (t0 + k < ntail) ? pt[min(t0 + k, kTailTok - 1)] * v4[k] : 0.0f;
+  }
+  for (int o = 1; o < TPC; o <<= 1) tv += __shfl_xor(tv, o);
   const int lane = tid & 63, wv = tid >> 6;
-  if (lane < 4) *reinterpret_cast<float4*>(red + wv * kCombineCh + 4 * lane) = sum;
+  if (lane < NQ) *reinterpret_cast<float4*>(part + wv * CH + 4 * lane) = sum;
+  if (tid % TPC == 0) tsum[cv] = tv;
   __syncthreads();
-  if (tid < kCombineCh) {
-    float t = 0.0f;
-    for (int i = 0; i < kCombineThreads / 64; ++i) t += red[i * kCombineCh + tid];
-    out[((size_t)si * Hq + hq) * D + cb * kCombineCh + tid] = f32_to_bf16_rne(t / den);
+  if (tid < CH) {
+    float t = tsum[tid];
+#pragma unroll
+    for (int i = 0; i < kCombineThreads / 64; ++i) t += part[i * CH + tid];
+    a.out[((size_t)si * G.Hq + hq) * D + cb * CH + tid] = f32_to_bf16_rne(t / den);
   }
 }
 
@@ -909,10 +1026,37 @@ int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& S, 
   }
 }
 
-int launch_combine(const Geo& G, int n_seqs, int n_splits, const float* ws_acc, const float* ws_ml, uint16_t* out,
-                   void* stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(G.D / kCombineCh, G.Hq, n_seqs), dim3(kCombineThreads), 0,
-                     (hipStream_t)stream, G.Hq, G.D, n_splits, ws_acc, ws_ml, out);
+template <int NR, int FMT>
+void (*pick_combine(int n_splits))(CombineArgs) {
+  constexpr int D = 32 * NR;
+  if (n_splits <= 4 * (kCombineThreads / (D / 4))) return combine_kernel<NR, FMT, D, 4>;
+  if (n_splits <= 4 * (kCombineThreads / 4)) return combine_kernel<NR, FMT, 16, 4>;
+  return combine_kernel<NR, FMT, 16, 16>;
+}
+
+int launch_combine(const Geo& G, const DevBufs& B, const SeqList& S, const uint16_t* q, float scale, int n_splits,
+                   const float* ws_acc, const float* ws_ml, uint16_t* out, void* stream) {
+  CombineArgs a;
+  a.G = G;
+  a.S = S;
+  a.tail = reinterpret_cast<const uint8_t*>(B.tail);
+  a.q = q;
+  a.ws_acc = ws_acc;
+  a.ws_ml = ws_ml;
+  a.out = out;
+  a.sl2 = scale * 1.4426950408889634f;
+  a.n_splits = n_splits;
+  if (n_splits < 1 || n_splits > kMaxSplits || G.T > kTailTok || G.T < 4) return (int)hipErrorInvalidValue;
+  void (*k)(CombineArgs) = nullptr;
+  const bool d128 = G.D == 128;
+  switch (G.fmt) {
+    case 0: k = d128 ? pick_combine<4, 0>(n_splits) : pick_combine<2, 0>(n_splits); break;
+    case 1: k = d128 ? pick_combine<4, 1>(n_splits) : pick_combine<2, 1>(n_splits); break;
+    case 2: k = d128 ? pick_combine<4, 2>(n_splits) : pick_combine<2, 2>(n_splits); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  const int ch = n_splits <= 4 * (kCombineThreads / (G.D / 4)) ? G.D : 16;
+  hipLaunchKernelGGL(k, dim3(G.D / ch, G.Hq, S.n), dim3(kCombineThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

@@ -83,9 +83,10 @@ int launch_append(const Geo& G, const DevBufs& B, const SeqList& seqs, const voi
 int launch_release(const Geo& G, const DevBufs& B, int seq, int n_blocks, void* stream);
 int launch_decode_blocks(const Geo& G, const DevBufs& B, int seq, int first, int n, void* k_out, void* v_out,
                          void* stream);
+// seqs.lens: tokens of the finished blocks (partials) or of the whole sequence (combine)
 int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale,
                               int n_splits, float* ws_acc, float* ws_ml, void* stream);
-int launch_combine(const Geo& G, int n_seqs, int n_splits, const float* ws_acc, const float* ws_ml, uint16_t* out,
-                   void* stream);
+int launch_combine(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale, int n_splits,
+                   const float* ws_acc, const float* ws_ml, uint16_t* out, void* stream);
 
 }  // namespace kvc

@@ -148,22 +148,26 @@ size_t kv_attention_workspace_bytes(const kvc_params* params, int32_t n_seqs, in
  *   out[s][hq][c] = sum_t softmax_t(scale * q[s][hq] . k_t) v_t[c]
  * over every token of the sequence (finished blocks, compressed or raw, and the tail), with
  * query head hq reading KV head hq / (Hq / Hkv).  q_dev: [n_seqs][Hq][D] BF16; out_dev:
- * [n_seqs][Hq][D] BF16 (round-to-nearest-even of an fp32 result).  The context of each
- * sequence is split into n_splits contiguous ranges of 64 tokens processed in parallel
- * (1 <= n_splits <= 1024); their partial results are merged by log-sum-exp.  Every listed
- * sequence must hold at least one token (KVC_EINVAL otherwise). */
+ * [n_seqs][Hq][D] BF16 (round-to-nearest-even of an fp32 result).  The finished blocks of each
+ * sequence are split into n_splits contiguous ranges of 64 tokens processed in parallel
+ * (1 <= n_splits <= 1024); their partial results and the tail are merged by log-sum-exp.
+ * Every listed sequence must hold at least one token (KVC_EINVAL otherwise). */
 int kv_decode_attention(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
                         float scale, int32_t n_splits, void* ws_dev, size_t ws_bytes, void* out_dev, void* stream);
 
 /* The two halves of kv_decode_attention, for callers that schedule or time them apart:
- * kv_attention_partials runs the split kernel and leaves, for every (sequence, query head,
- * split), the unnormalised partial output, the running maximum (base-2 units) and the sum of
- * weights in the workspace; kv_attention_combine merges the splits of those n_seqs sequences
- * (log-sum-exp) into out.  Same arguments and checks as kv_decode_attention. */
+ * kv_attention_partials runs the split kernel over the finished blocks and leaves, for every
+ * (sequence, query head, split), the unnormalised partial output, the running maximum
+ * (base-2 units) and the sum of weights in the workspace; kv_attention_combine attends the
+ * tail of each sequence (its tokens not yet in a finished block) and merges it with the splits
+ * (log-sum-exp) into out.  Both take the arguments and checks of kv_decode_attention; the
+ * sequences, query, scale, split count and workspace must be the same in the two calls, with
+ * no append to those sequences between them. */
 int kv_attention_partials(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
                           float scale, int32_t n_splits, void* ws_dev, size_t ws_bytes, void* stream);
-int kv_attention_combine(kvc_cache* cache, int32_t n_seqs, int32_t n_splits, const void* ws_dev, size_t ws_bytes,
-                         void* out_dev, void* stream);
+int kv_attention_combine(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
+                         float scale, int32_t n_splits, const void* ws_dev, size_t ws_bytes, void* out_dev,
+                         void* stream);
 
 /* Returns every slot of a sequence to the free stacks and empties it (enqueued). */
 int kv_release_seq(kvc_cache* cache, int32_t seq, void* stream);

@@ -78,6 +78,44 @@ def test_ragged_lengths_and_tail(L):
             assert err <= TOL, (compressed, S, err)
 
 
+@pytest.mark.parametrize("T", [16, 32, 64])
+def test_tail_at_every_block_size(T):
+    """The tail (tokens past the last finished block) is merged with the splits of the finished
+    blocks: lengths with an empty tail, the longest one (T - 1), and tails behind 0, 1 and
+    several blocks, at every supported block size."""
+    cfg = synth.config(0)
+    g, toks = synth.sequence_tokens(cfg)
+    k, v = toks[0]
+    for L in (T - 1, T, T + 1, 2 * T - 1, 5 * T + 7, 1024 - 1):
+        kk, vv = k[:L], v[:L]
+        q = synth.queries(cfg, step=L)
+        ref = _oracle(cfg, [(kk, vv)], q)
+        for compressed in (True, False):
+            cache = new_cache(Hkv=cfg.Hkv, Hq=cfg.Hq, D=cfg.D, T=T, max_seqs=1, max_blocks=1024 // T + 1,
+                              compressed=compressed)
+            cache.calibrate(dev(k[:cfg.n_cal]), dev(v[:cfg.n_cal]))
+            cache.append([0], dev(kk[None]), dev(vv[None]))
+            for S in (1, 3):
+                err = row_rel_err(host(cache.attention([0], dev(q), cfg.scale, S)), ref)
+                assert err <= TOL, (L, compressed, S, err)
+
+
+def test_partials_then_combine_equals_one_call():
+    """kv_attention_partials followed by kv_attention_combine gives the bits of
+    kv_decode_attention."""
+    cfg = synth.config(0)
+    g, toks = synth.sequence_tokens(cfg)
+    k, v = toks[0]
+    cache = _fill(cfg, [(k[:1000], v[:1000])])
+    q = dev(synth.queries(cfg, step=7))
+    one = host(cache.attention([0], q, cfg.scale, 5))
+    ws = cache.workspace(1, 5)
+    out = torch.empty((1, cfg.Hq, cfg.D), dtype=torch.int16, device="cuda")
+    cache.attention_partials([0], q, cfg.scale, 5, ws)
+    cache.attention_combine([0], q, cfg.scale, 5, ws, out)
+    assert np.array_equal(host(out), one)
+
+
 def test_single_token_returns_its_value():
     cfg = synth.config(0)
     g, toks = synth.sequence_tokens(cfg)
@@ -96,11 +134,11 @@ def test_split_counts_agree():
     q = synth.queries(cfg, step=3)
     ref = _oracle(cfg, toks, q)
     outs = []
-    for S in (1, 2, 5, 7, 16, 64):
+    for S in (1, 2, 5, 7, 16, 33, 64, 300, 1024):  # every merge variant; most of 300+ splits empty
         outs.append(host(cache.attention([0], dev(q), cfg.scale, S)))
-        assert row_rel_err(outs[-1], ref) <= TOL
+        assert row_rel_err(outs[-1], ref) <= TOL, S
     # identical inputs, identical launch: bitwise-identical output
-    again = host(cache.attention([0], dev(q), cfg.scale, 64))
+    again = host(cache.attention([0], dev(q), cfg.scale, 1024))
     assert np.array_equal(again, outs[-1])
 
 
@@ -160,15 +198,25 @@ def test_cfg1_decode_with_64_appends():
 
 def test_cfg2_full_context_sampled_heads():
     """The 64K-token headline layer in the benchmark's launch shape; the oracle evaluates 8 of
-    the 32 query heads (two per KV-head group sampled across the heads)."""
+    the 32 query heads (two per KV-head group sampled across the heads).  Then 27 single-token
+    decode appends put a tail behind the 1024 finished blocks, as in the benchmark's steps."""
     cfg = synth.config(2)
     g, toks = synth.sequence_tokens(cfg)
+    k, v = toks[0]
+    kn, vn = g.tokens(27)
+    k2, v2 = np.concatenate([k, kn]), np.concatenate([v, vn])
     q = synth.queries(cfg)
+    q2 = synth.queries(cfg, step=27)
     heads = [0, 3, 9, 14, 17, 22, 27, 31]
     ref = _oracle(cfg, toks, q, heads=heads)
+    ref2 = _oracle(cfg, [(k2, v2)], q2, heads=heads)
     for compressed in (True, False):
         cache = _fill(cfg, toks, compressed)
         out = host(cache.attention([0], dev(q), cfg.scale, 256))
         assert row_rel_err(out[:, heads], ref) <= TOL
+        for i in range(27):
+            cache.append([0], dev(kn[None, i:i + 1]), dev(vn[None, i:i + 1]))
+        out = host(cache.attention([0], dev(q2), cfg.scale, 256))
+        assert row_rel_err(out[:, heads], ref2) <= TOL, compressed
         del cache
         torch.cuda.empty_cache()
