@@ -85,6 +85,7 @@ struct TG {
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Two FP8 values (bytes 2*HI, 2*HI+1 of x) -> two BF16 (low half = the lower byte); exact.
 template <int FMT, bool HI>
@@ -204,20 +205,23 @@ __device__ __forceinline__ void load_tile(const TileRef& r, int n, CRegs<NR, FMT
   c.esc0 = c.esc1 = make_uint4(0, 0, 0, 0);
   if (n < r.escu) c.esc0 = ld128(t + Q::ESC_OFF + 16 * n);
   if (n + 16 < r.escu) c.esc1 = ld128(t + Q::ESC_OFF + 16 * (n + 16));
+  // one base per section for this lane's first pair; round i adds 16 pairs (immediate offsets)
+  const uint32_t pr0 = (uint32_t)(r.tg * (Q::D / 2) + n);
+  const uint8_t* smb = t + Q::SM_OFF + (FMT == 0 ? 32u : FMT == 1 ? 12u : 16u) * pr0;
+  const uint8_t* cpb = t + Q::CODE_OFF + 12u * pr0;
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    const int pr = r.tg * (Q::D / 2) + 16 * i + n;
     if constexpr (FMT == 0) {
-      c.sm.v[i][0] = ld128(t + Q::SM_OFF + 32 * pr);
-      c.sm.v[i][1] = ld128(t + Q::SM_OFF + 32 * pr + 16);
+      c.sm.v[i][0] = ld128(smb + 32 * 16 * i);
+      c.sm.v[i][1] = ld128(smb + 32 * 16 * i + 16);
     } else if constexpr (FMT == 1) {
-      const uint8_t* sp = t + Q::SM_OFF + 12 * pr;
+      const uint8_t* sp = smb + 12 * 16 * i;
       c.sm.w[i][0] = ld32(sp); c.sm.w[i][1] = ld32(sp + 4); c.sm.w[i][2] = ld32(sp + 8);
     } else {
-      const uint4 a = ld128(t + Q::SM_OFF + 16 * pr);
+      const uint4 a = ld128(smb + 16 * 16 * i);
       c.sm.w[i][0] = a.x; c.sm.w[i][1] = a.y; c.sm.w[i][2] = a.z; c.sm.w[i][3] = a.w;
     }
-    const uint8_t* cp = t + Q::CODE_OFF + 12 * pr;
+    const uint8_t* cp = cpb + 12 * 16 * i;
     c.cd[i][0] = ld32(cp);
     c.cd[i][1] = ld32(cp + 4);
     c.cd[i][2] = ld32(cp + 8);
@@ -250,27 +254,40 @@ __device__ __forceinline__ void init_esc_lut() {
 // b4[c0], b4[c1]; below = (1 << 2n) - 1.  Output, low half first: BF16 o[gi][0][q] = tokens
 // (4q, 4q+2), o[gi][1][q] = (4q+1, 4q+3); FP8 (converted exactly to BF16) o[gi][0][q] = tokens
 // (4q, 4q+1), o[gi][1][q] = (4q+2, 4q+3).
+// The tag words E, R and escape prefix P of round i's pair, for every round of a tile, fetched
+// together (the cross-lane reads of all rounds are in flight at once).
 template <int NR, int FMT>
-__device__ __forceinline__ void rebuild_round(const CRegs<NR, FMT>& c, int i, int j, int n, int tg, uint32_t pfx,
+__device__ __forceinline__ void fetch_tags(const CRegs<NR, FMT>& c, int j, int tg, uint32_t pfx, uint32_t t[NR][3]) {
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int w = tg * NR + i;
+    t[i][0] = (uint32_t)__shfl((int)c.tE, 16 * j + w);
+    t[i][1] = (uint32_t)__shfl((int)c.tR, 16 * j + w);
+    t[i][2] = (uint32_t)__shfl((int)pfx, 16 * j + w);
+  }
+}
+
+template <int NR, int FMT>
+__device__ __forceinline__ void rebuild_round(const CRegs<NR, FMT>& c, int i, int j, int n, const uint32_t tw[3],
                                               uint32_t bases, const uint16_t* esc16, uint32_t below, uint32_t& bad,
                                               uint32_t o[2][2][4]) {
   constexpr int RU = FmtT<FMT>::F - 3;  // escape units of a raw group
-  const int w = tg * NR + i;  // tag word holding both groups of this pair
-  const uint32_t Ew = (uint32_t)__shfl((int)c.tE, 16 * j + w);
-  const uint32_t Rw = (uint32_t)__shfl((int)c.tR, 16 * j + w);
-  const uint32_t Pw = (uint32_t)__shfl((int)pfx, 16 * j + w);
+  const uint32_t Ew = tw[0], Rw = tw[1], Pw = tw[2];
   bad |= Rw & ~Ew;
   if constexpr (FMT == 2) bad |= Ew & ~Rw;  // no wide mode in a 4-bit exponent field
   const uint32_t P0 = Pw + __popc(Ew & below) + (uint32_t)(RU - 1) * __popc(Rw & below);
-  const uint32_t e2 = (Ew >> (2 * n)) & 3u, r2 = (Rw >> (2 * n)) & 3u;
+  const uint32_t e2 = __builtin_amdgcn_ubfe(Ew, 2 * n, 2), r2 = __builtin_amdgcn_ubfe(Rw, 2 * n, 2);
   const uint32_t W0 = c.cd[i][0], W1 = c.cd[i][1], W2 = c.cd[i][2];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const uint32_t E = (e2 >> gi) & 1u, R = (r2 >> gi) & 1u;
     const uint32_t P = gi ? P0 + (e2 & 1u) + (uint32_t)(RU - 1) * (r2 & 1u) : P0;
-    const uint32_t b3 = (bases >> (8 * gi)) & 0xFFu, b4 = (bases >> (16 + 8 * gi)) & 0xFFu;
-    const uint32_t H = perm_b32(0u, R ? 0u : (E ? b4 : b3), 0x00000000u);  // base in all four bytes
-    const uint32_t plane0 = (uint32_t)esc16[P] & (0u - E);                  // read always, keep if escaped
+    // base in all four bytes: byte gi (b3) or 2 + gi (b4) of `bases`, 0 for a raw group
+    const uint32_t sel = R ? 0x0C0C0C0Cu : E * 0x02020202u + (uint32_t)gi * 0x01010101u;
+    const uint32_t H = perm_b32(0u, bases, sel);
+    const uint32_t pw = esc16[P];                                             // read always,
+    const uint32_t plane0 = E ? pw : 0u;                                      // keep if escaped
+    uint32_t Evq[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int slot = 4 * gi + q;
@@ -278,7 +295,23 @@ __device__ __forceinline__ void rebuild_round(const CRegs<NR, FMT>& c, int i, in
                         : slot == 2 ? code_slot<2>(W0, W1, W2) : slot == 3 ? code_slot<3>(W0, W1, W2)
                         : slot == 4 ? code_slot<4>(W0, W1, W2) : slot == 5 ? code_slot<5>(W0, W1, W2)
                         : slot == 6 ? code_slot<6>(W0, W1, W2) : code_slot<7>(W0, W1, W2);
-      const uint32_t Ev = H + cs + esc_lut[(plane0 >> (4 * q)) & 0xFu];
+      Evq[q] = H + cs + esc_lut[(plane0 >> (4 * q)) & 0xFu];
+    }
+    if constexpr (FMT == 0) {
+      if (R) {  // raw group (rare): base 0; offset bits 4..7 of each token go into its exponent byte
+        const uint2 hw = *reinterpret_cast<const uint2*>(esc16 + P + 1);  // four 16-bit units
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t u = q < 2 ? hw.x : hw.y;
+          const uint32_t y = perm_b32(u, u, (q & 1) ? 0x03030202u : 0x01010000u);
+          Evq[q] += ((y << 4) & 0x00F000F0u) | (y & 0xF000F000u);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int slot = 4 * gi + q;
+      const uint32_t Ev = Evq[q];
       if constexpr (FMT == 0) {
         const uint4 s4 = c.sm.v[i][gi];
         const uint32_t sv = q == 0 ? s4.x : q == 1 ? s4.y : q == 2 ? s4.z : s4.w;
@@ -305,16 +338,6 @@ __device__ __forceinline__ void rebuild_round(const CRegs<NR, FMT>& c, int i, in
         }
         o[gi][0][q] = fp8x2_to_bf16x2<FMT, false>(B);
         o[gi][1][q] = fp8x2_to_bf16x2<FMT, true>(B);
-      }
-    }
-    if constexpr (FMT == 0) {
-      if (R) {  // raw group (rare): base 0, add offset bits 4..7 into the exponent field
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t X = raw_high_nibbles(esc16[P + 1 + q]);
-          o[gi][0][q] |= (X << 7) & 0x7F807F80u;
-          o[gi][1][q] |= (X >> 1) & 0x7F807F80u;
-        }
       }
     }
   }
@@ -356,20 +379,26 @@ __device__ __forceinline__ void rescale_acc(f32x4_t acc[NR][2], float alpha, int
 }
 
 // P as MFMA A operands (high and low bf16 parts).  INTERLEAVED: token order (0,2,1,3,4,6,5,7)
-// matching the rebuilt V words; otherwise natural order.
+// matching the rebuilt V words; otherwise natural order.  Two values per conversion: the high
+// part is the round-to-nearest-even BF16 pair, the low part the BF16 pair of the exact
+// remainders.
 template <bool INTERLEAVED>
 __device__ __forceinline__ void pack_p(const float p[16], uint4 hi[2], uint4 lo[2]) {
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    float v[8], w[8];
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int src = INTERLEAVED ? ((k & 4) | ((k & 1) << 1) | ((k >> 1) & 1)) : k;
-      v[k] = p[8 * e + src];
-      w[k] = v[k] - bf16_round(v[k]);
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const int k0 = 2 * k2, k1 = 2 * k2 + 1;
+      const int s0 = INTERLEAVED ? ((k0 & 4) | ((k0 & 1) << 1) | ((k0 >> 1) & 1)) : k0;
+      const int s1 = INTERLEAVED ? ((k1 & 4) | ((k1 & 1) << 1) | ((k1 >> 1) & 1)) : k1;
+      const float a = p[8 * e + s0], b = p[8 * e + s1];
+      h[k2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+      const float al = a - __uint_as_float(h[k2] << 16), bl = b - __uint_as_float(h[k2] & 0xFFFF0000u);
+      l[k2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){al, bl}, bf16x2_t));
     }
-    hi[e] = make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
-    lo[e] = make_uint4(pack2(w[0], w[1]), pack2(w[2], w[3]), pack2(w[4], w[5]), pack2(w[6], w[7]));
+    hi[e] = make_uint4(h[0], h[1], h[2], h[3]);
+    lo[e] = make_uint4(l[0], l[1], l[2], l[3]);
   }
 }
 
@@ -508,10 +537,12 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       const uint32_t pfxK = stage_escape<NR, FMT>(cK, rK, n, esc_lds);
       __syncthreads();
       if (rK.kind == SRC_COMP) {
+        uint32_t tags[NR][3];
+        fetch_tags<NR, FMT>(cK, j, rK.tg, pfxK, tags);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
           uint32_t o[2][2][4];
-          rebuild_round<NR, FMT>(cK, i, j, n, rK.tg, pfxK, blds[i * 16 + n], esc16, below, bad, o);
+          rebuild_round<NR, FMT>(cK, i, j, n, tags[i], blds[i * 16 + n], esc16, below, bad, o);
           // transpose to token-major rows: token 16j + 4q + k gets the (c0, c0+1) word, taken
           // from one half of each of the two channels' token-pair words (BF16: word k & 1, half
           // k >> 1; FP8: word k >> 1, half k & 1)
@@ -594,12 +625,19 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
         }
       }
       float s[16];
+      if (__builtin_amdgcn_ballot_w64(valid < 16)) {  // a group past the finished blocks (T < 64)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+        for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[4 * rb + r] = (4 * rb + r < valid) ? cc[rb][r] * a.sl2 : -INFINITY;
+          for (int r = 0; r < 4; ++r) s[4 * rb + r] = (4 * rb + r < valid) ? cc[rb][r] * a.sl2 : -INFINITY;
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[4 * rb + r] = cc[rb][r] * a.sl2;
+      }
       const float alpha = softmax_update(s, m, l);
-      rescale_acc<NR>(acc, alpha, j);
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) rescale_acc<NR>(acc, alpha, j);  // a running max moved
       uint4 phi[2], plo[2];
       pack_p<!NAT>(s, phi, plo);
 
@@ -614,12 +652,14 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       __syncthreads();
       const uint32_t pfxV = stage_escape<NR, FMT>(cV, rV, n, esc_lds);
       __syncthreads();
+      uint32_t tagsV[NR][3];
+      fetch_tags<NR, FMT>(cV, j, rV.tg, pfxV, tagsV);
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         uint4 bv[2][2];
         if (rV.kind == SRC_COMP) {
           uint32_t o[2][2][4];
-          rebuild_round<NR, FMT>(cV, i, j, n, rV.tg, pfxV, blds[(NR + i) * 16 + n], esc16, below, bad, o);
+          rebuild_round<NR, FMT>(cV, i, j, n, tagsV[i], blds[(NR + i) * 16 + n], esc16, below, bad, o);
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
             bv[x][0] = make_uint4(o[x][0][0], o[x][1][0], o[x][0][1], o[x][1][1]);
