@@ -142,6 +142,26 @@ class KVCache:
                                               ws.numel(), _ptr(out), self._stream()))
         return out
 
+    def decode_step(self, seq_ids, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, scale: float,
+                    n_splits: int, ws=None, out=None) -> torch.Tensor:
+        """Append one token per sequence (k_new, v_new: [n][1][Hkv][D] or [n][Hkv][D] elements)
+        and attend over every token including it."""
+        n = len(seq_ids)
+        self._check_q(q, n)
+        for t, what in ((k_new, "k_new"), (v_new, "v_new")):
+            _elem(t, what, self.EB)
+            if t.numel() != n * self.Hkv * self.D or not t.is_contiguous() or t.device != self.device:
+                raise ValueError(f"{what} must be a contiguous [{n}][{self.Hkv}][{self.D}] tensor on {self.device}")
+        if ws is None:
+            ws = self.workspace(n, n_splits)
+        if out is None:
+            out = torch.empty((n, self.Hq, self.D), dtype=torch.int16, device=self.device)
+        self._check_out(out, n)
+        ids = (ctypes.c_int32 * n)(*seq_ids)
+        L.check(self.lib.kv_decode_step(self.handle, ids, n, _ptr(k_new), _ptr(v_new), _ptr(q), float(scale), n_splits,
+                                        _ptr(ws), ws.numel(), _ptr(out), self._stream()))
+        return out
+
     # ---- bookkeeping ----
     def release(self, seq: int):
         L.check(self.lib.kv_release_seq(self.handle, seq, self._stream()))

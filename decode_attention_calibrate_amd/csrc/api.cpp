@@ -329,7 +329,7 @@ int kv_attention_combine(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_se
     }
     rc = hip_fail(kvc::launch_combine(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale, n_splits,
                                       acc + (size_t)s0 * G.Hq * n_splits * G.D, ml + (size_t)s0 * G.Hq * n_splits * 2,
-                                      (uint16_t*)out_dev + (size_t)s0 * G.Hq * G.D, stream),
+                                      (uint16_t*)out_dev + (size_t)s0 * G.Hq * G.D, nullptr, nullptr, stream),
                   "launch combine");
     if (rc != KVC_OK) return rc;
   }
@@ -342,6 +342,55 @@ int kv_decode_attention(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seq
   const int rc = kv_attention_partials(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, stream);
   if (rc != KVC_OK) return rc;
   return kv_attention_combine(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, out_dev, stream);
+}
+
+int kv_decode_step(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* k_new_dev,
+                   const void* v_new_dev, const void* q_dev, float scale, int32_t n_splits, void* ws_dev, size_t ws_bytes,
+                   void* out_dev, void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  int rc = check_seq_ids(c, seq_ids_host, n_seqs);
+  if (rc != KVC_OK) return rc;
+  if (!k_new_dev || !v_new_dev || !out_dev) return fail(KVC_EINVAL, "k_new, v_new and out must not be NULL");
+  if (((uintptr_t)k_new_dev & 15u) || ((uintptr_t)v_new_dev & 15u))
+    return fail(KVC_EINVAL, "k_new and v_new must be 16-byte aligned");
+  const Geo& G = c->G;
+  bool completes = false;  // does this token finish a block of some listed sequence?
+  for (int i = 0; i < n_seqs; ++i) completes |= (c->len[seq_ids_host[i]] + 1) % G.T == 0;
+  if (completes) {  // the block must be encoded first: the append, then both attention halves
+    rc = kv_encode_append(c, seq_ids_host, n_seqs, k_new_dev, v_new_dev, 1, stream);
+    if (rc != KVC_OK) return rc;
+    return kv_decode_attention(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, out_dev, stream);
+  }
+  for (int i = 0; i < n_seqs; ++i)
+    if (c->len[seq_ids_host[i]] >= INT32_MAX - 1) return fail(KVC_EINVAL, "sequence too long");
+  // the finished blocks do not change: split attention over them as they are
+  for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] += 1;  // the checks below see the new token
+  rc = check_attention_args(c, seq_ids_host, n_seqs, q_dev, n_splits, ws_dev, ws_bytes);
+  if (rc == KVC_OK) rc = kv_attention_partials(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, stream);
+  if (rc != KVC_OK) {
+    for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] -= 1;
+    return rc;
+  }
+  float* acc = (float*)ws_dev;
+  float* ml = acc + (size_t)n_seqs * G.Hq * n_splits * G.D;
+  const size_t row = (size_t)G.Hkv * G.D * G.EB;  // bytes of one token of all KV heads
+  for (int s0 = 0; s0 < n_seqs && rc == KVC_OK; s0 += kvc::kMaxSeqsPerLaunch) {
+    SeqList S;
+    S.n = std::min(kvc::kMaxSeqsPerLaunch, n_seqs - s0);
+    for (int i = 0; i < S.n; ++i) {
+      S.ids[i] = seq_ids_host[s0 + i];
+      S.lens[i] = c->len[S.ids[i]];
+    }
+    rc = hip_fail(kvc::launch_combine(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale, n_splits,
+                                      acc + (size_t)s0 * G.Hq * n_splits * G.D, ml + (size_t)s0 * G.Hq * n_splits * 2,
+                                      (uint16_t*)out_dev + (size_t)s0 * G.Hq * G.D,
+                                      (const uint8_t*)k_new_dev + (size_t)s0 * row,
+                                      (const uint8_t*)v_new_dev + (size_t)s0 * row, stream),
+                  "launch combine");
+  }
+  if (rc != KVC_OK)
+    for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] -= 1;
+  return rc;
 }
 
 int kv_release_seq(kvc_cache* c, int32_t seq, void* stream) {

@@ -840,6 +840,9 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 //   * M = the largest of the split maxima (splits that saw a token) and the tail scores; the
 //     weights exp2(m_s - M), exp2(s_t - M) go to LDS; den = sum_s w_s l_s + sum_t w_t.
 //   * out = (sum_s w_s acc_s + sum_t w_t v_t) / den, rounded to BF16.
+// Decode step (k_new != null): the sequence's newest token, the last of its tail, is read from
+// k_new / v_new instead of the tail, and the first block of each KV-head group writes it into
+// the tail for later steps (no other block reads that tail position in this launch).
 constexpr int kCombineThreads = 256;
 constexpr int kMaxSplits = 1024;
 constexpr int kTailTok = 64;        // tail tokens a block can hold (T <= 64)
@@ -847,7 +850,9 @@ constexpr int kTailTok = 64;        // tail tokens a block can hold (T <= 64)
 struct CombineArgs {
   Geo G;
   SeqList S;
-  const uint8_t* tail;
+  uint8_t* tail;
+  const uint8_t* k_new;  // decode step: this step's token, [n][Hkv][D] elements (else null)
+  const uint8_t* v_new;
   const uint16_t* q;
   const float* ws_acc;
   const float* ws_ml;
@@ -933,20 +938,31 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
 #pragma unroll
   for (int u = 0; u < UPT; ++u)
     av[u] = *reinterpret_cast<const float4*>(acc + (size_t)min(slice + NSL * u, S - 1) * D + 4 * quad);
-  const uint8_t* tk_base = a.tail + tail_offset(G, seq, 0, h) * EB;  // K tail [t][c]
-  const uint8_t* tv_base = a.tail + tail_offset(G, seq, 1, h) * EB;  // V tail [c][t]
+  uint8_t* tk_base = a.tail + tail_offset(G, seq, 0, h) * EB;  // K tail [t][c]
+  uint8_t* tv_base = a.tail + tail_offset(G, seq, 1, h) * EB;  // V tail [c][t]
   const uint16_t* qrow = a.q + ((size_t)si * G.Hq + hq) * D + KPL * kq4;
   const int tkc = min(tk, T - 1);
+  const bool step = a.k_new != nullptr;
+  const int tnew = step ? ntail - 1 : -1;  // tail position of this step's token
+  const uint8_t* kn = step ? a.k_new + ((size_t)si * G.Hkv + h) * D * EB : nullptr;
+  const uint8_t* vn = step ? a.v_new + ((size_t)si * G.Hkv + h) * D * EB : nullptr;
+  const uint8_t* krow = tk == tnew ? kn : tk_base + (size_t)tkc * D * EB;
   uint4 kk[KPL / 8], qq[KPL / 8];
 #pragma unroll
   for (int p = 0; p < KPL / 8; ++p) {
-    kk[p] = tail_oct<FMT>(tk_base + ((size_t)tkc * D + KPL * kq4 + 8 * p) * EB);
+    kk[p] = tail_oct<FMT>(krow + (KPL * kq4 + 8 * p) * EB);
     qq[p] = *reinterpret_cast<const uint4*>(qrow + 8 * p);
   }
   uint2 vv[QPT];
 #pragma unroll
   for (int u = 0; u < QPT; ++u)
     vv[u] = tail_quad<FMT>(tv_base + ((size_t)(cb * CH + cv) * T + min(4 * (tq0 + u), T - 4)) * EB);
+  // this step's V value of channel cb*CH + cv, as a BF16 word (low half)
+  uint32_t vnew = 0;
+  if (step) {
+    if constexpr (FMT == 0) vnew = reinterpret_cast<const uint16_t*>(vn)[cb * CH + cv];
+    else vnew = fp8x2_to_bf16x2<FMT, false>(vn[cb * CH + cv]) & 0xFFFFu;
+  }
 
   // ---- maximum ----
   float dot = 0.0f;
@@ -1002,7 +1018,10 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
     const int t0 = 4 * (tq0 + u);
     const float v4[4] = {bf16_lo(vv[u].x), bf16_hi(vv[u].x), bf16_lo(vv[u].y), bf16_hi(vv[u].y)};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) tv += (t0 + k < ntail) ? pt[min(t0 + k, kTailTok - 1)] * v4[k] : 0.0f;
+    for (int k = 0; k < 4; ++k) {
+      const float v = (t0 + k == tnew) ? bf16_lo(vnew) : v4[k];
+      tv += (t0 + k < ntail) ? pt[min(t0 + k, kTailTok - 1)] * v : 0.0f;
+    }
   }
   for (int o = 1; o < TPC; o <<= 1) tv += __shfl_xor(tv, o);
   const int lane = tid & 63, wv = tid >> 6;
@@ -1014,6 +1033,18 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
 #pragma unroll
     for (int i = 0; i < kCombineThreads / 64; ++i) t += part[i * CH + tid];
     a.out[((size_t)si * G.Hq + hq) * D + cb * CH + tid] = f32_to_bf16_rne(t / den);
+  }
+  // decode step: the first block of the KV-head group stores the new token into the tail
+  if (step && cb == 0 && hq % G.g == 0) {
+    for (int c = tid; c < D; c += kCombineThreads) {
+      if constexpr (FMT == 0) {
+        reinterpret_cast<uint16_t*>(tk_base)[(size_t)tnew * D + c] = reinterpret_cast<const uint16_t*>(kn)[c];
+        reinterpret_cast<uint16_t*>(tv_base)[(size_t)c * T + tnew] = reinterpret_cast<const uint16_t*>(vn)[c];
+      } else {
+        tk_base[(size_t)tnew * D + c] = kn[c];
+        tv_base[(size_t)c * T + tnew] = vn[c];
+      }
+    }
   }
 }
 
@@ -1075,11 +1106,14 @@ void (*pick_combine(int n_splits))(CombineArgs) {
 }
 
 int launch_combine(const Geo& G, const DevBufs& B, const SeqList& S, const uint16_t* q, float scale, int n_splits,
-                   const float* ws_acc, const float* ws_ml, uint16_t* out, void* stream) {
+                   const float* ws_acc, const float* ws_ml, uint16_t* out, const void* k_new, const void* v_new,
+                   void* stream) {
   CombineArgs a;
   a.G = G;
   a.S = S;
-  a.tail = reinterpret_cast<const uint8_t*>(B.tail);
+  a.tail = reinterpret_cast<uint8_t*>(B.tail);
+  a.k_new = reinterpret_cast<const uint8_t*>(k_new);
+  a.v_new = reinterpret_cast<const uint8_t*>(v_new);
   a.q = q;
   a.ws_acc = ws_acc;
   a.ws_ml = ws_ml;

@@ -86,7 +86,10 @@ int launch_decode_blocks(const Geo& G, const DevBufs& B, int seq, int first, int
 // seqs.lens: tokens of the finished blocks (partials) or of the whole sequence (combine)
 int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale,
                               int n_splits, float* ws_acc, float* ws_ml, void* stream);
+// k_new / v_new (decode step, else null): each sequence's newest token, [n][Hkv][D] elements,
+// the last token of its tail (seqs.lens counts it); the kernel also stores it into the tail
 int launch_combine(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale, int n_splits,
-                   const float* ws_acc, const float* ws_ml, uint16_t* out, void* stream);
+                   const float* ws_acc, const float* ws_ml, uint16_t* out, const void* k_new, const void* v_new,
+                   void* stream);
 
 }  // namespace kvc

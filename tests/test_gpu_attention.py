@@ -220,3 +220,39 @@ def test_cfg2_full_context_sampled_heads():
         assert row_rel_err(out[:, heads], ref2) <= TOL, compressed
         del cache
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("compressed", [True, False])
+@pytest.mark.parametrize("T", [16, 64])
+def test_decode_step_equals_append_then_attention(compressed, T):
+    """kv_decode_step (the new token attended and stored by the merge kernel, or the plain
+    append + attention on block-completing steps) gives the bits of kv_encode_append followed
+    by kv_decode_attention, step after step across block boundaries, for three sequences at
+    different tail positions; the final state also matches the oracle."""
+    cfg = synth.config(0)
+    g = synth.LayerGen(cfg)
+    starts = [T - 3, 2 * T + 5, 1]
+    toks = [g.tokens(L0 + 40) for L0 in starts]
+    caches = []
+    for _ in range(2):
+        c = new_cache(Hkv=cfg.Hkv, Hq=cfg.Hq, D=cfg.D, T=T, max_seqs=3, max_blocks=(3 * T + 50) // T + 2,
+                      compressed=compressed)
+        c.calibrate(dev(toks[0][0][:cfg.n_cal]), dev(toks[0][1][:cfg.n_cal]))
+        for sid, (k, v) in enumerate(toks):
+            c.append([sid], dev(k[None, :starts[sid]]), dev(v[None, :starts[sid]]))
+        caches.append(c)
+    step_cache, ref_cache = caches
+    ids = [2, 0, 1]  # any order
+    for st in range(40):
+        kn = np.stack([toks[s][0][starts[s] + st] for s in ids])[:, None]
+        vn = np.stack([toks[s][1][starts[s] + st] for s in ids])[:, None]
+        q = dev(synth.queries(cfg, step=st)[:1].repeat(3, axis=0))
+        a = step_cache.decode_step(ids, dev(kn), dev(vn), q, cfg.scale, 3)
+        ref_cache.append(ids, dev(kn), dev(vn))
+        b = ref_cache.attention(ids, q, cfg.scale, 3)
+        assert np.array_equal(host(a), host(b)), st
+    q = synth.queries(cfg, step=99)[:1].repeat(3, axis=0)
+    out = host(step_cache.attention(ids, dev(q), cfg.scale, 2))
+    ref = _oracle(cfg, [(toks[s][0][:starts[s] + 40], toks[s][1][:starts[s] + 40]) for s in ids], q)
+    assert row_rel_err(out, ref) <= TOL
+    assert [step_cache.seq_length(s) for s in range(3)] == [L0 + 40 for L0 in starts]

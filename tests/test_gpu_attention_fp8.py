@@ -132,3 +132,23 @@ def test_fp8_full_context_sampled_heads(fmt):
         assert row_rel_err(out[:, heads], ref) <= TOL, compressed
         del cache
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_fp8_decode_step_equals_append_then_attention(fmt):
+    cfg = _cfg0(fmt)
+    g, toks = synth.sequence_tokens(cfg)
+    kx, vx = g.tokens(40)  # the stream continues past the configured 1,024 tokens
+    k, v = np.concatenate([toks[0][0], kx]), np.concatenate([toks[0][1], vx])
+    L0 = 1000
+    caches = [_fill(cfg, [(k[:L0], v[:L0])], max_blocks=18) for _ in range(2)]
+    for st in range(40):  # crosses the block boundary at 1024
+        kn, vn = dev(k[None, L0 + st:L0 + st + 1], fmt), dev(v[None, L0 + st:L0 + st + 1], fmt)
+        q = dev(synth.queries(cfg, step=st))
+        a = caches[0].decode_step([0], kn, vn, q, cfg.scale, 4)
+        caches[1].append([0], kn, vn)
+        b = caches[1].attention([0], q, cfg.scale, 4)
+        assert np.array_equal(host(a), host(b)), st
+    q = synth.queries(cfg, step=77)
+    ref = _oracle(cfg, [(k[:L0 + 40], v[:L0 + 40])], q)
+    assert row_rel_err(host(caches[0].attention([0], dev(q), cfg.scale, 4)), ref) <= TOL
