@@ -104,6 +104,28 @@ def main():
         c.append([0], kd[:, :n0].contiguous(), vd[:, :n0].contiguous())
         return c
 
+    # prefill: the bulk encode of the whole 64K-token layer (every block encoded in one launch)
+    def bulk_encode_us(compressed):
+        ts = []
+        for _ in range(3):
+            c = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=1,
+                          max_blocks_per_seq=max_blocks, num_comp_slots=n_tiles if compressed else 0,
+                          num_raw_slots=256 if compressed else n_tiles, compressed=compressed, perm_seed=7)
+            c.calibrate(dev(k0[:cfg.n_cal]), dev(v0[:cfg.n_cal]))
+            torch.cuda.synchronize()
+            a_ = torch.cuda.Event(enable_timing=True)
+            b_ = torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            c.append([0], kd, vd)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a_.elapsed_time(b_) * 1e3)
+            del c
+        return float(np.median(ts))
+    stream = torch.cuda.current_stream()
+    bulk_c, bulk_r = bulk_encode_us(True), bulk_encode_us(False)
+    log(f"[bench] bulk encode of {L0} tokens: compressed {bulk_c:.1f} us, uncompressed {bulk_r:.1f} us")
+
     log(f"[bench] building {n_layers} compressed + {n_layers} uncompressed layer caches")
     comp = [make(True, li) for li in range(n_layers)]
     raw = [make(False, li) for li in range(n_layers)]
@@ -270,6 +292,9 @@ def main():
                          "in_step_uncompressed_median": float(np.median(r_attn))},
         "append_us": {"compressed_median": float(np.median(c_app)), "uncompressed_median": float(np.median(r_app)),
                       "block_encode_append": enc_us},
+        "prefill_encode": {"tokens": L0, "compressed_us": round(bulk_c, 1), "uncompressed_us": round(bulk_r, 1),
+                           "input_GBps": round(L0 * Hkv * D * 2 * 2 / (bulk_c * 1e-6) / 1e9, 1),
+                           "note": "one kv_encode_append of the whole layer into an empty cache"},
         "combine_us": float(np.median(c_comb)),
         "host_enqueue_us_per_step": {"compressed": round(c_host, 2), "uncompressed": round(r_host, 2)},
         "uncompressed_step_us": round(r_total * 1e3 / args.steps, 3),

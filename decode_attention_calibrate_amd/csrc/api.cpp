@@ -111,7 +111,7 @@ void sizes_of(const kvc_params& p, const Geo& G, size_t out[KVC_NUM_BUFFERS]) {
   out[4] = (size_t)p.max_seqs * p.max_blocks_per_seq * 2 * G.Hkv * 4;
   out[5] = (size_t)G.n_comp * 4;
   out[6] = (size_t)G.n_raw * 4;
-  out[7] = sizeof(kvc::Counters) <= 128 ? 128 : sizeof(kvc::Counters);
+  out[7] = kvc::kCountersBytes;
 }
 
 uint64_t splitmix64(uint64_t& s) {
@@ -227,6 +227,7 @@ int kv_encode_append(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, 
   int rc = check_seq_ids(c, seq_ids_host, n_seqs);
   if (rc != KVC_OK) return rc;
   if (!k_dev || !v_dev || n_tokens < 1) return fail(KVC_EINVAL, "append needs K and V with n_tokens >= 1");
+  if (((uintptr_t)k_dev & 15u) || ((uintptr_t)v_dev & 15u)) return fail(KVC_EINVAL, "K and V must be 16-byte aligned");
   const int T = c->G.T;
   long long new_blocks = 0;
   for (int i = 0; i < n_seqs; ++i) {
@@ -421,10 +422,13 @@ int kv_get_status(kvc_cache* c, uint32_t* flags, kvc_stats* stats, void* stream)
   if (rc != KVC_OK) return rc;
   if (flags) *flags = h.status;
   if (stats) {
-    stats->comp_tiles = h.comp_tiles;
-    stats->raw_tiles = h.raw_tiles;
-    for (int i = 0; i < 3; ++i) stats->groups[i] = h.groups[i];
-    stats->esc_bytes = h.esc_bytes;
+    *stats = kvc_stats{};
+    for (const kvc::StatStripe& st : h.stat) {
+      stats->comp_tiles += st.comp_tiles;
+      stats->raw_tiles += st.raw_tiles;
+      for (int i = 0; i < 3; ++i) stats->groups[i] += st.groups[i];
+      stats->esc_bytes += st.esc_bytes;
+    }
     stats->comp_free = h.comp_top;
     stats->raw_free = h.raw_top;
   }

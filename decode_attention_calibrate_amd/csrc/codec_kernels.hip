@@ -82,9 +82,12 @@ __global__ void init_kernel(Geo G, DevBufs B) {
     c->raw_top = G.n_raw;
     c->status = 0;
     c->pad = 0;
-    c->comp_tiles = c->raw_tiles = 0;
-    c->groups[0] = c->groups[1] = c->groups[2] = 0;
-    c->esc_bytes = 0;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < kStatStripes) {
+    StatStripe& st = B.counters->stat[threadIdx.x];
+    st.comp_tiles = st.raw_tiles = 0;
+    st.groups[0] = st.groups[1] = st.groups[2] = 0;
+    st.esc_bytes = 0;
   }
 }
 
@@ -154,8 +157,31 @@ __device__ __forceinline__ int mode_planes(const Geo& G, int m) { return m == 0 
 // One block per newly full block of one (sequence, K|V, head): gathers its T tokens from the
 // old tail and the appended tokens, encodes it (or stores it raw), pops a slot and writes the
 // block-table entry.
+// Element format constants (kvc_dtype: 0 BF16, 1 FP8 E5M2, 2 FP8 E4M3).
+template <int FMT>
+struct EncFmt {
+  static constexpr int F = FMT == 0 ? 8 : (FMT == 1 ? 5 : 4);
+  static constexpr int MB = FMT == 0 ? 7 : (FMT == 1 ? 2 : 3);
+  static constexpr int EB = FMT == 0 ? 2 : 1;
+};
+
+// Place the four 3-bit fields of slot s (one per byte lane, bits 0..2) at bits 3s..3s+2 of
+// the byte lanes' 24-bit streams held in W[0..2] (byte lane k of word w = stream bits 8w..8w+7).
+template <int SL>
+__device__ __forceinline__ void place_slot(uint32_t W[3], uint32_t f) {
+  constexpr int x = 3 * SL, w = x >> 3, b = x & 7;
+  if constexpr (b <= 5) {
+    W[w] |= f << b;  // fields < 8: no bit leaves its byte lane
+  } else {
+    W[w] |= (f << b) & (b == 6 ? 0xC0C0C0C0u : 0x80808080u);
+    W[w + 1] |= (f >> (8 - b)) & (b == 6 ? 0x01010101u : 0x03030303u);
+  }
+}
+
+template <int FMT>
 __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqList S, const void* __restrict__ kin,
                                                           const void* __restrict__ vin, int n_tok) {
+  using EF = EncFmt<FMT>;
   extern __shared__ uint32_t smem[];
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);                  // [T][D] logical
   uint32_t* tagw = smem + (G.raw_elems / 2);                            // [2][PW]
@@ -173,16 +199,52 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
   const uint8_t* tail = reinterpret_cast<const uint8_t*>(B.tail) + tail_offset(G, seq, kv, h) * G.EB;
   const int tail_base = first_blk * T;
 
-  for (int i = tid; i < G.raw_elems; i += kThreads) {
-    const int t = i / D, c = i % D, p = b * T + t;
-    uint32_t x;
-    if (p < L0) {
-      const int tt = p - tail_base;
-      x = elem_at(tail, kv ? (size_t)c * T + tt : (size_t)tt * D + c, G.EB);
-    } else {
-      x = elem_at(in, (((size_t)si * n_tok + (p - L0)) * G.Hkv + h) * D + c, G.EB);
+  // Gather the block's T tokens into the LDS tile with 16-byte loads along each source's
+  // contiguous axis: tokens still in the old tail (K token-major, V channel-major), then the
+  // appended tokens (token-major input).  Unrolled so a thread's loads are in flight together.
+  {
+    constexpr int VE = 16 / EF::EB;  // elements per 16-byte vector
+    const int n_tail = min(max(L0 - b * T, 0), T);  // tokens of this block taken from the tail
+    const int tt0 = b * T - tail_base;              // tail position of the block's first token
+    const int nvpc = (n_tail + VE - 1) / VE;  // V: vectors per channel (the last one may be partial)
+    const int nvt = kv ? D * nvpc : n_tail * (D / VE);
+    const int nvi = (T - n_tail) * (D / VE);  // vectors of the appended tokens
+#pragma unroll 4
+    for (int v = tid; v < nvt; v += kThreads) {
+      int t, c, st, sc;  // first element (t, c) and the element step along the vector
+      const uint8_t* src;
+      if (kv) { c = v / nvpc; t = (v % nvpc) * VE; src = tail + ((size_t)c * T + tt0 + t) * EF::EB; st = 1; sc = 0; }
+      else { t = v / (D / VE); c = (v % (D / VE)) * VE; src = tail + ((size_t)(tt0 + t) * D + c) * EF::EB; st = 0; sc = 1; }
+      const int ne = kv ? min(VE, n_tail - t) : VE;  // elements of this vector inside the tail
+      uint4 x;
+      if (ne == VE) {
+        x = *reinterpret_cast<const uint4*>(src);
+      } else {  // the ragged end of a V channel: element by element
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        for (int e = 0; e < ne; ++e)
+          w4[e / (4 / EF::EB)] |= elem_at(src, e, EF::EB) << (8 * EF::EB * (e % (4 / EF::EB)));
+        x = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const uint32_t val = EF::EB == 2 ? (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu : (w[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+        if (e < ne) tile[(t + st * e) * D + c + sc * e] = (uint16_t)val;
+      }
     }
-    tile[i] = (uint16_t)x;
+#pragma unroll 4
+    for (int v = tid; v < nvi; v += kThreads) {
+      const int t = n_tail + v / (D / VE), c = (v % (D / VE)) * VE, p = b * T + t;
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(in) +
+                           ((((size_t)si * n_tok + (p - L0)) * G.Hkv + h) * D + c) * EF::EB;
+      const uint4 x = *reinterpret_cast<const uint4*>(src);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const uint32_t val = EF::EB == 2 ? (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu : (w[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+        tile[t * D + c + e] = (uint16_t)val;
+      }
+    }
   }
   for (int i = tid; i < 2 * G.PW; i += kThreads) tagw[i] = 0;
   if (tid < 3) sh_modes[tid] = 0;
@@ -239,14 +301,15 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
     sh_slot = slot;
     sh_raw = raw;
     if (slot >= 0) {
+      StatStripe& st = C->stat[(blockIdx.x + 7 * blockIdx.y + 3 * blockIdx.z) % kStatStripes];
       if (raw) {
-        atomicAdd(&C->raw_tiles, 1ull);
+        atomicAdd(&st.raw_tiles, 1ull);
       } else {
-        atomicAdd(&C->comp_tiles, 1ull);
-        atomicAdd(&C->groups[0], sh_modes[0]);
-        atomicAdd(&C->groups[1], sh_modes[1]);
-        atomicAdd(&C->groups[2], sh_modes[2]);
-        atomicAdd(&C->esc_bytes, (unsigned long long)(2 * total));
+        atomicAdd(&st.comp_tiles, 1ull);
+        atomicAdd(&st.groups[0], sh_modes[0]);
+        atomicAdd(&st.groups[1], sh_modes[1]);
+        atomicAdd(&st.groups[2], sh_modes[2]);
+        atomicAdd(&st.esc_bytes, (unsigned long long)(2 * total));
       }
     }
   }
@@ -278,33 +341,50 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
     if (pr >= G.NP) break;
     const PairInfo PI = pair_info(G, tile, b3, b4, pr);
     uint32_t W[3] = {0u, 0u, 0u};
-    uint32_t smw[8];  // SM words of the pair: BF16 8 (bytes), E5M2 3 (unit layout), E4M3 4 (nibbles)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) smw[i] = 0;
+    uint32_t SM[4] = {0u, 0u, 0u, 0u};  // E5M2: 3 words in the CODE unit layout; E4M3: 4 words of nibbles
+    uint32_t smb[8];                      // BF16: the 8 SM words (one byte per element)
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       const int q = 2 * pr + gi, tg = q / D, c = q % D;
-      const int np = mode_planes(G, PI.mode[gi]);
+      const uint32_t base = PI.base[gi];
       // escape units: [0] = plane of offset bit 3; a raw BF16 group adds [1..4] = 4-bit fields
-      // of offset bits 4..7 (token tau at bits 4*tau.. of the 64-bit little-endian run), a raw
-      // E5M2 group adds [1] = plane of offset bit 4
+      // of offset bits 4..7 (token tau at bits 4*(tau%4) of unit 1 + tau/4), a raw E5M2 group
+      // adds [1] = plane of offset bit 4
       uint32_t units[5] = {0u, 0u, 0u, 0u, 0u};
-      for (int tau = 0; tau < kGroup; ++tau) {
-        const uint32_t x = tile[(tg * kGroup + tau) * D + c];
-        const uint32_t o = exp_of(G, x) - PI.base[gi];
-        const int r = gi * kGroup + tau, lk = r & 3, s = r >> 2;
-        const uint32_t code = o & 7u, f = sm_of(G, x);
-        for (int bb = 0; bb < 3; ++bb) {
-          const int xs = 3 * s + bb;
-          W[xs >> 3] |= ((code >> bb) & 1u) << (8 * lk + (xs & 7));
-          if (G.MB == 2) smw[xs >> 3] |= ((f >> bb) & 1u) << (8 * lk + (xs & 7));
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        uint32_t cf = 0, sf = 0;  // this slot's code / sign-mantissa fields, one per byte lane
+#pragma unroll
+        for (int lk = 0; lk < 4; ++lk) {
+          const int tau = 4 * t4 + lk;
+          const uint32_t x = tile[(tg * kGroup + tau) * D + c];
+          const uint32_t o = ((x >> EF::MB) & ((1u << EF::F) - 1u)) - base;
+          const uint32_t f = ((x >> (EF::MB + EF::F)) << EF::MB) | (x & ((1u << EF::MB) - 1u));
+          cf |= (o & 7u) << (8 * lk);
+          sf |= f << (8 * lk);
+          units[0] |= ((o >> 3) & 1u) << tau;
+          if constexpr (EF::F == 8) units[1 + t4] |= ((o >> 4) & 0xFu) << (4 * lk);
+          if constexpr (EF::F == 5) units[1] |= ((o >> 4) & 1u) << tau;
         }
-        if (G.MB == 7) smw[r >> 2] |= f << (8 * (r & 3));
-        if (G.MB == 3) smw[r >> 3] |= f << (4 * (r & 7));
-        units[0] |= ((o >> 3) & 1u) << tau;
-        if (G.F == 8) units[1 + (tau >> 2)] |= ((o >> 4) & 0xFu) << (4 * (tau & 3));
-        if (G.F == 5) units[1] |= ((o >> 4) & 1u) << tau;
+        const int sl = 4 * gi + t4;  // slot of the unit (elements 4*sl .. 4*sl+3)
+        switch (sl) {
+          case 0: place_slot<0>(W, cf); if constexpr (FMT == 1) place_slot<0>(SM, sf); break;
+          case 1: place_slot<1>(W, cf); if constexpr (FMT == 1) place_slot<1>(SM, sf); break;
+          case 2: place_slot<2>(W, cf); if constexpr (FMT == 1) place_slot<2>(SM, sf); break;
+          case 3: place_slot<3>(W, cf); if constexpr (FMT == 1) place_slot<3>(SM, sf); break;
+          case 4: place_slot<4>(W, cf); if constexpr (FMT == 1) place_slot<4>(SM, sf); break;
+          case 5: place_slot<5>(W, cf); if constexpr (FMT == 1) place_slot<5>(SM, sf); break;
+          case 6: place_slot<6>(W, cf); if constexpr (FMT == 1) place_slot<6>(SM, sf); break;
+          default: place_slot<7>(W, cf); if constexpr (FMT == 1) place_slot<7>(SM, sf); break;
+        }
+        if constexpr (FMT == 0) smb[sl] = sf;
+        if constexpr (FMT == 2) {  // four nibbles: element 4sl + lk at bits 4*(4*(sl%2) + lk) of word sl/2
+          const uint32_t t = sf | (sf >> 4);
+          const uint32_t nib16 = (t & 0xFFu) | ((t >> 8) & 0xFF00u);
+          SM[sl >> 1] |= nib16 << (16 * (sl & 1));
+        }
       }
+      const int np = mode_planes(G, PI.mode[gi]);
       uint16_t* esc16 = reinterpret_cast<uint16_t*>(dst + G.esc_off);
       for (int p = 0; p < np; ++p) esc16[P + p] = (uint16_t)units[p];
       P += np;
@@ -316,7 +396,14 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
     code[1] = W[1];
     code[2] = W[2];
     uint32_t* smd = reinterpret_cast<uint32_t*>(dst + G.sm_off + G.sm_pair * pr);
-    for (int i = 0; i < G.sm_pair / 4; ++i) smd[i] = smw[i];
+    if constexpr (FMT == 0) {
+      *reinterpret_cast<uint4*>(smd) = make_uint4(smb[0], smb[1], smb[2], smb[3]);
+      *reinterpret_cast<uint4*>(smd + 4) = make_uint4(smb[4], smb[5], smb[6], smb[7]);
+    } else if constexpr (FMT == 1) {
+      smd[0] = SM[0]; smd[1] = SM[1]; smd[2] = SM[2];
+    } else {
+      *reinterpret_cast<uint4*>(smd) = make_uint4(SM[0], SM[1], SM[2], SM[3]);
+    }
   }
   // zero the unused escape bytes [2*total, esc_cap)
   {
@@ -518,8 +605,10 @@ int launch_append(const Geo& G, const DevBufs& B, const SeqList& S, const void* 
                   int max_new_blocks, void* stream) {
   if (max_new_blocks > 0) {
     const size_t lds = (size_t)G.raw_elems * 2 + (size_t)2 * G.PW * 4;
-    hipLaunchKernelGGL(encode_kernel, dim3(max_new_blocks, S.n, 2 * G.Hkv), dim3(kThreads), lds,
-                       (hipStream_t)stream, G, B, S, k, v, n_tokens);
+    void (*kern)(Geo, DevBufs, SeqList, const void*, const void*, int) =
+        G.fmt == 0 ? encode_kernel<0> : (G.fmt == 1 ? encode_kernel<1> : encode_kernel<2>);
+    hipLaunchKernelGGL(kern, dim3(max_new_blocks, S.n, 2 * G.Hkv), dim3(kThreads), lds, (hipStream_t)stream, G, B,
+                       S, k, v, n_tokens);
     const int err = (int)hipGetLastError();
     if (err) return err;
   }

@@ -42,12 +42,20 @@ struct Geo {
   int compressed;
 };
 
-// counters buffer (128 bytes)
+// counters buffer (1 KB).  The statistics are spread over kStatStripes copies (one chosen per
+// encoding workgroup) so concurrent encodes do not all update the same few words; readers add
+// the stripes.
+constexpr int kStatStripes = 16;
+struct StatStripe {
+  unsigned long long comp_tiles, raw_tiles, groups[3], esc_bytes;
+};
 struct Counters {
   int32_t comp_top, raw_top;
   uint32_t status, pad;
-  unsigned long long comp_tiles, raw_tiles, groups[3], esc_bytes;
+  StatStripe stat[kStatStripes];
 };
+constexpr size_t kCountersBytes = 1024;
+static_assert(sizeof(Counters) <= kCountersBytes, "counters buffer");
 
 struct DevBufs {
   uint8_t* comp_pool;

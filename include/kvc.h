@@ -88,7 +88,7 @@ typedef struct {
                         bytes used in 16-byte units, bits 0..23 = slot index                */
   void* comp_free;   /* [num_comp_slots] int32 free stack of compressed slots               */
   void* raw_free;    /* [num_raw_slots] int32 free stack of raw slots                       */
-  void* counters;    /* 128 bytes: int32 stack tops, uint32 status, uint64 statistics       */
+  void* counters;    /* 1 KB: int32 stack tops, uint32 status, uint64 statistics (striped)  */
 } kvc_buffers;
 
 #define KVC_NUM_BUFFERS 8
@@ -125,7 +125,8 @@ void kv_cache_destroy(kvc_cache* cache);
 int kv_calibrate(kvc_cache* cache, const void* k_dev, const void* v_dev, int32_t n_tokens, void* stream);
 
 /* Appends n_tokens tokens to each listed sequence (GAAC page §3.3, fill-then-finalize).
- * k_dev, v_dev: [n_seqs][n_tokens][Hkv][D] elements.  Tokens go to the sequence's tail; each
+ * k_dev, v_dev: [n_seqs][n_tokens][Hkv][D] elements, 16-byte aligned (KVC_EINVAL otherwise).
+ * Tokens go to the sequence's tail; each
  * block that becomes full is encoded once into a compressed slot, or stored raw when its
  * escape planes exceed the capacity (or when compressed == 0), and its table entry is written.
  * n_tokens == 1 is a decode step; larger values are a bulk (prefill) append.  seq_ids_host:

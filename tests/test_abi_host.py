@@ -64,7 +64,7 @@ def test_slot_stride_matches_format(K, T, D, fmt):
     assert sz[2] == 2 * 2 * 8 * T * D * eb
     assert sz[3] == 4 * 8 * D
     assert sz[4] == 2 * 1024 * 2 * 8 * 4
-    assert sz[5] == 2048 * 4 and sz[6] == 64 * 4 and sz[7] == 128
+    assert sz[5] == 2048 * 4 and sz[6] == 64 * 4 and sz[7] == 1024
 
 
 @pytest.mark.parametrize("kw,code", [
