@@ -290,6 +290,12 @@ static int check_attention_args(kvc_cache* c, const int32_t* seq_ids_host, int32
   return KVC_OK;
 }
 
+static int check_out(const void* out_dev) {
+  if (!out_dev) return fail(KVC_EINVAL, "out must not be NULL");
+  if ((uintptr_t)out_dev & 15u) return fail(KVC_EINVAL, "out must be 16-byte aligned");
+  return KVC_OK;
+}
+
 int kv_attention_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev, float scale,
                           int32_t n_splits, void* ws_dev, size_t ws_bytes, void* stream) {
   int rc = check_attention_args(c, seq_ids_host, n_seqs, q_dev, n_splits, ws_dev, ws_bytes);
@@ -317,7 +323,8 @@ int kv_attention_combine(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_se
                          int32_t n_splits, const void* ws_dev, size_t ws_bytes, void* out_dev, void* stream) {
   int rc = check_attention_args(c, seq_ids_host, n_seqs, q_dev, n_splits, ws_dev, ws_bytes);
   if (rc != KVC_OK) return rc;
-  if (!out_dev) return fail(KVC_EINVAL, "out must not be NULL");
+  rc = check_out(out_dev);
+  if (rc != KVC_OK) return rc;
   const Geo& G = c->G;
   const float* acc = (const float*)ws_dev;
   const float* ml = acc + (size_t)n_seqs * G.Hq * n_splits * G.D;
@@ -339,7 +346,7 @@ int kv_attention_combine(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_se
 
 int kv_decode_attention(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev, float scale,
                         int32_t n_splits, void* ws_dev, size_t ws_bytes, void* out_dev, void* stream) {
-  if (!out_dev) return fail(KVC_EINVAL, "out must not be NULL");
+  if (check_out(out_dev) != KVC_OK) return KVC_EINVAL;
   const int rc = kv_attention_partials(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, stream);
   if (rc != KVC_OK) return rc;
   return kv_attention_combine(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, out_dev, stream);
@@ -351,7 +358,9 @@ int kv_decode_step(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, co
   if (!c) return fail(KVC_EINVAL, "cache is NULL");
   int rc = check_seq_ids(c, seq_ids_host, n_seqs);
   if (rc != KVC_OK) return rc;
-  if (!k_new_dev || !v_new_dev || !out_dev) return fail(KVC_EINVAL, "k_new, v_new and out must not be NULL");
+  if (!k_new_dev || !v_new_dev) return fail(KVC_EINVAL, "k_new and v_new must not be NULL");
+  rc = check_out(out_dev);
+  if (rc != KVC_OK) return rc;
   if (((uintptr_t)k_new_dev & 15u) || ((uintptr_t)v_new_dev & 15u))
     return fail(KVC_EINVAL, "k_new and v_new must be 16-byte aligned");
   const Geo& G = c->G;

@@ -149,7 +149,8 @@ size_t kv_attention_workspace_bytes(const kvc_params* params, int32_t n_seqs, in
  *   out[s][hq][c] = sum_t softmax_t(scale * q[s][hq] . k_t) v_t[c]
  * over every token of the sequence (finished blocks, compressed or raw, and the tail), with
  * query head hq reading KV head hq / (Hq / Hkv).  q_dev: [n_seqs][Hq][D] BF16; out_dev:
- * [n_seqs][Hq][D] BF16 (round-to-nearest-even of an fp32 result).  The finished blocks of each
+ * [n_seqs][Hq][D] BF16 (round-to-nearest-even of an fp32 result); q, out and the workspace
+ * 16-byte aligned (KVC_EINVAL otherwise).  The finished blocks of each
  * sequence are split into n_splits contiguous ranges of 64 tokens processed in parallel
  * (1 <= n_splits <= 1024); their partial results and the tail are merged by log-sum-exp.
  * Every listed sequence must hold at least one token (KVC_EINVAL otherwise). */
