@@ -62,7 +62,8 @@ int check_params(const kvc_params* p) {
   if (p->compressed && p->num_comp_slots < 1) return fail(KVC_EINVAL, "a compressed cache needs compressed slots");
   if (!p->compressed && p->num_raw_slots < 1) return fail(KVC_EINVAL, "an uncompressed cache needs raw slots");
   // valid requests the kernels of this build do not implement
-  if (p->group_tokens != kvc::kGroup) return fail(KVC_EUNSUPPORTED, "these kernels implement 16-token groups");
+  if (p->group_tokens != 16 && p->group_tokens != 8)
+    return fail(KVC_EUNSUPPORTED, "these kernels implement 16- and 8-token groups");
   if (p->block_tokens != 16 && p->block_tokens != 32 && p->block_tokens != 64)
     return fail(KVC_EUNSUPPORTED, "these kernels implement block_tokens 16, 32 or 64");
   if (cap > 512) return fail(KVC_EUNSUPPORTED, "these kernels implement esc_cap_bytes <= 512");
@@ -84,7 +85,8 @@ Geo make_geo(const kvc_params& p) {
   G.Hkv = p.num_kv_heads;
   G.Hq = p.num_q_heads;
   G.g = p.num_q_heads / p.num_kv_heads;
-  G.NT = G.T / kvc::kGroup;
+  G.GT = p.group_tokens;
+  G.NT = G.T / G.GT;
   G.NG = G.NT * G.D;
   G.NP = G.NG / 2;
   G.PW = (G.NG + 31) / 32;
@@ -275,10 +277,18 @@ size_t kv_attention_workspace_bytes(const kvc_params* p, int32_t n_seqs, int32_t
 }
 
 // Shared argument checks of the attention calls.
+static int check_group_tokens_for_attention(const kvc_cache* c) {
+  if (c->G.compressed && c->G.GT != kvc::kGroup)
+    return fail(KVC_EUNSUPPORTED, "the attention kernels rebuild 16-token groups; this cache uses 8-token groups");
+  return KVC_OK;
+}
+
 static int check_attention_args(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
                                 int32_t n_splits, const void* ws_dev, size_t ws_bytes) {
   if (!c) return fail(KVC_EINVAL, "cache is NULL");
-  int rc = check_seq_ids(c, seq_ids_host, n_seqs);
+  int rc = check_group_tokens_for_attention(c);
+  if (rc != KVC_OK) return rc;
+  rc = check_seq_ids(c, seq_ids_host, n_seqs);
   if (rc != KVC_OK) return rc;
   if (!q_dev || !ws_dev) return fail(KVC_EINVAL, "q and workspace must not be NULL");
   if (n_splits < 1 || n_splits > 1024) return fail(KVC_EINVAL, "n_splits must be in 1..1024");
@@ -356,7 +366,9 @@ int kv_decode_step(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, co
                    const void* v_new_dev, const void* q_dev, float scale, int32_t n_splits, void* ws_dev, size_t ws_bytes,
                    void* out_dev, void* stream) {
   if (!c) return fail(KVC_EINVAL, "cache is NULL");
-  int rc = check_seq_ids(c, seq_ids_host, n_seqs);
+  int rc = check_group_tokens_for_attention(c);  // before the append changes anything
+  if (rc != KVC_OK) return rc;
+  rc = check_seq_ids(c, seq_ids_host, n_seqs);
   if (rc != KVC_OK) return rc;
   if (!k_new_dev || !v_new_dev) return fail(KVC_EINVAL, "k_new and v_new must not be NULL");
   rc = check_out(out_dev);
@@ -364,6 +376,13 @@ int kv_decode_step(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, co
   if (((uintptr_t)k_new_dev & 15u) || ((uintptr_t)v_new_dev & 15u))
     return fail(KVC_EINVAL, "k_new and v_new must be 16-byte aligned");
   const Geo& G = c->G;
+  for (int i = 0; i < n_seqs; ++i)
+    if (c->len[seq_ids_host[i]] >= INT32_MAX - 1) return fail(KVC_EINVAL, "sequence too long");
+  // the attention arguments are checked against the lengths after the append, before anything runs
+  for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] += 1;
+  rc = check_attention_args(c, seq_ids_host, n_seqs, q_dev, n_splits, ws_dev, ws_bytes);
+  for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] -= 1;
+  if (rc != KVC_OK) return rc;
   bool completes = false;  // does this token finish a block of some listed sequence?
   for (int i = 0; i < n_seqs; ++i) completes |= (c->len[seq_ids_host[i]] + 1) % G.T == 0;
   if (completes) {  // the block must be encoded first: the append, then both attention halves
@@ -371,12 +390,9 @@ int kv_decode_step(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, co
     if (rc != KVC_OK) return rc;
     return kv_decode_attention(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, out_dev, stream);
   }
-  for (int i = 0; i < n_seqs; ++i)
-    if (c->len[seq_ids_host[i]] >= INT32_MAX - 1) return fail(KVC_EINVAL, "sequence too long");
   // the finished blocks do not change: split attention over them as they are
-  for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] += 1;  // the checks below see the new token
-  rc = check_attention_args(c, seq_ids_host, n_seqs, q_dev, n_splits, ws_dev, ws_bytes);
-  if (rc == KVC_OK) rc = kv_attention_partials(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, stream);
+  for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] += 1;
+  rc = kv_attention_partials(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, stream);
   if (rc != KVC_OK) {
     for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] -= 1;
     return rc;

@@ -150,9 +150,117 @@ __device__ __forceinline__ PairInfo pair_info(const Geo& G, const uint16_t* tile
   return P;
 }
 
-// 16-bit escape units of a group: none (narrow), one plane (wide), F - 3 units (raw: bit 3,
+// GT-bit escape units of a group: none (narrow), one plane (wide), F - 3 units (raw: bit 3,
 // then BF16 bits 4..7 as four units of nibbles, E5M2 bit 4 as one more plane).
 __device__ __forceinline__ int mode_planes(const Geo& G, int m) { return m == 0 ? 0 : (m == 1 ? 1 : G.F - 3); }
+
+// Gathers block b's T tokens into the LDS tile [T][D] with 16-byte loads along each source's
+// contiguous axis: tokens still in the old tail (K token-major, V channel-major), then the
+// appended tokens (token-major input, 16-byte aligned).  Unrolled so a thread's loads are in
+// flight together.
+template <int EB>
+__device__ __forceinline__ void gather_block(const Geo& G, const uint8_t* tail, const void* in, int si, int h, int kv,
+                                             int b, int L0, int n_tok, int tail_base, uint16_t* tile) {
+  const int tid = threadIdx.x, D = G.D, T = G.T;
+  constexpr int VE = 16 / EB;  // elements per 16-byte vector
+  const int n_tail = min(max(L0 - b * T, 0), T);  // tokens of this block taken from the tail
+  const int tt0 = b * T - tail_base;              // tail position of the block's first token
+  const int nvpc = (n_tail + VE - 1) / VE;  // V: vectors per channel (the last one may be partial)
+  const int nvt = kv ? D * nvpc : n_tail * (D / VE);
+  const int nvi = (T - n_tail) * (D / VE);  // vectors of the appended tokens
+#pragma unroll 4
+  for (int v = tid; v < nvt; v += kThreads) {
+    int t, c, st, sc;  // first element (t, c) and the element step along the vector
+    const uint8_t* src;
+    if (kv) { c = v / nvpc; t = (v % nvpc) * VE; src = tail + ((size_t)c * T + tt0 + t) * EB; st = 1; sc = 0; }
+    else { t = v / (D / VE); c = (v % (D / VE)) * VE; src = tail + ((size_t)(tt0 + t) * D + c) * EB; st = 0; sc = 1; }
+    const int ne = kv ? min(VE, n_tail - t) : VE;  // elements of this vector inside the tail
+    uint4 x;
+    if (ne == VE) {
+      x = *reinterpret_cast<const uint4*>(src);
+    } else {  // the ragged end of a V channel: element by element
+      uint32_t w4[4] = {0u, 0u, 0u, 0u};
+      for (int e = 0; e < ne; ++e)
+        w4[e / (4 / EB)] |= elem_at(src, e, EB) << (8 * EB * (e % (4 / EB)));
+      x = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const uint32_t val = EB == 2 ? (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu : (w[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+      if (e < ne) tile[(t + st * e) * D + c + sc * e] = (uint16_t)val;
+    }
+  }
+#pragma unroll 4
+  for (int v = tid; v < nvi; v += kThreads) {
+    const int t = n_tail + v / (D / VE), c = (v % (D / VE)) * VE, p = b * T + t;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(in) +
+                         ((((size_t)si * n_tok + (p - L0)) * G.Hkv + h) * D + c) * EB;
+    const uint4 x = *reinterpret_cast<const uint4*>(src);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const uint32_t val = EB == 2 ? (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu : (w[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+      tile[t * D + c + e] = (uint16_t)val;
+    }
+  }
+}
+
+// Pops a slot for one tile (raw or compressed, falling back to raw when the compressed pool is
+// empty) and adds the tile to the statistics.  Thread 0 only; returns the slot (-1: both pools
+// empty) and sets *raw.
+__device__ int pop_slot(const DevBufs& B, int want_raw, const unsigned long long modes[3], int esc_bytes, int* raw_out) {
+Counters* C = B.counters;
+int slot = -1, raw = want_raw;
+if (!raw) {
+  const int idx = atomicSub(&C->comp_top, 1) - 1;
+  if (idx >= 0) {
+    slot = B.comp_free[idx];
+  } else {
+    atomicAdd(&C->comp_top, 1);
+    atomicOr(&C->status, 1u);
+    raw = 1;
+  }
+}
+if (raw) {
+  const int idx = atomicSub(&C->raw_top, 1) - 1;
+  if (idx >= 0) {
+    slot = B.raw_free[idx];
+  } else {
+    atomicAdd(&C->raw_top, 1);
+    atomicOr(&C->status, 2u);
+  }
+}
+if (slot >= 0) {
+  StatStripe& st = C->stat[(blockIdx.x + 7 * blockIdx.y + 3 * blockIdx.z) % kStatStripes];
+  if (raw) {
+    atomicAdd(&st.raw_tiles, 1ull);
+  } else {
+    atomicAdd(&st.comp_tiles, 1ull);
+    atomicAdd(&st.groups[0], modes[0]);
+    atomicAdd(&st.groups[1], modes[1]);
+    atomicAdd(&st.groups[2], modes[2]);
+    atomicAdd(&st.esc_bytes, (unsigned long long)esc_bytes);
+  }
+}
+*raw_out = raw;
+return slot;
+}
+
+// Stores the LDS tile [T][D] as a raw tile (K token-major, V channel-major) and its table entry.
+__device__ void store_raw_tile(const Geo& G, const DevBufs& B, int slot, int kv, const uint16_t* tile, size_t entry_idx) {
+  const int D = G.D, T = G.T;
+  uint8_t* dst = reinterpret_cast<uint8_t*>(B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
+  for (int i = threadIdx.x; i < G.raw_elems; i += blockDim.x) {
+    if (kv) {
+      const int c = i / T, t = i % T;
+      elem_put(dst, i, G.EB, tile[t * D + c]);
+    } else {
+      elem_put(dst, i, G.EB, tile[i]);
+    }
+  }
+  if (threadIdx.x == 0) B.table[entry_idx] = (uint32_t)slot | 0x80000000u;
+}
 
 // One block per newly full block of one (sequence, K|V, head): gathers its T tokens from the
 // old tail and the appended tokens, encodes it (or stores it raw), pops a slot and writes the
@@ -199,53 +307,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
   const uint8_t* tail = reinterpret_cast<const uint8_t*>(B.tail) + tail_offset(G, seq, kv, h) * G.EB;
   const int tail_base = first_blk * T;
 
-  // Gather the block's T tokens into the LDS tile with 16-byte loads along each source's
-  // contiguous axis: tokens still in the old tail (K token-major, V channel-major), then the
-  // appended tokens (token-major input).  Unrolled so a thread's loads are in flight together.
-  {
-    constexpr int VE = 16 / EF::EB;  // elements per 16-byte vector
-    const int n_tail = min(max(L0 - b * T, 0), T);  // tokens of this block taken from the tail
-    const int tt0 = b * T - tail_base;              // tail position of the block's first token
-    const int nvpc = (n_tail + VE - 1) / VE;  // V: vectors per channel (the last one may be partial)
-    const int nvt = kv ? D * nvpc : n_tail * (D / VE);
-    const int nvi = (T - n_tail) * (D / VE);  // vectors of the appended tokens
-#pragma unroll 4
-    for (int v = tid; v < nvt; v += kThreads) {
-      int t, c, st, sc;  // first element (t, c) and the element step along the vector
-      const uint8_t* src;
-      if (kv) { c = v / nvpc; t = (v % nvpc) * VE; src = tail + ((size_t)c * T + tt0 + t) * EF::EB; st = 1; sc = 0; }
-      else { t = v / (D / VE); c = (v % (D / VE)) * VE; src = tail + ((size_t)(tt0 + t) * D + c) * EF::EB; st = 0; sc = 1; }
-      const int ne = kv ? min(VE, n_tail - t) : VE;  // elements of this vector inside the tail
-      uint4 x;
-      if (ne == VE) {
-        x = *reinterpret_cast<const uint4*>(src);
-      } else {  // the ragged end of a V channel: element by element
-        uint32_t w4[4] = {0u, 0u, 0u, 0u};
-        for (int e = 0; e < ne; ++e)
-          w4[e / (4 / EF::EB)] |= elem_at(src, e, EF::EB) << (8 * EF::EB * (e % (4 / EF::EB)));
-        x = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-      }
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        const uint32_t val = EF::EB == 2 ? (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu : (w[e >> 2] >> (8 * (e & 3))) & 0xFFu;
-        if (e < ne) tile[(t + st * e) * D + c + sc * e] = (uint16_t)val;
-      }
-    }
-#pragma unroll 4
-    for (int v = tid; v < nvi; v += kThreads) {
-      const int t = n_tail + v / (D / VE), c = (v % (D / VE)) * VE, p = b * T + t;
-      const uint8_t* src = reinterpret_cast<const uint8_t*>(in) +
-                           ((((size_t)si * n_tok + (p - L0)) * G.Hkv + h) * D + c) * EF::EB;
-      const uint4 x = *reinterpret_cast<const uint4*>(src);
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        const uint32_t val = EF::EB == 2 ? (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu : (w[e >> 2] >> (8 * (e & 3))) & 0xFFu;
-        tile[t * D + c + e] = (uint16_t)val;
-      }
-    }
-  }
+  gather_block<EF::EB>(G, tail, in, si, h, kv, b, L0, n_tok, tail_base, tile);
   for (int i = tid; i < 2 * G.PW; i += kThreads) tagw[i] = 0;
   if (tid < 3) sh_modes[tid] = 0;
   __syncthreads();
@@ -276,43 +338,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
     }
   }
 
-  if (tid == 0) {
-    Counters* C = B.counters;
-    int slot = -1, raw = is_raw;
-    if (!raw) {
-      const int idx = atomicSub(&C->comp_top, 1) - 1;
-      if (idx >= 0) {
-        slot = B.comp_free[idx];
-      } else {
-        atomicAdd(&C->comp_top, 1);
-        atomicOr(&C->status, 1u);
-        raw = 1;
-      }
-    }
-    if (raw) {
-      const int idx = atomicSub(&C->raw_top, 1) - 1;
-      if (idx >= 0) {
-        slot = B.raw_free[idx];
-      } else {
-        atomicAdd(&C->raw_top, 1);
-        atomicOr(&C->status, 2u);
-      }
-    }
-    sh_slot = slot;
-    sh_raw = raw;
-    if (slot >= 0) {
-      StatStripe& st = C->stat[(blockIdx.x + 7 * blockIdx.y + 3 * blockIdx.z) % kStatStripes];
-      if (raw) {
-        atomicAdd(&st.raw_tiles, 1ull);
-      } else {
-        atomicAdd(&st.comp_tiles, 1ull);
-        atomicAdd(&st.groups[0], sh_modes[0]);
-        atomicAdd(&st.groups[1], sh_modes[1]);
-        atomicAdd(&st.groups[2], sh_modes[2]);
-        atomicAdd(&st.esc_bytes, (unsigned long long)(2 * total));
-      }
-    }
-  }
+  if (tid == 0) sh_slot = pop_slot(B, is_raw, sh_modes, 2 * total, &sh_raw);
   __syncthreads();
   const int slot = sh_slot, raw = sh_raw;
   if (slot < 0) {
@@ -321,16 +347,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
   }
 
   if (raw) {
-    uint8_t* dst = reinterpret_cast<uint8_t*>(B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
-    for (int i = tid; i < G.raw_elems; i += kThreads) {
-      if (kv) {
-        const int c = i / T, t = i % T;
-        elem_put(dst, i, G.EB, tile[t * D + c]);
-      } else {
-        elem_put(dst, i, G.EB, tile[i]);
-      }
-    }
-    if (tid == 0) B.table[entry_idx] = (uint32_t)slot | 0x80000000u;
+    store_raw_tile(G, B, slot, kv, tile, entry_idx);
     return;
   }
 
@@ -421,6 +438,150 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
   }
 }
 
+// Any group size (8-token groups; 16 works too): the slot is assembled in LDS by OR-ing every
+// field into zeroed words at the bit positions FORMAT v1 gives it, then copied out whole.
+// One 256-thread workgroup per new tile, as encode_kernel.
+// ORs the low nbits (<= 32) of val into an LSB-first bit stream of LDS words at bit bp.
+__device__ __forceinline__ void or_bits(uint32_t* words, int bp, uint32_t val, int nbits) {
+  const int w = bp >> 5, sh = bp & 31;
+  atomicOr(&words[w], val << sh);
+  if (sh + nbits > 32) atomicOr(&words[w + 1], val >> (32 - sh));
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(kThreads) encode_any_kernel(Geo G, DevBufs B, SeqList S, const void* __restrict__ kin,
+                                                              const void* __restrict__ vin, int n_tok) {
+  using EF = EncFmt<FMT>;
+  extern __shared__ uint32_t smem[];
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);                        // [T][D] logical
+  uint32_t* slotw = smem + G.raw_elems / 2;                                   // the slot, stride bytes
+  uint16_t* gP = reinterpret_cast<uint16_t*>(slotw + G.stride / 4);           // [NG] escape units before q
+  uint8_t* gm = reinterpret_cast<uint8_t*>(gP + G.NG);                        // [NG] group modes
+  __shared__ int red[8];
+  __shared__ int sh_slot, sh_raw;
+  __shared__ unsigned long long sh_modes[3];
+
+  const int si = blockIdx.y, kv = blockIdx.z / G.Hkv, h = blockIdx.z % G.Hkv;
+  const int seq = S.ids[si], L0 = S.lens[si];
+  const int first_blk = L0 / G.T, last_full = (L0 + n_tok) / G.T;
+  const int b = first_blk + blockIdx.x;
+  if (b >= last_full) return;
+  const int tid = threadIdx.x, D = G.D, GT = G.GT, NG = G.NG;
+  const uint8_t* tail = reinterpret_cast<const uint8_t*>(B.tail) + tail_offset(G, seq, kv, h) * G.EB;
+  gather_block<EF::EB>(G, tail, kv ? vin : kin, si, h, kv, b, L0, n_tok, first_blk * G.T, tile);
+  for (int i = tid; i < G.stride / 4; i += kThreads) slotw[i] = 0u;
+  __syncthreads();
+
+  const uint8_t* b3 = B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
+  const uint8_t* b4 = B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;
+  // modes; each thread takes consecutive groups, so a block scan gives every group's escape offset
+  const int per = (NG + kThreads - 1) / kThreads, q0 = min(NG, tid * per), q1 = min(NG, q0 + per);
+  int units = 0, cnt[3] = {0, 0, 0};
+  if (G.compressed) {
+    for (int q = q0; q < q1; ++q) {
+      const int tg = q / D, c = q % D;
+      uint32_t mn = 255, mx = 0;
+      for (int tau = 0; tau < GT; ++tau) {
+        const uint32_t e = exp_of(G, tile[(tg * GT + tau) * D + c]);
+        mn = min(mn, e);
+        mx = max(mx, e);
+      }
+      const int m = choose_mode(mn, mx, b3[c], b4[c], EF::F > 4);
+      gm[q] = (uint8_t)m;
+      cnt[m]++;
+      units += mode_planes(G, m);
+    }
+  }
+  int total;
+  int P = block_exclusive_scan(units, red, &total);
+  for (int q = q0; q < q1 && G.compressed; ++q) {
+    gP[q] = (uint16_t)P;
+    P += mode_planes(G, gm[q]);
+  }
+  const int esc_bytes = (total * GT + 7) / 8;
+  for (int m = 0; m < 3; ++m) {
+    const int sm = block_sum(cnt[m], red);
+    if (tid == 0) sh_modes[m] = (unsigned long long)sm;
+  }
+  if (tid == 0) sh_slot = pop_slot(B, (!G.compressed || esc_bytes > G.esc_cap) ? 1 : 0, sh_modes, esc_bytes, &sh_raw);
+  __syncthreads();
+  const int slot = sh_slot, raw = sh_raw;
+  const size_t entry_idx = table_index(G, seq, b, kv, h);
+  if (slot < 0) {
+    if (tid == 0) B.table[entry_idx] = kUnallocated;
+    return;
+  }
+  if (raw) {
+    store_raw_tile(G, B, slot, kv, tile, entry_idx);
+    return;
+  }
+
+  // one element quad per step: elements n0 .. n0+3 = tokens tau0 .. tau0+3 of group q
+  const int esc_bit0 = 8 * G.esc_off;
+  for (int k = tid; k < G.raw_elems / 4; k += kThreads) {
+    const int n0 = 4 * k, q = n0 / GT, tau0 = n0 % GT, tg = q / D, c = q % D;
+    const int m = gm[q];
+    const uint32_t base = m == 0 ? b3[c] : (m == 1 ? b4[c] : 0u);
+    uint32_t cf = 0, sf = 0, e3 = 0, hi = 0;
+#pragma unroll
+    for (int lk = 0; lk < 4; ++lk) {
+      const uint32_t x = tile[(tg * GT + tau0 + lk) * D + c];
+      const uint32_t o = exp_of(G, x) - base;
+      cf |= (o & 7u) << (8 * lk);
+      sf |= sm_of(G, x) << (8 * lk);
+      e3 |= ((o >> 3) & 1u) << lk;
+      if constexpr (EF::F == 8) hi |= ((o >> 4) & 0xFu) << (4 * lk);
+      if constexpr (EF::F == 5) hi |= ((o >> 4) & 1u) << lk;
+    }
+    // CODE (and the E5M2 SM fields): slot s of 32-element unit u
+    const int u = n0 >> 5, sl = (n0 & 31) >> 2;
+    uint32_t W[3] = {0u, 0u, 0u}, SMW[3] = {0u, 0u, 0u};
+    switch (sl) {
+      case 0: place_slot<0>(W, cf); if constexpr (FMT == 1) place_slot<0>(SMW, sf); break;
+      case 1: place_slot<1>(W, cf); if constexpr (FMT == 1) place_slot<1>(SMW, sf); break;
+      case 2: place_slot<2>(W, cf); if constexpr (FMT == 1) place_slot<2>(SMW, sf); break;
+      case 3: place_slot<3>(W, cf); if constexpr (FMT == 1) place_slot<3>(SMW, sf); break;
+      case 4: place_slot<4>(W, cf); if constexpr (FMT == 1) place_slot<4>(SMW, sf); break;
+      case 5: place_slot<5>(W, cf); if constexpr (FMT == 1) place_slot<5>(SMW, sf); break;
+      case 6: place_slot<6>(W, cf); if constexpr (FMT == 1) place_slot<6>(SMW, sf); break;
+      default: place_slot<7>(W, cf); if constexpr (FMT == 1) place_slot<7>(SMW, sf); break;
+    }
+    uint32_t* cw = slotw + (G.code_off + 12 * u) / 4;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+      if (W[w]) atomicOr(&cw[w], W[w]);
+    if constexpr (FMT == 0) {
+      slotw[(G.sm_off + n0) / 4] = sf;  // one byte per element: this quad owns the word
+    } else if constexpr (FMT == 1) {
+      uint32_t* sw = slotw + (G.sm_off + 12 * u) / 4;
+#pragma unroll
+      for (int w = 0; w < 3; ++w)
+        if (SMW[w]) atomicOr(&sw[w], SMW[w]);
+    } else {  // 4-bit fields, element n at bits 4n..4n+3
+      const uint32_t t2 = sf | (sf >> 4);
+      const uint32_t nib16 = (t2 & 0xFFu) | ((t2 >> 8) & 0xFF00u);
+      atomicOr(&slotw[G.sm_off / 4 + (n0 >> 3)], nib16 << (16 * (k & 1)));
+    }
+    if (m >= 1) {  // escape planes: bit 3 of the offsets, then the raw group's high bits
+      const int P0 = gP[q];
+      or_bits(slotw, esc_bit0 + P0 * GT + tau0, e3, 4);
+      if (m == 2) {
+        if constexpr (EF::F == 8) or_bits(slotw, esc_bit0 + (P0 + 1) * GT + 4 * tau0, hi, 16);
+        else if constexpr (EF::F == 5) or_bits(slotw, esc_bit0 + (P0 + 1) * GT + tau0, hi, 4);
+      }
+    }
+    if (tau0 == 0) {  // the group's tag bits
+      if (m >= 1) atomicOr(&slotw[G.tag_off / 4 + (q >> 5)], 1u << (q & 31));
+      if (m == 2) atomicOr(&slotw[G.tag_off / 4 + G.PW + (q >> 5)], 1u << (q & 31));
+    }
+  }
+  __syncthreads();
+  uint4* dst = reinterpret_cast<uint4*>(B.comp_pool + (size_t)slot * G.stride);
+  const uint4* src = reinterpret_cast<const uint4*>(slotw);
+  for (int i = tid; i < G.stride / 16; i += kThreads) dst[i] = src[i];
+  if (tid == 0) B.table[entry_idx] = (uint32_t)slot | ((uint32_t)((esc_bytes + 15) >> 4) << 24);
+}
+
 // Writes the appended tokens that do not complete a block into the sequence's tail.
 __global__ void tail_kernel(Geo G, DevBufs B, SeqList S, const void* __restrict__ kin, const void* __restrict__ vin,
                             int n_tok) {
@@ -456,11 +617,12 @@ __global__ void release_kernel(Geo G, DevBufs B, int seq, int n_blocks) {
   }
 }
 
-// FP8 tiles, one element at a time: every group's mode and first escape unit go to LDS (a block
-// scan of the unit counts), then each thread rebuilds elements from their 3-bit code, escape
-// bits and sign/mantissa field.  (BF16 tiles take the four-token SWAR path below.)
-__device__ void decode_fp8_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
-                                const uint8_t* b4, uint8_t* out, int bi, int h) {
+// Any format and group size, one element at a time: every group's mode and first escape unit go
+// to LDS (a block scan of the unit counts), then each thread rebuilds elements from their 3-bit
+// code, escape bits and sign/mantissa field.  (BF16 tiles with 16-token groups take the SWAR
+// path below.)
+__device__ void decode_tile_any(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
+                                const uint8_t* b4, void* out, int bi, int h) {
   __shared__ uint16_t gP[1024];
   __shared__ uint8_t gm[1024];
   __shared__ int red[8];
@@ -490,8 +652,8 @@ __device__ void decode_fp8_tile(const Geo& G, const DevBufs& B, const uint8_t* t
   auto bit = [](const uint8_t* buf, int b) -> uint32_t { return (buf[b >> 3] >> (b & 7)) & 1u; };
   auto ebit = [&](int b) -> uint32_t { return b < max_bit ? bit(esc, b) : 0u; };
   for (int i = tid; i < G.raw_elems; i += kThreads) {
-    const int t = i / D, c = i % D, tg = t / kGroup, tau = t % kGroup;
-    const int q = tg * D + c, n = q * kGroup + tau;
+    const int t = i / D, c = i % D, tg = t / G.GT, tau = t % G.GT;
+    const int q = tg * D + c, n = q * G.GT + tau;
     const int mode = gm[q];
     const int Pq = gP[q];
     // 3-bit fields in the 32-element unit layout: element r of unit u in byte lane r%4, slot r/4
@@ -503,13 +665,16 @@ __device__ void decode_fp8_tile(const Geo& G, const DevBufs& B, const uint8_t* t
       if (G.MB == 2) f |= ((sm[byte] >> (x & 7)) & 1u) << bb;
     }
     if (G.MB == 3) f = (sm[n >> 1] >> (4 * (n & 1))) & 0xFu;
-    if (mode >= 1) o |= ebit(Pq * kGroup + tau) << 3;
-    if (mode == 2 && G.F == 5) o |= ebit((Pq + 1) * kGroup + tau) << 4;
+    if (G.MB == 7) f = sm[n];
+    if (mode >= 1) o |= ebit(Pq * G.GT + tau) << 3;
+    if (mode == 2 && G.F == 5) o |= ebit((Pq + 1) * G.GT + tau) << 4;
+    if (mode == 2 && G.F == 8)
+      for (int bb = 0; bb < 4; ++bb) o |= ebit((Pq + 1) * G.GT + 4 * tau + bb) << (4 + bb);
     const uint32_t base = mode == 0 ? b3[c] : (mode == 1 ? b4[c] : 0u);
     if (base + o >= (1u << G.F)) atomicOr(&B.counters->status, 8u);  // corrupt offset
     const uint32_t e = (base + o) & ((1u << G.F) - 1u);
-    const uint32_t x = ((f >> G.MB) << 7) | (e << G.MB) | (f & ((1u << G.MB) - 1u));
-    out[(((size_t)bi * T + t) * G.Hkv + h) * D + c] = (uint8_t)x;
+    const uint32_t x = ((f >> G.MB) << (G.F + G.MB)) | (e << G.MB) | (f & ((1u << G.MB) - 1u));
+    elem_put(out, (((size_t)bi * T + t) * G.Hkv + h) * D + c, G.EB, x);
   }
 }
 
@@ -536,9 +701,9 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
     return;
   }
   const uint8_t* tile = B.comp_pool + (size_t)slot * G.stride;
-  if (G.EB == 1) {
-    decode_fp8_tile(G, B, tile, B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
-                    B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, reinterpret_cast<uint8_t*>(outv), bi, h);
+  if (G.EB == 1 || G.GT != kGroup) {
+    decode_tile_any(G, B, tile, B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
+                    B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, outv, bi, h);
     return;
   }
   uint16_t* out = reinterpret_cast<uint16_t*>(outv);
@@ -604,9 +769,12 @@ int launch_calibrate(const Geo& G, const DevBufs& B, const void* k, const void* 
 int launch_append(const Geo& G, const DevBufs& B, const SeqList& S, const void* k, const void* v, int n_tokens,
                   int max_new_blocks, void* stream) {
   if (max_new_blocks > 0) {
-    const size_t lds = (size_t)G.raw_elems * 2 + (size_t)2 * G.PW * 4;
+    const bool any = G.GT != kGroup;  // 8-token groups: the bit-assembling encoder
+    const size_t lds = any ? (size_t)G.raw_elems * 2 + (size_t)G.stride + (size_t)(3 * G.NG + 3) / 4 * 4
+                           : (size_t)G.raw_elems * 2 + (size_t)2 * G.PW * 4;
     void (*kern)(Geo, DevBufs, SeqList, const void*, const void*, int) =
-        G.fmt == 0 ? encode_kernel<0> : (G.fmt == 1 ? encode_kernel<1> : encode_kernel<2>);
+        any ? (G.fmt == 0 ? encode_any_kernel<0> : (G.fmt == 1 ? encode_any_kernel<1> : encode_any_kernel<2>))
+            : (G.fmt == 0 ? encode_kernel<0> : (G.fmt == 1 ? encode_kernel<1> : encode_kernel<2>));
     hipLaunchKernelGGL(kern, dim3(max_new_blocks, S.n, 2 * G.Hkv), dim3(kThreads), lds, (hipStream_t)stream, G, B,
                        S, k, v, n_tokens);
     const int err = (int)hipGetLastError();

@@ -4,18 +4,19 @@
 // Compressed tile layout (FORMAT v1, this library's byte layout for the codec of the page
 // "GAAC: Lossless KV Compression for Bandwidth-Efficient LLM Inference on Personal Devices",
 // §3.1 codec, App. D stored pieces).  One tile = T tokens x D channels of one (K|V, kv-head):
-//   group q = tg*D + c = tokens tg*16 .. tg*16+15 of channel c; element n = 16q + tau;
+//   group q = tg*D + c = tokens tg*GT .. tg*GT+GT-1 of channel c (GT = 16 or 8 tokens);
+//          element n = GT*q + tau;
 //   TAG  : plane E (mode >= 1) then plane R (mode == 2), PW = NG/32 little-endian words each;
-//   CODE : 3-bit offset codes; 12-byte units of 32 elements (one pair of groups); element
+//   CODE : 3-bit offset codes; 12-byte units of 32 elements (32/GT groups); element
 //          r of a unit lives in byte lane r%4, slot r/4 of a 24-bit lane stream spread over
 //          the unit's three words (byte lane k of word w = stream bits 8w..8w+7);
 //   SM   : sign/mantissa field (s << MB) | m per element, element order: BF16 one byte each;
 //          E5M2 3-bit fields in the CODE unit layout (12 bytes per 32 elements); E4M3 4-bit
 //          fields, element n at bits 4n..4n+3 (16 bytes per 32 elements);
-//   ESC  : for every group with mode >= 1, in q order: a 16-bit plane with bit 3 of the 16
-//          offsets (bit tau = token tau); a raw BF16 group then adds the offset bits 4..7 as
-//          one 4-bit field per token (4 units), a raw E5M2 group one more plane (bit 4); zero
-//          up to esc_cap;
+//   ESC  : an LSB-first bit stream; for every group with mode >= 1, in q order: a GT-bit
+//          plane with bit 3 of the GT offsets (bit tau = token tau); a raw BF16 group then
+//          adds the offset bits 4..7 as one 4-bit field per token (4 more GT-bit units), a raw
+//          E5M2 group one more plane (bit 4); zero up to esc_cap;
 //   RAW  : tiles that overflow esc_cap (and every tile of an uncompressed cache) are stored
 //          as native elements, K token-major [t][c], V channel-major [c][t].
 #pragma once
@@ -24,7 +25,7 @@
 
 namespace kvc {
 
-constexpr int kGroup = 16;          // tokens per exponent group handled by these kernels
+constexpr int kGroup = 16;          // group size of the SWAR paths (attention, fast encode/decode)
 constexpr int kMaxSeqsPerLaunch = 64;
 constexpr uint32_t kUnallocated = 0xFFFFFFFFu;
 
@@ -33,6 +34,7 @@ struct Geo {
   int F, MB, EB;                    // exponent bits, mantissa bits, bytes per element
   int sm_pair;                      // SM bytes per pair of groups (32 elements)
   int T, D, Hkv, Hq, g;             // block tokens, head dim, KV heads, query heads, Hq/Hkv
+  int GT;                           // tokens per exponent group (16, or 8)
   int NT, NG, NP, PW;               // token groups per tile, groups, group pairs, tag words
   int tag_off, code_off, sm_off, esc_off, stride;  // compressed tile offsets (bytes)
   int esc_cap;                      // escape capacity (bytes)

@@ -50,13 +50,14 @@ def _sizes(K, p):
     return rc, list(sz), st.value, lib.kv_last_error().decode()
 
 
+@pytest.mark.parametrize("Gt", [16, 8])
 @pytest.mark.parametrize("fmt", [oracle.BF16, oracle.E5M2, oracle.E4M3])
 @pytest.mark.parametrize("T,D", [(64, 128), (16, 128), (64, 64), (32, 128)])
-def test_slot_stride_matches_format(K, T, D, fmt):
+def test_slot_stride_matches_format(K, T, D, fmt, Gt):
     """The library's slot stride equals the stride of FORMAT v1 as the oracle lays it out."""
-    rc, sz, stride, _ = _sizes(K, _params(K, block_tokens=T, head_dim=D, dtype=fmt))
+    rc, sz, stride, _ = _sizes(K, _params(K, block_tokens=T, head_dim=D, dtype=fmt, group_tokens=Gt))
     assert rc == 0
-    lay = oracle.layout(oracle.Params(fmt, T, D, 16))
+    lay = oracle.layout(oracle.Params(fmt, T, D, Gt))
     eb = 2 if fmt == oracle.BF16 else 1
     assert stride == lay["stride"]
     assert sz[0] == 2048 * stride
@@ -71,7 +72,7 @@ def test_slot_stride_matches_format(K, T, D, fmt):
     (dict(head_dim=96), -1), (dict(num_q_heads=12), -1), (dict(num_q_heads=8 * 17), -1),
     (dict(block_tokens=40), -1), (dict(esc_cap_bytes=24), -1), (dict(max_seqs=0), -1),
     (dict(num_comp_slots=0), -1), (dict(compressed=0, num_raw_slots=0), -1), (dict(dtype=7), -1),
-    (dict(group_tokens=8), -3), (dict(block_tokens=128), -3),
+    (dict(group_tokens=4), -3), (dict(group_tokens=32), -3), (dict(block_tokens=128), -3),
     (dict(block_tokens=48), -3),
 ])
 def test_parameter_validation(K, kw, code):
