@@ -57,9 +57,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep", type=str, default="", help="comma-separated split counts to time (extra)")
     ap.add_argument("--probe", action="store_true", help="also time plain HBM copy / read kernels (torch)")
-    ap.add_argument("--extra", type=str, default="fp8,paged",
+    ap.add_argument("--extra", type=str, default="fp8,paged,groups",
                     help="comma list of extra workloads measured after the headline one: fp8 (the 64K layer in "
-                         "FP8 E5M2 and E4M3), paged (32-sequence paged serving mix); '' for none")
+                         "FP8 E5M2 and E4M3), paged (32-sequence paged serving mix), groups (the 64K layer's "
+                         "codec with 16- and 8-token exponent groups); '' for none")
     ap.add_argument("--extra-steps", type=int, default=48)
     ap.add_argument("--paged-splits", type=int, default=16)
     return ap.parse_args()
@@ -321,9 +322,73 @@ def main():
                              for name, fmt in (("e5m2", synth.E5M2), ("e4m3", synth.E4M3))}
     if "paged" in extras:
         result["paged_mix"] = extra_steps(torch, K, synth, synth.config(3), args, splits=args.paged_splits, layers=2)
+    if "groups" in extras:
+        result["codec_groups_64k"] = codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, k0, v0)
     print(json.dumps(result), flush=True)
+
+
+def codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, reps=5):
+    """The 64K layer's codec with 16- and 8-token exponent groups (GAAC page §3.1 groups eight
+    values): codec ratio, mode shares and escape bytes per tile; one bulk append encoding all
+    blocks; decoding every block back to BF16 (kv_decode_blocks) and a single block.  Encoders:
+    16-token groups the register-packing kernel, 8-token groups the bit-assembling one; decoders:
+    16-token groups the four-token SWAR kernel, 8-token groups the element-wise one."""
+    T, D, Hkv, Hq = cfg.T, cfg.D, cfg.Hkv, cfg.Hq
+    L0 = kd.shape[1]
+    nb = L0 // T
+    TD = T * D
+
+    def ev_us(fn):
+        a_ = torch.cuda.Event(enable_timing=True)
+        b_ = torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        fn()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return a_.elapsed_time(b_) * 1e3
+
+    res = {"workload": "qwen3-8b-like-64k", "tokens": L0, "block_tokens": T}
+    for Gt in (16, 8):
+        enc, dec_all, dec_one = [], [], []
+        for _ in range(reps):
+            c = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=1,
+                          max_blocks_per_seq=nb + 1, num_comp_slots=(nb + 1) * 2 * Hkv, num_raw_slots=256,
+                          compressed=True, group_tokens=Gt, perm_seed=7)
+            c.calibrate(dev(k0[:cfg.n_cal]), dev(v0[:cfg.n_cal]))
+            torch.cuda.synchronize()
+            enc.append(ev_us(lambda: c.append([0], kd, vd)))
+            kout = torch.empty((nb * T, Hkv, D), dtype=torch.int16, device="cuda")
+            vout = torch.empty_like(kout)
+            dec_all.append(ev_us(lambda: c.decode_blocks(0, 0, nb, (kout, vout))))
+            k1 = torch.empty((T, Hkv, D), dtype=torch.int16, device="cuda")
+            v1 = torch.empty_like(k1)
+            dec_one.append(ev_us(lambda: c.decode_blocks(0, nb // 2, 1, (k1, v1))))
+        if not (torch.equal(kout, kd[0, :nb * T]) and torch.equal(vout, vd[0, :nb * T])):
+            raise RuntimeError(f"decode_blocks with {Gt}-token groups did not rebuild the layer bit for bit")
+        flags, st = c.status()
+        if flags:
+            raise RuntimeError(f"cache status flags {flags}")
+        payload = (2 * TD // Gt + 3 * TD + 8 * TD) // 8  # TAG + CODE + SM of a compressed tile
+        stored = st["comp_tiles"] * payload + st["esc_bytes"] + st["raw_tiles"] * TD * 2
+        tiles = st["comp_tiles"] + st["raw_tiles"]
+        groups = st["groups"]
+        res[f"g{Gt}"] = {
+            "codec_ratio": round(tiles * TD * 2 / stored, 4),
+            "resident_ratio": round(tiles * TD * 2 / (st["comp_tiles"] * c.slot_stride + st["raw_tiles"] * TD * 2 + 4 * tiles), 4),
+            "mode_share": [round(x / max(sum(groups), 1), 5) for x in groups],
+            "raw_tiles": st["raw_tiles"],
+            "esc_bytes_per_tile": round(st["esc_bytes"] / max(st["comp_tiles"], 1), 1),
+            "slot_stride": c.slot_stride,
+            "bulk_encode_us": round(float(np.median(enc)), 1),
+            "decode_all_blocks_us": round(float(np.median(dec_all)), 1),
+            "decode_one_block_us": round(float(np.median(dec_one)), 1),
+            "decode_GBps_out": round(tiles * TD * 2 / (float(np.median(dec_all)) * 1e-6) / 1e9, 1),
+        }
+        del c
+    log(f"[bench] codec groups: {res}")
+    return res
 
 
 def extra_steps(torch, K, synth, cfg, args, splits, layers=4):

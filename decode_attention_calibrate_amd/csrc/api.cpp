@@ -267,6 +267,8 @@ int kv_decode_blocks(kvc_cache* c, int32_t seq, int32_t first_block, int32_t n_b
   if (seq < 0 || seq >= c->p.max_seqs) return fail(KVC_EINVAL, "sequence id out of range");
   if (!k_out_dev || !v_out_dev || first_block < 0 || n_blocks < 1) return fail(KVC_EINVAL, "bad block range");
   if (first_block + n_blocks > c->len[seq] / c->G.T) return fail(KVC_EINVAL, "blocks past the finished blocks");
+  if (((uintptr_t)k_out_dev & 15u) || ((uintptr_t)v_out_dev & 15u))
+    return fail(KVC_EINVAL, "k_out and v_out must be 16-byte aligned");
   return hip_fail(kvc::launch_decode_blocks(c->G, c->B, seq, first_block, n_blocks, k_out_dev, v_out_dev, stream),
                   "launch decode_blocks");
 }

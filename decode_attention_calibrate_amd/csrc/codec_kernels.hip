@@ -678,6 +678,82 @@ __device__ void decode_tile_any(const Geo& G, const DevBufs& B, const uint8_t* t
   }
 }
 
+// Codes of slot s (0..7, a run-time value) of a CODE unit, one 3-bit code per byte lane.
+__device__ __forceinline__ uint32_t code_slot_rt(uint32_t W0, uint32_t W1, uint32_t W2, int s) {
+  switch (s) {
+    case 0: return code_slot<0>(W0, W1, W2);
+    case 1: return code_slot<1>(W0, W1, W2);
+    case 2: return code_slot<2>(W0, W1, W2);
+    case 3: return code_slot<3>(W0, W1, W2);
+    case 4: return code_slot<4>(W0, W1, W2);
+    case 5: return code_slot<5>(W0, W1, W2);
+    case 6: return code_slot<6>(W0, W1, W2);
+    default: return code_slot<7>(W0, W1, W2);
+  }
+}
+
+// BF16 tiles with 8-token groups, four tokens per 32-bit word as the 16-token path: one thread
+// per CODE unit (32 elements = channels c0..c0+3 x tokens 8tg..8tg+7, one group per channel).
+// Escape units are single bytes (an 8-bit plane per escaped group; a raw group adds four bytes
+// of offset bits 4..7, token tau's nibble at bits 4*tau).
+__device__ void decode_bf16_g8_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
+                                    const uint8_t* b4, uint16_t* out, int bi, int h) {
+  const int D = G.D, T = G.T;
+  const uint32_t* tagE = reinterpret_cast<const uint32_t*>(tile + G.tag_off);
+  const uint32_t* tagR = tagE + G.PW;
+  const uint8_t* esc = tile + G.esc_off;
+  const int n_units = G.raw_elems / 32;
+  for (int u = threadIdx.x; u < n_units; u += blockDim.x) {
+    const int q0 = 4 * u, w = q0 >> 5, bit = q0 & 31, tg = q0 / D, c0 = q0 % D;
+    uint32_t P = 0;  // escape bytes before group q0
+    for (int i = 0; i < w; ++i) P += __popc(tagE[i]) + 4u * __popc(tagR[i]);
+    const uint32_t Ew = tagE[w], Rw = tagR[w];
+    const uint32_t below = bit == 0 ? 0u : (0xFFFFFFFFu >> (32 - bit));
+    P += __popc(Ew & below) + 4u * __popc(Rw & below);
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(tile + G.code_off + 12 * u);
+    const uint32_t W0 = cw[0], W1 = cw[1], W2 = cw[2];
+    const uint4 s4[2] = {*reinterpret_cast<const uint4*>(tile + G.sm_off + 32 * u),
+                         *reinterpret_cast<const uint4*>(tile + G.sm_off + 32 * u + 16)};
+    const uint32_t smw[8] = {s4[0].x, s4[0].y, s4[0].z, s4[0].w, s4[1].x, s4[1].y, s4[1].z, s4[1].w};
+    uint32_t o02[4][2], o13[4][2];  // [channel][token quad]
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const uint32_t E = (Ew >> (bit + gi)) & 1u, R = (Rw >> (bit + gi)) & 1u;
+      if (R && !E) atomicOr(&B.counters->status, 8u);
+      const int c = c0 + gi;
+      const uint32_t base = R ? 0u : (E ? b4[c] : b3[c]);
+      const uint32_t H = perm_b32(base, base, 0u);
+      uint32_t plane = 0, hi = 0;
+      if (E && (int)P < G.esc_cap) plane = esc[P];
+      if (R) {  // four bytes at P + 1 (not word aligned in general): byte by byte
+        for (int k = 0; k < 4; ++k) hi |= ((int)P + 1 + k < G.esc_cap ? (uint32_t)esc[P + 1 + k] : 0u) << (8 * k);
+      }
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const uint32_t cs = code_slot_rt(W0, W1, W2, 2 * gi + qq);
+        const uint32_t e3 = spread4((plane >> (4 * qq)) & 0xFu) << 3;
+        const uint32_t X = R ? raw_high_nibbles((hi >> (16 * qq)) & 0xFFFFu) : 0u;
+        const uint32_t Ev = H + cs + e3 + X;
+        const uint32_t sv = smw[2 * gi + qq];
+        o02[gi][qq] = bitsel(0x7F807F80u, Ev << 7, perm_b32(sv, sv, 0x02020000u));
+        o13[gi][qq] = bitsel(0x7F807F80u, Ev >> 1, perm_b32(sv, sv, 0x03030101u));
+      }
+      P += E + 4u * R;
+    }
+    // token t = 8tg + 4qq + k: channels c0..c0+3 as one 8-byte store
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t sel = (k >> 1) ? 0x07060302u : 0x05040100u;  // tokens 4qq+{0,1}: low halves
+        const uint32_t w01 = (k & 1) ? perm_b32(o13[1][qq], o13[0][qq], sel) : perm_b32(o02[1][qq], o02[0][qq], sel);
+        const uint32_t w23 = (k & 1) ? perm_b32(o13[3][qq], o13[2][qq], sel) : perm_b32(o02[3][qq], o02[2][qq], sel);
+        const int t = 8 * tg + 4 * qq + k;
+        *reinterpret_cast<uint2*>(out + (((size_t)bi * T + t) * G.Hkv + h) * D + c0) = make_uint2(w01, w23);
+      }
+  }
+}
+
 // One block per (block, K|V, head): rebuilds the tile into [n*T][Hkv][D].
 __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs B, int seq, int first,
                                                                   void* __restrict__ kout, void* __restrict__ vout) {
@@ -701,6 +777,11 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
     return;
   }
   const uint8_t* tile = B.comp_pool + (size_t)slot * G.stride;
+  if (G.EB == 2 && G.GT == 8) {
+    decode_bf16_g8_tile(G, B, tile, B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
+                        B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, reinterpret_cast<uint16_t*>(outv), bi, h);
+    return;
+  }
   if (G.EB == 1 || G.GT != kGroup) {
     decode_tile_any(G, B, tile, B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
                     B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, outv, bi, h);

@@ -141,8 +141,9 @@ int kv_encode_append(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_se
                      const void* v_dev, int32_t n_tokens, void* stream);
 
 /* Rebuilds finished blocks first_block .. first_block+n_blocks-1 of one sequence into plain
- * element tensors k_out_dev, v_out_dev: [n_blocks*T][Hkv][D] (GAAC page §3.2 reconstruction,
- * bit for bit).  Unallocated blocks come out as zeros and set KVC_STATUS_MISSING_BLOCK. */
+ * element tensors k_out_dev, v_out_dev: [n_blocks*T][Hkv][D], 16-byte aligned (GAAC page §3.2
+ * reconstruction, bit for bit).  Unallocated blocks come out as zeros and set
+ * KVC_STATUS_MISSING_BLOCK. */
 int kv_decode_blocks(kvc_cache* cache, int32_t seq, int32_t first_block, int32_t n_blocks, void* k_out_dev,
                      void* v_out_dev, void* stream);
 

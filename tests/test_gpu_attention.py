@@ -259,8 +259,9 @@ def test_decode_step_equals_append_then_attention(compressed, T):
 
 
 def test_misaligned_buffers_rejected():
-    """q, out and the new token must be 16-byte aligned: a misaligned buffer is an argument error
-    raised before any launch, and a rejected decode step leaves the sequence as it was."""
+    """q, out, the new token and decoded-block outputs must be 16-byte aligned: a misaligned
+    buffer is an argument error raised before any launch, and a rejected decode step leaves the
+    sequence as it was."""
     from decode_attention_calibrate_amd._lib import KVCError
     cfg = synth.config(0)
     g, toks = synth.sequence_tokens(cfg)
@@ -279,6 +280,11 @@ def test_misaligned_buffers_rejected():
     with pytest.raises(KVCError):
         cache.decode_step([0], dev(k[None, -1:]), dev(v[None, -1:]), q, cfg.scale, 2, out=bad_out)
     assert cache.seq_length(0) == L0
+    nk = cfg.T * cfg.Hkv * cfg.D
+    bad_k = torch.empty(nk + 8, dtype=torch.int16, device=q.device)[1:1 + nk].view(cfg.T, cfg.Hkv, cfg.D)
+    good_v = torch.empty((cfg.T, cfg.Hkv, cfg.D), dtype=torch.int16, device=q.device)
+    with pytest.raises(KVCError):
+        cache.decode_blocks(0, 0, 1, (bad_k, good_v))
     out = host(cache.decode_step([0], dev(k[None, -1:]), dev(v[None, -1:]), q, cfg.scale, 2))
     assert cache.seq_length(0) == L0 + 1
     assert row_rel_err(out, _oracle(cfg, [(k, v)], host(q))) <= TOL
