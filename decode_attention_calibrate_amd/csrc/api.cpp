@@ -308,27 +308,42 @@ static int check_out(const void* out_dev) {
   return KVC_OK;
 }
 
-int kv_attention_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev, float scale,
-                          int32_t n_splits, void* ws_dev, size_t ws_bytes, void* stream) {
-  int rc = check_attention_args(c, seq_ids_host, n_seqs, q_dev, n_splits, ws_dev, ws_bytes);
-  if (rc != KVC_OK) return rc;
+// The split kernel over the finished blocks of every listed sequence (argument checks done by the
+// caller).  k_new / v_new (a decode step, else null): the new token of each sequence, already
+// counted in c->len, which the kernel stores into the tail.
+static int run_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev, float scale,
+                        int32_t n_splits, void* ws_dev, const void* k_new_dev, const void* v_new_dev, void* stream) {
+  int rc = KVC_OK;
   const Geo& G = c->G;
+  const size_t row = (size_t)G.Hkv * G.D * G.EB;  // bytes of one token of all KV heads
   float* acc = (float*)ws_dev;
   float* ml = acc + (size_t)n_seqs * G.Hq * n_splits * G.D;
   for (int s0 = 0; s0 < n_seqs; s0 += kvc::kMaxSeqsPerLaunch) {
     SeqList S;
+    int new_pos[kvc::kMaxSeqsPerLaunch];
     S.n = std::min(kvc::kMaxSeqsPerLaunch, n_seqs - s0);
     for (int i = 0; i < S.n; ++i) {
       S.ids[i] = seq_ids_host[s0 + i];
       S.lens[i] = c->len[S.ids[i]] / G.T * G.T;  // the finished blocks; the merge adds the tail
+      new_pos[i] = c->len[S.ids[i]] % G.T - 1;   // a decode step's token: the tail's last position
     }
     rc = hip_fail(kvc::launch_attention_partials(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale,
                                                  n_splits, acc + (size_t)s0 * G.Hq * n_splits * G.D,
-                                                 ml + (size_t)s0 * G.Hq * n_splits * 2, stream),
+                                                 ml + (size_t)s0 * G.Hq * n_splits * 2,
+                                                 k_new_dev ? (const uint8_t*)k_new_dev + (size_t)s0 * row : nullptr,
+                                                 v_new_dev ? (const uint8_t*)v_new_dev + (size_t)s0 * row : nullptr,
+                                                 new_pos, stream),
                   "launch attention");
     if (rc != KVC_OK) return rc;
   }
   return KVC_OK;
+}
+
+int kv_attention_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev, float scale,
+                          int32_t n_splits, void* ws_dev, size_t ws_bytes, void* stream) {
+  int rc = check_attention_args(c, seq_ids_host, n_seqs, q_dev, n_splits, ws_dev, ws_bytes);
+  if (rc != KVC_OK) return rc;
+  return run_partials(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, nullptr, nullptr, stream);
 }
 
 int kv_attention_combine(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev, float scale,
@@ -349,7 +364,7 @@ int kv_attention_combine(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_se
     }
     rc = hip_fail(kvc::launch_combine(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale, n_splits,
                                       acc + (size_t)s0 * G.Hq * n_splits * G.D, ml + (size_t)s0 * G.Hq * n_splits * 2,
-                                      (uint16_t*)out_dev + (size_t)s0 * G.Hq * G.D, nullptr, nullptr, stream),
+                                      (uint16_t*)out_dev + (size_t)s0 * G.Hq * G.D, stream),
                   "launch combine");
     if (rc != KVC_OK) return rc;
   }
@@ -392,30 +407,11 @@ int kv_decode_step(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, co
     if (rc != KVC_OK) return rc;
     return kv_decode_attention(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, out_dev, stream);
   }
-  // the finished blocks do not change: split attention over them as they are
+  // the finished blocks do not change: the split kernel attends them as they are and stores the
+  // new token into the tail; the merge then attends the tail with the new token in it
   for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] += 1;
-  rc = kv_attention_partials(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, stream);
-  if (rc != KVC_OK) {
-    for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] -= 1;
-    return rc;
-  }
-  float* acc = (float*)ws_dev;
-  float* ml = acc + (size_t)n_seqs * G.Hq * n_splits * G.D;
-  const size_t row = (size_t)G.Hkv * G.D * G.EB;  // bytes of one token of all KV heads
-  for (int s0 = 0; s0 < n_seqs && rc == KVC_OK; s0 += kvc::kMaxSeqsPerLaunch) {
-    SeqList S;
-    S.n = std::min(kvc::kMaxSeqsPerLaunch, n_seqs - s0);
-    for (int i = 0; i < S.n; ++i) {
-      S.ids[i] = seq_ids_host[s0 + i];
-      S.lens[i] = c->len[S.ids[i]];
-    }
-    rc = hip_fail(kvc::launch_combine(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale, n_splits,
-                                      acc + (size_t)s0 * G.Hq * n_splits * G.D, ml + (size_t)s0 * G.Hq * n_splits * 2,
-                                      (uint16_t*)out_dev + (size_t)s0 * G.Hq * G.D,
-                                      (const uint8_t*)k_new_dev + (size_t)s0 * row,
-                                      (const uint8_t*)v_new_dev + (size_t)s0 * row, stream),
-                  "launch combine");
-  }
+  rc = run_partials(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, k_new_dev, v_new_dev, stream);
+  if (rc == KVC_OK) rc = kv_attention_combine(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, out_dev, stream);
   if (rc != KVC_OK)
     for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] -= 1;
   return rc;

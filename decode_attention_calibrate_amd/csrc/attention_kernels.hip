@@ -56,7 +56,11 @@ struct AttnArgs {
   float* ws_ml;
   float sl2;  // scale * log2(e)
   int n_splits;
+  const uint8_t* k_new;  // decode step: the new tokens, [n][Hkv][D] elements (else null)
+  const uint8_t* v_new;
+  int new_pos[kMaxSeqsPerLaunch];  // their tail positions
 };
+
 
 // Element format: 0 BF16, 1 FP8 E5M2, 2 FP8 E4M3 (kvc_dtype).
 template <int FMT>
@@ -72,6 +76,28 @@ struct FmtT {
 
 // Compile-time geometry of a compressed tile (FORMAT v1) for head_dim 32*NR, T = TT tokens and
 // element format FMT.
+// Decode step: the first split of each (sequence, KV head) stores the sequence's new token into
+// the tail (K row new_pos, V column new_pos); the merge kernel that follows reads it there.
+template <int FMT>
+__device__ __forceinline__ void store_new_token(const AttnArgs& a, int si, int h) {
+  constexpr int EB = FmtT<FMT>::EB;
+  const Geo& G = a.G;
+  const int seq = a.S.ids[si], t = a.new_pos[si];
+  uint8_t* tk = reinterpret_cast<uint8_t*>(a.B.tail) + tail_offset(G, seq, 0, h) * EB;
+  uint8_t* tv = reinterpret_cast<uint8_t*>(a.B.tail) + tail_offset(G, seq, 1, h) * EB;
+  const uint8_t* kn = a.k_new + ((size_t)si * G.Hkv + h) * G.D * EB;
+  const uint8_t* vn = a.v_new + ((size_t)si * G.Hkv + h) * G.D * EB;
+  for (int c = threadIdx.x; c < G.D; c += blockDim.x) {
+    if constexpr (EB == 2) {
+      reinterpret_cast<uint16_t*>(tk)[(size_t)t * G.D + c] = reinterpret_cast<const uint16_t*>(kn)[c];
+      reinterpret_cast<uint16_t*>(tv)[(size_t)c * G.T + t] = reinterpret_cast<const uint16_t*>(vn)[c];
+    } else {
+      tk[(size_t)t * G.D + c] = kn[c];
+      tv[(size_t)c * G.T + t] = vn[c];
+    }
+  }
+}
+
 template <int NR, int TT, int FMT>
 struct TG {
   static constexpr int D = 32 * NR;
@@ -491,6 +517,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   const int split = blockIdx.x, h = blockIdx.y, si = blockIdx.z;
   const int seq = a.S.ids[si], L = a.S.lens[si];
   const SbOrder ord(L, a.n_splits, split);
+  if (a.k_new != nullptr && split == 0) store_new_token<FMT>(a, si, h);
   uint8_t* esc_lds = esc_base + j * esc_room;
   const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(esc_lds);
   const uint32_t below = (1u << (2 * n)) - 1u;
@@ -756,6 +783,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   const int split = blockIdx.x, h = blockIdx.y, si = blockIdx.z;
   const int seq = a.S.ids[si], L = a.S.lens[si];
   const SbOrder ord(L, a.n_splits, split);
+  if (a.k_new != nullptr && split == 0) store_new_token<FMT>(a, si, h);
   uint32_t flags = 0;
 
   uint4 qb[NR];
@@ -850,9 +878,7 @@ constexpr int kTailTok = 64;        // tail tokens a block can hold (T <= 64)
 struct CombineArgs {
   Geo G;
   SeqList S;
-  uint8_t* tail;
-  const uint8_t* k_new;  // decode step: this step's token, [n][Hkv][D] elements (else null)
-  const uint8_t* v_new;
+  const uint8_t* tail;
   const uint16_t* q;
   const float* ws_acc;
   const float* ws_ml;
@@ -938,15 +964,11 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
 #pragma unroll
   for (int u = 0; u < UPT; ++u)
     av[u] = *reinterpret_cast<const float4*>(acc + (size_t)min(slice + NSL * u, S - 1) * D + 4 * quad);
-  uint8_t* tk_base = a.tail + tail_offset(G, seq, 0, h) * EB;  // K tail [t][c]
-  uint8_t* tv_base = a.tail + tail_offset(G, seq, 1, h) * EB;  // V tail [c][t]
+  const uint8_t* tk_base = a.tail + tail_offset(G, seq, 0, h) * EB;  // K tail [t][c]
+  const uint8_t* tv_base = a.tail + tail_offset(G, seq, 1, h) * EB;  // V tail [c][t]
   const uint16_t* qrow = a.q + ((size_t)si * G.Hq + hq) * D + KPL * kq4;
   const int tkc = min(tk, T - 1);
-  const bool step = a.k_new != nullptr;
-  const int tnew = step ? ntail - 1 : -1;  // tail position of this step's token
-  const uint8_t* kn = step ? a.k_new + ((size_t)si * G.Hkv + h) * D * EB : nullptr;
-  const uint8_t* vn = step ? a.v_new + ((size_t)si * G.Hkv + h) * D * EB : nullptr;
-  const uint8_t* krow = tk == tnew ? kn : tk_base + (size_t)tkc * D * EB;
+  const uint8_t* krow = tk_base + (size_t)tkc * D * EB;
   uint4 kk[KPL / 8], qq[KPL / 8];
 #pragma unroll
   for (int p = 0; p < KPL / 8; ++p) {
@@ -957,12 +979,6 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
 #pragma unroll
   for (int u = 0; u < QPT; ++u)
     vv[u] = tail_quad<FMT>(tv_base + ((size_t)(cb * CH + cv) * T + min(4 * (tq0 + u), T - 4)) * EB);
-  // this step's V value of channel cb*CH + cv, as a BF16 word (low half)
-  uint32_t vnew = 0;
-  if (step) {
-    if constexpr (FMT == 0) vnew = reinterpret_cast<const uint16_t*>(vn)[cb * CH + cv];
-    else vnew = fp8x2_to_bf16x2<FMT, false>(vn[cb * CH + cv]) & 0xFFFFu;
-  }
 
   // ---- maximum ----
   float dot = 0.0f;
@@ -1019,8 +1035,7 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
     const float v4[4] = {bf16_lo(vv[u].x), bf16_hi(vv[u].x), bf16_lo(vv[u].y), bf16_hi(vv[u].y)};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float v = (t0 + k == tnew) ? bf16_lo(vnew) : v4[k];
-      tv += (t0 + k < ntail) ? pt[min(t0 + k, kTailTok - 1)] * v : 0.0f;
+      tv += (t0 + k < ntail) ? pt[min(t0 + k, kTailTok - 1)] * v4[k] : 0.0f;
     }
   }
   for (int o = 1; o < TPC; o <<= 1) tv += __shfl_xor(tv, o);
@@ -1033,18 +1048,6 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
 #pragma unroll
     for (int i = 0; i < kCombineThreads / 64; ++i) t += part[i * CH + tid];
     a.out[((size_t)si * G.Hq + hq) * D + cb * CH + tid] = f32_to_bf16_rne(t / den);
-  }
-  // decode step: the first block of the KV-head group stores the new token into the tail
-  if (step && cb == 0 && hq % G.g == 0) {
-    for (int c = tid; c < D; c += kCombineThreads) {
-      if constexpr (FMT == 0) {
-        reinterpret_cast<uint16_t*>(tk_base)[(size_t)tnew * D + c] = reinterpret_cast<const uint16_t*>(kn)[c];
-        reinterpret_cast<uint16_t*>(tv_base)[(size_t)c * T + tnew] = reinterpret_cast<const uint16_t*>(vn)[c];
-      } else {
-        tk_base[(size_t)tnew * D + c] = kn[c];
-        tv_base[(size_t)c * T + tnew] = vn[c];
-      }
-    }
   }
 }
 
@@ -1079,8 +1082,12 @@ int launch_attn_f(const AttnArgs& a, int n_seqs, void* stream) {
 }  // namespace
 
 int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& S, const uint16_t* q, float scale,
-                              int n_splits, float* ws_acc, float* ws_ml, void* stream) {
+                              int n_splits, float* ws_acc, float* ws_ml, const void* k_new, const void* v_new,
+                              const int* new_pos, void* stream) {
   AttnArgs a;
+  a.k_new = reinterpret_cast<const uint8_t*>(k_new);
+  a.v_new = reinterpret_cast<const uint8_t*>(v_new);
+  for (int i = 0; i < kMaxSeqsPerLaunch; ++i) a.new_pos[i] = (k_new && i < S.n) ? new_pos[i] : 0;
   a.G = G;
   a.B = B;
   a.S = S;
@@ -1106,14 +1113,11 @@ void (*pick_combine(int n_splits))(CombineArgs) {
 }
 
 int launch_combine(const Geo& G, const DevBufs& B, const SeqList& S, const uint16_t* q, float scale, int n_splits,
-                   const float* ws_acc, const float* ws_ml, uint16_t* out, const void* k_new, const void* v_new,
-                   void* stream) {
+                   const float* ws_acc, const float* ws_ml, uint16_t* out, void* stream) {
   CombineArgs a;
   a.G = G;
   a.S = S;
-  a.tail = reinterpret_cast<uint8_t*>(B.tail);
-  a.k_new = reinterpret_cast<const uint8_t*>(k_new);
-  a.v_new = reinterpret_cast<const uint8_t*>(v_new);
+  a.tail = reinterpret_cast<const uint8_t*>(B.tail);
   a.q = q;
   a.ws_acc = ws_acc;
   a.ws_ml = ws_ml;

@@ -93,13 +93,14 @@ int launch_append(const Geo& G, const DevBufs& B, const SeqList& seqs, const voi
 int launch_release(const Geo& G, const DevBufs& B, int seq, int n_blocks, void* stream);
 int launch_decode_blocks(const Geo& G, const DevBufs& B, int seq, int first, int n, void* k_out, void* v_out,
                          void* stream);
-// seqs.lens: tokens of the finished blocks (partials) or of the whole sequence (combine)
+// seqs.lens: tokens of the finished blocks (partials) or of the whole sequence (combine).
+// k_new / v_new (a decode step, else null): each sequence's new token, [n][Hkv][D] elements,
+// which the split kernel's first split of every (sequence, head) stores at tail position
+// new_pos[i] while the blocks are attended (the split kernel never reads the tail).
 int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale,
-                              int n_splits, float* ws_acc, float* ws_ml, void* stream);
-// k_new / v_new (decode step, else null): each sequence's newest token, [n][Hkv][D] elements,
-// the last token of its tail (seqs.lens counts it); the kernel also stores it into the tail
+                              int n_splits, float* ws_acc, float* ws_ml, const void* k_new, const void* v_new,
+                              const int* new_pos, void* stream);
 int launch_combine(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale, int n_splits,
-                   const float* ws_acc, const float* ws_ml, uint16_t* out, const void* k_new, const void* v_new,
-                   void* stream);
+                   const float* ws_acc, const float* ws_ml, uint16_t* out, void* stream);
 
 }  // namespace kvc
