@@ -57,10 +57,11 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep", type=str, default="", help="comma-separated split counts to time (extra)")
     ap.add_argument("--probe", action="store_true", help="also time plain HBM copy / read kernels (torch)")
-    ap.add_argument("--extra", type=str, default="fp8,paged,groups",
+    ap.add_argument("--extra", type=str, default="fp8,paged,groups,rope",
                     help="comma list of extra workloads measured after the headline one: fp8 (the 64K layer in "
                          "FP8 E5M2 and E4M3), paged (32-sequence paged serving mix), groups (the 64K layer's "
-                         "codec with 16- and 8-token exponent groups); '' for none")
+                         "codec with 16- and 8-token exponent groups), rope (escape bytes and raw tiles along "
+                         "the 64K layer with RoPE-rotated keys, per calibration policy); '' for none")
     ap.add_argument("--extra-steps", type=int, default=48)
     ap.add_argument("--paged-splits", type=int, default=16)
     return ap.parse_args()
@@ -324,6 +325,8 @@ def main():
         result["paged_mix"] = extra_steps(torch, K, synth, synth.config(3), args, splits=args.paged_splits, layers=2)
     if "groups" in extras:
         result["codec_groups_64k"] = codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream)
+    if "rope" in extras:
+        result["rope_drift_64k"] = rope_drift(torch, K, synth, cfg, k0, v0, dev)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, k0, v0)
     print(json.dumps(result), flush=True)
@@ -388,6 +391,53 @@ def codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, reps=5):
         }
         del c
     log(f"[bench] codec groups: {res}")
+    return res
+
+
+def rope_drift(torch, K, synth, cfg, k0, v0, dev, seg=8192):
+    """RoPE positional drift (GAAC page App. C): the 64K layer with keys rotated by rotary
+    position embedding (theta = 1e6), encoded once per calibration policy; per 8K-token segment,
+    the mean escape bytes of the compressed K and V tiles (from their stored tag planes) and the
+    share of tiles stored raw.  Policies: unrotated keys, first 256 tokens; rotated keys
+    calibrated on the first 256, 8K or 32K tokens, or on 256 tokens spread evenly over the
+    context (same calibration budget as the first, spread over the positions)."""
+    T, D, Hkv, Hq = cfg.T, cfg.D, cfg.Hkv, cfg.Hq
+    L0 = k0.shape[0]
+    nb = L0 // T
+    kr = synth.rope_keys(k0)
+    policies = [("unrotated_first256", k0, np.arange(256)), ("first256", kr, np.arange(256)),
+                ("first8k", kr, np.arange(8192)), ("first32k", kr, np.arange(32768)),
+                ("spread256", kr, np.arange(0, L0, L0 // 256))]
+    popc = torch.tensor([bin(i).count("1") for i in range(256)], dtype=torch.int32, device="cuda")
+    res = {"workload": "qwen3-8b-like-64k, RoPE theta 1e6 on K", "segment_tokens": seg, "block_tokens": T}
+    for name, ks, cal in policies:
+        c = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=1,
+                      max_blocks_per_seq=nb + 1, num_comp_slots=(nb + 1) * 2 * Hkv, num_raw_slots=(nb + 1) * 2 * Hkv,
+                      compressed=True, perm_seed=7)
+        c.calibrate(dev(ks[cal]), dev(v0[cal]))
+        c.append([0], dev(ks[None]), dev(v0[None]))
+        torch.cuda.synchronize()
+        e = c.table()[: (nb + 1) * 2 * Hkv].view(nb + 1, 2, Hkv)[:nb]
+        raw = e < 0
+        slot = (e & 0xFFFFFF).long()
+        pw_bytes = 4 * ((T // 16 * D + 31) // 32)  # one tag plane
+        tagpool = c.buffers["comp_pool"].view(-1, c.slot_stride)[:, : 2 * pw_bytes]  # TAG sections only
+        tags = tagpool[torch.where(raw, torch.zeros_like(slot), slot)].long()
+        units = popc[tags[..., :pw_bytes]].sum(-1) + 4 * popc[tags[..., pw_bytes:]].sum(-1)  # wide 1, raw 5
+        esc = torch.where(raw, torch.zeros_like(units), 2 * units).double()  # 16-bit escape units
+        segs = []
+        for s0 in range(0, nb, seg // T):
+            row = {}
+            for kv, nm in ((0, "k"), (1, "v")):
+                r = raw[s0:s0 + seg // T, kv]
+                n_comp = int((~r).sum())
+                row[f"{nm}_esc_bytes_per_tile"] = round(float(esc[s0:s0 + seg // T, kv].sum()) / max(n_comp, 1), 1)
+                row[f"{nm}_raw_tile_share"] = round(float(r.double().mean()), 4)
+            segs.append(row)
+        flags, st = c.status()
+        res[name] = {"segments": segs, "raw_tiles": st["raw_tiles"], "status_flags": flags}
+        del c
+    log(f"[bench] rope drift: {res}")
     return res
 
 

@@ -11,6 +11,9 @@ Recipe (per layer, numpy PCG64, seed = (config index, layer)):
   2. each call to ``tokens(n)`` draws K = N(0,1)[n][Hkv][D] * sK, then V likewise with sV,
      in float32, then rounds to BF16 (round-to-nearest-even), optionally then to FP8.
 Queries: q = N(0,1)[n_seqs][Hq][D] -> BF16, seed = (config index, 7919, step).
+Rotated keys (``rope_keys``): a model caches keys after its rotary position embedding; these
+are the BF16 keys above rotated at their positions (pairs (c, c + D/2), inverse frequencies
+theta^(-2i/D), Qwen3's theta = 1e6) in float32 and rounded back to BF16.
 """
 from __future__ import annotations
 
@@ -115,6 +118,20 @@ class LayerGen:
         if self.cfg.fmt != BF16:
             kb, vb = bf16_bits_to_fp8_bits(kb, self.cfg.fmt), bf16_bits_to_fp8_bits(vb, self.cfg.fmt)
         return kb, vb
+
+
+def rope_keys(k_bits: np.ndarray, theta: float = 1.0e6, first_pos: int = 0) -> np.ndarray:
+    """Keys [n][Hkv][D] (BF16 bits) rotated by rotary position embedding at positions
+    first_pos .. first_pos + n - 1: channel pair (i, i + D/2) turns by angle pos * theta^(-2i/D)."""
+    n, H, D = k_bits.shape
+    half = D // 2
+    x = bf16_bits_to_f32(k_bits).reshape(n, H, D)
+    inv = theta ** (-2.0 * np.arange(half, dtype=np.float64) / D)
+    ang = (first_pos + np.arange(n, dtype=np.float64))[:, None] * inv[None, :]
+    c = np.cos(ang).astype(np.float32)[:, None, :]
+    s = np.sin(ang).astype(np.float32)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return f32_to_bf16_bits(np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1))
 
 
 def sequence_tokens(cfg: Config, layer: int = 0):
