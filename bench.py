@@ -57,11 +57,12 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep", type=str, default="", help="comma-separated split counts to time (extra)")
     ap.add_argument("--probe", action="store_true", help="also time plain HBM copy / read kernels (torch)")
-    ap.add_argument("--extra", type=str, default="fp8,paged,groups,rope",
+    ap.add_argument("--extra", type=str, default="fp8,paged,groups,rope,serving",
                     help="comma list of extra workloads measured after the headline one: fp8 (the 64K layer in "
                          "FP8 E5M2 and E4M3), paged (32-sequence paged serving mix), groups (the 64K layer's "
                          "codec with 16- and 8-token exponent groups), rope (escape bytes and raw tiles along "
-                         "the 64K layer with RoPE-rotated keys, per calibration policy); '' for none")
+                         "the 64K layer with RoPE-rotated keys, per calibration policy), serving (sequences "
+                         "admitted and decode throughput under one KV byte budget); '' for none")
     ap.add_argument("--extra-steps", type=int, default=48)
     ap.add_argument("--paged-splits", type=int, default=16)
     return ap.parse_args()
@@ -327,6 +328,8 @@ def main():
         result["codec_groups_64k"] = codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream)
     if "rope" in extras:
         result["rope_drift_64k"] = rope_drift(torch, K, synth, cfg, k0, v0, dev)
+    if "serving" in extras:
+        result["equal_memory_serving"] = equal_memory_serving(torch, K, synth, splits=args.paged_splits)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, k0, v0)
     print(json.dumps(result), flush=True)
@@ -438,6 +441,96 @@ def rope_drift(torch, K, synth, cfg, k0, v0, dev, seg=8192):
         res[name] = {"segments": segs, "raw_tiles": st["raw_tiles"], "status_flags": flags}
         del c
     log(f"[bench] rope drift: {res}")
+    return res
+
+
+def equal_memory_serving(torch, K, synth, splits, budget_mb=1536, n_requests=96, layers=2, steps=24):
+    """Equal-memory serving (GAAC page §4.5): one KV byte budget per layer for both caches, the
+    compressed one spending 1/64 of it on raw-fallback slots and the rest on compressed slots,
+    the uncompressed one all of it on raw tiles.  Requests with paged-mix lengths (T = 16;
+    U[4096, 32768] tokens, seeded) are admitted first come, first served while their finished
+    blocks plus one spare block fit in the free slots; then the admitted batch decodes
+    (kv_decode_step over every admitted sequence) on `layers` rotated layer caches.  Sequences
+    take their tokens from one shared token stream at staggered offsets.  No model weights
+    exist here: a step is the attention layer alone, so the throughput is attention-only."""
+    import dataclasses
+    cfg = synth.config(3)
+    T, D, Hkv, Hq = cfg.T, cfg.D, cfg.Hkv, cfg.Hq
+    lens = np.random.default_rng([3, 4242]).integers(4096, 32768, size=n_requests, endpoint=True).tolist()
+    budget = budget_mb << 20
+    tile_raw = T * D * 2
+    g = synth.LayerGen(cfg)
+    pk_h, pv_h = g.tokens(max(lens) + 4096)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    pk, pv = dev(pk_h), dev(pv_h)
+    stream = torch.cuda.current_stream()
+    res = {"workload": "paged-mix requests, T = 16, 8/32 heads, D = 128", "budget_bytes_per_layer": budget,
+           "requests": n_requests, "n_splits": splits, "layers_rotated": layers, "steps": steps}
+
+    for name, compressed in (("uncompressed", False), ("compressed", True)):
+        probe = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=1,
+                          max_blocks_per_seq=1, num_comp_slots=1, num_raw_slots=1, compressed=True)
+        stride = probe.slot_stride
+        del probe
+        if compressed:
+            n_raw = (budget // 64) // tile_raw
+            n_comp = (budget - n_raw * tile_raw) // stride
+            free = n_comp
+        else:
+            n_raw, n_comp = budget // tile_raw, 0
+            free = n_raw
+        admitted = []
+        for L in lens:  # first come, first served: stop at the first request that does not fit
+            need = (L // T + 1) * 2 * Hkv
+            if need > free:
+                break
+            free -= need
+            admitted.append(L)
+        n = len(admitted)
+        ids = list(range(n))
+        max_blocks = max(admitted) // T + 2
+        caches = []
+        for li in range(layers):
+            c = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=n,
+                          max_blocks_per_seq=max_blocks, num_comp_slots=n_comp, num_raw_slots=n_raw,
+                          compressed=compressed, perm_seed=13 + li)
+            c.calibrate(pk[:256], pv[:256])
+            for sid, L in enumerate(admitted):
+                off = (997 * (sid + 7 * li)) % 4096
+                c.append([sid], pk[None, off:off + L], pv[None, off:off + L])
+            caches.append(c)
+        torch.cuda.synchronize()
+        flags, st = caches[0].status()
+        if flags:
+            raise RuntimeError(f"equal-memory serving ({name}): cache status flags {flags}")
+        q = dev(synth.queries(dataclasses.replace(cfg, n_seqs=n)))
+        out = torch.empty((n, Hq, D), dtype=torch.int16, device="cuda")
+        ws = caches[0].workspace(n, splits)
+        for i in range(4):  # warm-up
+            caches[i % layers].decode_step(ids, pk[i * n:(i + 1) * n], pv[i * n:(i + 1) * n], q, cfg.scale, splits, ws, out)
+        torch.cuda.synchronize()
+        a_ = torch.cuda.Event(enable_timing=True)
+        b_ = torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        for i in range(4, 4 + steps):
+            caches[i % layers].decode_step(ids, pk[i * n:(i + 1) * n], pv[i * n:(i + 1) * n], q, cfg.scale, splits, ws, out)
+        b_.record(stream)
+        torch.cuda.synchronize()
+        step_us = a_.elapsed_time(b_) * 1e3 / steps
+        flags, st = caches[0].status()
+        if flags:
+            raise RuntimeError(f"equal-memory serving ({name}): cache status flags {flags} after the steps")
+        res[name] = {"admitted": n, "context_tokens": sum(admitted), "comp_slots": n_comp, "raw_slots": n_raw,
+                     "raw_fallback_tiles": st["raw_tiles"] if compressed else None,
+                     "step_us_per_layer": round(step_us, 1),
+                     "decode_tokens_per_s_per_layer": round(n / (step_us * 1e-6), 1)}
+        del caches, ws, out, q
+        torch.cuda.empty_cache()
+    res["admitted_ratio"] = round(res["compressed"]["admitted"] / res["uncompressed"]["admitted"], 4)
+    res["context_tokens_ratio"] = round(res["compressed"]["context_tokens"] / res["uncompressed"]["context_tokens"], 4)
+    res["throughput_ratio"] = round(res["compressed"]["decode_tokens_per_s_per_layer"] /
+                                    res["uncompressed"]["decode_tokens_per_s_per_layer"], 4)
+    log(f"[bench] equal-memory serving: {res}")
     return res
 
 
