@@ -57,8 +57,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep", type=str, default="", help="comma-separated split counts to time (extra)")
     ap.add_argument("--probe", action="store_true", help="also time plain HBM copy / read kernels (torch)")
-    ap.add_argument("--extra", type=str, default="fp8,paged,groups,rope,serving",
-                    help="comma list of extra workloads measured after the headline one: fp8 (the 64K layer in "
+    ap.add_argument("--extra", type=str, default="context,fp8,paged,groups,rope,serving",
+                    help="comma list of extra workloads measured after the headline one: context (the cfg2 "
+                         "layer at 32K and 128K tokens), fp8 (the 64K layer in "
                          "FP8 E5M2 and E4M3), paged (32-sequence paged serving mix), groups (the 64K layer's "
                          "codec with 16- and 8-token exponent groups), rope (escape bytes and raw tiles along "
                          "the 64K layer with RoPE-rotated keys, per calibration policy), serving (sequences "
@@ -319,6 +320,12 @@ def main():
     if extras:
         del comp, raw
         torch.cuda.empty_cache()
+    if "context" in extras:
+        import dataclasses
+        result["context_sweep"] = {
+            f"{L // 1024}k": extra_steps(torch, K, synth, dataclasses.replace(cfg, context=(L,), name=f"qwen3-8b-like-{L // 1024}k"),
+                                         args, splits=S)
+            for L in (32768, 131072)}
     if "fp8" in extras:
         result["fp8_64k"] = {name: extra_steps(torch, K, synth, synth.config(4, fmt), args, splits=S)
                              for name, fmt in (("e5m2", synth.E5M2), ("e4m3", synth.E4M3))}
