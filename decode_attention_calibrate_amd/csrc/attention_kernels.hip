@@ -27,6 +27,8 @@
 //   Softmax: online, fp32, base-2 (scores pre-multiplied by scale*log2(e)); per-split outputs
 //          (acc, max, sum) go to the workspace and combine_kernel merges them.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -59,6 +61,8 @@ struct AttnArgs {
   const uint8_t* k_new;  // decode step: the new tokens, [n][Hkv][D] elements (else null)
   const uint8_t* v_new;
   int new_pos[kMaxSeqsPerLaunch];  // their tail positions
+  int order[kMaxSeqsPerLaunch];    // blockIdx.z -> sequence index: longest sequences first, so the
+                                   // workgroups with the most blocks are dispatched first
 };
 
 
@@ -514,7 +518,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   uint4* qlds = reinterpret_cast<uint4*>(esc_base + 4 * esc_room);  // [g][D/8] query chunks
   uint32_t* blds = reinterpret_cast<uint32_t*>(qlds + G.g * (D / 8));  // [2][NR][16] packed bases
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
-  const int split = blockIdx.x, h = blockIdx.y, si = blockIdx.z;
+  const int split = blockIdx.x, h = blockIdx.y, si = a.order[blockIdx.z];
   const int seq = a.S.ids[si], L = a.S.lens[si];
   const SbOrder ord(L, a.n_splits, split);
   if (a.k_new != nullptr && split == 0) store_new_token<FMT>(a, si, h);
@@ -780,7 +784,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   constexpr int D = 32 * NR;
   const Geo& G = a.G;
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
-  const int split = blockIdx.x, h = blockIdx.y, si = blockIdx.z;
+  const int split = blockIdx.x, h = blockIdx.y, si = a.order[blockIdx.z];
   const int seq = a.S.ids[si], L = a.S.lens[si];
   const SbOrder ord(L, a.n_splits, split);
   if (a.k_new != nullptr && split == 0) store_new_token<FMT>(a, si, h);
@@ -1087,7 +1091,13 @@ int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& S, 
   AttnArgs a;
   a.k_new = reinterpret_cast<const uint8_t*>(k_new);
   a.v_new = reinterpret_cast<const uint8_t*>(v_new);
-  for (int i = 0; i < kMaxSeqsPerLaunch; ++i) a.new_pos[i] = (k_new && i < S.n) ? new_pos[i] : 0;
+  for (int i = 0; i < kMaxSeqsPerLaunch; ++i) {
+    a.new_pos[i] = (k_new && i < S.n) ? new_pos[i] : 0;
+    a.order[i] = i;
+  }
+  // longest first (stable): with the same split count for every sequence, a long sequence's
+  // workgroups carry the most blocks, and dispatching them first shortens the kernel's tail
+  std::stable_sort(a.order, a.order + S.n, [&](int x, int y) { return S.lens[x] > S.lens[y]; });
   a.G = G;
   a.B = B;
   a.S = S;
