@@ -288,3 +288,34 @@ def test_misaligned_buffers_rejected():
     out = host(cache.decode_step([0], dev(k[None, -1:]), dev(v[None, -1:]), q, cfg.scale, 2))
     assert cache.seq_length(0) == L0 + 1
     assert row_rel_err(out, _oracle(cfg, [(k, v)], host(q))) <= TOL
+
+
+def test_more_sequences_than_one_launch():
+    """70 sequences of mixed lengths (two launches of at most 64, each dispatched longest first),
+    listed in a shuffled order: attention and a decode step (no block completed, so the split
+    kernel stores every new token) match the oracle for every sequence."""
+    import dataclasses
+    cfg = synth.config(0)
+    g = synth.LayerGen(cfg)
+    rng = np.random.default_rng(5)
+    lens = [int(L) + 2 if (int(L) + 1) % cfg.T == 0 else int(L) for L in rng.integers(1, 300, size=70)]
+    kc, vc = g.tokens(256)
+    toks = [g.tokens(L + 1) for L in lens]
+    cache = new_cache(Hkv=cfg.Hkv, Hq=cfg.Hq, D=cfg.D, T=cfg.T, max_seqs=70, max_blocks=6)
+    cache.calibrate(dev(kc), dev(vc))
+    for sid, (k, v) in enumerate(toks):
+        cache.append([sid], dev(k[None, :lens[sid]]), dev(v[None, :lens[sid]]))
+    ids = rng.permutation(70).tolist()
+    q = synth.queries(dataclasses.replace(cfg, n_seqs=70), step=4)
+
+    def ref(extra):
+        return np.stack([oracle.attention(oracle.BF16, q[i], toks[s][0][:lens[s] + extra], toks[s][1][:lens[s] + extra],
+                                          cfg.scale) for i, s in enumerate(ids)])
+
+    out = host(cache.attention(ids, dev(q), cfg.scale, 3))
+    assert row_rel_err(out, ref(0)) <= TOL
+    kn = np.stack([toks[s][0][lens[s]] for s in ids])
+    vn = np.stack([toks[s][1][lens[s]] for s in ids])
+    out = host(cache.decode_step(ids, dev(kn), dev(vn), dev(q), cfg.scale, 3))
+    assert row_rel_err(out, ref(1)) <= TOL
+    assert [cache.seq_length(s) for s in range(70)] == [L + 1 for L in lens]
