@@ -2,7 +2,7 @@
 
 The method is GAAC's (page "GAAC: Lossless KV Compression for Bandwidth-Efficient LLM Inference
 on Personal Devices"): calibrated per-(head, channel) exponent bases, 3-bit / 4-bit / raw
-exponent modes per 16-token group, sign and mantissa stored raw, fixed-capacity slots behind a
+exponent modes per 16-token (or 8-token) group, sign and mantissa stored raw, fixed-capacity slots behind a
 paged block table, and a decode-attention kernel that rebuilds tiles on chip.
 
 Everything runs in hand-written HIP kernels behind the C ABI of include/kvc.h (libkvc.so);

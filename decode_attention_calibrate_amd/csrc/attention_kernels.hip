@@ -872,9 +872,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 //   * M = the largest of the split maxima (splits that saw a token) and the tail scores; the
 //     weights exp2(m_s - M), exp2(s_t - M) go to LDS; den = sum_s w_s l_s + sum_t w_t.
 //   * out = (sum_s w_s acc_s + sum_t w_t v_t) / den, rounded to BF16.
-// Decode step (k_new != null): the sequence's newest token, the last of its tail, is read from
-// k_new / v_new instead of the tail, and the first block of each KV-head group writes it into
-// the tail for later steps (no other block reads that tail position in this launch).
+// In a decode step the newest token is already in the tail: the split kernel that ran before
+// this one stored it there (store_new_token).
 constexpr int kCombineThreads = 256;
 constexpr int kMaxSplits = 1024;
 constexpr int kTailTok = 64;        // tail tokens a block can hold (T <= 64)

@@ -2,7 +2,7 @@
 // tile (codec of the page "GAAC: Lossless KV Compression ...", §3.1: exponent = calibrated
 // base + offset, sign and mantissa stored unchanged; §3.2: values are rebuilt on chip).
 //
-// The rebuild works on one group of 16 tokens of one channel at a time, four tokens per
+// The rebuild works on one exponent group (16 or 8 tokens of one channel) at a time, four tokens per
 // 32-bit word ("SWAR"): the 3-bit codes arrive one per byte lane, the escape planes are
 // spread to bit 3+p of each byte, the base is added to all four bytes at once (no carry can
 // cross a byte since every exponent is <= 255), and two v_perm/v_bfi steps interleave the

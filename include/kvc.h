@@ -183,10 +183,11 @@ int kv_attention_combine(kvc_cache* cache, const int32_t* seq_ids_host, int32_t 
  * [n_seqs][Hkv][D] elements, 16-byte aligned) and evaluates kv_decode_attention over all of its
  * tokens including the new one (GAAC page §3.2 with §3.3's fill-then-finalize), with the result
  * of kv_encode_append(.., n_tokens = 1) followed by kv_decode_attention, bit for bit.  When no
- * listed sequence's new token completes a block, the new token is attended and stored into the
- * tail by the merge kernel itself (no separate append launch); otherwise the step is exactly
- * that append (which encodes the finished block) and that attention.  Arguments and checks as
- * kv_encode_append and kv_decode_attention. */
+ * listed sequence's new token completes a block, the split kernel stores the new token into the
+ * tail while it attends the finished blocks, and the merge kernel attends the tail with it (no
+ * separate append launch); otherwise the step is exactly that append (which encodes the
+ * finished block) and that attention.  Arguments and checks as kv_encode_append and
+ * kv_decode_attention, all made before anything runs. */
 int kv_decode_step(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs, const void* k_new_dev,
                    const void* v_new_dev, const void* q_dev, float scale, int32_t n_splits, void* ws_dev,
                    size_t ws_bytes, void* out_dev, void* stream);
