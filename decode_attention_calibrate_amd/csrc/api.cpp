@@ -134,6 +134,18 @@ std::vector<int32_t> permutation(int n, uint64_t seed) {
   return v;
 }
 
+// The free-stack array for a permuted pool: the slots of sub-stack s (those equal to s modulo
+// kPoolStripes) keep their order in perm and go to indices s, s + 16, s + 32, ...
+std::vector<int32_t> stack_layout(const std::vector<int32_t>& perm) {
+  std::vector<int32_t> out(perm.size());
+  int next[kvc::kPoolStripes] = {};
+  for (int32_t slot : perm) {
+    const int s = slot % kvc::kPoolStripes;
+    out[(size_t)kvc::kPoolStripes * next[s]++ + s] = slot;
+  }
+  return out;
+}
+
 int check_seq_ids(const kvc_cache* c, const int32_t* ids, int n) {
   if (!ids || n < 1) return fail(KVC_EINVAL, "seq_ids must list at least one sequence");
   std::vector<char> seen(c->p.max_seqs, 0);
@@ -190,13 +202,13 @@ int kv_cache_create(const kvc_params* params, const kvc_buffers* buffers, uint64
   c->len.assign(params->max_seqs, 0);
   hipStream_t st = (hipStream_t)stream;
   if (G.n_comp > 0) {
-    const std::vector<int32_t> perm = permutation(G.n_comp, perm_seed);
+    const std::vector<int32_t> perm = stack_layout(permutation(G.n_comp, perm_seed));
     rc = hip_fail((int)hipMemcpyAsync(c->B.comp_free, perm.data(), perm.size() * 4, hipMemcpyHostToDevice, st),
                   "copy compressed free stack");
     if (rc == KVC_OK) rc = hip_fail((int)hipStreamSynchronize(st), "synchronise");
   }
   if (rc == KVC_OK && G.n_raw > 0) {
-    const std::vector<int32_t> perm = permutation(G.n_raw, perm_seed ^ 0x5A5A5A5A5A5A5A5Aull);
+    const std::vector<int32_t> perm = stack_layout(permutation(G.n_raw, perm_seed ^ 0x5A5A5A5A5A5A5A5Aull));
     rc = hip_fail((int)hipMemcpyAsync(c->B.raw_free, perm.data(), perm.size() * 4, hipMemcpyHostToDevice, st),
                   "copy raw free stack");
     if (rc == KVC_OK) rc = hip_fail((int)hipStreamSynchronize(st), "synchronise");
@@ -447,13 +459,17 @@ int kv_get_status(kvc_cache* c, uint32_t* flags, kvc_stats* stats, void* stream)
   if (stats) {
     *stats = kvc_stats{};
     for (const kvc::StatStripe& st : h.stat) {
-      stats->comp_tiles += st.comp_tiles;
       stats->raw_tiles += st.raw_tiles;
       for (int i = 0; i < 3; ++i) stats->groups[i] += st.groups[i];
       stats->esc_bytes += st.esc_bytes;
     }
-    stats->comp_free = h.comp_top;
-    stats->raw_free = h.raw_top;
+    // every compressed tile adds exactly NG groups
+    stats->comp_tiles = (stats->groups[0] + stats->groups[1] + stats->groups[2]) / (uint64_t)c->G.NG;
+    stats->comp_free = stats->raw_free = 0;
+    for (int s = 0; s < kvc::kPoolStripes; ++s) {
+      stats->comp_free += h.comp_top[s].n;
+      stats->raw_free += h.raw_top[s].n;
+    }
   }
   return KVC_OK;
 }

@@ -76,16 +76,15 @@ __global__ void init_kernel(Geo G, DevBufs B) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_table; i += stride) B.table[i] = kUnallocated;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_bases; i += stride) B.bases[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+  if (blockIdx.x == 0 && threadIdx.x < kPoolStripes) {
     Counters* c = B.counters;
-    c->comp_top = G.compressed ? G.n_comp : 0;
-    c->raw_top = G.n_raw;
-    c->status = 0;
-    c->pad = 0;
+    c->comp_top[threadIdx.x].n = G.compressed ? pool_stripe_size(G.n_comp, threadIdx.x) : 0;
+    c->raw_top[threadIdx.x].n = pool_stripe_size(G.n_raw, threadIdx.x);
+    if (threadIdx.x == 0) c->status = 0;
   }
   if (blockIdx.x == 0 && threadIdx.x < kStatStripes) {
     StatStripe& st = B.counters->stat[threadIdx.x];
-    st.comp_tiles = st.raw_tiles = 0;
+    st.raw_tiles = 0;
     st.groups[0] = st.groups[1] = st.groups[2] = 0;
     st.esc_bytes = 0;
   }
@@ -209,42 +208,45 @@ __device__ __forceinline__ void gather_block(const Geo& G, const uint8_t* tail, 
 // Pops a slot for one tile (raw or compressed, falling back to raw when the compressed pool is
 // empty) and adds the tile to the statistics.  Thread 0 only; returns the slot (-1: both pools
 // empty) and sets *raw.
+// Pops a slot from one pool's sub-stacks, starting at sub-stack s0; -1 when all are empty.
+__device__ int pop_from(PoolTop* top, const int32_t* stack, int s0) {
+  for (int k = 0; k < kPoolStripes; ++k) {
+    const int s = (s0 + k) % kPoolStripes;
+    const int idx = atomicSub(&top[s].n, 1) - 1;
+    if (idx >= 0) return stack[kPoolStripes * idx + s];
+    atomicAdd(&top[s].n, 1);
+  }
+  return -1;
+}
+
 __device__ int pop_slot(const DevBufs& B, int want_raw, const unsigned long long modes[3], int esc_bytes, int* raw_out) {
-Counters* C = B.counters;
-int slot = -1, raw = want_raw;
-if (!raw) {
-  const int idx = atomicSub(&C->comp_top, 1) - 1;
-  if (idx >= 0) {
-    slot = B.comp_free[idx];
-  } else {
-    atomicAdd(&C->comp_top, 1);
-    atomicOr(&C->status, 1u);
-    raw = 1;
+  Counters* C = B.counters;
+  const int h = blockIdx.x + 7 * blockIdx.y + 3 * blockIdx.z;  // spreads workgroups over the stripes
+  int slot = -1, raw = want_raw;
+  if (!raw) {
+    slot = pop_from(C->comp_top, B.comp_free, h % kPoolStripes);
+    if (slot < 0) {
+      atomicOr(&C->status, 1u);
+      raw = 1;
+    }
   }
-}
-if (raw) {
-  const int idx = atomicSub(&C->raw_top, 1) - 1;
-  if (idx >= 0) {
-    slot = B.raw_free[idx];
-  } else {
-    atomicAdd(&C->raw_top, 1);
-    atomicOr(&C->status, 2u);
-  }
-}
-if (slot >= 0) {
-  StatStripe& st = C->stat[(blockIdx.x + 7 * blockIdx.y + 3 * blockIdx.z) % kStatStripes];
   if (raw) {
-    atomicAdd(&st.raw_tiles, 1ull);
-  } else {
-    atomicAdd(&st.comp_tiles, 1ull);
-    atomicAdd(&st.groups[0], modes[0]);
-    atomicAdd(&st.groups[1], modes[1]);
-    atomicAdd(&st.groups[2], modes[2]);
-    atomicAdd(&st.esc_bytes, (unsigned long long)esc_bytes);
+    slot = pop_from(C->raw_top, B.raw_free, h % kPoolStripes);
+    if (slot < 0) atomicOr(&C->status, 2u);
   }
-}
-*raw_out = raw;
-return slot;
+  if (slot >= 0) {
+    StatStripe& st = C->stat[h % kStatStripes];
+    if (raw) {
+      atomicAdd(&st.raw_tiles, 1ull);
+    } else {
+      atomicAdd(&st.groups[0], modes[0]);
+      atomicAdd(&st.groups[1], modes[1]);
+      atomicAdd(&st.groups[2], modes[2]);
+      atomicAdd(&st.esc_bytes, (unsigned long long)esc_bytes);
+    }
+  }
+  *raw_out = raw;
+  return slot;
 }
 
 // Stores the LDS tile [T][D] as a raw tile (K token-major, V channel-major) and its table entry.
@@ -606,12 +608,13 @@ __global__ void release_kernel(Geo G, DevBufs B, int seq, int n_blocks) {
     const uint32_t e = B.table[idx];
     if (e == kUnallocated) continue;
     const int slot = (int)(e & 0x00FFFFFFu);
+    const int s = slot % kPoolStripes;  // back to the sub-stack the slot belongs to
     if (e & 0x80000000u) {
-      const int t = atomicAdd(&B.counters->raw_top, 1);
-      B.raw_free[t] = slot;
+      const int t = atomicAdd(&B.counters->raw_top[s].n, 1);
+      B.raw_free[kPoolStripes * t + s] = slot;
     } else {
-      const int t = atomicAdd(&B.counters->comp_top, 1);
-      B.comp_free[t] = slot;
+      const int t = atomicAdd(&B.counters->comp_top[s].n, 1);
+      B.comp_free[kPoolStripes * t + s] = slot;
     }
     B.table[idx] = kUnallocated;
   }

@@ -44,20 +44,33 @@ struct Geo {
   int compressed;
 };
 
-// counters buffer (1 KB).  The statistics are spread over kStatStripes copies (one chosen per
-// encoding workgroup) so concurrent encodes do not all update the same few words; readers add
-// the stripes.
-constexpr int kStatStripes = 16;
-struct StatStripe {
-  unsigned long long comp_tiles, raw_tiles, groups[3], esc_bytes;
+// counters buffer (12,416 bytes).  Atomics to one 128-byte line are performed one after
+// another, and a bulk append encodes thousands of tiles at once, so every hot word has a line
+// of its own:
+//   * each free stack is kPoolStripes interleaved sub-stacks: sub-stack s holds the slots
+//     s, s + 16, s + 32, ... (a seeded permutation of them), its element k at index 16k + s of
+//     the stack array, with its own top; a tile pops from a preferred sub-stack and moves on
+//     to the next ones when it is empty; a released slot goes back to sub-stack slot % 16;
+//   * the statistics are kStatStripes copies (one chosen per encoding workgroup), which
+//     readers add; compressed tiles are not counted separately (each adds exactly NG groups).
+constexpr int kPoolStripes = 16;
+constexpr int kStatStripes = 64;
+struct alignas(128) PoolTop {
+  int32_t n;  // slots in this sub-stack
+};
+struct alignas(128) StatStripe {
+  unsigned long long raw_tiles, groups[3], esc_bytes;
 };
 struct Counters {
-  int32_t comp_top, raw_top;
-  uint32_t status, pad;
+  PoolTop comp_top[kPoolStripes];
+  PoolTop raw_top[kPoolStripes];
+  alignas(128) uint32_t status;
   StatStripe stat[kStatStripes];
 };
-constexpr size_t kCountersBytes = 1024;
-static_assert(sizeof(Counters) <= kCountersBytes, "counters buffer");
+constexpr size_t kCountersBytes = 128 * (2 * kPoolStripes + 1 + kStatStripes);
+static_assert(sizeof(Counters) == kCountersBytes, "counters buffer");
+// slots of sub-stack s in a pool of n slots
+__host__ __device__ inline int pool_stripe_size(int n, int s) { return n > s ? (n - s + kPoolStripes - 1) / kPoolStripes : 0; }
 
 struct DevBufs {
   uint8_t* comp_pool;

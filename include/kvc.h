@@ -93,7 +93,8 @@ typedef struct {
                         bytes used in 16-byte units, bits 0..23 = slot index                */
   void* comp_free;   /* [num_comp_slots] int32 free stack of compressed slots               */
   void* raw_free;    /* [num_raw_slots] int32 free stack of raw slots                       */
-  void* counters;    /* 1 KB: int32 stack tops, uint32 status, uint64 statistics (striped)  */
+  void* counters;    /* 8,320 B: int32 stack tops, uint32 status, uint64 statistics (64
+                        stripes of 128 B)                                                  */
 } kvc_buffers;
 
 #define KVC_NUM_BUFFERS 8

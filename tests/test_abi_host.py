@@ -65,7 +65,7 @@ def test_slot_stride_matches_format(K, T, D, fmt, Gt):
     assert sz[2] == 2 * 2 * 8 * T * D * eb
     assert sz[3] == 4 * 8 * D
     assert sz[4] == 2 * 1024 * 2 * 8 * 4
-    assert sz[5] == 2048 * 4 and sz[6] == 64 * 4 and sz[7] == 1024
+    assert sz[5] == 2048 * 4 and sz[6] == 64 * 4 and sz[7] == 128 * (2 * 16 + 1 + 64)
 
 
 @pytest.mark.parametrize("kw,code", [
