@@ -91,10 +91,13 @@ typedef struct {
   void* block_table; /* [max_seqs][max_blocks_per_seq][2 (K,V)][Hkv] uint32 entries:
                         0xFFFFFFFF = unallocated; else bit 31 = raw, bits 24..30 = escape
                         bytes used in 16-byte units, bits 0..23 = slot index                */
-  void* comp_free;   /* [num_comp_slots] int32 free stack of compressed slots               */
-  void* raw_free;    /* [num_raw_slots] int32 free stack of raw slots                       */
-  void* counters;    /* 8,320 B: int32 stack tops, uint32 status, uint64 statistics (64
-                        stripes of 128 B)                                                  */
+  void* comp_free;   /* [num_comp_slots] int32 free stack of compressed slots: 16
+                        interleaved sub-stacks (sub-stack s = the slots equal to s mod 16,
+                        its element k at index 16k + s), popped from a preferred sub-stack
+                        first                                                              */
+  void* raw_free;    /* [num_raw_slots] int32 free stack of raw slots, the same layout      */
+  void* counters;    /* 12,416 B: the 32 sub-stack tops, the status word and 64 stripes of
+                        uint64 statistics, each on its own 128-byte line                   */
 } kvc_buffers;
 
 #define KVC_NUM_BUFFERS 8
@@ -115,7 +118,8 @@ typedef struct kvc_cache kvc_cache; /* opaque host object */
 int kv_buffer_sizes(const kvc_params* params, size_t* out_bytes, size_t* slot_stride);
 
 /* Validates the parameters and buffers, initialises the block table (all unallocated), the
- * free stacks (a permutation of the slot ids seeded by perm_seed), the counters and the bases
+ * free stacks (a permutation of the slot ids seeded by perm_seed, dealt to the sub-stacks in
+ * that order), the counters and the bases
  * (zero), then synchronises the stream.  *out receives a host object the caller frees with
  * kv_cache_destroy.  The buffers must stay valid for the cache's lifetime. */
 int kv_cache_create(const kvc_params* params, const kvc_buffers* buffers, uint64_t perm_seed, void* stream,
