@@ -681,6 +681,31 @@ __device__ void decode_tile_any(const Geo& G, const DevBufs& B, const uint8_t* t
   }
 }
 
+// A compressed tile's tag planes and escape area in LDS, loaded by the whole workgroup in one
+// coalesced pass, with the escape units before every tag word (a wide or raw group has E set;
+// a raw BF16 group adds four more units).  Decoding threads then read only LDS.
+constexpr int kMaxTagWords = 64 * 128 / 8 / 32;  // T <= 64, D <= 128, groups of >= 8 tokens
+struct TileMeta {
+  uint32_t tag[2 * kMaxTagWords];  // plane E, then plane R
+  uint32_t pre[kMaxTagWords];
+  uint32_t esc[512 / 4];           // esc_cap <= 512
+};
+__device__ void stage_tile_meta(const Geo& G, const uint8_t* tile, TileMeta& m) {
+  const uint32_t* tag_g = reinterpret_cast<const uint32_t*>(tile + G.tag_off);
+  const uint32_t* esc_g = reinterpret_cast<const uint32_t*>(tile + G.esc_off);
+  for (int i = threadIdx.x; i < 2 * G.PW; i += blockDim.x) m.tag[i] = tag_g[i];
+  for (int i = threadIdx.x; i < G.esc_cap / 4; i += blockDim.x) m.esc[i] = esc_g[i];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t acc = 0;
+    for (int i = 0; i < G.PW; ++i) {
+      m.pre[i] = acc;
+      acc += __popc(m.tag[i]) + (uint32_t)(G.F - 4) * __popc(m.tag[G.PW + i]);
+    }
+  }
+  __syncthreads();
+}
+
 // Codes of slot s (0..7, a run-time value) of a CODE unit, one 3-bit code per byte lane.
 __device__ __forceinline__ uint32_t code_slot_rt(uint32_t W0, uint32_t W1, uint32_t W2, int s) {
   switch (s) {
@@ -700,17 +725,15 @@ __device__ __forceinline__ uint32_t code_slot_rt(uint32_t W0, uint32_t W1, uint3
 // Escape units are single bytes (an 8-bit plane per escaped group; a raw group adds four bytes
 // of offset bits 4..7, token tau's nibble at bits 4*tau).
 __device__ void decode_bf16_g8_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
-                                    const uint8_t* b4, uint16_t* out, int bi, int h) {
+                                    const uint8_t* b4, uint16_t* out, int bi, int h, TileMeta& m) {
   const int D = G.D, T = G.T;
-  const uint32_t* tagE = reinterpret_cast<const uint32_t*>(tile + G.tag_off);
-  const uint32_t* tagR = tagE + G.PW;
-  const uint8_t* esc = tile + G.esc_off;
+  stage_tile_meta(G, tile, m);
+  const uint8_t* esc = reinterpret_cast<const uint8_t*>(m.esc);
   const int n_units = G.raw_elems / 32;
   for (int u = threadIdx.x; u < n_units; u += blockDim.x) {
     const int q0 = 4 * u, w = q0 >> 5, bit = q0 & 31, tg = q0 / D, c0 = q0 % D;
-    uint32_t P = 0;  // escape bytes before group q0
-    for (int i = 0; i < w; ++i) P += __popc(tagE[i]) + 4u * __popc(tagR[i]);
-    const uint32_t Ew = tagE[w], Rw = tagR[w];
+    uint32_t P = m.pre[w];  // escape bytes before group q0
+    const uint32_t Ew = m.tag[w], Rw = m.tag[G.PW + w];
     const uint32_t below = bit == 0 ? 0u : (0xFFFFFFFFu >> (32 - bit));
     P += __popc(Ew & below) + 4u * __popc(Rw & below);
     const uint32_t* cw = reinterpret_cast<const uint32_t*>(tile + G.code_off + 12 * u);
@@ -780,9 +803,11 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
     return;
   }
   const uint8_t* tile = B.comp_pool + (size_t)slot * G.stride;
+  __shared__ TileMeta meta;
   if (G.EB == 2 && G.GT == 8) {
     decode_bf16_g8_tile(G, B, tile, B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
-                        B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, reinterpret_cast<uint16_t*>(outv), bi, h);
+                        B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, reinterpret_cast<uint16_t*>(outv), bi, h,
+                        meta);
     return;
   }
   if (G.EB == 1 || G.GT != kGroup) {
@@ -792,17 +817,15 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
   }
   uint16_t* out = reinterpret_cast<uint16_t*>(outv);
   auto out_at = [&](int t, int c) -> uint16_t* { return out + out_idx(t, c); };
-  const uint32_t* tagE = reinterpret_cast<const uint32_t*>(tile + G.tag_off);
-  const uint32_t* tagR = tagE + G.PW;
-  const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(tile + G.esc_off);
+  stage_tile_meta(G, tile, meta);
+  const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(meta.esc);
   const uint8_t* b3 = B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
   const uint8_t* b4 = B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;
   const int max_plane = G.esc_cap / 2;
   for (int pr = tid; pr < G.NP; pr += kThreads) {
     const int q0 = 2 * pr, w = q0 >> 5, bit = q0 & 31;
-    uint32_t Pw = 0;
-    for (int i = 0; i < w; ++i) Pw += __popc(tagE[i]) + 4u * __popc(tagR[i]);
-    const uint32_t Ew = tagE[w], Rw = tagR[w];
+    const uint32_t Pw = meta.pre[w];
+    const uint32_t Ew = meta.tag[w], Rw = meta.tag[G.PW + w];
     uint32_t P = planes_before(Ew, Rw, Pw, bit);
     const uint4 s0 = *reinterpret_cast<const uint4*>(tile + G.sm_off + 32 * pr);
     const uint4 s1 = *reinterpret_cast<const uint4*>(tile + G.sm_off + 32 * pr + 16);
