@@ -41,7 +41,9 @@ int hip_fail(int err, const char* what) {
   return KVC_EHIP;
 }
 
-int esc_cap_of(const kvc_params& p) { return p.esc_cap_bytes < 0 ? p.block_tokens * p.head_dim / 16 : p.esc_cap_bytes; }
+// Channels of one stored tile: a 256-channel head is stored as two 128-channel half-heads.
+int tile_channels(const kvc_params& p) { return p.head_dim == 256 ? 128 : p.head_dim; }
+int esc_cap_of(const kvc_params& p) { return p.esc_cap_bytes < 0 ? p.block_tokens * tile_channels(p) / 16 : p.esc_cap_bytes; }
 
 int check_params(const kvc_params* p) {
   if (!p) return fail(KVC_EINVAL, "params is NULL");
@@ -49,7 +51,8 @@ int check_params(const kvc_params* p) {
   if (p->num_kv_heads < 1 || p->num_q_heads < 1) return fail(KVC_EINVAL, "head counts must be >= 1");
   if (p->num_q_heads % p->num_kv_heads != 0) return fail(KVC_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
   if (p->num_q_heads / p->num_kv_heads > 16) return fail(KVC_EINVAL, "at most 16 query heads per KV head");
-  if (p->head_dim != 64 && p->head_dim != 128) return fail(KVC_EINVAL, "head_dim must be 64 or 128");
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return fail(KVC_EINVAL, "head_dim must be 64, 128 or 256");
   if (p->block_tokens < 16 || p->block_tokens % 16 != 0) return fail(KVC_EINVAL, "block_tokens must be a multiple of 16");
   if (p->group_tokens < 1 || p->block_tokens % p->group_tokens != 0)
     return fail(KVC_EINVAL, "group_tokens must divide block_tokens");
@@ -81,9 +84,12 @@ Geo make_geo(const kvc_params& p) {
   G.EB = p.dtype == KVC_BF16 ? 2 : 1;
   G.sm_pair = 4 * (1 + G.MB);
   G.T = p.block_tokens;
-  G.D = p.head_dim;
-  G.Hkv = p.num_kv_heads;
-  G.Hq = p.num_q_heads;
+  // a 256-channel head is stored as two 128-channel half-heads: the same memory as
+  // [..][2 Hkv][128], so every kernel sees half-heads
+  const int halves = p.head_dim / tile_channels(p);
+  G.D = tile_channels(p);
+  G.Hkv = p.num_kv_heads * halves;
+  G.Hq = p.num_q_heads * halves;
   G.g = p.num_q_heads / p.num_kv_heads;
   G.GT = p.group_tokens;
   G.NT = G.T / G.GT;
@@ -294,6 +300,8 @@ size_t kv_attention_workspace_bytes(const kvc_params* p, int32_t n_seqs, int32_t
 static int check_group_tokens_for_attention(const kvc_cache* c) {
   if (c->G.compressed && c->G.GT != kvc::kGroup)
     return fail(KVC_EUNSUPPORTED, "the attention kernels rebuild 16-token groups; this cache uses 8-token groups");
+  if (c->p.head_dim == 256)
+    return fail(KVC_EUNSUPPORTED, "the attention kernels take head_dim 64 or 128; 256-channel heads are stored only");
   return KVC_OK;
 }
 

@@ -63,7 +63,12 @@ typedef struct {
   int32_t num_kv_heads;       /* Hkv                                                         */
   int32_t num_q_heads;        /* Hq; Hq % Hkv == 0, Hq / Hkv <= 16 (query head hq reads KV
                                  head hq / (Hq / Hkv))                                       */
-  int32_t head_dim;           /* D in {64, 128}                                              */
+  int32_t head_dim;           /* D in {64, 128, 256}.  A 256-channel head is stored as two
+                                 128-channel half-heads (GAAC page App. D): the tiles, tails,
+                                 bases and table rows of [..][Hkv][256] data are those of
+                                 [..][2 Hkv][128], the same memory (a block takes 2 x 2 Hkv
+                                 slots); calibration, encode, decode and statistics work on
+                                 it, decode attention returns KVC_EUNSUPPORTED               */
   int32_t block_tokens;       /* T: tokens per block/tile, multiple of 16, 16..256           */
   int32_t group_tokens;       /* G: tokens per exponent group, 16 or 8 in this build (GAAC
                                  page §3.1 groups the exponents of a few tokens of one

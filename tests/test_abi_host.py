@@ -95,3 +95,12 @@ def test_null_handles_rejected(K):
     assert lib.kv_decode_attention(None, ids, 1, None, 1.0, 1, None, 0, None, None) == -1
     assert lib.kv_get_status(None, None, None, None) == -1
     assert b"NULL" in lib.kv_last_error()
+
+
+def test_head_dim_256_is_stored_as_half_heads(K):
+    """A 256-channel head is two 128-channel half-heads: every buffer size and the slot stride are
+    those of the same cache with twice the KV heads at head_dim 128."""
+    rc, sz, stride, _ = _sizes(K, _params(K, head_dim=256, num_kv_heads=8, num_q_heads=32))
+    rc2, sz2, stride2, _ = _sizes(K, _params(K, head_dim=128, num_kv_heads=16, num_q_heads=64))
+    assert rc == 0 and rc2 == 0
+    assert sz == sz2 and stride == stride2 == oracle.layout(oracle.Params(oracle.BF16, 64, 128, 16))["stride"]

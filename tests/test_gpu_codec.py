@@ -159,3 +159,34 @@ def test_cfg2_full_context_codec():
     ost = oracle.stats(p, oseqs)
     assert st["raw_tiles"] == ost["raw_tiles"]
     assert st["esc_bytes"] == sum(int(t["esc"].sum()) for t in oseqs[0].tiles)
+
+
+def test_head_dim_256_half_heads():
+    """A 256-channel head (GAAC page App. D: two 128-channel half-heads): encoded bytes equal the
+    oracle's for the half-head view of the same tokens, blocks decode back bit for bit, and
+    decode attention is refused before anything runs."""
+    import dataclasses
+    from decode_attention_calibrate_amd._lib import KVCError
+    cfg = dataclasses.replace(synth.config(0), D=256)
+    g, toks = synth.sequence_tokens(cfg)
+    k, v = toks[0]
+    n_tiles = 17 * 2 * 2 * cfg.Hkv  # a block holds two half-head tiles per head, for K and V
+    cache = new_cache(Hkv=cfg.Hkv, Hq=cfg.Hq, D=256, T=cfg.T, max_seqs=1, max_blocks=17, comp_slots=n_tiles,
+                      raw_slots=n_tiles)
+    cache.calibrate(dev(k[:cfg.n_cal]), dev(v[:cfg.n_cal]))
+    cache.append([0], dev(k[None, :1000]), dev(v[None, :1000]))
+    half = lambda a: a.reshape(a.shape[0], 2 * cfg.Hkv, 128)  # the same memory as half-heads
+    p = oracle.Params(oracle.BF16, cfg.T, 128, cfg.G)
+    _, oseqs = oracle_layer(p, 2 * cfg.Hkv, half(k[:cfg.n_cal]), half(v[:cfg.n_cal]), [(half(k[:1000]), half(v[:1000]))])
+    view = new_cache(Hkv=2 * cfg.Hkv, Hq=2 * cfg.Hq, D=128, T=cfg.T, max_seqs=1, max_blocks=17)  # for its metadata
+    view.buffers = cache.buffers
+    view.slot_stride = cache.slot_stride
+    assert compare_tiles(view, p, oseqs, [0]) == 15 * 2 * 2 * cfg.Hkv
+    kd, vd = cache.decode_blocks(0, 0, 15)
+    assert np.array_equal(host(kd), k[:960]) and np.array_equal(host(vd), v[:960])
+    flags, st = cache.status()
+    assert flags == 0 and st["comp_tiles"] == 15 * 2 * 2 * cfg.Hkv and st["raw_tiles"] == 0
+    q = dev(synth.queries(dataclasses.replace(cfg, D=256)))
+    with pytest.raises(KVCError) as e:
+        cache.attention([0], q, cfg.scale, 2)
+    assert e.value.code == -3
