@@ -725,6 +725,14 @@ def cpu_baseline(cfg, k0, v0, min_seconds=10.0):
         t_att += t2 - t1
         reps += 1
         del kd, vd
+    # the same step once on a single thread
+    t0 = time.perf_counter()
+    kd, vd = s.decoded(nthreads=1)
+    t1 = time.perf_counter()
+    oracle.attention(oracle.BF16, q, kd, vd, cfg.scale, nthreads=1)
+    t2 = time.perf_counter()
+    del kd, vd
+    single = {"us_per_step": round((t2 - t0) * 1e6, 1), "decode_s": round(t1 - t0, 3), "attention_s": round(t2 - t1, 3)}
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -737,7 +745,7 @@ def cpu_baseline(cfg, k0, v0, min_seconds=10.0):
             "sample": f"{reps} full decode steps of the 64K layer, each: rebuild all {len(s.tiles) * 2 * cfg.Hkv} "
                       f"tiles from their stored bytes ({t_dec / reps:.3f} s) + exact fp64 attention for all "
                       f"{cfg.Hq} query heads ({t_att / reps:.3f} s); {t_dec + t_att:.1f} s in total",
-            "cpu_model": cpu_model, "nproc": os.cpu_count()}
+            "cpu_model": cpu_model, "nproc": os.cpu_count(), "single_thread": single}
 
 
 if __name__ == "__main__":
