@@ -52,7 +52,6 @@ enum : int { SRC_COMP = 0, SRC_RAW = 1, SRC_NONE = 2 };
 struct AttnArgs {
   Geo G;
   DevBufs B;
-  SeqList S;
   const uint16_t* q;
   float* ws_acc;
   float* ws_ml;
@@ -60,9 +59,10 @@ struct AttnArgs {
   int n_splits;
   const uint8_t* k_new;  // decode step: the new tokens, [n][Hkv][D] elements (else null)
   const uint8_t* v_new;
-  int new_pos[kMaxSeqsPerLaunch];  // their tail positions
-  int order[kMaxSeqsPerLaunch];    // blockIdx.z -> sequence index: longest sequences first, so the
-                                   // workgroups with the most blocks are dispatched first
+  // blockIdx.z -> {sequence index i (row of q, k_new, v_new and the workspace), sequence id,
+  // tokens in finished blocks, tail position of the new token}; longest sequences first, so the
+  // workgroups with the most blocks are dispatched first.  One scalar load per workgroup.
+  int4 zrow[kMaxSeqsPerLaunch];
 };
 
 
@@ -81,12 +81,12 @@ struct FmtT {
 // Compile-time geometry of a compressed tile (FORMAT v1) for head_dim 32*NR, T = TT tokens and
 // element format FMT.
 // Decode step: the first split of each (sequence, KV head) stores the sequence's new token into
-// the tail (K row new_pos, V column new_pos); the merge kernel that follows reads it there.
+// the tail (K row t, V column t) once its own work is done; the merge kernel that follows reads
+// it there.
 template <int FMT>
-__device__ __forceinline__ void store_new_token(const AttnArgs& a, int si, int h) {
+__device__ __forceinline__ void store_new_token(const AttnArgs& a, int si, int seq, int t, int h) {
   constexpr int EB = FmtT<FMT>::EB;
   const Geo& G = a.G;
-  const int seq = a.S.ids[si], t = a.new_pos[si];
   uint8_t* tk = reinterpret_cast<uint8_t*>(a.B.tail) + tail_offset(G, seq, 0, h) * EB;
   uint8_t* tv = reinterpret_cast<uint8_t*>(a.B.tail) + tail_offset(G, seq, 1, h) * EB;
   const uint8_t* kn = a.k_new + ((size_t)si * G.Hkv + h) * G.D * EB;
@@ -503,6 +503,18 @@ struct SbOrder {
 // First token of lane group j's 16-token group in super-block sb.
 __device__ __forceinline__ int group_token(int sb, int j) { return sb * kSB + 16 * j; }
 
+// Co-resident waves of a SIMD issue in age order when their priorities are equal, so the wave
+// dispatched first runs ahead and the later one finishes alone, at a fraction of the SIMD's
+// issue rate.  Each wave lowers its priority as its remaining work shrinks (rp = K and V phases
+// left, the current one included): the wave that is behind wins the issue slot, and waves that
+// share a SIMD finish together.
+__device__ __forceinline__ void phase_priority(int rp) {
+  if (rp >= 6) __builtin_amdgcn_s_setprio(3);
+  else if (rp >= 4) __builtin_amdgcn_s_setprio(2);
+  else if (rp >= 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // ------------------------------------------------------------------------------------------
 // Compressed cache.
 template <int NR, int TT, int FMT>
@@ -518,25 +530,40 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   uint4* qlds = reinterpret_cast<uint4*>(esc_base + 4 * esc_room);  // [g][D/8] query chunks
   uint32_t* blds = reinterpret_cast<uint32_t*>(qlds + G.g * (D / 8));  // [2][NR][16] packed bases
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
-  const int split = blockIdx.x, h = blockIdx.y, si = a.order[blockIdx.z];
-  const int seq = a.S.ids[si], L = a.S.lens[si];
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int4 z = a.zrow[blockIdx.z];
+  const int si = z.x, seq = z.y, L = z.z;
   const SbOrder ord(L, a.n_splits, split);
-  if (a.k_new != nullptr && split == 0) store_new_token<FMT>(a, si, h);
   uint8_t* esc_lds = esc_base + j * esc_room;
   const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(esc_lds);
   const uint32_t below = (1u << (2 * n)) - 1u;
   uint32_t flags = 0, bad = 0;
   init_esc_lut();
 
-  // query heads h*g .. h*g+g-1 and the calibrated bases of every lane's channel pairs go to
-  // LDS once (keeps the per-lane register budget at two waves per SIMD)
-  for (int k = lane; k < G.g * (D / 8); k += kWave)
-    qlds[k] = ld128(a.q + ((size_t)si * G.Hq + h * G.g) * D + 8 * k);
-  for (int k = lane; k < 2 * NR * 16; k += kWave) {
+  // Prologue: one memory round trip before the first tile loads.  The first super-block's
+  // table entries, the query heads h*g .. h*g+g-1 (g * D/8 <= 256 chunks: at most four per lane)
+  // and the calibrated bases of every lane's channel pairs are all requested together; the
+  // query and the bases go to LDS (keeping the per-lane register budget at two waves per SIMD)
+  // only after the first tiles' loads are in flight.
+  uint32_t eK = kUnallocated, eV = kUnallocated;
+  if (ord.cnt > 0) {
+    eK = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 0, h);
+    eV = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 1, h);
+  }
+  uint4 qr[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int k = lane + kWave * u;
+    qr[u] = k < G.g * (D / 8) ? ld128(a.q + ((size_t)si * G.Hq + h * G.g) * D + 8 * k) : make_uint4(0, 0, 0, 0);
+  }
+  uint32_t br[2 * NR * 16 / kWave];
+#pragma unroll
+  for (int u = 0; u < 2 * NR * 16 / kWave; ++u) {
+    const int k = lane + kWave * u;
     const int kv = k / (NR * 16), i = (k / 16) % NR, nn = k % 16, c0 = 32 * i + 2 * nn;
     const uint8_t* b3 = a.B.bases + ((size_t)(2 * kv) * G.Hkv + h) * D;
     const uint8_t* b4 = b3 + (size_t)G.Hkv * D;
-    blds[k] = b3[c0] | (b3[c0 + 1] << 8) | (b4[c0] << 16) | (b4[c0 + 1] << 24);
+    br[u] = b3[c0] | (b3[c0 + 1] << 8) | (b4[c0] << 16) | (b4[c0 + 1] << 24);
   }
 
   float m = -INFINITY, l = 0.0f;
@@ -544,15 +571,22 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
   for (int i = 0; i < NR; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  CRegs<NR, FMT> cK, cV;
+  TileRef rK, rV;
   if (ord.cnt > 0) {
-    CRegs<NR, FMT> cK, cV;
-    TileRef rK, rV;
-    uint32_t eK = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 0, h);
-    uint32_t eV = load_entry<TT>(a, seq, L, group_token(ord.at(0), j), 1, h);
     rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(0), j), 0, h, eK);
     flags |= missing_flag(L, group_token(ord.at(0), j), eK);
     load_tile<NR, TT, FMT>(rK, n, cK);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (lane + kWave * u < G.g * (D / 8)) qlds[lane + kWave * u] = qr[u];
+#pragma unroll
+  for (int u = 0; u < 2 * NR * 16 / kWave; ++u) blds[lane + kWave * u] = br[u];
+
+  if (ord.cnt > 0) {
     for (int it = 0; it < ord.cnt; ++it) {
+      phase_priority(2 * (ord.cnt - it));
       const int sb = ord.at(it);
       // V bytes of this super-block load while K is rebuilt and scored
       rV = tile_ref<NR, TT, FMT>(a, seq, L, group_token(sb, j), 1, h, eV);
@@ -679,6 +713,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
         load_tile<NR, TT, FMT>(rK, n, cK);
       }
 
+      phase_priority(2 * (ord.cnt - it) - 1);
       // ---- V: rebuild straight into B operands ----
       __syncthreads();
       const uint32_t pfxV = stage_escape<NR, FMT>(cV, rV, n, esc_lds);
@@ -728,6 +763,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   if (bad) flags |= 8u;
   if (flags) atomicOr(&a.B.counters->status, flags);
   write_partial<NR>(a, si, h, split, m, l, acc);
+  if (a.k_new != nullptr && split == 0) store_new_token<FMT>(a, si, seq, z.w, h);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -784,10 +820,10 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   constexpr int D = 32 * NR;
   const Geo& G = a.G;
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
-  const int split = blockIdx.x, h = blockIdx.y, si = a.order[blockIdx.z];
-  const int seq = a.S.ids[si], L = a.S.lens[si];
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int4 z = a.zrow[blockIdx.z];
+  const int si = z.x, seq = z.y, L = z.z;
   const SbOrder ord(L, a.n_splits, split);
-  if (a.k_new != nullptr && split == 0) store_new_token<FMT>(a, si, h);
   uint32_t flags = 0;
 
   uint4 qb[NR];
@@ -810,6 +846,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
     flags |= missing_flag(L, group_token(ord.at(0), jr), eK);
     raw_load_k<NR, TT, FMT>(rK, n, j, ck);
     for (int it = 0; it < ord.cnt; ++it) {
+      phase_priority(2 * (ord.cnt - it));
       const int sb = ord.at(it);
       const TileRef rV = tile_ref<NR, TT, FMT>(a, seq, L, group_token(sb, j), 1, h, eV);
       flags |= missing_flag(L, group_token(sb, j), eV);
@@ -841,6 +878,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
         flags |= missing_flag(L, group_token(ord.at(it + 1), jr), eK);
         raw_load_k<NR, TT, FMT>(rK, n, j, ck);
       }
+      phase_priority(2 * (ord.cnt - it) - 1);
 #pragma unroll
       for (int i = 0; i < NR; ++i)
 #pragma unroll
@@ -855,6 +893,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   }
   if (flags) atomicOr(&a.B.counters->status, flags);
   write_partial<NR>(a, si, h, split, m, l, acc);
+  if (a.k_new != nullptr && split == 0) store_new_token<FMT>(a, si, seq, z.w, h);
 }
 
 // Log-sum-exp merge of the splits, with the tail.  The split kernels cover the finished blocks;
@@ -1090,16 +1129,17 @@ int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& S, 
   AttnArgs a;
   a.k_new = reinterpret_cast<const uint8_t*>(k_new);
   a.v_new = reinterpret_cast<const uint8_t*>(v_new);
-  for (int i = 0; i < kMaxSeqsPerLaunch; ++i) {
-    a.new_pos[i] = (k_new && i < S.n) ? new_pos[i] : 0;
-    a.order[i] = i;
-  }
   // longest first (stable): with the same split count for every sequence, a long sequence's
   // workgroups carry the most blocks, and dispatching them first shortens the kernel's tail
-  std::stable_sort(a.order, a.order + S.n, [&](int x, int y) { return S.lens[x] > S.lens[y]; });
+  int order[kMaxSeqsPerLaunch];
+  for (int i = 0; i < S.n; ++i) order[i] = i;
+  std::stable_sort(order, order + S.n, [&](int x, int y) { return S.lens[x] > S.lens[y]; });
+  for (int z = 0; z < kMaxSeqsPerLaunch; ++z) {
+    const int i = z < S.n ? order[z] : 0;
+    a.zrow[z] = z < S.n ? make_int4(i, S.ids[i], S.lens[i], k_new ? new_pos[i] : 0) : make_int4(0, 0, 0, 0);
+  }
   a.G = G;
   a.B = B;
-  a.S = S;
   a.q = q;
   a.ws_acc = ws_acc;
   a.ws_ml = ws_ml;
