@@ -154,6 +154,39 @@ def test_raw_fallback_tiles_in_attention():
     assert row_rel_err(host(out), _oracle(cfg, toks, q)) <= TOL
 
 
+@pytest.mark.parametrize("cfg_i,T", [(0, 16), (0, 64), (1, 64)])
+def test_compressed_and_uncompressed_caches_give_the_same_bits(cfg_i, T):
+    """Lossless end to end (GAAC page, §3.1 and §3.2): the compressed kernel rebuilds every
+    stored value exactly and runs the same per-split sequence of MFMA contractions and softmax
+    updates as the uncompressed kernel (the two differ only in the order of tokens inside an
+    MFMA's k dimension, which does not change its result), so caches of the same tokens give
+    bit-identical outputs whatever each tile's form: all tiles compressed, many tiles raw (a
+    small escape capacity), or every tile raw (the uncompressed cache).  Tails of 0, 1 and
+    T - 1 tokens; split counts 1 to 256."""
+    cfg = synth.config(cfg_i)
+    g, toks = synth.sequence_tokens(cfg)
+    k, v = toks[0]
+    raw_seen = 0
+    for L in (T - 1, 4 * T, 4 * T + 1, 1000, 4097):
+        kk, vv = k[:L], v[:L]
+        q = dev(synth.queries(cfg, step=L))
+        outs = []
+        for compressed, esc_cap in ((True, -1), (True, 16), (False, -1)):
+            cache = new_cache(Hkv=cfg.Hkv, Hq=cfg.Hq, D=cfg.D, T=T, max_seqs=1, max_blocks=L // T + 2,
+                              compressed=compressed, esc_cap=esc_cap)
+            cache.calibrate(dev(k[:cfg.n_cal]), dev(v[:cfg.n_cal]))
+            cache.append([0], dev(kk[None]), dev(vv[None]))
+            if compressed and esc_cap == 16:
+                raw_seen += cache.status()[1]["raw_tiles"]
+            outs.append([host(cache.attention([0], q, cfg.scale, S)) for S in (1, 3, 16, 256)])
+        ref = _oracle(cfg, [(kk, vv)], synth.queries(cfg, step=L))
+        assert row_rel_err(outs[2][0], ref) <= TOL, L
+        for S_i in range(4):
+            assert np.array_equal(outs[0][S_i], outs[2][S_i]), (L, S_i, "compressed")
+            assert np.array_equal(outs[1][S_i], outs[2][S_i]), (L, S_i, "raw fallbacks")
+    assert raw_seen > 0
+
+
 def test_paged_mix_t16_permuted_pool():
     """Several sequences of mixed length, T=16 blocks scattered over a permuted slot pool,
     batched attention (the serving-mix geometry at reduced lengths)."""

@@ -152,3 +152,32 @@ def test_fp8_decode_step_equals_append_then_attention(fmt):
     q = synth.queries(cfg, step=77)
     ref = _oracle(cfg, [(k[:L0 + 40], v[:L0 + 40])], q)
     assert row_rel_err(host(caches[0].attention([0], dev(q), cfg.scale, 4)), ref) <= TOL
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T", [16, 64])
+def test_fp8_compressed_and_uncompressed_caches_give_the_same_bits(fmt, T):
+    """Lossless end to end for FP8 caches (GAAC page App. B with §3.2): compressed tiles, raw
+    fallback tiles (a small escape capacity) and an uncompressed cache of the same tokens give
+    bit-identical outputs; split counts 1 to 256."""
+    cfg = _cfg0(fmt)
+    g, toks = synth.sequence_tokens(cfg)
+    k, v = toks[0]
+    raw_seen = 0
+    for L in (T - 1, 4 * T + 1, 1000):
+        kk, vv = k[:L], v[:L]
+        q = dev(synth.queries(cfg, step=L))
+        outs = []
+        for compressed, esc_cap in ((True, -1), (True, 16), (False, -1)):
+            cache = new_cache(Hkv=cfg.Hkv, Hq=cfg.Hq, D=cfg.D, T=T, max_seqs=1, max_blocks=L // T + 2,
+                              compressed=compressed, esc_cap=esc_cap, fmt=fmt)
+            cache.calibrate(dev(k[:cfg.n_cal], fmt), dev(v[:cfg.n_cal], fmt))
+            cache.append([0], dev(kk[None], fmt), dev(vv[None], fmt))
+            if compressed and esc_cap == 16:
+                raw_seen += cache.status()[1]["raw_tiles"]
+            outs.append([host(cache.attention([0], q, cfg.scale, S)) for S in (1, 3, 16, 256)])
+        assert row_rel_err(outs[2][0], _oracle(cfg, [(kk, vv)], synth.queries(cfg, step=L))) <= TOL, L
+        for S_i in range(4):
+            assert np.array_equal(outs[0][S_i], outs[2][S_i]), (L, S_i, "compressed")
+            assert np.array_equal(outs[1][S_i], outs[2][S_i]), (L, S_i, "raw fallbacks")
+    assert raw_seen > 0
