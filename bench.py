@@ -332,7 +332,7 @@ def main():
     if "paged" in extras:
         result["paged_mix"] = extra_steps(torch, K, synth, synth.config(3), args, splits=args.paged_splits, layers=2)
     if "groups" in extras:
-        result["codec_groups_64k"] = codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream)
+        result["codec_groups_64k"] = codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, q, args.splits)
     if "rope" in extras:
         result["rope_drift_64k"] = rope_drift(torch, K, synth, cfg, k0, v0, dev)
     if "serving" in extras:
@@ -342,12 +342,15 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, reps=5):
+def codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, q, n_splits, reps=5):
     """The 64K layer's codec with 16- and 8-token exponent groups (GAAC page §3.1 groups eight
     values): codec ratio, mode shares and escape bytes per tile; one bulk append encoding all
-    blocks; decoding every block back to BF16 (kv_decode_blocks) and a single block.  Encoders:
-    16-token groups the register-packing kernel, 8-token groups the bit-assembling one; decoders:
-    16-token groups the four-token SWAR kernel, 8-token groups the element-wise one."""
+    blocks; decoding every block back to BF16 (kv_decode_blocks) and a single block; decode
+    attention over the layer (kv_attention_partials, back to back on the one layer, so its
+    bytes sit in the last-level cache: "hot").  Encoders: 16-token groups the register-packing
+    kernel, 8-token groups the bit-assembling one; decoders: 16-token groups the four-token SWAR
+    kernel, 8-token groups the element-wise one; attention: 16-token groups the register-rebuild
+    split kernel, 8-token groups the LDS-rebuild one."""
     T, D, Hkv, Hq = cfg.T, cfg.D, cfg.Hkv, cfg.Hq
     L0 = kd.shape[1]
     nb = L0 // T
@@ -380,6 +383,10 @@ def codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, reps=5):
             dec_one.append(ev_us(lambda: c.decode_blocks(0, nb // 2, 1, (k1, v1))))
         if not (torch.equal(kout, kd[0, :nb * T]) and torch.equal(vout, vd[0, :nb * T])):
             raise RuntimeError(f"decode_blocks with {Gt}-token groups did not rebuild the layer bit for bit")
+        ws = c.workspace(1, n_splits)
+        for _ in range(3):
+            c.attention_partials([0], q, cfg.scale, n_splits, ws)
+        attn = ev_us(lambda: [c.attention_partials([0], q, cfg.scale, n_splits, ws) for _ in range(20)]) / 20
         flags, st = c.status()
         if flags:
             raise RuntimeError(f"cache status flags {flags}")
@@ -398,6 +405,7 @@ def codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, reps=5):
             "decode_all_blocks_us": round(float(np.median(dec_all)), 1),
             "decode_one_block_us": round(float(np.median(dec_one)), 1),
             "decode_GBps_out": round(tiles * TD * 2 / (float(np.median(dec_all)) * 1e-6) / 1e9, 1),
+            "attention_hot_us": round(attn, 1),
         }
         del c
     log(f"[bench] codec groups: {res}")

@@ -297,9 +297,7 @@ size_t kv_attention_workspace_bytes(const kvc_params* p, int32_t n_seqs, int32_t
 }
 
 // Shared argument checks of the attention calls.
-static int check_group_tokens_for_attention(const kvc_cache* c) {
-  if (c->G.compressed && c->G.GT != kvc::kGroup)
-    return fail(KVC_EUNSUPPORTED, "the attention kernels rebuild 16-token groups; this cache uses 8-token groups");
+static int check_attention_head_dim(const kvc_cache* c) {
   if (c->p.head_dim == 256)
     return fail(KVC_EUNSUPPORTED, "the attention kernels take head_dim 64 or 128; 256-channel heads are stored only");
   return KVC_OK;
@@ -308,7 +306,7 @@ static int check_group_tokens_for_attention(const kvc_cache* c) {
 static int check_attention_args(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
                                 int32_t n_splits, const void* ws_dev, size_t ws_bytes) {
   if (!c) return fail(KVC_EINVAL, "cache is NULL");
-  int rc = check_group_tokens_for_attention(c);
+  int rc = check_attention_head_dim(c);
   if (rc != KVC_OK) return rc;
   rc = check_seq_ids(c, seq_ids_host, n_seqs);
   if (rc != KVC_OK) return rc;
@@ -347,12 +345,13 @@ static int run_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seq
       S.lens[i] = c->len[S.ids[i]] / G.T * G.T;  // the finished blocks; the merge adds the tail
       new_pos[i] = c->len[S.ids[i]] % G.T - 1;   // a decode step's token: the tail's last position
     }
-    rc = hip_fail(kvc::launch_attention_partials(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale,
-                                                 n_splits, acc + (size_t)s0 * G.Hq * n_splits * G.D,
-                                                 ml + (size_t)s0 * G.Hq * n_splits * 2,
-                                                 k_new_dev ? (const uint8_t*)k_new_dev + (size_t)s0 * row : nullptr,
-                                                 v_new_dev ? (const uint8_t*)v_new_dev + (size_t)s0 * row : nullptr,
-                                                 new_pos, stream),
+    // compressed caches with 8-token groups take the LDS-rebuild kernel; everything else the
+    // register-rebuild split kernels
+    auto launch = (G.compressed && G.GT != kvc::kGroup) ? kvc::launch_attention_any : kvc::launch_attention_partials;
+    rc = hip_fail(launch(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale, n_splits,
+                         acc + (size_t)s0 * G.Hq * n_splits * G.D, ml + (size_t)s0 * G.Hq * n_splits * 2,
+                         k_new_dev ? (const uint8_t*)k_new_dev + (size_t)s0 * row : nullptr,
+                         v_new_dev ? (const uint8_t*)v_new_dev + (size_t)s0 * row : nullptr, new_pos, stream),
                   "launch attention");
     if (rc != KVC_OK) return rc;
   }
@@ -403,7 +402,7 @@ int kv_decode_step(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, co
                    const void* v_new_dev, const void* q_dev, float scale, int32_t n_splits, void* ws_dev, size_t ws_bytes,
                    void* out_dev, void* stream) {
   if (!c) return fail(KVC_EINVAL, "cache is NULL");
-  int rc = check_group_tokens_for_attention(c);  // before the append changes anything
+  int rc = check_attention_head_dim(c);  // before the append changes anything
   if (rc != KVC_OK) return rc;
   rc = check_seq_ids(c, seq_ids_host, n_seqs);
   if (rc != KVC_OK) return rc;

@@ -622,10 +622,12 @@ __global__ void release_kernel(Geo G, DevBufs B, int seq, int n_blocks) {
 
 // Any format and group size, one element at a time: every group's mode and first escape unit go
 // to LDS (a block scan of the unit counts), then each thread rebuilds elements from their 3-bit
-// code, escape bits and sign/mantissa field.  (BF16 tiles with 16-token groups take the SWAR
-// path below.)
+// code, escape bits and sign/mantissa field and hands element (t, c) to put(t, c, bits).  (BF16
+// tiles with 16-token groups take the SWAR path below.)  The caller synchronises before the
+// next call or before reading what put wrote to LDS.
+template <class Put>
 __device__ void decode_tile_any(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
-                                const uint8_t* b4, void* out, int bi, int h) {
+                                const uint8_t* b4, Put put) {
   __shared__ uint16_t gP[1024];
   __shared__ uint8_t gm[1024];
   __shared__ int red[8];
@@ -677,7 +679,7 @@ __device__ void decode_tile_any(const Geo& G, const DevBufs& B, const uint8_t* t
     if (base + o >= (1u << G.F)) atomicOr(&B.counters->status, 8u);  // corrupt offset
     const uint32_t e = (base + o) & ((1u << G.F) - 1u);
     const uint32_t x = ((f >> G.MB) << (G.F + G.MB)) | (e << G.MB) | (f & ((1u << G.MB) - 1u));
-    elem_put(out, (((size_t)bi * T + t) * G.Hkv + h) * D + c, G.EB, x);
+    put(t, c, x);
   }
 }
 
@@ -724,9 +726,11 @@ __device__ __forceinline__ uint32_t code_slot_rt(uint32_t W0, uint32_t W1, uint3
 // per CODE unit (32 elements = channels c0..c0+3 x tokens 8tg..8tg+7, one group per channel).
 // Escape units are single bytes (an 8-bit plane per escaped group; a raw group adds four bytes
 // of offset bits 4..7, token tau's nibble at bits 4*tau).
+// put4(t, c0, w) receives BF16 channels c0..c0+3 of token t (w.x: c0, c0+1; w.y: c0+2, c0+3).
+template <class Put4>
 __device__ void decode_bf16_g8_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
-                                    const uint8_t* b4, uint16_t* out, int bi, int h, TileMeta& m) {
-  const int D = G.D, T = G.T;
+                                    const uint8_t* b4, TileMeta& m, Put4 put4) {
+  const int D = G.D;
   stage_tile_meta(G, tile, m);
   const uint8_t* esc = reinterpret_cast<const uint8_t*>(m.esc);
   const int n_units = G.raw_elems / 32;
@@ -774,8 +778,7 @@ __device__ void decode_bf16_g8_tile(const Geo& G, const DevBufs& B, const uint8_
         const uint32_t sel = (k >> 1) ? 0x07060302u : 0x05040100u;  // tokens 4qq+{0,1}: low halves
         const uint32_t w01 = (k & 1) ? perm_b32(o13[1][qq], o13[0][qq], sel) : perm_b32(o02[1][qq], o02[0][qq], sel);
         const uint32_t w23 = (k & 1) ? perm_b32(o13[3][qq], o13[2][qq], sel) : perm_b32(o02[3][qq], o02[2][qq], sel);
-        const int t = 8 * tg + 4 * qq + k;
-        *reinterpret_cast<uint2*>(out + (((size_t)bi * T + t) * G.Hkv + h) * D + c0) = make_uint2(w01, w23);
+        put4(8 * tg + 4 * qq + k, c0, make_uint2(w01, w23));
       }
   }
 }
@@ -805,14 +808,16 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
   const uint8_t* tile = B.comp_pool + (size_t)slot * G.stride;
   __shared__ TileMeta meta;
   if (G.EB == 2 && G.GT == 8) {
+    uint16_t* o16 = reinterpret_cast<uint16_t*>(outv);
     decode_bf16_g8_tile(G, B, tile, B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
-                        B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, reinterpret_cast<uint16_t*>(outv), bi, h,
-                        meta);
+                        B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, meta,
+                        [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(o16 + out_idx(t, c0)) = w; });
     return;
   }
   if (G.EB == 1 || G.GT != kGroup) {
     decode_tile_any(G, B, tile, B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
-                    B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, outv, bi, h);
+                    B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D,
+                    [&](int t, int c, uint32_t x) { elem_put(outv, out_idx(t, c), G.EB, x); });
     return;
   }
   uint16_t* out = reinterpret_cast<uint16_t*>(outv);
@@ -861,6 +866,183 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
   }
 }
 
+
+// ------------------------------------------------------------------------------------------
+// Decode attention over compressed caches with 8-token groups (the split kernels of the
+// attention library rebuild 16-token groups only).  Method as there (GAAC page §3.2): each
+// workgroup covers a contiguous range of finished blocks of one (sequence, KV head), rebuilds
+// every block's K and V tile on chip, into LDS (the cache is never decompressed to HBM), and
+// keeps an fp32 online softmax for each query head of the GQA group; the partial results (acc,
+// and max and sum in base-2 units) go to the same workspace, for the same merge kernel.  Scores
+// and PV are fp32 multiply-adds over LDS: this path is correct for every format and block size,
+// not tuned.
+struct AnyAttnArgs {
+  Geo G;
+  DevBufs B;
+  const uint16_t* q;
+  float* ws_acc;
+  float* ws_ml;
+  float sl2;  // scale * log2(e)
+  int n_splits;
+  const uint8_t* k_new;  // decode step: the new tokens, [n][Hkv][D] elements (else null)
+  const uint8_t* v_new;
+  int4 zrow[kMaxSeqsPerLaunch];  // blockIdx.z -> {sequence index, sequence id, tokens in finished
+                                 // blocks, tail position of the new token}
+};
+
+constexpr int kAnyMaxG = 16;   // query heads per KV head
+constexpr int kAnyMaxTD = 64 * 128;
+
+// Element bits -> value, exactly: FMT 0 BF16, 1 OCP E5M2, 2 OCP E4M3 (FN).
+template <int FMT>
+__device__ __forceinline__ float elem_value(uint32_t x) {
+  if constexpr (FMT == 0) {
+    return __uint_as_float(x << 16);
+  } else {
+    constexpr int F = FMT == 1 ? 5 : 4, MB = 7 - F, bias = FMT == 1 ? 15 : 7;
+    const uint32_t e = (x >> MB) & ((1u << F) - 1u), m = x & ((1u << MB) - 1u);
+    float v;
+    if (FMT == 1 && e == 31) v = m ? __uint_as_float(0x7FC00000u) : __uint_as_float(0x7F800000u);
+    else if (FMT == 2 && e == 15 && m == 7) v = __uint_as_float(0x7FC00000u);
+    else if (e == 0) v = ldexpf((float)m, 1 - bias - MB);
+    else v = ldexpf((float)((1u << MB) | m), (int)e - bias - MB);
+    return (x >> 7) ? -v : v;
+  }
+}
+
+// Sum / maximum over aligned segments of W lanes (W = 16, 32 or 64 divides the wave).
+__device__ __forceinline__ float seg_sum(float v, int W) {
+  for (int o = 1; o < W; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float seg_max(float v, int W) {
+  for (int o = 1; o < W; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
+  const Geo& G = a.G;
+  const int D = G.D, T = G.T, g = G.g, S = a.n_splits, tid = threadIdx.x;
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int4 z = a.zrow[blockIdx.z];
+  const int si = z.x, seq = z.y, L = z.z;
+  __shared__ __align__(16) uint16_t kvt[2][kAnyMaxTD];  // the block's K and V as element bits, [t][c]
+  __shared__ float qf[kAnyMaxG * 128];    // query heads h*g .. h*g+g-1
+  __shared__ float pr[kAnyMaxG * 64];     // scores, then probabilities, [head][t]
+  __shared__ float mh[kAnyMaxG], lh[kAnyMaxG], al[kAnyMaxG];
+  __shared__ TileMeta meta;
+  // blocks [b0, b1): the finished blocks dealt out as evenly as possible
+  const int nb = L / T, per = nb / S, rem = nb % S;
+  const int b0 = split * per + min(split, rem), b1 = b0 + per + (split < rem ? 1 : 0);
+  for (int i = tid; i < g * D; i += kThreads)
+    qf[i] = __uint_as_float((uint32_t)a.q[((size_t)si * G.Hq + h * g) * D + i] << 16);
+  if (tid < g) {
+    mh[tid] = -INFINITY;
+    lh[tid] = 0.0f;
+  }
+  constexpr int OPT = kAnyMaxG * 128 / kThreads;  // outputs (head, channel) per thread
+  float acc[OPT];
+#pragma unroll
+  for (int u = 0; u < OPT; ++u) acc[u] = 0.0f;
+  uint32_t flags = 0;
+  __syncthreads();
+  for (int b = b0; b < b1; ++b) {
+    for (int kv = 0; kv < 2; ++kv) {
+      uint16_t* dst = kvt[kv];
+      const uint32_t e = a.B.table[table_index(G, seq, b, kv, h)];
+      const uint32_t slot = e & 0x00FFFFFFu;
+      if (e == kUnallocated) {  // missing: zeros, reported
+        for (int i = tid; i < T * D; i += kThreads) dst[i] = 0;
+        flags |= 4u;
+      } else if (e & 0x80000000u) {  // raw tile: K [t][c], V [c][t]
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
+        for (int i = tid; i < T * D; i += kThreads) {
+          const int t = i / D, c = i % D;
+          dst[i] = (uint16_t)elem_at(src, kv ? (size_t)c * T + t : (size_t)i, G.EB);
+        }
+      } else {
+        const uint8_t* tile = a.B.comp_pool + (size_t)slot * G.stride;
+        const uint8_t* b3 = a.B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
+        const uint8_t* b4 = a.B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;
+        if (G.EB == 2 && G.GT == 8)
+          decode_bf16_g8_tile(G, a.B, tile, b3, b4, meta,
+                              [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(dst + t * D + c0) = w; });
+        else
+          decode_tile_any(G, a.B, tile, b3, b4, [&](int t, int c, uint32_t x) { dst[t * D + c] = (uint16_t)x; });
+      }
+      __syncthreads();
+    }
+    // scores and the online softmax: one (head, token) pair per thread and pass, so a head's T
+    // tokens sit in an aligned segment of T lanes of one wave (T divides 64).  Each thread walks
+    // the channels from its own offset, so the threads of a wave read different LDS banks.
+    for (int p0 = 0; p0 < g * T; p0 += kThreads) {
+      const int p = p0 + tid;
+      const bool on = p < g * T;  // whole segments are on or off together
+      const int hh = on ? p / T : 0, t = p % T;
+      float d = 0.0f;
+      if (on) {
+        const uint16_t* kr = kvt[0] + t * D;
+        const float* qr = qf + hh * D;
+        for (int cc = 0; cc < D; cc += 2) {
+          const int c = (cc + 2 * t) & (D - 1);
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(kr + c);
+          d += elem_value<FMT>(w & 0xFFFFu) * qr[c] + elem_value<FMT>(w >> 16) * qr[c + 1];
+        }
+      }
+      const float sc = d * a.sl2;
+      const float m_old = on ? mh[hh] : 0.0f;
+      const float m_new = fmaxf(m_old, seg_max(sc, T));
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float pv = exp2f(sc - m_use);
+      const float sum = seg_sum(pv, T);
+      if (on) {
+        pr[hh * 64 + t] = pv;
+        if (t == 0) {
+          const float alpha = exp2f(m_old - m_use);
+          lh[hh] = lh[hh] * alpha + sum;
+          mh[hh] = m_new;
+          al[hh] = alpha;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int o = tid + kThreads * u;
+      if (o < g * D) {
+        const int hh = o / D, c = o % D;
+        float s = acc[u] * al[hh];
+        for (int t = 0; t < T; ++t) s += pr[hh * 64 + t] * elem_value<FMT>(kvt[1][t * D + c]);
+        acc[u] = s;
+      }
+    }
+    __syncthreads();  // before the next block overwrites the tiles and the probabilities
+  }
+#pragma unroll
+  for (int u = 0; u < OPT; ++u) {
+    const int o = tid + kThreads * u;
+    if (o < g * D) a.ws_acc[(((size_t)si * G.Hq + h * g + o / D) * S + split) * D + o % D] = acc[u];
+  }
+  if (tid < g) {
+    float* ml = a.ws_ml + (((size_t)si * G.Hq + h * g + tid) * S + split) * 2;
+    ml[0] = mh[tid];
+    ml[1] = lh[tid];
+  }
+  if (flags && tid == 0) atomicOr(&a.B.counters->status, flags);
+  // decode step: the first split stores the sequence's new token into the tail (K row t, V
+  // column t); the merge kernel that follows reads it there
+  if (a.k_new != nullptr && split == 0) {
+    const int t = z.w;
+    void* tail = a.B.tail;
+    const size_t ko = tail_offset(G, seq, 0, h), vo = tail_offset(G, seq, 1, h);
+    const size_t src = ((size_t)si * G.Hkv + h) * D;
+    for (int c = tid; c < D; c += kThreads) {
+      elem_put(tail, ko + (size_t)t * D + c, G.EB, elem_at(a.k_new, src + c, G.EB));
+      elem_put(tail, vo + (size_t)c * T + t, G.EB, elem_at(a.v_new, src + c, G.EB));
+    }
+  }
+}
 }  // namespace
 
 int launch_init(const Geo& G, const DevBufs& B, const int32_t*, const int32_t*, void* stream) {
@@ -903,6 +1085,28 @@ int launch_decode_blocks(const Geo& G, const DevBufs& B, int seq, int first, int
   if (n <= 0) return 0;
   hipLaunchKernelGGL(decode_blocks_kernel, dim3(n, 2 * G.Hkv), dim3(kThreads), 0, (hipStream_t)stream, G, B, seq,
                      first, k_out, v_out);
+  return (int)hipGetLastError();
+}
+
+int launch_attention_any(const Geo& G, const DevBufs& B, const SeqList& S, const uint16_t* q, float scale,
+                         int n_splits, float* ws_acc, float* ws_ml, const void* k_new, const void* v_new,
+                         const int* new_pos, void* stream) {
+  // shapes the LDS arrays hold: T <= 64 tokens, D <= 128 channels (a power of two), g <= 16
+  if (G.T > 64 || G.D > 128 || G.g > kAnyMaxG || (G.D & (G.D - 1))) return (int)hipErrorInvalidValue;
+  AnyAttnArgs a;
+  a.G = G;
+  a.B = B;
+  a.q = q;
+  a.ws_acc = ws_acc;
+  a.ws_ml = ws_ml;
+  a.sl2 = scale * 1.4426950408889634f;
+  a.n_splits = n_splits;
+  a.k_new = reinterpret_cast<const uint8_t*>(k_new);
+  a.v_new = reinterpret_cast<const uint8_t*>(v_new);
+  for (int z = 0; z < kMaxSeqsPerLaunch; ++z)
+    a.zrow[z] = z < S.n ? make_int4(z, S.ids[z], S.lens[z], k_new ? new_pos[z] : 0) : make_int4(0, 0, 0, 0);
+  auto k = G.fmt == 0 ? attn_any_kernel<0> : G.fmt == 1 ? attn_any_kernel<1> : attn_any_kernel<2>;
+  hipLaunchKernelGGL(k, dim3(n_splits, G.Hkv, S.n), dim3(kThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

@@ -72,10 +72,10 @@ typedef struct {
   int32_t block_tokens;       /* T: tokens per block/tile, multiple of 16, 16..256           */
   int32_t group_tokens;       /* G: tokens per exponent group, 16 or 8 in this build (GAAC
                                  page §3.1 groups the exponents of a few tokens of one
-                                 channel).  G = 8 caches encode, decode (kv_decode_blocks) and
-                                 report statistics; decode attention over a compressed G = 8
-                                 cache returns KVC_EUNSUPPORTED (the attention kernels rebuild
-                                 16-token groups)                                            */
+                                 channel).  Decode attention over a compressed G = 16 cache
+                                 rebuilds tiles in registers (the tuned path); over a
+                                 compressed G = 8 cache it rebuilds each block's tiles into
+                                 LDS (correct for every format, not tuned)                   */
   int32_t esc_cap_bytes;      /* escape capacity per tile, multiple of 16, <= 2032;
                                  < 0 selects T*D/16                                          */
   int32_t compressed;         /* 1: blocks are encoded; 0: every block is stored raw (the
@@ -167,11 +167,11 @@ size_t kv_attention_workspace_bytes(const kvc_params* params, int32_t n_seqs, in
  * query head hq reading KV head hq / (Hq / Hkv).  q_dev: [n_seqs][Hq][D] BF16; out_dev:
  * [n_seqs][Hq][D] BF16 (round-to-nearest-even of an fp32 result); q, out and the workspace
  * 16-byte aligned (KVC_EINVAL otherwise).  The finished blocks of each
- * sequence are split into n_splits contiguous ranges of 64 tokens processed in parallel
- * (1 <= n_splits <= 1024); their partial results and the tail are merged by log-sum-exp.
- * Every listed sequence must hold at least one token (KVC_EINVAL otherwise).  A compressed
- * cache with 8-token groups returns KVC_EUNSUPPORTED (also from the split halves and from
- * kv_decode_step, before anything runs). */
+ * sequence are split into n_splits contiguous ranges (of 64-token super-blocks; of blocks for
+ * a compressed cache with 8-token groups) processed in parallel (1 <= n_splits <= 1024); their
+ * partial results and the tail are merged by log-sum-exp.  Every listed sequence must hold at
+ * least one token (KVC_EINVAL otherwise).  head_dim 256 returns KVC_EUNSUPPORTED (also from
+ * the split halves and from kv_decode_step, before anything runs). */
 int kv_decode_attention(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
                         float scale, int32_t n_splits, void* ws_dev, size_t ws_bytes, void* out_dev, void* stream);
 
