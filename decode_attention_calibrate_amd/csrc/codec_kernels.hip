@@ -692,13 +692,18 @@ struct TileMeta {
   uint32_t pre[kMaxTagWords];
   uint32_t esc[512 / 4];           // esc_cap <= 512
 };
-__device__ void stage_tile_meta(const Geo& G, const uint8_t* tile, TileMeta& m) {
+// tl / nt: this thread's index among the nt threads staging the tile (the whole block, or one
+// half of it when two tiles are staged at once); every thread of the block reaches the
+// barriers, `active` false for threads with no tile to stage.
+__device__ void stage_tile_meta(const Geo& G, const uint8_t* tile, TileMeta& m, int tl, int nt, bool active) {
   const uint32_t* tag_g = reinterpret_cast<const uint32_t*>(tile + G.tag_off);
   const uint32_t* esc_g = reinterpret_cast<const uint32_t*>(tile + G.esc_off);
-  for (int i = threadIdx.x; i < 2 * G.PW; i += blockDim.x) m.tag[i] = tag_g[i];
-  for (int i = threadIdx.x; i < G.esc_cap / 4; i += blockDim.x) m.esc[i] = esc_g[i];
+  if (active) {
+    for (int i = tl; i < 2 * G.PW; i += nt) m.tag[i] = tag_g[i];
+    for (int i = tl; i < G.esc_cap / 4; i += nt) m.esc[i] = esc_g[i];
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (active && tl == 0) {
     uint32_t acc = 0;
     for (int i = 0; i < G.PW; ++i) {
       m.pre[i] = acc;
@@ -727,14 +732,15 @@ __device__ __forceinline__ uint32_t code_slot_rt(uint32_t W0, uint32_t W1, uint3
 // Escape units are single bytes (an 8-bit plane per escaped group; a raw group adds four bytes
 // of offset bits 4..7, token tau's nibble at bits 4*tau).
 // put4(t, c0, w) receives BF16 channels c0..c0+3 of token t (w.x: c0, c0+1; w.y: c0+2, c0+3).
+// tl, nt, active: as stage_tile_meta (every thread of the block calls it).
 template <class Put4>
 __device__ void decode_bf16_g8_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
-                                    const uint8_t* b4, TileMeta& m, Put4 put4) {
+                                    const uint8_t* b4, TileMeta& m, Put4 put4, int tl, int nt, bool active) {
   const int D = G.D;
-  stage_tile_meta(G, tile, m);
+  stage_tile_meta(G, tile, m, tl, nt, active);
   const uint8_t* esc = reinterpret_cast<const uint8_t*>(m.esc);
-  const int n_units = G.raw_elems / 32;
-  for (int u = threadIdx.x; u < n_units; u += blockDim.x) {
+  const int n_units = active ? G.raw_elems / 32 : 0;
+  for (int u = tl; u < n_units; u += nt) {
     const int q0 = 4 * u, w = q0 >> 5, bit = q0 & 31, tg = q0 / D, c0 = q0 % D;
     uint32_t P = m.pre[w];  // escape bytes before group q0
     const uint32_t Ew = m.tag[w], Rw = m.tag[G.PW + w];
@@ -811,7 +817,8 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
     uint16_t* o16 = reinterpret_cast<uint16_t*>(outv);
     decode_bf16_g8_tile(G, B, tile, B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
                         B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, meta,
-                        [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(o16 + out_idx(t, c0)) = w; });
+                        [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(o16 + out_idx(t, c0)) = w; },
+                        tid, kThreads, true);
     return;
   }
   if (G.EB == 1 || G.GT != kGroup) {
@@ -822,7 +829,7 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
   }
   uint16_t* out = reinterpret_cast<uint16_t*>(outv);
   auto out_at = [&](int t, int c) -> uint16_t* { return out + out_idx(t, c); };
-  stage_tile_meta(G, tile, meta);
+  stage_tile_meta(G, tile, meta, tid, kThreads, true);
   const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(meta.esc);
   const uint8_t* b3 = B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
   const uint8_t* b4 = B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;
@@ -931,7 +938,7 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
   __shared__ float qf[kAnyMaxG * 128];    // query heads h*g .. h*g+g-1
   __shared__ float pr[kAnyMaxG * 64];     // scores, then probabilities, [head][t]
   __shared__ float mh[kAnyMaxG], lh[kAnyMaxG], al[kAnyMaxG];
-  __shared__ TileMeta meta;
+  __shared__ TileMeta meta[2];
   // blocks [b0, b1): the finished blocks dealt out as evenly as possible
   const int nb = L / T, per = nb / S, rem = nb % S;
   const int b0 = split * per + min(split, rem), b1 = b0 + per + (split < rem ? 1 : 0);
@@ -947,32 +954,58 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
   for (int u = 0; u < OPT; ++u) acc[u] = 0.0f;
   uint32_t flags = 0;
   __syncthreads();
+  auto entry = [&](int b, int kv) -> uint32_t { return a.B.table[table_index(G, seq, b, kv, h)]; };
+  uint32_t eK = b0 < b1 ? entry(b0, 0) : kUnallocated, eV = b0 < b1 ? entry(b0, 1) : kUnallocated;
   for (int b = b0; b < b1; ++b) {
-    for (int kv = 0; kv < 2; ++kv) {
-      uint16_t* dst = kvt[kv];
-      const uint32_t e = a.B.table[table_index(G, seq, b, kv, h)];
-      const uint32_t slot = e & 0x00FFFFFFu;
-      if (e == kUnallocated) {  // missing: zeros, reported
-        for (int i = tid; i < T * D; i += kThreads) dst[i] = 0;
-        flags |= 4u;
-      } else if (e & 0x80000000u) {  // raw tile: K [t][c], V [c][t]
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
-        for (int i = tid; i < T * D; i += kThreads) {
-          const int t = i / D, c = i % D;
-          dst[i] = (uint16_t)elem_at(src, kv ? (size_t)c * T + t : (size_t)i, G.EB);
-        }
-      } else {
-        const uint8_t* tile = a.B.comp_pool + (size_t)slot * G.stride;
-        const uint8_t* b3 = a.B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
-        const uint8_t* b4 = a.B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;
-        if (G.EB == 2 && G.GT == 8)
-          decode_bf16_g8_tile(G, a.B, tile, b3, b4, meta,
-                              [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(dst + t * D + c0) = w; });
-        else
-          decode_tile_any(G, a.B, tile, b3, b4, [&](int t, int c, uint32_t x) { dst[t * D + c] = (uint16_t)x; });
-      }
-      __syncthreads();
+    // the next block's table entries load while this block is rebuilt
+    uint32_t nK = kUnallocated, nV = kUnallocated;
+    if (b + 1 < b1) {
+      nK = entry(b + 1, 0);
+      nV = entry(b + 1, 1);
     }
+    if constexpr (FMT == 0) {
+      // BF16, 8-token groups: the K tile by threads 0..127 and the V tile by 128..255 at once
+      const int kv = tid >> 7, tl = tid & 127;
+      const uint32_t e = kv ? eV : eK, slot = e & 0x00FFFFFFu;
+      const bool comp = e != kUnallocated && !(e & 0x80000000u);
+      uint16_t* dst = kvt[kv];
+      if (e == kUnallocated) {  // missing: zeros, reported
+        for (int i = tl; i < T * D; i += kThreads / 2) dst[i] = 0;
+        flags |= 4u;
+      } else if (!comp) {  // raw tile: K [t][c], V [c][t]
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems;
+        for (int i = tl; i < T * D; i += kThreads / 2) dst[i] = src[kv ? (size_t)(i % D) * T + i / D : (size_t)i];
+      }
+      const uint8_t* tile = a.B.comp_pool + (comp ? (size_t)slot * G.stride : 0);
+      decode_bf16_g8_tile(G, a.B, tile, a.B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
+                          a.B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, meta[kv],
+                          [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(dst + t * D + c0) = w; },
+                          tl, kThreads / 2, comp);
+      __syncthreads();
+    } else {
+      for (int kv = 0; kv < 2; ++kv) {
+        uint16_t* dst = kvt[kv];
+        const uint32_t e = kv ? eV : eK, slot = e & 0x00FFFFFFu;
+        if (e == kUnallocated) {  // missing: zeros, reported
+          for (int i = tid; i < T * D; i += kThreads) dst[i] = 0;
+          flags |= 4u;
+        } else if (e & 0x80000000u) {  // raw tile: K [t][c], V [c][t]
+          const uint8_t* src = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems;
+          for (int i = tid; i < T * D; i += kThreads) {
+            const int t = i / D, c = i % D;
+            dst[i] = src[kv ? (size_t)c * T + t : (size_t)i];
+          }
+        } else {
+          decode_tile_any(G, a.B, a.B.comp_pool + (size_t)slot * G.stride,
+                          a.B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
+                          a.B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D,
+                          [&](int t, int c, uint32_t x) { dst[t * D + c] = (uint16_t)x; });
+        }
+        __syncthreads();
+      }
+    }
+    eK = nK;
+    eV = nV;
     // scores and the online softmax: one (head, token) pair per thread and pass, so a head's T
     // tokens sit in an aligned segment of T lanes of one wave (T divides 64).  Each thread walks
     // the channels from its own offset, so the threads of a wave read different LDS banks.
@@ -1029,7 +1062,7 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
     ml[0] = mh[tid];
     ml[1] = lh[tid];
   }
-  if (flags && tid == 0) atomicOr(&a.B.counters->status, flags);
+  if (flags && (tid & (kThreads / 2 - 1)) == 0) atomicOr(&a.B.counters->status, flags);  // either half may see a gap
   // decode step: the first split stores the sequence's new token into the tail (K row t, V
   // column t); the merge kernel that follows reads it there
   if (a.k_new != nullptr && split == 0) {
