@@ -69,7 +69,8 @@ typedef struct {
                                  [..][2 Hkv][128], the same memory (a block takes 2 x 2 Hkv
                                  slots); calibration, encode, decode and statistics work on
                                  it, decode attention returns KVC_EUNSUPPORTED               */
-  int32_t block_tokens;       /* T: tokens per block/tile, multiple of 16, 16..256           */
+  int32_t block_tokens;       /* T: tokens per block/tile: a multiple of 16 is valid; this
+                                 build implements 16, 32 and 64 (others: KVC_EUNSUPPORTED)   */
   int32_t group_tokens;       /* G: tokens per exponent group, 16 or 8 in this build (GAAC
                                  page §3.1 groups the exponents of a few tokens of one
                                  channel).  Decode attention over a compressed G = 16 cache
