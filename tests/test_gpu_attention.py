@@ -187,6 +187,30 @@ def test_compressed_and_uncompressed_caches_give_the_same_bits(cfg_i, T):
     assert raw_seen > 0
 
 
+@pytest.mark.parametrize("cfg_i", [0, 1])
+@pytest.mark.parametrize("g", [1, 3, 8, 16])
+def test_gqa_group_sizes(cfg_i, g):
+    """Query heads per KV head from 1 (plain multi-head) to 16 (every column of the QK MFMA
+    used), D = 64 and 128, compressed and uncompressed caches, and the 8-token-group kernel;
+    against the oracle (query head hq reads KV head hq // g)."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.config(cfg_i), Hq=synth.config(cfg_i).Hkv * g)
+    g_, toks = synth.sequence_tokens(cfg)
+    k, v = toks[0]
+    L = 777
+    k, v = k[:L], v[:L]
+    q = synth.queries(cfg, step=L)
+    ref = oracle.attention(oracle.BF16, q[0], k, v, cfg.scale)
+    for compressed, Gt in ((True, 16), (False, 16), (True, 8)):
+        cache = new_cache(Hkv=cfg.Hkv, Hq=cfg.Hq, D=cfg.D, T=cfg.T, max_seqs=1, max_blocks=L // cfg.T + 2,
+                          compressed=compressed, Gt=Gt)
+        cache.calibrate(dev(k[:cfg.n_cal]), dev(v[:cfg.n_cal]))
+        cache.append([0], dev(k[None]), dev(v[None]))
+        for S in (1, 5):
+            out = host(cache.attention([0], dev(q), cfg.scale, S))
+            assert row_rel_err(out[0], ref) <= TOL, (compressed, Gt, S)
+
+
 def test_paged_mix_t16_permuted_pool():
     """Several sequences of mixed length, T=16 blocks scattered over a permuted slot pool,
     batched attention (the serving-mix geometry at reduced lengths)."""
