@@ -631,7 +631,7 @@ __device__ void decode_tile_any(const Geo& G, const DevBufs& B, const uint8_t* t
   __shared__ uint16_t gP[1024];
   __shared__ uint8_t gm[1024];
   __shared__ int red[8];
-  const int tid = threadIdx.x, D = G.D, T = G.T;
+  const int tid = threadIdx.x, D = G.D;
   const uint32_t* tagE = reinterpret_cast<const uint32_t*>(tile + G.tag_off);
   const uint32_t* tagR = tagE + G.PW;
   const int per = (G.NG + kThreads - 1) / kThreads, q0 = tid * per;
