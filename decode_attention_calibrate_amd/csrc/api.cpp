@@ -297,18 +297,10 @@ size_t kv_attention_workspace_bytes(const kvc_params* p, int32_t n_seqs, int32_t
 }
 
 // Shared argument checks of the attention calls.
-static int check_attention_head_dim(const kvc_cache* c) {
-  if (c->p.head_dim == 256)
-    return fail(KVC_EUNSUPPORTED, "the attention kernels take head_dim 64 or 128; 256-channel heads are stored only");
-  return KVC_OK;
-}
-
 static int check_attention_args(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
                                 int32_t n_splits, const void* ws_dev, size_t ws_bytes) {
   if (!c) return fail(KVC_EINVAL, "cache is NULL");
-  int rc = check_attention_head_dim(c);
-  if (rc != KVC_OK) return rc;
-  rc = check_seq_ids(c, seq_ids_host, n_seqs);
+  int rc = check_seq_ids(c, seq_ids_host, n_seqs);
   if (rc != KVC_OK) return rc;
   if (!q_dev || !ws_dev) return fail(KVC_EINVAL, "q and workspace must not be NULL");
   if (n_splits < 1 || n_splits > 1024) return fail(KVC_EINVAL, "n_splits must be in 1..1024");
@@ -334,6 +326,7 @@ static int run_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seq
   int rc = KVC_OK;
   const Geo& G = c->G;
   const size_t row = (size_t)G.Hkv * G.D * G.EB;  // bytes of one token of all KV heads
+  const size_t hq = c->p.num_q_heads;             // query heads (G.Hq counts half-heads)
   float* acc = (float*)ws_dev;
   float* ml = acc + (size_t)n_seqs * G.Hq * n_splits * G.D;
   for (int s0 = 0; s0 < n_seqs; s0 += kvc::kMaxSeqsPerLaunch) {
@@ -345,11 +338,21 @@ static int run_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seq
       S.lens[i] = c->len[S.ids[i]] / G.T * G.T;  // the finished blocks; the merge adds the tail
       new_pos[i] = c->len[S.ids[i]] % G.T - 1;   // a decode step's token: the tail's last position
     }
+    if (c->p.head_dim == 256) {  // half-head pairs; the kernel attends the tail too
+      int ntail[kvc::kMaxSeqsPerLaunch];
+      for (int i = 0; i < S.n; ++i) ntail[i] = c->len[S.ids[i]] % G.T;
+      rc = hip_fail(kvc::launch_attention_half(G, c->B, S, ntail, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale,
+                                               n_splits, acc + (size_t)s0 * G.Hq * n_splits * G.D,
+                                               ml + (size_t)s0 * hq * n_splits * 2, stream),
+                    "launch attention");
+      if (rc != KVC_OK) return rc;
+      continue;
+    }
     // compressed caches with 8-token groups take the LDS-rebuild kernel; everything else the
     // register-rebuild split kernels
     auto launch = (G.compressed && G.GT != kvc::kGroup) ? kvc::launch_attention_any : kvc::launch_attention_partials;
     rc = hip_fail(launch(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale, n_splits,
-                         acc + (size_t)s0 * G.Hq * n_splits * G.D, ml + (size_t)s0 * G.Hq * n_splits * 2,
+                         acc + (size_t)s0 * G.Hq * n_splits * G.D, ml + (size_t)s0 * hq * n_splits * 2,
                          k_new_dev ? (const uint8_t*)k_new_dev + (size_t)s0 * row : nullptr,
                          v_new_dev ? (const uint8_t*)v_new_dev + (size_t)s0 * row : nullptr, new_pos, stream),
                   "launch attention");
@@ -371,7 +374,15 @@ int kv_attention_combine(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_se
   if (rc != KVC_OK) return rc;
   rc = check_out(out_dev);
   if (rc != KVC_OK) return rc;
-  const Geo& G = c->G;
+  // 256-channel heads: the real head geometry, and no tail (the split kernel attended it)
+  const bool wide = c->p.head_dim == 256;
+  Geo G = c->G;
+  if (wide) {
+    G.D = 256;
+    G.Hkv = c->p.num_kv_heads;
+    G.Hq = c->p.num_q_heads;
+    G.raw_elems = G.T * G.D;
+  }
   const float* acc = (const float*)ws_dev;
   const float* ml = acc + (size_t)n_seqs * G.Hq * n_splits * G.D;
   for (int s0 = 0; s0 < n_seqs; s0 += kvc::kMaxSeqsPerLaunch) {
@@ -379,7 +390,7 @@ int kv_attention_combine(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_se
     S.n = std::min(kvc::kMaxSeqsPerLaunch, n_seqs - s0);
     for (int i = 0; i < S.n; ++i) {
       S.ids[i] = seq_ids_host[s0 + i];
-      S.lens[i] = c->len[S.ids[i]];
+      S.lens[i] = wide ? c->len[S.ids[i]] / G.T * G.T : c->len[S.ids[i]];
     }
     rc = hip_fail(kvc::launch_combine(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale, n_splits,
                                       acc + (size_t)s0 * G.Hq * n_splits * G.D, ml + (size_t)s0 * G.Hq * n_splits * 2,
@@ -402,9 +413,7 @@ int kv_decode_step(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, co
                    const void* v_new_dev, const void* q_dev, float scale, int32_t n_splits, void* ws_dev, size_t ws_bytes,
                    void* out_dev, void* stream) {
   if (!c) return fail(KVC_EINVAL, "cache is NULL");
-  int rc = check_attention_head_dim(c);  // before the append changes anything
-  if (rc != KVC_OK) return rc;
-  rc = check_seq_ids(c, seq_ids_host, n_seqs);
+  int rc = check_seq_ids(c, seq_ids_host, n_seqs);
   if (rc != KVC_OK) return rc;
   if (!k_new_dev || !v_new_dev) return fail(KVC_EINVAL, "k_new and v_new must not be NULL");
   rc = check_out(out_dev);
@@ -419,7 +428,9 @@ int kv_decode_step(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, co
   rc = check_attention_args(c, seq_ids_host, n_seqs, q_dev, n_splits, ws_dev, ws_bytes);
   for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] -= 1;
   if (rc != KVC_OK) return rc;
-  bool completes = false;  // does this token finish a block of some listed sequence?
+  // does this token finish a block of some listed sequence?  (256-channel heads: the kernel
+  // that attends them reads the tail itself, so the token is always appended first)
+  bool completes = c->p.head_dim == 256;
   for (int i = 0; i < n_seqs; ++i) completes |= (c->len[seq_ids_host[i]] + 1) % G.T == 0;
   if (completes) {  // the block must be encoded first: the append, then both attention halves
     rc = kv_encode_append(c, seq_ids_host, n_seqs, k_new_dev, v_new_dev, 1, stream);

@@ -1156,7 +1156,8 @@ int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& S, 
 template <int NR, int FMT>
 void (*pick_combine(int n_splits))(CombineArgs) {
   constexpr int D = 32 * NR;
-  if (n_splits <= 4 * (kCombineThreads / (D / 4))) return combine_kernel<NR, FMT, D, 4>;
+  if constexpr (D <= 128)  // one block per head (a 256-channel head always takes 16-channel slices)
+    if (n_splits <= 4 * (kCombineThreads / (D / 4))) return combine_kernel<NR, FMT, D, 4>;
   if (n_splits <= 4 * (kCombineThreads / 4)) return combine_kernel<NR, FMT, 16, 4>;
   return combine_kernel<NR, FMT, 16, 16>;
 }
@@ -1175,14 +1176,14 @@ int launch_combine(const Geo& G, const DevBufs& B, const SeqList& S, const uint1
   a.n_splits = n_splits;
   if (n_splits < 1 || n_splits > kMaxSplits || G.T > kTailTok || G.T < 4) return (int)hipErrorInvalidValue;
   void (*k)(CombineArgs) = nullptr;
-  const bool d128 = G.D == 128;
+  const bool d128 = G.D == 128, d256 = G.D == 256;
   switch (G.fmt) {
-    case 0: k = d128 ? pick_combine<4, 0>(n_splits) : pick_combine<2, 0>(n_splits); break;
-    case 1: k = d128 ? pick_combine<4, 1>(n_splits) : pick_combine<2, 1>(n_splits); break;
-    case 2: k = d128 ? pick_combine<4, 2>(n_splits) : pick_combine<2, 2>(n_splits); break;
+    case 0: k = d256 ? pick_combine<8, 0>(n_splits) : d128 ? pick_combine<4, 0>(n_splits) : pick_combine<2, 0>(n_splits); break;
+    case 1: k = d256 ? pick_combine<8, 1>(n_splits) : d128 ? pick_combine<4, 1>(n_splits) : pick_combine<2, 1>(n_splits); break;
+    case 2: k = d256 ? pick_combine<8, 2>(n_splits) : d128 ? pick_combine<4, 2>(n_splits) : pick_combine<2, 2>(n_splits); break;
     default: return (int)hipErrorInvalidValue;
   }
-  const int ch = n_splits <= 4 * (kCombineThreads / (G.D / 4)) ? G.D : 16;
+  const int ch = (G.D <= 128 && n_splits <= 4 * (kCombineThreads / (G.D / 4))) ? G.D : 16;
   hipLaunchKernelGGL(k, dim3(G.D / ch, G.Hq, S.n), dim3(kCombineThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }

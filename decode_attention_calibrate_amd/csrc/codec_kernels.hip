@@ -1076,6 +1076,153 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
     }
   }
 }
+// ------------------------------------------------------------------------------------------
+// Decode attention over 256-channel heads, stored as two 128-channel half-heads (GAAC page App.
+// D): a head's score needs both halves, so one workgroup takes both.  Per block: the two K
+// half-tiles are rebuilt into LDS and scored (fp32 dot products over the 256 channels), the
+// online softmax advances, then the two V half-tiles replace them and accumulate PV.  The last
+// split also attends the tail (the merge kernel then merges splits only).  Any format, group
+// size and tile form (compressed, raw); correct, not tuned.
+struct HalfAttnArgs {
+  Geo G;  // the half-head geometry the cache stores (D = 128, Hkv and Hq doubled)
+  DevBufs B;
+  const uint16_t* q;  // [n][Hq][256]
+  float* ws_acc;
+  float* ws_ml;
+  float sl2;
+  int n_splits;
+  int4 zrow[kMaxSeqsPerLaunch];  // {sequence index, sequence id, tokens in finished blocks, tail tokens}
+};
+
+template <int FMT>
+__global__ void __launch_bounds__(kThreads) attn_half_kernel(HalfAttnArgs a) {
+  constexpr int DH = 128, DR = 256;  // half-head and head channels
+  const Geo& G = a.G;
+  const int T = G.T, g = G.g, S = a.n_splits, tid = threadIdx.x;
+  const int Hq = G.Hq / 2;
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int4 z = a.zrow[blockIdx.z];
+  const int si = z.x, seq = z.y, L = z.z, ntail = z.w;
+  __shared__ __align__(16) uint16_t kvt[2][64 * DH];  // the two half-tiles (K, then V) as element bits, [t][c]
+  __shared__ float qf[kAnyMaxG * DR];
+  __shared__ float pr[kAnyMaxG * 64];
+  __shared__ float mh[kAnyMaxG], lh[kAnyMaxG], al[kAnyMaxG];
+  __shared__ TileMeta meta[2];
+  const int nb = L / T, per = nb / S, rem = nb % S;
+  const int b0 = split * per + min(split, rem), b1 = b0 + per + (split < rem ? 1 : 0);
+  const int bend = b1 + ((split == S - 1 && ntail > 0) ? 1 : 0);  // block b1 = the tail
+  for (int i = tid; i < g * DR; i += kThreads)
+    qf[i] = __uint_as_float((uint32_t)a.q[((size_t)si * Hq + h * g) * DR + i] << 16);
+  if (tid < g) {
+    mh[tid] = -INFINITY;
+    lh[tid] = 0.0f;
+  }
+  constexpr int OPT = kAnyMaxG * DR / kThreads;
+  float acc[OPT];
+#pragma unroll
+  for (int u = 0; u < OPT; ++u) acc[u] = 0.0f;
+  uint32_t flags = 0;
+  __syncthreads();
+  // the two half-tiles of (K|V) kv of block b into kvt[0], kvt[1] as [t][c] element bits
+  auto fill = [&](int b, int kv) {
+    const bool tailblk = b == b1;
+    auto one = [&](int hf, int tl, int nt, bool decode_here) {
+      const int hh = 2 * h + hf;
+      uint16_t* dst = kvt[hf];
+      const uint32_t e = tailblk ? 0u : a.B.table[table_index(G, seq, b, kv, hh)];
+      const uint32_t slot = e & 0x00FFFFFFu;
+      const bool comp = !tailblk && e != kUnallocated && !(e & 0x80000000u);
+      if (!comp) {  // tail, raw tile (K [t][c], V [c][t]) or missing (zeros, reported)
+        const uint8_t* src = nullptr;
+        if (tailblk) src = reinterpret_cast<const uint8_t*>(a.B.tail) + tail_offset(G, seq, kv, hh) * G.EB;
+        else if (e != kUnallocated) src = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
+        else flags |= 4u;
+        for (int i = tl; i < T * DH; i += nt) {
+          const int t = i / DH, c = i % DH;
+          dst[i] = src ? (uint16_t)elem_at(src, kv ? (size_t)c * T + t : (size_t)i, G.EB) : (uint16_t)0;
+        }
+      }
+      const uint8_t* b3 = a.B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + hh) * DH;
+      const uint8_t* b4 = a.B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + hh) * DH;
+      const uint8_t* tile = a.B.comp_pool + (comp ? (size_t)slot * G.stride : 0);
+      if (decode_here) {  // BF16, 8-token groups: every thread reaches the decoder's barriers
+        decode_bf16_g8_tile(G, a.B, tile, b3, b4, meta[hf],
+                            [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(dst + t * DH + c0) = w; },
+                            tl, nt, comp);
+      } else if (comp) {  // the whole block decodes (comp is the same for every thread)
+        decode_tile_any(G, a.B, tile, b3, b4, [&](int t, int c, uint32_t x) { dst[t * DH + c] = (uint16_t)x; });
+      }
+    };
+    if (FMT == 0 && G.GT == 8) {
+      one(tid >> 7, tid & 127, kThreads / 2, true);  // the two half-tiles at once, one per thread half
+    } else {
+      for (int hf = 0; hf < 2; ++hf) {
+        one(hf, tid, kThreads, false);
+        __syncthreads();
+      }
+    }
+    __syncthreads();
+  };
+  for (int b = b0; b < bend; ++b) {
+    const int nvalid = b == b1 ? ntail : T;
+    fill(b, 0);
+    for (int p0 = 0; p0 < g * T; p0 += kThreads) {
+      const int p = p0 + tid;
+      const bool on = p < g * T;
+      const int hh = on ? p / T : 0, t = p % T;
+      float d = 0.0f;
+      if (on && t < nvalid) {
+        const float* qr = qf + hh * DR;
+        for (int cc = 0; cc < DR; cc += 2) {
+          const int c = (cc + 2 * t) & (DR - 1);
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(kvt[c >> 7] + t * DH + (c & (DH - 1)));
+          d += elem_value<FMT>(w & 0xFFFFu) * qr[c] + elem_value<FMT>(w >> 16) * qr[c + 1];
+        }
+      }
+      const float sc = t < nvalid ? d * a.sl2 : -INFINITY;
+      const float m_old = on ? mh[hh] : 0.0f;
+      const float m_new = fmaxf(m_old, seg_max(sc, T));
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float pv = exp2f(sc - m_use);
+      const float sum = seg_sum(pv, T);
+      if (on) {
+        pr[hh * 64 + t] = pv;
+        if (t == 0) {
+          const float alpha = exp2f(m_old - m_use);
+          lh[hh] = lh[hh] * alpha + sum;
+          mh[hh] = m_new;
+          al[hh] = alpha;
+        }
+      }
+    }
+    __syncthreads();  // scores done with K: the V half-tiles may replace it
+    fill(b, 1);
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int o = tid + kThreads * u;
+      if (o < g * DR) {
+        const int hh = o / DR, c = o % DR;
+        const uint16_t* vc = kvt[c >> 7] + (c & (DH - 1));
+        float s = acc[u] * al[hh];
+        for (int t = 0; t < nvalid; ++t) s += pr[hh * 64 + t] * elem_value<FMT>(vc[t * DH]);
+        acc[u] = s;
+      }
+    }
+    __syncthreads();  // before the next block overwrites the tiles and the probabilities
+  }
+#pragma unroll
+  for (int u = 0; u < OPT; ++u) {
+    const int o = tid + kThreads * u;
+    if (o < g * DR) a.ws_acc[(((size_t)si * Hq + h * g + o / DR) * S + split) * DR + o % DR] = acc[u];
+  }
+  if (tid < g) {
+    float* ml = a.ws_ml + (((size_t)si * Hq + h * g + tid) * S + split) * 2;
+    ml[0] = mh[tid];
+    ml[1] = lh[tid];
+  }
+  if (flags) atomicOr(&a.B.counters->status, flags);
+}
+
 }  // namespace
 
 int launch_init(const Geo& G, const DevBufs& B, const int32_t*, const int32_t*, void* stream) {
@@ -1140,6 +1287,24 @@ int launch_attention_any(const Geo& G, const DevBufs& B, const SeqList& S, const
     a.zrow[z] = z < S.n ? make_int4(z, S.ids[z], S.lens[z], k_new ? new_pos[z] : 0) : make_int4(0, 0, 0, 0);
   auto k = G.fmt == 0 ? attn_any_kernel<0> : G.fmt == 1 ? attn_any_kernel<1> : attn_any_kernel<2>;
   hipLaunchKernelGGL(k, dim3(n_splits, G.Hkv, S.n), dim3(kThreads), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_attention_half(const Geo& G, const DevBufs& B, const SeqList& S, const int* ntail, const uint16_t* q,
+                          float scale, int n_splits, float* ws_acc, float* ws_ml, void* stream) {
+  if (G.D != 128 || G.T > 64 || G.g > kAnyMaxG || (G.Hkv & 1)) return (int)hipErrorInvalidValue;
+  HalfAttnArgs a;
+  a.G = G;
+  a.B = B;
+  a.q = q;
+  a.ws_acc = ws_acc;
+  a.ws_ml = ws_ml;
+  a.sl2 = scale * 1.4426950408889634f;
+  a.n_splits = n_splits;
+  for (int z = 0; z < kMaxSeqsPerLaunch; ++z)
+    a.zrow[z] = z < S.n ? make_int4(z, S.ids[z], S.lens[z], ntail[z]) : make_int4(0, 0, 0, 0);
+  auto k = G.fmt == 0 ? attn_half_kernel<0> : G.fmt == 1 ? attn_half_kernel<1> : attn_half_kernel<2>;
+  hipLaunchKernelGGL(k, dim3(n_splits, G.Hkv / 2, S.n), dim3(kThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

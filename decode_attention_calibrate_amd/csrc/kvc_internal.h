@@ -118,6 +118,11 @@ int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& seq
 int launch_attention_any(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale,
                          int n_splits, float* ws_acc, float* ws_ml, const void* k_new, const void* v_new,
                          const int* new_pos, void* stream);
+// Partials for 256-channel heads stored as two half-heads: seqs.lens are the finished tokens and
+// ntail[i] the tail tokens, which the last split attends (the merge then merges splits only).
+// Workspace and q in the real head geometry ([..][Hq/2 of G][256]).
+int launch_attention_half(const Geo& G, const DevBufs& B, const SeqList& seqs, const int* ntail, const uint16_t* q,
+                          float scale, int n_splits, float* ws_acc, float* ws_ml, void* stream);
 int launch_combine(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale, int n_splits,
                    const float* ws_acc, const float* ws_ml, uint16_t* out, void* stream);
 

@@ -67,8 +67,9 @@ typedef struct {
                                  128-channel half-heads (GAAC page App. D): the tiles, tails,
                                  bases and table rows of [..][Hkv][256] data are those of
                                  [..][2 Hkv][128], the same memory (a block takes 2 x 2 Hkv
-                                 slots); calibration, encode, decode and statistics work on
-                                 it, decode attention returns KVC_EUNSUPPORTED               */
+                                 slots); calibration, encode, decode, statistics and decode
+                                 attention (both halves of a head in one softmax, through a
+                                 simpler LDS-rebuild kernel) work on it                      */
   int32_t block_tokens;       /* T: tokens per block/tile: a multiple of 16 is valid; this
                                  build implements 16, 32 and 64 (others: KVC_EUNSUPPORTED)   */
   int32_t group_tokens;       /* G: tokens per exponent group, 16 or 8 in this build (GAAC
@@ -171,8 +172,9 @@ size_t kv_attention_workspace_bytes(const kvc_params* params, int32_t n_seqs, in
  * sequence are split into n_splits contiguous ranges (of 64-token super-blocks; of blocks for
  * a compressed cache with 8-token groups) processed in parallel (1 <= n_splits <= 1024); their
  * partial results and the tail are merged by log-sum-exp.  Every listed sequence must hold at
- * least one token (KVC_EINVAL otherwise).  head_dim 256 returns KVC_EUNSUPPORTED (also from
- * the split halves and from kv_decode_step, before anything runs). */
+ * least one token (KVC_EINVAL otherwise).  With head_dim 256 the split kernel's last split
+ * attends the tail and the merge kernel merges the splits only; kv_decode_step then runs as
+ * the append followed by this attention. */
 int kv_decode_attention(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
                         float scale, int32_t n_splits, void* ws_dev, size_t ws_bytes, void* out_dev, void* stream);
 

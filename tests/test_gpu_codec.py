@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import synth
-from kvtest import compare_tiles, dev, host, new_cache, oracle_layer
+from kvtest import compare_tiles, dev, host, new_cache, oracle_layer, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -163,10 +163,8 @@ def test_cfg2_full_context_codec():
 
 def test_head_dim_256_half_heads():
     """A 256-channel head (GAAC page App. D: two 128-channel half-heads): encoded bytes equal the
-    oracle's for the half-head view of the same tokens, blocks decode back bit for bit, and
-    decode attention is refused before anything runs."""
+    oracle's for the half-head view of the same tokens, and blocks decode back bit for bit."""
     import dataclasses
-    from decode_attention_calibrate_amd._lib import KVCError
     cfg = dataclasses.replace(synth.config(0), D=256)
     g, toks = synth.sequence_tokens(cfg)
     k, v = toks[0]
@@ -186,7 +184,46 @@ def test_head_dim_256_half_heads():
     assert np.array_equal(host(kd), k[:960]) and np.array_equal(host(vd), v[:960])
     flags, st = cache.status()
     assert flags == 0 and st["comp_tiles"] == 15 * 2 * 2 * cfg.Hkv and st["raw_tiles"] == 0
-    q = dev(synth.queries(dataclasses.replace(cfg, D=256)))
-    with pytest.raises(KVCError) as e:
-        cache.attention([0], q, cfg.scale, 2)
-    assert e.value.code == -3
+
+
+@pytest.mark.parametrize("fmt,Gt,T", [(oracle.BF16, 16, 64), (oracle.BF16, 8, 16), (oracle.E5M2, 16, 64),
+                                      (oracle.E4M3, 8, 64)])
+def test_head_dim_256_attention(fmt, Gt, T):
+    """Decode attention over 256-channel heads (both half-heads of a head in one softmax; the
+    tail attended by the last split): compressed, raw-fallback and uncompressed caches against
+    the oracle's fp64 attention, lengths with tails of 0, 1 and T - 1 tokens, split counts 1 to
+    16, and a decode step equal to append + attention bit for bit."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.config(0), D=256, fmt=fmt)
+    g, toks = synth.sequence_tokens(cfg)
+    k, v = toks[0]
+    for L in (T - 1, 3 * T, 3 * T + 1, 700):
+        q = synth.queries(cfg, step=L)
+        ref = oracle.attention(fmt, q[0], k[:L], v[:L], cfg.scale)
+        for compressed, esc_cap in ((True, -1), (True, 16), (False, -1)):
+            n_tiles = (L // T + 2) * 2 * 2 * cfg.Hkv
+            cache = new_cache(Hkv=cfg.Hkv, Hq=cfg.Hq, D=256, T=T, max_seqs=1, max_blocks=L // T + 2,
+                              comp_slots=n_tiles if compressed else None, raw_slots=n_tiles, compressed=compressed,
+                              esc_cap=esc_cap, fmt=fmt, Gt=Gt)
+            cache.calibrate(dev(k[:cfg.n_cal], fmt), dev(v[:cfg.n_cal], fmt))
+            cache.append([0], dev(k[None, :L], fmt), dev(v[None, :L], fmt))
+            for S in (1, 3, 16):
+                out = host(cache.attention([0], dev(q), cfg.scale, S))
+                assert row_rel_err(out[0], ref) <= 4e-3, (L, compressed, esc_cap, S)
+            assert cache.status()[0] == 0
+    # decode step against append + attention
+    L = 3 * T - 2
+    a, b = [new_cache(Hkv=cfg.Hkv, Hq=cfg.Hq, D=256, T=T, max_seqs=1, max_blocks=L // T + 3,
+                      comp_slots=(L // T + 3) * 4 * cfg.Hkv, raw_slots=(L // T + 3) * 4 * cfg.Hkv, fmt=fmt, Gt=Gt)
+            for _ in range(2)]
+    for c in (a, b):
+        c.calibrate(dev(k[:cfg.n_cal], fmt), dev(v[:cfg.n_cal], fmt))
+        c.append([0], dev(k[None, :L], fmt), dev(v[None, :L], fmt))
+    for t in range(L, L + 4):
+        q = dev(synth.queries(cfg, step=t))
+        kn, vn = dev(k[None, t:t + 1], fmt), dev(v[None, t:t + 1], fmt)
+        out_a = host(a.decode_step([0], kn, vn, q, cfg.scale, 4))
+        b.append([0], kn, vn)
+        assert np.array_equal(out_a, host(b.attention([0], q, cfg.scale, 4))), t
+        ref = oracle.attention(fmt, synth.queries(cfg, step=t)[0], k[:t + 1], v[:t + 1], cfg.scale)
+        assert row_rel_err(out_a[0], ref) <= 4e-3, t
