@@ -57,10 +57,11 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep", type=str, default="", help="comma-separated split counts to time (extra)")
     ap.add_argument("--probe", action="store_true", help="also time plain HBM copy / read kernels (torch)")
-    ap.add_argument("--extra", type=str, default="context,fp8,paged,groups,rope,serving",
+    ap.add_argument("--extra", type=str, default="context,fp8,paged,groups,rope,serving,prefill",
                     help="comma list of extra workloads measured after the headline one: context (the cfg2 "
                          "layer at 32K and 128K tokens), fp8 (the 64K layer in "
-                         "FP8 E5M2 and E4M3), paged (32-sequence paged serving mix), groups (the 64K layer's "
+                         "FP8 E5M2 and E4M3), paged (32-sequence paged serving mix), prefill (a 4K-token prompt: encode, "
+                         "decode_blocks, causal prefill attention), groups (the 64K layer's "
                          "codec with 16- and 8-token exponent groups), rope (escape bytes and raw tiles along "
                          "the 64K layer with RoPE-rotated keys, per calibration policy), serving (sequences "
                          "admitted and decode throughput under one KV byte budget); '' for none")
@@ -335,6 +336,8 @@ def main():
         result["codec_groups_64k"] = codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, q, args.splits)
     if "rope" in extras:
         result["rope_drift_64k"] = rope_drift(torch, K, synth, cfg, k0, v0, dev)
+    if "prefill" in extras:
+        result["prefill_4k"] = prefill(torch, K, synth, cfg, k0, v0, dev, stream)
     if "serving" in extras:
         result["equal_memory_serving"] = equal_memory_serving(torch, K, synth, splits=args.paged_splits)
     if not args.no_cpu:
@@ -409,6 +412,49 @@ def codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, q, n_splits, reps=5
         }
         del c
     log(f"[bench] codec groups: {res}")
+    return res
+
+
+def prefill(torch, K, synth, cfg, k0, v0, dev, stream, n=4096, reps=5):
+    """Prefill of an n-token prompt over its decoded blocks (GAAC page §3.3): the bulk append
+    that encodes every block, kv_decode_blocks rebuilding them, and causal prefill attention of
+    all n queries over them (the 64K layer's geometry; queries from the same seeded generator
+    as the decode steps)."""
+    import dataclasses
+    T, D, Hkv, Hq = cfg.T, cfg.D, cfg.Hkv, cfg.Hq
+    nb = n // T
+    c = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=1, max_blocks_per_seq=nb + 1,
+                  num_comp_slots=(nb + 1) * 2 * Hkv, num_raw_slots=64, compressed=True, perm_seed=7)
+    c.calibrate(dev(k0[:cfg.n_cal]), dev(v0[:cfg.n_cal]))
+    kd, vd = dev(k0[None, :n]), dev(v0[None, :n])
+    q = dev(synth.queries(dataclasses.replace(cfg, n_seqs=n)))
+    kout = torch.empty((n, Hkv, D), dtype=torch.int16, device="cuda")
+    vout = torch.empty_like(kout)
+    out = torch.empty((n, Hq, D), dtype=torch.int16, device="cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    enc, dec, att = [], [], []
+    for r in range(reps):
+        c.release(0) if r else None
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+        e0.record(stream)
+        c.append([0], kd, vd)
+        e1.record(stream)
+        c.decode_blocks(0, 0, nb, (kout, vout))
+        e2.record(stream)
+        c.prefill_attention(kout, vout, q, cfg.scale, out)
+        e3.record(stream)
+        torch.cuda.synchronize()
+        enc.append(e0.elapsed_time(e1) * 1e3)
+        dec.append(e1.elapsed_time(e2) * 1e3)
+        att.append(e2.elapsed_time(e3) * 1e3)
+    if not (torch.equal(kout, kd[0]) and torch.equal(vout, vd[0])):
+        raise RuntimeError("decode_blocks did not rebuild the prompt bit for bit")
+    flops = 4.0 * Hq * D * (n * (n + 1) / 2)  # QK and PV over the causal pairs
+    a_us = float(np.median(att))
+    res = {"workload": f"qwen3-8b-like-prefill-{n}", "tokens": n, "encode_us": round(float(np.median(enc)), 1),
+           "decode_blocks_us": round(float(np.median(dec)), 1), "prefill_attention_us": round(a_us, 1),
+           "prefill_attention_TFLOPs": round(flops / (a_us * 1e-6) / 1e12, 2)}
+    log(f"[bench] prefill: {res}")
     return res
 
 

@@ -48,6 +48,7 @@ SIGNATURES = {
     "kv_calibrate": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
     "kv_encode_append": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, _vp, _i32, _vp]),
     "kv_decode_blocks": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "kv_prefill_attention": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp, _vp]),
     "kv_attention_workspace_bytes": (_sz, [_P(Params), _i32, _i32]),
     "kv_decode_attention": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, ctypes.c_float, _i32, _vp, _sz, _vp, _vp]),
     "kv_attention_partials": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, ctypes.c_float, _i32, _vp, _sz, _vp]),

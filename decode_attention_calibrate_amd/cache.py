@@ -98,6 +98,22 @@ class KVCache:
         L.check(self.lib.kv_decode_blocks(self.handle, seq, first, n, _ptr(k), _ptr(v), self._stream()))
         return k, v
 
+    def prefill_attention(self, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, scale: float, out=None) -> torch.Tensor:
+        """Causal attention of q ([n_q][Hq][D] BF16 bits, the last n_q positions) over k, v
+        ([n_kv][Hkv][D] elements, e.g. from decode_blocks) -> [n_q][Hq][D] BF16 bits."""
+        n_kv, n_q = k.shape[0], q.shape[0]
+        for t in (k, v):
+            _elem(t, "k/v", self.EB)
+            if tuple(t.shape) != (n_kv, self.Hkv, self.D):
+                raise ValueError("k and v must be [n_kv][Hkv][D]")
+        if tuple(q.shape) != (n_q, self.Hq, self.D) or q.device != self.device:
+            raise ValueError(f"q must be [n_q][{self.Hq}][{self.D}] on {self.device}")
+        if out is None:
+            out = torch.empty((n_q, self.Hq, self.D), dtype=torch.int16, device=self.device)
+        L.check(self.lib.kv_prefill_attention(self.handle, _ptr(k), _ptr(v), n_kv, _ptr(q), n_q, float(scale), _ptr(out),
+                                              self._stream()))
+        return out
+
     def workspace(self, n_seqs: int, n_splits: int) -> torch.Tensor:
         nb = self.lib.kv_attention_workspace_bytes(ctypes.byref(self.params), n_seqs, n_splits)
         return torch.empty(max(nb, 16), dtype=torch.uint8, device=self.device)

@@ -291,6 +291,22 @@ int kv_decode_blocks(kvc_cache* c, int32_t seq, int32_t first_block, int32_t n_b
                   "launch decode_blocks");
 }
 
+int kv_prefill_attention(kvc_cache* c, const void* k_dev, const void* v_dev, int32_t n_kv, const void* q_dev,
+                         int32_t n_q, float scale, void* out_dev, void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  if (!k_dev || !v_dev || !q_dev || !out_dev) return fail(KVC_EINVAL, "k, v, q and out must not be NULL");
+  if (n_q < 1 || n_q > n_kv) return fail(KVC_EINVAL, "need 1 <= n_q <= n_kv");
+  for (const void* p : {k_dev, v_dev, q_dev, (const void*)out_dev})
+    if ((uintptr_t)p & 15u) return fail(KVC_EINVAL, "k, v, q and out must be 16-byte aligned");
+  Geo G = c->G;  // the real head layout (a 256-channel head is not split here)
+  G.D = c->p.head_dim;
+  G.Hkv = c->p.num_kv_heads;
+  G.Hq = c->p.num_q_heads;
+  return hip_fail(kvc::launch_prefill(G, k_dev, v_dev, n_kv, (const uint16_t*)q_dev, n_q, scale, (uint16_t*)out_dev,
+                                      stream),
+                  "launch prefill attention");
+}
+
 size_t kv_attention_workspace_bytes(const kvc_params* p, int32_t n_seqs, int32_t n_splits) {
   if (!p || n_seqs < 1 || n_splits < 1) return 0;
   return (size_t)n_seqs * p->num_q_heads * n_splits * ((size_t)p->head_dim + 2) * 4;

@@ -1223,6 +1223,109 @@ __global__ void __launch_bounds__(kThreads) attn_half_kernel(HalfAttnArgs a) {
   if (flags) atomicOr(&a.B.counters->status, flags);
 }
 
+// ------------------------------------------------------------------------------------------
+// Prefill attention (GAAC page §3.3: prefill runs standard attention over blocks rebuilt by
+// the block decoder).  Causal: query i of n_q (token position n_kv - n_q + i) attends tokens
+// 0 .. its own position.  One 256-thread workgroup per (16-query tile, query head); key blocks
+// of KB = min(64, 8192 / D) tokens go to LDS; fp32 scores, an online softmax per query row and
+// PV, as in the decode kernels.  Correct for D <= 256 and every format; not tuned.
+struct PrefillArgs {
+  Geo G;               // the cache's geometry (format; D and heads in the real head layout)
+  const uint8_t* k;    // [n_kv][Hkv][D] elements
+  const uint8_t* v;
+  const uint16_t* q;   // [n_q][Hq][D] BF16
+  uint16_t* out;       // [n_q][Hq][D] BF16
+  int n_kv, n_q;
+  float sl2;
+};
+
+template <int FMT>
+__global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
+  constexpr int QT = 16;  // queries per workgroup
+  const Geo& G = a.G;
+  const int D = G.D, Hkv = G.Hkv, Hq = G.Hq, g = G.g, EB = G.EB, tid = threadIdx.x;
+  const int KB = min(64, 8192 / D);
+  const int qt0 = blockIdx.x * QT, hq = blockIdx.y, h = hq / g;
+  const int pos0 = a.n_kv - a.n_q;  // position of query 0
+  const int nq = min(QT, a.n_q - qt0);
+  __shared__ __align__(16) uint16_t kt[8192], vt[8192];  // key block, [t][c] element bits
+  __shared__ float qf[QT * 256];
+  __shared__ float pr[QT * 64];
+  __shared__ float mh[QT], lh[QT], al[QT];
+  for (int i = tid; i < QT * D; i += kThreads) {
+    const int r = i / D, c = i % D;
+    qf[i] = r < nq ? __uint_as_float((uint32_t)a.q[((size_t)(qt0 + r) * Hq + hq) * D + c] << 16) : 0.0f;
+  }
+  if (tid < QT) {
+    mh[tid] = -INFINITY;
+    lh[tid] = 0.0f;
+  }
+  constexpr int OPT = QT * 256 / kThreads;
+  float acc[OPT];
+#pragma unroll
+  for (int u = 0; u < OPT; ++u) acc[u] = 0.0f;
+  __syncthreads();
+  const int last = pos0 + qt0 + nq - 1;  // the last key any query of this tile sees
+  for (int kb0 = 0; kb0 <= last; kb0 += KB) {
+    for (int i = tid; i < KB * D; i += kThreads) {
+      const int t = i / D, c = i % D, tok = kb0 + t;
+      const size_t e = ((size_t)tok * Hkv + h) * D + c;
+      kt[i] = tok <= last ? (uint16_t)elem_at(a.k, e, EB) : (uint16_t)0;
+      vt[i] = tok <= last ? (uint16_t)elem_at(a.v, e, EB) : (uint16_t)0;
+    }
+    __syncthreads();
+    // scores and online softmax: pair (query r, key t), a query's KB keys in one aligned segment
+    for (int p0 = 0; p0 < QT * KB; p0 += kThreads) {
+      const int p = p0 + tid, r = p / KB, t = p % KB, tok = kb0 + t;
+      const bool ok = r < nq && tok <= pos0 + qt0 + r;
+      float d = 0.0f;
+      if (ok) {
+        const uint16_t* kr = kt + t * D;
+        const float* qr = qf + r * D;
+        for (int cc = 0; cc < D; cc += 2) {
+          const int c = (cc + 2 * t) & (D - 1);
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(kr + c);
+          d += elem_value<FMT>(w & 0xFFFFu) * qr[c] + elem_value<FMT>(w >> 16) * qr[c + 1];
+        }
+      }
+      const float sc = ok ? d * a.sl2 : -INFINITY;
+      const float m_old = mh[r];
+      const float m_new = fmaxf(m_old, seg_max(sc, KB));
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float pv = exp2f(sc - m_use);
+      const float sum = seg_sum(pv, KB);
+      pr[r * 64 + t] = pv;
+      if (t == 0) {
+        const float alpha = exp2f(m_old - m_use);
+        lh[r] = lh[r] * alpha + sum;
+        mh[r] = m_new;
+        al[r] = alpha;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int o = tid + kThreads * u;
+      if (o < QT * D) {
+        const int r = o / D, c = o % D;
+        float s = acc[u] * al[r];
+        for (int t = 0; t < KB; ++t) s += pr[r * 64 + t] * elem_value<FMT>(vt[t * D + c]);
+        acc[u] = s;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < OPT; ++u) {
+    const int o = tid + kThreads * u;
+    if (o < QT * D) {
+      const int r = o / D, c = o % D;
+      if (r < nq)
+        a.out[((size_t)(qt0 + r) * Hq + hq) * D + c] = __builtin_bit_cast(uint16_t, (__bf16)(acc[u] / lh[r]));
+    }
+  }
+}
+
 }  // namespace
 
 int launch_init(const Geo& G, const DevBufs& B, const int32_t*, const int32_t*, void* stream) {
@@ -1305,6 +1408,23 @@ int launch_attention_half(const Geo& G, const DevBufs& B, const SeqList& S, cons
     a.zrow[z] = z < S.n ? make_int4(z, S.ids[z], S.lens[z], ntail[z]) : make_int4(0, 0, 0, 0);
   auto k = G.fmt == 0 ? attn_half_kernel<0> : G.fmt == 1 ? attn_half_kernel<1> : attn_half_kernel<2>;
   hipLaunchKernelGGL(k, dim3(n_splits, G.Hkv / 2, S.n), dim3(kThreads), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_prefill(const Geo& G, const void* k, const void* v, int n_kv, const uint16_t* q, int n_q, float scale,
+                   uint16_t* out, void* stream) {
+  if (G.D > 256 || (G.D & (G.D - 1)) || n_q < 1 || n_q > n_kv) return (int)hipErrorInvalidValue;
+  PrefillArgs a;
+  a.G = G;
+  a.k = reinterpret_cast<const uint8_t*>(k);
+  a.v = reinterpret_cast<const uint8_t*>(v);
+  a.q = q;
+  a.out = out;
+  a.n_kv = n_kv;
+  a.n_q = n_q;
+  a.sl2 = scale * 1.4426950408889634f;
+  auto kern = G.fmt == 0 ? prefill_kernel<0> : G.fmt == 1 ? prefill_kernel<1> : prefill_kernel<2>;
+  hipLaunchKernelGGL(kern, dim3((n_q + 15) / 16, G.Hq), dim3(kThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

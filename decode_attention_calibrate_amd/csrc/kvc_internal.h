@@ -123,6 +123,10 @@ int launch_attention_any(const Geo& G, const DevBufs& B, const SeqList& seqs, co
 // Workspace and q in the real head geometry ([..][Hq/2 of G][256]).
 int launch_attention_half(const Geo& G, const DevBufs& B, const SeqList& seqs, const int* ntail, const uint16_t* q,
                           float scale, int n_splits, float* ws_acc, float* ws_ml, void* stream);
+// Causal prefill attention over decoded K/V ([n_kv][Hkv][D]) for the last n_q positions; G in the
+// real head layout (D up to 256).
+int launch_prefill(const Geo& G, const void* k, const void* v, int n_kv, const uint16_t* q, int n_q, float scale,
+                   uint16_t* out, void* stream);
 int launch_combine(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale, int n_splits,
                    const float* ws_acc, const float* ws_ml, uint16_t* out, void* stream);
 

@@ -159,6 +159,17 @@ int kv_encode_append(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_se
 int kv_decode_blocks(kvc_cache* cache, int32_t seq, int32_t first_block, int32_t n_blocks, void* k_out_dev,
                      void* v_out_dev, void* stream);
 
+/* Causal prefill attention over K/V in plain element tensors, e.g. the blocks kv_decode_blocks
+ * rebuilt (GAAC page §3.3: prefill runs standard attention on decoded blocks).  k_dev, v_dev:
+ * [n_kv][Hkv][D] elements of the cache's format (the sequence's first n_kv tokens); q_dev:
+ * [n_q][Hq][D] BF16, the queries of positions n_kv - n_q .. n_kv - 1; out_dev: [n_q][Hq][D] BF16
+ * (round-to-nearest-even of an fp32 result).  Query i attends tokens 0 .. n_kv - n_q + i with
+ * softmax(scale * q . k); query head hq reads KV head hq / (Hq / Hkv).  1 <= n_q <= n_kv; every
+ * pointer 16-byte aligned (KVC_EINVAL otherwise).  The cache handle supplies the format and the
+ * head geometry only.  Correct for every format and head_dim; not tuned. */
+int kv_prefill_attention(kvc_cache* cache, const void* k_dev, const void* v_dev, int32_t n_kv, const void* q_dev,
+                         int32_t n_q, float scale, void* out_dev, void* stream);
+
 /* Bytes of workspace kv_decode_attention needs for n_seqs sequences and n_splits splits:
  * fp32 partial outputs [n_seqs][Hq][n_splits][D] and (max, sum) pairs [n_seqs][Hq][n_splits][2]. */
 size_t kv_attention_workspace_bytes(const kvc_params* params, int32_t n_seqs, int32_t n_splits);
