@@ -1226,9 +1226,11 @@ __global__ void __launch_bounds__(kThreads) attn_half_kernel(HalfAttnArgs a) {
 // ------------------------------------------------------------------------------------------
 // Prefill attention (GAAC page §3.3: prefill runs standard attention over blocks rebuilt by
 // the block decoder).  Causal: query i of n_q (token position n_kv - n_q + i) attends tokens
-// 0 .. its own position.  One 256-thread workgroup per (16-query tile, query head); key blocks
-// of KB = min(64, 8192 / D) tokens go to LDS; fp32 scores, an online softmax per query row and
-// PV, as in the decode kernels.  Correct for D <= 256 and every format; not tuned.
+// 0 .. its own position.  One 256-thread workgroup per (64 queries, query head), 16 queries
+// per wave; key blocks of KB tokens (64, or 32 for 256-channel heads) go to LDS as BF16 (K as
+// rows, V transposed); QK and PV on v_mfma_f32_16x16x32_bf16 (P as a BF16 high part plus
+// remainder, ~16 mantissa bits), an online softmax per query row in between; each wave's P
+// tile passes through LDS to change from the QK output layout to the PV operand layout.
 struct PrefillArgs {
   Geo G;               // the cache's geometry (format; D and heads in the real head layout)
   const uint8_t* k;    // [n_kv][Hkv][D] elements
@@ -1239,89 +1241,167 @@ struct PrefillArgs {
   float sl2;
 };
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+// Element bits -> BF16 bits (exact: every FP8 value is a BF16 value).
+template <int FMT>
+__device__ __forceinline__ uint16_t bf16_of(uint32_t x) {
+  if constexpr (FMT == 0) return (uint16_t)x;
+  else return (uint16_t)(__float_as_uint(elem_value<FMT>(x)) >> 16);
+}
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
-  constexpr int QT = 16;  // queries per workgroup
+  constexpr int QW = 16;           // queries per wave
+  constexpr int QT = 4 * QW;       // queries per workgroup
   const Geo& G = a.G;
   const int D = G.D, Hkv = G.Hkv, Hq = G.Hq, g = G.g, EB = G.EB, tid = threadIdx.x;
-  const int KB = min(64, 8192 / D);
-  const int qt0 = blockIdx.x * QT, hq = blockIdx.y, h = hq / g;
-  const int pos0 = a.n_kv - a.n_q;  // position of query 0
-  const int nq = min(QT, a.n_q - qt0);
-  __shared__ __align__(16) uint16_t kt[8192], vt[8192];  // key block, [t][c] element bits
-  __shared__ float qf[QT * 256];
-  __shared__ float pr[QT * 64];
-  __shared__ float mh[QT], lh[QT], al[QT];
-  for (int i = tid; i < QT * D; i += kThreads) {
-    const int r = i / D, c = i % D;
-    qf[i] = r < nq ? __uint_as_float((uint32_t)a.q[((size_t)(qt0 + r) * Hq + hq) * D + c] << 16) : 0.0f;
-  }
-  if (tid < QT) {
-    mh[tid] = -INFINITY;
-    lh[tid] = 0.0f;
-  }
-  constexpr int OPT = QT * 256 / kThreads;
-  float acc[OPT];
+  const int lane = tid & 63, wv = tid >> 6, col = lane & 15, kq = lane >> 4;
+  const int KB = D > 128 ? 32 : 64;  // keys per block in LDS
+  const int q0 = blockIdx.x * QT, hq = blockIdx.y, h = hq / g;
+  const int pos0 = a.n_kv - a.n_q;   // position of query 0
+  const int nq = min(QT, a.n_q - q0);
+  __shared__ __align__(16) uint16_t kl[64 * 128];     // key block, BF16 bits, [t][c]
+  __shared__ __align__(16) uint16_t vtl[64 * 128];    // value block, BF16 bits, [c][t]
+  __shared__ __align__(16) float pl[4][QW * 64];      // each wave's probabilities, [query][key]
+  // this wave's queries as QK A operands (rows = queries, k = channels), zero past n_q
+  const int qw0 = q0 + QW * wv;                        // first query of this wave
+  uint4 qa[8];
 #pragma unroll
-  for (int u = 0; u < OPT; ++u) acc[u] = 0.0f;
-  __syncthreads();
-  const int last = pos0 + qt0 + nq - 1;  // the last key any query of this tile sees
+  for (int ks = 0; ks < 8; ++ks) {
+    qa[ks] = make_uint4(0, 0, 0, 0);
+    if (32 * ks < D && qw0 + col < a.n_q)
+      qa[ks] = *reinterpret_cast<const uint4*>(a.q + ((size_t)(qw0 + col) * Hq + hq) * D + 32 * ks + 8 * kq);
+  }
+  float m[4], l[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.0f;
+  }
+  f32x4_t o[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) o[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int last = pos0 + q0 + nq - 1;       // the last key any query of this workgroup sees
+  const int wlast = pos0 + qw0 + QW - 1;     // ... of this wave (clamped below by the data)
   for (int kb0 = 0; kb0 <= last; kb0 += KB) {
-    for (int i = tid; i < KB * D; i += kThreads) {
-      const int t = i / D, c = i % D, tok = kb0 + t;
-      const size_t e = ((size_t)tok * Hkv + h) * D + c;
-      kt[i] = tok <= last ? (uint16_t)elem_at(a.k, e, EB) : (uint16_t)0;
-      vt[i] = tok <= last ? (uint16_t)elem_at(a.v, e, EB) : (uint16_t)0;
+    if constexpr (FMT == 0) {  // eight channels per thread and pass, 16-byte loads
+      for (int i = 8 * tid; i < KB * D; i += 8 * kThreads) {
+        const int t = i / D, c = i % D, tok = kb0 + t;
+        const size_t e = ((size_t)tok * Hkv + h) * D + c;
+        uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+        if (tok <= last) {
+          kx = *reinterpret_cast<const uint4*>(a.k + 2 * e);
+          vx = *reinterpret_cast<const uint4*>(a.v + 2 * e);
+        }
+        *reinterpret_cast<uint4*>(kl + i) = kx;
+        const uint32_t vw[4] = {vx.x, vx.y, vx.z, vx.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) vtl[(c + k) * KB + t] = (uint16_t)(vw[k >> 1] >> (16 * (k & 1)));
+      }
+    } else {
+      for (int i = tid; i < KB * D; i += kThreads) {
+        const int t = i / D, c = i % D, tok = kb0 + t;
+        const size_t e = ((size_t)tok * Hkv + h) * D + c;
+        uint16_t kx = 0, vx = 0;
+        if (tok <= last) {
+          kx = bf16_of<FMT>(elem_at(a.k, e, EB));
+          vx = bf16_of<FMT>(elem_at(a.v, e, EB));
+        }
+        kl[i] = kx;
+        vtl[c * KB + t] = vx;
+      }
     }
     __syncthreads();
-    // scores and online softmax: pair (query r, key t), a query's KB keys in one aligned segment
-    for (int p0 = 0; p0 < QT * KB; p0 += kThreads) {
-      const int p = p0 + tid, r = p / KB, t = p % KB, tok = kb0 + t;
-      const bool ok = r < nq && tok <= pos0 + qt0 + r;
-      float d = 0.0f;
-      if (ok) {
-        const uint16_t* kr = kt + t * D;
-        const float* qr = qf + r * D;
-        for (int cc = 0; cc < D; cc += 2) {
-          const int c = (cc + 2 * t) & (D - 1);
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(kr + c);
-          d += elem_value<FMT>(w & 0xFFFFu) * qr[c] + elem_value<FMT>(w >> 16) * qr[c + 1];
+    if (kb0 <= wlast && qw0 < a.n_q) {
+      // scores: sub-block sb = keys kb0+16sb..; lane holds key kb0+16sb+col for queries 4kq+r
+      f32x4_t sc[4];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        sc[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (16 * sb < KB) {
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks)
+            if (32 * ks < D)
+              sc[sb] = mfma_bf16(qa[ks], *reinterpret_cast<const uint4*>(kl + (16 * sb + col) * D + 32 * ks + 8 * kq), sc[sb]);
         }
       }
-      const float sc = ok ? d * a.sl2 : -INFINITY;
-      const float m_old = mh[r];
-      const float m_new = fmaxf(m_old, seg_max(sc, KB));
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float pv = exp2f(sc - m_use);
-      const float sum = seg_sum(pv, KB);
-      pr[r * 64 + t] = pv;
-      if (t == 0) {
-        const float alpha = exp2f(m_old - m_use);
-        lh[r] = lh[r] * alpha + sum;
-        mh[r] = m_new;
-        al[r] = alpha;
-      }
-    }
-    __syncthreads();
+      float rmax[4];
 #pragma unroll
-    for (int u = 0; u < OPT; ++u) {
-      const int o = tid + kThreads * u;
-      if (o < QT * D) {
-        const int r = o / D, c = o % D;
-        float s = acc[u] * al[r];
-        for (int t = 0; t < KB; ++t) s += pr[r * 64 + t] * elem_value<FMT>(vt[t * D + c]);
-        acc[u] = s;
+      for (int r = 0; r < 4; ++r) {
+        const int qpos = pos0 + qw0 + 4 * kq + r;
+        rmax[r] = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+          const int tok = kb0 + 16 * sb + col;
+          const bool ok = 16 * sb < KB && tok <= qpos && qw0 + 4 * kq + r < a.n_q;
+          sc[sb][r] = ok ? sc[sb][r] * a.sl2 : -INFINITY;
+          rmax[r] = fmaxf(rmax[r], sc[sb][r]);
+        }
+        for (int x = 1; x < 16; x <<= 1) rmax[r] = fmaxf(rmax[r], __shfl_xor(rmax[r], x));
+      }
+      float alpha[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float m_new = fmaxf(m[r], rmax[r]);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        alpha[r] = exp2f(m[r] - m_use);
+        float sum = 0.0f;
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+          const float p = exp2f(sc[sb][r] - m_use);
+          if (16 * sb < KB) pl[wv][(4 * kq + r) * 64 + 16 * sb + col] = p;
+          sum += p;
+        }
+        for (int x = 1; x < 16; x <<= 1) sum += __shfl_xor(sum, x);
+        l[r] = l[r] * alpha[r] + sum;
+        m[r] = m_new;
+      }
+      // the wave's own P rows are read back as PV A operands (rows = queries, k = keys); LDS
+      // accesses of one wave complete in order, no barrier needed
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        if (16 * s < D)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[s][r] *= alpha[r];
+      for (int kc = 0; kc < KB / 32; ++kc) {
+        const float* pr = &pl[wv][col * 64 + 32 * kc + 8 * kq];
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = bf16_pair(pr[2 * e], pr[2 * e + 1]);
+          lo[e] = bf16_pair(pr[2 * e] - __uint_as_float(hi[e] << 16), pr[2 * e + 1] - __uint_as_float(hi[e] & 0xFFFF0000u));
+        }
+        const uint4 ph = make_uint4(hi[0], hi[1], hi[2], hi[3]), plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          if (16 * s < D) {
+            const uint4 vb = *reinterpret_cast<const uint4*>(vtl + (16 * s + col) * KB + 32 * kc + 8 * kq);
+            o[s] = mfma_bf16(ph, vb, o[s]);
+            o[s] = mfma_bf16(plo, vb, o[s]);
+          }
+        }
       }
     }
-    __syncthreads();
+    __syncthreads();  // before the next key block replaces kl and vtl
   }
+  // out: lane holds channel 16s+col of queries 4kq+r
 #pragma unroll
-  for (int u = 0; u < OPT; ++u) {
-    const int o = tid + kThreads * u;
-    if (o < QT * D) {
-      const int r = o / D, c = o % D;
-      if (r < nq)
-        a.out[((size_t)(qt0 + r) * Hq + hq) * D + c] = __builtin_bit_cast(uint16_t, (__bf16)(acc[u] / lh[r]));
+  for (int r = 0; r < 4; ++r) {
+    const int qi = qw0 + 4 * kq + r;
+    if (qi < a.n_q) {
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        if (16 * s < D)
+          a.out[((size_t)qi * Hq + hq) * D + 16 * s + col] = __builtin_bit_cast(uint16_t, (__bf16)(o[s][r] / l[r]));
     }
   }
 }
@@ -1424,7 +1504,7 @@ int launch_prefill(const Geo& G, const void* k, const void* v, int n_kv, const u
   a.n_q = n_q;
   a.sl2 = scale * 1.4426950408889634f;
   auto kern = G.fmt == 0 ? prefill_kernel<0> : G.fmt == 1 ? prefill_kernel<1> : prefill_kernel<2>;
-  hipLaunchKernelGGL(kern, dim3((n_q + 15) / 16, G.Hq), dim3(kThreads), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(kern, dim3((n_q + 63) / 64, G.Hq), dim3(kThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
