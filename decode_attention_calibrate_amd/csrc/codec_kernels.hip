@@ -1266,7 +1266,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   const int D = G.D, Hkv = G.Hkv, Hq = G.Hq, g = G.g, EB = G.EB, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6, col = lane & 15, kq = lane >> 4;
   const int KB = D > 128 ? 32 : 64;  // keys per block in LDS
-  const int q0 = blockIdx.x * QT, hq = blockIdx.y, h = hq / g;
+  // the last query tiles attend the most keys: they go first (longest processing time first)
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * QT, hq = blockIdx.y, h = hq / g;
   const int pos0 = a.n_kv - a.n_q;   // position of query 0
   const int nq = min(QT, a.n_q - q0);
   __shared__ __align__(16) uint16_t kl[64 * 128];     // key block, BF16 bits, [t][c]
