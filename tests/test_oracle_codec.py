@@ -12,6 +12,7 @@ import pytest
 
 import synth
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -79,29 +80,115 @@ def test_fp8_every_pattern_roundtrips(orc, fmt):
 
 # ---- golden bytes derived by hand from the format -----------------------------------------
 
-@pytest.mark.parametrize("name", ["tile_t16_d2_narrow_wide", "tile_t16_d2_raw_group"])
-def test_golden_tile_bytes(orc, name):
+GOLDEN_TILES = ["tile_t16_d2_narrow_wide", "tile_t16_d2_raw_group", "tile_e5m2_t16_d4_narrow_wide_raw",
+                "tile_e4m3_t16_d2_g8_narrow_raw", "tile_bf16_t16_d2_g8_raw_wide"]
+
+
+def _golden(orc, name):
+    """(params, elements [T][D], b3, b4, expected slot bytes, stride) of one golden tile."""
     d = json.load(open(os.path.join(GOLDEN, name + ".json")))
     p = orc.Params(**d["params"])
-    T, D = p.T, p.D
-    x = np.zeros((T, D), np.uint16)
-    for t in range(T):
-        if name.endswith("narrow_wide"):
-            x[t, 0] = ((t % 2) << 15) | ((120 + t % 8) << 7) | t
-            x[t, 1] = ((t % 2) << 15) | ((120 + t) << 7) | (16 + t)
-        else:
-            x[t, 0] = ((8 * t + 7) << 7) | t
-            x[t, 1] = 127 << 7
-    b3 = np.array(d["b3"], np.uint8)
-    b4 = np.array(d["b4"], np.uint8)
+    if "x" in d:
+        x = np.array(d["x"], np.uint16)
+    else:  # the first two fixtures state their elements as formulas
+        x = np.zeros((p.T, p.D), np.uint16)
+        for t in range(p.T):
+            if name.endswith("narrow_wide"):
+                x[t, 0] = ((t % 2) << 15) | ((120 + t % 8) << 7) | t
+                x[t, 1] = ((t % 2) << 15) | ((120 + t) << 7) | (16 + t)
+            else:
+                x[t, 0] = ((8 * t + 7) << 7) | t
+                x[t, 1] = 127 << 7
+    assert x.shape == (p.T, p.D)
+    want = bytes.fromhex(d["expected_hex"].replace(" ", ""))
+    return p, x, np.array(d["b3"], np.uint8), np.array(d["b4"], np.uint8), want, d["stride"]
+
+
+@pytest.mark.parametrize("name", GOLDEN_TILES)
+def test_golden_tile_bytes(orc, name):
+    p, x, b3, b4, want, stride = _golden(orc, name)
     data, is_raw, esc, modes = orc.encode_tiles(p, x[None], b3, b4, 0)
     lay = orc.layout(p)
-    assert lay["stride"] == d["stride"]
-    want = bytes.fromhex(d["expected_hex"].replace(" ", ""))
+    assert lay["stride"] == stride == len(want)
     assert is_raw[0] == 0
     assert bytes(data[0, :lay["stride"]]) == want
     back, st = orc.decode_tiles(p, data, is_raw, 0, b3, b4)
     assert st[0] == 0 and np.array_equal(back[0], x)
+    # decoding the hand-written bytes (not the oracle's own) gives the elements back too
+    back2, st2 = orc.decode_tiles(p, np.frombuffer(want, np.uint8)[None], [0], 0, b3, b4)
+    assert st2[0] == 0 and np.array_equal(back2[0], x)
+
+
+# Layout mistakes a round trip cannot see (encoder and decoder wrong the same way), planted in
+# scratch copies of the oracle source: each must change the bytes of at least one golden tile.
+PLANTED = {
+    "E5M2 raw escape planes swapped": [
+        ("if (w > 3) put_bit(esc, P * G + tau, o >> 3);",
+         "if (w > 3) put_bit(esc, P * G + tau, (w == 5) ? (o >> 4) : (o >> 3));"),
+        ("put_bit(esc, (P + 1) * G + tau, o >> 4);", "put_bit(esc, (P + 1) * G + tau, o >> 3);"),
+        ("if (w > 3) o |= get_bit(esc, P * G + tau) << 3;",
+         "if (w > 3) o |= get_bit(esc, P * G + tau) << ((w == 5) ? 4 : 3);"),
+        ("o |= get_bit(esc, (P + 1) * G + tau) << 4;", "o |= get_bit(esc, (P + 1) * G + tau) << 3;")],
+    "E4M3 sign/mantissa nibbles swapped": [("4L * n + b", "4L * (n ^ 1) + b")],
+    "E5M2 sign/mantissa as a plain stream": [("(W == 3) ? unit_bit(n, 3, b)", "(W == 3) ? 3L * n + b")],
+    "BF16 raw offset nibble bit order reversed": [("4L * tau + b, o >> (4 + b)", "4L * tau + (3 - b), o >> (4 + b)"),
+                                                  ("4L * tau + b) << (4 + b)", "4L * tau + (3 - b)) << (4 + b)")],
+    "BF16 raw offset nibbles as bit planes": [("4L * tau + b, o >> (4 + b)", "(long)b * G + tau, o >> (4 + b)"),
+                                              ("4L * tau + b) << (4 + b)", "(long)b * G + tau) << (4 + b)")],
+    "groups channel-major": [("int tg = q / D, c = q % D;", "int tg = q % (p->T / G), c = q / (p->T / G);")],
+    "tag planes swapped": [("in + L.tag_off;\n", "in + L.tag_off + L.plane_bytes;\n"),
+                           ("in + L.tag_off + L.plane_bytes;\n  const uint8_t* code",
+                            "in + L.tag_off;\n  const uint8_t* code"),
+                           ("out + L.tag_off;\n", "out + L.tag_off + L.plane_bytes;\n"),
+                           ("out + L.tag_off + L.plane_bytes;\n  uint8_t* code", "out + L.tag_off;\n  uint8_t* code")],
+    "code lanes and slots transposed": [("int k = r % 4, s = r / 4;", "int k = r / 8, s = r % 8;")],
+    "escape bit-3 plane reversed": [("P * G + tau, o >> 3", "P * G + (G - 1 - tau), o >> 3"),
+                                    ("get_bit(esc, P * G + tau) << 3", "get_bit(esc, P * G + (G - 1 - tau)) << 3")],
+}
+
+
+def _planted_lib(tmp_path, name, edits):
+    import ctypes
+    import subprocess
+    src = open(os.path.join(ROOT, "oracle", "kvc_oracle.c")).read()
+    for old, new in edits:
+        n = src.count(old)
+        assert n >= 1, f"planted edit not found: {old!r}"
+        src = src.replace(old, new)
+    c = tmp_path / "planted.c"
+    so = tmp_path / ("planted_%d.so" % abs(hash(name)))
+    c.write_text(src)
+    subprocess.check_call(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", str(c), "-o", str(so), "-lm"])
+    return ctypes.CDLL(str(so))
+
+
+@pytest.mark.parametrize("mistake", sorted(PLANTED))
+def test_goldens_catch_planted_layout_mistakes(orc, tmp_path, mistake):
+    import ctypes
+    lib = _planted_lib(tmp_path, mistake, PLANTED[mistake])
+    P = ctypes.POINTER
+    lib.orc_encode_tile.argtypes = [P(orc._Params), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_void_p, P(ctypes.c_int32), P(ctypes.c_int32), ctypes.c_void_p]
+    lib.orc_decode_tile.argtypes = [P(orc._Params), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    caught = []
+    for name in GOLDEN_TILES:
+        p, x, b3, b4, want, stride = _golden(orc, name)
+        x = np.ascontiguousarray(x)
+        out = np.zeros(max(stride, 4096), np.uint8)
+        isr, esc = ctypes.c_int32(), ctypes.c_int32()
+        modes = np.zeros(3, np.int32)
+        rc = lib.orc_encode_tile(ctypes.byref(p.c()), x.ctypes.data, b3.ctypes.data, b4.ctypes.data, 0,
+                                 out.ctypes.data, ctypes.byref(isr), ctypes.byref(esc), modes.ctypes.data)
+        assert rc == 0
+        # the planted copy still round-trips its own bytes: only the goldens can see the mistake
+        back = np.zeros_like(x)
+        assert lib.orc_decode_tile(ctypes.byref(p.c()), out.ctypes.data, isr.value, 0, b3.ctypes.data,
+                                   b4.ctypes.data, back.ctypes.data) == 0
+        assert np.array_equal(back, x)
+        if bytes(out[:stride]) != want:
+            caught.append(name)
+    assert caught, f"no golden tile detects: {mistake}"
 
 
 def test_raw_fallback_layout(orc):
