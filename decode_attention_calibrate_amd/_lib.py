@@ -14,6 +14,7 @@ BF16, FP8_E5M2, FP8_E4M3 = 0, 1, 2
 OK, EINVAL, ENOSLOT, EUNSUPPORTED, EHIP, ECORRUPT, ESTATE, ESMALLWS = 0, -1, -2, -3, -4, -5, -6, -7
 STATUS_COMP_EXHAUSTED, STATUS_RAW_EXHAUSTED, STATUS_MISSING_BLOCK, STATUS_CORRUPT = 1, 2, 4, 8
 NUM_BUFFERS = 8
+NOALLOC_WS_BYTES = 16 << 20  # KVC_NOALLOC_WS_BYTES
 BUFFER_NAMES = ("comp_pool", "raw_pool", "tail", "bases", "block_table", "comp_free", "raw_free", "counters")
 
 
@@ -53,6 +54,7 @@ SIGNATURES = {
     "kv_decode_attention": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, ctypes.c_float, _i32, _vp, _sz, _vp, _vp]),
     "kv_attention_partials": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, ctypes.c_float, _i32, _vp, _sz, _vp]),
     "kv_attention_combine": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, ctypes.c_float, _i32, _vp, _sz, _vp, _vp]),
+    "kv_decode_attention_noalloc": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, ctypes.c_float, _i32, _vp, _vp]),
     "kv_decode_step": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, _vp, _vp, ctypes.c_float, _i32, _vp, _sz, _vp, _vp]),
     "kv_release_seq": (ctypes.c_int, [_vp, _i32, _vp]),
     "kv_seq_length": (ctypes.c_int, [_vp, _i32, _P(_i32)]),

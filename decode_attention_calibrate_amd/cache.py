@@ -132,6 +132,17 @@ class KVCache:
                                              ws.numel(), _ptr(out), self._stream()))
         return out
 
+    def attention_noalloc(self, seq_ids, q: torch.Tensor, scale: float, n_splits: int, out: torch.Tensor) -> torch.Tensor:
+        """kv_decode_attention_noalloc: as attention(), with the split partials in the library's fixed
+        per-GPU workspace (no workspace argument; out must be given, so nothing is allocated)."""
+        n = len(seq_ids)
+        self._check_q(q, n)
+        self._check_out(out, n)
+        ids = (ctypes.c_int32 * n)(*seq_ids)
+        L.check(self.lib.kv_decode_attention_noalloc(self.handle, ids, n, _ptr(q), float(scale), n_splits, _ptr(out),
+                                                     self._stream()))
+        return out
+
     def _check_q(self, q: torch.Tensor, n: int):
         _elem(q, "q")
         if tuple(q.shape) != (n, self.Hq, self.D) or q.device != self.device:

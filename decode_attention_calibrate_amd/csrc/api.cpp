@@ -24,6 +24,7 @@ struct kvc_cache {
   std::vector<int32_t> len;  // tokens per sequence (host mirror)
   bool calibrated = false;
   long long blocks = 0;      // finished blocks over all sequences
+  void* noalloc_ws = nullptr;  // this device's fixed split workspace (kv_decode_attention_noalloc)
 };
 
 namespace {
@@ -221,6 +222,9 @@ int kv_cache_create(const kvc_params* params, const kvc_buffers* buffers, uint64
   }
   if (rc == KVC_OK) rc = hip_fail(kvc::launch_init(G, c->B, nullptr, nullptr, stream), "launch init");
   if (rc == KVC_OK) rc = hip_fail((int)hipStreamSynchronize(st), "synchronise");
+  // the fixed workspace of kv_decode_attention_noalloc on this (the current) device; a failure
+  // here is reported by that entry point, which resolves it again
+  if (rc == KVC_OK && kvc::noalloc_workspace(&c->noalloc_ws) != 0) c->noalloc_ws = nullptr;
   if (rc != KVC_OK) {
     delete c;
     return rc;
@@ -423,6 +427,21 @@ int kv_decode_attention(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seq
   const int rc = kv_attention_partials(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, stream);
   if (rc != KVC_OK) return rc;
   return kv_attention_combine(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, ws_dev, ws_bytes, out_dev, stream);
+}
+
+int kv_decode_attention_noalloc(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
+                                float scale, int32_t n_splits, void* out_dev, void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  if (n_seqs < 1 || n_splits < 1) return fail(KVC_EINVAL, "n_seqs and n_splits must be >= 1");
+  if (kv_attention_workspace_bytes(&c->p, n_seqs, n_splits) > (size_t)KVC_NOALLOC_WS_BYTES)
+    return fail(KVC_ESMALLWS, "n_seqs x n_splits needs more workspace than the fixed " +
+                                  std::to_string(KVC_NOALLOC_WS_BYTES) + " bytes of kv_decode_attention_noalloc");
+  if (!c->noalloc_ws) {
+    const int rc = hip_fail(kvc::noalloc_workspace(&c->noalloc_ws), "resolve the fixed workspace");
+    if (rc != KVC_OK) return rc;
+  }
+  return kv_decode_attention(c, seq_ids_host, n_seqs, q_dev, scale, n_splits, c->noalloc_ws, KVC_NOALLOC_WS_BYTES,
+                             out_dev, stream);
 }
 
 int kv_decode_step(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, const void* k_new_dev,

@@ -30,11 +30,13 @@
 
 #include <algorithm>
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
 
 #include <type_traits>
 
 #include "codec_dev.h"
+#include "kvc.h"
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -1186,6 +1188,33 @@ int launch_combine(const Geo& G, const DevBufs& B, const SeqList& S, const uint1
   const int ch = (G.D <= 128 && n_splits <= 4 * (kCombineThreads / (G.D / 4))) ? G.D : 16;
   hipLaunchKernelGGL(k, dim3(G.D / ch, G.Hq, S.n), dim3(kCombineThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
+}
+
+// ---- the split workspace of kv_decode_attention_noalloc -----------------------------------
+// A fixed array of device memory for callers that cannot allocate.  Each GPU the library runs
+// on holds its own copy (at its own address) until the process ends.  In host code the name
+// `scratch` is only a host-side stand-in: its device address comes from hipGetSymbolAddress,
+// resolved once per device with that device current, and only that address is ever passed on.
+static __device__ __align__(256) uint8_t scratch[KVC_NOALLOC_WS_BYTES];
+
+int noalloc_workspace(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 }  // namespace kvc

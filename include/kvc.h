@@ -216,6 +216,24 @@ int kv_decode_step(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs
                    const void* v_new_dev, const void* q_dev, float scale, int32_t n_splits, void* ws_dev,
                    size_t ws_bytes, void* out_dev, void* stream);
 
+/* Bytes of the fixed split workspace of kv_decode_attention_noalloc (per GPU). */
+#define KVC_NOALLOC_WS_BYTES (16u << 20)
+
+/* kv_decode_attention without a caller workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, checks and results as kv_decode_attention (bit for bit: the same kernels), except
+ * that the split partials go to a fixed array of KVC_NOALLOC_WS_BYTES inside the library; each
+ * GPU the library runs on holds its own copy until the process ends.  Returns KVC_ESMALLWS,
+ * with nothing enqueued, when kv_attention_workspace_bytes(params, n_seqs, n_splits) exceeds
+ * KVC_NOALLOC_WS_BYTES (with 32 query heads of 128 channels: n_seqs * n_splits <= 1008).  It
+ * calls no allocating routine; the array's device address is resolved by kv_cache_create on
+ * the device current at that time.  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's partials (each call writes every entry it reads, so nothing is cleared):
+ * calls ordered on one stream are safe, calls that overlap on one GPU (other streams or host
+ * threads without ordering between them) race and give wrong results. */
+int kv_decode_attention_noalloc(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
+                                float scale, int32_t n_splits, void* out_dev, void* stream);
+
 /* Returns every slot of a sequence to the free stacks and empties it (enqueued). */
 int kv_release_seq(kvc_cache* cache, int32_t seq, void* stream);
 
