@@ -200,7 +200,7 @@ __device__ __forceinline__ TileRef tile_ref(const AttnArgs& a, int seq, int L, i
   } else {
     r.kind = SRC_COMP;
     r.p = a.B.comp_pool + (size_t)slot * (uint32_t)a.G.stride;
-    r.escu = (int)((entry >> 24) & 0x7Fu);
+    r.escu = min((int)((entry >> 24) & 0x7Fu), a.G.esc_cap >> 4);  // never past the slot's escape area
   }
   return r;
 }
@@ -261,16 +261,27 @@ __device__ __forceinline__ void load_tile(const TileRef& r, int n, CRegs<NR, FMT
 }
 
 // Stage the escape bytes of this lane group's tile into its LDS area; return the exclusive
-// escape-unit prefix of tag word n (a wide group has 1 unit, a raw group F - 3).
+// escape-unit prefix of tag word n (a wide group has 1 unit, a raw group F - 3).  A tag word
+// whose groups would end past the escape units the table entry staged (corrupt tags) is
+// flagged (bad) and cleared, prefix 0: its groups rebuild as narrow and read unit 0 only.  The
+// prefix grows with n, so every later word of that tile is cleared too, and the words kept
+// read only staged units.
 template <int NR, int FMT>
-__device__ __forceinline__ uint32_t stage_escape(const CRegs<NR, FMT>& c, const TileRef& r, int n, uint8_t* esc_lds) {
+__device__ __forceinline__ uint32_t stage_escape(CRegs<NR, FMT>& c, const TileRef& r, int n, uint8_t* esc_lds,
+                                                 uint32_t& bad) {
   if (r.kind == SRC_COMP) {
     if (n < r.escu) *reinterpret_cast<uint4*>(esc_lds + 16 * n) = c.esc0;
     if (n + 16 < r.escu) *reinterpret_cast<uint4*>(esc_lds + 16 * (n + 16)) = c.esc1;
   }
   // escape units per group: wide 1, raw F - 3 (the E plane counts 1 for both)
   const uint32_t cnt = __popc(c.tE) + (uint32_t)(FmtT<FMT>::F - 4) * __popc(c.tR);
-  return row_scan16(cnt) - cnt;
+  const uint32_t incl = row_scan16(cnt);
+  if (r.kind == SRC_COMP && !esc_tags_fit(incl, (uint32_t)r.escu)) {
+    bad |= 1u;
+    c.tE = c.tR = 0u;
+    return 0u;
+  }
+  return incl - cnt;
 }
 
 // Escape spread table: entry v holds bit 3 set in byte k for every set bit k of v (the
@@ -307,13 +318,12 @@ __device__ __forceinline__ void rebuild_round(const CRegs<NR, FMT>& c, int i, in
   const uint32_t Ew = tw[0], Rw = tw[1], Pw = tw[2];
   bad |= Rw & ~Ew;
   if constexpr (FMT == 2) bad |= Ew & ~Rw;  // no wide mode in a 4-bit exponent field
-  const uint32_t P0 = Pw + __popc(Ew & below) + (uint32_t)(RU - 1) * __popc(Rw & below);
   const uint32_t e2 = __builtin_amdgcn_ubfe(Ew, 2 * n, 2), r2 = __builtin_amdgcn_ubfe(Rw, 2 * n, 2);
   const uint32_t W0 = c.cd[i][0], W1 = c.cd[i][1], W2 = c.cd[i][2];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const uint32_t E = (e2 >> gi) & 1u, R = (r2 >> gi) & 1u;
-    const uint32_t P = gi ? P0 + (e2 & 1u) + (uint32_t)(RU - 1) * (r2 & 1u) : P0;
+    const uint32_t P = esc_unit_of_group(Ew, Rw, Pw, below, e2, r2, gi, RU);
     // base in all four bytes: byte gi (b3) or 2 + gi (b4) of `bases`, 0 for a raw group
     const uint32_t sel = R ? 0x0C0C0C0Cu : E * 0x02020202u + (uint32_t)gi * 0x01010101u;
     const uint32_t H = perm_b32(0u, bases, sel);
@@ -331,10 +341,12 @@ __device__ __forceinline__ void rebuild_round(const CRegs<NR, FMT>& c, int i, in
     }
     if constexpr (FMT == 0) {
       if (R) {  // raw group (rare): base 0; offset bits 4..7 of each token go into its exponent byte
-        const uint2 hw = *reinterpret_cast<const uint2*>(esc16 + P + 1);  // four 16-bit units
+        // four 16-bit units P+1 .. P+4 (only 2-byte aligned in general: read one by one)
+        const uint32_t hx = (uint32_t)esc16[P + 1] | ((uint32_t)esc16[P + 2] << 16);
+        const uint32_t hy = (uint32_t)esc16[P + 3] | ((uint32_t)esc16[P + 4] << 16);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t u = q < 2 ? hw.x : hw.y;
+          const uint32_t u = q < 2 ? hx : hy;
           const uint32_t y = perm_b32(u, u, (q & 1) ? 0x03030202u : 0x01010000u);
           Evq[q] += ((y << 4) & 0x00F000F0u) | (y & 0xF000F000u);
         }
@@ -399,9 +411,16 @@ __device__ __forceinline__ float softmax_update(float s[16], float& m, float& l)
 
 template <int NR>
 __device__ __forceinline__ void rescale_acc(f32x4_t acc[NR][2], float alpha, int j) {
+  // lane 16j + n takes the factors of query heads 4j .. 4j+3 (lanes 4j + r): byte addresses
+  // (lane & 48) + 4r.  Formed here, on this rarely taken path, behind a volatile asm so that
+  // they are not hoisted out of the loop and kept live across it.
+  (void)j;
+  uint32_t base;
+  asm volatile("v_and_b32 %0, 48, %1" : "=v"(base) : "v"((uint32_t)threadIdx.x));
   float a[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) a[r] = __shfl(alpha, 4 * j + r);
+  for (int r = 0; r < 4; ++r)
+    a[r] = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(base + 4 * r), __float_as_int(alpha)));
 #pragma unroll
   for (int i = 0; i < NR; ++i)
 #pragma unroll
@@ -601,7 +620,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 
       // ---- K: rebuild into the LDS tile ----
       __syncthreads();
-      const uint32_t pfxK = stage_escape<NR, FMT>(cK, rK, n, esc_lds);
+      const uint32_t pfxK = stage_escape<NR, FMT>(cK, rK, n, esc_lds, bad);
       __syncthreads();
       if (rK.kind == SRC_COMP) {
         uint32_t tags[NR][3];
@@ -718,7 +737,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       phase_priority(2 * (ord.cnt - it) - 1);
       // ---- V: rebuild straight into B operands ----
       __syncthreads();
-      const uint32_t pfxV = stage_escape<NR, FMT>(cV, rV, n, esc_lds);
+      const uint32_t pfxV = stage_escape<NR, FMT>(cV, rV, n, esc_lds, bad);
       __syncthreads();
       uint32_t tagsV[NR][3];
       fetch_tags<NR, FMT>(cV, j, rV.tg, pfxV, tagsV);

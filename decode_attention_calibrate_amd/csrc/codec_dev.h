@@ -88,6 +88,25 @@ __device__ __forceinline__ uint32_t planes_before(uint32_t Ew, uint32_t Rw, uint
   return Pw + __popc(Ew & below) + 4u * __popc(Rw & below);
 }
 
+// Escape units (16-bit units of the tile's escape area) of the split attention's rebuild: a wide
+// group holds one, a raw group RU = F - 3.  For group 2n + gi of a tag word (E, R planes Ew, Rw)
+// whose earlier words hold Pw units: below = (1 << 2n) - 1, e2 / r2 = bits 2n, 2n+1 of Ew / Rw.
+// Returns the unit where the group's escape starts (its planes are units P .. P + RU - 1).
+__host__ __device__ inline uint32_t esc_unit_of_group(uint32_t Ew, uint32_t Rw, uint32_t Pw, uint32_t below, uint32_t e2,
+                                                      uint32_t r2, int gi, int RU) {
+  const uint32_t P0 = Pw + (uint32_t)__builtin_popcount(Ew & below) + (uint32_t)(RU - 1) * (uint32_t)__builtin_popcount(Rw & below);
+  return gi ? P0 + (e2 & 1u) + (uint32_t)(RU - 1) * (r2 & 1u) : P0;
+}
+
+// Whether the groups of a tag word may read their escape: units_through is the escape units of
+// this word and every earlier word of the tile (16 tokens per group; a wide group 1, a raw group
+// RU), esc_pieces the 16-byte pieces (8 units each) the tile's table entry says are stored.  A
+// word that does not fit (corrupt tags) is rebuilt as narrow; by esc_unit_of_group every group
+// of a word that fits ends at or before units_through, inside the stored pieces.
+__host__ __device__ inline bool esc_tags_fit(uint32_t units_through, uint32_t esc_pieces) {
+  return units_through <= 8u * esc_pieces;
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN

@@ -645,6 +645,7 @@ __device__ void decode_tile_any(const Geo& G, const DevBufs& B, const uint8_t* t
   }
   int total;
   int P = block_exclusive_scan(cnt, red, &total);
+  if (tid == 0 && (long)total * G.GT > 8L * G.esc_cap) atomicOr(&B.counters->status, 8u);  // escape overrun
   for (int q = q0; q < min(G.NG, q0 + per); ++q) {
     gP[q] = (uint16_t)P;
     P += mode_planes(G, gm[q]);
@@ -695,7 +696,10 @@ struct TileMeta {
 // tl / nt: this thread's index among the nt threads staging the tile (the whole block, or one
 // half of it when two tiles are staged at once); every thread of the block reaches the
 // barriers, `active` false for threads with no tile to stage.
-__device__ void stage_tile_meta(const Geo& G, const uint8_t* tile, TileMeta& m, int tl, int nt, bool active) {
+// A tile whose tags claim more escape bits than the escape capacity holds is corrupt: flagged
+// (status bit 8); its reads past the capacity are clamped by the decoders.
+__device__ void stage_tile_meta(const Geo& G, const DevBufs& B, const uint8_t* tile, TileMeta& m, int tl, int nt,
+                                bool active) {
   const uint32_t* tag_g = reinterpret_cast<const uint32_t*>(tile + G.tag_off);
   const uint32_t* esc_g = reinterpret_cast<const uint32_t*>(tile + G.esc_off);
   if (active) {
@@ -709,6 +713,7 @@ __device__ void stage_tile_meta(const Geo& G, const uint8_t* tile, TileMeta& m, 
       m.pre[i] = acc;
       acc += __popc(m.tag[i]) + (uint32_t)(G.F - 4) * __popc(m.tag[G.PW + i]);
     }
+    if (acc * (uint32_t)G.GT > 8u * (uint32_t)G.esc_cap) atomicOr(&B.counters->status, 8u);  // escape overrun
   }
   __syncthreads();
 }
@@ -737,7 +742,7 @@ template <class Put4>
 __device__ void decode_bf16_g8_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
                                     const uint8_t* b4, TileMeta& m, Put4 put4, int tl, int nt, bool active) {
   const int D = G.D;
-  stage_tile_meta(G, tile, m, tl, nt, active);
+  stage_tile_meta(G, B, tile, m, tl, nt, active);
   const uint8_t* esc = reinterpret_cast<const uint8_t*>(m.esc);
   const int n_units = active ? G.raw_elems / 32 : 0;
   for (int u = tl; u < n_units; u += nt) {
@@ -829,7 +834,7 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
   }
   uint16_t* out = reinterpret_cast<uint16_t*>(outv);
   auto out_at = [&](int t, int c) -> uint16_t* { return out + out_idx(t, c); };
-  stage_tile_meta(G, tile, meta, tid, kThreads, true);
+  stage_tile_meta(G, B, tile, meta, tid, kThreads, true);
   const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(meta.esc);
   const uint8_t* b3 = B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
   const uint8_t* b4 = B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;

@@ -45,7 +45,7 @@ def row_rel_err(out_bits: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.max(np.abs(o - r), axis=1) / np.max(np.abs(r), axis=1)))
 
 
-def gpu_tile_bytes(cache, seq, blk, kv, h):
+def gpu_tile_bytes(cache, seq, blk, kv, h):  # one tile; compare_tiles reads many at once
     """(is_raw, esc_units, bytes) of one finished tile as the GPU stored it."""
     e = int(cache.table()[((seq * cache.params.max_blocks_per_seq + blk) * 2 + kv) * cache.Hkv + h].item()) & 0xFFFFFFFF
     assert e != 0xFFFFFFFF, "unallocated tile"
@@ -70,6 +70,24 @@ def oracle_layer(p: oracle.Params, Hkv: int, k_cal: np.ndarray, v_cal: np.ndarra
     return bases, seqs
 
 
+def _stored_tiles(cache, jobs):
+    """(is_raw, esc_units, bytes) per (seq, blk, kv, h) job as the GPU stored them: the table is
+    read once and the slots are gathered on the device, so large samples cost one copy."""
+    tab = cache.table().cpu().numpy().view(np.uint32)
+    Hkv, MB = cache.Hkv, cache.params.max_blocks_per_seq
+    ent = np.array([tab[((sid * MB + b) * 2 + kv) * Hkv + h] for sid, b, kv, h in jobs], np.uint32)
+    assert (ent != 0xFFFFFFFF).all(), "unallocated tile"
+    raw = (ent >> 31).astype(bool)
+    slot = torch.from_numpy((ent & 0xFFFFFF).astype(np.int64)).cuda()
+    n_raw = cache.T * cache.D * cache.EB
+    comp = cache.buffers["comp_pool"].view(-1, cache.slot_stride) if cache.compressed else None
+    rawp = cache.buffers["raw_pool"][: (cache.buffers["raw_pool"].numel() // n_raw) * n_raw].view(-1, n_raw)
+    rb = torch.from_numpy(raw).cuda()
+    got_c = comp[torch.where(rb, torch.zeros_like(slot), slot)].cpu().numpy() if comp is not None else None
+    got_r = rawp[torch.where(rb, slot, torch.zeros_like(slot))].cpu().numpy()
+    return [(bool(raw[i]), int((ent[i] >> 24) & 0x7F), got_r[i] if raw[i] else got_c[i]) for i in range(len(jobs))]
+
+
 def compare_tiles(cache, p: oracle.Params, oseqs, seq_ids, sample=None, rng=None):
     """Every (or a sample of) finished tiles: GPU bytes == oracle bytes, same storage form and
     escape length.  Returns the number of tiles compared."""
@@ -83,12 +101,13 @@ def compare_tiles(cache, p: oracle.Params, oseqs, seq_ids, sample=None, rng=None
     if sample is not None and len(jobs) > sample:
         idx = (rng or np.random.default_rng(0)).choice(len(jobs), sample, replace=False)
         jobs = [jobs[i] for i in sorted(idx)]
-    for sid, s, b, kv, h in jobs:
-        raw, units, got = gpu_tile_bytes(cache, sid, b, kv, h)
+    stored = _stored_tiles(cache, [(sid, b, kv, h) for sid, s, b, kv, h in jobs])
+    for (sid, s, b, kv, h), (raw, units, got) in zip(jobs, stored):
         t = s.tiles[b]
         assert raw == bool(t["is_raw"][kv, h]), (sid, b, kv, h)
         if raw:
             want = t["data"][kv, h][:lay["raw_bytes"]]
+            got = got[:lay["raw_bytes"]]
         else:
             want = t["data"][kv, h][:lay["stride"]]
             assert units == (int(t["esc"][kv, h]) + 15) // 16, (sid, b, kv, h)
@@ -96,4 +115,35 @@ def compare_tiles(cache, p: oracle.Params, oseqs, seq_ids, sample=None, rng=None
             diff = np.nonzero(got != want)[0]
             raise AssertionError(f"tile seq={sid} blk={b} kv={kv} h={h} raw={raw}: {diff.size} bytes differ, "
                                  f"first at {diff[:8].tolist()}")
+    return len(jobs)
+
+
+def compare_sampled_tiles(cache, p: oracle.Params, bases, toks, n_sample: int, rng):
+    """n_sample finished tiles drawn over all sequences: GPU bytes == the oracle's encoding of the
+    same tokens with the same bases (only the sampled tiles are encoded by the oracle)."""
+    lay = oracle.layout(p)
+    b3, b4 = bases
+    jobs = []
+    per_seq = [k.shape[0] // p.T for k, _ in toks]
+    total = sum(per_seq) * 2 * cache.Hkv
+    for i in sorted(rng.choice(total, n_sample, replace=False)):
+        h = i % cache.Hkv
+        kv = (i // cache.Hkv) % 2
+        blk = i // (2 * cache.Hkv)
+        sid = 0
+        while blk >= per_seq[sid]:
+            blk -= per_seq[sid]
+            sid += 1
+        jobs.append((sid, blk, kv, h))
+    tiles = np.stack([toks[sid][kv][blk * p.T:(blk + 1) * p.T, h] for sid, blk, kv, h in jobs])
+    data, is_raw, esc, _ = oracle.encode_tiles(p, tiles, np.stack([b3[kv, h] for _, _, kv, h in jobs]),
+                                               np.stack([b4[kv, h] for _, _, kv, h in jobs]),
+                                               np.array([kv for _, _, kv, _ in jobs], np.int32))
+    for n, ((sid, blk, kv, h), (raw, units, got)) in enumerate(zip(jobs, _stored_tiles(cache, jobs))):
+        assert raw == bool(is_raw[n]), (sid, blk, kv, h)
+        size = lay["raw_bytes"] if raw else lay["stride"]
+        if not raw:
+            assert units == (int(esc[n]) + 15) // 16, (sid, blk, kv, h)
+        if not np.array_equal(got[:size], data[n, :size]):
+            raise AssertionError(f"tile seq={sid} blk={blk} kv={kv} h={h} raw={raw} differs from the oracle")
     return len(jobs)

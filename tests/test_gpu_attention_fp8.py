@@ -118,18 +118,17 @@ def test_fp8_paged_t16_permuted_pool(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_fp8_full_context_sampled_heads(fmt):
+def test_fp8_full_context_all_heads(fmt):
     """The 64K-token layer in FP8 (compressed and uncompressed) at the benchmark's split count,
-    checked on sampled query heads."""
+    all 32 query heads against the oracle."""
     cfg = synth.config(4, fmt)
     g, toks = synth.sequence_tokens(cfg)
     q = synth.queries(cfg)
-    heads = [0, 5, 13, 31]
-    ref = _oracle(cfg, toks, q, heads)
+    ref = _oracle(cfg, toks, q)
     for compressed in (True, False):
         cache = _fill(cfg, toks, compressed)
         out = host(cache.attention([0], dev(q), cfg.scale, 256))
-        assert row_rel_err(out[:, heads], ref) <= TOL, compressed
+        assert row_rel_err(out, ref) <= TOL, compressed
         del cache
         torch.cuda.empty_cache()
 
