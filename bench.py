@@ -430,7 +430,7 @@ def codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, q, n_splits, reps=5
         payload = (2 * TD // Gt + 3 * TD + 8 * TD) // 8  # TAG + CODE + SM of a compressed tile
         stored = st["comp_tiles"] * payload + st["esc_bytes"] + st["raw_tiles"] * TD * 2
         tiles = st["comp_tiles"] + st["raw_tiles"]
-        groups = st["groups"]
+        groups = st["groups"][:3]  # FORMAT v1: narrow, wide, raw
         res[f"g{Gt}"] = {
             "codec_ratio": round(tiles * TD * 2 / stored, 4),
             "resident_ratio": round(tiles * TD * 2 / (st["comp_tiles"] * c.slot_stride + st["raw_tiles"] * TD * 2 + 4 * tiles), 4),

@@ -21,7 +21,7 @@ BUFFER_NAMES = ("comp_pool", "raw_pool", "tail", "bases", "block_table", "comp_f
 class Params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "dtype", "num_kv_heads", "num_q_heads", "head_dim", "block_tokens", "group_tokens", "esc_cap_bytes",
-        "compressed", "max_seqs", "max_blocks_per_seq", "num_comp_slots", "num_raw_slots")]
+        "compressed", "max_seqs", "max_blocks_per_seq", "num_comp_slots", "num_raw_slots", "mode_set")]
 
 
 class Buffers(ctypes.Structure):
@@ -29,7 +29,7 @@ class Buffers(ctypes.Structure):
 
 
 class Stats(ctypes.Structure):
-    _fields_ = [("comp_tiles", ctypes.c_uint64), ("raw_tiles", ctypes.c_uint64), ("groups", ctypes.c_uint64 * 3),
+    _fields_ = [("comp_tiles", ctypes.c_uint64), ("raw_tiles", ctypes.c_uint64), ("groups", ctypes.c_uint64 * 4),
                 ("esc_bytes", ctypes.c_uint64), ("comp_free", ctypes.c_int32), ("raw_free", ctypes.c_int32)]
 
 

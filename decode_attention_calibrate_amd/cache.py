@@ -28,13 +28,15 @@ class KVCache:
     def __init__(self, *, num_kv_heads: int, num_q_heads: int, head_dim: int, block_tokens: int,
                  max_seqs: int, max_blocks_per_seq: int, num_comp_slots: int, num_raw_slots: int,
                  compressed: bool = True, group_tokens: int = 16, esc_cap_bytes: int = -1, dtype: int = L.BF16,
-                 device: str | torch.device = "cuda", perm_seed: int = 0):
+                 device: str | torch.device = "cuda", perm_seed: int = 0, mode_set: int = 0):
         self.lib = L.load()
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self.params = L.Params(dtype, num_kv_heads, num_q_heads, head_dim, block_tokens, group_tokens, esc_cap_bytes,
-                               1 if compressed else 0, max_seqs, max_blocks_per_seq, num_comp_slots, num_raw_slots)
+                               1 if compressed else 0, max_seqs, max_blocks_per_seq, num_comp_slots, num_raw_slots,
+                               mode_set)
+        self.mode_set = mode_set
         sizes = (ctypes.c_size_t * L.NUM_BUFFERS)()
         stride = ctypes.c_size_t()
         L.check(self.lib.kv_buffer_sizes(ctypes.byref(self.params), sizes, ctypes.byref(stride)))
@@ -211,3 +213,8 @@ class KVCache:
 
     def bases(self) -> torch.Tensor:
         return self.buffers["bases"][: 4 * self.Hkv * self.D].view(2, 2, self.Hkv, self.D)
+
+    def bases2(self) -> torch.Tensor:
+        """The 2-bit-window bases of mode set 1, [2 (K, V)][Hkv][D]."""
+        n = 4 * self.Hkv * self.D
+        return self.buffers["bases"][n: n + 2 * self.Hkv * self.D].view(2, self.Hkv, self.D)

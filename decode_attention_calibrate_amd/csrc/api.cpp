@@ -71,6 +71,9 @@ int check_params(const kvc_params* p) {
   if (p->block_tokens != 16 && p->block_tokens != 32 && p->block_tokens != 64)
     return fail(KVC_EUNSUPPORTED, "these kernels implement block_tokens 16, 32 or 64");
   if (cap > 512) return fail(KVC_EUNSUPPORTED, "these kernels implement esc_cap_bytes <= 512");
+  if (p->mode_set < 0 || p->mode_set > 3) return fail(KVC_EINVAL, "mode_set must be 0, 1, 2 or 3");
+  if (p->mode_set != 0 && (p->dtype != KVC_BF16 || p->head_dim > 128))
+    return fail(KVC_EUNSUPPORTED, "FORMAT v2 mode sets are implemented for BF16 caches with head_dim <= 128");
   return KVC_OK;
 }
 
@@ -109,6 +112,18 @@ Geo make_geo(const kvc_params& p) {
   G.n_comp = p.compressed ? p.num_comp_slots : 0;
   G.n_raw = p.num_raw_slots;
   G.compressed = p.compressed;
+  G.mode_set = p.mode_set;
+  if (p.mode_set != 0) {  // FORMAT v2: TAG | SM | CODES (each group's offsets at its mode's width)
+    static const int widths[4][4] = {{3, 4, 8, 0}, {2, 3, 4, 8}, {4, 8, 0, 0}, {3, 4, 8, 0}};
+    static const int counts[4] = {3, 4, 2, 3};
+    G.n_modes = counts[p.mode_set];
+    for (int k = 0; k < 4; ++k) G.mw[k] = widths[p.mode_set][k];
+    G.sm_off = align16(2 * G.PW * 4);
+    G.code_off = G.sm_off + align16(G.T * G.D);
+    G.code_cap = G.T * G.D * std::max(3, G.mw[0]) / 8 + G.esc_cap;
+    G.stride = G.code_off + align16(G.code_cap);
+    G.esc_off = G.code_off;
+  }
   return G;
 }
 
@@ -116,7 +131,7 @@ void sizes_of(const kvc_params& p, const Geo& G, size_t out[KVC_NUM_BUFFERS]) {
   out[0] = (size_t)G.n_comp * G.stride;
   out[1] = (size_t)G.n_raw * G.raw_elems * G.EB;
   out[2] = (size_t)p.max_seqs * 2 * G.Hkv * G.raw_elems * G.EB;
-  out[3] = (size_t)4 * G.Hkv * G.D;
+  out[3] = (size_t)(p.mode_set == 1 ? 6 : 4) * G.Hkv * G.D;
   out[4] = (size_t)p.max_seqs * p.max_blocks_per_seq * 2 * G.Hkv * 4;
   out[5] = (size_t)G.n_comp * 4;
   out[6] = (size_t)G.n_raw * 4;
@@ -368,9 +383,10 @@ static int run_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seq
       if (rc != KVC_OK) return rc;
       continue;
     }
-    // compressed caches with 8-token groups take the LDS-rebuild kernel; everything else the
-    // register-rebuild split kernels
-    auto launch = (G.compressed && G.GT != kvc::kGroup) ? kvc::launch_attention_any : kvc::launch_attention_partials;
+    // compressed caches with 8-token groups or in FORMAT v2 take the LDS-rebuild kernel;
+    // everything else the register-rebuild split kernels
+    auto launch = (G.compressed && (G.GT != kvc::kGroup || G.mode_set != 0)) ? kvc::launch_attention_any
+                                                                               : kvc::launch_attention_partials;
     rc = hip_fail(launch(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale, n_splits,
                          acc + (size_t)s0 * G.Hq * n_splits * G.D, ml + (size_t)s0 * hq * n_splits * 2,
                          k_new_dev ? (const uint8_t*)k_new_dev + (size_t)s0 * row : nullptr,
@@ -513,11 +529,11 @@ int kv_get_status(kvc_cache* c, uint32_t* flags, kvc_stats* stats, void* stream)
     *stats = kvc_stats{};
     for (const kvc::StatStripe& st : h.stat) {
       stats->raw_tiles += st.raw_tiles;
-      for (int i = 0; i < 3; ++i) stats->groups[i] += st.groups[i];
+      for (int i = 0; i < 4; ++i) stats->groups[i] += st.groups[i];
       stats->esc_bytes += st.esc_bytes;
     }
     // every compressed tile adds exactly NG groups
-    stats->comp_tiles = (stats->groups[0] + stats->groups[1] + stats->groups[2]) / (uint64_t)c->G.NG;
+    stats->comp_tiles = (stats->groups[0] + stats->groups[1] + stats->groups[2] + stats->groups[3]) / (uint64_t)c->G.NG;
     stats->comp_free = stats->raw_free = 0;
     for (int s = 0; s < kvc::kPoolStripes; ++s) {
       stats->comp_free += h.comp_top[s].n;

@@ -72,7 +72,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total)
 
 __global__ void init_kernel(Geo G, DevBufs B) {
   const size_t n_table = (size_t)G.max_seqs * G.max_blocks * 2 * G.Hkv;
-  const size_t n_bases = (size_t)4 * G.Hkv * G.D;
+  const size_t n_bases = (size_t)(G.mode_set == 1 ? 6 : 4) * G.Hkv * G.D;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_table; i += stride) B.table[i] = kUnallocated;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_bases; i += stride) B.bases[i] = 0;
@@ -85,7 +85,7 @@ __global__ void init_kernel(Geo G, DevBufs B) {
   if (blockIdx.x == 0 && threadIdx.x < kStatStripes) {
     StatStripe& st = B.counters->stat[threadIdx.x];
     st.raw_tiles = 0;
-    st.groups[0] = st.groups[1] = st.groups[2] = 0;
+    st.groups[0] = st.groups[1] = st.groups[2] = st.groups[3] = 0;
     st.esc_bytes = 0;
   }
 }
@@ -93,7 +93,7 @@ __global__ void init_kernel(Geo G, DevBufs B) {
 // One block per (channel, kv-head, K|V): histogram of the F-bit exponent field over the
 // calibration tokens, then the 8- and 16-wide windows with the largest count (ties: lower median
 // start).  A format whose exponent field is only 4 bits wide (E4M3) has no 16-wide window; its
-// b4 stays 0.
+// b4 stays 0.  Mode set 1 (a 2-bit mode) also takes the 4-wide window, stored after b3 and b4.
 __global__ void calibrate_kernel(Geo G, DevBufs B, const void* __restrict__ k, const void* __restrict__ v, int n) {
   __shared__ int hist[256];
   __shared__ int red[8];
@@ -103,7 +103,7 @@ __global__ void calibrate_kernel(Geo G, DevBufs B, const void* __restrict__ k, c
   const void* src = kv ? v : k;
   for (int t = tid; t < n; t += kThreads) atomicAdd(&hist[exp_of(G, elem_at(src, ((size_t)t * G.Hkv + h) * G.D + c, G.EB))], 1);
   __syncthreads();
-  for (int w = 3; w <= 4 && w < G.F; ++w) {
+  for (int w = G.mode_set == 1 ? 2 : 3; w <= 4 && w < G.F; ++w) {
     const int width = 1 << w, nb = (1 << G.F) - width + 1;
     int cov = -1;
     if (tid < nb) {
@@ -114,7 +114,11 @@ __global__ void calibrate_kernel(Geo G, DevBufs B, const void* __restrict__ k, c
     const int flag = (tid < nb && cov == best) ? 1 : 0;
     int count;
     const int rank = block_exclusive_scan(flag, red, &count);
-    if (flag && rank == (count - 1) / 2) B.bases[(((size_t)kv * 2 + (w - 3)) * G.Hkv + h) * G.D + c] = (uint8_t)tid;
+    if (flag && rank == (count - 1) / 2) {
+      const size_t at = w == 2 ? (size_t)4 * G.Hkv * G.D + ((size_t)kv * G.Hkv + h) * G.D + c
+                               : (((size_t)kv * 2 + (w - 3)) * G.Hkv + h) * G.D + c;
+      B.bases[at] = (uint8_t)tid;
+    }
     __syncthreads();
   }
 }
@@ -219,7 +223,7 @@ __device__ int pop_from(PoolTop* top, const int32_t* stack, int s0) {
   return -1;
 }
 
-__device__ int pop_slot(const DevBufs& B, int want_raw, const unsigned long long modes[3], int esc_bytes, int* raw_out) {
+__device__ int pop_slot(const DevBufs& B, int want_raw, const unsigned long long modes[4], int esc_bytes, int* raw_out) {
   Counters* C = B.counters;
   const int h = blockIdx.x + 7 * blockIdx.y + 3 * blockIdx.z;  // spreads workgroups over the stripes
   int slot = -1, raw = want_raw;
@@ -242,6 +246,7 @@ __device__ int pop_slot(const DevBufs& B, int want_raw, const unsigned long long
       atomicAdd(&st.groups[0], modes[0]);
       atomicAdd(&st.groups[1], modes[1]);
       atomicAdd(&st.groups[2], modes[2]);
+      if (modes[3]) atomicAdd(&st.groups[3], modes[3]);
       atomicAdd(&st.esc_bytes, (unsigned long long)esc_bytes);
     }
   }
@@ -297,7 +302,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
   uint32_t* tagw = smem + (G.raw_elems / 2);                            // [2][PW]
   __shared__ int red[8];
   __shared__ int sh_slot, sh_raw;
-  __shared__ unsigned long long sh_modes[3];
+  __shared__ unsigned long long sh_modes[4];
 
   const int si = blockIdx.y, kv = blockIdx.z / G.Hkv, h = blockIdx.z % G.Hkv;
   const int seq = S.ids[si], L0 = S.lens[si];
@@ -338,6 +343,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
       const int s = block_sum(cnt[m], red);
       if (tid == 0) sh_modes[m] = (unsigned long long)s;
     }
+    if (tid == 0) sh_modes[3] = 0;
   }
 
   if (tid == 0) sh_slot = pop_slot(B, is_raw, sh_modes, 2 * total, &sh_raw);
@@ -461,7 +467,7 @@ __global__ void __launch_bounds__(kThreads) encode_any_kernel(Geo G, DevBufs B, 
   uint8_t* gm = reinterpret_cast<uint8_t*>(gP + G.NG);                        // [NG] group modes
   __shared__ int red[8];
   __shared__ int sh_slot, sh_raw;
-  __shared__ unsigned long long sh_modes[3];
+  __shared__ unsigned long long sh_modes[4];
 
   const int si = blockIdx.y, kv = blockIdx.z / G.Hkv, h = blockIdx.z % G.Hkv;
   const int seq = S.ids[si], L0 = S.lens[si];
@@ -505,6 +511,7 @@ __global__ void __launch_bounds__(kThreads) encode_any_kernel(Geo G, DevBufs B, 
     const int sm = block_sum(cnt[m], red);
     if (tid == 0) sh_modes[m] = (unsigned long long)sm;
   }
+  if (tid == 0) sh_modes[3] = 0;
   if (tid == 0) sh_slot = pop_slot(B, (!G.compressed || esc_bytes > G.esc_cap) ? 1 : 0, sh_modes, esc_bytes, &sh_raw);
   __syncthreads();
   const int slot = sh_slot, raw = sh_raw;
@@ -582,6 +589,114 @@ __global__ void __launch_bounds__(kThreads) encode_any_kernel(Geo G, DevBufs B, 
   const uint4* src = reinterpret_cast<const uint4*>(slotw);
   for (int i = tid; i < G.stride / 16; i += kThreads) dst[i] = src[i];
   if (tid == 0) B.table[entry_idx] = (uint32_t)slot | ((uint32_t)((esc_bytes + 15) >> 4) << 24);
+}
+
+// FORMAT v2 (the nested precision modes of GAAC page §4.7.2; BF16): one 256-thread workgroup per
+// new tile, as encode_any_kernel.  Each group takes the first mode of the set whose calibrated
+// window holds its exponents; a block scan of the groups' code bits gives every group's offset
+// in the CODES stream; the slot is assembled in LDS (TAG planes = bits 0 and 1 of the mode
+// index, SM bytes, the codes of four tokens at a time OR-ed in at their stream position), then
+// copied out whole.  A tile whose codes exceed the capacity is stored raw.
+__device__ __forceinline__ uint32_t v2_base(const Geo& G, int k, const uint8_t* b2, const uint8_t* b3,
+                                            const uint8_t* b4, int c) {
+  const int w = G.mw[k];
+  return k == G.n_modes - 1 ? 0u : (w == 2 ? b2[c] : (w == 3 ? b3[c] : b4[c]));
+}
+
+__global__ void __launch_bounds__(kThreads) encode_v2_kernel(Geo G, DevBufs B, SeqList S, const void* __restrict__ kin,
+                                                             const void* __restrict__ vin, int n_tok) {
+  extern __shared__ uint32_t smem[];
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);                  // [T][D] logical
+  uint32_t* slotw = smem + G.raw_elems / 2;                             // the slot, stride bytes
+  uint32_t* gO = slotw + G.stride / 4;                                  // [NG] code bit offset of q
+  uint8_t* gk = reinterpret_cast<uint8_t*>(gO + G.NG);                  // [NG] mode index of q
+  __shared__ int red[8];
+  __shared__ int sh_slot, sh_raw;
+  __shared__ unsigned long long sh_modes[4];
+
+  const int si = blockIdx.y, kv = blockIdx.z / G.Hkv, h = blockIdx.z % G.Hkv;
+  const int seq = S.ids[si], L0 = S.lens[si];
+  const int first_blk = L0 / G.T, last_full = (L0 + n_tok) / G.T;
+  const int b = first_blk + blockIdx.x;
+  if (b >= last_full) return;
+  const int tid = threadIdx.x, D = G.D, GT = G.GT, NG = G.NG;
+  const uint8_t* tail = reinterpret_cast<const uint8_t*>(B.tail) + tail_offset(G, seq, kv, h) * 2;
+  gather_block<2>(G, tail, kv ? vin : kin, si, h, kv, b, L0, n_tok, first_blk * G.T, tile);
+  for (int i = tid; i < G.stride / 4; i += kThreads) slotw[i] = 0u;
+  __syncthreads();
+
+  const uint8_t* b3 = B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
+  const uint8_t* b4 = B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;
+  const uint8_t* b2 = B.bases + (size_t)4 * G.Hkv * D + ((size_t)kv * G.Hkv + h) * D;  // mode set 1 only
+  const int per = (NG + kThreads - 1) / kThreads, q0 = min(NG, tid * per), q1 = min(NG, q0 + per);
+  int bits = 0, cnt[4] = {0, 0, 0, 0};
+  if (G.compressed) {
+    for (int q = q0; q < q1; ++q) {
+      const int tg = q / D, c = q % D;
+      uint32_t mn = 255, mx = 0;
+      for (int tau = 0; tau < GT; ++tau) {
+        const uint32_t e = exp_of(G, tile[(tg * GT + tau) * D + c]);
+        mn = min(mn, e);
+        mx = max(mx, e);
+      }
+      int k = G.n_modes - 1;
+      for (int j = 0; j < G.n_modes - 1; ++j) {
+        const uint32_t base = v2_base(G, j, b2, b3, b4, c);
+        if (base <= mn && mx <= base + (1u << G.mw[j]) - 1u) { k = j; break; }
+      }
+      gk[q] = (uint8_t)k;
+      cnt[k]++;
+      bits += GT * G.mw[k];
+    }
+  }
+  int total;
+  int O = block_exclusive_scan(bits, red, &total);
+  for (int q = q0; q < q1 && G.compressed; ++q) {
+    gO[q] = (uint32_t)O;
+    O += GT * G.mw[gk[q]];
+  }
+  const int used = (total + 7) / 8;
+  for (int m = 0; m < 4; ++m) {
+    const int sm = block_sum(cnt[m], red);
+    if (tid == 0) sh_modes[m] = (unsigned long long)sm;
+  }
+  if (tid == 0) sh_slot = pop_slot(B, (!G.compressed || used > G.code_cap) ? 1 : 0, sh_modes, used, &sh_raw);
+  __syncthreads();
+  const int slot = sh_slot, raw = sh_raw;
+  const size_t entry_idx = table_index(G, seq, b, kv, h);
+  if (slot < 0) {
+    if (tid == 0) B.table[entry_idx] = kUnallocated;
+    return;
+  }
+  if (raw) {
+    store_raw_tile(G, B, slot, kv, tile, entry_idx);
+    return;
+  }
+  // four consecutive tokens of one group per step: their codes are 4w consecutive stream bits
+  const int code_bit0 = 8 * G.code_off;
+  for (int k4 = tid; k4 < G.raw_elems / 4; k4 += kThreads) {
+    const int n0 = 4 * k4, q = n0 / GT, tau0 = n0 % GT, tg = q / D, c = q % D;
+    const int k = gk[q], w = G.mw[k];
+    const uint32_t base = v2_base(G, k, b2, b3, b4, c);
+    uint32_t cf = 0, sf = 0;
+#pragma unroll
+    for (int lk = 0; lk < 4; ++lk) {
+      const uint32_t x = tile[(tg * GT + tau0 + lk) * D + c];
+      cf |= (exp_of(G, x) - base) << (w * lk);
+      sf |= sm_of(G, x) << (8 * lk);
+    }
+    or_bits(slotw, code_bit0 + (int)gO[q] + tau0 * w, cf, 4 * w);
+    slotw[(G.sm_off + n0) / 4] = sf;
+    if (tau0 == 0) {
+      if (k & 1) atomicOr(&slotw[G.tag_off / 4 + (q >> 5)], 1u << (q & 31));
+      if (k & 2) atomicOr(&slotw[G.tag_off / 4 + G.PW + (q >> 5)], 1u << (q & 31));
+    }
+  }
+  __syncthreads();
+  uint4* dst = reinterpret_cast<uint4*>(B.comp_pool + (size_t)slot * G.stride);
+  const uint4* src = reinterpret_cast<const uint4*>(slotw);
+  for (int i = tid; i < G.stride / 16; i += kThreads) dst[i] = src[i];
+  if (tid == 0) B.table[entry_idx] = (uint32_t)slot;
 }
 
 // Writes the appended tokens that do not complete a block into the sequence's tail.
@@ -682,6 +797,64 @@ __device__ void decode_tile_any(const Geo& G, const DevBufs& B, const uint8_t* t
     const uint32_t x = ((f >> G.MB) << (G.F + G.MB)) | (e << G.MB) | (f & ((1u << G.MB) - 1u));
     put(t, c, x);
   }
+}
+
+// FORMAT v2 tile (BF16), one element at a time: every group's mode index from the two tag
+// planes and, by a block scan of their code bits, its offset in the CODES stream (in LDS); then
+// each thread rebuilds elements from their w-bit code and sign/mantissa byte and hands element
+// (t, c) to put(t, c, bits).  Corrupt tiles (a mode index outside the set, codes past the
+// capacity, an exponent past 8 bits) set status bit 8; every read stays inside the slot: the
+// mode index is clamped to the set and code reads past the capacity return 0.
+template <class Put>
+__device__ void decode_tile_v2(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b2,
+                               const uint8_t* b3, const uint8_t* b4, Put put) {
+  __shared__ uint32_t gO[1024];
+  __shared__ uint8_t gk[1024];
+  __shared__ int red[8];
+  const int tid = threadIdx.x, D = G.D, GT = G.GT;
+  const uint32_t* tag0 = reinterpret_cast<const uint32_t*>(tile + G.tag_off);
+  const uint32_t* tag1 = tag0 + G.PW;
+  const int per = (G.NG + kThreads - 1) / kThreads, q0 = min(G.NG, tid * per), q1 = min(G.NG, q0 + per);
+  int bits = 0;
+  bool bad = false;
+  for (int q = q0; q < q1; ++q) {
+    int k = (int)(((tag0[q >> 5] >> (q & 31)) & 1u) | (((tag1[q >> 5] >> (q & 31)) & 1u) << 1));
+    if (k >= G.n_modes) {
+      bad = true;
+      k = G.n_modes - 1;
+    }
+    gk[q] = (uint8_t)k;
+    bits += GT * G.mw[k];
+  }
+  int total;
+  int O = block_exclusive_scan(bits, red, &total);
+  for (int q = q0; q < q1; ++q) {
+    gO[q] = (uint32_t)O;
+    O += GT * G.mw[gk[q]];
+  }
+  if (tid == 0 && total > 8 * G.code_cap) bad = true;  // codes past the capacity
+  __syncthreads();
+  const uint8_t* code = tile + G.code_off;
+  const uint8_t* sm = tile + G.sm_off;
+  const int max_bit = 8 * G.code_cap;
+  for (int i = tid; i < G.raw_elems; i += kThreads) {
+    const int t = i / D, c = i % D, tg = t / GT, tau = t % GT;
+    const int q = tg * D + c, n = q * GT + tau;
+    const int k = gk[q], w = G.mw[k];
+    const int bp = (int)gO[q] + tau * w;
+    uint32_t o = 0;
+    if (bp + w <= max_bit) {
+      const int by = bp >> 3, sh = bp & 7;
+      uint32_t v = code[by];
+      if (sh + w > 8) v |= (uint32_t)code[by + 1] << 8;
+      o = (v >> sh) & ((1u << w) - 1u);
+    }
+    const uint32_t e = v2_base(G, k, b2, b3, b4, c) + o;
+    bad |= e > 255u;
+    const uint32_t s8 = sm[n];
+    put(t, c, ((s8 >> 7) << 15) | ((e & 0xFFu) << 7) | (s8 & 0x7Fu));
+  }
+  if (bad) atomicOr(&B.counters->status, 8u);
 }
 
 // A compressed tile's tag planes and escape area in LDS, loaded by the whole workgroup in one
@@ -818,6 +991,12 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
   }
   const uint8_t* tile = B.comp_pool + (size_t)slot * G.stride;
   __shared__ TileMeta meta;
+  if (G.mode_set != 0) {
+    decode_tile_v2(G, B, tile, B.bases + (size_t)4 * G.Hkv * D + ((size_t)kv * G.Hkv + h) * D,
+                   B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D, B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D,
+                   [&](int t, int c, uint32_t x) { elem_put(outv, out_idx(t, c), 2, x); });
+    return;
+  }
   if (G.EB == 2 && G.GT == 8) {
     uint16_t* o16 = reinterpret_cast<uint16_t*>(outv);
     decode_bf16_g8_tile(G, B, tile, B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
@@ -968,7 +1147,7 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
       nK = entry(b + 1, 0);
       nV = entry(b + 1, 1);
     }
-    if constexpr (FMT == 0) {
+    if (FMT == 0 && G.mode_set == 0) {
       // BF16, 8-token groups: the K tile by threads 0..127 and the V tile by 128..255 at once
       const int kv = tid >> 7, tl = tid & 127;
       const uint32_t e = kv ? eV : eK, slot = e & 0x00FFFFFFu;
@@ -995,11 +1174,17 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
           for (int i = tid; i < T * D; i += kThreads) dst[i] = 0;
           flags |= 4u;
         } else if (e & 0x80000000u) {  // raw tile: K [t][c], V [c][t]
-          const uint8_t* src = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems;
+          const uint8_t* src = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
           for (int i = tid; i < T * D; i += kThreads) {
             const int t = i / D, c = i % D;
-            dst[i] = src[kv ? (size_t)c * T + t : (size_t)i];
+            dst[i] = (uint16_t)elem_at(src, kv ? (size_t)c * T + t : (size_t)i, G.EB);
           }
+        } else if (G.mode_set != 0) {  // FORMAT v2 (nested precision modes, BF16)
+          decode_tile_v2(G, a.B, a.B.comp_pool + (size_t)slot * G.stride,
+                         a.B.bases + (size_t)4 * G.Hkv * D + ((size_t)kv * G.Hkv + h) * D,
+                         a.B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
+                         a.B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D,
+                         [&](int t, int c, uint32_t x) { dst[t * D + c] = (uint16_t)x; });
         } else {
           decode_tile_any(G, a.B, a.B.comp_pool + (size_t)slot * G.stride,
                           a.B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
@@ -1426,7 +1611,13 @@ int launch_calibrate(const Geo& G, const DevBufs& B, const void* k, const void* 
 
 int launch_append(const Geo& G, const DevBufs& B, const SeqList& S, const void* k, const void* v, int n_tokens,
                   int max_new_blocks, void* stream) {
-  if (max_new_blocks > 0) {
+  if (max_new_blocks > 0 && G.mode_set != 0) {  // FORMAT v2: the nested-mode encoder
+    const size_t lds = (size_t)G.raw_elems * 2 + (size_t)G.stride + (size_t)(5 * G.NG + 3) / 4 * 4;
+    hipLaunchKernelGGL(encode_v2_kernel, dim3(max_new_blocks, S.n, 2 * G.Hkv), dim3(kThreads), lds,
+                       (hipStream_t)stream, G, B, S, k, v, n_tokens);
+    const int err = (int)hipGetLastError();
+    if (err) return err;
+  } else if (max_new_blocks > 0) {
     const bool any = G.GT != kGroup;  // 8-token groups: the bit-assembling encoder
     const size_t lds = any ? (size_t)G.raw_elems * 2 + (size_t)G.stride + (size_t)(3 * G.NG + 3) / 4 * 4
                            : (size_t)G.raw_elems * 2 + (size_t)2 * G.PW * 4;

@@ -19,6 +19,10 @@
 //          E5M2 group one more plane (bit 4); zero up to esc_cap;
 //   RAW  : tiles that overflow esc_cap (and every tile of an uncompressed cache) are stored
 //          as native elements, K token-major [t][c], V channel-major [c][t].
+// FORMAT v2 (the nested precision modes, BF16; Geo::mode_set != 0): TAG (two planes holding bit
+// 0 and bit 1 of each group's mode index) | SM (one byte per element) | CODES: one LSB-first
+// stream with each group's offsets, in group order, at its mode's width; a tile whose codes
+// exceed the capacity is stored RAW.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -42,6 +46,11 @@ struct Geo {
   int max_seqs, max_blocks;
   int n_comp, n_raw;
   int compressed;
+  // FORMAT v2 (nested precision modes, BF16): mode_set 0 = FORMAT v1; 1, 2, 3 = the mode widths
+  // mw[0..n_modes) = {2,3,4,8}, {4,8}, {3,4,8} (raw last).  A v2 slot is TAG | SM | CODES:
+  // sm_off, code_off (the stream start) and code_cap (its capacity in bytes) above; esc_cap
+  // stays the escape allowance the capacity includes.
+  int mode_set, n_modes, mw[4], code_cap;
 };
 
 // counters buffer (12,416 bytes).  Atomics to one 128-byte line are performed one after
@@ -59,7 +68,7 @@ struct alignas(128) PoolTop {
   int32_t n;  // slots in this sub-stack
 };
 struct alignas(128) StatStripe {
-  unsigned long long raw_tiles, groups[3], esc_bytes;
+  unsigned long long raw_tiles, groups[4], esc_bytes;  // groups per mode index; FORMAT v2: code bytes
 };
 struct Counters {
   PoolTop comp_top[kPoolStripes];

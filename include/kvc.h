@@ -86,6 +86,14 @@ typedef struct {
   int32_t max_blocks_per_seq; /* finished blocks a sequence may hold                         */
   int32_t num_comp_slots;     /* compressed slot pool size (ignored when compressed == 0)    */
   int32_t num_raw_slots;      /* raw slot pool size                                          */
+  int32_t mode_set;           /* exponent modes (GAAC page §4.7.2, nested precision modes):
+                                 0 = 3-bit, 4-bit and raw in FORMAT v1 (the tuned path);
+                                 FORMAT v2, each group's offsets at its own mode's width in
+                                 one stream: 1 = 2-, 3-, 4-bit and raw (a 2-bit mode added),
+                                 2 = 4-bit and raw (no 3-bit mode), 3 = 3-, 4-bit and raw.
+                                 FORMAT v2 needs BF16 and head_dim <= 128
+                                 (KVC_EUNSUPPORTED otherwise); its caches are decoded and
+                                 attended by the element-wise LDS-rebuild kernels           */
 } kvc_params;
 
 /* Device buffers, all owned by the caller; sizes from kv_buffer_sizes (same order). */
@@ -94,10 +102,11 @@ typedef struct {
   void* raw_pool;    /* [num_raw_slots][T*D] elements: raw tiles, K token-major [t][c],
                         V channel-major [c][t]                                              */
   void* tail;        /* [max_seqs][2 (K,V)][Hkv][T*D] elements, raw-tile layout             */
-  void* bases;       /* [2 (K,V)][2 (narrow b3, wide b4)][Hkv][D] uint8 calibrated bases    */
+  void* bases;       /* [2 (K,V)][2 (narrow b3, wide b4)][Hkv][D] uint8 calibrated bases;
+                        mode_set 1 adds [2 (K,V)][Hkv][D] 2-bit-window bases b2 after them  */
   void* block_table; /* [max_seqs][max_blocks_per_seq][2 (K,V)][Hkv] uint32 entries:
                         0xFFFFFFFF = unallocated; else bit 31 = raw, bits 24..30 = escape
-                        bytes used in 16-byte units, bits 0..23 = slot index                */
+                        bytes used in 16-byte units (0 in FORMAT v2), bits 0..23 = slot     */
   void* comp_free;   /* [num_comp_slots] int32 free stack of compressed slots: 16
                         interleaved sub-stacks (sub-stack s = the slots equal to s mod 16,
                         its element k at index 16k + s), popped from a preferred sub-stack
@@ -112,8 +121,9 @@ typedef struct {
 typedef struct {
   uint64_t comp_tiles;    /* tiles stored compressed                                        */
   uint64_t raw_tiles;     /* tiles stored raw (escape overflow or compressed == 0)          */
-  uint64_t groups[3];     /* groups per mode: narrow, wide, raw (compressed tiles only)      */
-  uint64_t esc_bytes;     /* escape bytes used by compressed tiles                          */
+  uint64_t groups[4];     /* groups per mode index (compressed tiles only): FORMAT v1 narrow,
+                             wide, raw, 0; FORMAT v2 the modes of the set in width order     */
+  uint64_t esc_bytes;     /* escape bytes used by compressed tiles (FORMAT v2: code bytes)  */
   int32_t comp_free;      /* free compressed slots                                          */
   int32_t raw_free;       /* free raw slots                                                 */
 } kvc_stats;

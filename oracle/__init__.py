@@ -166,6 +166,100 @@ def decode_tiles(p: Params, data: np.ndarray, is_raw, is_v, b3: np.ndarray, b4: 
     return out, status
 
 
+# ---- FORMAT v2: nested precision modes (page §4.7.2), BF16 -----------------------------------
+
+MODE_SETS = {1: (2, 3, 4, 8), 2: (4, 8), 3: (3, 4, 8)}   # exponent widths of each mode, raw last
+
+
+class _V2Layout(ctypes.Structure):
+    _fields_ = [("n_modes", ctypes.c_int32), ("width", ctypes.c_int32 * 4)] + [(n, ctypes.c_int32) for n in (
+        "n_groups", "plane_bytes", "tag_bytes", "sm_bytes", "code_cap", "tag_off", "sm_off", "code_off", "stride",
+        "raw_bytes")]
+
+
+def _v2_lib():
+    L = lib()
+    if not getattr(L, "_v2_bound", False):
+        P = ctypes.POINTER
+        L.orc_v2_layout_of.argtypes = [P(_Params), ctypes.c_int32, P(_V2Layout)]
+        L.orc_v2_calibrate.argtypes = [P(_Params), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+        L.orc_v2_encode_batch.argtypes = [P(_Params), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_int32]
+        L.orc_v2_decode_batch.argtypes = [P(_Params), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+        L._v2_bound = True
+    return L
+
+
+def v2_layout(p: Params, mode_set: int) -> dict:
+    out = _V2Layout()
+    if _v2_lib().orc_v2_layout_of(ctypes.byref(p.c()), mode_set, ctypes.byref(out)) != 0:
+        raise ValueError(f"invalid FORMAT v2 parameters {p}, mode set {mode_set}")
+    d = {n: getattr(out, n) for n, _ in _V2Layout._fields_ if n != "width"}
+    d["width"] = list(out.width)[:out.n_modes]
+    return d
+
+
+def v2_calibrate(p: Params, x: np.ndarray, w: int) -> np.ndarray:
+    """Start of the calibrated window of 2^w exponents per channel: x [n_tokens][D] -> [D] uint8."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    b = np.zeros(p.D, np.uint8)
+    if _v2_lib().orc_v2_calibrate(ctypes.byref(p.c()), _ptr(x), x.shape[0], w, _ptr(b)) != 0:
+        raise ValueError("calibrate failed")
+    return b
+
+
+def v2_calibrate_layer(p: Params, k_cal: np.ndarray, v_cal: np.ndarray):
+    """(b2, b3, b4) each [2 (K, V)][Hkv][D] from calibration rows [n][Hkv][D]."""
+    Hkv = k_cal.shape[1]
+    out = []
+    for w in (2, 3, 4):
+        b = np.zeros((2, Hkv, p.D), np.uint8)
+        for kv, x in enumerate((k_cal, v_cal)):
+            for h in range(Hkv):
+                b[kv, h] = v2_calibrate(p, np.ascontiguousarray(x[:, h, :]), w)
+        out.append(b)
+    return tuple(out)
+
+
+def v2_encode_tiles(p: Params, mode_set: int, tiles, b2, b3, b4, is_v, nthreads=None):
+    """FORMAT v2 encode: tiles [n][T][D]; b2, b3, b4 [n][D] (or broadcastable).  Returns
+    (bytes [n][max(stride, raw)], is_raw [n], code_bytes [n], mode_counts [n][4])."""
+    tiles = np.ascontiguousarray(tiles, dtype=np.uint16)
+    n = tiles.shape[0]
+    lay = v2_layout(p, mode_set)
+    width = max(lay["stride"], lay["raw_bytes"])
+    bs = [np.ascontiguousarray(np.broadcast_to(b, (n, p.D)), dtype=np.uint8) for b in (b2, b3, b4)]
+    isv = np.ascontiguousarray(np.broadcast_to(np.asarray(is_v, np.int32), (n,)), dtype=np.int32)
+    out = np.zeros((n, width), np.uint8)
+    is_raw = np.zeros(n, np.int32)
+    used = np.zeros(n, np.int32)
+    modes = np.zeros((n, 4), np.int32)
+    rc = _v2_lib().orc_v2_encode_batch(ctypes.byref(p.c()), mode_set, n, _ptr(tiles), _ptr(bs[0]), _ptr(bs[1]),
+                                       _ptr(bs[2]), _ptr(isv), _ptr(out), width, _ptr(is_raw), _ptr(used),
+                                       _ptr(modes), _threads(nthreads))
+    if rc != 0:
+        raise ValueError("v2 encode failed")
+    return out, is_raw, used, modes
+
+
+def v2_decode_tiles(p: Params, mode_set: int, data, is_raw, is_v, b2, b3, b4, nthreads=None):
+    """Inverse of v2_encode_tiles: (tiles [n][T][D], status [n])."""
+    data = np.ascontiguousarray(data, dtype=np.uint8)
+    n = data.shape[0]
+    bs = [np.ascontiguousarray(np.broadcast_to(b, (n, p.D)), dtype=np.uint8) for b in (b2, b3, b4)]
+    isr = np.ascontiguousarray(np.broadcast_to(np.asarray(is_raw, np.int32), (n,)), dtype=np.int32)
+    isv = np.ascontiguousarray(np.broadcast_to(np.asarray(is_v, np.int32), (n,)), dtype=np.int32)
+    out = np.zeros((n, p.T, p.D), np.uint16)
+    status = np.zeros(n, np.int32)
+    _v2_lib().orc_v2_decode_batch(ctypes.byref(p.c()), mode_set, n, _ptr(data), data.shape[1], _ptr(isr), _ptr(isv),
+                                  _ptr(bs[0]), _ptr(bs[1]), _ptr(bs[2]), _ptr(out), _ptr(status), _threads(nthreads))
+    return out, status
+
+
 def value(fmt: int, bits: int) -> float:
     return lib().orc_value(fmt, bits)
 

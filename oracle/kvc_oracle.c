@@ -44,6 +44,22 @@
  *               the four 16-aligned section sizes (ESC counted at esc_cap).
  *   fallback    if the escape planes need more than esc_cap bytes, the tile is RAW: native
  *               elements, K tiles token-major [t][c], V tiles channel-major [c][t].
+ *
+ * FORMAT v2 ("orc_v2_*", BF16 only) -- the nested precision modes of §4.7.2 / Table 4: other
+ * sets of exponent modes, each group storing its offsets at its own mode's width:
+ *   mode sets   1: widths {2, 3, 4, 8} (a 2-bit mode added), 2: {4, 8} (no 3-bit mode),
+ *               3: {3, 4, 8} (the v1 modes in the v2 layout).  Mode k has width W[k] and base
+ *               b_W[c] (a calibrated window of 2^W exponents), the last mode is raw (base 0).
+ *               A group takes the first mode whose window holds all its exponents.
+ *   TAG         two bit planes of N_G bits: plane 0 bit 0 of k, plane 1 bit 1 of k (words).
+ *   SM          one byte (s << 7) | m per element, as v1.
+ *   CODES       one LSB-first bit stream: the groups in q order, each holding its G offsets in
+ *               token order at W_q bits each (element tau of group q at bit O_q + tau * W_q,
+ *               O_q = G * sum of W over the earlier groups).  Capacity: every offset at
+ *               max(3, narrowest width) bits plus esc_cap bytes (v1's CODE plus ESC bytes for
+ *               the sets with a 3-bit mode); unused bytes up to it are zero.
+ *   sections    TAG | SM | CODES, each starting 16-byte aligned; slot stride = their sum.
+ *   fallback    codes needing more than the capacity: the tile is RAW as in v1.
  */
 #include <math.h>
 #include <stdint.h>
@@ -406,3 +422,181 @@ int orc_attention(int32_t fmt, const uint16_t* q, const uint16_t* k, const uint1
   }
   return rc;
 }
+
+/* ---- FORMAT v2: nested precision modes (BF16) ------------------------------------------ */
+
+typedef struct {
+  int32_t n_modes, width[4];
+  int32_t n_groups, plane_bytes, tag_bytes, sm_bytes, code_cap;
+  int32_t tag_off, sm_off, code_off, stride, raw_bytes;
+} orc_v2_layout;
+
+int orc_v2_layout_of(const orc_params* p, int32_t mode_set, orc_v2_layout* L) {
+  memset(L, 0, sizeof(*L));
+  if (p->fmt != ORC_BF16) return ORC_EINVAL;
+  if (p->T <= 0 || p->D <= 0 || p->G <= 0 || p->T % p->G != 0 || (p->T * p->D) % 32 != 0) return ORC_EINVAL;
+  if (p->esc_cap < 0 || p->esc_cap % 16 != 0) return ORC_EINVAL;
+  if (mode_set == 1) { L->n_modes = 4; L->width[0] = 2; L->width[1] = 3; L->width[2] = 4; L->width[3] = 8; }
+  else if (mode_set == 2) { L->n_modes = 2; L->width[0] = 4; L->width[1] = 8; }
+  else if (mode_set == 3) { L->n_modes = 3; L->width[0] = 3; L->width[1] = 4; L->width[2] = 8; }
+  else return ORC_EINVAL;
+  L->n_groups = (p->T / p->G) * p->D;
+  L->plane_bytes = (L->n_groups + 31) / 32 * 4;
+  L->tag_bytes = 2 * L->plane_bytes;
+  L->sm_bytes = p->T * p->D;
+  L->code_cap = p->T * p->D * (L->width[0] < 3 ? 3 : L->width[0]) / 8 + p->esc_cap;
+  L->tag_off = 0;
+  L->sm_off = align16(L->tag_bytes);
+  L->code_off = L->sm_off + align16(L->sm_bytes);
+  L->stride = L->code_off + align16(L->code_cap);
+  L->raw_bytes = p->T * p->D * 2;
+  return ORC_OK;
+}
+
+/* Calibrated start of the window of 2^w exponents (same objective and tie-break as v1). */
+int orc_v2_calibrate(const orc_params* p, const uint16_t* x, int32_t n_tokens, int32_t w, uint8_t* b) {
+  orc_layout L;
+  if (orc_layout_of(p, &L) != ORC_OK || n_tokens < 0 || w < 1 || w >= L.F) return ORC_EINVAL;
+  long hist[256];
+  for (int c = 0; c < p->D; ++c) {
+    for (int e = 0; e < 256; ++e) hist[e] = 0;
+    for (int t = 0; t < n_tokens; ++t) hist[f_exp(&L, x[(long)t * p->D + c])] += 1;
+    b[c] = (uint8_t)pick_window(hist, L.F, w);
+  }
+  return ORC_OK;
+}
+
+/* base of mode width w for channel c: bases[0] = b2, bases[1] = b3, bases[2] = b4 */
+static uint32_t v2_base(int w, const uint8_t* const bases[3], int c) { return w >= 8 ? 0u : bases[w - 2][c]; }
+
+/* x: [T][D] BF16 bits.  b2, b3, b4: per-channel bases (unused ones may be any array).  out:
+ * at least max(stride, raw_bytes) bytes.  *code_bytes = used CODES bytes; mode_counts[4] =
+ * groups per mode index (as chosen before any fallback). */
+int orc_v2_encode_tile(const orc_params* p, int32_t mode_set, const uint16_t* x, const uint8_t* b2, const uint8_t* b3,
+                       const uint8_t* b4, int32_t is_v, uint8_t* out, int32_t* is_raw, int32_t* code_bytes,
+                       int32_t* mode_counts) {
+  orc_v2_layout L;
+  orc_layout L1;
+  if (orc_v2_layout_of(p, mode_set, &L) != ORC_OK || orc_layout_of(p, &L1) != ORC_OK) return ORC_EINVAL;
+  const uint8_t* bases[3] = {b2, b3, b4};
+  int NG = L.n_groups, G = p->G, D = p->D;
+  int* mode = (int*)malloc(sizeof(int) * (size_t)NG);
+  long bits = 0;
+  for (int k = 0; k < 4; ++k) mode_counts[k] = 0;
+  for (int q = 0; q < NG; ++q) {
+    int tg = q / D, c = q % D;
+    uint32_t mn = 0xFFFFFFFFu, mx = 0;
+    for (int tau = 0; tau < G; ++tau) {
+      uint32_t e = f_exp(&L1, x[(long)(tg * G + tau) * D + c]);
+      if (e < mn) mn = e;
+      if (e > mx) mx = e;
+    }
+    int k = L.n_modes - 1;  /* raw unless a window holds the group */
+    for (int j = 0; j < L.n_modes - 1; ++j) {
+      uint32_t b = v2_base(L.width[j], bases, c);
+      if (b <= mn && mx <= b + (1u << L.width[j]) - 1u) { k = j; break; }
+    }
+    mode[q] = k;
+    mode_counts[k] += 1;
+    bits += (long)G * L.width[k];
+  }
+  long used = (bits + 7) / 8;
+  long total = L.stride > L.raw_bytes ? L.stride : L.raw_bytes;
+  memset(out, 0, (size_t)total);
+  if (used > L.code_cap) {
+    write_raw(p, &L1, x, is_v, out);
+    *is_raw = 1;
+    *code_bytes = 0;
+    free(mode);
+    return ORC_OK;
+  }
+  uint8_t* tag0 = out + L.tag_off;
+  uint8_t* tag1 = out + L.tag_off + L.plane_bytes;
+  uint8_t* sm = out + L.sm_off;
+  uint8_t* code = out + L.code_off;
+  long O = 0;
+  for (int q = 0; q < NG; ++q) {
+    int tg = q / D, c = q % D, k = mode[q], w = L.width[k];
+    uint32_t base = v2_base(w, bases, c);
+    put_bit(tag0, q, (uint32_t)k & 1u);
+    put_bit(tag1, q, ((uint32_t)k >> 1) & 1u);
+    for (int tau = 0; tau < G; ++tau) {
+      uint32_t v = x[(long)(tg * G + tau) * D + c];
+      long n = (long)q * G + tau;
+      uint32_t o = f_exp(&L1, v) - base;
+      for (int b = 0; b < w; ++b) put_bit(code, O + (long)tau * w + b, o >> b);
+      sm[n] = (uint8_t)((f_sign(&L1, v) << 7) | f_man(&L1, v));
+    }
+    O += (long)G * w;
+  }
+  *is_raw = 0;
+  *code_bytes = (int32_t)used;
+  free(mode);
+  return ORC_OK;
+}
+
+/* Inverse of orc_v2_encode_tile.  Rejects a mode index outside the set, codes that run past
+ * the capacity, and exponents past the 8-bit field. */
+int orc_v2_decode_tile(const orc_params* p, int32_t mode_set, const uint8_t* in, int32_t is_raw, int32_t is_v,
+                       const uint8_t* b2, const uint8_t* b3, const uint8_t* b4, uint16_t* x) {
+  orc_v2_layout L;
+  orc_layout L1;
+  if (orc_v2_layout_of(p, mode_set, &L) != ORC_OK || orc_layout_of(p, &L1) != ORC_OK) return ORC_EINVAL;
+  if (is_raw) return orc_decode_tile(p, in, 1, is_v, b3, b4, x);
+  const uint8_t* bases[3] = {b2, b3, b4};
+  int NG = L.n_groups, G = p->G, D = p->D;
+  const uint8_t* tag0 = in + L.tag_off;
+  const uint8_t* tag1 = in + L.tag_off + L.plane_bytes;
+  const uint8_t* sm = in + L.sm_off;
+  const uint8_t* code = in + L.code_off;
+  long O = 0;
+  for (int q = 0; q < NG; ++q) {
+    int tg = q / D, c = q % D;
+    int k = (int)(get_bit(tag0, q) | (get_bit(tag1, q) << 1));
+    if (k >= L.n_modes) return ORC_ECORRUPT;
+    int w = L.width[k];
+    if (O + (long)G * w > 8L * L.code_cap) return ORC_ECORRUPT;
+    uint32_t base = v2_base(w, bases, c);
+    for (int tau = 0; tau < G; ++tau) {
+      long n = (long)q * G + tau;
+      uint32_t o = 0;
+      for (int b = 0; b < w; ++b) o |= get_bit(code, O + (long)tau * w + b) << b;
+      uint32_t e = base + o;
+      if (e >= 256u) return ORC_ECORRUPT;
+      x[(long)(tg * G + tau) * D + c] = (uint16_t)f_join(&L1, (uint32_t)sm[n] >> 7, e, sm[n] & 0x7Fu);
+    }
+    O += (long)G * w;
+  }
+  return ORC_OK;
+}
+
+int orc_v2_encode_batch(const orc_params* p, int32_t mode_set, int32_t n, const uint16_t* x, const uint8_t* b2,
+                        const uint8_t* b3, const uint8_t* b4, const int32_t* is_v, uint8_t* out, int64_t out_stride,
+                        int32_t* is_raw, int32_t* code_bytes, int32_t* mode_counts, int32_t nthreads) {
+  orc_v2_layout L;
+  if (orc_v2_layout_of(p, mode_set, &L) != ORC_OK) return ORC_EINVAL;
+  if (out_stride < L.stride || out_stride < L.raw_bytes) return ORC_EINVAL;
+  long td = (long)p->T * p->D;
+  int rc = ORC_OK;
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(min : rc)
+  for (int i = 0; i < n; ++i) {
+    int r = orc_v2_encode_tile(p, mode_set, x + i * td, b2 + (long)i * p->D, b3 + (long)i * p->D, b4 + (long)i * p->D,
+                               is_v[i], out + i * out_stride, is_raw + i, code_bytes + i, mode_counts + 4L * i);
+    if (r < rc) rc = r;
+  }
+  return rc;
+}
+
+int orc_v2_decode_batch(const orc_params* p, int32_t mode_set, int32_t n, const uint8_t* in, int64_t in_stride,
+                        const int32_t* is_raw, const int32_t* is_v, const uint8_t* b2, const uint8_t* b3,
+                        const uint8_t* b4, uint16_t* x, int32_t* status, int32_t nthreads) {
+  orc_v2_layout L;
+  if (orc_v2_layout_of(p, mode_set, &L) != ORC_OK) return ORC_EINVAL;
+  long td = (long)p->T * p->D;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+  for (int i = 0; i < n; ++i)
+    status[i] = orc_v2_decode_tile(p, mode_set, in + i * in_stride, is_raw[i], is_v[i], b2 + (long)i * p->D,
+                                   b3 + (long)i * p->D, b4 + (long)i * p->D, x + i * td);
+  return ORC_OK;
+}
+

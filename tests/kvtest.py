@@ -28,14 +28,14 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def new_cache(*, Hkv, Hq, D, T, max_seqs, max_blocks, comp_slots=None, raw_slots=None, compressed=True,
-              esc_cap=-1, perm_seed=0, fmt=oracle.BF16, Gt=16):
+              esc_cap=-1, perm_seed=0, fmt=oracle.BF16, Gt=16, mode_set=0):
     from decode_attention_calibrate_amd import KVCache
     n_tiles = max_seqs * max_blocks * 2 * Hkv
     return KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=max_seqs,
                    max_blocks_per_seq=max_blocks, group_tokens=Gt,
                    num_comp_slots=(n_tiles if comp_slots is None else comp_slots) if compressed else 0,
                    num_raw_slots=(n_tiles if raw_slots is None else raw_slots), compressed=compressed,
-                   esc_cap_bytes=esc_cap, perm_seed=perm_seed, dtype=fmt)
+                   esc_cap_bytes=esc_cap, perm_seed=perm_seed, dtype=fmt, mode_set=mode_set)
 
 
 def row_rel_err(out_bits: np.ndarray, ref: np.ndarray) -> float:
