@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep", type=str, default="", help="comma-separated split counts to time (extra)")
     ap.add_argument("--probe", action="store_true", help="also time plain HBM copy / read kernels (torch)")
-    ap.add_argument("--extra", type=str, default="context,fp8,paged,groups,rope,serving,prefill",
+    ap.add_argument("--extra", type=str, default="context,fp8,paged,groups,nested,rope,serving,prefill",
                     help="comma list of extra workloads measured after the headline one: context (the cfg2 "
                          "layer at 32K and 128K tokens), fp8 (the 64K layer in "
                          "FP8 E5M2 and E4M3), paged (32-sequence paged serving mix), prefill (a 4K-token prompt: encode, "
@@ -368,6 +368,8 @@ def main():
         result["paged_mix"] = extra_steps(torch, K, synth, synth.config(3), args, splits=args.paged_splits, layers=2)
     if "groups" in extras:
         result["codec_groups_64k"] = codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, q, args.splits)
+    if "nested" in extras:
+        result["nested_modes_64k"] = nested_modes(torch, K, cfg, kd, vd, k0, v0, dev, stream, q, args.splits)
     if "rope" in extras:
         result["rope_drift_64k"] = rope_drift(torch, K, synth, cfg, k0, v0, dev)
     if "prefill" in extras:
@@ -446,6 +448,83 @@ def codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, q, n_splits, reps=5
         }
         del c
     log(f"[bench] codec groups: {res}")
+    return res
+
+
+def nested_modes(torch, K, cfg, kd, vd, k0, v0, dev, stream, q, n_splits, reps=3):
+    """The nested precision modes of GAAC page §4.7.2 / Table 4 on the 64K layer: FORMAT v1
+    (3-bit, 4-bit and raw modes; the tuned path) against FORMAT v2 with a 2-bit mode added, with
+    the 3-bit mode removed, and with the v1 modes in the v2 layout (each group's offsets at its
+    own width in one stream), for 16- and 8-token groups: codec and resident ratio, mode shares,
+    one bulk encode of the layer, kv_decode_blocks of every block (the decode latency the page
+    compares) and decode attention over the layer (hot, back to back)."""
+    T, D, Hkv, Hq = cfg.T, cfg.D, cfg.Hkv, cfg.Hq
+    L0 = kd.shape[1]
+    nb = L0 // T
+    TD = T * D
+
+    def ev_us(fn):
+        a_ = torch.cuda.Event(enable_timing=True)
+        b_ = torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        fn()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return a_.elapsed_time(b_) * 1e3
+
+    variants = [("v1_3_4_raw", 0), ("v2_2_3_4_raw", 1), ("v2_4_raw", 2), ("v2_3_4_raw", 3)]
+    res = {"workload": "qwen3-8b-like-64k", "tokens": L0, "block_tokens": T}
+    for Gt in (8, 16):
+        row = {}
+        for name, ms in variants:
+            enc, dec = [], []
+            for _ in range(reps):
+                c = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=1,
+                              max_blocks_per_seq=nb + 1, num_comp_slots=(nb + 1) * 2 * Hkv, num_raw_slots=(nb + 1) * 2 * Hkv,
+                              compressed=True, group_tokens=Gt, perm_seed=7, mode_set=ms)
+                c.calibrate(dev(k0[:cfg.n_cal]), dev(v0[:cfg.n_cal]))
+                torch.cuda.synchronize()
+                enc.append(ev_us(lambda: c.append([0], kd, vd)))
+                kout = torch.empty((nb * T, Hkv, D), dtype=torch.int16, device="cuda")
+                vout = torch.empty_like(kout)
+                dec.append(ev_us(lambda: c.decode_blocks(0, 0, nb, (kout, vout))))
+            if not (torch.equal(kout, kd[0, :nb * T]) and torch.equal(vout, vd[0, :nb * T])):
+                raise RuntimeError(f"{name}, {Gt}-token groups: decode_blocks did not rebuild the layer bit for bit")
+            ws = c.workspace(1, n_splits)
+            for _ in range(2):
+                c.attention_partials([0], q, cfg.scale, n_splits, ws)
+            attn = ev_us(lambda: [c.attention_partials([0], q, cfg.scale, n_splits, ws) for _ in range(10)]) / 10
+            flags, st = c.status()
+            if flags:
+                raise RuntimeError(f"cache status flags {flags}")
+            n_tiles = st["comp_tiles"] + st["raw_tiles"]
+            ng = TD // Gt
+            if ms == 0:
+                payload = (2 * ng + 3 * TD + 8 * TD) // 8
+                stored = st["comp_tiles"] * payload + st["esc_bytes"] + st["raw_tiles"] * TD * 2
+            else:  # TAG + SM + used code bytes
+                stored = st["comp_tiles"] * ((2 * ng) // 8 + TD) + st["esc_bytes"] + st["raw_tiles"] * TD * 2
+            groups = st["groups"]
+            row[name] = {
+                "codec_ratio": round(n_tiles * TD * 2 / stored, 4),
+                "resident_ratio": round(n_tiles * TD * 2 / (st["comp_tiles"] * c.slot_stride + st["raw_tiles"] * TD * 2
+                                                             + 4 * n_tiles), 4),
+                "mode_share": [round(x / max(sum(groups), 1), 5) for x in groups],
+                "raw_tiles": st["raw_tiles"], "slot_stride": c.slot_stride,
+                "bulk_encode_us": round(float(np.median(enc)), 1),
+                "decode_all_blocks_us": round(float(np.median(dec)), 1),
+                "attention_hot_us": round(attn, 1),
+            }
+            del c
+            torch.cuda.empty_cache()
+        base, same_layout = row["v1_3_4_raw"], row["v2_3_4_raw"]
+        for name in ("v2_2_3_4_raw", "v2_4_raw"):
+            r = row[name]
+            r["ratio_change_vs_v1_pct"] = round(100 * (r["codec_ratio"] / base["codec_ratio"] - 1), 2)
+            r["decode_latency_vs_v1"] = round(r["decode_all_blocks_us"] / base["decode_all_blocks_us"], 2)
+            r["decode_latency_vs_v2_3_4_raw"] = round(r["decode_all_blocks_us"] / same_layout["decode_all_blocks_us"], 2)
+        res[f"g{Gt}"] = row
+    log(f"[bench] nested modes: {res}")
     return res
 
 
