@@ -154,6 +154,14 @@ def main():
     q_bytes = Hq * D * 2
     table_bytes = 4 * (st["comp_tiles"] + st["raw_tiles"])
     log(f"[bench] codec ratio {codec_ratio:.4f}, resident ratio {resident_ratio:.4f}, tiles {st}")
+    # exponent concentration (GAAC page §3.1): share of each head-channel's 65,536 exponents
+    # inside its best window of w consecutive values (kv_window_coverage), mean over channels
+    coverage = {"what": "mean over (kv-head, channel) of the share of the layer's exponents inside the "
+                        "channel's best window of w consecutive exponent values (kv_window_coverage)"}
+    for nm, x in (("k", kd[0]), ("v", vd[0])):
+        for w in (4, 6, 8, 16):
+            coverage[f"{nm}_w{w}"] = round(float(comp[0].window_coverage(x, w).double().mean()) / L0, 4)
+    log(f"[bench] exponent coverage {coverage}")
 
     wsc = comp[0].workspace(1, S)
     out = torch.empty((1, Hq, D), dtype=torch.int16, device="cuda")
@@ -344,6 +352,7 @@ def main():
         "uncompressed_GBps": round(bytes_r / (attn_r * 1e-6) / 1e9, 1),
         "codec_ratio": round(codec_ratio, 4),
         "resident_ratio": round(resident_ratio, 4),
+        "exponent_coverage": coverage,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "attn_comp_kernel<4,64>", "bytes_per_launch": bytes_c,
@@ -577,7 +586,8 @@ def rope_drift(torch, K, synth, cfg, k0, v0, dev, seg=8192):
     the mean escape bytes of the compressed K and V tiles (from their stored tag planes) and the
     share of tiles stored raw.  Policies: unrotated keys, first 256 tokens; rotated keys
     calibrated on the first 256, 8K or 32K tokens, or on 256 tokens spread evenly over the
-    context (same calibration budget as the first, spread over the positions)."""
+    context (same calibration budget as the first, spread over the positions).  The per-tile
+    figures come from kv_tile_stats (read on the device from the stored tag planes)."""
     T, D, Hkv, Hq = cfg.T, cfg.D, cfg.Hkv, cfg.Hq
     L0 = k0.shape[0]
     nb = L0 // T
@@ -585,7 +595,6 @@ def rope_drift(torch, K, synth, cfg, k0, v0, dev, seg=8192):
     policies = [("unrotated_first256", k0, np.arange(256)), ("first256", kr, np.arange(256)),
                 ("first8k", kr, np.arange(8192)), ("first32k", kr, np.arange(32768)),
                 ("spread256", kr, np.arange(0, L0, L0 // 256))]
-    popc = torch.tensor([bin(i).count("1") for i in range(256)], dtype=torch.int32, device="cuda")
     res = {"workload": "qwen3-8b-like-64k, RoPE theta 1e6 on K", "segment_tokens": seg, "block_tokens": T}
     for name, ks, cal in policies:
         c = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=1,
@@ -593,15 +602,9 @@ def rope_drift(torch, K, synth, cfg, k0, v0, dev, seg=8192):
                       compressed=True, perm_seed=7)
         c.calibrate(dev(ks[cal]), dev(v0[cal]))
         c.append([0], dev(ks[None]), dev(v0[None]))
-        torch.cuda.synchronize()
-        e = c.table()[: (nb + 1) * 2 * Hkv].view(nb + 1, 2, Hkv)[:nb]
-        raw = e < 0
-        slot = (e & 0xFFFFFF).long()
-        pw_bytes = 4 * ((T // 16 * D + 31) // 32)  # one tag plane
-        tagpool = c.buffers["comp_pool"].view(-1, c.slot_stride)[:, : 2 * pw_bytes]  # TAG sections only
-        tags = tagpool[torch.where(raw, torch.zeros_like(slot), slot)].long()
-        units = popc[tags[..., :pw_bytes]].sum(-1) + 4 * popc[tags[..., pw_bytes:]].sum(-1)  # wide 1, raw 5
-        esc = torch.where(raw, torch.zeros_like(units), 2 * units).double()  # 16-bit escape units
+        stats = c.tile_stats(0, 0, nb)            # kv_tile_stats: [nb][2][Hkv][6] {state, escape bytes, modes}
+        raw = stats[..., 0] == 1
+        esc = stats[..., 1].double()
         segs = []
         for s0 in range(0, nb, seg // T):
             row = {}
@@ -618,48 +621,34 @@ def rope_drift(torch, K, synth, cfg, k0, v0, dev, seg=8192):
     return res
 
 
-def equal_memory_serving(torch, K, synth, splits, budget_mb=1536, n_requests=96, layers=2, steps=24):
-    """Equal-memory serving (GAAC page §4.5): one KV byte budget per layer for both caches, the
-    compressed one spending 1/64 of it on raw-fallback slots and the rest on compressed slots,
-    the uncompressed one all of it on raw tiles.  Requests with paged-mix lengths (T = 16;
-    U[4096, 32768] tokens, seeded) are admitted first come, first served while their finished
-    blocks plus one spare block fit in the free slots; then the admitted batch decodes
-    (kv_decode_step over every admitted sequence) on `layers` rotated layer caches.  Sequences
-    take their tokens from one shared token stream at staggered offsets.  No model weights
-    exist here: a step is the attention layer alone, so the throughput is attention-only."""
+def equal_memory_serving(torch, K, synth, splits, budget_mb=1536, n_requests=96, layers=4, steps=24):
+    """Equal-memory serving (GAAC page §4.5): one KV byte budget per layer for both caches,
+    planned and admitted by kv_admit_fcfs (the compressed cache spends 1/64 of it on raw-fallback
+    slots and the rest on compressed slots, the uncompressed one all of it on raw tiles; requests
+    with paged-mix lengths, T = 16, U[4096, 32768] tokens, seeded, are admitted first come, first
+    served while their finished blocks plus one spare block fit in the free slots); then the
+    admitted batch decodes (kv_decode_step over every admitted sequence) on `layers` rotated layer
+    caches.  Sequences take their tokens from one shared token stream at staggered offsets.  No
+    model weights exist here: a step is the attention layer alone, so the throughput is
+    attention-only."""
     import dataclasses
     cfg = synth.config(3)
     T, D, Hkv, Hq = cfg.T, cfg.D, cfg.Hkv, cfg.Hq
     lens = np.random.default_rng([3, 4242]).integers(4096, 32768, size=n_requests, endpoint=True).tolist()
     budget = budget_mb << 20
-    tile_raw = T * D * 2
     g = synth.LayerGen(cfg)
     pk_h, pv_h = g.tokens(max(lens) + 4096)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
     pk, pv = dev(pk_h), dev(pv_h)
     stream = torch.cuda.current_stream()
     res = {"workload": "paged-mix requests, T = 16, 8/32 heads, D = 128", "budget_bytes_per_layer": budget,
-           "requests": n_requests, "n_splits": splits, "layers_rotated": layers, "steps": steps}
+           "requests": n_requests, "n_splits": splits, "layers_rotated": layers, "steps": steps,
+           "admission": "kv_admit_fcfs"}
 
     for name, compressed in (("uncompressed", False), ("compressed", True)):
-        probe = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=1,
-                          max_blocks_per_seq=1, num_comp_slots=1, num_raw_slots=1, compressed=True)
-        stride = probe.slot_stride
-        del probe
-        if compressed:
-            n_raw = (budget // 64) // tile_raw
-            n_comp = (budget - n_raw * tile_raw) // stride
-            free = n_comp
-        else:
-            n_raw, n_comp = budget // tile_raw, 0
-            free = n_raw
-        admitted = []
-        for L in lens:  # first come, first served: stop at the first request that does not fit
-            need = (L // T + 1) * 2 * Hkv
-            if need > free:
-                break
-            free -= need
-            admitted.append(L)
+        n, n_comp, n_raw = K.admit_fcfs(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T,
+                                        budget_bytes=budget, lengths=lens, compressed=compressed, raw_share=1.0 / 64)
+        admitted = lens[:n]
         n = len(admitted)
         ids = list(range(n))
         max_blocks = max(admitted) // T + 2

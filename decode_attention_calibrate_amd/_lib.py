@@ -56,6 +56,10 @@ SIGNATURES = {
     "kv_attention_combine": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, ctypes.c_float, _i32, _vp, _sz, _vp, _vp]),
     "kv_decode_attention_noalloc": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, ctypes.c_float, _i32, _vp, _vp]),
     "kv_decode_step": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, _vp, _vp, ctypes.c_float, _i32, _vp, _sz, _vp, _vp]),
+    "kv_tile_stats": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
+    "kv_window_coverage": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "kv_admit_fcfs": (ctypes.c_int, [_P(Params), _u64, ctypes.c_double, _P(_i32), _i32, _P(_i32), _P(_i32),
+                                     _P(_i32)]),
     "kv_release_seq": (ctypes.c_int, [_vp, _i32, _vp]),
     "kv_seq_length": (ctypes.c_int, [_vp, _i32, _P(_i32)]),
     "kv_get_status": (ctypes.c_int, [_vp, _P(ctypes.c_uint32), _P(Stats), _vp]),

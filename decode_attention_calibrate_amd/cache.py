@@ -191,6 +191,21 @@ class KVCache:
                                         _ptr(ws), ws.numel(), _ptr(out), self._stream()))
         return out
 
+    # ---- diagnostics ----
+    def tile_stats(self, seq: int, first: int, n: int) -> torch.Tensor:
+        """kv_tile_stats: [n][2][Hkv][6] int32 {state, bytes, groups per mode index [4]}."""
+        out = torch.empty((n, 2, self.Hkv, 6), dtype=torch.int32, device=self.device)
+        L.check(self.lib.kv_tile_stats(self.handle, seq, first, n, _ptr(out), self._stream()))
+        return out
+
+    def window_coverage(self, x: torch.Tensor, window: int) -> torch.Tensor:
+        """kv_window_coverage of x [n][Hkv][D] elements -> [Hkv][D] int32 counts."""
+        _elem(x, "x", self.EB)
+        self._shape(x, "x", 1)
+        out = torch.empty((self.Hkv, self.D), dtype=torch.int32, device=self.device)
+        L.check(self.lib.kv_window_coverage(self.handle, _ptr(x), x.shape[0], window, _ptr(out), self._stream()))
+        return out
+
     # ---- bookkeeping ----
     def release(self, seq: int):
         L.check(self.lib.kv_release_seq(self.handle, seq, self._stream()))
@@ -218,3 +233,19 @@ class KVCache:
         """The 2-bit-window bases of mode set 1, [2 (K, V)][Hkv][D]."""
         n = 4 * self.Hkv * self.D
         return self.buffers["bases"][n: n + 2 * self.Hkv * self.D].view(2, self.Hkv, self.D)
+
+
+def admit_fcfs(*, num_kv_heads: int, head_dim: int, block_tokens: int, budget_bytes: int, lengths,
+               compressed: bool = True, raw_share: float = 1.0 / 64, group_tokens: int = 16, dtype: int = L.BF16,
+               mode_set: int = 0, num_q_heads: int | None = None):
+    """kv_admit_fcfs: (admitted count, compressed slots, raw slots) for one layer's KV byte budget
+    and requests admitted first come, first served (host only)."""
+    lib = L.load()
+    p = L.Params(dtype, num_kv_heads, num_q_heads or num_kv_heads, head_dim, block_tokens, group_tokens, -1,
+                 1 if compressed else 0, 1, 1, 1, 1, mode_set)
+    arr = (ctypes.c_int32 * len(lengths))(*[int(x) for x in lengths])
+    n, nc, nr = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    L.check(lib.kv_admit_fcfs(ctypes.byref(p), int(budget_bytes), float(raw_share), arr, len(lengths), ctypes.byref(n),
+                              ctypes.byref(nc), ctypes.byref(nr)))
+    return n.value, nc.value, nr.value
+

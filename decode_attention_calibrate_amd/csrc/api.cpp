@@ -498,6 +498,59 @@ int kv_decode_step(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, co
   return rc;
 }
 
+int kv_tile_stats(kvc_cache* c, int32_t seq, int32_t first_block, int32_t n_blocks, int32_t* out_dev, void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  if (seq < 0 || seq >= c->p.max_seqs) return fail(KVC_EINVAL, "sequence id out of range");
+  if (!out_dev || first_block < 0 || n_blocks < 1) return fail(KVC_EINVAL, "bad block range");
+  if (first_block + n_blocks > c->len[seq] / c->G.T) return fail(KVC_EINVAL, "blocks past the finished blocks");
+  if ((uintptr_t)out_dev & 3u) return fail(KVC_EINVAL, "out must be 4-byte aligned");
+  return hip_fail(kvc::launch_tile_stats(c->G, c->B, seq, first_block, n_blocks, out_dev, stream), "launch tile stats");
+}
+
+int kv_window_coverage(kvc_cache* c, const void* x_dev, int32_t n_tokens, int32_t window, int32_t* out_dev,
+                       void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  if (!x_dev || !out_dev || n_tokens < 1) return fail(KVC_EINVAL, "coverage needs x, out and n_tokens >= 1");
+  if (window < 1 || window > (1 << c->G.F)) return fail(KVC_EINVAL, "window must be in 1 .. 2^(exponent bits)");
+  if ((uintptr_t)out_dev & 3u) return fail(KVC_EINVAL, "out must be 4-byte aligned");
+  return hip_fail(kvc::launch_coverage(c->G, x_dev, n_tokens, window, out_dev, stream), "launch coverage");
+}
+
+int kv_admit_fcfs(const kvc_params* params, uint64_t budget_bytes, double raw_share, const int32_t* lengths_host,
+                  int32_t n_requests, int32_t* n_admitted, int32_t* num_comp_slots, int32_t* num_raw_slots) {
+  if (!params || !n_admitted || !num_comp_slots || !num_raw_slots) return fail(KVC_EINVAL, "NULL argument");
+  if (n_requests < 0 || (n_requests > 0 && !lengths_host)) return fail(KVC_EINVAL, "bad request list");
+  if (!(raw_share >= 0.0 && raw_share <= 1.0)) return fail(KVC_EINVAL, "raw_share must be in [0, 1]");
+  kvc_params p = *params;  // slot counts are what this call plans: any valid value passes the checks
+  p.num_comp_slots = p.num_raw_slots = 1;
+  const int rc = check_params(&p);
+  if (rc != KVC_OK) return rc;
+  const Geo G = make_geo(p);
+  const uint64_t raw_tile = (uint64_t)G.raw_elems * G.EB, tiles_per_block = 2ull * G.Hkv;
+  uint64_t n_raw, n_comp;
+  if (p.compressed) {
+    n_raw = (uint64_t)((double)budget_bytes * raw_share) / raw_tile;
+    n_comp = (budget_bytes - n_raw * raw_tile) / (uint64_t)G.stride;
+  } else {
+    n_raw = budget_bytes / raw_tile;
+    n_comp = 0;
+  }
+  if (n_raw >= (1u << 24) || n_comp >= (1u << 24)) return fail(KVC_EINVAL, "budget exceeds 2^24 slots per pool");
+  uint64_t free_slots = p.compressed ? n_comp : n_raw;
+  int admitted = 0;
+  for (; admitted < n_requests; ++admitted) {
+    const int32_t L = lengths_host[admitted];
+    if (L < 1) return fail(KVC_EINVAL, "request lengths must be >= 1");
+    const uint64_t need = ((uint64_t)L / G.T + 1) * tiles_per_block;  // its finished blocks + one spare block
+    if (need > free_slots) break;                                     // first come, first served: stop here
+    free_slots -= need;
+  }
+  *n_admitted = admitted;
+  *num_comp_slots = (int32_t)n_comp;
+  *num_raw_slots = (int32_t)n_raw;
+  return KVC_OK;
+}
+
 int kv_release_seq(kvc_cache* c, int32_t seq, void* stream) {
   if (!c) return fail(KVC_EINVAL, "cache is NULL");
   if (seq < 0 || seq >= c->p.max_seqs) return fail(KVC_EINVAL, "sequence id out of range");

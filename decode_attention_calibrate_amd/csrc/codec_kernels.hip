@@ -699,6 +699,66 @@ __global__ void __launch_bounds__(kThreads) encode_v2_kernel(Geo G, DevBufs B, S
   if (tid == 0) B.table[entry_idx] = (uint32_t)slot;
 }
 
+// Storage statistics of finished tiles from their table entries and stored tag planes (the
+// positional-drift study of GAAC page App. C reads these per segment): one thread per tile;
+// out[i][6] = {state (0 compressed, 1 raw, -1 unallocated), bytes (FORMAT v1: the escape bytes
+// the tags call for; FORMAT v2: the code bytes), groups per mode index [4]}.  A raw bit without
+// its escape bit (FORMAT v1, corrupt) counts as raw.
+__global__ void tile_stats_kernel(Geo G, DevBufs B, int seq, int first, int n, int32_t* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n * 2 * G.Hkv) return;
+  const int bi = i / (2 * G.Hkv), kv = (i / G.Hkv) % 2, h = i % G.Hkv;
+  const uint32_t e = B.table[table_index(G, seq, first + bi, kv, h)];
+  int32_t* o = out + (size_t)i * 6;
+  int c[4] = {0, 0, 0, 0}, state = 0;
+  long bits = 0;
+  if (e == kUnallocated) {
+    state = -1;
+  } else if (e & 0x80000000u) {
+    state = 1;
+  } else {
+    const uint32_t* tag0 = reinterpret_cast<const uint32_t*>(B.comp_pool + (size_t)(e & 0x00FFFFFFu) * G.stride + G.tag_off);
+    const uint32_t* tag1 = tag0 + G.PW;
+    for (int w = 0; w < G.PW; ++w) {
+      const uint32_t valid = (w == G.PW - 1 && (G.NG & 31)) ? ((1u << (G.NG & 31)) - 1u) : 0xFFFFFFFFu;
+      const uint32_t a = tag0[w] & valid, b = tag1[w] & valid;
+      if (G.mode_set == 0) {  // planes E (mode >= wide) and R (raw)
+        c[2] += __popc(b);
+        c[1] += __popc(a & ~b);
+      } else {                // bits 0 and 1 of the mode index
+        c[1] += __popc(a & ~b);
+        c[2] += __popc(~a & b);
+        c[3] += __popc(a & b);
+      }
+    }
+    c[0] = G.NG - c[1] - c[2] - c[3];
+    if (G.mode_set == 0) bits = (long)G.GT * (c[1] + (long)(G.F - 3) * c[2]);
+    else for (int k = 0; k < G.n_modes; ++k) bits += (long)G.GT * G.mw[k] * c[k];
+  }
+  o[0] = state;
+  o[1] = (int32_t)((bits + 7) / 8);
+  for (int k = 0; k < 4; ++k) o[2 + k] = c[k];
+}
+
+// Exponent concentration (GAAC page §3.1: most exponents of a head-channel lie in a few
+// consecutive values): one block per (channel, kv-head), the largest number of the n tokens'
+// exponents inside any window of w consecutive exponent values.  x: [n][Hkv][D] elements.
+__global__ void coverage_kernel(Geo G, const void* __restrict__ x, int n, int w, int32_t* __restrict__ out) {
+  __shared__ int hist[256];
+  __shared__ int red[8];
+  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  hist[tid] = 0;
+  __syncthreads();
+  for (int t = tid; t < n; t += kThreads) atomicAdd(&hist[exp_of(G, elem_at(x, ((size_t)t * G.Hkv + h) * G.D + c, G.EB))], 1);
+  __syncthreads();
+  const int nb = (1 << G.F) - w + 1;
+  int cov = 0;
+  if (tid < nb)
+    for (int e = tid; e < tid + w; ++e) cov += hist[e];
+  const int best = block_max(cov, red);
+  if (tid == 0) out[(size_t)h * G.D + c] = best;
+}
+
 // Writes the appended tokens that do not complete a block into the sequence's tail.
 __global__ void tail_kernel(Geo G, DevBufs B, SeqList S, const void* __restrict__ kin, const void* __restrict__ vin,
                             int n_tok) {
@@ -1630,6 +1690,18 @@ int launch_append(const Geo& G, const DevBufs& B, const SeqList& S, const void* 
     if (err) return err;
   }
   hipLaunchKernelGGL(tail_kernel, dim3(S.n, 2 * G.Hkv), dim3(256), 0, (hipStream_t)stream, G, B, S, k, v, n_tokens);
+  return (int)hipGetLastError();
+}
+
+int launch_tile_stats(const Geo& G, const DevBufs& B, int seq, int first, int n, int32_t* out, void* stream) {
+  const int tiles = n * 2 * G.Hkv;
+  hipLaunchKernelGGL(tile_stats_kernel, dim3((tiles + 255) / 256), dim3(256), 0, (hipStream_t)stream, G, B, seq, first, n,
+                     out);
+  return (int)hipGetLastError();
+}
+
+int launch_coverage(const Geo& G, const void* x, int n, int w, int32_t* out, void* stream) {
+  hipLaunchKernelGGL(coverage_kernel, dim3(G.D, G.Hkv), dim3(kThreads), 0, (hipStream_t)stream, G, x, n, w, out);
   return (int)hipGetLastError();
 }
 

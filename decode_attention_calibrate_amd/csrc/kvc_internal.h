@@ -138,6 +138,8 @@ int launch_prefill(const Geo& G, const void* k, const void* v, int n_kv, const u
                    uint16_t* out, void* stream);
 int launch_combine(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale, int n_splits,
                    const float* ws_acc, const float* ws_ml, uint16_t* out, void* stream);
+int launch_tile_stats(const Geo& G, const DevBufs& B, int seq, int first, int n, int32_t* out, void* stream);
+int launch_coverage(const Geo& G, const void* x, int n, int w, int32_t* out, void* stream);
 // Device address of the current device's KVC_NOALLOC_WS_BYTES split workspace (resolved once per
 // device; later calls only look it up).  Returns a hipError_t as int.
 int noalloc_workspace(void** ptr);

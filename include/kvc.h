@@ -244,6 +244,35 @@ int kv_decode_step(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs
 int kv_decode_attention_noalloc(kvc_cache* cache, const int32_t* seq_ids_host, int32_t n_seqs, const void* q_dev,
                                 float scale, int32_t n_splits, void* out_dev, void* stream);
 
+/* Storage statistics of finished blocks first_block .. first_block+n_blocks-1 of one sequence,
+ * read on the device from the table entries and the stored tag planes (GAAC page App. C studies
+ * escape bytes per tile and raw fallbacks along the context).  out_dev: [n_blocks][2 (K,V)][Hkv]
+ * [6] int32, 4-byte aligned: {state: 0 compressed, 1 raw, -1 unallocated; bytes: FORMAT v1 the
+ * escape bytes the tile's tags call for, FORMAT v2 its code bytes, 0 for raw tiles; groups per
+ * mode index [4] (compressed tiles)}.  Enqueued; KVC_EINVAL for blocks past the finished ones. */
+int kv_tile_stats(kvc_cache* cache, int32_t seq, int32_t first_block, int32_t n_blocks, int32_t* out_dev,
+                  void* stream);
+
+/* Exponent concentration (GAAC page §3.1: most exponents of a head-channel lie in a few
+ * consecutive values): for each (kv-head h, channel c) of x_dev [n_tokens][Hkv][D] elements of
+ * the cache's format, out_dev[h][c] (int32) = the largest number of its n_tokens exponents
+ * inside any window of `window` consecutive exponent values.  1 <= window <= 2^(exponent bits)
+ * (KVC_EINVAL otherwise).  Enqueued; the cache supplies the format and geometry only. */
+int kv_window_coverage(kvc_cache* cache, const void* x_dev, int32_t n_tokens, int32_t window, int32_t* out_dev,
+                       void* stream);
+
+/* Equal-memory admission (GAAC page §4.5: more sequences in the same KV memory): plans the slot
+ * pools one layer's budget_bytes buys for caches of these parameters (their slot counts are
+ * ignored) and admits requests first come, first served.  A compressed cache spends raw_share
+ * of the budget on raw-fallback slots (whole raw tiles) and the rest on compressed slots (slot
+ * stride each); an uncompressed cache spends all of it on raw slots.  Requests of
+ * lengths_host[0 .. n_requests) tokens are admitted in order while the main pool still holds
+ * each one's finished blocks plus one spare block (2 * Hkv slots per block); the first that does
+ * not fit stops admission.  Outputs the admitted count and the two pool sizes.  Host only; the
+ * budget pays for slots only (tables, tails and counters are not counted). */
+int kv_admit_fcfs(const kvc_params* params, uint64_t budget_bytes, double raw_share, const int32_t* lengths_host,
+                  int32_t n_requests, int32_t* n_admitted, int32_t* num_comp_slots, int32_t* num_raw_slots);
+
 /* Returns every slot of a sequence to the free stacks and empties it (enqueued). */
 int kv_release_seq(kvc_cache* cache, int32_t seq, void* stream);
 

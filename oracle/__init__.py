@@ -260,6 +260,19 @@ def v2_decode_tiles(p: Params, mode_set: int, data, is_raw, is_v, b2, b3, b4, nt
     return out, status
 
 
+def window_coverage(p: Params, x: np.ndarray, w: int) -> np.ndarray:
+    """Per channel of x [n_tokens][D]: the most exponents inside any window of w consecutive
+    exponent values -> [D] int32."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    out = np.zeros(p.D, np.int32)
+    L = lib()
+    L.orc_window_coverage.argtypes = [ctypes.POINTER(_Params), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p]
+    if L.orc_window_coverage(ctypes.byref(p.c()), _ptr(x), x.shape[0], w, _ptr(out)) != 0:
+        raise ValueError("window coverage: invalid arguments")
+    return out
+
+
 def value(fmt: int, bits: int) -> float:
     return lib().orc_value(fmt, bits)
 

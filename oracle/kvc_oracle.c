@@ -192,6 +192,27 @@ int orc_calibrate(const orc_params* p, const uint16_t* x, int32_t n_tokens, uint
   return ORC_OK;
 }
 
+/* Exponent concentration (§3.1: most exponents of a head-channel fall in a few consecutive
+ * values): for each channel of x [n_tokens][D], the largest number of its exponents inside any
+ * window of w consecutive exponent values [b, b + w - 1], 0 <= b <= 2^F - w. */
+int orc_window_coverage(const orc_params* p, const uint16_t* x, int32_t n_tokens, int32_t w, int32_t* out) {
+  orc_layout L;
+  if (orc_layout_of(p, &L) != ORC_OK || n_tokens < 0 || w < 1 || w > (1 << L.F)) return ORC_EINVAL;
+  long hist[256];
+  for (int c = 0; c < p->D; ++c) {
+    for (int e = 0; e < 256; ++e) hist[e] = 0;
+    for (int t = 0; t < n_tokens; ++t) hist[f_exp(&L, x[(long)t * p->D + c])] += 1;
+    long best = 0;
+    for (int b = 0; b + w <= (1 << L.F); ++b) {
+      long s = 0;
+      for (int e = b; e < b + w; ++e) s += hist[e];
+      if (s > best) best = s;
+    }
+    out[c] = (int32_t)best;
+  }
+  return ORC_OK;
+}
+
 /* ---- encode / decode of one tile ---------------------------------------------------- */
 
 static int group_mode(const orc_layout* L, uint32_t mn, uint32_t mx, uint32_t b3, uint32_t b4) {

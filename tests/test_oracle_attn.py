@@ -144,3 +144,36 @@ def test_lossless_invariant_on_cfg0(orc):
     a = orc.attention(orc.BF16, q, k, v, cfg.scale)
     b = orc.attention(orc.BF16, q, kd, vd, cfg.scale)
     assert np.array_equal(a, b)
+
+
+# ---- exponent concentration (§3.1) ---------------------------------------------------------
+
+def test_window_coverage_pins(orc):
+    """The best window of w consecutive exponents, pinned by a different algorithm (a two-pointer
+    sweep over the sorted exponents) and by closed forms: w = 2^F covers every token, equal
+    exponents are covered by any window, w = 1 is the largest histogram bin."""
+    rng = np.random.default_rng(3)
+    for fmt, F, MB in ((orc.BF16, 8, 7), (orc.E5M2, 5, 2), (orc.E4M3, 4, 3)):
+        p = orc.Params(fmt, 16, 32, 16, esc_cap=0)
+        e = np.clip(rng.normal(rng.integers(2, (1 << F) - 2, 32), rng.uniform(0.3, 4, 32), (300, 32)), 0,
+                    (1 << F) - 1).astype(np.uint16)
+        x = np.ascontiguousarray(e << MB)
+        for w in (1, 2, 6, 8, 16, 1 << F):
+            if w > (1 << F):
+                continue
+            got = orc.window_coverage(p, x, w)
+            for c in range(32):
+                s = np.sort(e[:, c].astype(np.int64))
+                best, lo = 0, 0
+                for hi in range(len(s)):      # largest run of sorted values within w consecutive ones
+                    while s[hi] - s[lo] >= w:
+                        lo += 1
+                    best = max(best, hi - lo + 1)
+                assert got[c] == best, (fmt, w, c)
+            if w == (1 << F):
+                assert (got == 300).all()
+            if w == 1:
+                assert all(got[c] == np.bincount(e[:, c]).max() for c in range(32))
+        same = np.ascontiguousarray(np.full((50, 32), 3 << MB, np.uint16))
+        assert (orc.window_coverage(p, same, 2) == 50).all()
+
