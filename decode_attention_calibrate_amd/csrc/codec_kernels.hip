@@ -1474,8 +1474,10 @@ __global__ void __launch_bounds__(kThreads) attn_half_kernel(HalfAttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Prefill attention (GAAC page §3.3: prefill runs standard attention over blocks rebuilt by
-// the block decoder).  Causal: query i of n_q (token position n_kv - n_q + i) attends tokens
+// Prefill attention over blocks rebuilt by the block decoder (GAAC page §3.3 encodes a prompt's
+// complete blocks during prefill and says nothing about how prefill attention reads them; this
+// library runs standard causal attention on the rebuilt blocks).  Causal: query i of n_q (token
+// position n_kv - n_q + i) attends tokens
 // 0 .. its own position.  One 256-thread workgroup per (64 queries, query head), 16 queries
 // per wave; key blocks of KB tokens (64, or 32 for 256-channel heads) go to LDS as BF16 (K as
 // rows, V transposed); QK and PV on v_mfma_f32_16x16x32_bf16 (P as a BF16 high part plus

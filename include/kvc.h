@@ -170,7 +170,9 @@ int kv_decode_blocks(kvc_cache* cache, int32_t seq, int32_t first_block, int32_t
                      void* v_out_dev, void* stream);
 
 /* Causal prefill attention over K/V in plain element tensors, e.g. the blocks kv_decode_blocks
- * rebuilt (GAAC page §3.3: prefill runs standard attention on decoded blocks).  k_dev, v_dev:
+ * rebuilt.  GAAC page §3.3 encodes a prompt's complete blocks during prefill and leaves the
+ * incomplete suffix uncompressed; it does not say how prefill attention reads them.  This
+ * library's reading: standard causal attention over the rebuilt blocks.  k_dev, v_dev:
  * [n_kv][Hkv][D] elements of the cache's format (the sequence's first n_kv tokens); q_dev:
  * [n_q][Hq][D] BF16, the queries of positions n_kv - n_q .. n_kv - 1; out_dev: [n_q][Hq][D] BF16
  * (round-to-nearest-even of an fp32 result).  Query i attends tokens 0 .. n_kv - n_q + i with

@@ -1,5 +1,6 @@
-"""GPU causal prefill attention over blocks rebuilt by kv_decode_blocks (GAAC page §3.3: the
-prefill runs standard attention on decoded blocks) through the C ABI.  Every query row against
+"""GPU causal prefill attention over blocks rebuilt by kv_decode_blocks (GAAC page §3.3 encodes a
+prompt's complete blocks during prefill; attending the rebuilt blocks with standard causal
+attention is this library's reading) through the C ABI.  Every query row against
 the oracle's exact fp64 attention over the tokens up to its position: per (query, head) row,
 max_c |o - r| / max_c |r| <= 4e-3."""
 import dataclasses
