@@ -1518,8 +1518,9 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   const int D = G.D, Hkv = G.Hkv, Hq = G.Hq, g = G.g, EB = G.EB, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6, col = lane & 15, kq = lane >> 4;
   const int KB = D > 128 ? 32 : 64;  // keys per block in LDS
-  // the last query tiles attend the most keys: they go first (longest processing time first)
-  const int q0 = (gridDim.x - 1 - blockIdx.x) * QT, hq = blockIdx.y, h = hq / g;
+  // the last query tiles attend the most keys: they go first (longest processing time first);
+  // heads are the fastest grid dimension, so every head's longest tiles precede all shorter ones
+  const int q0 = (gridDim.y - 1 - blockIdx.y) * QT, hq = blockIdx.x, h = hq / g;
   const int pos0 = a.n_kv - a.n_q;   // position of query 0
   const int nq = min(QT, a.n_q - q0);
   __shared__ __align__(16) uint16_t kl[64 * 128];     // key block, BF16 bits, [t][c]
@@ -1775,7 +1776,7 @@ int launch_prefill(const Geo& G, const void* k, const void* v, int n_kv, const u
   a.n_q = n_q;
   a.sl2 = scale * 1.4426950408889634f;
   auto kern = G.fmt == 0 ? prefill_kernel<0> : G.fmt == 1 ? prefill_kernel<1> : prefill_kernel<2>;
-  hipLaunchKernelGGL(kern, dim3((n_q + 63) / 64, G.Hq), dim3(kThreads), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(kern, dim3(G.Hq, (n_q + 63) / 64), dim3(kThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
