@@ -307,6 +307,7 @@ def main():
     bytes_c = comp_kv_bytes + q_bytes + table_bytes
     bytes_r = raw_kv_bytes + q_bytes + table_bytes
     achieved = bytes_c / (attn_c * 1e-6) / 1e9
+    attain = attainable_read(torch, K, stream, bytes_c)
     digest = kernel_source_digest()
     traffic = counter_traffic(digest, S, n_layers)
     value_us = c_total * 1e3 / args.steps
@@ -356,7 +357,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "attn_comp_kernel<4,64>", "bytes_per_launch": bytes_c,
-                     "source_digest": digest},
+                     "source_digest": digest, "attainable_GBps": attain["GBps"],
+                     "frac_of_attainable": round(achieved / attain["GBps"], 4)},
+        "attainable_read": attain,
         "sweep_attention_us": sweep or None,
         "hbm_probe": probe,
     }
@@ -827,6 +830,34 @@ def counter_traffic(digest, splits, layers):
         return int(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def attainable_read(torch, K, stream, nbytes, waves=2048, n_buf=8, reps=48):
+    """The library's streaming-read kernel (kv_read_probe) at the split attention kernel's launch
+    shape -- `waves` workgroups of one wave, here one per wave slot of the chip -- reading about
+    nbytes per launch, rotated over n_buf buffers so every launch reads from HBM: the read rate
+    this launch shape attains on the GPU at hand, beside the 8 TB/s peak."""
+    per = max(8192, int(round(nbytes / waves / 8192)) * 8192)
+    bufs = [torch.zeros(waves * per // 4, dtype=torch.int32, device="cuda") for _ in range(n_buf)]
+    sink = torch.empty((waves, 64), dtype=torch.int32, device="cuda")
+    for i in range(2 * n_buf):
+        K.read_probe(bufs[i % n_buf], per, waves, sink)
+    torch.cuda.synchronize()
+    a_ = torch.cuda.Event(enable_timing=True)
+    b_ = torch.cuda.Event(enable_timing=True)
+    a_.record(stream)
+    for i in range(reps):
+        K.read_probe(bufs[i % n_buf], per, waves, sink)
+    b_.record(stream)
+    torch.cuda.synchronize()
+    us = a_.elapsed_time(b_) * 1e3 / reps
+    out = {"GBps": round(waves * per / (us * 1e-6) / 1e9, 1), "us": round(us, 3), "bytes_per_launch": waves * per,
+           "waves": waves, "bytes_per_wave": per, "buffers_rotated": n_buf,
+           "method": "kv_read_probe launched back to back, events at the loop ends"}
+    log(f"[bench] attainable read: {out}")
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return out
 
 
 def hbm_probe(torch, stream, nbytes=2 << 30, reps=10):

@@ -11,7 +11,7 @@ libkvc.so has not been built; there is no CPU fallback.
 """
 from ._lib import (BF16, FP8_E4M3, FP8_E5M2, KVCError, LIB_PATH, STATUS_COMP_EXHAUSTED, STATUS_CORRUPT,
                    STATUS_MISSING_BLOCK, STATUS_RAW_EXHAUSTED, load)
-from .cache import KVCache, admit_fcfs
+from .cache import KVCache, admit_fcfs, read_probe
 
-__all__ = ["KVCache", "admit_fcfs", "KVCError", "load", "LIB_PATH", "BF16", "FP8_E5M2", "FP8_E4M3", "STATUS_COMP_EXHAUSTED",
+__all__ = ["KVCache", "admit_fcfs", "read_probe", "KVCError", "load", "LIB_PATH", "BF16", "FP8_E5M2", "FP8_E4M3", "STATUS_COMP_EXHAUSTED",
            "STATUS_RAW_EXHAUSTED", "STATUS_MISSING_BLOCK", "STATUS_CORRUPT"]

@@ -58,6 +58,7 @@ SIGNATURES = {
     "kv_decode_step": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, _vp, _vp, ctypes.c_float, _i32, _vp, _sz, _vp, _vp]),
     "kv_tile_stats": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "kv_window_coverage": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "kv_read_probe": (ctypes.c_int, [_vp, ctypes.c_uint64, _i32, _vp, _vp]),
     "kv_admit_fcfs": (ctypes.c_int, [_P(Params), _u64, ctypes.c_double, _P(_i32), _i32, _P(_i32), _P(_i32),
                                      _P(_i32)]),
     "kv_release_seq": (ctypes.c_int, [_vp, _i32, _vp]),

@@ -249,3 +249,20 @@ def admit_fcfs(*, num_kv_heads: int, head_dim: int, block_tokens: int, budget_by
                               ctypes.byref(nc), ctypes.byref(nr)))
     return n.value, nc.value, nr.value
 
+
+
+def read_probe(src: torch.Tensor, bytes_per_wave: int, waves: int, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """kv_read_probe over the first waves * bytes_per_wave bytes of the contiguous device tensor
+    src, enqueued on src's current stream; returns the [waves][64] int32 checksum words (sink)."""
+    lib = L.load()
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    if src.numel() * src.element_size() < waves * bytes_per_wave:
+        raise ValueError("src holds fewer than waves * bytes_per_wave bytes")
+    if sink is None:
+        sink = torch.empty((waves, 64), dtype=torch.int32, device=src.device)
+    elif not sink.is_cuda or not sink.is_contiguous() or sink.numel() * sink.element_size() < waves * 256:
+        raise ValueError("sink must be a contiguous device tensor of waves * 64 32-bit words")
+    L.check(lib.kv_read_probe(_ptr(src), int(bytes_per_wave), int(waves), _ptr(sink),
+                              ctypes.c_void_p(torch.cuda.current_stream(src.device).cuda_stream)))
+    return sink

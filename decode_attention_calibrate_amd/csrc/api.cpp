@@ -516,6 +516,14 @@ int kv_window_coverage(kvc_cache* c, const void* x_dev, int32_t n_tokens, int32_
   return hip_fail(kvc::launch_coverage(c->G, x_dev, n_tokens, window, out_dev, stream), "launch coverage");
 }
 
+int kv_read_probe(const void* src_dev, uint64_t bytes_per_wave, int32_t waves, uint32_t* sink_dev, void* stream) {
+  if (!src_dev || !sink_dev) return fail(KVC_EINVAL, "read probe needs src and sink");
+  if (((uintptr_t)src_dev & 15u) || ((uintptr_t)sink_dev & 3u)) return fail(KVC_EINVAL, "src must be 16-byte, sink 4-byte aligned");
+  if (bytes_per_wave == 0 || bytes_per_wave % KVC_READ_PROBE_UNIT) return fail(KVC_EINVAL, "bytes_per_wave must be a positive multiple of 8192");
+  if (waves < 1 || waves > (1 << 20)) return fail(KVC_EINVAL, "waves must be in 1 .. 2^20");
+  return hip_fail(kvc::launch_read_probe(src_dev, (size_t)bytes_per_wave, waves, sink_dev, stream), "launch read probe");
+}
+
 int kv_admit_fcfs(const kvc_params* params, uint64_t budget_bytes, double raw_share, const int32_t* lengths_host,
                   int32_t n_requests, int32_t* n_admitted, int32_t* num_comp_slots, int32_t* num_raw_slots) {
   if (!params || !n_admitted || !num_comp_slots || !num_raw_slots) return fail(KVC_EINVAL, "NULL argument");

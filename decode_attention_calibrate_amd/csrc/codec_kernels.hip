@@ -743,10 +743,13 @@ __global__ void tile_stats_kernel(Geo G, DevBufs B, int seq, int first, int n, i
 // Exponent concentration (GAAC page §3.1: most exponents of a head-channel lie in a few
 // consecutive values): one block per (channel, kv-head), the largest number of the n tokens'
 // exponents inside any window of w consecutive exponent values.  x: [n][Hkv][D] elements.
+// Block b takes head b % Hkv: workgroups are dealt to the eight XCDs round robin, so with 8
+// (or a divisor of 8) heads all channels of a head run on one XCD and share its L2 copy of the
+// head's token rows instead of every XCD fetching every row.
 __global__ void coverage_kernel(Geo G, const void* __restrict__ x, int n, int w, int32_t* __restrict__ out) {
   __shared__ int hist[256];
   __shared__ int red[8];
-  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int c = blockIdx.x / G.Hkv, h = blockIdx.x % G.Hkv, tid = threadIdx.x;
   hist[tid] = 0;
   __syncthreads();
   for (int t = tid; t < n; t += kThreads) atomicAdd(&hist[exp_of(G, elem_at(x, ((size_t)t * G.Hkv + h) * G.D + c, G.EB))], 1);
@@ -757,6 +760,32 @@ __global__ void coverage_kernel(Geo G, const void* __restrict__ x, int n, int w,
     for (int e = tid; e < tid + w; ++e) cov += hist[e];
   const int best = block_max(cov, red);
   if (tid == 0) out[(size_t)h * G.D + c] = best;
+}
+
+// Streaming-read probe: one 64-lane wave per workgroup (the split attention kernels' shape);
+// wave w reads n16 16-byte words from src + w * n16 with eight 16-byte loads per lane per batch,
+// the next batch in flight while the current one is folded into a checksum, and writes one
+// checksum word per lane (so no load is dead).  n16 is a multiple of 512.
+__global__ void __launch_bounds__(64) read_probe_kernel(const uint4* __restrict__ src, size_t n16,
+                                                        uint32_t* __restrict__ sink) {
+  constexpr int U = 8;
+  const uint4* p = src + (size_t)blockIdx.x * n16 + threadIdx.x;
+  const size_t nb = n16 / (64 * U);
+  uint4 a[U], b[U];
+  uint32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) a[u] = p[64 * u];
+  for (size_t i = 0; i < nb; ++i) {
+    if (i + 1 < nb) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) b[u] = p[(i + 1) * 64 * U + 64 * u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = acc * 31u + (a[u].x ^ a[u].y ^ a[u].z ^ a[u].w);
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = b[u];
+  }
+  sink[(size_t)blockIdx.x * 64 + threadIdx.x] = acc;
 }
 
 // Writes the appended tokens that do not complete a block into the sequence's tail.
@@ -1704,7 +1733,13 @@ int launch_tile_stats(const Geo& G, const DevBufs& B, int seq, int first, int n,
 }
 
 int launch_coverage(const Geo& G, const void* x, int n, int w, int32_t* out, void* stream) {
-  hipLaunchKernelGGL(coverage_kernel, dim3(G.D, G.Hkv), dim3(kThreads), 0, (hipStream_t)stream, G, x, n, w, out);
+  hipLaunchKernelGGL(coverage_kernel, dim3(G.D * G.Hkv), dim3(kThreads), 0, (hipStream_t)stream, G, x, n, w, out);
+  return (int)hipGetLastError();
+}
+
+int launch_read_probe(const void* src, size_t bytes_per_wave, int waves, uint32_t* sink, void* stream) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(waves), dim3(64), 0, (hipStream_t)stream,
+                     reinterpret_cast<const uint4*>(src), bytes_per_wave / 16, sink);
   return (int)hipGetLastError();
 }
 

@@ -140,6 +140,7 @@ int launch_combine(const Geo& G, const DevBufs& B, const SeqList& seqs, const ui
                    const float* ws_acc, const float* ws_ml, uint16_t* out, void* stream);
 int launch_tile_stats(const Geo& G, const DevBufs& B, int seq, int first, int n, int32_t* out, void* stream);
 int launch_coverage(const Geo& G, const void* x, int n, int w, int32_t* out, void* stream);
+int launch_read_probe(const void* src, size_t bytes_per_wave, int waves, uint32_t* sink, void* stream);
 // Device address of the current device's KVC_NOALLOC_WS_BYTES split workspace (resolved once per
 // device; later calls only look it up).  Returns a hipError_t as int.
 int noalloc_workspace(void** ptr);

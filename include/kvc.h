@@ -275,6 +275,19 @@ int kv_window_coverage(kvc_cache* cache, const void* x_dev, int32_t n_tokens, in
 int kv_admit_fcfs(const kvc_params* params, uint64_t budget_bytes, double raw_share, const int32_t* lengths_host,
                   int32_t n_requests, int32_t* n_admitted, int32_t* num_comp_slots, int32_t* num_raw_slots);
 
+/* Streaming-read probe, a measurement aid rather than an operation of the page (its case for
+ * compressing the cache, GAAC page §1 and §3.2, is that decode attention is bound by reading
+ * it): `waves` workgroups of one 64-lane wave, the split attention kernels' launch shape; wave w
+ * reads bytes_per_wave contiguous bytes of src_dev from offset w * bytes_per_wave with 16-byte
+ * loads, the next 8 KiB batch in flight while the current one is consumed, and writes one
+ * checksum word per lane to sink_dev[w * 64 + lane].  Reads waves * bytes_per_wave bytes of
+ * src_dev (caller-owned, 16-byte aligned) and writes waves * 64 uint32 words of sink_dev
+ * (caller-owned, 4-byte aligned).  bytes_per_wave must be a positive multiple of
+ * KVC_READ_PROBE_UNIT and 1 <= waves <= 2^20, else KVC_EINVAL.  Enqueued on stream; time it
+ * with events to get the attainable read rate the attention kernels are measured against. */
+#define KVC_READ_PROBE_UNIT 8192u
+int kv_read_probe(const void* src_dev, uint64_t bytes_per_wave, int32_t waves, uint32_t* sink_dev, void* stream);
+
 /* Returns every slot of a sequence to the free stacks and empties it (enqueued). */
 int kv_release_seq(kvc_cache* cache, int32_t seq, void* stream);
 

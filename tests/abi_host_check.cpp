@@ -67,6 +67,12 @@ int main() {
   bad |= expect(kv_prefill_attention(nullptr, fake, fake, 1, fake, 1, 1.f, fake, nullptr), KVC_EINVAL, "prefill");
   bad |= expect(kv_tile_stats(nullptr, 0, 0, 1, (int32_t*)fake, nullptr), KVC_EINVAL, "tile stats");
   bad |= expect(kv_window_coverage(nullptr, fake, 1, 6, (int32_t*)fake, nullptr), KVC_EINVAL, "coverage");
+  bad |= expect(kv_read_probe(nullptr, 8192, 1, (uint32_t*)fake, nullptr), KVC_EINVAL, "probe NULL src");
+  bad |= expect(kv_read_probe(fake, 8192, 1, nullptr, nullptr), KVC_EINVAL, "probe NULL sink");
+  bad |= expect(kv_read_probe(odd, 8192, 1, (uint32_t*)fake, nullptr), KVC_EINVAL, "probe misaligned src");
+  bad |= expect(kv_read_probe(fake, 4096, 1, (uint32_t*)fake, nullptr), KVC_EINVAL, "probe ragged bytes");
+  bad |= expect(kv_read_probe(fake, 0, 1, (uint32_t*)fake, nullptr), KVC_EINVAL, "probe zero bytes");
+  bad |= expect(kv_read_probe(fake, 8192, 0, (uint32_t*)fake, nullptr), KVC_EINVAL, "probe zero waves");
   bad |= expect(kv_release_seq(nullptr, 0, nullptr), KVC_EINVAL, "release");
   bad |= expect(kv_seq_length(nullptr, 0, &len), KVC_EINVAL, "length");
   bad |= expect(kv_get_status(nullptr, &flags, nullptr, nullptr), KVC_EINVAL, "status");

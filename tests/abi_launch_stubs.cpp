@@ -27,5 +27,6 @@ int launch_combine(const Geo&, const DevBufs&, const SeqList&, const uint16_t*, 
                    uint16_t*, void*) { return kNoDevice; }
 int launch_tile_stats(const Geo&, const DevBufs&, int, int, int, int32_t*, void*) { return kNoDevice; }
 int launch_coverage(const Geo&, const void*, int, int, int32_t*, void*) { return kNoDevice; }
+int launch_read_probe(const void*, size_t, int, uint32_t*, void*) { return kNoDevice; }
 int noalloc_workspace(void** ptr) { *ptr = nullptr; return kNoDevice; }
 }  // namespace kvc

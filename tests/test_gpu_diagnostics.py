@@ -72,3 +72,25 @@ def test_window_coverage_matches_oracle(fmt):
             assert np.array_equal(got, want), (fmt, w)
     with pytest.raises(Exception):
         c.window_coverage(dev(k, fmt), (1 << F) + 1)
+
+
+def test_read_probe_reads_every_byte():
+    """kv_read_probe: every lane's checksum equals the fold of exactly the 16-byte words the
+    probe is documented to read (wave w's region, batch by batch, four words per lane), and
+    misshaped requests are refused."""
+    import decode_attention_calibrate_amd as K
+    rng = np.random.default_rng(11)
+    waves, per = 5, 3 * 8192
+    words = rng.integers(0, 1 << 32, size=(waves * per) // 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32).copy()).cuda()
+    got = K.read_probe(src, per, waves).cpu().numpy().view(np.uint32)
+    w4 = words.reshape(waves, per // 16, 4)
+    x = (w4[..., 0] ^ w4[..., 1] ^ w4[..., 2] ^ w4[..., 3]).astype(np.uint64)   # [wave][16-byte word]
+    want = np.zeros((waves, 64), np.uint64)
+    for i in range(per // 8192):
+        for u in range(8):
+            want = (want * 31 + x[:, i * 512 + 64 * u + np.arange(64)]) & 0xFFFFFFFF
+    assert np.array_equal(got, want.astype(np.uint32))
+    for nbytes, nw in ((8192 + 4096, 1), (0, 1), (8192, 0)):  # refused by the library's own checks
+        with pytest.raises(K.KVCError):
+            K.read_probe(src, nbytes, nw)

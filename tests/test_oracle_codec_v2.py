@@ -148,18 +148,29 @@ def test_v2_mode_choice_is_the_narrowest_fitting_window(orc, ms):
         assert np.array_equal(got, want), (ms, start)
 
 
-def test_v2_calibration_2bit_bruteforce(orc):
+@pytest.mark.parametrize("w", [2, 3, 4])
+def test_v2_calibration_bruteforce(orc, w):
+    """The base of every window width (2-, 3- and 4-bit offsets) against a brute force over all
+    window starts: the lower median of the starts of maximal coverage."""
     p = orc.Params(orc.BF16, 16, 4, 16, esc_cap=0)
-    rng = np.random.default_rng(9)
+    rng = np.random.default_rng(9 + w)
+    n = 1 << w
     for trial in range(40):
         e = rng.integers(100, 140, (256, 4)) if trial % 2 else rng.normal(120, 3, (256, 4)).astype(int)
+        if trial % 5 == 0:
+            e[:, 1] = 0          # a window that must start at 0
+            e[:, 2] = 255        # and one pressed against the top of the field
         x = (np.clip(e, 0, 255).astype(np.uint16) << 7)
-        b = orc.v2_calibrate(p, x, 2)
+        b = orc.v2_calibrate(p, x, w)
         for c in range(4):
             hist = np.bincount((x[:, c] >> 7) & 0xFF, minlength=256)
-            cov = np.array([hist[s:s + 4].sum() for s in range(253)])
+            cov = np.array([hist[s:s + n].sum() for s in range(256 - n + 1)])
             ties = np.nonzero(cov == cov.max())[0]
-            assert b[c] == ties[(len(ties) - 1) // 2]
+            assert b[c] == ties[(len(ties) - 1) // 2], (w, trial, c)
+    if w > 2:  # the 3- and 4-bit bases are FORMAT v1's b3 and b4
+        x = (rng.integers(90, 150, (256, 4)).astype(np.uint16) << 7)
+        b3, b4 = orc.calibrate(p, x)
+        assert np.array_equal(orc.v2_calibrate(p, x, w), b3 if w == 3 else b4)
 
 
 @pytest.mark.parametrize("G", [8, 16])
