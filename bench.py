@@ -589,8 +589,10 @@ def rope_drift(torch, K, synth, cfg, k0, v0, dev, seg=8192):
     the mean escape bytes of the compressed K and V tiles (from their stored tag planes) and the
     share of tiles stored raw.  Policies: unrotated keys, first 256 tokens; rotated keys
     calibrated on the first 256, 8K or 32K tokens, or on 256 tokens spread evenly over the
-    context (same calibration budget as the first, spread over the positions).  The per-tile
-    figures come from kv_tile_stats (read on the device from the stored tag planes)."""
+    context (same calibration budget as the first, spread over the positions); and a live cache
+    recalibrated (kv_recalibrate) before each 16K-token chunk on the 256 tokens just before it.
+    The per-tile figures come from kv_tile_stats (read on the device from the stored tag planes
+    and table entries)."""
     T, D, Hkv, Hq = cfg.T, cfg.D, cfg.Hkv, cfg.Hq
     L0 = k0.shape[0]
     nb = L0 // T
@@ -599,13 +601,8 @@ def rope_drift(torch, K, synth, cfg, k0, v0, dev, seg=8192):
                 ("first8k", kr, np.arange(8192)), ("first32k", kr, np.arange(32768)),
                 ("spread256", kr, np.arange(0, L0, L0 // 256))]
     res = {"workload": "qwen3-8b-like-64k, RoPE theta 1e6 on K", "segment_tokens": seg, "block_tokens": T}
-    for name, ks, cal in policies:
-        c = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=1,
-                      max_blocks_per_seq=nb + 1, num_comp_slots=(nb + 1) * 2 * Hkv, num_raw_slots=(nb + 1) * 2 * Hkv,
-                      compressed=True, perm_seed=7)
-        c.calibrate(dev(ks[cal]), dev(v0[cal]))
-        c.append([0], dev(ks[None]), dev(v0[None]))
-        stats = c.tile_stats(0, 0, nb)            # kv_tile_stats: [nb][2][Hkv][6] {state, escape bytes, modes}
+    def summary(c):
+        stats = c.tile_stats(0, 0, nb)            # kv_tile_stats: [nb][2][Hkv][7] {state, escape bytes, modes, version}
         raw = stats[..., 0] == 1
         esc = stats[..., 1].double()
         segs = []
@@ -616,10 +613,34 @@ def rope_drift(torch, K, synth, cfg, k0, v0, dev, seg=8192):
                 n_comp = int((~r).sum())
                 row[f"{nm}_esc_bytes_per_tile"] = round(float(esc[s0:s0 + seg // T, kv].sum()) / max(n_comp, 1), 1)
                 row[f"{nm}_raw_tile_share"] = round(float(r.double().mean()), 4)
+            row["base_versions"] = sorted({int(x) for x in stats[s0:s0 + seg // T, ..., 6].flatten().tolist() if x >= 0})
             segs.append(row)
         flags, st = c.status()
-        res[name] = {"segments": segs, "raw_tiles": st["raw_tiles"], "status_flags": flags}
+        return {"segments": segs, "raw_tiles": st["raw_tiles"], "status_flags": flags}
+
+    def new_cache(versions=1):
+        return K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=1,
+                         max_blocks_per_seq=nb + 1, num_comp_slots=(nb + 1) * 2 * Hkv,
+                         num_raw_slots=(nb + 1) * 2 * Hkv, compressed=True, perm_seed=7, base_versions=versions)
+
+    for name, ks, cal in policies:
+        c = new_cache()
+        c.calibrate(dev(ks[cal]), dev(v0[cal]))
+        c.append([0], dev(ks[None]), dev(v0[None]))
+        res[name] = summary(c)
         del c
+    # live recalibration (kv_recalibrate): calibrated on the first 256 tokens; before each further
+    # 16K-token chunk is appended, a new base version from the 256 tokens just before it (four
+    # versions in all); stored blocks keep the version they were encoded with
+    chunk = 16384
+    c = new_cache(versions=4)
+    c.calibrate(dev(kr[:256]), dev(v0[:256]))
+    for s0 in range(0, L0, chunk):
+        if s0 > 0:
+            c.recalibrate(dev(kr[s0 - 256:s0]), dev(v0[s0 - 256:s0]))
+        c.append([0], dev(kr[None, s0:s0 + chunk]), dev(v0[None, s0:s0 + chunk]))
+    res["live_recalibration_every_16k"] = summary(c)
+    del c
     log(f"[bench] rope drift: {res}")
     return res
 

@@ -21,7 +21,8 @@ BUFFER_NAMES = ("comp_pool", "raw_pool", "tail", "bases", "block_table", "comp_f
 class Params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "dtype", "num_kv_heads", "num_q_heads", "head_dim", "block_tokens", "group_tokens", "esc_cap_bytes",
-        "compressed", "max_seqs", "max_blocks_per_seq", "num_comp_slots", "num_raw_slots", "mode_set")]
+        "compressed", "max_seqs", "max_blocks_per_seq", "num_comp_slots", "num_raw_slots", "mode_set",
+        "base_versions")]
 
 
 class Buffers(ctypes.Structure):
@@ -47,6 +48,7 @@ SIGNATURES = {
     "kv_cache_create": (ctypes.c_int, [_P(Params), _P(Buffers), _u64, _vp, _P(_vp)]),
     "kv_cache_destroy": (None, [_vp]),
     "kv_calibrate": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
+    "kv_recalibrate": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
     "kv_encode_append": (ctypes.c_int, [_vp, _P(_i32), _i32, _vp, _vp, _i32, _vp]),
     "kv_decode_blocks": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "kv_prefill_attention": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _i32, ctypes.c_float, _vp, _vp]),

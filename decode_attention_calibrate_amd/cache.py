@@ -28,15 +28,16 @@ class KVCache:
     def __init__(self, *, num_kv_heads: int, num_q_heads: int, head_dim: int, block_tokens: int,
                  max_seqs: int, max_blocks_per_seq: int, num_comp_slots: int, num_raw_slots: int,
                  compressed: bool = True, group_tokens: int = 16, esc_cap_bytes: int = -1, dtype: int = L.BF16,
-                 device: str | torch.device = "cuda", perm_seed: int = 0, mode_set: int = 0):
+                 device: str | torch.device = "cuda", perm_seed: int = 0, mode_set: int = 0, base_versions: int = 1):
         self.lib = L.load()
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self.params = L.Params(dtype, num_kv_heads, num_q_heads, head_dim, block_tokens, group_tokens, esc_cap_bytes,
                                1 if compressed else 0, max_seqs, max_blocks_per_seq, num_comp_slots, num_raw_slots,
-                               mode_set)
+                               mode_set, base_versions)
         self.mode_set = mode_set
+        self.base_versions = max(1, base_versions)
         sizes = (ctypes.c_size_t * L.NUM_BUFFERS)()
         stride = ctypes.c_size_t()
         L.check(self.lib.kv_buffer_sizes(ctypes.byref(self.params), sizes, ctypes.byref(stride)))
@@ -75,6 +76,15 @@ class KVCache:
         if k.shape != v.shape:
             raise ValueError("k and v differ in shape")
         L.check(self.lib.kv_calibrate(self.handle, _ptr(k), _ptr(v), k.shape[0], self._stream()))
+
+    def recalibrate(self, k: torch.Tensor, v: torch.Tensor):
+        """kv_recalibrate: a new base version from k, v [n][Hkv][D] element bits for the blocks
+        finished from now on; stored blocks keep theirs."""
+        _elem(k, "k", self.EB), _elem(v, "v", self.EB)
+        self._shape(k, "k", 1), self._shape(v, "v", 1)
+        if k.shape != v.shape:
+            raise ValueError("k and v differ in shape")
+        L.check(self.lib.kv_recalibrate(self.handle, _ptr(k), _ptr(v), k.shape[0], self._stream()))
 
     def append(self, seq_ids, k: torch.Tensor, v: torch.Tensor):
         """k, v: [n_seqs][n_tokens][Hkv][D] element bits."""
@@ -193,8 +203,9 @@ class KVCache:
 
     # ---- diagnostics ----
     def tile_stats(self, seq: int, first: int, n: int) -> torch.Tensor:
-        """kv_tile_stats: [n][2][Hkv][6] int32 {state, bytes, groups per mode index [4]}."""
-        out = torch.empty((n, 2, self.Hkv, 6), dtype=torch.int32, device=self.device)
+        """kv_tile_stats: [n][2][stored heads][7] int32 {state, bytes, groups per mode index [4], base
+        version}; a 256-channel head is stored as two half-heads (2 Hkv rows)."""
+        out = torch.empty((n, 2, self.Hkv * (2 if self.D == 256 else 1), 7), dtype=torch.int32, device=self.device)
         L.check(self.lib.kv_tile_stats(self.handle, seq, first, n, _ptr(out), self._stream()))
         return out
 
@@ -226,12 +237,19 @@ class KVCache:
     def table(self) -> torch.Tensor:
         return self.buffers["block_table"].view(torch.int32)
 
-    def bases(self) -> torch.Tensor:
-        return self.buffers["bases"][: 4 * self.Hkv * self.D].view(2, 2, self.Hkv, self.D)
+    def _version_offset(self, version: int) -> int:
+        if not 0 <= version < self.base_versions:
+            raise ValueError("no such base version")
+        return version * (6 if self.mode_set == 1 else 4) * self.Hkv * self.D
 
-    def bases2(self) -> torch.Tensor:
+    def bases(self, version: int = 0) -> torch.Tensor:
+        """The b3 and b4 bases of one base version, [2 (K, V)][2 (b3, b4)][Hkv][D]."""
+        n = self._version_offset(version)
+        return self.buffers["bases"][n: n + 4 * self.Hkv * self.D].view(2, 2, self.Hkv, self.D)
+
+    def bases2(self, version: int = 0) -> torch.Tensor:
         """The 2-bit-window bases of mode set 1, [2 (K, V)][Hkv][D]."""
-        n = 4 * self.Hkv * self.D
+        n = self._version_offset(version) + 4 * self.Hkv * self.D
         return self.buffers["bases"][n: n + 2 * self.Hkv * self.D].view(2, self.Hkv, self.D)
 
 
@@ -242,7 +260,7 @@ def admit_fcfs(*, num_kv_heads: int, head_dim: int, block_tokens: int, budget_by
     and requests admitted first come, first served (host only)."""
     lib = L.load()
     p = L.Params(dtype, num_kv_heads, num_q_heads or num_kv_heads, head_dim, block_tokens, group_tokens, -1,
-                 1 if compressed else 0, 1, 1, 1, 1, mode_set)
+                 1 if compressed else 0, 1, 1, 1, 1, mode_set, 1)
     arr = (ctypes.c_int32 * len(lengths))(*[int(x) for x in lengths])
     n, nc, nr = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     L.check(lib.kv_admit_fcfs(ctypes.byref(p), int(budget_bytes), float(raw_share), arr, len(lengths), ctypes.byref(n),

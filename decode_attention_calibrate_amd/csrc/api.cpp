@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <array>
 #include <new>
 #include <string>
 #include <vector>
@@ -24,6 +25,10 @@ struct kvc_cache {
   std::vector<int32_t> len;  // tokens per sequence (host mirror)
   bool calibrated = false;
   long long blocks = 0;      // finished blocks over all sequences
+  // finished blocks per base version, over all sequences and per sequence (a version holding
+  // none may be recalibrated); G.cur_ver is the version new blocks are encoded with
+  std::array<long long, kvc::kMaxVersions> ver_blocks{};
+  std::vector<std::array<long long, kvc::kMaxVersions>> seq_ver_blocks;
   void* noalloc_ws = nullptr;  // this device's fixed split workspace (kv_decode_attention_noalloc)
 };
 
@@ -62,7 +67,8 @@ int check_params(const kvc_params* p) {
   if (p->compressed != 0 && p->compressed != 1) return fail(KVC_EINVAL, "compressed must be 0 or 1");
   if (p->max_seqs < 1 || p->max_blocks_per_seq < 1) return fail(KVC_EINVAL, "max_seqs and max_blocks_per_seq >= 1");
   if (p->num_raw_slots < 0 || p->num_comp_slots < 0) return fail(KVC_EINVAL, "slot counts must be >= 0");
-  if (p->num_raw_slots >= (1 << 24) || p->num_comp_slots >= (1 << 24)) return fail(KVC_EINVAL, "slot counts < 2^24");
+  if (p->num_raw_slots >= kvc::kMaxSlots || p->num_comp_slots >= kvc::kMaxSlots) return fail(KVC_EINVAL, "slot counts < 2^23");
+  if (p->base_versions < 0 || p->base_versions > kvc::kMaxVersions) return fail(KVC_EINVAL, "base_versions must be 0 .. 4");
   if (p->compressed && p->num_comp_slots < 1) return fail(KVC_EINVAL, "a compressed cache needs compressed slots");
   if (!p->compressed && p->num_raw_slots < 1) return fail(KVC_EINVAL, "an uncompressed cache needs raw slots");
   // valid requests the kernels of this build do not implement
@@ -70,6 +76,7 @@ int check_params(const kvc_params* p) {
     return fail(KVC_EUNSUPPORTED, "these kernels implement 16- and 8-token groups");
   if (p->block_tokens != 16 && p->block_tokens != 32 && p->block_tokens != 64)
     return fail(KVC_EUNSUPPORTED, "these kernels implement block_tokens 16, 32 or 64");
+  // (the table entry's 6-bit escape-length field holds up to 1,008 bytes)
   if (cap > 512) return fail(KVC_EUNSUPPORTED, "these kernels implement esc_cap_bytes <= 512");
   if (p->mode_set < 0 || p->mode_set > 3) return fail(KVC_EINVAL, "mode_set must be 0, 1, 2 or 3");
   if (p->mode_set != 0 && (p->dtype != KVC_BF16 || p->head_dim > 128))
@@ -124,6 +131,9 @@ Geo make_geo(const kvc_params& p) {
     G.stride = G.code_off + align16(G.code_cap);
     G.esc_off = G.code_off;
   }
+  G.n_versions = std::max(1, p.base_versions);
+  G.cur_ver = 0;
+  G.ver_bytes = (p.mode_set == 1 ? 6 : 4) * G.Hkv * G.D;
   return G;
 }
 
@@ -131,7 +141,7 @@ void sizes_of(const kvc_params& p, const Geo& G, size_t out[KVC_NUM_BUFFERS]) {
   out[0] = (size_t)G.n_comp * G.stride;
   out[1] = (size_t)G.n_raw * G.raw_elems * G.EB;
   out[2] = (size_t)p.max_seqs * 2 * G.Hkv * G.raw_elems * G.EB;
-  out[3] = (size_t)(p.mode_set == 1 ? 6 : 4) * G.Hkv * G.D;
+  out[3] = (size_t)G.n_versions * G.ver_bytes;
   out[4] = (size_t)p.max_seqs * p.max_blocks_per_seq * 2 * G.Hkv * 4;
   out[5] = (size_t)G.n_comp * 4;
   out[6] = (size_t)G.n_raw * 4;
@@ -222,6 +232,7 @@ int kv_cache_create(const kvc_params* params, const kvc_buffers* buffers, uint64
   c->B.raw_free = (int32_t*)buffers->raw_free;
   c->B.counters = (kvc::Counters*)buffers->counters;
   c->len.assign(params->max_seqs, 0);
+  c->seq_ver_blocks.assign(params->max_seqs, std::array<long long, kvc::kMaxVersions>{});
   hipStream_t st = (hipStream_t)stream;
   if (G.n_comp > 0) {
     const std::vector<int32_t> perm = stack_layout(permutation(G.n_comp, perm_seed));
@@ -254,9 +265,29 @@ int kv_calibrate(kvc_cache* c, const void* k_dev, const void* v_dev, int32_t n_t
   if (!c) return fail(KVC_EINVAL, "cache is NULL");
   if (!k_dev || !v_dev || n_tokens < 1) return fail(KVC_EINVAL, "calibration needs K and V with n_tokens >= 1");
   if (c->blocks > 0) return fail(KVC_ESTATE, "calibration must precede the first finished block");
+  c->G.cur_ver = 0;
   const int rc = hip_fail(kvc::launch_calibrate(c->G, c->B, k_dev, v_dev, n_tokens, stream),
                           "launch calibrate");
   if (rc == KVC_OK) c->calibrated = true;
+  return rc;
+}
+
+int kv_recalibrate(kvc_cache* c, const void* k_dev, const void* v_dev, int32_t n_tokens, void* stream) {
+  if (!c) return fail(KVC_EINVAL, "cache is NULL");
+  if (!k_dev || !v_dev || n_tokens < 1) return fail(KVC_EINVAL, "recalibration needs K and V with n_tokens >= 1");
+  if (!c->calibrated) return fail(KVC_ESTATE, "kv_calibrate must run before kv_recalibrate");
+  int next = -1;
+  for (int d = 1; d < c->G.n_versions && next < 0; ++d) {
+    const int v = (c->G.cur_ver + d) % c->G.n_versions;
+    if (c->ver_blocks[v] == 0) next = v;
+  }
+  if (next < 0)
+    return fail(KVC_ESTATE, c->G.n_versions == 1 ? "the cache holds one base version (base_versions = 1)"
+                                                  : "every other base version still holds live blocks");
+  Geo G = c->G;
+  G.cur_ver = next;
+  const int rc = hip_fail(kvc::launch_calibrate(G, c->B, k_dev, v_dev, n_tokens, stream), "launch calibrate");
+  if (rc == KVC_OK) c->G.cur_ver = next;
   return rc;
 }
 
@@ -293,7 +324,13 @@ int kv_encode_append(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seqs, 
     rc = hip_fail(kvc::launch_append(c->G, c->B, S, k, v, n_tokens, max_new, stream), "launch append");
     if (rc != KVC_OK) return rc;
   }
-  for (int i = 0; i < n_seqs; ++i) c->len[seq_ids_host[i]] += n_tokens;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int id = seq_ids_host[i];
+    const long long nb = ((long long)c->len[id] + n_tokens) / T - c->len[id] / T;
+    c->seq_ver_blocks[id][c->G.cur_ver] += nb;
+    c->ver_blocks[c->G.cur_ver] += nb;
+    c->len[id] += n_tokens;
+  }
   c->blocks += new_blocks;
   return KVC_OK;
 }
@@ -543,7 +580,7 @@ int kv_admit_fcfs(const kvc_params* params, uint64_t budget_bytes, double raw_sh
     n_raw = budget_bytes / raw_tile;
     n_comp = 0;
   }
-  if (n_raw >= (1u << 24) || n_comp >= (1u << 24)) return fail(KVC_EINVAL, "budget exceeds 2^24 slots per pool");
+  if (n_raw >= (uint64_t)kvc::kMaxSlots || n_comp >= (uint64_t)kvc::kMaxSlots) return fail(KVC_EINVAL, "budget exceeds 2^23 slots per pool");
   uint64_t free_slots = p.compressed ? n_comp : n_raw;
   int admitted = 0;
   for (; admitted < n_requests; ++admitted) {
@@ -567,6 +604,10 @@ int kv_release_seq(kvc_cache* c, int32_t seq, void* stream) {
   if (rc == KVC_OK) {
     c->blocks -= nb;
     c->len[seq] = 0;
+    for (int v = 0; v < kvc::kMaxVersions; ++v) {
+      c->ver_blocks[v] -= c->seq_ver_blocks[seq][v];
+      c->seq_ver_blocks[seq][v] = 0;
+    }
   }
   return rc;
 }

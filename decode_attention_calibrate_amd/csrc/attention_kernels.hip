@@ -163,6 +163,7 @@ struct TileRef {
   int kind;              // SRC_COMP, SRC_RAW (raw tile), SRC_NONE
   int tg;                // token group inside the tile
   int escu;              // escape bytes / 16 (compressed)
+  int bo;                // offset of the tile's base version in the packed LDS bases (compressed)
   const uint8_t* p;      // the compressed or raw tile; for SRC_NONE a dummy tile-sized area (the
                          // tail buffer), so every load a kernel issues from it stays in bounds
   __device__ __forceinline__ int valid() const { return kind == SRC_NONE ? 0 : 16; }
@@ -188,19 +189,21 @@ __device__ __forceinline__ TileRef tile_ref(const AttnArgs& a, int seq, int L, i
   r.kind = SRC_NONE;
   r.tg = (t % TT) >> 4;
   r.escu = 0;
+  r.bo = 0;
   r.p = reinterpret_cast<const uint8_t*>(a.B.tail);
   if (t >= L || entry == kUnallocated) {  // past the finished blocks, or missing (missing_flag)
     r.tg = 0;
     return r;
   }
-  const uint32_t slot = entry & 0x00FFFFFFu;
-  if (entry & 0x80000000u) {
+  const uint32_t slot = entry_slot(entry);
+  if (entry & kRawTile) {
     r.kind = SRC_RAW;
     r.p = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * TG<NR, TT, FMT>::RAW * FmtT<FMT>::EB;
   } else {
     r.kind = SRC_COMP;
     r.p = a.B.comp_pool + (size_t)slot * (uint32_t)a.G.stride;
-    r.escu = min((int)((entry >> 24) & 0x7Fu), a.G.esc_cap >> 4);  // never past the slot's escape area
+    r.escu = min(entry_esc_units(entry), a.G.esc_cap >> 4);  // never past the slot's escape area
+    r.bo = entry_version(entry) * (2 * NR * 16);  // the bases the tile was encoded with
   }
   return r;
 }
@@ -547,15 +550,18 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   const Geo& G = a.G;
   const int esc_room = max(G.esc_cap, 16);
   uint8_t* klds = reinterpret_cast<uint8_t*>(lds4);              // [64][D] bf16, swizzled
-  uint8_t* esc_base = klds + kSB * D * 2;                         // [4][esc_room]
-  uint4* qlds = reinterpret_cast<uint4*>(esc_base + 4 * esc_room);  // [g][D/8] query chunks
-  uint32_t* blds = reinterpret_cast<uint32_t*>(qlds + G.g * (D / 8));  // [2][NR][16] packed bases
+  // escape staging: one area per lane group; with 64-token blocks the four lane groups hold the
+  // same tile (one block per super-block) and share one copy
+  constexpr int kEscAreas = TT == kSB ? 1 : 4;
+  uint8_t* esc_base = klds + kSB * D * 2;                         // [kEscAreas][esc_room]
+  uint4* qlds = reinterpret_cast<uint4*>(esc_base + kEscAreas * esc_room);  // [g][D/8] query chunks
+  uint32_t* blds = reinterpret_cast<uint32_t*>(qlds + G.g * (D / 8));  // [version][2][NR][16] packed bases
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y;
   const int4 z = a.zrow[blockIdx.z];
   const int si = z.x, seq = z.y, L = z.z;
   const SbOrder ord(L, a.n_splits, split);
-  uint8_t* esc_lds = esc_base + j * esc_room;
+  uint8_t* esc_lds = esc_base + (kEscAreas == 1 ? 0 : j * esc_room);
   const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(esc_lds);
   const uint32_t below = (1u << (2 * n)) - 1u;
   uint32_t flags = 0, bad = 0;
@@ -577,15 +583,22 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
     const int k = lane + kWave * u;
     qr[u] = k < G.g * (D / 8) ? ld128(a.q + ((size_t)si * G.Hq + h * G.g) * D + 8 * k) : make_uint4(0, 0, 0, 0);
   }
-  uint32_t br[2 * NR * 16 / kWave];
+  // the packed bases of every base version the cache holds (one unless it was recalibrated)
+  constexpr int BU = 2 * NR * 16 / kWave;
+  uint32_t br[kMaxVersions][BU];
 #pragma unroll
-  for (int u = 0; u < 2 * NR * 16 / kWave; ++u) {
-    const int k = lane + kWave * u;
-    const int kv = k / (NR * 16), i = (k / 16) % NR, nn = k % 16, c0 = 32 * i + 2 * nn;
-    const uint8_t* b3 = a.B.bases + ((size_t)(2 * kv) * G.Hkv + h) * D;
-    const uint8_t* b4 = b3 + (size_t)G.Hkv * D;
-    br[u] = b3[c0] | (b3[c0 + 1] << 8) | (b4[c0] << 16) | (b4[c0 + 1] << 24);
-  }
+  for (int v = 0; v < kMaxVersions; ++v)
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      const int k = lane + kWave * u;
+      const int kv = k / (NR * 16), i = (k / 16) % NR, nn = k % 16, c0 = 32 * i + 2 * nn;
+      br[v][u] = 0;
+      if (v < G.n_versions) {
+        const uint8_t* b3 = bases_of(G, a.B.bases, v, 3, kv, h);
+        const uint8_t* b4 = bases_of(G, a.B.bases, v, 4, kv, h);
+        br[v][u] = b3[c0] | (b3[c0 + 1] << 8) | (b4[c0] << 16) | (b4[c0 + 1] << 24);
+      }
+    }
 
   float m = -INFINITY, l = 0.0f;
   f32x4_t acc[NR][2];
@@ -603,7 +616,10 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   for (int u = 0; u < 4; ++u)
     if (lane + kWave * u < G.g * (D / 8)) qlds[lane + kWave * u] = qr[u];
 #pragma unroll
-  for (int u = 0; u < 2 * NR * 16 / kWave; ++u) blds[lane + kWave * u] = br[u];
+  for (int v = 0; v < kMaxVersions; ++v)
+    if (v < G.n_versions)
+#pragma unroll
+      for (int u = 0; u < BU; ++u) blds[v * 2 * NR * 16 + lane + kWave * u] = br[v][u];
 
   if (ord.cnt > 0) {
     for (int it = 0; it < ord.cnt; ++it) {
@@ -628,7 +644,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
           uint32_t o[2][2][4];
-          rebuild_round<NR, FMT>(cK, i, j, n, tags[i], blds[i * 16 + n], esc16, below, bad, o);
+          rebuild_round<NR, FMT>(cK, i, j, n, tags[i], blds[rK.bo + i * 16 + n], esc16, below, bad, o);
           // transpose to token-major rows: token 16j + 4q + k gets the (c0, c0+1) word, taken
           // from one half of each of the two channels' token-pair words (BF16: word k & 1, half
           // k >> 1; FP8: word k >> 1, half k & 1)
@@ -746,7 +762,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
         uint4 bv[2][2];
         if (rV.kind == SRC_COMP) {
           uint32_t o[2][2][4];
-          rebuild_round<NR, FMT>(cV, i, j, n, tagsV[i], blds[(NR + i) * 16 + n], esc16, below, bad, o);
+          rebuild_round<NR, FMT>(cV, i, j, n, tagsV[i], blds[rV.bo + (NR + i) * 16 + n], esc16, below, bad, o);
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
             bv[x][0] = make_uint4(o[x][0][0], o[x][1][0], o[x][0][1], o[x][1][1]);
@@ -1118,8 +1134,9 @@ template <int NR, int TT, int FMT>
 int launch_attn(const AttnArgs& a, int n_seqs, void* stream) {
   const dim3 grid(a.n_splits, a.G.Hkv, n_seqs);
   if (a.G.compressed) {
-    const size_t lds = (size_t)kSB * (32 * NR) * 2 + (size_t)4 * max(a.G.esc_cap, 16) +
-                       (size_t)a.G.g * (32 * NR) * 2 + (size_t)2 * NR * 16 * 4;
+    // K tile, escape staging (one shared area for 64-token blocks), query, bases per version
+    const size_t lds = (size_t)kSB * (32 * NR) * 2 + (size_t)(TT == kSB ? 1 : 4) * max(a.G.esc_cap, 16) +
+                       (size_t)a.G.g * (32 * NR) * 2 + (size_t)a.G.n_versions * 2 * NR * 16 * 4;
     hipLaunchKernelGGL((attn_comp_kernel<NR, TT, FMT>), grid, dim3(kWave), lds, (hipStream_t)stream, a);
   } else {
     hipLaunchKernelGGL((attn_raw_kernel<NR, TT, FMT>), grid, dim3(kWave), 0, (hipStream_t)stream, a);

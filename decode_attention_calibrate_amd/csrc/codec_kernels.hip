@@ -72,7 +72,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total)
 
 __global__ void init_kernel(Geo G, DevBufs B) {
   const size_t n_table = (size_t)G.max_seqs * G.max_blocks * 2 * G.Hkv;
-  const size_t n_bases = (size_t)(G.mode_set == 1 ? 6 : 4) * G.Hkv * G.D;
+  const size_t n_bases = (size_t)G.n_versions * G.ver_bytes;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_table; i += stride) B.table[i] = kUnallocated;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_bases; i += stride) B.bases[i] = 0;
@@ -94,6 +94,7 @@ __global__ void init_kernel(Geo G, DevBufs B) {
 // calibration tokens, then the 8- and 16-wide windows with the largest count (ties: lower median
 // start).  A format whose exponent field is only 4 bits wide (E4M3) has no 16-wide window; its
 // b4 stays 0.  Mode set 1 (a 2-bit mode) also takes the 4-wide window, stored after b3 and b4.
+// The bases go to base version G.cur_ver.
 __global__ void calibrate_kernel(Geo G, DevBufs B, const void* __restrict__ k, const void* __restrict__ v, int n) {
   __shared__ int hist[256];
   __shared__ int red[8];
@@ -115,9 +116,7 @@ __global__ void calibrate_kernel(Geo G, DevBufs B, const void* __restrict__ k, c
     int count;
     const int rank = block_exclusive_scan(flag, red, &count);
     if (flag && rank == (count - 1) / 2) {
-      const size_t at = w == 2 ? (size_t)4 * G.Hkv * G.D + ((size_t)kv * G.Hkv + h) * G.D + c
-                               : (((size_t)kv * 2 + (w - 3)) * G.Hkv + h) * G.D + c;
-      B.bases[at] = (uint8_t)tid;
+      B.bases[bases_at(G, G.cur_ver, w, kv, h) + c] = (uint8_t)tid;
     }
     __syncthreads();
   }
@@ -266,7 +265,7 @@ __device__ void store_raw_tile(const Geo& G, const DevBufs& B, int slot, int kv,
       elem_put(dst, i, G.EB, tile[i]);
     }
   }
-  if (threadIdx.x == 0) B.table[entry_idx] = (uint32_t)slot | 0x80000000u;
+  if (threadIdx.x == 0) B.table[entry_idx] = (uint32_t)slot | kRawTile;
 }
 
 // One block per newly full block of one (sequence, K|V, head): gathers its T tokens from the
@@ -321,8 +320,8 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
 
   const size_t entry_idx = table_index(G, seq, b, kv, h);
   int is_raw = 1, total = 0;
-  const uint8_t* b3 = B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
-  const uint8_t* b4 = B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;
+  const uint8_t* b3 = bases_of(G, B.bases, G.cur_ver, 3, kv, h);  // blocks are encoded with the current bases
+  const uint8_t* b4 = bases_of(G, B.bases, G.cur_ver, 4, kv, h);
   const int ppt = (G.NP + kThreads - 1) / kThreads;  // pairs per thread (consecutive)
   const int pr0 = tid * ppt;
   int my_before = 0;
@@ -442,7 +441,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
   for (int i = tid; i < 2 * G.PW; i += kThreads) reinterpret_cast<uint32_t*>(dst + G.tag_off)[i] = tagw[i];
   if (tid == 0) {
     const uint32_t units = (uint32_t)((2 * total + 15) >> 4);
-    B.table[entry_idx] = (uint32_t)slot | (units << 24);
+    B.table[entry_idx] = comp_entry((uint32_t)slot, units, G.cur_ver);
   }
 }
 
@@ -480,8 +479,8 @@ __global__ void __launch_bounds__(kThreads) encode_any_kernel(Geo G, DevBufs B, 
   for (int i = tid; i < G.stride / 4; i += kThreads) slotw[i] = 0u;
   __syncthreads();
 
-  const uint8_t* b3 = B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
-  const uint8_t* b4 = B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;
+  const uint8_t* b3 = bases_of(G, B.bases, G.cur_ver, 3, kv, h);  // blocks are encoded with the current bases
+  const uint8_t* b4 = bases_of(G, B.bases, G.cur_ver, 4, kv, h);
   // modes; each thread takes consecutive groups, so a block scan gives every group's escape offset
   const int per = (NG + kThreads - 1) / kThreads, q0 = min(NG, tid * per), q1 = min(NG, q0 + per);
   int units = 0, cnt[3] = {0, 0, 0};
@@ -588,7 +587,7 @@ __global__ void __launch_bounds__(kThreads) encode_any_kernel(Geo G, DevBufs B, 
   uint4* dst = reinterpret_cast<uint4*>(B.comp_pool + (size_t)slot * G.stride);
   const uint4* src = reinterpret_cast<const uint4*>(slotw);
   for (int i = tid; i < G.stride / 16; i += kThreads) dst[i] = src[i];
-  if (tid == 0) B.table[entry_idx] = (uint32_t)slot | ((uint32_t)((esc_bytes + 15) >> 4) << 24);
+  if (tid == 0) B.table[entry_idx] = comp_entry((uint32_t)slot, (uint32_t)((esc_bytes + 15) >> 4), G.cur_ver);
 }
 
 // FORMAT v2 (the nested precision modes of GAAC page §4.7.2; BF16): one 256-thread workgroup per
@@ -625,9 +624,9 @@ __global__ void __launch_bounds__(kThreads) encode_v2_kernel(Geo G, DevBufs B, S
   for (int i = tid; i < G.stride / 4; i += kThreads) slotw[i] = 0u;
   __syncthreads();
 
-  const uint8_t* b3 = B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
-  const uint8_t* b4 = B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;
-  const uint8_t* b2 = B.bases + (size_t)4 * G.Hkv * D + ((size_t)kv * G.Hkv + h) * D;  // mode set 1 only
+  const uint8_t* b3 = bases_of(G, B.bases, G.cur_ver, 3, kv, h);  // blocks are encoded with the current bases
+  const uint8_t* b4 = bases_of(G, B.bases, G.cur_ver, 4, kv, h);
+  const uint8_t* b2 = bases_of(G, B.bases, G.cur_ver, 2, kv, h);  // mode set 1 only
   const int per = (NG + kThreads - 1) / kThreads, q0 = min(NG, tid * per), q1 = min(NG, q0 + per);
   int bits = 0, cnt[4] = {0, 0, 0, 0};
   if (G.compressed) {
@@ -696,28 +695,29 @@ __global__ void __launch_bounds__(kThreads) encode_v2_kernel(Geo G, DevBufs B, S
   uint4* dst = reinterpret_cast<uint4*>(B.comp_pool + (size_t)slot * G.stride);
   const uint4* src = reinterpret_cast<const uint4*>(slotw);
   for (int i = tid; i < G.stride / 16; i += kThreads) dst[i] = src[i];
-  if (tid == 0) B.table[entry_idx] = (uint32_t)slot;
+  if (tid == 0) B.table[entry_idx] = comp_entry((uint32_t)slot, 0u, G.cur_ver);
 }
 
 // Storage statistics of finished tiles from their table entries and stored tag planes (the
 // positional-drift study of GAAC page App. C reads these per segment): one thread per tile;
-// out[i][6] = {state (0 compressed, 1 raw, -1 unallocated), bytes (FORMAT v1: the escape bytes
-// the tags call for; FORMAT v2: the code bytes), groups per mode index [4]}.  A raw bit without
-// its escape bit (FORMAT v1, corrupt) counts as raw.
+// out[i][7] = {state (0 compressed, 1 raw, -1 unallocated), bytes (FORMAT v1: the escape bytes
+// the tags call for; FORMAT v2: the code bytes), groups per mode index [4], base version (-1
+// unless compressed)}.  A raw bit without its escape bit (FORMAT v1, corrupt) counts as raw.
 __global__ void tile_stats_kernel(Geo G, DevBufs B, int seq, int first, int n, int32_t* __restrict__ out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n * 2 * G.Hkv) return;
   const int bi = i / (2 * G.Hkv), kv = (i / G.Hkv) % 2, h = i % G.Hkv;
   const uint32_t e = B.table[table_index(G, seq, first + bi, kv, h)];
-  int32_t* o = out + (size_t)i * 6;
-  int c[4] = {0, 0, 0, 0}, state = 0;
+  int32_t* o = out + (size_t)i * 7;
+  int c[4] = {0, 0, 0, 0}, state = 0, ver = -1;
   long bits = 0;
   if (e == kUnallocated) {
     state = -1;
-  } else if (e & 0x80000000u) {
+  } else if (e & kRawTile) {
     state = 1;
   } else {
-    const uint32_t* tag0 = reinterpret_cast<const uint32_t*>(B.comp_pool + (size_t)(e & 0x00FFFFFFu) * G.stride + G.tag_off);
+    ver = entry_version(e);
+    const uint32_t* tag0 = reinterpret_cast<const uint32_t*>(B.comp_pool + (size_t)entry_slot(e) * G.stride + G.tag_off);
     const uint32_t* tag1 = tag0 + G.PW;
     for (int w = 0; w < G.PW; ++w) {
       const uint32_t valid = (w == G.PW - 1 && (G.NG & 31)) ? ((1u << (G.NG & 31)) - 1u) : 0xFFFFFFFFu;
@@ -738,6 +738,7 @@ __global__ void tile_stats_kernel(Geo G, DevBufs B, int seq, int first, int n, i
   o[0] = state;
   o[1] = (int32_t)((bits + 7) / 8);
   for (int k = 0; k < 4; ++k) o[2 + k] = c[k];
+  o[6] = ver;
 }
 
 // Exponent concentration (GAAC page §3.1: most exponents of a head-channel lie in a few
@@ -811,9 +812,9 @@ __global__ void release_kernel(Geo G, DevBufs B, int seq, int n_blocks) {
     const size_t idx = (size_t)seq * G.max_blocks * 2 * G.Hkv + i;
     const uint32_t e = B.table[idx];
     if (e == kUnallocated) continue;
-    const int slot = (int)(e & 0x00FFFFFFu);
+    const int slot = (int)entry_slot(e);
     const int s = slot % kPoolStripes;  // back to the sub-stack the slot belongs to
-    if (e & 0x80000000u) {
+    if (e & kRawTile) {
       const int t = atomicAdd(&B.counters->raw_top[s].n, 1);
       B.raw_free[kPoolStripes * t + s] = slot;
     } else {
@@ -1069,8 +1070,8 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
     if (tid == 0) atomicOr(&B.counters->status, 4u);
     return;
   }
-  const int slot = (int)(e & 0x00FFFFFFu);
-  if (e & 0x80000000u) {
+  const int slot = (int)entry_slot(e);
+  if (e & kRawTile) {
     const uint8_t* src = reinterpret_cast<const uint8_t*>(B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
     for (int i = tid; i < G.raw_elems; i += kThreads) {
       const int t = i / D, c = i % D;
@@ -1079,33 +1080,30 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
     return;
   }
   const uint8_t* tile = B.comp_pool + (size_t)slot * G.stride;
+  const int ver = entry_version(e);  // the base version this tile was encoded with
+  const uint8_t* b3 = bases_of(G, B.bases, ver, 3, kv, h);
+  const uint8_t* b4 = bases_of(G, B.bases, ver, 4, kv, h);
   __shared__ TileMeta meta;
   if (G.mode_set != 0) {
-    decode_tile_v2(G, B, tile, B.bases + (size_t)4 * G.Hkv * D + ((size_t)kv * G.Hkv + h) * D,
-                   B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D, B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D,
+    decode_tile_v2(G, B, tile, bases_of(G, B.bases, ver, 2, kv, h), b3, b4,
                    [&](int t, int c, uint32_t x) { elem_put(outv, out_idx(t, c), 2, x); });
     return;
   }
   if (G.EB == 2 && G.GT == 8) {
     uint16_t* o16 = reinterpret_cast<uint16_t*>(outv);
-    decode_bf16_g8_tile(G, B, tile, B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
-                        B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, meta,
+    decode_bf16_g8_tile(G, B, tile, b3, b4, meta,
                         [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(o16 + out_idx(t, c0)) = w; },
                         tid, kThreads, true);
     return;
   }
   if (G.EB == 1 || G.GT != kGroup) {
-    decode_tile_any(G, B, tile, B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
-                    B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D,
-                    [&](int t, int c, uint32_t x) { elem_put(outv, out_idx(t, c), G.EB, x); });
+    decode_tile_any(G, B, tile, b3, b4, [&](int t, int c, uint32_t x) { elem_put(outv, out_idx(t, c), G.EB, x); });
     return;
   }
   uint16_t* out = reinterpret_cast<uint16_t*>(outv);
   auto out_at = [&](int t, int c) -> uint16_t* { return out + out_idx(t, c); };
   stage_tile_meta(G, B, tile, meta, tid, kThreads, true);
   const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(meta.esc);
-  const uint8_t* b3 = B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D;
-  const uint8_t* b4 = B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D;
   const int max_plane = G.esc_cap / 2;
   for (int pr = tid; pr < G.NP; pr += kThreads) {
     const int q0 = 2 * pr, w = q0 >> 5, bit = q0 & 31;
@@ -1239,8 +1237,9 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
     if (FMT == 0 && G.mode_set == 0) {
       // BF16, 8-token groups: the K tile by threads 0..127 and the V tile by 128..255 at once
       const int kv = tid >> 7, tl = tid & 127;
-      const uint32_t e = kv ? eV : eK, slot = e & 0x00FFFFFFu;
-      const bool comp = e != kUnallocated && !(e & 0x80000000u);
+      const uint32_t e = kv ? eV : eK, slot = entry_slot(e);
+      const bool comp = e != kUnallocated && !(e & kRawTile);
+      const int ver = comp ? entry_version(e) : 0;
       uint16_t* dst = kvt[kv];
       if (e == kUnallocated) {  // missing: zeros, reported
         for (int i = tl; i < T * D; i += kThreads / 2) dst[i] = 0;
@@ -1250,34 +1249,31 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
         for (int i = tl; i < T * D; i += kThreads / 2) dst[i] = src[kv ? (size_t)(i % D) * T + i / D : (size_t)i];
       }
       const uint8_t* tile = a.B.comp_pool + (comp ? (size_t)slot * G.stride : 0);
-      decode_bf16_g8_tile(G, a.B, tile, a.B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
-                          a.B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D, meta[kv],
+      decode_bf16_g8_tile(G, a.B, tile, bases_of(G, a.B.bases, ver, 3, kv, h), bases_of(G, a.B.bases, ver, 4, kv, h), meta[kv],
                           [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(dst + t * D + c0) = w; },
                           tl, kThreads / 2, comp);
       __syncthreads();
     } else {
       for (int kv = 0; kv < 2; ++kv) {
         uint16_t* dst = kvt[kv];
-        const uint32_t e = kv ? eV : eK, slot = e & 0x00FFFFFFu;
+        const uint32_t e = kv ? eV : eK, slot = entry_slot(e);
+        const int ver = entry_version(e);
         if (e == kUnallocated) {  // missing: zeros, reported
           for (int i = tid; i < T * D; i += kThreads) dst[i] = 0;
           flags |= 4u;
-        } else if (e & 0x80000000u) {  // raw tile: K [t][c], V [c][t]
+        } else if (e & kRawTile) {  // raw tile: K [t][c], V [c][t]
           const uint8_t* src = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
           for (int i = tid; i < T * D; i += kThreads) {
             const int t = i / D, c = i % D;
             dst[i] = (uint16_t)elem_at(src, kv ? (size_t)c * T + t : (size_t)i, G.EB);
           }
         } else if (G.mode_set != 0) {  // FORMAT v2 (nested precision modes, BF16)
-          decode_tile_v2(G, a.B, a.B.comp_pool + (size_t)slot * G.stride,
-                         a.B.bases + (size_t)4 * G.Hkv * D + ((size_t)kv * G.Hkv + h) * D,
-                         a.B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
-                         a.B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D,
+          decode_tile_v2(G, a.B, a.B.comp_pool + (size_t)slot * G.stride, bases_of(G, a.B.bases, ver, 2, kv, h),
+                         bases_of(G, a.B.bases, ver, 3, kv, h), bases_of(G, a.B.bases, ver, 4, kv, h),
                          [&](int t, int c, uint32_t x) { dst[t * D + c] = (uint16_t)x; });
         } else {
-          decode_tile_any(G, a.B, a.B.comp_pool + (size_t)slot * G.stride,
-                          a.B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + h) * D,
-                          a.B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + h) * D,
+          decode_tile_any(G, a.B, a.B.comp_pool + (size_t)slot * G.stride, bases_of(G, a.B.bases, ver, 3, kv, h),
+                          bases_of(G, a.B.bases, ver, 4, kv, h),
                           [&](int t, int c, uint32_t x) { dst[t * D + c] = (uint16_t)x; });
         }
         __syncthreads();
@@ -1409,8 +1405,9 @@ __global__ void __launch_bounds__(kThreads) attn_half_kernel(HalfAttnArgs a) {
       const int hh = 2 * h + hf;
       uint16_t* dst = kvt[hf];
       const uint32_t e = tailblk ? 0u : a.B.table[table_index(G, seq, b, kv, hh)];
-      const uint32_t slot = e & 0x00FFFFFFu;
-      const bool comp = !tailblk && e != kUnallocated && !(e & 0x80000000u);
+      const uint32_t slot = entry_slot(e);
+      const bool comp = !tailblk && e != kUnallocated && !(e & kRawTile);
+      const int ver = comp ? entry_version(e) : 0;
       if (!comp) {  // tail, raw tile (K [t][c], V [c][t]) or missing (zeros, reported)
         const uint8_t* src = nullptr;
         if (tailblk) src = reinterpret_cast<const uint8_t*>(a.B.tail) + tail_offset(G, seq, kv, hh) * G.EB;
@@ -1421,8 +1418,8 @@ __global__ void __launch_bounds__(kThreads) attn_half_kernel(HalfAttnArgs a) {
           dst[i] = src ? (uint16_t)elem_at(src, kv ? (size_t)c * T + t : (size_t)i, G.EB) : (uint16_t)0;
         }
       }
-      const uint8_t* b3 = a.B.bases + ((size_t)(kv * 2 + 0) * G.Hkv + hh) * DH;
-      const uint8_t* b4 = a.B.bases + ((size_t)(kv * 2 + 1) * G.Hkv + hh) * DH;
+      const uint8_t* b3 = bases_of(G, a.B.bases, ver, 3, kv, hh);
+      const uint8_t* b4 = bases_of(G, a.B.bases, ver, 4, kv, hh);
       const uint8_t* tile = a.B.comp_pool + (comp ? (size_t)slot * G.stride : 0);
       if (decode_here) {  // BF16, 8-token groups: every thread reaches the decoder's barriers
         decode_bf16_g8_tile(G, a.B, tile, b3, b4, meta[hf],

@@ -51,6 +51,10 @@ struct Geo {
   // sm_off, code_off (the stream start) and code_cap (its capacity in bytes) above; esc_cap
   // stays the escape allowance the capacity includes.
   int mode_set, n_modes, mw[4], code_cap;
+  // base versions: n_versions calibrated base sets (1..4) of ver_bytes each in the bases
+  // buffer; cur_ver is the set blocks are encoded with now.  Each compressed tile's table entry
+  // names the set it was encoded with (entry_version).
+  int n_versions, cur_ver, ver_bytes;
 };
 
 // counters buffer (12,416 bytes).  Atomics to one 128-byte line are performed one after
@@ -85,7 +89,7 @@ struct DevBufs {
   uint8_t* comp_pool;
   uint16_t* raw_pool;    // element storage: 16-bit words (BF16) or bytes (FP8, cast to uint8_t*)
   uint16_t* tail;        // same
-  uint8_t* bases;        // [2][2][Hkv][D]
+  uint8_t* bases;        // [version][K|V][b3|b4][Hkv][D], then (mode set 1) [K|V][Hkv][D] of b2 per version
   uint32_t* table;       // [max_seqs][max_blocks][2][Hkv]
   int32_t* comp_free;
   int32_t* raw_free;
@@ -98,7 +102,30 @@ struct SeqList {
   int lens[kMaxSeqsPerLaunch];     // token count (attention) or token count before append
 };
 
-// table entry helpers
+// Table entry of one (sequence, block, K|V, kv-head): kUnallocated, or bit 31 = raw tile,
+// bits 29..30 = the base version a compressed tile was encoded with, bits 23..28 = the escape
+// bytes a FORMAT v1 tile uses in 16-byte units (<= 63, i.e. <= 1,008 bytes), bits 0..22 = slot.
+constexpr uint32_t kRawTile = 0x80000000u;
+constexpr uint32_t kSlotMask = 0x007FFFFFu;
+constexpr int kMaxSlots = 1 << 23;
+constexpr int kMaxVersions = 4;
+__host__ __device__ inline uint32_t entry_slot(uint32_t e) { return e & kSlotMask; }
+__host__ __device__ inline int entry_esc_units(uint32_t e) { return (int)((e >> 23) & 0x3Fu); }
+__host__ __device__ inline int entry_version(uint32_t e) { return (int)((e >> 29) & 3u); }
+__host__ __device__ inline uint32_t comp_entry(uint32_t slot, uint32_t esc_units, int ver) {
+  return slot | (esc_units << 23) | ((uint32_t)ver << 29);
+}
+// Calibrated bases of version ver, K|V kv, kv-head h: w = 3 (8-exponent window), 4 (16) or 2
+// (4-exponent window, FORMAT v2 mode set 1); D bytes, one per channel.
+__host__ __device__ inline size_t bases_at(const Geo& G, int ver, int w, int kv, int h) {
+  const size_t v0 = (size_t)ver * G.ver_bytes;
+  if (w == 2) return v0 + (size_t)4 * G.Hkv * G.D + ((size_t)kv * G.Hkv + h) * G.D;
+  return v0 + ((size_t)(2 * kv + (w - 3)) * G.Hkv + h) * G.D;
+}
+__host__ __device__ inline const uint8_t* bases_of(const Geo& G, const uint8_t* bases, int ver, int w, int kv, int h) {
+  return bases + bases_at(G, ver, w, kv, h);
+}
+
 __host__ __device__ inline size_t table_index(const Geo& G, int seq, int blk, int kv, int h) {
   return (((size_t)seq * G.max_blocks + blk) * 2 + kv) * G.Hkv + h;
 }

@@ -78,8 +78,8 @@ typedef struct {
                                  rebuilds tiles in registers (the tuned path); over a
                                  compressed G = 8 cache it rebuilds each block's tiles into
                                  LDS (correct for every format, not tuned)                   */
-  int32_t esc_cap_bytes;      /* escape capacity per tile, multiple of 16, <= 2032;
-                                 < 0 selects T*D/16                                          */
+  int32_t esc_cap_bytes;      /* escape capacity per tile, multiple of 16, <= 2032 (this
+                                 build implements <= 512); < 0 selects T*D/16                */
   int32_t compressed;         /* 1: blocks are encoded; 0: every block is stored raw (the
                                  uncompressed baseline cache, same table and layout)         */
   int32_t max_seqs;           /* sequence ids are 0 .. max_seqs-1                            */
@@ -94,6 +94,11 @@ typedef struct {
                                  FORMAT v2 needs BF16 and head_dim <= 128
                                  (KVC_EUNSUPPORTED otherwise); its caches are decoded and
                                  attended by the element-wise LDS-rebuild kernels           */
+  int32_t base_versions;      /* calibrated base sets the cache can hold at once, 1..4 (0
+                                 means 1): kv_recalibrate switches later blocks to a new set
+                                 while every stored tile keeps decoding with the set it was
+                                 encoded with (GAAC page App. C: windows calibrated near the
+                                 start of a context drift away from rotated keys)           */
 } kvc_params;
 
 /* Device buffers, all owned by the caller; sizes from kv_buffer_sizes (same order). */
@@ -102,11 +107,14 @@ typedef struct {
   void* raw_pool;    /* [num_raw_slots][T*D] elements: raw tiles, K token-major [t][c],
                         V channel-major [c][t]                                              */
   void* tail;        /* [max_seqs][2 (K,V)][Hkv][T*D] elements, raw-tile layout             */
-  void* bases;       /* [2 (K,V)][2 (narrow b3, wide b4)][Hkv][D] uint8 calibrated bases;
+  void* bases;       /* per base version (base_versions of them, version-major):
+                        [2 (K,V)][2 (narrow b3, wide b4)][Hkv][D] uint8 calibrated bases;
                         mode_set 1 adds [2 (K,V)][Hkv][D] 2-bit-window bases b2 after them  */
   void* block_table; /* [max_seqs][max_blocks_per_seq][2 (K,V)][Hkv] uint32 entries:
-                        0xFFFFFFFF = unallocated; else bit 31 = raw, bits 24..30 = escape
-                        bytes used in 16-byte units (0 in FORMAT v2), bits 0..23 = slot     */
+                        0xFFFFFFFF = unallocated; else bit 31 = raw, bits 29..30 = the base
+                        version a compressed tile was encoded with, bits 23..28 = escape
+                        bytes used in 16-byte units (0 in FORMAT v2), bits 0..22 = slot
+                        (slot counts < 2^23)                                                */
   void* comp_free;   /* [num_comp_slots] int32 free stack of compressed slots: 16
                         interleaved sub-stacks (sub-stack s = the slots equal to s mod 16,
                         its element k at index 16k + s), popped from a preferred sub-stack
@@ -147,9 +155,22 @@ void kv_cache_destroy(kvc_cache* cache);
  * from calibration data).  k_dev, v_dev: [n_tokens][Hkv][D] elements (typically the first
  * tokens of one sequence).  For each (K|V, head, channel) the narrow base b3 is the start of
  * the 8-wide exponent window holding the most calibration exponents and b4 the same for the
- * 16-wide window; ties take the lower median of the tied starts.  Must precede the first
- * block encode (KVC_ESTATE otherwise) and may not be repeated once blocks exist. */
+ * 16-wide window; ties take the lower median of the tied starts.  The bases go to base
+ * version 0, which blocks are then encoded with.  Must precede the first block encode
+ * (KVC_ESTATE otherwise) and may not be repeated once blocks exist. */
 int kv_calibrate(kvc_cache* cache, const void* k_dev, const void* v_dev, int32_t n_tokens, void* stream);
+
+/* Recalibration of a live cache (GAAC page App. C: exponent windows calibrated near the start
+ * of a context drift away from RoPE-rotated keys further on).  Calibrates a new base version
+ * from k_dev, v_dev ([n_tokens][Hkv][D] elements, as kv_calibrate) and encodes every block
+ * finished after this call with it; blocks already stored keep the version they were encoded
+ * with (tiles are never re-encoded), and every decoder reads a tile's version from its table
+ * entry.  The new version is the first of the cache's base_versions, after the current one,
+ * that holds no live block (blocks of released sequences do not count).  KVC_ESTATE if
+ * kv_calibrate has not run, or if every other version still holds live blocks (base_versions
+ * = 1 always); KVC_EINVAL for NULL or empty inputs.  Enqueued on stream; host bookkeeping
+ * only otherwise. */
+int kv_recalibrate(kvc_cache* cache, const void* k_dev, const void* v_dev, int32_t n_tokens, void* stream);
 
 /* Appends n_tokens tokens to each listed sequence (GAAC page §3.3, fill-then-finalize).
  * k_dev, v_dev: [n_seqs][n_tokens][Hkv][D] elements, 16-byte aligned (KVC_EINVAL otherwise).
@@ -249,9 +270,10 @@ int kv_decode_attention_noalloc(kvc_cache* cache, const int32_t* seq_ids_host, i
 /* Storage statistics of finished blocks first_block .. first_block+n_blocks-1 of one sequence,
  * read on the device from the table entries and the stored tag planes (GAAC page App. C studies
  * escape bytes per tile and raw fallbacks along the context).  out_dev: [n_blocks][2 (K,V)][Hkv]
- * [6] int32, 4-byte aligned: {state: 0 compressed, 1 raw, -1 unallocated; bytes: FORMAT v1 the
+ * [7] int32 (2 Hkv rows for head_dim 256: one per stored half-head), 4-byte aligned: {state: 0 compressed, 1 raw, -1 unallocated; bytes: FORMAT v1 the
  * escape bytes the tile's tags call for, FORMAT v2 its code bytes, 0 for raw tiles; groups per
- * mode index [4] (compressed tiles)}.  Enqueued; KVC_EINVAL for blocks past the finished ones. */
+ * mode index [4] (compressed tiles); the base version of a compressed tile, else -1}.
+ * Enqueued; KVC_EINVAL for blocks past the finished ones. */
 int kv_tile_stats(kvc_cache* cache, int32_t seq, int32_t first_block, int32_t n_blocks, int32_t* out_dev,
                   void* stream);
 

@@ -28,16 +28,19 @@ int main() {
         for (int G : Gs)
           for (int ms = -1; ms <= 4; ++ms)
             for (int comp = 0; comp <= 1; ++comp) {
-              kvc_params p = {dt, 8, 32, D, T, G, -1, comp, 4, 100, 1000, 100, ms};
+              const int nv = (int)(cases % 7) - 1;  // base versions -1 .. 5 across the cases
+              kvc_params p = {dt, 8, 32, D, T, G, -1, comp, 4, 100, 1000, 100, ms, nv};
               size_t sz[KVC_NUM_BUFFERS], stride = 0;
               const int rc = kv_buffer_sizes(&p, sz, &stride);
               const bool valid = (D == 64 || D == 128 || D == 256) && (T == 16 || T == 32 || T == 64) && (G == 8 || G == 16) &&
-                                 ms >= 0 && ms <= 3 && (ms == 0 || (dt == KVC_BF16 && D <= 128));
+                                 ms >= 0 && ms <= 3 && (ms == 0 || (dt == KVC_BF16 && D <= 128)) && nv >= 0 && nv <= 4;
               if (valid != (rc == KVC_OK)) {
                 printf("FAIL sizes dt=%d D=%d T=%d G=%d ms=%d: rc %d\n", dt, D, T, G, ms, rc);
                 bad = 1;
               }
               if (rc == KVC_OK && (stride == 0 || stride % 16 || sz[7] != 12416)) bad = 1;
+              // the bases buffer holds one calibrated set per base version
+              if (rc == KVC_OK && sz[3] != (size_t)(nv < 1 ? 1 : nv) * (ms == 1 ? 6 : 4) * 8 * D) bad = 1;
               int32_t lens[5] = {4096, 8000, 100, 32768, 1};
               int32_t n = -1, nc = -1, nr = -1;
               const int ra = kv_admit_fcfs(&p, 1ull << 30, 1.0 / 64, lens, 5, &n, &nc, &nr);
@@ -59,6 +62,7 @@ int main() {
   uint32_t flags;
   int32_t len;
   bad |= expect(kv_calibrate(nullptr, fake, fake, 1, nullptr), KVC_EINVAL, "calibrate NULL cache");
+  bad |= expect(kv_recalibrate(nullptr, fake, fake, 1, nullptr), KVC_EINVAL, "recalibrate NULL cache");
   bad |= expect(kv_encode_append(nullptr, ids, 1, fake, fake, 1, nullptr), KVC_EINVAL, "append NULL cache");
   bad |= expect(kv_decode_blocks(nullptr, 0, 0, 1, fake, fake, nullptr), KVC_EINVAL, "decode NULL cache");
   bad |= expect(kv_decode_attention(nullptr, ids, 1, fake, 1.f, 1, fake, 64, fake, nullptr), KVC_EINVAL, "attn NULL");

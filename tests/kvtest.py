@@ -28,14 +28,24 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def new_cache(*, Hkv, Hq, D, T, max_seqs, max_blocks, comp_slots=None, raw_slots=None, compressed=True,
-              esc_cap=-1, perm_seed=0, fmt=oracle.BF16, Gt=16, mode_set=0):
+              esc_cap=-1, perm_seed=0, fmt=oracle.BF16, Gt=16, mode_set=0, base_versions=1):
     from decode_attention_calibrate_amd import KVCache
     n_tiles = max_seqs * max_blocks * 2 * Hkv
     return KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=max_seqs,
                    max_blocks_per_seq=max_blocks, group_tokens=Gt,
                    num_comp_slots=(n_tiles if comp_slots is None else comp_slots) if compressed else 0,
                    num_raw_slots=(n_tiles if raw_slots is None else raw_slots), compressed=compressed,
-                   esc_cap_bytes=esc_cap, perm_seed=perm_seed, dtype=fmt, mode_set=mode_set)
+                   esc_cap_bytes=esc_cap, perm_seed=perm_seed, dtype=fmt, mode_set=mode_set,
+                   base_versions=base_versions)
+
+
+# table entry fields (include/kvc.h): bit 31 raw, bits 29..30 base version, bits 23..28 escape
+# units of 16 bytes, bits 0..22 slot
+SLOT_MASK = 0x7FFFFF
+
+
+def esc_units(e: int) -> int:
+    return (e >> 23) & 0x3F
 
 
 def row_rel_err(out_bits: np.ndarray, ref: np.ndarray) -> float:
@@ -49,12 +59,12 @@ def gpu_tile_bytes(cache, seq, blk, kv, h):  # one tile; compare_tiles reads man
     """(is_raw, esc_units, bytes) of one finished tile as the GPU stored it."""
     e = int(cache.table()[((seq * cache.params.max_blocks_per_seq + blk) * 2 + kv) * cache.Hkv + h].item()) & 0xFFFFFFFF
     assert e != 0xFFFFFFFF, "unallocated tile"
-    slot = e & 0xFFFFFF
+    slot = e & SLOT_MASK
     if e >> 31:
         n = cache.T * cache.D * cache.EB
         return True, 0, cache.buffers["raw_pool"][slot * n:(slot + 1) * n].cpu().numpy()
     st = cache.slot_stride
-    return False, (e >> 24) & 0x7F, cache.buffers["comp_pool"][slot * st:(slot + 1) * st].cpu().numpy()
+    return False, esc_units(e), cache.buffers["comp_pool"][slot * st:(slot + 1) * st].cpu().numpy()
 
 
 def oracle_layer(p: oracle.Params, Hkv: int, k_cal: np.ndarray, v_cal: np.ndarray, seq_tokens, chunks=None):
@@ -70,22 +80,39 @@ def oracle_layer(p: oracle.Params, Hkv: int, k_cal: np.ndarray, v_cal: np.ndarra
     return bases, seqs
 
 
+def _stored_heads(cache) -> int:
+    """Heads the table rows count: a 256-channel head is stored as two 128-channel half-heads."""
+    return cache.Hkv * (2 if cache.D == 256 else 1)
+
+
 def _stored_tiles(cache, jobs):
     """(is_raw, esc_units, bytes) per (seq, blk, kv, h) job as the GPU stored them: the table is
     read once and the slots are gathered on the device, so large samples cost one copy."""
     tab = cache.table().cpu().numpy().view(np.uint32)
-    Hkv, MB = cache.Hkv, cache.params.max_blocks_per_seq
+    Hkv, MB = _stored_heads(cache), cache.params.max_blocks_per_seq
     ent = np.array([tab[((sid * MB + b) * 2 + kv) * Hkv + h] for sid, b, kv, h in jobs], np.uint32)
     assert (ent != 0xFFFFFFFF).all(), "unallocated tile"
     raw = (ent >> 31).astype(bool)
-    slot = torch.from_numpy((ent & 0xFFFFFF).astype(np.int64)).cuda()
-    n_raw = cache.T * cache.D * cache.EB
+    slot = torch.from_numpy((ent & SLOT_MASK).astype(np.int64)).cuda()
+    n_raw = cache.T * min(cache.D, 128) * cache.EB
     comp = cache.buffers["comp_pool"].view(-1, cache.slot_stride) if cache.compressed else None
     rawp = cache.buffers["raw_pool"][: (cache.buffers["raw_pool"].numel() // n_raw) * n_raw].view(-1, n_raw)
     rb = torch.from_numpy(raw).cuda()
     got_c = comp[torch.where(rb, torch.zeros_like(slot), slot)].cpu().numpy() if comp is not None else None
     got_r = rawp[torch.where(rb, slot, torch.zeros_like(slot))].cpu().numpy()
-    return [(bool(raw[i]), int((ent[i] >> 24) & 0x7F), got_r[i] if raw[i] else got_c[i]) for i in range(len(jobs))]
+    return [(bool(raw[i]), esc_units(int(ent[i])), got_r[i] if raw[i] else got_c[i]) for i in range(len(jobs))]
+
+
+def stored_versions(cache, jobs):
+    """Base version of each (seq, blk, kv, h) job's compressed tile (-1 for raw tiles)."""
+    tab = cache.table().cpu().numpy().view(np.uint32)
+    Hkv, MB = _stored_heads(cache), cache.params.max_blocks_per_seq
+    out = []
+    for sid, b, kv, h in jobs:
+        e = int(tab[((sid * MB + b) * 2 + kv) * Hkv + h])
+        assert e != 0xFFFFFFFF, "unallocated tile"
+        out.append(-1 if e >> 31 else (e >> 29) & 3)
+    return out
 
 
 def compare_tiles(cache, p: oracle.Params, oseqs, seq_ids, sample=None, rng=None):

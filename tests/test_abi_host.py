@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(K):
 def _params(K, **kw):
     d = dict(dtype=0, num_kv_heads=8, num_q_heads=32, head_dim=128, block_tokens=64, group_tokens=16,
              esc_cap_bytes=-1, compressed=1, max_seqs=2, max_blocks_per_seq=1024, num_comp_slots=2048,
-             num_raw_slots=64, mode_set=0)
+             num_raw_slots=64, mode_set=0, base_versions=1)
     d.update(kw)
     return K._lib.Params(*[d[f] for f, _ in K._lib.Params._fields_])
 

@@ -30,7 +30,7 @@ def test_rope_drift_tile_stats_match_oracle(ms):
     c = new_cache(Hkv=8, Hq=32, D=128, T=64, max_seqs=1, max_blocks=nb + 1, Gt=Gt, mode_set=ms)
     c.calibrate(dev(cal_k), dev(vc))
     c.append([0], dev(kr[None]), dev(v[None]))
-    got = c.tile_stats(0, 0, nb).cpu().numpy()               # [nb][2][8][6]
+    got = c.tile_stats(0, 0, nb).cpu().numpy()               # [nb][2][8][7]
     tiles = np.stack([x[b * 64:(b + 1) * 64, h] for b in range(nb) for x in (kr, v) for h in range(8)])
     isv = np.array([kv for b in range(nb) for kv in (0, 1) for h in range(8)], np.int32)
     kvh = [(kv, h) for b in range(nb) for kv in (0, 1) for h in range(8)]
@@ -43,14 +43,15 @@ def test_rope_drift_tile_stats_match_oracle(ms):
         b2, b3, b4 = oracle.v2_calibrate_layer(p, cal_k, vc)
         _, is_raw, nbytes, modes = oracle.v2_encode_tiles(p, ms, tiles, *[np.stack([b[a, h] for a, h in kvh])
                                                                            for b in (b2, b3, b4)], isv)
-    got = got.reshape(-1, 6)
+    got = got.reshape(-1, 7)
     assert np.array_equal(got[:, 0], is_raw), "storage modes differ"
     comp = is_raw == 0
     assert np.array_equal(got[comp, 1], nbytes[comp]), "escape/code bytes differ"
-    assert np.array_equal(got[comp, 2:], modes[comp]), "mode counts differ"
-    assert (got[~comp, 1:] == 0).all()
+    assert np.array_equal(got[comp, 2:6], modes[comp]), "mode counts differ"
+    assert (got[~comp, 1:6] == 0).all()
+    assert (got[comp, 6] == 0).all() and (got[~comp, 6] == -1).all()  # one base version
     if ms == 0:  # the drifted keys need more escape bytes than the unrotated values
-        kt = got.reshape(nb, 2, 8, 6)
+        kt = got.reshape(nb, 2, 8, 7)
         assert kt[:, 0, :, 1].mean() > kt[:, 1, :, 1].mean()
     flags, st = c.status()
     assert flags == 0 and st["raw_tiles"] == int((~comp).sum())
