@@ -160,13 +160,15 @@ __device__ __forceinline__ uint32_t row_scan16(uint32_t v) {
 
 // Where the 16-token group starting at token t of one (sequence, K|V, head) lives.
 struct TileRef {
-  int kind;              // SRC_COMP, SRC_RAW (raw tile), SRC_NONE
+  int kind;              // bits 0..1: SRC_COMP, SRC_RAW (raw tile), SRC_NONE; above them (compressed
+                         // tiles) the offset of the tile's base version in the packed LDS bases
   int tg;                // token group inside the tile
   int escu;              // escape bytes / 16 (compressed)
-  int bo;                // offset of the tile's base version in the packed LDS bases (compressed)
   const uint8_t* p;      // the compressed or raw tile; for SRC_NONE a dummy tile-sized area (the
                          // tail buffer), so every load a kernel issues from it stays in bounds
-  __device__ __forceinline__ int valid() const { return kind == SRC_NONE ? 0 : 16; }
+  __device__ __forceinline__ int src() const { return kind & 3; }
+  __device__ __forceinline__ int bo() const { return kind >> 2; }
+  __device__ __forceinline__ int valid() const { return src() == SRC_NONE ? 0 : 16; }
 };
 
 // L here is the token count of the finished blocks (a multiple of T): the tail is merged in
@@ -189,7 +191,6 @@ __device__ __forceinline__ TileRef tile_ref(const AttnArgs& a, int seq, int L, i
   r.kind = SRC_NONE;
   r.tg = (t % TT) >> 4;
   r.escu = 0;
-  r.bo = 0;
   r.p = reinterpret_cast<const uint8_t*>(a.B.tail);
   if (t >= L || entry == kUnallocated) {  // past the finished blocks, or missing (missing_flag)
     r.tg = 0;
@@ -200,10 +201,9 @@ __device__ __forceinline__ TileRef tile_ref(const AttnArgs& a, int seq, int L, i
     r.kind = SRC_RAW;
     r.p = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * TG<NR, TT, FMT>::RAW * FmtT<FMT>::EB;
   } else {
-    r.kind = SRC_COMP;
+    r.kind = SRC_COMP | (entry_version(entry) * (2 * NR * 16)) << 2;  // and the bases it was encoded with
     r.p = a.B.comp_pool + (size_t)slot * (uint32_t)a.G.stride;
     r.escu = min(entry_esc_units(entry), a.G.esc_cap >> 4);  // never past the slot's escape area
-    r.bo = entry_version(entry) * (2 * NR * 16);  // the bases the tile was encoded with
   }
   return r;
 }
@@ -228,8 +228,10 @@ struct CRegs {
   uint32_t cd[NR][3];
 };
 
+// esc_loader: this lane's group stages the tile's escape bytes (with 64-token blocks the four
+// lane groups hold the same tile and group 0 stages them for all).
 template <int NR, int TT, int FMT>
-__device__ __forceinline__ void load_tile(const TileRef& r, int n, CRegs<NR, FMT>& c) {
+__device__ __forceinline__ void load_tile(const TileRef& r, int n, CRegs<NR, FMT>& c, bool esc_loader) {
   using Q = TG<NR, TT, FMT>;
   const uint8_t* t = r.p;  // a raw or dummy tile is large enough for every load below
   c.tE = c.tR = 0;
@@ -238,8 +240,8 @@ __device__ __forceinline__ void load_tile(const TileRef& r, int n, CRegs<NR, FMT
     c.tR = ld32(t + 4 * (Q::PW + n));
   }
   c.esc0 = c.esc1 = make_uint4(0, 0, 0, 0);
-  if (n < r.escu) c.esc0 = ld128(t + Q::ESC_OFF + 16 * n);
-  if (n + 16 < r.escu) c.esc1 = ld128(t + Q::ESC_OFF + 16 * (n + 16));
+  if (esc_loader && n < r.escu) c.esc0 = ld128(t + Q::ESC_OFF + 16 * n);
+  if (esc_loader && n + 16 < r.escu) c.esc1 = ld128(t + Q::ESC_OFF + 16 * (n + 16));
   // one base per section for this lane's first pair; round i adds 16 pairs (immediate offsets)
   const uint32_t pr0 = (uint32_t)(r.tg * (Q::D / 2) + n);
   const uint8_t* smb = t + Q::SM_OFF + (FMT == 0 ? 32u : FMT == 1 ? 12u : 16u) * pr0;
@@ -271,15 +273,15 @@ __device__ __forceinline__ void load_tile(const TileRef& r, int n, CRegs<NR, FMT
 // read only staged units.
 template <int NR, int FMT>
 __device__ __forceinline__ uint32_t stage_escape(CRegs<NR, FMT>& c, const TileRef& r, int n, uint8_t* esc_lds,
-                                                 uint32_t& bad) {
-  if (r.kind == SRC_COMP) {
+                                                 bool esc_loader, uint32_t& bad) {
+  if (esc_loader && r.src() == SRC_COMP) {
     if (n < r.escu) *reinterpret_cast<uint4*>(esc_lds + 16 * n) = c.esc0;
     if (n + 16 < r.escu) *reinterpret_cast<uint4*>(esc_lds + 16 * (n + 16)) = c.esc1;
   }
   // escape units per group: wide 1, raw F - 3 (the E plane counts 1 for both)
   const uint32_t cnt = __popc(c.tE) + (uint32_t)(FmtT<FMT>::F - 4) * __popc(c.tR);
   const uint32_t incl = row_scan16(cnt);
-  if (r.kind == SRC_COMP && !esc_tags_fit(incl, (uint32_t)r.escu)) {
+  if (r.src() == SRC_COMP && !esc_tags_fit(incl, (uint32_t)r.escu)) {
     bad |= 1u;
     c.tE = c.tR = 0u;
     return 0u;
@@ -540,6 +542,16 @@ __device__ __forceinline__ void phase_priority(int rp) {
 }
 
 // ------------------------------------------------------------------------------------------
+// b3[c0], b3[c0+1], b4[c0], b4[c0+1] of base version ver for packed-bases slot k = (K|V, round i,
+// lane n): c0 = 32i + 2n, one byte each.
+template <int NR>
+__device__ __forceinline__ uint32_t packed_bases(const Geo& G, const uint8_t* bases, int ver, int k, int h) {
+  const int kv = k / (NR * 16), i = (k / 16) % NR, nn = k % 16, c0 = 32 * i + 2 * nn;
+  const uint8_t* b3 = bases_of(G, bases, ver, 3, kv, h);
+  const uint8_t* b4 = bases_of(G, bases, ver, 4, kv, h);
+  return b3[c0] | (b3[c0 + 1] << 8) | (b4[c0] << 16) | (b4[c0 + 1] << 24);
+}
+
 // Compressed cache.
 template <int NR, int TT, int FMT>
 __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_comp_kernel(AttnArgs a) {
@@ -562,6 +574,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   const int si = z.x, seq = z.y, L = z.z;
   const SbOrder ord(L, a.n_splits, split);
   uint8_t* esc_lds = esc_base + (kEscAreas == 1 ? 0 : j * esc_room);
+  const bool esc_loader = kEscAreas > 1 || j == 0;  // the lanes that load and stage escape bytes
   const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(esc_lds);
   const uint32_t below = (1u << (2 * n)) - 1u;
   uint32_t flags = 0, bad = 0;
@@ -583,22 +596,11 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
     const int k = lane + kWave * u;
     qr[u] = k < G.g * (D / 8) ? ld128(a.q + ((size_t)si * G.Hq + h * G.g) * D + 8 * k) : make_uint4(0, 0, 0, 0);
   }
-  // the packed bases of every base version the cache holds (one unless it was recalibrated)
+  // the packed bases of base version 0 (every cache has it)
   constexpr int BU = 2 * NR * 16 / kWave;
-  uint32_t br[kMaxVersions][BU];
+  uint32_t br[BU];
 #pragma unroll
-  for (int v = 0; v < kMaxVersions; ++v)
-#pragma unroll
-    for (int u = 0; u < BU; ++u) {
-      const int k = lane + kWave * u;
-      const int kv = k / (NR * 16), i = (k / 16) % NR, nn = k % 16, c0 = 32 * i + 2 * nn;
-      br[v][u] = 0;
-      if (v < G.n_versions) {
-        const uint8_t* b3 = bases_of(G, a.B.bases, v, 3, kv, h);
-        const uint8_t* b4 = bases_of(G, a.B.bases, v, 4, kv, h);
-        br[v][u] = b3[c0] | (b3[c0 + 1] << 8) | (b4[c0] << 16) | (b4[c0 + 1] << 24);
-      }
-    }
+  for (int u = 0; u < BU; ++u) br[u] = packed_bases<NR>(G, a.B.bases, 0, lane + kWave * u, h);
 
   float m = -INFINITY, l = 0.0f;
   f32x4_t acc[NR][2];
@@ -610,16 +612,17 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   if (ord.cnt > 0) {
     rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(0), j), 0, h, eK);
     flags |= missing_flag(L, group_token(ord.at(0), j), eK);
-    load_tile<NR, TT, FMT>(rK, n, cK);
+    load_tile<NR, TT, FMT>(rK, n, cK, esc_loader);
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u)
     if (lane + kWave * u < G.g * (D / 8)) qlds[lane + kWave * u] = qr[u];
 #pragma unroll
-  for (int v = 0; v < kMaxVersions; ++v)
-    if (v < G.n_versions)
+  for (int u = 0; u < BU; ++u) blds[lane + kWave * u] = br[u];
+  // further base versions (a recalibrated cache), after the first tile loads are in flight
+  for (int v = 1; v < G.n_versions; ++v)
 #pragma unroll
-      for (int u = 0; u < BU; ++u) blds[v * 2 * NR * 16 + lane + kWave * u] = br[v][u];
+    for (int u = 0; u < BU; ++u) blds[v * 2 * NR * 16 + lane + kWave * u] = packed_bases<NR>(G, a.B.bases, v, lane + kWave * u, h);
 
   if (ord.cnt > 0) {
     for (int it = 0; it < ord.cnt; ++it) {
@@ -628,7 +631,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       // V bytes of this super-block load while K is rebuilt and scored
       rV = tile_ref<NR, TT, FMT>(a, seq, L, group_token(sb, j), 1, h, eV);
       flags |= missing_flag(L, group_token(sb, j), eV);
-      load_tile<NR, TT, FMT>(rV, n, cV);
+      load_tile<NR, TT, FMT>(rV, n, cV, esc_loader);
       if (it + 1 < ord.cnt) {
         eK = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), j), 0, h);
         eV = load_entry<TT>(a, seq, L, group_token(ord.at(it + 1), j), 1, h);
@@ -636,15 +639,17 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 
       // ---- K: rebuild into the LDS tile ----
       __syncthreads();
-      const uint32_t pfxK = stage_escape<NR, FMT>(cK, rK, n, esc_lds, bad);
+      const uint32_t pfxK = stage_escape<NR, FMT>(cK, rK, n, esc_lds, esc_loader, bad);
       __syncthreads();
-      if (rK.kind == SRC_COMP) {
+      if (rK.src() == SRC_COMP) {
         uint32_t tags[NR][3];
+        // the tile's base version: one per wave with 64-token blocks (a scalar), else per lane group
+        const int boK = kEscAreas == 1 ? __builtin_amdgcn_readfirstlane(rK.bo()) : rK.bo();
         fetch_tags<NR, FMT>(cK, j, rK.tg, pfxK, tags);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
           uint32_t o[2][2][4];
-          rebuild_round<NR, FMT>(cK, i, j, n, tags[i], blds[rK.bo + i * 16 + n], esc16, below, bad, o);
+          rebuild_round<NR, FMT>(cK, i, j, n, tags[i], blds[boK + i * 16 + n], esc16, below, bad, o);
           // transpose to token-major rows: token 16j + 4q + k gets the (c0, c0+1) word, taken
           // from one half of each of the two channels' token-pair words (BF16: word k & 1, half
           // k >> 1; FP8: word k >> 1, half k & 1)
@@ -668,7 +673,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       // to BF16 on the way.  Rows past the valid tokens hold stale but finite-or-not data;
       // their scores are masked before the softmax.
       if constexpr (FMT != 0) {
-        if (rK.kind == SRC_RAW) {
+        if (rK.src() == SRC_RAW) {
           constexpr int NCH = D / 8;  // 8-element pieces per row; lane n takes pieces n, n+16, ...
 #pragma unroll
           for (int m0 = 0; m0 < NCH; m0 += 4) {
@@ -691,7 +696,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
         bool dma = false;
 #pragma unroll 1
         for (int g = 0; g < 4; ++g) {
-          if (__builtin_amdgcn_readlane(rK.kind, 16 * g) != SRC_RAW) continue;
+          if ((__builtin_amdgcn_readlane(rK.kind, 16 * g) & 3) != SRC_RAW) continue;
           const uint64_t rp = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)((uintptr_t)rK.p >> 32), 16 * g) << 32) |
                               (uint32_t)__builtin_amdgcn_readlane((int)(uintptr_t)rK.p, 16 * g);
           const int tg_g = __builtin_amdgcn_readlane(rK.tg, 16 * g);
@@ -747,28 +752,29 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       if (it + 1 < ord.cnt) {
         rK = tile_ref<NR, TT, FMT>(a, seq, L, group_token(ord.at(it + 1), j), 0, h, eK);
         flags |= missing_flag(L, group_token(ord.at(it + 1), j), eK);
-        load_tile<NR, TT, FMT>(rK, n, cK);
+        load_tile<NR, TT, FMT>(rK, n, cK, esc_loader);
       }
 
       phase_priority(2 * (ord.cnt - it) - 1);
       // ---- V: rebuild straight into B operands ----
       __syncthreads();
-      const uint32_t pfxV = stage_escape<NR, FMT>(cV, rV, n, esc_lds, bad);
+      const uint32_t pfxV = stage_escape<NR, FMT>(cV, rV, n, esc_lds, esc_loader, bad);
       __syncthreads();
       uint32_t tagsV[NR][3];
+      const int boV = kEscAreas == 1 ? __builtin_amdgcn_readfirstlane(rV.bo()) : rV.bo();
       fetch_tags<NR, FMT>(cV, j, rV.tg, pfxV, tagsV);
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         uint4 bv[2][2];
-        if (rV.kind == SRC_COMP) {
+        if (rV.src() == SRC_COMP) {
           uint32_t o[2][2][4];
-          rebuild_round<NR, FMT>(cV, i, j, n, tagsV[i], blds[rV.bo + (NR + i) * 16 + n], esc16, below, bad, o);
+          rebuild_round<NR, FMT>(cV, i, j, n, tagsV[i], blds[boV + (NR + i) * 16 + n], esc16, below, bad, o);
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
             bv[x][0] = make_uint4(o[x][0][0], o[x][1][0], o[x][0][1], o[x][1][1]);
             bv[x][1] = make_uint4(o[x][0][2], o[x][1][2], o[x][0][3], o[x][1][3]);
           }
-        } else if (rV.kind == SRC_RAW) {
+        } else if (rV.src() == SRC_RAW) {
 #pragma unroll
           for (int x = 0; x < 2; ++x)
 #pragma unroll
