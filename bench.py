@@ -58,7 +58,9 @@ def parse():
     ap.add_argument("--splits", type=int, default=256)
     ap.add_argument("--layers", type=int, default=8, help="layer caches rotated through (cold-cache protocol)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--sweep", type=str, default="", help="comma-separated split counts to time (extra)")
+    ap.add_argument("--sweep", type=str, default="4,8,16,128,512",
+                    help="comma-separated split counts at which the attention kernel alone is also timed (4, 8 "
+                         "and 16 splits are the literal reading of 64-256 blocks per split); '' for none")
     ap.add_argument("--probe", action="store_true", help="also time plain HBM copy / read kernels (torch)")
     ap.add_argument("--extra", type=str, default="context,fp8,paged,groups,nested,rope,serving,prefill",
                     help="comma list of extra workloads measured after the headline one: context (the cfg2 "
@@ -360,7 +362,9 @@ def main():
                      "source_digest": digest, "attainable_GBps": attain["GBps"],
                      "frac_of_attainable": round(achieved / attain["GBps"], 4)},
         "attainable_read": attain,
-        "sweep_attention_us": sweep or None,
+        "sweep_attention_us": dict(sweep, note="the split kernel alone at other split counts (median of 32 "
+                                   "cold launches, an event pair around each); 4, 8 and 16 splits = 256, 128 and "
+                                   "64 blocks per split, the literal reading of 64-256 blocks per split") if sweep else None,
         "hbm_probe": probe,
     }
     extras = [x for x in args.extra.split(",") if x]
@@ -912,7 +916,8 @@ def cpu_baseline(cfg, k0, v0, min_seconds=10.0):
     """The oracle as it stands, on the host.  value: one full decode step -- rebuild every tile of
     the layer from its stored form and evaluate exact fp64 attention for all 32 query heads --
     repeated for about min_seconds on all threads.  Also: the same step on one thread, the encode
-    of the whole layer cache on all threads and on one, and the tiny layer end to end."""
+    of the whole layer cache on all threads and on one, the tiny layer end to end, and one step
+    each of the FP8 layer and of the paged serving mix."""
     import oracle
     import synth
     p = oracle.Params(oracle.BF16, cfg.T, cfg.D, cfg.G)
@@ -958,6 +963,38 @@ def cpu_baseline(cfg, k0, v0, min_seconds=10.0):
     k_, v_ = s0.decoded()
     oracle.attention(oracle.BF16, synth.queries(c0)[0], k_, v_, c0.scale)
     tiny_us = (time.perf_counter() - t0) * 1e6
+    # one step of the FP8 E5M2 64K layer and one of the 32-sequence paged mix, all threads
+    # (encode untimed: the cache is built first, as on the GPU)
+    other = {}
+    c4 = synth.config(4, synth.E5M2)
+    _, toks4 = synth.sequence_tokens(c4)
+    k4, v4 = toks4[0]
+    p4 = oracle.Params(c4.fmt, c4.T, c4.D, c4.G)
+    s4 = oracle.Sequence(p4, c4.Hkv, oracle.calibrate_layer(p4, k4[:c4.n_cal], v4[:c4.n_cal]))
+    s4.append(k4, v4)
+    t0 = time.perf_counter()
+    k_, v_ = s4.decoded()
+    oracle.attention(c4.fmt, synth.queries(c4)[0], k_, v_, c4.scale)
+    other[c4.name + "-e5m2"] = {"us_per_step": round((time.perf_counter() - t0) * 1e6, 1),
+                                "what": "rebuild all 16384 FP8 tiles + fp64 attention, 32 query heads"}
+    del s4, k_, v_, toks4, k4, v4
+    c3 = synth.config(3)
+    _, toks3 = synth.sequence_tokens(c3)
+    p3 = oracle.Params(oracle.BF16, c3.T, c3.D, c3.G)
+    b3_ = oracle.calibrate_layer(p3, toks3[0][0][:c3.n_cal], toks3[0][1][:c3.n_cal])
+    seqs3 = []
+    for kk, vv in toks3:
+        sq = oracle.Sequence(p3, c3.Hkv, b3_)
+        sq.append(kk, vv)
+        seqs3.append(sq)
+    q3 = synth.queries(c3)
+    t0 = time.perf_counter()
+    for si, sq in enumerate(seqs3):
+        k_, v_ = sq.decoded()
+        oracle.attention(oracle.BF16, q3[si], k_, v_, c3.scale)
+    other[c3.name] = {"us_per_step": round((time.perf_counter() - t0) * 1e6, 1),
+                      "what": f"32 sequences, {sum(len(t[0]) for t in toks3)} tokens: rebuild every tile + fp64 attention"}
+    del seqs3, toks3
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -974,7 +1011,8 @@ def cpu_baseline(cfg, k0, v0, min_seconds=10.0):
             "encode_layer_s": {"threads": threads, "all_threads": round(enc_s[threads], 3), "one_thread": round(enc_s[1], 3),
                                "tiles": len(s.tiles) * 2 * cfg.Hkv},
             "tiny_layer_end_to_end_us": {"value": round(tiny_us, 1),
-                                         "what": f"{c0.name}: calibrate, encode, rebuild and fp64 attention, {threads} threads"}}
+                                         "what": f"{c0.name}: calibrate, encode, rebuild and fp64 attention, {threads} threads"},
+            "other_steps": other}
 
 
 if __name__ == "__main__":
