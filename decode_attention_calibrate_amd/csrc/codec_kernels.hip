@@ -1536,22 +1536,49 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
+// An 8-element piece of one token's channels as stored (BF16: 16 bytes; FP8: 8 bytes).
+template <int FMT> struct PrefillPiece { typedef uint4 type; };
+template <> struct PrefillPiece<1> { typedef uint2 type; };
+template <> struct PrefillPiece<2> { typedef uint2 type; };
+
+// The piece as eight BF16 values in natural order (FP8 converted exactly).
 template <int FMT>
+__device__ __forceinline__ uint4 piece_bf16(const typename PrefillPiece<FMT>::type& x) {
+  if constexpr (FMT == 0) {
+    return x;
+  } else {
+    const uint32_t w[2] = {x.x, x.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t b = w[k >> 1] >> (16 * (k & 1));
+      o[k] = (uint32_t)bf16_of<FMT>(b & 0xFFu) | ((uint32_t)bf16_of<FMT>((b >> 8) & 0xFFu) << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// D: head channels (64, 128 or 256).
+template <int FMT, int D>
 __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   constexpr int QW = 16;           // queries per wave
   constexpr int QT = 4 * QW;       // queries per workgroup
+  using Piece = typename PrefillPiece<FMT>::type;
   const Geo& G = a.G;
-  const int D = G.D, Hkv = G.Hkv, Hq = G.Hq, g = G.g, EB = G.EB, tid = threadIdx.x;
+  const int Hkv = G.Hkv, Hq = G.Hq, g = G.g, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6, col = lane & 15, kq = lane >> 4;
-  const int KB = D > 128 ? 32 : 64;  // keys per block in LDS
+  constexpr int KB = D > 128 ? 32 : 64;  // keys per block in LDS
+  // LDS row strides, each an odd number of 16-byte units, so that the 16 rows an MFMA operand
+  // read touches (and the rows the fill writes at once) fall in different bank groups
+  constexpr int KS = D + 8, VS = KB + 8;
+  constexpr int C8 = D / 8, TO = KB / 8;  // 8-channel pieces per token, 8-token octets per block
   // the last query tiles attend the most keys: they go first (longest processing time first);
   // heads are the fastest grid dimension, so every head's longest tiles precede all shorter ones
   const int q0 = (gridDim.y - 1 - blockIdx.y) * QT, hq = blockIdx.x, h = hq / g;
   const int pos0 = a.n_kv - a.n_q;   // position of query 0
   const int nq = min(QT, a.n_q - q0);
-  __shared__ __align__(16) uint16_t kl[64 * 128];     // key block, BF16 bits, [t][c]
-  __shared__ __align__(16) uint16_t vtl[64 * 128];    // value block, BF16 bits, [c][t]
-  __shared__ __align__(16) float pl[4][QW * 64];      // each wave's probabilities, [query][key]
+  __shared__ __align__(16) uint16_t kl[64 * 136];     // key block, BF16 bits, [t][KS]
+  __shared__ __align__(16) uint16_t vtl[256 * 40];    // value block transposed, BF16 bits, [c][VS]
   // this wave's queries as QK A operands (rows = queries, k = channels), zero past n_q
   const int qw0 = q0 + QW * wv;                        // first query of this wave
   uint4 qa[8];
@@ -1561,48 +1588,82 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
     if (32 * ks < D && qw0 + col < a.n_q)
       qa[ks] = *reinterpret_cast<const uint4*>(a.q + ((size_t)(qw0 + col) * Hq + hq) * D + 32 * ks + 8 * kq);
   }
-  float m[4], l[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m[r] = -INFINITY;
-    l[r] = 0.0f;
-  }
-  f32x4_t o[16];
+  // the online softmax of query qw0 + col (every lane of a column holds the same state)
+  float m = -INFINITY, l = 0.0f;
+  f32x4_t o[16];  // O^T: lane holds channels 16s + 4kq + i of query qw0 + col
 #pragma unroll
   for (int s = 0; s < 16; ++s) o[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int last = pos0 + q0 + nq - 1;       // the last key any query of this workgroup sees
   const int wlast = pos0 + qw0 + QW - 1;     // ... of this wave (clamped below by the data)
-  for (int kb0 = 0; kb0 <= last; kb0 += KB) {
-    if constexpr (FMT == 0) {  // eight channels per thread and pass, 16-byte loads
-      for (int i = 8 * tid; i < KB * D; i += 8 * kThreads) {
-        const int t = i / D, c = i % D, tok = kb0 + t;
-        const size_t e = ((size_t)tok * Hkv + h) * D + c;
-        uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-        if (tok <= last) {
-          kx = *reinterpret_cast<const uint4*>(a.k + 2 * e);
-          vx = *reinterpret_cast<const uint4*>(a.v + 2 * e);
-        }
-        *reinterpret_cast<uint4*>(kl + i) = kx;
-        const uint32_t vw[4] = {vx.x, vx.y, vx.z, vx.w};
+
+  // The fill: threads 0..127 carry K pieces (piece p = tid + 128u: token p / C8, channels
+  // 8 (p % C8) ..), threads 128..255 an 8-token x 8-channel block of V each, transposed in
+  // registers so that one 16-byte store writes 8 tokens of one channel.  The 16 lanes of each
+  // V store phase cover 8 token octets x 2 channel parities (4 x 4 for 32-key blocks), which
+  // puts their rows in distinct bank groups.  A block's pieces load into registers while the
+  // previous block is being attended.
+  const bool kthr = tid < 128;
+  const int vt = tid - 128, v16 = vt & 15;
+  const int vj = v16 % TO, vc8 = (16 / TO) * (vt >> 4) + v16 / TO;  // V: token octet, channel piece
+  const bool vok = !kthr && vc8 < C8;
+  Piece pc[8];
+  auto load_block = [&](int kb) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) vtl[(c + k) * KB + t] = (uint16_t)(vw[k >> 1] >> (16 * (k & 1)));
+    for (int u = 0; u < 8; ++u) {
+      int t, c8;
+      bool ok;
+      if (kthr) {
+        const int p = tid + 128 * u;
+        t = p / C8;
+        c8 = p % C8;
+        ok = p < KB * C8;
+      } else {
+        t = 8 * vj + u;
+        c8 = vc8;
+        ok = vok;
       }
-    } else {
-      for (int i = tid; i < KB * D; i += kThreads) {
-        const int t = i / D, c = i % D, tok = kb0 + t;
-        const size_t e = ((size_t)tok * Hkv + h) * D + c;
-        uint16_t kx = 0, vx = 0;
-        if (tok <= last) {
-          kx = bf16_of<FMT>(elem_at(a.k, e, EB));
-          vx = bf16_of<FMT>(elem_at(a.v, e, EB));
-        }
-        kl[i] = kx;
-        vtl[c * KB + t] = vx;
+      const int tok = kb + t;
+      Piece x;
+      if constexpr (FMT == 0) x = make_uint4(0, 0, 0, 0);
+      else x = make_uint2(0, 0);
+      if (ok && tok <= last) {
+        const uint8_t* src = (kthr ? a.k : a.v) + (((size_t)tok * Hkv + h) * D + 8 * c8) * (FMT == 0 ? 2 : 1);
+        x = *reinterpret_cast<const Piece*>(src);
+      }
+      pc[u] = x;
+    }
+  };
+  auto store_block = [&]() {
+    if (kthr) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int p = tid + 128 * u;
+        if (p < KB * C8) *reinterpret_cast<uint4*>(kl + (p / C8) * KS + 8 * (p % C8)) = piece_bf16<FMT>(pc[u]);
+      }
+    } else if (vok) {
+      uint32_t x[8][4];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint4 b = piece_bf16<FMT>(pc[u]);
+        x[u][0] = b.x; x[u][1] = b.y; x[u][2] = b.z; x[u][3] = b.w;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {  // channel 8 vc8 + k: tokens 8 vj .. 8 vj + 7
+        const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
+        const int w = k >> 1;
+        const uint4 y = make_uint4(perm_b32(x[1][w], x[0][w], sel), perm_b32(x[3][w], x[2][w], sel),
+                                   perm_b32(x[5][w], x[4][w], sel), perm_b32(x[7][w], x[6][w], sel));
+        *reinterpret_cast<uint4*>(vtl + (8 * vc8 + k) * VS + 8 * vj) = y;
       }
     }
+  };
+  load_block(0);
+  for (int kb0 = 0; kb0 <= last; kb0 += KB) {
+    store_block();
     __syncthreads();
+    if (kb0 + KB <= last) load_block(kb0 + KB);  // the next block's loads run under this block's math
     if (kb0 <= wlast && qw0 < a.n_q) {
-      // scores: sub-block sb = keys kb0+16sb..; lane holds key kb0+16sb+col for queries 4kq+r
+      // S^T = K Q^T: sub-block sb = keys kb0+16sb..; lane holds keys kb0+16sb+4kq+i of query col
       f32x4_t sc[4];
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) {
@@ -1611,78 +1672,80 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int ks = 0; ks < 8; ++ks)
             if (32 * ks < D)
-              sc[sb] = mfma_bf16(qa[ks], *reinterpret_cast<const uint4*>(kl + (16 * sb + col) * D + 32 * ks + 8 * kq), sc[sb]);
+              sc[sb] = mfma_bf16(*reinterpret_cast<const uint4*>(kl + (16 * sb + col) * KS + 32 * ks + 8 * kq), qa[ks], sc[sb]);
         }
       }
-      float rmax[4];
+      const int qpos = pos0 + qw0 + col;
+      const bool qok = qw0 + col < a.n_q;
+      float rmax = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qpos = pos0 + qw0 + 4 * kq + r;
-        rmax[r] = -INFINITY;
+      for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-          const int tok = kb0 + 16 * sb + col;
-          const bool ok = 16 * sb < KB && tok <= qpos && qw0 + 4 * kq + r < a.n_q;
-          sc[sb][r] = ok ? sc[sb][r] * a.sl2 : -INFINITY;
-          rmax[r] = fmaxf(rmax[r], sc[sb][r]);
+        for (int i = 0; i < 4; ++i) {
+          const int tok = kb0 + 16 * sb + 4 * kq + i;
+          const bool ok = 16 * sb < KB && tok <= qpos && qok;
+          sc[sb][i] = ok ? sc[sb][i] * a.sl2 : -INFINITY;
+          rmax = fmaxf(rmax, sc[sb][i]);
         }
-        for (int x = 1; x < 16; x <<= 1) rmax[r] = fmaxf(rmax[r], __shfl_xor(rmax[r], x));
-      }
-      float alpha[4];
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 16));  // the query's other keys sit in lanes col + 16 kq
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+      const float m_new = fmaxf(m, rmax);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = exp2f(m - m_use);
+      float sum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float m_new = fmaxf(m[r], rmax[r]);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        alpha[r] = exp2f(m[r] - m_use);
-        float sum = 0.0f;
+      for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-          const float p = exp2f(sc[sb][r] - m_use);
-          if (16 * sb < KB) pl[wv][(4 * kq + r) * 64 + 16 * sb + col] = p;
-          sum += p;
+        for (int i = 0; i < 4; ++i) {
+          sc[sb][i] = exp2f(sc[sb][i] - m_use);
+          sum += sc[sb][i];
         }
-        for (int x = 1; x < 16; x <<= 1) sum += __shfl_xor(sum, x);
-        l[r] = l[r] * alpha[r] + sum;
-        m[r] = m_new;
-      }
-      // the wave's own P rows are read back as PV A operands (rows = queries, k = keys); LDS
-      // accesses of one wave complete in order, no barrier needed
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      l = l * alpha + sum;
+      m = m_new;
 #pragma unroll
       for (int s = 0; s < 16; ++s)
         if (16 * s < D)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[s][r] *= alpha[r];
+          for (int i = 0; i < 4; ++i) o[s][i] *= alpha;
+      // O^T += V^T P^T over 32-key chunks (sub-blocks 2kc, 2kc+1).  Inside a chunk the MFMA's
+      // k slots 8kq+j and 8kq+4+j stand for keys 16(2kc)+4kq+j and 16(2kc+1)+4kq+j, so each
+      // lane's own probabilities are its P^T operand (as a BF16 high part plus remainder) and
+      // the V^T operand reads the same keys: two 8-byte pieces of a channel row.
       for (int kc = 0; kc < KB / 32; ++kc) {
-        const float* pr = &pl[wv][col * 64 + 32 * kc + 8 * kq];
         uint32_t hi[4], lo[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          hi[e] = bf16_pair(pr[2 * e], pr[2 * e + 1]);
-          lo[e] = bf16_pair(pr[2 * e] - __uint_as_float(hi[e] << 16), pr[2 * e + 1] - __uint_as_float(hi[e] & 0xFFFF0000u));
+          const float p0 = sc[2 * kc + (e >> 1)][2 * (e & 1)], p1 = sc[2 * kc + (e >> 1)][2 * (e & 1) + 1];
+          hi[e] = bf16_pair(p0, p1);
+          lo[e] = bf16_pair(p0 - __uint_as_float(hi[e] << 16), p1 - __uint_as_float(hi[e] & 0xFFFF0000u));
         }
         const uint4 ph = make_uint4(hi[0], hi[1], hi[2], hi[3]), plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
           if (16 * s < D) {
-            const uint4 vb = *reinterpret_cast<const uint4*>(vtl + (16 * s + col) * KB + 32 * kc + 8 * kq);
-            o[s] = mfma_bf16(ph, vb, o[s]);
-            o[s] = mfma_bf16(plo, vb, o[s]);
+            const uint16_t* vr = vtl + (16 * s + col) * VS + 32 * kc + 4 * kq;
+            const uint2 v0 = *reinterpret_cast<const uint2*>(vr), v1 = *reinterpret_cast<const uint2*>(vr + 16);
+            const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
+            o[s] = mfma_bf16(va, ph, o[s]);
+            o[s] = mfma_bf16(va, plo, o[s]);
           }
         }
       }
     }
     __syncthreads();  // before the next key block replaces kl and vtl
   }
-  // out: lane holds channel 16s+col of queries 4kq+r
+  // out: lane holds channels 16s + 4kq .. 16s + 4kq + 3 of query qw0 + col
+  const int qi = qw0 + col;
+  if (qi < a.n_q) {
+    const float inv = 1.0f / l;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int qi = qw0 + 4 * kq + r;
-    if (qi < a.n_q) {
-#pragma unroll
-      for (int s = 0; s < 16; ++s)
-        if (16 * s < D)
-          a.out[((size_t)qi * Hq + hq) * D + 16 * s + col] = __builtin_bit_cast(uint16_t, (__bf16)(o[s][r] / l[r]));
-    }
+    for (int s = 0; s < 16; ++s)
+      if (16 * s < D) {
+        uint16_t* dst = a.out + ((size_t)qi * Hq + hq) * D + 16 * s + 4 * kq;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_pair(o[s][0] * inv, o[s][1] * inv), bf16_pair(o[s][2] * inv, o[s][3] * inv));
+      }
   }
 }
 
@@ -1807,7 +1870,11 @@ int launch_prefill(const Geo& G, const void* k, const void* v, int n_kv, const u
   a.n_kv = n_kv;
   a.n_q = n_q;
   a.sl2 = scale * 1.4426950408889634f;
-  auto kern = G.fmt == 0 ? prefill_kernel<0> : G.fmt == 1 ? prefill_kernel<1> : prefill_kernel<2>;
+  if (G.D != 64 && G.D != 128 && G.D != 256) return (int)hipErrorInvalidValue;
+  void (*kern)(PrefillArgs);
+  if (G.D == 64) kern = G.fmt == 0 ? prefill_kernel<0, 64> : G.fmt == 1 ? prefill_kernel<1, 64> : prefill_kernel<2, 64>;
+  else if (G.D == 128) kern = G.fmt == 0 ? prefill_kernel<0, 128> : G.fmt == 1 ? prefill_kernel<1, 128> : prefill_kernel<2, 128>;
+  else kern = G.fmt == 0 ? prefill_kernel<0, 256> : G.fmt == 1 ? prefill_kernel<1, 256> : prefill_kernel<2, 256>;
   hipLaunchKernelGGL(kern, dim3(G.Hq, (n_q + 63) / 64), dim3(kThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
