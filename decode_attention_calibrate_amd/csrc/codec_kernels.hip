@@ -924,25 +924,39 @@ __device__ void decode_tile_v2(const Geo& G, const DevBufs& B, const uint8_t* ti
   }
   if (tid == 0 && total > 8 * G.code_cap) bad = true;  // codes past the capacity
   __syncthreads();
-  const uint8_t* code = tile + G.code_off;
-  const uint8_t* sm = tile + G.sm_off;
-  const int max_bit = 8 * G.code_cap;
-  for (int i = tid; i < G.raw_elems; i += kThreads) {
-    const int t = i / D, c = i % D, tg = t / GT, tau = t % GT;
-    const int q = tg * D + c, n = q * GT + tau;
+  // one group per thread and pass: its code bits (at most GT * 8 = 128, plus up to 31 bits of
+  // word offset: five words) in registers from aligned word loads, clamped to the slot's code
+  // area; its GT sign/mantissa bytes in one 8- or 16-byte load; its base once
+  const uint32_t* code32 = reinterpret_cast<const uint32_t*>(tile + G.code_off);
+  const int n_words = (G.code_cap + 15) / 16 * 4;  // the code area (16-byte aligned) in words
+  for (int q = tid; q < G.NG; q += kThreads) {
     const int k = gk[q], w = G.mw[k];
-    const int bp = (int)gO[q] + tau * w;
-    uint32_t o = 0;
-    if (bp + w <= max_bit) {
-      const int by = bp >> 3, sh = bp & 7;
-      uint32_t v = code[by];
-      if (sh + w > 8) v |= (uint32_t)code[by + 1] << 8;
-      o = (v >> sh) & ((1u << w) - 1u);
+    const int tg = q / D, c = q % D;
+    const uint32_t base = v2_base(G, k, b2, b3, b4, c);
+    const int O = (int)gO[q], w0 = O >> 5, sh = O & 31;
+    uint32_t cw[5];
+#pragma unroll
+    for (int u = 0; u < 5; ++u) cw[u] = (w0 + u < n_words && (u == 0 || 32 * u < sh + GT * w)) ? code32[w0 + u] : 0u;
+    uint32_t smw[4];
+    if (GT == 16) {
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + G.sm_off + (size_t)q * 16);
+      smw[0] = v.x; smw[1] = v.y; smw[2] = v.z; smw[3] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(tile + G.sm_off + (size_t)q * 8);
+      smw[0] = v.x; smw[1] = v.y; smw[2] = smw[3] = 0u;
     }
-    const uint32_t e = v2_base(G, k, b2, b3, b4, c) + o;
-    bad |= e > 255u;
-    const uint32_t s8 = sm[n];
-    put(t, c, ((s8 >> 7) << 15) | ((e & 0xFFu) << 7) | (s8 & 0x7Fu));
+    const uint32_t mask = (1u << w) - 1u;
+    for (int tau = 0; tau < GT; ++tau) {
+      const int bp = sh + tau * w, wi = bp >> 5, bs = bp & 31;
+      const uint32_t lo = cw[0], hi = cw[1];
+      uint32_t a0 = wi == 0 ? lo : wi == 1 ? hi : wi == 2 ? cw[2] : wi == 3 ? cw[3] : cw[4];
+      uint32_t a1 = wi == 0 ? hi : wi == 1 ? cw[2] : wi == 2 ? cw[3] : wi == 3 ? cw[4] : 0u;
+      const uint32_t o = (uint32_t)(((((uint64_t)a1 << 32) | a0) >> bs) & mask);
+      const uint32_t e = base + o;
+      bad |= e > 255u;
+      const uint32_t s8 = (smw[tau >> 2] >> (8 * (tau & 3))) & 0xFFu;
+      put(tg * GT + tau, c, ((s8 >> 7) << 15) | ((e & 0xFFu) << 7) | (s8 & 0x7Fu));
+    }
   }
   if (bad) atomicOr(&B.counters->status, 8u);
 }
