@@ -1591,8 +1591,9 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
   const int q0 = (gridDim.y - 1 - blockIdx.y) * QT, hq = blockIdx.x, h = hq / g;
   const int pos0 = a.n_kv - a.n_q;   // position of query 0
   const int nq = min(QT, a.n_q - q0);
-  __shared__ __align__(16) uint16_t kl[64 * 136];     // key block, BF16 bits, [t][KS]
-  __shared__ __align__(16) uint16_t vtl[256 * 40];    // value block transposed, BF16 bits, [c][VS]
+  // two buffers: the next key block is stored while the current one is attended
+  __shared__ __align__(16) uint16_t klb[2][64 * 136];   // key block, BF16 bits, [t][KS]
+  __shared__ __align__(16) uint16_t vtlb[2][256 * 40];  // value block transposed, BF16 bits, [c][VS]
   // this wave's queries as QK A operands (rows = queries, k = channels), zero past n_q
   const int qw0 = q0 + QW * wv;                        // first query of this wave
   uint4 qa[8];
@@ -1647,7 +1648,9 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
       pc[u] = x;
     }
   };
-  auto store_block = [&]() {
+  auto store_block = [&](int buf) {
+    uint16_t* kl = klb[buf];
+    uint16_t* vtl = vtlb[buf];
     if (kthr) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -1672,10 +1675,12 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
     }
   };
   load_block(0);
-  for (int kb0 = 0; kb0 <= last; kb0 += KB) {
-    store_block();
-    __syncthreads();
-    if (kb0 + KB <= last) load_block(kb0 + KB);  // the next block's loads run under this block's math
+  store_block(0);
+  __syncthreads();
+  if (KB <= last) load_block(KB);
+  for (int kb0 = 0, buf = 0; kb0 <= last; kb0 += KB, buf ^= 1) {
+    const uint16_t* kl = klb[buf];
+    const uint16_t* vtl = vtlb[buf];
     if (kb0 <= wlast && qw0 < a.n_q) {
       // S^T = K Q^T: sub-block sb = keys kb0+16sb..; lane holds keys kb0+16sb+4kq+i of query col
       f32x4_t sc[4];
@@ -1748,7 +1753,11 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
         }
       }
     }
-    __syncthreads();  // before the next key block replaces kl and vtl
+    // the next block (loaded during the previous block's math) into the other buffer, then one
+    // barrier: this block's reads are done and the next block's stores are visible
+    if (kb0 + KB <= last) store_block(buf ^ 1);
+    __syncthreads();
+    if (kb0 + 2 * KB <= last) load_block(kb0 + 2 * KB);
   }
   // out: lane holds channels 16s + 4kq .. 16s + 4kq + 3 of query qw0 + col
   const int qi = qw0 + col;
