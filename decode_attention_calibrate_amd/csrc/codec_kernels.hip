@@ -1517,12 +1517,13 @@ __global__ void __launch_bounds__(kThreads) attn_half_kernel(HalfAttnArgs a) {
 // Prefill attention over blocks rebuilt by the block decoder (GAAC page §3.3 encodes a prompt's
 // complete blocks during prefill and says nothing about how prefill attention reads them; this
 // library runs standard causal attention on the rebuilt blocks).  Causal: query i of n_q (token
-// position n_kv - n_q + i) attends tokens
-// 0 .. its own position.  One 256-thread workgroup per (64 queries, query head), 16 queries
-// per wave; key blocks of KB tokens (64, or 32 for 256-channel heads) go to LDS as BF16 (K as
-// rows, V transposed); QK and PV on v_mfma_f32_16x16x32_bf16 (P as a BF16 high part plus
-// remainder, ~16 mantissa bits), an online softmax per query row in between; each wave's P
-// tile passes through LDS to change from the QK output layout to the PV operand layout.
+// position n_kv - n_q + i) attends tokens 0 .. its own position.  One 256-thread workgroup per
+// (64 queries, query head), 16 queries per wave; key blocks of KB tokens (64, or 32 for
+// 256-channel heads) go to double-buffered LDS as BF16 (K as rows, V transposed); the scores
+// are computed transposed, S^T = K Q^T, and the output as O^T = V^T P^T on
+// v_mfma_f32_16x16x32_bf16, so each lane holds one query's scores and they serve directly as
+// its PV operand (P as a BF16 high part plus remainder, ~16 mantissa bits), with an online
+// softmax per query in between.
 struct PrefillArgs {
   Geo G;               // the cache's geometry (format; D and heads in the real head layout)
   const uint8_t* k;    // [n_kv][Hkv][D] elements
