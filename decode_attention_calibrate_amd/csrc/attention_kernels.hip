@@ -75,6 +75,10 @@ struct FmtT {
   static constexpr int MB = FMT == 0 ? 7 : (FMT == 1 ? 2 : 3);  // mantissa bits
   static constexpr int EB = FMT == 0 ? 2 : 1;                   // bytes per element
   static constexpr int SMW = FMT == 0 ? 8 : (FMT == 1 ? 3 : 4); // SM words per pair of groups
+  // FP8 exponents are rebuilt in place, at bit MB of their byte lane (bases, codes and escape
+  // bits all pre-shifted), so that the element byte is one bit-select away; BF16 at bit 0.
+  static constexpr int XS = FMT == 0 ? 0 : MB;
+  static constexpr uint32_t XMASK = FMT == 0 ? 0xFFFFFFFFu : ((1u << F) - 1u) * (0x01010101u << MB);
   // Rebuilt words of four tokens 4q..4q+3: BF16 pairs (4q, 4q+2), (4q+1, 4q+3) [interleaved];
   // FP8 (converted to BF16) pairs (4q, 4q+1), (4q+2, 4q+3) [natural].
   static constexpr bool NATURAL = FMT != 0;
@@ -289,14 +293,47 @@ __device__ __forceinline__ uint32_t stage_escape(CRegs<NR, FMT>& c, const TileRe
   return incl - cnt;
 }
 
-// Escape spread table: entry v holds bit 3 set in byte k for every set bit k of v (the
-// plane bits of four tokens moved to exponent bit 3 of their byte lanes).  Lives at LDS
-// offset 0 of every attention workgroup.
+// Escape spread table: entry v holds exponent bit 3 set in byte k for every set bit k of v (the
+// plane bits of four tokens moved to exponent bit 3 of their byte lanes; for FP8 the exponent
+// sits at bit MB of the lane).  Lives at LDS offset 0 of every attention workgroup.
 __shared__ uint32_t esc_lut[16];
 
+template <int FMT>
 __device__ __forceinline__ void init_esc_lut() {
-  if (threadIdx.x < 16) esc_lut[threadIdx.x] = spread4(threadIdx.x) << 3;
+  if (threadIdx.x < 16) esc_lut[threadIdx.x] = spread4(threadIdx.x) << (3 + FmtT<FMT>::XS);
 }
+
+// (a & mask) | (b & ~mask) as one v_bfi_b32.  Written as asm: given chains of constant-mask
+// selects the compiler splits them into separate ANDs and an OR3 (two more instructions each).
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(b));
+  return r;
+}
+
+// Sign and mantissa of the E5M2 elements of slot S of an SM unit (3-bit fields sign:mantissa,
+// laid out like the exponent codes) at their FP8 bit positions: sign at bit 7, mantissa at bits
+// 0..1 of each byte lane (bits 2..6 undefined).
+template <int S>
+__device__ __forceinline__ uint32_t e5m2_sign_mant(uint32_t W0, uint32_t W1, uint32_t W2) {
+  constexpr int x = 3 * S, w = x / 8, b = x % 8;
+  const uint32_t lo = (w == 0 ? W0 : (w == 1 ? W1 : W2));
+  if constexpr (b <= 5) {
+    return bfi(0x80808080u, lo << (5 - b), lo >> b);
+  } else {
+    const uint32_t hi = (w == 0 ? W1 : W2);
+    if constexpr (b == 6) return bfi(0x80808080u, hi << 7, lo >> 6);
+    else return bfi(0x80808080u, hi << 6, bfi(0x02020202u, hi << 1, lo >> 7));
+  }
+}
+
+// Sign and mantissa of four E4M3 elements from y = bytes (a, a, b, b) of an SM word (4-bit
+// fields sign:mantissa, low nibble first): elements (a.lo, a.hi, b.lo, b.hi) with the sign at
+// bit 7 and the mantissa at bits 0..2 of their byte lanes (bits 3..6 undefined).  Lanes 0 and 1
+// (2 and 3) hold the same byte, so y >> 4 brings each low nibble's sign to bit 7 of lane 0 (2)
+// and each high nibble's mantissa down to bits 0..2 of lane 1 (3); the other bits are already
+// in place in y.
+__device__ __forceinline__ uint32_t e4m3_sign_mant(uint32_t y) { return bfi(0x07800780u, y >> 4, y); }
 
 // Rebuild the two groups of round i for lane n of lane group j.  bases packs b3[c0], b3[c1],
 // b4[c0], b4[c1]; below = (1 << 2n) - 1.  Output, low half first: BF16 o[gi][0][q] = tokens
@@ -338,10 +375,11 @@ __device__ __forceinline__ void rebuild_round(const CRegs<NR, FMT>& c, int i, in
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int slot = 4 * gi + q;
-      const uint32_t cs = slot == 0 ? code_slot<0>(W0, W1, W2) : slot == 1 ? code_slot<1>(W0, W1, W2)
-                        : slot == 2 ? code_slot<2>(W0, W1, W2) : slot == 3 ? code_slot<3>(W0, W1, W2)
-                        : slot == 4 ? code_slot<4>(W0, W1, W2) : slot == 5 ? code_slot<5>(W0, W1, W2)
-                        : slot == 6 ? code_slot<6>(W0, W1, W2) : code_slot<7>(W0, W1, W2);
+      constexpr int XS = FmtT<FMT>::XS;
+      const uint32_t cs = slot == 0 ? code_slot<0, XS>(W0, W1, W2) : slot == 1 ? code_slot<1, XS>(W0, W1, W2)
+                        : slot == 2 ? code_slot<2, XS>(W0, W1, W2) : slot == 3 ? code_slot<3, XS>(W0, W1, W2)
+                        : slot == 4 ? code_slot<4, XS>(W0, W1, W2) : slot == 5 ? code_slot<5, XS>(W0, W1, W2)
+                        : slot == 6 ? code_slot<6, XS>(W0, W1, W2) : code_slot<7, XS>(W0, W1, W2);
       Evq[q] = H + cs + esc_lut[(plane0 >> (4 * q)) & 0xFu];
     }
     if constexpr (FMT == 0) {
@@ -356,6 +394,12 @@ __device__ __forceinline__ void rebuild_round(const CRegs<NR, FMT>& c, int i, in
           Evq[q] += ((y << 4) & 0x00F000F0u) | (y & 0xF000F000u);
         }
       }
+    } else if constexpr (FMT == 1) {
+      if (R) {  // raw group (rare): offset bit 4 of each token from unit P+1
+        const uint32_t u = esc16[P + 1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Evq[q] += esc_lut[(u >> (4 * q)) & 0xFu] << 1;
+      }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -367,24 +411,18 @@ __device__ __forceinline__ void rebuild_round(const CRegs<NR, FMT>& c, int i, in
         o[gi][0][q] = bitsel(0x7F807F80u, Ev << 7, perm_b32(sv, sv, 0x02020000u));
         o[gi][1][q] = bitsel(0x7F807F80u, Ev >> 1, perm_b32(sv, sv, 0x03030101u));
       } else {
-        uint32_t Eq = Ev;
-        if constexpr (FMT == 1) {
-          if (R) Eq += esc_lut[((uint32_t)esc16[P + 1] >> (4 * q)) & 0xFu] << 1;  // raw: offset bit 4
-        }
-        uint32_t f, B;  // f: (sign << MB) | mantissa per byte lane; B: the four FP8 bytes
+        uint32_t g;  // sign at bit 7, mantissa at bits 0..MB-1 of each byte lane
         if constexpr (FMT == 1) {
           const uint32_t S0 = c.sm.w[i][0], S1 = c.sm.w[i][1], S2 = c.sm.w[i][2];
-          f = slot == 0 ? code_slot<0>(S0, S1, S2) : slot == 1 ? code_slot<1>(S0, S1, S2)
-            : slot == 2 ? code_slot<2>(S0, S1, S2) : slot == 3 ? code_slot<3>(S0, S1, S2)
-            : slot == 4 ? code_slot<4>(S0, S1, S2) : slot == 5 ? code_slot<5>(S0, S1, S2)
-            : slot == 6 ? code_slot<6>(S0, S1, S2) : code_slot<7>(S0, S1, S2);
-          B = (Eq << 2) | (f & 0x03030303u) | ((f << 5) & 0x80808080u);
+          g = slot == 0 ? e5m2_sign_mant<0>(S0, S1, S2) : slot == 1 ? e5m2_sign_mant<1>(S0, S1, S2)
+            : slot == 2 ? e5m2_sign_mant<2>(S0, S1, S2) : slot == 3 ? e5m2_sign_mant<3>(S0, S1, S2)
+            : slot == 4 ? e5m2_sign_mant<4>(S0, S1, S2) : slot == 5 ? e5m2_sign_mant<5>(S0, S1, S2)
+            : slot == 6 ? e5m2_sign_mant<6>(S0, S1, S2) : e5m2_sign_mant<7>(S0, S1, S2);
         } else {
           const uint32_t sw = c.sm.w[i][2 * gi + (q >> 1)];
-          const uint32_t y = perm_b32(sw, sw, (q & 1) ? 0x03030202u : 0x01010000u);
-          f = (y & 0x000F000Fu) | ((y >> 4) & 0x0F000F00u);
-          B = (Eq << 3) | (f & 0x07070707u) | ((f << 4) & 0x80808080u);
+          g = e4m3_sign_mant(perm_b32(sw, sw, (q & 1) ? 0x03030202u : 0x01010000u));
         }
+        const uint32_t B = bfi(FmtT<FMT>::XMASK, Ev, g);  // the four FP8 bytes
         o[gi][0][q] = fp8x2_to_bf16x2<FMT, false>(B);
         o[gi][1][q] = fp8x2_to_bf16x2<FMT, true>(B);
       }
@@ -544,12 +582,13 @@ __device__ __forceinline__ void phase_priority(int rp) {
 // ------------------------------------------------------------------------------------------
 // b3[c0], b3[c0+1], b4[c0], b4[c0+1] of base version ver for packed-bases slot k = (K|V, round i,
 // lane n): c0 = 32i + 2n, one byte each.
-template <int NR>
+template <int NR, int FMT>
 __device__ __forceinline__ uint32_t packed_bases(const Geo& G, const uint8_t* bases, int ver, int k, int h) {
   const int kv = k / (NR * 16), i = (k / 16) % NR, nn = k % 16, c0 = 32 * i + 2 * nn;
   const uint8_t* b3 = bases_of(G, bases, ver, 3, kv, h);
   const uint8_t* b4 = bases_of(G, bases, ver, 4, kv, h);
-  return b3[c0] | (b3[c0 + 1] << 8) | (b4[c0] << 16) | (b4[c0 + 1] << 24);
+  const uint32_t w = b3[c0] | (b3[c0 + 1] << 8) | (b4[c0] << 16) | (b4[c0 + 1] << 24);
+  return w << FmtT<FMT>::XS;  // FP8 bases are < 32: each byte stays in its lane
 }
 
 // Compressed cache.
@@ -578,7 +617,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(esc_lds);
   const uint32_t below = (1u << (2 * n)) - 1u;
   uint32_t flags = 0, bad = 0;
-  init_esc_lut();
+  init_esc_lut<FMT>();
 
   // Prologue: one memory round trip before the first tile loads.  The first super-block's
   // table entries, the query heads h*g .. h*g+g-1 (g * D/8 <= 256 chunks: at most four per lane)
@@ -600,7 +639,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   constexpr int BU = 2 * NR * 16 / kWave;
   uint32_t br[BU];
 #pragma unroll
-  for (int u = 0; u < BU; ++u) br[u] = packed_bases<NR>(G, a.B.bases, 0, lane + kWave * u, h);
+  for (int u = 0; u < BU; ++u) br[u] = packed_bases<NR, FMT>(G, a.B.bases, 0, lane + kWave * u, h);
 
   float m = -INFINITY, l = 0.0f;
   f32x4_t acc[NR][2];
@@ -622,7 +661,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
   // further base versions (a recalibrated cache), after the first tile loads are in flight
   for (int v = 1; v < G.n_versions; ++v)
 #pragma unroll
-    for (int u = 0; u < BU; ++u) blds[v * 2 * NR * 16 + lane + kWave * u] = packed_bases<NR>(G, a.B.bases, v, lane + kWave * u, h);
+    for (int u = 0; u < BU; ++u) blds[v * 2 * NR * 16 + lane + kWave * u] = packed_bases<NR, FMT>(G, a.B.bases, v, lane + kWave * u, h);
 
   if (ord.cnt > 0) {
     for (int it = 0; it < ord.cnt; ++it) {

@@ -18,20 +18,23 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t 
 }
 __device__ __forceinline__ uint32_t bitsel(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
 
-// Codes of slot S (0..7) of a 32-element CODE unit: one 3-bit code per byte lane.  Lane k's
-// 24-bit stream holds slot s at bits 3s..3s+2; stream byte w of lane k is byte k of word w.
-template <int S>
+// Codes of slot S (0..7) of a 32-element CODE unit: one 3-bit code per byte lane, at bits
+// SH..SH+2 of the lane (SH <= 3; every other bit is zero).  Lane k's 24-bit stream holds slot s
+// at bits 3s..3s+2; stream byte w of lane k is byte k of word w.
+template <int S, int SH = 0>
 __device__ __forceinline__ uint32_t code_slot(uint32_t W0, uint32_t W1, uint32_t W2) {
   constexpr int x = 3 * S, w = x / 8, b = x % 8;
   const uint32_t lo = (w == 0 ? W0 : (w == 1 ? W1 : W2));
-  if constexpr (b <= 5) {
-    return (lo >> b) & 0x07070707u;
+  if constexpr (b <= 5 && b >= SH) {
+    return (lo >> (b - SH)) & (0x07070707u << SH);
+  } else if constexpr (b <= 5) {
+    return (lo << (SH - b)) & (0x07070707u << SH);
   } else if constexpr (b == 6) {
     const uint32_t hi = (w == 0 ? W1 : W2);
-    return ((lo >> 6) & 0x03030303u) | ((hi << 2) & 0x04040404u);
+    return ((lo >> (6 - SH)) & (0x03030303u << SH)) | ((hi << (2 + SH)) & (0x04040404u << SH));
   } else {
     const uint32_t hi = (w == 0 ? W1 : W2);
-    return ((lo >> 7) & 0x01010101u) | ((hi << 1) & 0x06060606u);
+    return ((lo >> (7 - SH)) & (0x01010101u << SH)) | ((hi << (1 + SH)) & (0x06060606u << SH));
   }
 }
 
