@@ -1013,15 +1013,18 @@ __device__ __forceinline__ uint32_t code_slot_rt(uint32_t W0, uint32_t W1, uint3
 // per CODE unit (32 elements = channels c0..c0+3 x tokens 8tg..8tg+7, one group per channel).
 // Escape units are single bytes (an 8-bit plane per escaped group; a raw group adds four bytes
 // of offset bits 4..7, token tau's nibble at bits 4*tau).
-// put4(t, c0, w) receives BF16 channels c0..c0+3 of token t (w.x: c0, c0+1; w.y: c0+2, c0+3).
+// put4(t, c0, w) receives BF16 channels c0..c0+3 of token t (w.x: c0, c0+1; w.y: c0+2, c0+3);
+// with by_cols, put8(tg, c, w) instead receives tokens 8tg..8tg+7 of channel c in order (two per
+// word, the earlier token in the low half).
 // tl, nt, active: as stage_tile_meta (every thread of the block calls it).
-template <class Put4>
+template <class Put4, class Put8>
 __device__ void decode_bf16_g8_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
-                                    const uint8_t* b4, TileMeta& m, Put4 put4, int tl, int nt, bool active) {
+                                    const uint8_t* b4, TileMeta& m, Put4 put4, Put8 put8, bool by_cols, int tl, int nt,
+                                    bool active) {
   const int D = G.D;
+  const int n_units = active ? G.raw_elems / 32 : 0;
   stage_tile_meta(G, B, tile, m, tl, nt, active);
   const uint8_t* esc = reinterpret_cast<const uint8_t*>(m.esc);
-  const int n_units = active ? G.raw_elems / 32 : 0;
   for (int u = tl; u < n_units; u += nt) {
     const int q0 = 4 * u, w = q0 >> 5, bit = q0 & 31, tg = q0 / D, c0 = q0 % D;
     uint32_t P = m.pre[w];  // escape bytes before group q0
@@ -1058,6 +1061,13 @@ __device__ void decode_bf16_g8_tile(const Geo& G, const DevBufs& B, const uint8_
       }
       P += E + 4u * R;
     }
+    if (by_cols) {  // channel c0+gi: tokens 4qq+{0,1} are the low halves of o02, o13; 4qq+{2,3} the high
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+        put8(tg, c0 + gi, make_uint4(perm_b32(o13[gi][0], o02[gi][0], 0x05040100u), perm_b32(o13[gi][0], o02[gi][0], 0x07060302u),
+                                     perm_b32(o13[gi][1], o02[gi][1], 0x05040100u), perm_b32(o13[gi][1], o02[gi][1], 0x07060302u)));
+      continue;
+    }
     // token t = 8tg + 4qq + k: channels c0..c0+3 as one 8-byte store
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
@@ -1069,6 +1079,11 @@ __device__ void decode_bf16_g8_tile(const Geo& G, const DevBufs& B, const uint8_
         put4(8 * tg + 4 * qq + k, c0, make_uint2(w01, w23));
       }
   }
+}
+template <class Put4>
+__device__ void decode_bf16_g8_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
+                                    const uint8_t* b4, TileMeta& m, Put4 put4, int tl, int nt, bool active) {
+  decode_bf16_g8_tile(G, B, tile, b3, b4, m, put4, [](int, int, uint4) {}, false, tl, nt, active);
 }
 
 // One block per (block, K|V, head): rebuilds the tile into [n*T][Hkv][D].
@@ -1165,9 +1180,12 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
 // workgroup covers a contiguous range of finished blocks of one (sequence, KV head), rebuilds
 // every block's K and V tile on chip, into LDS (the cache is never decompressed to HBM), and
 // keeps an fp32 online softmax for each query head of the GQA group; the partial results (acc,
-// and max and sum in base-2 units) go to the same workspace, for the same merge kernel.  Scores
-// and PV are fp32 multiply-adds over LDS: this path is correct for every format and block size,
-// not tuned.
+// and max and sum in base-2 units) go to the same workspace, for the same merge kernel.  The
+// rebuilt tiles go to LDS as BF16 (FP8 converted exactly; K as rows, V transposed, rows padded
+// to an odd number of 16-byte units); scores and PV run on v_mfma_f32_16x16x32_bf16 with the
+// query heads as the 16 rows (zero past the GQA group): wave w scores tokens 16w..16w+15, the
+// block's maximum per head meets in LDS, the probabilities go to LDS as a BF16 high part plus
+// remainder (~16 mantissa bits), and wave w accumulates channels (D/4)w .. (D/4)(w+1)-1.
 struct AnyAttnArgs {
   Geo G;
   DevBufs B;
@@ -1212,34 +1230,82 @@ __device__ __forceinline__ float seg_max(float v, int W) {
   return v;
 }
 
+// Element bits -> BF16 bits, exactly (every FP8 value is a BF16 value).
+template <int FMT>
+__device__ __forceinline__ uint16_t elem_bf16(uint32_t x) {
+  if constexpr (FMT == 0) return (uint16_t)x;
+  else return (uint16_t)(__float_as_uint(elem_value<FMT>(x)) >> 16);
+}
+
+typedef __bf16 any_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float any_f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ any_f32x4_t any_mfma(const uint4& a, const uint4& b, any_f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(any_bf16x8_t, a), __builtin_bit_cast(any_bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+// Maximum / sum over each row of 16 lanes (DPP: quad swaps, then the half-row and row mirrors),
+// the same value in all 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float any_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, any_dpp<0xB1>(v));
+  v = fmaxf(v, any_dpp<0x4E>(v));
+  v = fmaxf(v, any_dpp<0x141>(v));
+  return fmaxf(v, any_dpp<0x140>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += any_dpp<0xB1>(v);
+  v += any_dpp<0x4E>(v);
+  v += any_dpp<0x141>(v);
+  return v + any_dpp<0x140>(v);
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
+  constexpr int KS = 128 + 8;  // K rows [t][KS], BF16 bits
+  constexpr int VS = 64 + 8;   // V transposed [c][VS]; P [head][VS]
   const Geo& G = a.G;
   const int D = G.D, T = G.T, g = G.g, S = a.n_splits, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6, col = lane & 15, kq = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y;
   const int4 z = a.zrow[blockIdx.z];
   const int si = z.x, seq = z.y, L = z.z;
-  __shared__ __align__(16) uint16_t kvt[2][kAnyMaxTD];  // the block's K and V as element bits, [t][c]
-  __shared__ float qf[kAnyMaxG * 128];    // query heads h*g .. h*g+g-1
-  __shared__ float pr[kAnyMaxG * 64];     // scores, then probabilities, [head][t]
-  __shared__ float mh[kAnyMaxG], lh[kAnyMaxG], al[kAnyMaxG];
+  __shared__ __align__(16) uint16_t kt[64 * KS];
+  __shared__ __align__(16) uint16_t vt[128 * VS];
+  __shared__ __align__(16) uint16_t pl[2][16 * VS];  // probabilities, BF16 high part and remainder
+  __shared__ float wmx[4][16], wsm[4][16];            // per wave: maximum and sum of each head's row
+  __shared__ float mh[16], lh[16];                    // running maximum and sum per head (row)
   __shared__ TileMeta meta[2];
   // blocks [b0, b1): the finished blocks dealt out as evenly as possible
   const int nb = L / T, per = nb / S, rem = nb % S;
   const int b0 = split * per + min(split, rem), b1 = b0 + per + (split < rem ? 1 : 0);
-  for (int i = tid; i < g * D; i += kThreads)
-    qf[i] = __uint_as_float((uint32_t)a.q[((size_t)si * G.Hq + h * g) * D + i] << 16);
-  if (tid < g) {
+  // zeros where a 16-token block leaves the MFMA's 32-token K steps short (tokens 16..31 of P and
+  // V are never written then)
+  for (int i = tid; i < 128 * VS / 8; i += kThreads) reinterpret_cast<uint4*>(vt)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < 2 * 16 * VS / 8; i += kThreads) reinterpret_cast<uint4*>(pl)[i] = make_uint4(0, 0, 0, 0);
+  if (tid < 16) {
     mh[tid] = -INFINITY;
     lh[tid] = 0.0f;
   }
-  constexpr int OPT = kAnyMaxG * 128 / kThreads;  // outputs (head, channel) per thread
-  float acc[OPT];
+  // this lane's query operands: head col (zero past the group), channels 32i + 8kq .. +7
+  uint4 qa[4];
 #pragma unroll
-  for (int u = 0; u < OPT; ++u) acc[u] = 0.0f;
+  for (int i = 0; i < 4; ++i)
+    qa[i] = (col < g && 32 * i < D) ? *reinterpret_cast<const uint4*>(a.q + ((size_t)si * G.Hq + h * g + col) * D + 32 * i + 8 * kq)
+                                    : make_uint4(0, 0, 0, 0);
+  const int CTW = D / 64;  // 16-channel output tiles per wave
+  any_f32x4_t o[2];
+  o[0] = o[1] = any_f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint32_t flags = 0;
   __syncthreads();
   auto entry = [&](int b, int kv) -> uint32_t { return a.B.table[table_index(G, seq, b, kv, h)]; };
+  // rebuilt element (t, c) of the K (kv 0) or V (kv 1) tile, as BF16 bits, to LDS
+  auto put = [&](int kv, int t, int c, uint32_t x) {
+    if (kv) vt[c * VS + t] = elem_bf16<FMT>(x);
+    else kt[t * KS + c] = elem_bf16<FMT>(x);
+  };
   uint32_t eK = b0 < b1 ? entry(b0, 0) : kUnallocated, eV = b0 < b1 ? entry(b0, 1) : kUnallocated;
   for (int b = b0; b < b1; ++b) {
     // the next block's table entries load while this block is rebuilt
@@ -1254,97 +1320,108 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
       const uint32_t e = kv ? eV : eK, slot = entry_slot(e);
       const bool comp = e != kUnallocated && !(e & kRawTile);
       const int ver = comp ? entry_version(e) : 0;
-      uint16_t* dst = kvt[kv];
       if (e == kUnallocated) {  // missing: zeros, reported
-        for (int i = tl; i < T * D; i += kThreads / 2) dst[i] = 0;
+        for (int i = tl; i < T * D; i += kThreads / 2) put(kv, i / D, i % D, 0u);
         flags |= 4u;
       } else if (!comp) {  // raw tile: K [t][c], V [c][t]
         const uint16_t* src = reinterpret_cast<const uint16_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems;
-        for (int i = tl; i < T * D; i += kThreads / 2) dst[i] = src[kv ? (size_t)(i % D) * T + i / D : (size_t)i];
+        for (int i = tl; i < T * D; i += kThreads / 2) put(kv, i / D, i % D, src[kv ? (size_t)(i % D) * T + i / D : (size_t)i]);
       }
       const uint8_t* tile = a.B.comp_pool + (comp ? (size_t)slot * G.stride : 0);
       decode_bf16_g8_tile(G, a.B, tile, bases_of(G, a.B.bases, ver, 3, kv, h), bases_of(G, a.B.bases, ver, 4, kv, h), meta[kv],
-                          [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(dst + t * D + c0) = w; },
+                          [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(kt + t * KS + c0) = w; },
+                          [&](int tg, int c, uint4 w) { *reinterpret_cast<uint4*>(vt + c * VS + 8 * tg) = w; }, kv == 1,
                           tl, kThreads / 2, comp);
       __syncthreads();
     } else {
       for (int kv = 0; kv < 2; ++kv) {
-        uint16_t* dst = kvt[kv];
         const uint32_t e = kv ? eV : eK, slot = entry_slot(e);
         const int ver = entry_version(e);
         if (e == kUnallocated) {  // missing: zeros, reported
-          for (int i = tid; i < T * D; i += kThreads) dst[i] = 0;
+          for (int i = tid; i < T * D; i += kThreads) put(kv, i / D, i % D, 0u);
           flags |= 4u;
         } else if (e & kRawTile) {  // raw tile: K [t][c], V [c][t]
           const uint8_t* src = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
           for (int i = tid; i < T * D; i += kThreads) {
             const int t = i / D, c = i % D;
-            dst[i] = (uint16_t)elem_at(src, kv ? (size_t)c * T + t : (size_t)i, G.EB);
+            put(kv, t, c, elem_at(src, kv ? (size_t)c * T + t : (size_t)i, G.EB));
           }
         } else if (G.mode_set != 0) {  // FORMAT v2 (nested precision modes, BF16)
           decode_tile_v2(G, a.B, a.B.comp_pool + (size_t)slot * G.stride, bases_of(G, a.B.bases, ver, 2, kv, h),
                          bases_of(G, a.B.bases, ver, 3, kv, h), bases_of(G, a.B.bases, ver, 4, kv, h),
-                         [&](int t, int c, uint32_t x) { dst[t * D + c] = (uint16_t)x; });
+                         [&](int t, int c, uint32_t x) { put(kv, t, c, x); });
         } else {
           decode_tile_any(G, a.B, a.B.comp_pool + (size_t)slot * G.stride, bases_of(G, a.B.bases, ver, 3, kv, h),
-                          bases_of(G, a.B.bases, ver, 4, kv, h),
-                          [&](int t, int c, uint32_t x) { dst[t * D + c] = (uint16_t)x; });
+                          bases_of(G, a.B.bases, ver, 4, kv, h), [&](int t, int c, uint32_t x) { put(kv, t, c, x); });
         }
         __syncthreads();
       }
     }
     eK = nK;
     eV = nV;
-    // scores and the online softmax: one (head, token) pair per thread and pass, so a head's T
-    // tokens sit in an aligned segment of T lanes of one wave (T divides 64).  Each thread walks
-    // the channels from its own offset, so the threads of a wave read different LDS banks.
-    for (int p0 = 0; p0 < g * T; p0 += kThreads) {
-      const int p = p0 + tid;
-      const bool on = p < g * T;  // whole segments are on or off together
-      const int hh = on ? p / T : 0, t = p % T;
-      float d = 0.0f;
-      if (on) {
-        const uint16_t* kr = kvt[0] + t * D;
-        const float* qr = qf + hh * D;
-        for (int cc = 0; cc < D; cc += 2) {
-          const int c = (cc + 2 * t) & (D - 1);
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(kr + c);
-          d += elem_value<FMT>(w & 0xFFFFu) * qr[c] + elem_value<FMT>(w >> 16) * qr[c + 1];
-        }
-      }
-      const float sc = d * a.sl2;
-      const float m_old = on ? mh[hh] : 0.0f;
-      const float m_new = fmaxf(m_old, seg_max(sc, T));
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float pv = exp2f(sc - m_use);
-      const float sum = seg_sum(pv, T);
-      if (on) {
-        pr[hh * 64 + t] = pv;
-        if (t == 0) {
-          const float alpha = exp2f(m_old - m_use);
-          lh[hh] = lh[hh] * alpha + sum;
-          mh[hh] = m_new;
-          al[hh] = alpha;
-        }
+    // ---- scores: wave w takes tokens 16w .. 16w+15; lane holds heads 4kq+r of token 16w+col ----
+    float sc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (16 * wv < T) {
+      any_f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (32 * i < D) acc = any_mfma(qa[i], *reinterpret_cast<const uint4*>(kt + (16 * wv + col) * KS + 32 * i + 8 * kq), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[r] = acc[r] * a.sl2;
+        const float mx = row16_max(sc[r]);
+        if (col == 0) wmx[wv][4 * kq + r] = mx;
       }
     }
     __syncthreads();
+    // ---- the block's maximum per head, probabilities, rescale factors ----
+    float alpha[4];
 #pragma unroll
-    for (int u = 0; u < OPT; ++u) {
-      const int o = tid + kThreads * u;
-      if (o < g * D) {
-        const int hh = o / D, c = o % D;
-        float s = acc[u] * al[hh];
-        for (int t = 0; t < T; ++t) s += pr[hh * 64 + t] * elem_value<FMT>(kvt[1][t * D + c]);
-        acc[u] = s;
+    for (int r = 0; r < 4; ++r) {
+      const int hd = 4 * kq + r;
+      float mb = wmx[0][hd];
+      for (int w = 1; w < T / 16; ++w) mb = fmaxf(mb, wmx[w][hd]);
+      const float m_old = mh[hd], m_new = fmaxf(m_old, mb);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      alpha[r] = exp2f(m_old - m_use);
+      if (16 * wv < T) {
+        const float p = exp2f(sc[r] - m_use);
+        const float hi = (float)(__bf16)p;
+        pl[0][hd * VS + 16 * wv + col] = __builtin_bit_cast(uint16_t, (__bf16)p);
+        pl[1][hd * VS + 16 * wv + col] = __builtin_bit_cast(uint16_t, (__bf16)(p - hi));
+        const float sm = row16_sum(p);
+        if (col == 0) wsm[wv][hd] = sm;
       }
     }
-    __syncthreads();  // before the next block overwrites the tiles and the probabilities
-  }
+    __syncthreads();
+    // ---- PV: wave w accumulates channel tiles CTW*w .. ; the running state moves on ----
+    for (int u = 0; u < CTW; ++u) {
+      const int ct = CTW * wv + u;
 #pragma unroll
-  for (int u = 0; u < OPT; ++u) {
-    const int o = tid + kThreads * u;
-    if (o < g * D) a.ws_acc[(((size_t)si * G.Hq + h * g + o / D) * S + split) * D + o % D] = acc[u];
+      for (int r = 0; r < 4; ++r) o[u][r] *= alpha[r];
+      for (int j = 0; 32 * j < T; ++j) {
+        const uint4 vb = *reinterpret_cast<const uint4*>(vt + (16 * ct + col) * VS + 32 * j + 8 * kq);
+        o[u] = any_mfma(*reinterpret_cast<const uint4*>(pl[0] + col * VS + 32 * j + 8 * kq), vb, o[u]);
+        o[u] = any_mfma(*reinterpret_cast<const uint4*>(pl[1] + col * VS + 32 * j + 8 * kq), vb, o[u]);
+      }
+    }
+    if (tid < 16) {  // the running maximum and sum of head (row) tid, as every lane rescaled above
+      float mb = wmx[0][tid], sum = wsm[0][tid];
+      for (int w = 1; w < T / 16; ++w) mb = fmaxf(mb, wmx[w][tid]), sum += wsm[w][tid];
+      const float m_old = mh[tid], m_new = fmaxf(m_old, mb);
+      lh[tid] = lh[tid] * exp2f(m_old - (m_new == -INFINITY ? 0.0f : m_new)) + sum;
+      mh[tid] = m_new;
+    }
+    __syncthreads();  // before the next block overwrites the tiles, the probabilities and the state
+  }
+  // ---- partial results: heads 4kq+r, channels 16ct + col ----
+  for (int u = 0; u < CTW; ++u) {
+    const int ct = CTW * wv + u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hd = 4 * kq + r;
+      if (hd < g) a.ws_acc[(((size_t)si * G.Hq + h * g + hd) * S + split) * D + 16 * ct + col] = o[u][r];
+    }
   }
   if (tid < g) {
     float* ml = a.ws_ml + (((size_t)si * G.Hq + h * g + tid) * S + split) * 2;
