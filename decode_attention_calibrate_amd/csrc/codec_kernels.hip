@@ -984,13 +984,18 @@ __device__ void stage_tile_meta(const Geo& G, const DevBufs& B, const uint8_t* t
     for (int i = tl; i < G.esc_cap / 4; i += nt) m.esc[i] = esc_g[i];
   }
   __syncthreads();
-  if (active && tl == 0) {
-    uint32_t acc = 0;
-    for (int i = 0; i < G.PW; ++i) {
-      m.pre[i] = acc;
-      acc += __popc(m.tag[i]) + (uint32_t)(G.F - 4) * __popc(m.tag[G.PW + i]);
+  // escape units before each tag word: an exclusive scan over the PW <= 32 words by the first
+  // wave of the staging threads (nt >= 128 threads: tl < 64 is one whole wave)
+  if (active && tl < 64) {
+    const uint32_t cnt = tl < G.PW ? __popc(m.tag[tl]) + (uint32_t)(G.F - 4) * __popc(m.tag[G.PW + tl]) : 0u;
+    uint32_t inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = (uint32_t)__shfl_up((int)inc, o);
+      if (tl >= o) inc += t;
     }
-    if (acc * (uint32_t)G.GT > 8u * (uint32_t)G.esc_cap) atomicOr(&B.counters->status, 8u);  // escape overrun
+    if (tl < G.PW) m.pre[tl] = inc - cnt;
+    if (tl == 63 && inc * (uint32_t)G.GT > 8u * (uint32_t)G.esc_cap) atomicOr(&B.counters->status, 8u);  // escape overrun
   }
   __syncthreads();
 }
