@@ -1780,37 +1780,54 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
       const int qpos = pos0 + qw0 + col;
       const bool qok = qw0 + col < a.n_q;
       float rmax = -INFINITY;
+      // the causal mask and the query count matter only on the blocks that reach past this
+      // wave's first query or hold the last queries; elsewhere every score is kept
+      if (kb0 + KB - 1 <= pos0 + qw0 && qw0 + QW <= a.n_q) {
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
+        for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = kb0 + 16 * sb + 4 * kq + i;
-          const bool ok = 16 * sb < KB && tok <= qpos && qok;
-          sc[sb][i] = ok ? sc[sb][i] * a.sl2 : -INFINITY;
-          rmax = fmaxf(rmax, sc[sb][i]);
-        }
+          for (int i = 0; i < 4; ++i) {
+            sc[sb][i] = 16 * sb < KB ? sc[sb][i] * a.sl2 : -INFINITY;
+            rmax = fmaxf(rmax, sc[sb][i]);
+          }
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = kb0 + 16 * sb + 4 * kq + i;
+            const bool ok = 16 * sb < KB && tok <= qpos && qok;
+            sc[sb][i] = ok ? sc[sb][i] * a.sl2 : -INFINITY;
+            rmax = fmaxf(rmax, sc[sb][i]);
+          }
+      }
       rmax = fmaxf(rmax, __shfl_xor(rmax, 16));  // the query's other keys sit in lanes col + 16 kq
       rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
       const float m_new = fmaxf(m, rmax);
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = exp2f(m - m_use);
+      // exponents are <= 0 here: the hardware exp2 (results below 2^-126 flush to 0)
+      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
       float sum = 0.0f;
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sc[sb][i] = exp2f(sc[sb][i] - m_use);
+          sc[sb][i] = __builtin_amdgcn_exp2f(sc[sb][i] - m_use);
           sum += sc[sb][i];
         }
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
       l = l * alpha + sum;
+      // the running output needs rescaling only where a query's maximum moved (alpha < 1); once
+      // the maxima settle, whole blocks skip it
+      if (__any(m_new != m)) {
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+          if (16 * s < D)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[s][i] *= alpha;
+      }
       m = m_new;
-#pragma unroll
-      for (int s = 0; s < 16; ++s)
-        if (16 * s < D)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[s][i] *= alpha;
       // O^T += V^T P^T over 32-key chunks (sub-blocks 2kc, 2kc+1).  Inside a chunk the MFMA's
       // k slots 8kq+j and 8kq+4+j stand for keys 16(2kc)+4kq+j and 16(2kc+1)+4kq+j, so each
       // lane's own probabilities are its P^T operand (as a BF16 high part plus remainder) and
