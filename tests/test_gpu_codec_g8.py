@@ -102,7 +102,7 @@ def test_g8_every_fp8_pattern(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("T", [16, 64])
+@pytest.mark.parametrize("T", [16, 32, 64])
 def test_g8_compressed_attention_matches_oracle(fmt, T):
     """Decode attention over caches with 8-token groups (the kernel that rebuilds each block's
     tiles into LDS): lengths ending before the first block, just past a block and inside one,
@@ -144,6 +144,26 @@ def test_g8_head_dim_128_and_gqa_group_of_4():
     q = synth.queries(cfg, step=L)
     out = host(cache.attention([0], dev(q), cfg.scale, 32))
     assert row_rel_err(out[0], oracle.attention(oracle.BF16, q[0], k[:L], v[:L], cfg.scale)) <= 4e-3
+
+
+@pytest.mark.parametrize("fmt", [oracle.BF16, oracle.E4M3])
+def test_g8_gqa_group_of_16_at_32_token_blocks(fmt):
+    """Sixteen query heads per KV head (every row of the kernel's 16-row MFMA tiles a real head),
+    128 channels, 32-token blocks (two of the four waves score each block), a ragged length and
+    a tail; against the oracle."""
+    cfg = dataclasses.replace(synth.config(0), fmt=fmt, G=8, T=32, Hkv=1, Hq=16, D=128)
+    g, toks = synth.sequence_tokens(cfg)
+    k, v = toks[0]
+    L = 1000
+    cache = new_cache(Hkv=1, Hq=16, D=128, T=32, max_seqs=1, max_blocks=L // 32 + 2, fmt=fmt, Gt=8)
+    cache.calibrate(dev(k[:cfg.n_cal], fmt), dev(v[:cfg.n_cal], fmt))
+    cache.append([0], dev(k[None, :L], fmt), dev(v[None, :L], fmt))
+    q = synth.queries(cfg, step=L)
+    ref = oracle.attention(fmt, q[0], k[:L], v[:L], cfg.scale)
+    for S in (1, 7):
+        out = host(cache.attention([0], dev(q), cfg.scale, S))
+        assert row_rel_err(out[0], ref) <= 4e-3, S
+    assert cache.status()[0] == 0
 
 
 @pytest.mark.parametrize("fmt", FMTS)

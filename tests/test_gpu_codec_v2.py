@@ -119,19 +119,19 @@ def test_v2_raw_fallback():
         assert row_rel_err(host(c.attention([0], dev(q), cfg.scale, 4))[0], ref) <= TOL
 
 
-@pytest.mark.parametrize("ms", [1, 2, 3])
+@pytest.mark.parametrize("ms,T", [(1, 64), (2, 64), (3, 64), (1, 32)])
 @pytest.mark.parametrize("Gt", [8, 16])
-def test_v2_attention_and_decode_step(ms, Gt):
+def test_v2_attention_and_decode_step(ms, T, Gt):
     """Decode attention over FORMAT v2 caches against the oracle (three sequences of ragged
     lengths, several split counts), then decode steps bit-identical to append + attention."""
-    cfg = synth.config(0)
+    cfg = dataclasses.replace(synth.config(0), T=T)
     g = synth.LayerGen(cfg)
     lens = [1, 200, 777]
     toks = [g.tokens(L + 20) for L in lens]
     cal = toks[2]
     caches = []
     for _ in range(2):
-        c = _cache(cfg, 64, Gt, ms, max_seqs=3, max_blocks=15)
+        c = _cache(cfg, T, Gt, ms, max_seqs=3, max_blocks=800 // T + 3)
         c.calibrate(dev(cal[0][:256]), dev(cal[1][:256]))
         for sid, (k, v) in enumerate(toks):
             c.append([sid], dev(k[None, :lens[sid]]), dev(v[None, :lens[sid]]))
