@@ -38,6 +38,38 @@ __device__ __forceinline__ uint32_t code_slot(uint32_t W0, uint32_t W1, uint32_t
   }
 }
 
+// (a & mask) | (b & ~mask) as one v_bfi_b32.  Written as asm: given chains of constant-mask
+// selects the compiler splits them into separate ANDs and an OR3 (two more instructions each).
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(b));
+  return r;
+}
+
+// Sign and mantissa of the E5M2 elements of slot S of an SM unit (3-bit fields sign:mantissa,
+// laid out like the exponent codes) at their FP8 bit positions: sign at bit 7, mantissa at bits
+// 0..1 of each byte lane (bits 2..6 undefined).
+template <int S>
+__device__ __forceinline__ uint32_t e5m2_sign_mant(uint32_t W0, uint32_t W1, uint32_t W2) {
+  constexpr int x = 3 * S, w = x / 8, b = x % 8;
+  const uint32_t lo = (w == 0 ? W0 : (w == 1 ? W1 : W2));
+  if constexpr (b <= 5) {
+    return bfi(0x80808080u, lo << (5 - b), lo >> b);
+  } else {
+    const uint32_t hi = (w == 0 ? W1 : W2);
+    if constexpr (b == 6) return bfi(0x80808080u, hi << 7, lo >> 6);
+    else return bfi(0x80808080u, hi << 6, bfi(0x02020202u, hi << 1, lo >> 7));
+  }
+}
+
+// Sign and mantissa of four E4M3 elements from y = bytes (a, a, b, b) of an SM word (4-bit
+// fields sign:mantissa, low nibble first): elements (a.lo, a.hi, b.lo, b.hi) with the sign at
+// bit 7 and the mantissa at bits 0..2 of their byte lanes (bits 3..6 undefined).  Lanes 0 and 1
+// (2 and 3) hold the same byte, so y >> 4 brings each low nibble's sign to bit 7 of lane 0 (2)
+// and each high nibble's mantissa down to bits 0..2 of lane 1 (3); the other bits are already
+// in place in y.
+__device__ __forceinline__ uint32_t e4m3_sign_mant(uint32_t y) { return bfi(0x07800780u, y >> 4, y); }
+
 // 24-bit multiply (v_mul_u32_u24, full rate).  Written as asm so that the compiler cannot fold a
 // following shift into the constant and fall back to the quarter-rate 32-bit multiply.
 __device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) {

@@ -1091,6 +1091,110 @@ __device__ void decode_bf16_g8_tile(const Geo& G, const DevBufs& B, const uint8_
   decode_bf16_g8_tile(G, B, tile, b3, b4, m, put4, [](int, int, uint4) {}, false, tl, nt, active);
 }
 
+// Four FP8 values (bytes of w, in order) -> four BF16 values (two per word, in order), exactly.
+template <int FMT>
+__device__ __forceinline__ uint2 fp8x4_bf16(uint32_t w) {
+  if constexpr (FMT == 1)
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true)));
+  else
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
+}
+
+// FP8 tiles (E5M2, E4M3) with 16- or 8-token groups, four tokens per 32-bit word: one thread
+// per CODE unit (32 elements: 32/GT channels x GT tokens, one group per channel).  Each 4-token
+// slot's exponents are base (b3 narrow, b4 wide, 0 raw) + 3-bit code + escape bits (plane bit 3
+// for wide and raw groups; E5M2 raw groups a second plane for bit 4; escape units of GT bits),
+// then assembled with the sign/mantissa fields into the four FP8 bytes (E5M2: 3-bit fields laid
+// out like the codes; E4M3: a nibble per element, low nibble first).  Corrupt tags (raw without
+// escape, E4M3 wide, exponent sums past the field) set status bit 8; escape reads stay inside
+// the staged capacity.
+// put_tok(t, c0, w) receives the FP8 bytes of channels c0 .. c0 + 32/GT - 1 of token t (byte i:
+// channel c0 + i); with by_cols, put_col(t0, c, w) instead receives tokens t0 .. t0 + 3 of
+// channel c (byte k: token t0 + k).  tl, nt, active: as stage_tile_meta.
+template <int FMT, int GT, class PutTok, class PutCol>
+__device__ void decode_fp8_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
+                                const uint8_t* b4, TileMeta& m, PutTok put_tok, PutCol put_col, bool by_cols, int tl,
+                                int nt, bool active) {
+  constexpr int F = FMT == 1 ? 5 : 4, MB = 7 - F;
+  constexpr int GPU = 32 / GT;  // groups (channels) per unit
+  constexpr int SPG = GT / 4;   // 4-token slots per group
+  constexpr uint32_t EMAX = ((1u << F) - 1u) * 0x01010101u;
+  const int D = G.D;
+  stage_tile_meta(G, B, tile, m, tl, nt, active);
+  const uint8_t* esc8 = reinterpret_cast<const uint8_t*>(m.esc);
+  const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(m.esc);
+  const int max_unit = GT == 8 ? G.esc_cap : G.esc_cap / 2;
+  auto esc_unit = [&](uint32_t P) -> uint32_t { return (int)P < max_unit ? (GT == 8 ? esc8[P] : esc16[P]) : 0u; };
+  const int n_units = active ? G.raw_elems / 32 : 0;
+  for (int u = tl; u < n_units; u += nt) {
+    const int q0 = GPU * u, w = q0 >> 5, bit = q0 & 31, tg = q0 / D, c0 = q0 % D;
+    const uint32_t Ew = m.tag[w], Rw = m.tag[G.PW + w];
+    const uint32_t below = bit == 0 ? 0u : (0xFFFFFFFFu >> (32 - bit));
+    uint32_t P = m.pre[w] + __popc(Ew & below) + (uint32_t)(F - 4) * __popc(Rw & below);
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(tile + G.code_off + 12 * u);
+    const uint32_t W0 = cw[0], W1 = cw[1], W2 = cw[2];
+    uint32_t S[4];
+    if constexpr (FMT == 1) {
+      const uint32_t* sw = reinterpret_cast<const uint32_t*>(tile + G.sm_off + 12 * u);
+      S[0] = sw[0], S[1] = sw[1], S[2] = sw[2], S[3] = 0u;
+    } else {
+      const uint4 s4 = *reinterpret_cast<const uint4*>(tile + G.sm_off + 16 * u);
+      S[0] = s4.x, S[1] = s4.y, S[2] = s4.z, S[3] = s4.w;
+    }
+    uint32_t bytes[GPU][SPG];
+    uint32_t over = 0;
+#pragma unroll
+    for (int gi = 0; gi < GPU; ++gi) {
+      const uint32_t E = (Ew >> (bit + gi)) & 1u, R = (Rw >> (bit + gi)) & 1u;
+      if ((R && !E) || (FMT == 2 && E && !R)) atomicOr(&B.counters->status, 8u);
+      const int c = c0 + gi;
+      const uint32_t H = (R ? 0u : (E ? b4[c] : b3[c])) * 0x01010101u;
+      const uint32_t plane = E ? esc_unit(P) : 0u;
+      const uint32_t hip = (FMT == 1 && R) ? esc_unit(P + 1) : 0u;
+#pragma unroll
+      for (int q = 0; q < SPG; ++q) {
+        const int slot = SPG * gi + q;
+        const uint32_t cs = code_slot_rt(W0, W1, W2, slot);
+        uint32_t e = H + cs + (spread4((plane >> (4 * q)) & 0xFu) << 3);
+        if constexpr (FMT == 1) e += spread4((hip >> (4 * q)) & 0xFu) << 4;
+        over |= (e + (0x80u - (1u << F)) * 0x01010101u) & 0x80808080u;  // a lane at or past 2^F
+        e &= EMAX;
+        uint32_t g;  // sign at bit 7, mantissa at bits 0..MB-1
+        if constexpr (FMT == 1) {
+          g = slot == 0 ? e5m2_sign_mant<0>(S[0], S[1], S[2]) : slot == 1 ? e5m2_sign_mant<1>(S[0], S[1], S[2])
+            : slot == 2 ? e5m2_sign_mant<2>(S[0], S[1], S[2]) : slot == 3 ? e5m2_sign_mant<3>(S[0], S[1], S[2])
+            : slot == 4 ? e5m2_sign_mant<4>(S[0], S[1], S[2]) : slot == 5 ? e5m2_sign_mant<5>(S[0], S[1], S[2])
+            : slot == 6 ? e5m2_sign_mant<6>(S[0], S[1], S[2]) : e5m2_sign_mant<7>(S[0], S[1], S[2]);
+        } else {
+          const uint32_t sw = S[slot >> 1];
+          g = e4m3_sign_mant(perm_b32(sw, sw, (slot & 1) ? 0x03030202u : 0x01010000u));
+        }
+        bytes[gi][q] = bfi(EMAX << MB, e << MB, g);
+      }
+      P += E + (uint32_t)(F - 4) * R;
+    }
+    if (over) atomicOr(&B.counters->status, 8u);
+    if (by_cols) {
+#pragma unroll
+      for (int gi = 0; gi < GPU; ++gi)
+#pragma unroll
+        for (int q = 0; q < SPG; ++q) put_col(GT * tg + 4 * q, c0 + gi, bytes[gi][q]);
+      continue;
+    }
+#pragma unroll
+    for (int q = 0; q < SPG; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t sel = 0x0C0C0000u | ((4u + k) << 8) | (uint32_t)k;  // byte k of the low, then the high word
+        uint32_t wd = perm_b32(bytes[1][q], bytes[0][q], sel);
+        if constexpr (GPU == 4) wd |= perm_b32(bytes[3][q], bytes[2][q], sel) << 16;
+        put_tok(GT * tg + 4 * q + k, c0, wd);
+      }
+  }
+}
+
 // One block per (block, K|V, head): rebuilds the tile into [n*T][Hkv][D].
 __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs B, int seq, int first,
                                                                   void* __restrict__ kout, void* __restrict__ vout) {
@@ -1130,7 +1234,23 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
                         tid, kThreads, true);
     return;
   }
-  if (G.EB == 1 || G.GT != kGroup) {
+  if (G.EB == 1) {  // FP8: the bytes of two (16-token groups) or four (8-token groups) channels per token
+    uint8_t* o8 = reinterpret_cast<uint8_t*>(outv);
+    auto put_tok = [&](int t, int c0, uint32_t w) {
+      if (G.GT == 8) *reinterpret_cast<uint32_t*>(o8 + out_idx(t, c0)) = w;
+      else *reinterpret_cast<uint16_t*>(o8 + out_idx(t, c0)) = (uint16_t)w;
+    };
+    auto no_col = [](int, int, uint32_t) {};
+    if (G.fmt == 1) {
+      if (G.GT == 8) decode_fp8_tile<1, 8>(G, B, tile, b3, b4, meta, put_tok, no_col, false, tid, kThreads, true);
+      else decode_fp8_tile<1, 16>(G, B, tile, b3, b4, meta, put_tok, no_col, false, tid, kThreads, true);
+    } else {
+      if (G.GT == 8) decode_fp8_tile<2, 8>(G, B, tile, b3, b4, meta, put_tok, no_col, false, tid, kThreads, true);
+      else decode_fp8_tile<2, 16>(G, B, tile, b3, b4, meta, put_tok, no_col, false, tid, kThreads, true);
+    }
+    return;
+  }
+  if (G.GT != kGroup) {
     decode_tile_any(G, B, tile, b3, b4, [&](int t, int c, uint32_t x) { elem_put(outv, out_idx(t, c), G.EB, x); });
     return;
   }
@@ -1319,8 +1439,9 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
       nK = entry(b + 1, 0);
       nV = entry(b + 1, 1);
     }
-    if (FMT == 0 && G.mode_set == 0) {
-      // BF16, 8-token groups: the K tile by threads 0..127 and the V tile by 128..255 at once
+    if (G.mode_set == 0) {
+      // FORMAT v1: the K tile by threads 0..127 and the V tile by 128..255 at once (BF16 with
+      // 8-token groups, or FP8), K as rows, V as transposed columns
       const int kv = tid >> 7, tl = tid & 127;
       const uint32_t e = kv ? eV : eK, slot = entry_slot(e);
       const bool comp = e != kUnallocated && !(e & kRawTile);
@@ -1329,14 +1450,27 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
         for (int i = tl; i < T * D; i += kThreads / 2) put(kv, i / D, i % D, 0u);
         flags |= 4u;
       } else if (!comp) {  // raw tile: K [t][c], V [c][t]
-        const uint16_t* src = reinterpret_cast<const uint16_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems;
-        for (int i = tl; i < T * D; i += kThreads / 2) put(kv, i / D, i % D, src[kv ? (size_t)(i % D) * T + i / D : (size_t)i]);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
+        for (int i = tl; i < T * D; i += kThreads / 2)
+          put(kv, i / D, i % D, elem_at(src, kv ? (size_t)(i % D) * T + i / D : (size_t)i, G.EB));
       }
       const uint8_t* tile = a.B.comp_pool + (comp ? (size_t)slot * G.stride : 0);
-      decode_bf16_g8_tile(G, a.B, tile, bases_of(G, a.B.bases, ver, 3, kv, h), bases_of(G, a.B.bases, ver, 4, kv, h), meta[kv],
-                          [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(kt + t * KS + c0) = w; },
-                          [&](int tg, int c, uint4 w) { *reinterpret_cast<uint4*>(vt + c * VS + 8 * tg) = w; }, kv == 1,
-                          tl, kThreads / 2, comp);
+      const uint8_t* b3 = bases_of(G, a.B.bases, ver, 3, kv, h);
+      const uint8_t* b4 = bases_of(G, a.B.bases, ver, 4, kv, h);
+      if constexpr (FMT == 0) {
+        decode_bf16_g8_tile(G, a.B, tile, b3, b4, meta[kv],
+                            [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(kt + t * KS + c0) = w; },
+                            [&](int tg, int c, uint4 w) { *reinterpret_cast<uint4*>(vt + c * VS + 8 * tg) = w; }, kv == 1,
+                            tl, kThreads / 2, comp);
+      } else {
+        auto put_tok = [&](int t, int c0, uint32_t w) {
+          if (G.GT == 8) *reinterpret_cast<uint2*>(kt + t * KS + c0) = fp8x4_bf16<FMT>(w);
+          else *reinterpret_cast<uint32_t*>(kt + t * KS + c0) = fp8x4_bf16<FMT>(w).x;
+        };
+        auto put_col = [&](int t0, int c, uint32_t w) { *reinterpret_cast<uint2*>(vt + c * VS + t0) = fp8x4_bf16<FMT>(w); };
+        if (G.GT == 8) decode_fp8_tile<FMT, 8>(G, a.B, tile, b3, b4, meta[kv], put_tok, put_col, kv == 1, tl, kThreads / 2, comp);
+        else decode_fp8_tile<FMT, 16>(G, a.B, tile, b3, b4, meta[kv], put_tok, put_col, kv == 1, tl, kThreads / 2, comp);
+      }
       __syncthreads();
     } else {
       for (int kv = 0; kv < 2; ++kv) {
@@ -1351,13 +1485,10 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
             const int t = i / D, c = i % D;
             put(kv, t, c, elem_at(src, kv ? (size_t)c * T + t : (size_t)i, G.EB));
           }
-        } else if (G.mode_set != 0) {  // FORMAT v2 (nested precision modes, BF16)
+        } else {  // FORMAT v2 (nested precision modes, BF16)
           decode_tile_v2(G, a.B, a.B.comp_pool + (size_t)slot * G.stride, bases_of(G, a.B.bases, ver, 2, kv, h),
                          bases_of(G, a.B.bases, ver, 3, kv, h), bases_of(G, a.B.bases, ver, 4, kv, h),
                          [&](int t, int c, uint32_t x) { put(kv, t, c, x); });
-        } else {
-          decode_tile_any(G, a.B, a.B.comp_pool + (size_t)slot * G.stride, bases_of(G, a.B.bases, ver, 3, kv, h),
-                          bases_of(G, a.B.bases, ver, 4, kv, h), [&](int t, int c, uint32_t x) { put(kv, t, c, x); });
         }
         __syncthreads();
       }
@@ -1522,7 +1653,16 @@ __global__ void __launch_bounds__(kThreads) attn_half_kernel(HalfAttnArgs a) {
                             [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(dst + t * DH + c0) = w; },
                             tl, nt, comp);
       } else if (comp) {  // the whole block decodes (comp is the same for every thread)
-        decode_tile_any(G, a.B, tile, b3, b4, [&](int t, int c, uint32_t x) { dst[t * DH + c] = (uint16_t)x; });
+        if constexpr (FMT != 0) {  // FP8: the element bytes, one per 16-bit LDS entry
+          auto put_tok = [&](int t, int c0, uint32_t w) {
+            for (int i = 0; i < 32 / G.GT; ++i) dst[t * DH + c0 + i] = (uint16_t)((w >> (8 * i)) & 0xFFu);
+          };
+          auto no_col = [](int, int, uint32_t) {};
+          if (G.GT == 8) decode_fp8_tile<FMT, 8>(G, a.B, tile, b3, b4, meta[hf], put_tok, no_col, false, tl, nt, true);
+          else decode_fp8_tile<FMT, 16>(G, a.B, tile, b3, b4, meta[hf], put_tok, no_col, false, tl, nt, true);
+        } else {
+          decode_tile_any(G, a.B, tile, b3, b4, [&](int t, int c, uint32_t x) { dst[t * DH + c] = (uint16_t)x; });
+        }
       }
     };
     if (FMT == 0 && G.GT == 8) {
