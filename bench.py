@@ -62,14 +62,15 @@ def parse():
                     help="comma-separated split counts at which the attention kernel alone is also timed (4, 8 "
                          "and 16 splits are the literal reading of 64-256 blocks per split); '' for none")
     ap.add_argument("--probe", action="store_true", help="also time plain HBM copy / read kernels (torch)")
-    ap.add_argument("--extra", type=str, default="context,fp8,paged,groups,nested,rope,serving,prefill",
+    ap.add_argument("--extra", type=str, default="context,fp8,paged,groups,nested,rope,serving,prefill,d256",
                     help="comma list of extra workloads measured after the headline one: context (the cfg2 "
                          "layer at 32K and 128K tokens), fp8 (the 64K layer in "
                          "FP8 E5M2 and E4M3), paged (32-sequence paged serving mix), prefill (a 4K-token prompt: encode, "
                          "decode_blocks, causal prefill attention), groups (the 64K layer's "
                          "codec with 16- and 8-token exponent groups), rope (escape bytes and raw tiles along "
                          "the 64K layer with RoPE-rotated keys, per calibration policy), serving (sequences "
-                         "admitted and decode throughput under one KV byte budget); '' for none")
+                         "admitted and decode throughput under one KV byte budget), d256 (a 32K-token layer with "
+                         "256-channel heads, compressed and uncompressed decode steps); '' for none")
     ap.add_argument("--extra-steps", type=int, default=48)
     ap.add_argument("--paged-splits", type=int, default=16)
     return ap.parse_args()
@@ -390,6 +391,12 @@ def main():
         result["rope_drift_64k"] = rope_drift(torch, K, synth, cfg, k0, v0, dev)
     if "prefill" in extras:
         result["prefill_4k"] = prefill(torch, K, synth, cfg, k0, v0, dev, stream)
+    if "d256" in extras:
+        import dataclasses
+        c256 = dataclasses.replace(cfg, name="qwen3-8b-like-32k-head-dim-256", D=256, context=(32768,))
+        # 64 splits: the 256-channel kernel's per-workgroup set-up (both half-heads, LDS zeroing,
+        # the query) favours longer splits than the register-rebuild kernel's 256
+        result["head_dim_256_32k"] = extra_steps(torch, K, synth, c256, args, splits=64)
     if "serving" in extras:
         result["equal_memory_serving"] = equal_memory_serving(torch, K, synth, splits=args.paged_splits)
     if not args.no_cpu:
@@ -749,7 +756,7 @@ def extra_steps(torch, K, synth, cfg, args, splits, layers=4):
     q = dev(synth.queries(cfg)) if fmt == synth.BF16 else \
         torch.from_numpy(np.ascontiguousarray(synth.queries(cfg)).view(np.int16)).cuda()
     max_blocks = (max(lens) + per_layer) // T + 2
-    n_tiles = B * max_blocks * 2 * Hkv
+    n_tiles = B * max_blocks * 2 * Hkv * (2 if D == 256 else 1)  # 256-channel heads: two half-head tiles
     ids = list(range(B))
     log(f"[bench] {cfg.name}: building {layers} compressed + {layers} uncompressed layers ({sum(lens)} tokens each)")
 
@@ -772,12 +779,13 @@ def extra_steps(torch, K, synth, cfg, args, splits, layers=4):
         torch.cuda.synchronize()
         if compressed:
             flags, st = caches[0].status()
-            n_grp = T * D // 16
+            Dt = min(D, 128)  # channels of a stored tile (a 256-channel head is two half-head tiles)
+            n_grp = T * Dt // 16
             mb = {synth.BF16: 7, synth.E5M2: 2, synth.E4M3: 3}[fmt]
             eb = 2 if fmt == synth.BF16 else 1
-            payload = (2 * n_grp + 3 * T * D + (1 + mb) * T * D) // 8
-            comp_bytes = st["comp_tiles"] * payload + st["esc_bytes"] + st["raw_tiles"] * T * D * eb
-            res["codec_ratio"] = round((st["comp_tiles"] + st["raw_tiles"]) * T * D * eb / comp_bytes, 4)
+            payload = (2 * n_grp + 3 * T * Dt + (1 + mb) * T * Dt) // 8
+            comp_bytes = st["comp_tiles"] * payload + st["esc_bytes"] + st["raw_tiles"] * T * Dt * eb
+            res["codec_ratio"] = round((st["comp_tiles"] + st["raw_tiles"]) * T * Dt * eb / comp_bytes, 4)
             res["compressed_kv_bytes"] = comp_bytes
         ev = []
         for i in range(warm + steps):

@@ -1102,6 +1102,69 @@ __device__ __forceinline__ uint2 fp8x4_bf16(uint32_t w) {
                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
 }
 
+// BF16 tiles with 16-token groups: one thread per pair of groups (channels c0, c0+1 x 16 tokens,
+// one 32-element CODE unit), the four-token SWAR rebuild of rebuild_group.  put2(t, c0, w)
+// receives BF16 channels c0, c0+1 of token t (low half c0); with by_cols, put_col(t0, c, w)
+// instead receives tokens t0 .. t0+3 of channel c (two per word, the earlier token in the low
+// half).  tl, nt, active: as stage_tile_meta.
+template <class Put2, class PutCol>
+__device__ __forceinline__ void decode_bf16_g16_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
+                                     const uint8_t* b4, TileMeta& m, Put2 put2, PutCol put_col, bool by_cols, int tl,
+                                     int nt, bool active) {
+  const int D = G.D;
+  stage_tile_meta(G, B, tile, m, tl, nt, active);
+  const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(m.esc);
+  const int max_plane = G.esc_cap / 2;
+  const int n_pairs = active ? G.NP : 0;
+  for (int pr = tl; pr < n_pairs; pr += nt) {
+    const int q0 = 2 * pr, w = q0 >> 5, bit = q0 & 31;
+    const uint32_t Ew = m.tag[w], Rw = m.tag[G.PW + w];
+    uint32_t P = planes_before(Ew, Rw, m.pre[w], bit);
+    const uint4 s0 = *reinterpret_cast<const uint4*>(tile + G.sm_off + 32 * pr);
+    const uint4 s1 = *reinterpret_cast<const uint4*>(tile + G.sm_off + 32 * pr + 16);
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(tile + G.code_off + 12 * pr);
+    const uint32_t W0 = cw[0], W1 = cw[1], W2 = cw[2];
+    const int tg = q0 / D, c0 = q0 % D;
+    uint32_t outs[2][2][4];  // [channel][o02 | o13][token quad]
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const uint32_t E = (Ew >> (bit + gi)) & 1u, R = (Rw >> (bit + gi)) & 1u;
+      if (R && !E) atomicOr(&B.counters->status, 8u);
+      const int mode = (int)(E + R);
+      const int c = c0 + gi;
+      const uint32_t base = mode == 0 ? b3[c] : (mode == 1 ? b4[c] : 0u);
+      uint32_t plane0 = 0, X[4] = {0u, 0u, 0u, 0u};
+      if (E && (int)P < max_plane) plane0 = esc16[P];
+      if (R) {
+        for (int qq = 0; qq < 4; ++qq) X[qq] = ((int)P + 1 + qq < max_plane) ? raw_high_nibbles(esc16[P + 1 + qq]) : 0u;
+      }
+      const uint32_t smv[4] = {gi ? s1.x : s0.x, gi ? s1.y : s0.y, gi ? s1.z : s0.z, gi ? s1.w : s0.w};
+      if (gi == 0) rebuild_group<0>(smv, W0, W1, W2, base, plane0, X, outs[0][0], outs[0][1]);
+      else rebuild_group<1>(smv, W0, W1, W2, base, plane0, X, outs[1][0], outs[1][1]);
+      P += E + 4u * R;
+    }
+    if (by_cols) {  // channel c0+gi, tokens 4j..4j+3: the low halves of o02, o13, then the high halves
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          put_col(tg * kGroup + 4 * j, c0 + gi,
+                  make_uint2(perm_b32(outs[gi][1][j], outs[gi][0][j], 0x05040100u),
+                             perm_b32(outs[gi][1][j], outs[gi][0][j], 0x07060302u)));
+      continue;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = tg * kGroup + 4 * j;
+      // (c0, c1) pairs per token
+      put2(t + 0, c0, perm_b32(outs[1][0][j], outs[0][0][j], 0x05040100u));
+      put2(t + 2, c0, perm_b32(outs[1][0][j], outs[0][0][j], 0x07060302u));
+      put2(t + 1, c0, perm_b32(outs[1][1][j], outs[0][1][j], 0x05040100u));
+      put2(t + 3, c0, perm_b32(outs[1][1][j], outs[0][1][j], 0x07060302u));
+    }
+  }
+}
+
 // FP8 tiles (E5M2, E4M3) with 16- or 8-token groups, four tokens per 32-bit word: one thread
 // per CODE unit (32 elements: 32/GT channels x GT tokens, one group per channel).  Each 4-token
 // slot's exponents are base (b3 narrow, b4 wide, 0 raw) + 3-bit code + escape bits (plane bit 3
@@ -1114,7 +1177,7 @@ __device__ __forceinline__ uint2 fp8x4_bf16(uint32_t w) {
 // channel c0 + i); with by_cols, put_col(t0, c, w) instead receives tokens t0 .. t0 + 3 of
 // channel c (byte k: token t0 + k).  tl, nt, active: as stage_tile_meta.
 template <int FMT, int GT, class PutTok, class PutCol>
-__device__ void decode_fp8_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
+__device__ __forceinline__ void decode_fp8_tile(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
                                 const uint8_t* b4, TileMeta& m, PutTok put_tok, PutCol put_col, bool by_cols, int tl,
                                 int nt, bool active) {
   constexpr int F = FMT == 1 ? 5 : 4, MB = 7 - F;
@@ -1227,18 +1290,19 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
                    [&](int t, int c, uint32_t x) { elem_put(outv, out_idx(t, c), 2, x); });
     return;
   }
+  const int row = G.Hkv * D;  // elements between consecutive tokens of the output
   if (G.EB == 2 && G.GT == 8) {
-    uint16_t* o16 = reinterpret_cast<uint16_t*>(outv);
+    uint16_t* o16 = reinterpret_cast<uint16_t*>(outv) + out_idx(0, 0);
     decode_bf16_g8_tile(G, B, tile, b3, b4, meta,
-                        [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(o16 + out_idx(t, c0)) = w; },
+                        [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(o16 + t * row + c0) = w; },
                         tid, kThreads, true);
     return;
   }
   if (G.EB == 1) {  // FP8: the bytes of two (16-token groups) or four (8-token groups) channels per token
-    uint8_t* o8 = reinterpret_cast<uint8_t*>(outv);
+    uint8_t* o8 = reinterpret_cast<uint8_t*>(outv) + out_idx(0, 0);
     auto put_tok = [&](int t, int c0, uint32_t w) {
-      if (G.GT == 8) *reinterpret_cast<uint32_t*>(o8 + out_idx(t, c0)) = w;
-      else *reinterpret_cast<uint16_t*>(o8 + out_idx(t, c0)) = (uint16_t)w;
+      if (G.GT == 8) *reinterpret_cast<uint32_t*>(o8 + t * row + c0) = w;
+      else *reinterpret_cast<uint16_t*>(o8 + t * row + c0) = (uint16_t)w;
     };
     auto no_col = [](int, int, uint32_t) {};
     if (G.fmt == 1) {
@@ -1254,48 +1318,10 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
     decode_tile_any(G, B, tile, b3, b4, [&](int t, int c, uint32_t x) { elem_put(outv, out_idx(t, c), G.EB, x); });
     return;
   }
-  uint16_t* out = reinterpret_cast<uint16_t*>(outv);
-  auto out_at = [&](int t, int c) -> uint16_t* { return out + out_idx(t, c); };
-  stage_tile_meta(G, B, tile, meta, tid, kThreads, true);
-  const uint16_t* esc16 = reinterpret_cast<const uint16_t*>(meta.esc);
-  const int max_plane = G.esc_cap / 2;
-  for (int pr = tid; pr < G.NP; pr += kThreads) {
-    const int q0 = 2 * pr, w = q0 >> 5, bit = q0 & 31;
-    const uint32_t Pw = meta.pre[w];
-    const uint32_t Ew = meta.tag[w], Rw = meta.tag[G.PW + w];
-    uint32_t P = planes_before(Ew, Rw, Pw, bit);
-    const uint4 s0 = *reinterpret_cast<const uint4*>(tile + G.sm_off + 32 * pr);
-    const uint4 s1 = *reinterpret_cast<const uint4*>(tile + G.sm_off + 32 * pr + 16);
-    const uint32_t* cw = reinterpret_cast<const uint32_t*>(tile + G.code_off + 12 * pr);
-    const uint32_t W0 = cw[0], W1 = cw[1], W2 = cw[2];
-    const int tg = q0 / D, c0 = q0 % D;
-    uint32_t outs[2][2][4];
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const uint32_t E = (Ew >> (bit + gi)) & 1u, R = (Rw >> (bit + gi)) & 1u;
-      if (R && !E) atomicOr(&B.counters->status, 8u);
-      const int mode = (int)(E + R);
-      const int c = c0 + gi;
-      const uint32_t base = mode == 0 ? b3[c] : (mode == 1 ? b4[c] : 0u);
-      uint32_t plane0 = 0, X[4] = {0u, 0u, 0u, 0u};
-      if (E && (int)P < max_plane) plane0 = esc16[P];
-      if (R) {
-        for (int qq = 0; qq < 4; ++qq) X[qq] = ((int)P + 1 + qq < max_plane) ? raw_high_nibbles(esc16[P + 1 + qq]) : 0u;
-      }
-      const uint32_t smv[4] = {gi ? s1.x : s0.x, gi ? s1.y : s0.y, gi ? s1.z : s0.z, gi ? s1.w : s0.w};
-      if (gi == 0) rebuild_group<0>(smv, W0, W1, W2, base, plane0, X, outs[0][0], outs[0][1]);
-      else rebuild_group<1>(smv, W0, W1, W2, base, plane0, X, outs[1][0], outs[1][1]);
-      P += E + 4u * R;
-    }
-    for (int j = 0; j < 4; ++j) {
-      const int t = tg * kGroup + 4 * j;
-      // (c0, c1) pairs per token
-      *reinterpret_cast<uint32_t*>(out_at(t + 0, c0)) = perm_b32(outs[1][0][j], outs[0][0][j], 0x05040100u);
-      *reinterpret_cast<uint32_t*>(out_at(t + 2, c0)) = perm_b32(outs[1][0][j], outs[0][0][j], 0x07060302u);
-      *reinterpret_cast<uint32_t*>(out_at(t + 1, c0)) = perm_b32(outs[1][1][j], outs[0][1][j], 0x05040100u);
-      *reinterpret_cast<uint32_t*>(out_at(t + 3, c0)) = perm_b32(outs[1][1][j], outs[0][1][j], 0x07060302u);
-    }
-  }
+  uint16_t* out0 = reinterpret_cast<uint16_t*>(outv) + out_idx(0, 0);
+  decode_bf16_g16_tile(G, B, tile, b3, b4, meta,
+                       [&](int t, int c0, uint32_t w) { *reinterpret_cast<uint32_t*>(out0 + t * row + c0) = w; },
+                       [](int, int, uint2) {}, false, tid, kThreads, true);
 }
 
 
@@ -1580,11 +1606,12 @@ __global__ void __launch_bounds__(kThreads) attn_any_kernel(AnyAttnArgs a) {
 }
 // ------------------------------------------------------------------------------------------
 // Decode attention over 256-channel heads, stored as two 128-channel half-heads (GAAC page App.
-// D): a head's score needs both halves, so one workgroup takes both.  Per block: the two K
-// half-tiles are rebuilt into LDS and scored (fp32 dot products over the 256 channels), the
-// online softmax advances, then the two V half-tiles replace them and accumulate PV.  The last
-// split also attends the tail (the merge kernel then merges splits only).  Any format, group
-// size and tile form (compressed, raw); correct, not tuned.
+// D): a head's score needs both halves, so one workgroup takes both.  Per block the four
+// half-tiles (K and V of both halves) are rebuilt at once, one per wave, into LDS as BF16 (K as
+// rows, V transposed; the SWAR decoders of every format and group size); scores and PV then run
+// on v_mfma_f32_16x16x32_bf16 as in the 8-token-group kernel (query heads as the 16 rows, eight
+// 32-channel K steps over both halves, wave w accumulating channels 64w .. 64w+63).  The last
+// split also attends the tail (the merge kernel then merges splits only).
 struct HalfAttnArgs {
   Geo G;  // the half-head geometry the cache stores (D = 128, Hkv and Hq doubled)
   DevBufs B;
@@ -1599,133 +1626,179 @@ struct HalfAttnArgs {
 template <int FMT>
 __global__ void __launch_bounds__(kThreads) attn_half_kernel(HalfAttnArgs a) {
   constexpr int DH = 128, DR = 256;  // half-head and head channels
+  constexpr int KS = DH + 8;         // K half-tile rows [t][KS], BF16 bits
+  constexpr int VS = 64 + 8;         // V transposed [c][VS] (c over the whole head); P [head][VS]
   const Geo& G = a.G;
   const int T = G.T, g = G.g, S = a.n_splits, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6, col = lane & 15, kq = lane >> 4;
   const int Hq = G.Hq / 2;
   const int split = blockIdx.x, h = blockIdx.y;
   const int4 z = a.zrow[blockIdx.z];
   const int si = z.x, seq = z.y, L = z.z, ntail = z.w;
-  __shared__ __align__(16) uint16_t kvt[2][64 * DH];  // the two half-tiles (K, then V) as element bits, [t][c]
-  __shared__ float qf[kAnyMaxG * DR];
-  __shared__ float pr[kAnyMaxG * 64];
-  __shared__ float mh[kAnyMaxG], lh[kAnyMaxG], al[kAnyMaxG];
-  __shared__ TileMeta meta[2];
+  __shared__ __align__(16) uint16_t kt[2][64 * KS];
+  __shared__ __align__(16) uint16_t vt[DR * VS];
+  __shared__ __align__(16) uint16_t pl[2][16 * VS];  // probabilities, BF16 high part and remainder
+  __shared__ float wmx[4][16], wsm[4][16];            // per wave: maximum and sum of each head's row
+  __shared__ float mh[16], lh[16];                    // running maximum and sum per head (row)
+  __shared__ TileMeta meta[4];
   const int nb = L / T, per = nb / S, rem = nb % S;
   const int b0 = split * per + min(split, rem), b1 = b0 + per + (split < rem ? 1 : 0);
   const int bend = b1 + ((split == S - 1 && ntail > 0) ? 1 : 0);  // block b1 = the tail
-  for (int i = tid; i < g * DR; i += kThreads)
-    qf[i] = __uint_as_float((uint32_t)a.q[((size_t)si * Hq + h * g) * DR + i] << 16);
-  if (tid < g) {
+  // zeros where a 16-token block leaves the MFMA's 32-token K steps short
+  for (int i = tid; i < DR * VS / 8; i += kThreads) reinterpret_cast<uint4*>(vt)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < 2 * 16 * VS / 8; i += kThreads) reinterpret_cast<uint4*>(pl)[i] = make_uint4(0, 0, 0, 0);
+  if (tid < 16) {
     mh[tid] = -INFINITY;
     lh[tid] = 0.0f;
   }
-  constexpr int OPT = kAnyMaxG * DR / kThreads;
-  float acc[OPT];
+  // this lane's query operands: head col (zero past the group), channels 32i + 8kq .. +7
+  uint4 qa[8];
 #pragma unroll
-  for (int u = 0; u < OPT; ++u) acc[u] = 0.0f;
+  for (int i = 0; i < 8; ++i)
+    qa[i] = col < g ? *reinterpret_cast<const uint4*>(a.q + ((size_t)si * Hq + h * g + col) * DR + 32 * i + 8 * kq)
+                    : make_uint4(0, 0, 0, 0);
+  any_f32x4_t o[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) o[u] = any_f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint32_t flags = 0;
   __syncthreads();
-  // the two half-tiles of (K|V) kv of block b into kvt[0], kvt[1] as [t][c] element bits
-  auto fill = [&](int b, int kv) {
+  for (int b = b0; b < bend; ++b) {
     const bool tailblk = b == b1;
-    auto one = [&](int hf, int tl, int nt, bool decode_here) {
-      const int hh = 2 * h + hf;
-      uint16_t* dst = kvt[hf];
+    const int nvalid = tailblk ? ntail : T;
+    // ---- the four half-tiles at once, one per wave: wave w fills (K|V) w >> 1 of half-head w & 1 ----
+    {
+      const int kv = wv >> 1, hf = wv & 1, hh = 2 * h + hf;
       const uint32_t e = tailblk ? 0u : a.B.table[table_index(G, seq, b, kv, hh)];
       const uint32_t slot = entry_slot(e);
       const bool comp = !tailblk && e != kUnallocated && !(e & kRawTile);
       const int ver = comp ? entry_version(e) : 0;
+      uint16_t* krow = kt[hf];
+      uint16_t* vcol = vt + (size_t)DH * hf * VS;
       if (!comp) {  // tail, raw tile (K [t][c], V [c][t]) or missing (zeros, reported)
         const uint8_t* src = nullptr;
         if (tailblk) src = reinterpret_cast<const uint8_t*>(a.B.tail) + tail_offset(G, seq, kv, hh) * G.EB;
         else if (e != kUnallocated) src = reinterpret_cast<const uint8_t*>(a.B.raw_pool) + (size_t)slot * G.raw_elems * G.EB;
         else flags |= 4u;
-        for (int i = tl; i < T * DH; i += nt) {
-          const int t = i / DH, c = i % DH;
-          dst[i] = src ? (uint16_t)elem_at(src, kv ? (size_t)c * T + t : (size_t)i, G.EB) : (uint16_t)0;
+        // 8-element pieces in the stored orientation, which is the LDS one (K rows, V columns);
+        // tokens at or past nvalid (a tail's unused columns) are zeros
+        const int per_line = kv ? T / 8 : DH / 8;
+        for (int p = lane; p < T * DH / 8; p += 64) {
+          const int r = p / per_line, x0 = 8 * (p % per_line);  // K: token r, channels x0..; V: channel r, tokens x0..
+          uint4 v8 = make_uint4(0, 0, 0, 0);
+          if (src) {
+            const size_t off = (size_t)r * (kv ? T : DH) + x0;
+            if constexpr (FMT == 0) {
+              v8 = *reinterpret_cast<const uint4*>(src + 2 * off);
+            } else {
+              const uint2 b8 = *reinterpret_cast<const uint2*>(src + off);
+              const uint2 lo = fp8x4_bf16<FMT>(b8.x), hi = fp8x4_bf16<FMT>(b8.y);
+              v8 = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+          }
+          uint32_t wds[4] = {v8.x, v8.y, v8.z, v8.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {  // invalid tokens: a whole K row, or single V column entries
+            const int t_lo = kv ? x0 + 2 * k : r, t_hi = kv ? x0 + 2 * k + 1 : r;
+            if (t_lo >= nvalid) wds[k] &= 0xFFFF0000u;
+            if (t_hi >= nvalid) wds[k] &= 0x0000FFFFu;
+          }
+          v8 = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+          if (kv) *reinterpret_cast<uint4*>(vcol + r * VS + x0) = v8;
+          else *reinterpret_cast<uint4*>(krow + r * KS + x0) = v8;
         }
       }
       const uint8_t* b3 = bases_of(G, a.B.bases, ver, 3, kv, hh);
       const uint8_t* b4 = bases_of(G, a.B.bases, ver, 4, kv, hh);
       const uint8_t* tile = a.B.comp_pool + (comp ? (size_t)slot * G.stride : 0);
-      if (decode_here) {  // BF16, 8-token groups: every thread reaches the decoder's barriers
-        decode_bf16_g8_tile(G, a.B, tile, b3, b4, meta[hf],
-                            [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(dst + t * DH + c0) = w; },
-                            tl, nt, comp);
-      } else if (comp) {  // the whole block decodes (comp is the same for every thread)
-        if constexpr (FMT != 0) {  // FP8: the element bytes, one per 16-bit LDS entry
-          auto put_tok = [&](int t, int c0, uint32_t w) {
-            for (int i = 0; i < 32 / G.GT; ++i) dst[t * DH + c0 + i] = (uint16_t)((w >> (8 * i)) & 0xFFu);
-          };
-          auto no_col = [](int, int, uint32_t) {};
-          if (G.GT == 8) decode_fp8_tile<FMT, 8>(G, a.B, tile, b3, b4, meta[hf], put_tok, no_col, false, tl, nt, true);
-          else decode_fp8_tile<FMT, 16>(G, a.B, tile, b3, b4, meta[hf], put_tok, no_col, false, tl, nt, true);
-        } else {
-          decode_tile_any(G, a.B, tile, b3, b4, [&](int t, int c, uint32_t x) { dst[t * DH + c] = (uint16_t)x; });
-        }
-      }
-    };
-    if (FMT == 0 && G.GT == 8) {
-      one(tid >> 7, tid & 127, kThreads / 2, true);  // the two half-tiles at once, one per thread half
-    } else {
-      for (int hf = 0; hf < 2; ++hf) {
-        one(hf, tid, kThreads, false);
-        __syncthreads();
+      // every thread reaches its decoder's barriers (active only for a compressed tile)
+      if constexpr (FMT == 0) {
+        if (G.GT == 8)
+          decode_bf16_g8_tile(G, a.B, tile, b3, b4, meta[wv],
+                              [&](int t, int c0, uint2 w) { *reinterpret_cast<uint2*>(krow + t * KS + c0) = w; },
+                              [&](int tg, int c, uint4 w) { *reinterpret_cast<uint4*>(vcol + c * VS + 8 * tg) = w; },
+                              kv == 1, lane, 64, comp);
+        else
+          decode_bf16_g16_tile(G, a.B, tile, b3, b4, meta[wv],
+                               [&](int t, int c0, uint32_t w) { *reinterpret_cast<uint32_t*>(krow + t * KS + c0) = w; },
+                               [&](int t0, int c, uint2 w) { *reinterpret_cast<uint2*>(vcol + c * VS + t0) = w; },
+                               kv == 1, lane, 64, comp);
+      } else {
+        auto put_tok = [&](int t, int c0, uint32_t w) {
+          if (G.GT == 8) *reinterpret_cast<uint2*>(krow + t * KS + c0) = fp8x4_bf16<FMT>(w);
+          else *reinterpret_cast<uint32_t*>(krow + t * KS + c0) = fp8x4_bf16<FMT>(w).x;
+        };
+        auto put_col = [&](int t0, int c, uint32_t w) { *reinterpret_cast<uint2*>(vcol + c * VS + t0) = fp8x4_bf16<FMT>(w); };
+        if (G.GT == 8) decode_fp8_tile<FMT, 8>(G, a.B, tile, b3, b4, meta[wv], put_tok, put_col, kv == 1, lane, 64, comp);
+        else decode_fp8_tile<FMT, 16>(G, a.B, tile, b3, b4, meta[wv], put_tok, put_col, kv == 1, lane, 64, comp);
       }
     }
     __syncthreads();
-  };
-  for (int b = b0; b < bend; ++b) {
-    const int nvalid = b == b1 ? ntail : T;
-    fill(b, 0);
-    for (int p0 = 0; p0 < g * T; p0 += kThreads) {
-      const int p = p0 + tid;
-      const bool on = p < g * T;
-      const int hh = on ? p / T : 0, t = p % T;
-      float d = 0.0f;
-      if (on && t < nvalid) {
-        const float* qr = qf + hh * DR;
-        for (int cc = 0; cc < DR; cc += 2) {
-          const int c = (cc + 2 * t) & (DR - 1);
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(kvt[c >> 7] + t * DH + (c & (DH - 1)));
-          d += elem_value<FMT>(w & 0xFFFFu) * qr[c] + elem_value<FMT>(w >> 16) * qr[c + 1];
-        }
+    // ---- scores: wave w takes tokens 16w .. 16w+15 over the 256 channels of both halves ----
+    float sc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (16 * wv < T) {
+      any_f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc = any_mfma(qa[i], *reinterpret_cast<const uint4*>(kt[i >> 2] + (16 * wv + col) * KS + 32 * (i & 3) + 8 * kq), acc);
+      const bool tok_ok = 16 * wv + col < nvalid;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[r] = tok_ok ? acc[r] * a.sl2 : -INFINITY;
+        const float mx = row16_max(sc[r]);
+        if (col == 0) wmx[wv][4 * kq + r] = mx;
       }
-      const float sc = t < nvalid ? d * a.sl2 : -INFINITY;
-      const float m_old = on ? mh[hh] : 0.0f;
-      const float m_new = fmaxf(m_old, seg_max(sc, T));
+    }
+    __syncthreads();
+    // ---- the block's maximum per head, probabilities, rescale factors ----
+    float alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hd = 4 * kq + r;
+      float mb = wmx[0][hd];
+      for (int w = 1; w < T / 16; ++w) mb = fmaxf(mb, wmx[w][hd]);
+      const float m_old = mh[hd], m_new = fmaxf(m_old, mb);
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float pv = exp2f(sc - m_use);
-      const float sum = seg_sum(pv, T);
-      if (on) {
-        pr[hh * 64 + t] = pv;
-        if (t == 0) {
-          const float alpha = exp2f(m_old - m_use);
-          lh[hh] = lh[hh] * alpha + sum;
-          mh[hh] = m_new;
-          al[hh] = alpha;
-        }
+      alpha[r] = exp2f(m_old - m_use);
+      if (16 * wv < T) {
+        const float p = exp2f(sc[r] - m_use);
+        const float hi = (float)(__bf16)p;
+        pl[0][hd * VS + 16 * wv + col] = __builtin_bit_cast(uint16_t, (__bf16)p);
+        pl[1][hd * VS + 16 * wv + col] = __builtin_bit_cast(uint16_t, (__bf16)(p - hi));
+        const float sm = row16_sum(p);
+        if (col == 0) wsm[wv][hd] = sm;
       }
     }
-    __syncthreads();  // scores done with K: the V half-tiles may replace it
-    fill(b, 1);
+    __syncthreads();
+    // ---- PV: wave w accumulates channels 64w .. 64w+63 (four 16-channel tiles) ----
 #pragma unroll
-    for (int u = 0; u < OPT; ++u) {
-      const int o = tid + kThreads * u;
-      if (o < g * DR) {
-        const int hh = o / DR, c = o % DR;
-        const uint16_t* vc = kvt[c >> 7] + (c & (DH - 1));
-        float s = acc[u] * al[hh];
-        for (int t = 0; t < nvalid; ++t) s += pr[hh * 64 + t] * elem_value<FMT>(vc[t * DH]);
-        acc[u] = s;
+    for (int u = 0; u < 4; ++u) {
+      const int ct = 4 * wv + u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[u][r] *= alpha[r];
+      for (int j = 0; 32 * j < T; ++j) {
+        const uint4 vb = *reinterpret_cast<const uint4*>(vt + (16 * ct + col) * VS + 32 * j + 8 * kq);
+        o[u] = any_mfma(*reinterpret_cast<const uint4*>(pl[0] + col * VS + 32 * j + 8 * kq), vb, o[u]);
+        o[u] = any_mfma(*reinterpret_cast<const uint4*>(pl[1] + col * VS + 32 * j + 8 * kq), vb, o[u]);
       }
     }
-    __syncthreads();  // before the next block overwrites the tiles and the probabilities
+    if (tid < 16) {  // the running maximum and sum of head (row) tid, as every lane rescaled above
+      float mb = wmx[0][tid], sum = wsm[0][tid];
+      for (int w = 1; w < T / 16; ++w) mb = fmaxf(mb, wmx[w][tid]), sum += wsm[w][tid];
+      const float m_old = mh[tid], m_new = fmaxf(m_old, mb);
+      lh[tid] = lh[tid] * exp2f(m_old - (m_new == -INFINITY ? 0.0f : m_new)) + sum;
+      mh[tid] = m_new;
+    }
+    __syncthreads();  // before the next block overwrites the tiles, the probabilities and the state
   }
+  // ---- partial results: heads 4kq+r, channels 16ct + col ----
 #pragma unroll
-  for (int u = 0; u < OPT; ++u) {
-    const int o = tid + kThreads * u;
-    if (o < g * DR) a.ws_acc[(((size_t)si * Hq + h * g + o / DR) * S + split) * DR + o % DR] = acc[u];
+  for (int u = 0; u < 4; ++u) {
+    const int ct = 4 * wv + u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hd = 4 * kq + r;
+      if (hd < g) a.ws_acc[(((size_t)si * Hq + h * g + hd) * S + split) * DR + 16 * ct + col] = o[u][r];
+    }
   }
   if (tid < g) {
     float* ml = a.ws_ml + (((size_t)si * Hq + h * g + tid) * S + split) * 2;
