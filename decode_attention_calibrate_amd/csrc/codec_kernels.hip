@@ -825,70 +825,6 @@ __global__ void release_kernel(Geo G, DevBufs B, int seq, int n_blocks) {
   }
 }
 
-// Any format and group size, one element at a time: every group's mode and first escape unit go
-// to LDS (a block scan of the unit counts), then each thread rebuilds elements from their 3-bit
-// code, escape bits and sign/mantissa field and hands element (t, c) to put(t, c, bits).  (BF16
-// tiles with 16-token groups take the SWAR path below.)  The caller synchronises before the
-// next call or before reading what put wrote to LDS.
-template <class Put>
-__device__ void decode_tile_any(const Geo& G, const DevBufs& B, const uint8_t* tile, const uint8_t* b3,
-                                const uint8_t* b4, Put put) {
-  __shared__ uint16_t gP[1024];
-  __shared__ uint8_t gm[1024];
-  __shared__ int red[8];
-  const int tid = threadIdx.x, D = G.D;
-  const uint32_t* tagE = reinterpret_cast<const uint32_t*>(tile + G.tag_off);
-  const uint32_t* tagR = tagE + G.PW;
-  const int per = (G.NG + kThreads - 1) / kThreads, q0 = tid * per;
-  int cnt = 0;
-  for (int q = q0; q < min(G.NG, q0 + per); ++q) {
-    const uint32_t E = (tagE[q >> 5] >> (q & 31)) & 1u, R = (tagR[q >> 5] >> (q & 31)) & 1u;
-    const int mode = (int)(E + R);
-    if ((R && !E) || (mode == 1 && G.F <= 4)) atomicOr(&B.counters->status, 8u);
-    gm[q] = (uint8_t)mode;
-    cnt += mode_planes(G, mode);
-  }
-  int total;
-  int P = block_exclusive_scan(cnt, red, &total);
-  if (tid == 0 && (long)total * G.GT > 8L * G.esc_cap) atomicOr(&B.counters->status, 8u);  // escape overrun
-  for (int q = q0; q < min(G.NG, q0 + per); ++q) {
-    gP[q] = (uint16_t)P;
-    P += mode_planes(G, gm[q]);
-  }
-  __syncthreads();
-  const uint8_t* code = tile + G.code_off;
-  const uint8_t* sm = tile + G.sm_off;
-  const uint8_t* esc = tile + G.esc_off;
-  const int max_bit = 8 * G.esc_cap;
-  auto bit = [](const uint8_t* buf, int b) -> uint32_t { return (buf[b >> 3] >> (b & 7)) & 1u; };
-  auto ebit = [&](int b) -> uint32_t { return b < max_bit ? bit(esc, b) : 0u; };
-  for (int i = tid; i < G.raw_elems; i += kThreads) {
-    const int t = i / D, c = i % D, tg = t / G.GT, tau = t % G.GT;
-    const int q = tg * D + c, n = q * G.GT + tau;
-    const int mode = gm[q];
-    const int Pq = gP[q];
-    // 3-bit fields in the 32-element unit layout: element r of unit u in byte lane r%4, slot r/4
-    const int u = n >> 5, r = n & 31, lk = r & 3, sl = r >> 2;
-    uint32_t o = 0, f = 0;
-    for (int bb = 0; bb < 3; ++bb) {
-      const int x = 3 * sl + bb, byte = 12 * u + 4 * (x >> 3) + lk;
-      o |= ((code[byte] >> (x & 7)) & 1u) << bb;
-      if (G.MB == 2) f |= ((sm[byte] >> (x & 7)) & 1u) << bb;
-    }
-    if (G.MB == 3) f = (sm[n >> 1] >> (4 * (n & 1))) & 0xFu;
-    if (G.MB == 7) f = sm[n];
-    if (mode >= 1) o |= ebit(Pq * G.GT + tau) << 3;
-    if (mode == 2 && G.F == 5) o |= ebit((Pq + 1) * G.GT + tau) << 4;
-    if (mode == 2 && G.F == 8)
-      for (int bb = 0; bb < 4; ++bb) o |= ebit((Pq + 1) * G.GT + 4 * tau + bb) << (4 + bb);
-    const uint32_t base = mode == 0 ? b3[c] : (mode == 1 ? b4[c] : 0u);
-    if (base + o >= (1u << G.F)) atomicOr(&B.counters->status, 8u);  // corrupt offset
-    const uint32_t e = (base + o) & ((1u << G.F) - 1u);
-    const uint32_t x = ((f >> G.MB) << (G.F + G.MB)) | (e << G.MB) | (f & ((1u << G.MB) - 1u));
-    put(t, c, x);
-  }
-}
-
 // FORMAT v2 tile (BF16), one element at a time: every group's mode index from the two tag
 // planes and, by a block scan of their code bits, its offset in the CODES stream (in LDS); then
 // each thread rebuilds elements from their w-bit code and sign/mantissa byte and hands element
@@ -1312,10 +1248,6 @@ __global__ void __launch_bounds__(kThreads) decode_blocks_kernel(Geo G, DevBufs 
       if (G.GT == 8) decode_fp8_tile<2, 8>(G, B, tile, b3, b4, meta, put_tok, no_col, false, tid, kThreads, true);
       else decode_fp8_tile<2, 16>(G, B, tile, b3, b4, meta, put_tok, no_col, false, tid, kThreads, true);
     }
-    return;
-  }
-  if (G.GT != kGroup) {
-    decode_tile_any(G, B, tile, b3, b4, [&](int t, int c, uint32_t x) { elem_put(outv, out_idx(t, c), G.EB, x); });
     return;
   }
   uint16_t* out0 = reinterpret_cast<uint16_t*>(outv) + out_idx(0, 0);
