@@ -1841,7 +1841,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
 
   // The fill: threads 0..127 carry K pieces (piece p = tid + 128u: token p / C8, channels
   // 8 (p % C8) ..), threads 128..255 an 8-token x 8-channel block of V each, transposed in
-  // registers so that one 16-byte store writes 8 tokens of one channel.  The 16 lanes of each
+  // registers so that two 8-byte stores write 8 tokens of one channel (in each 32-token chunk
+  // the tokens sit in the order of the PV operand, see below).  The 16 lanes of each
   // V store phase cover 8 token octets x 2 channel parities (4 x 4 for 32-key blocks), which
   // puts their rows in distinct bank groups.  A block's pieces load into registers while the
   // previous block is being attended.
@@ -1898,7 +1899,12 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
         const int w = k >> 1;
         const uint4 y = make_uint4(perm_b32(x[1][w], x[0][w], sel), perm_b32(x[3][w], x[2][w], sel),
                                    perm_b32(x[5][w], x[4][w], sel), perm_b32(x[7][w], x[6][w], sel));
-        *reinterpret_cast<uint4*>(vtl + (8 * vc8 + k) * VS + 8 * vj) = y;
+        // tokens in each 32-token chunk stored in the order the PV operand reads them: position
+        // 8kq + j holds token 4kq + j (j < 4), then token 16 + 4kq + j - 4; quad q = 2 (vj % 4)
+        const int qa = 2 * (vj & 3), cb = 32 * (vj >> 2);
+        const int pa = cb + (qa < 4 ? 8 * qa : 8 * (qa - 4) + 4), pb = cb + (qa + 1 < 4 ? 8 * (qa + 1) : 8 * (qa - 3) + 4);
+        *reinterpret_cast<uint2*>(vtl + (8 * vc8 + k) * VS + pa) = make_uint2(y.x, y.y);
+        *reinterpret_cast<uint2*>(vtl + (8 * vc8 + k) * VS + pb) = make_uint2(y.z, y.w);
       }
     }
   };
@@ -1976,7 +1982,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
       // O^T += V^T P^T over 32-key chunks (sub-blocks 2kc, 2kc+1).  Inside a chunk the MFMA's
       // k slots 8kq+j and 8kq+4+j stand for keys 16(2kc)+4kq+j and 16(2kc+1)+4kq+j, so each
       // lane's own probabilities are its P^T operand (as a BF16 high part plus remainder) and
-      // the V^T operand reads the same keys: two 8-byte pieces of a channel row.
+      // the V^T operand reads the same keys, which the fill stored in that order: one 16-byte
+      // piece of a channel row.
       for (int kc = 0; kc < KB / 32; ++kc) {
         uint32_t hi[4], lo[4];
 #pragma unroll
@@ -1989,9 +1996,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
           if (16 * s < D) {
-            const uint16_t* vr = vtl + (16 * s + col) * VS + 32 * kc + 4 * kq;
-            const uint2 v0 = *reinterpret_cast<const uint2*>(vr), v1 = *reinterpret_cast<const uint2*>(vr + 16);
-            const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
+            const uint4 va = *reinterpret_cast<const uint4*>(vtl + (16 * s + col) * VS + 32 * kc + 8 * kq);
             o[s] = mfma_bf16(va, ph, o[s]);
             o[s] = mfma_bf16(va, plo, o[s]);
           }
