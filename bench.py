@@ -62,10 +62,10 @@ def parse():
                     help="comma-separated split counts at which the attention kernel alone is also timed (4, 8 "
                          "and 16 splits are the literal reading of 64-256 blocks per split); '' for none")
     ap.add_argument("--probe", action="store_true", help="also time plain HBM copy / read kernels (torch)")
-    ap.add_argument("--extra", type=str, default="context,fp8,paged,groups,nested,rope,serving,prefill,d256",
+    ap.add_argument("--extra", type=str, default="context,fp8,g8,paged,groups,nested,rope,serving,prefill,d256",
                     help="comma list of extra workloads measured after the headline one: context (the cfg2 "
                          "layer at 32K and 128K tokens), fp8 (the 64K layer in "
-                         "FP8 E5M2 and E4M3), paged (32-sequence paged serving mix), prefill (a 4K-token prompt: encode, "
+                         "FP8 E5M2 and E4M3), g8 (the 64K layer with 8-token exponent groups), paged (32-sequence paged serving mix), prefill (a 4K-token prompt: encode, "
                          "decode_blocks, causal prefill attention), groups (the 64K layer's "
                          "codec with 16- and 8-token exponent groups), rope (escape bytes and raw tiles along "
                          "the 64K layer with RoPE-rotated keys, per calibration policy), serving (sequences "
@@ -381,6 +381,10 @@ def main():
     if "fp8" in extras:
         result["fp8_64k"] = {name: extra_steps(torch, K, synth, synth.config(4, fmt), args, splits=S)
                              for name, fmt in (("e5m2", synth.E5M2), ("e4m3", synth.E4M3))}
+    if "g8" in extras:
+        import dataclasses
+        result["g8_64k"] = extra_steps(torch, K, synth, dataclasses.replace(cfg, G=8, name="qwen3-8b-like-64k-g8"),
+                                       args, splits=S)
     if "paged" in extras:
         result["paged_mix"] = extra_steps(torch, K, synth, synth.config(3), args, splits=args.paged_splits, layers=2)
     if "groups" in extras:
@@ -410,9 +414,8 @@ def codec_groups(torch, K, cfg, kd, vd, k0, v0, dev, stream, q, n_splits, reps=5
     blocks; decoding every block back to BF16 (kv_decode_blocks) and a single block; decode
     attention over the layer (kv_attention_partials, back to back on the one layer, so its
     bytes sit in the last-level cache: "hot").  Encoders: 16-token groups the register-packing
-    kernel, 8-token groups the bit-assembling one; decoders: 16-token groups the four-token SWAR
-    kernel, 8-token groups the element-wise one; attention: 16-token groups the register-rebuild
-    split kernel, 8-token groups the LDS-rebuild one."""
+    kernel, 8-token groups the bit-assembling one; decoders: the four-token SWAR decoders;
+    attention: the register-rebuild split kernels (one for each group size)."""
     T, D, Hkv, Hq = cfg.T, cfg.D, cfg.Hkv, cfg.Hq
     L0 = kd.shape[1]
     nb = L0 // T
@@ -763,7 +766,8 @@ def extra_steps(torch, K, synth, cfg, args, splits, layers=4):
     def make(compressed):
         c = K.KVCache(num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D, block_tokens=T, max_seqs=B,
                       max_blocks_per_seq=max_blocks, num_comp_slots=n_tiles if compressed else 0,
-                      num_raw_slots=1024 if compressed else n_tiles, compressed=compressed, perm_seed=11, dtype=fmt)
+                      num_raw_slots=1024 if compressed else n_tiles, compressed=compressed, perm_seed=11, dtype=fmt,
+                      group_tokens=cfg.G)
         c.calibrate(dev(pool_k[:cfg.n_cal]), dev(pool_v[:cfg.n_cal]))
         for sid, L in enumerate(lens):
             c.append([sid], dev(pool_k[None, :L]), dev(pool_v[None, :L]))
@@ -780,7 +784,7 @@ def extra_steps(torch, K, synth, cfg, args, splits, layers=4):
         if compressed:
             flags, st = caches[0].status()
             Dt = min(D, 128)  # channels of a stored tile (a 256-channel head is two half-head tiles)
-            n_grp = T * Dt // 16
+            n_grp = T * Dt // cfg.G
             mb = {synth.BF16: 7, synth.E5M2: 2, synth.E4M3: 3}[fmt]
             eb = 2 if fmt == synth.BF16 else 1
             payload = (2 * n_grp + 3 * T * Dt + (1 + mb) * T * Dt) // 8

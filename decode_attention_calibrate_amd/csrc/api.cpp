@@ -420,10 +420,11 @@ static int run_partials(kvc_cache* c, const int32_t* seq_ids_host, int32_t n_seq
       if (rc != KVC_OK) return rc;
       continue;
     }
-    // compressed caches with 8-token groups or in FORMAT v2 take the LDS-rebuild kernel;
-    // everything else the register-rebuild split kernels
-    auto launch = (G.compressed && (G.GT != kvc::kGroup || G.mode_set != 0)) ? kvc::launch_attention_any
-                                                                               : kvc::launch_attention_partials;
+    // compressed caches in FORMAT v2, or with 8-token groups in blocks other than 64 tokens, take
+    // the LDS-rebuild kernel; everything else the register-rebuild split kernels
+    auto launch = (G.compressed && (G.mode_set != 0 || (G.GT != kvc::kGroup && G.T != 64)))
+                      ? kvc::launch_attention_any
+                      : kvc::launch_attention_partials;
     rc = hip_fail(launch(G, c->B, S, (const uint16_t*)q_dev + (size_t)s0 * G.Hq * G.D, scale, n_splits,
                          acc + (size_t)s0 * G.Hq * n_splits * G.D, ml + (size_t)s0 * hq * n_splits * 2,
                          k_new_dev ? (const uint8_t*)k_new_dev + (size_t)s0 * row : nullptr,

@@ -818,6 +818,516 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 }
 
 // ------------------------------------------------------------------------------------------
+// Compressed caches with 8-token groups (FORMAT v1, 64-token blocks): the same split-K structure,
+// phase pipelining and rebuild-in-registers as attn_comp_kernel, with a lane layout made for
+// 8-token groups.  A CODE unit of an 8-token-group tile is 4 consecutive channels x the 8 tokens
+// of one token group (one group per channel), so each lane rebuilds whole units, four tokens per
+// 32-bit word:
+//   V    : lane n + 16j takes, for each 32-token half h of the block and each 64-channel slice r,
+//          the unit of token group 4h + j and channels 64r + 4n .. 64r + 4n + 3.  Its four
+//          channels' 8 tokens are PV B operands as rebuilt: MFMA column n of accumulator (r, m)
+//          is channel 64r + 4n + m, and k-group j of half h is tokens 32h + 8j .. 32h + 8j + 7.
+//   K    : lane n + 16j takes token group 2s + (j >> 1), slice j & 1 (one slice: 4s + j) for its
+//          unit s, so the 32 lanes of one LDS store pass cover both halves of a row's banks.
+//          Token t = 32h + 8j' + u is stored in LDS row 16j' + 8h + u: the QK A-operand reads
+//          (unchanged from attn_comp_kernel) then leave lane n + 16j with the scores of head n for
+//          tokens 32h + 8j + u in s[8h + u] -- exactly its P operand for half h.
+//   Escapes are bytes: a wide group one 8-bit plane, a raw group one more (E5M2) or four more
+//          bytes of 4-bit fields (BF16); tag words and the escape prefix of every word are shared
+//          across the wave by lane shuffles, as in attn_comp_kernel.
+template <int NH, int FMT>
+struct TG8 {
+  static constexpr int D = 64 * NH;
+  static constexpr int PW = D / 4;   // tag words per plane: 8 token groups x D groups / 32
+  static constexpr int US = 2 * NH;  // CODE units a lane holds per tile
+  static constexpr int CODE_OFF = (8 * PW + 15) / 16 * 16;
+  static constexpr int SM_OFF = CODE_OFF + 24 * D;  // 64 x D codes of 3 bits
+  static constexpr int ESC_OFF = SM_OFF + 64 * D * (1 + FmtT<FMT>::MB) / 8;
+  static constexpr int SMB = 32 * (1 + FmtT<FMT>::MB) / 8;  // sign/mantissa bytes of one unit
+  static constexpr int SMW = SMB / 4;
+};
+
+// LDS row of token t of a 64-token block (see above).
+__device__ __forceinline__ int g8_krow(int t) { return 16 * ((t >> 3) & 3) + 8 * (t >> 5) + (t & 7); }
+
+// Token group and 64-channel slice of a lane's unit s: K or V assignment (above).
+template <int NH, bool ISK>
+__device__ __forceinline__ void g8_unit(int s, int j, int& tg, int& r) {
+  if constexpr (ISK) {
+    if constexpr (NH == 2) { tg = 2 * s + (j >> 1); r = j & 1; }
+    else { tg = 4 * s + j; r = 0; }
+  } else {
+    tg = 4 * (s / NH) + j;
+    r = s % NH;
+  }
+}
+
+// Compressed bytes of one tile held by one lane: tag words `lane` of both planes (lanes < PW),
+// escape piece `lane` (lanes below the staged pieces), and the code and sign/mantissa words of
+// its units.
+template <int NH, int FMT>
+struct C8Regs {
+  uint32_t tE, tR;
+  uint4 esc;
+  uint32_t sm[TG8<NH, FMT>::US][TG8<NH, FMT>::SMW];
+  uint32_t cd[TG8<NH, FMT>::US][3];
+};
+
+template <int NH, int FMT, bool ISK>
+__device__ __forceinline__ void g8_load_tile(const TileRef& rf, int lane, C8Regs<NH, FMT>& c) {
+  using Q = TG8<NH, FMT>;
+  const uint8_t* t = rf.p;  // a raw or dummy tile is large enough for every load below
+  const int n = lane & 15, j = lane >> 4;
+  c.tE = c.tR = 0;
+  if (lane < Q::PW) {
+    c.tE = ld32(t + 4 * lane);
+    c.tR = ld32(t + 4 * (Q::PW + lane));
+  }
+  c.esc = make_uint4(0, 0, 0, 0);
+  if (lane < rf.escu) c.esc = ld128(t + Q::ESC_OFF + 16 * lane);
+#pragma unroll
+  for (int s = 0; s < Q::US; ++s) {
+    int tg, r;
+    g8_unit<NH, ISK>(s, j, tg, r);
+    const int u = tg * (Q::D / 4) + 16 * r + n;
+    const uint8_t* sp = t + Q::SM_OFF + Q::SMB * u;
+    if constexpr (Q::SMW == 8) {
+      const uint4 a = ld128(sp), b = ld128(sp + 16);
+      c.sm[s][0] = a.x; c.sm[s][1] = a.y; c.sm[s][2] = a.z; c.sm[s][3] = a.w;
+      c.sm[s][4] = b.x; c.sm[s][5] = b.y; c.sm[s][6] = b.z; c.sm[s][7] = b.w;
+    } else if constexpr (Q::SMW == 4) {
+      const uint4 a = ld128(sp);
+      c.sm[s][0] = a.x; c.sm[s][1] = a.y; c.sm[s][2] = a.z; c.sm[s][3] = a.w;
+    } else {
+      c.sm[s][0] = ld32(sp); c.sm[s][1] = ld32(sp + 4); c.sm[s][2] = ld32(sp + 8);
+    }
+    const uint8_t* cp = t + Q::CODE_OFF + 12 * u;
+    c.cd[s][0] = ld32(cp);
+    c.cd[s][1] = ld32(cp + 4);
+    c.cd[s][2] = ld32(cp + 8);
+  }
+}
+
+// Stage the tile's escape pieces into LDS; return the escape bytes before tag word `lane`
+// (lanes < PW).  A word whose groups would end past the staged bytes (corrupt tags) is flagged
+// and cleared, as in stage_escape.
+template <int NH, int FMT>
+__device__ __forceinline__ uint32_t g8_stage_escape(C8Regs<NH, FMT>& c, const TileRef& rf, int lane, uint8_t* esc_lds,
+                                                    uint32_t& bad) {
+  if (rf.src() == SRC_COMP && lane < rf.escu) *reinterpret_cast<uint4*>(esc_lds + 16 * lane) = c.esc;
+  const uint32_t cnt = __popc(c.tE) + (uint32_t)(FmtT<FMT>::F - 4) * __popc(c.tR);  // wide 1 byte, raw F - 3
+  uint32_t incl = row_scan16(cnt);
+  if constexpr (TG8<NH, FMT>::PW > 16)
+    incl += lane >= 16 ? (uint32_t)__builtin_amdgcn_readlane((int)incl, 15) : 0u;
+  if (rf.src() == SRC_COMP && incl > 16u * (uint32_t)rf.escu) {
+    bad |= 1u;
+    c.tE = c.tR = 0u;
+    return 0u;
+  }
+  return incl - cnt;
+}
+
+// Codes of slot S (a value the unrolled loops make constant) of a CODE unit.
+template <int XS>
+__device__ __forceinline__ uint32_t code_slot_of(int S, uint32_t W0, uint32_t W1, uint32_t W2) {
+  switch (S) {
+    case 0: return code_slot<0, XS>(W0, W1, W2);
+    case 1: return code_slot<1, XS>(W0, W1, W2);
+    case 2: return code_slot<2, XS>(W0, W1, W2);
+    case 3: return code_slot<3, XS>(W0, W1, W2);
+    case 4: return code_slot<4, XS>(W0, W1, W2);
+    case 5: return code_slot<5, XS>(W0, W1, W2);
+    case 6: return code_slot<6, XS>(W0, W1, W2);
+    default: return code_slot<7, XS>(W0, W1, W2);
+  }
+}
+__device__ __forceinline__ uint32_t e5m2_sign_mant_of(int S, uint32_t W0, uint32_t W1, uint32_t W2) {
+  switch (S) {
+    case 0: return e5m2_sign_mant<0>(W0, W1, W2);
+    case 1: return e5m2_sign_mant<1>(W0, W1, W2);
+    case 2: return e5m2_sign_mant<2>(W0, W1, W2);
+    case 3: return e5m2_sign_mant<3>(W0, W1, W2);
+    case 4: return e5m2_sign_mant<4>(W0, W1, W2);
+    case 5: return e5m2_sign_mant<5>(W0, W1, W2);
+    case 6: return e5m2_sign_mant<6>(W0, W1, W2);
+    default: return e5m2_sign_mant<7>(W0, W1, W2);
+  }
+}
+
+// The E and R words holding unit s of the lane and the escape bytes before them (cross-lane reads).
+template <int NH, int FMT, bool ISK>
+__device__ __forceinline__ void g8_fetch_tags(const C8Regs<NH, FMT>& c, int s, int j, int n, uint32_t pfx, uint32_t tw[3]) {
+  int tg, r;
+  g8_unit<NH, ISK>(s, j, tg, r);
+  const int w = tg * (TG8<NH, FMT>::D / 32) + 2 * r + (n >> 3);  // unit tg * D/4 + 16r + n, 8 units a word
+  tw[0] = (uint32_t)__shfl((int)c.tE, w);
+  tw[1] = (uint32_t)__shfl((int)c.tR, w);
+  tw[2] = (uint32_t)__shfl((int)pfx, w);
+}
+
+// Element words of quad qq of group gi of unit s from its rebuilt exponents Ev (four byte lanes) and
+// its stored sign/mantissa fields (layout of g8_rebuild_unit's output).
+template <int NH, int FMT>
+__device__ __forceinline__ void g8_assemble(const C8Regs<NH, FMT>& c, int s, int gi, int qq, uint32_t Ev,
+                                            uint32_t o[4][2][2]) {
+  const int slot = 2 * gi + qq;
+  if constexpr (FMT == 0) {
+    const uint32_t sv = c.sm[s][slot];
+    o[gi][0][qq] = bitsel(0x7F807F80u, Ev << 7, perm_b32(sv, sv, 0x02020000u));
+    o[gi][1][qq] = bitsel(0x7F807F80u, Ev >> 1, perm_b32(sv, sv, 0x03030101u));
+  } else {
+    uint32_t g;  // sign at bit 7, mantissa at bits 0..MB-1 of each byte lane
+    if constexpr (FMT == 1) {
+      g = e5m2_sign_mant_of(slot, c.sm[s][0], c.sm[s][1], c.sm[s][2]);
+    } else {
+      const uint32_t sw = c.sm[s][gi];
+      g = e4m3_sign_mant(perm_b32(sw, sw, qq ? 0x03030202u : 0x01010000u));
+    }
+    const uint32_t B = bfi(FmtT<FMT>::XMASK, Ev, g);  // the four FP8 bytes
+    o[gi][0][qq] = fp8x2_to_bf16x2<FMT, false>(B);
+    o[gi][1][qq] = fp8x2_to_bf16x2<FMT, true>(B);
+  }
+}
+
+// Rebuild unit s of lane n: channels gi = 0..3 x 8 tokens.  tw = the E and R words holding the
+// unit's four groups and the escape bytes before them; bw = b3 (x) and b4 (y) of the four
+// channels, one byte each (FP8: pre-shifted to the exponent position).  Output, low half first:
+// BF16 o[gi][0][qq] = tokens (4qq, 4qq+2), o[gi][1][qq] = (4qq+1, 4qq+3); FP8 (converted exactly
+// to BF16) o[gi][0][qq] = (4qq, 4qq+1), o[gi][1][qq] = (4qq+2, 4qq+3).
+template <int NH, int FMT>
+__device__ __forceinline__ void g8_rebuild_unit(const C8Regs<NH, FMT>& c, int s, int n, const uint32_t tw[3], uint2 bw,
+                                                const uint8_t* esc8, uint32_t& bad, uint32_t o[4][2][2]) {
+  constexpr int RU = FmtT<FMT>::F - 3;  // escape bytes of a raw group
+  constexpr int XS = FmtT<FMT>::XS;
+  const int bit = 4 * (n & 7);
+  const uint32_t Ew = tw[0], Rw = tw[1];
+  const uint32_t e4 = __builtin_amdgcn_ubfe(Ew, bit, 4), r4 = __builtin_amdgcn_ubfe(Rw, bit, 4);
+  bad |= r4 & ~e4;
+  if constexpr (FMT == 2) bad |= e4 & ~r4;  // no wide mode in a 4-bit exponent field
+  const uint32_t below = (1u << bit) - 1u;
+  uint32_t P = tw[2] + __popc(Ew & below) + (uint32_t)(RU - 1) * __popc(Rw & below);
+  const uint32_t W0 = c.cd[s][0], W1 = c.cd[s][1], W2 = c.cd[s][2];
+  // byte g of Hw: the base of group g's mode, b4 where the group escapes (wide or raw), else b3;
+  // a raw group's base is 0, which its rare path below restores by taking b4 back off
+  const uint32_t e1 = spread4(e4);        // bit 0 of byte g = group g escapes
+  const uint32_t mE = (e1 << 8) - e1;     // x 255 (exact mod 2^32): byte g all ones where it escapes
+  const uint32_t Hw = (bw.y & mE) | (bw.x & ~mE);  // per-lane mask: not bfi(), which takes a uniform one
+  // Every LDS read of the unit first (escape planes, then their spread words), so that they are in
+  // flight together; the rare raw groups afterwards, behind one branch for the unit.
+  uint32_t Pg[4], Ev[4][2];
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    Pg[gi] = P;
+    P += ((e4 >> gi) & 1u) + (uint32_t)(RU - 1) * ((r4 >> gi) & 1u);
+  }
+  uint32_t plane[4];
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) plane[gi] = esc8[Pg[gi]] & (0u - ((e4 >> gi) & 1u));  // read always, keep if escaped
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    const uint32_t H = perm_b32(0u, Hw, (uint32_t)gi * 0x01010101u);  // the group's base in all four bytes
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+      Ev[gi][qq] = H + code_slot_of<XS>(2 * gi + qq, W0, W1, W2) + esc_lut[(plane[gi] >> (4 * qq)) & 0xFu];
+  }
+  if (r4) {  // a raw group (rare): base 0 (b4 taken back off) and the offset bits above bit 3
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      if ((r4 >> gi) & 1u) {
+        const uint32_t H = perm_b32(0u, Hw, (uint32_t)gi * 0x01010101u);
+        Ev[gi][0] -= H;
+        Ev[gi][1] -= H;
+        if constexpr (FMT == 0) {  // four bytes of 4-bit fields at P + 1 (any alignment): two aligned words
+          const uint32_t a0 = Pg[gi] + 1u;
+          const uint32_t* e32 = reinterpret_cast<const uint32_t*>(esc8);
+          const uint32_t hi = __builtin_amdgcn_alignbyte(e32[(a0 >> 2) + 1], e32[a0 >> 2], a0 & 3u);
+          Ev[gi][0] += raw_high_nibbles(hi & 0xFFFFu);
+          Ev[gi][1] += raw_high_nibbles(hi >> 16);
+        } else if constexpr (FMT == 1) {  // the bit-4 plane
+          const uint32_t u = esc8[Pg[gi] + 1];
+          Ev[gi][0] += esc_lut[u & 0xFu] << 1;
+          Ev[gi][1] += esc_lut[(u >> 4) & 0xFu] << 1;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) g8_assemble<NH, FMT>(c, s, gi, qq, Ev[gi][qq], o);
+}
+
+// b3 (even k) or b4 (odd k) of the four channels 64r + 4nn .. +3 of base version ver, for packed
+// slot k = ((kv * NH + r) * 16 + nn) * 2 + which.
+template <int NH, int FMT>
+__device__ __forceinline__ uint32_t g8_packed_bases(const Geo& G, const uint8_t* bases, int ver, int k, int h) {
+  const int kv = k / (32 * NH), r = (k / 32) % NH, nn = (k / 2) % 16, which = k & 1;
+  return ld32(bases_of(G, bases, ver, 3 + which, kv, h) + 64 * r + 4 * nn) << FmtT<FMT>::XS;
+}
+
+// Scale accumulators of heads 4j .. 4j+3 (row r of lane 16j + n) by their heads' factors.
+template <int N>
+__device__ __forceinline__ void rescale_rows(f32x4_t (&acc)[N], float alpha) {
+  uint32_t base;
+  asm volatile("v_and_b32 %0, 48, %1" : "=v"(base) : "v"((uint32_t)threadIdx.x));
+  float a[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    a[r] = __int_as_float(__builtin_amdgcn_ds_bpermute((int)(base + 4 * r), __float_as_int(alpha)));
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[i][r] *= a[r];
+}
+
+template <int NH, int FMT>
+__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_g8_kernel(AttnArgs a) {
+  using Q = TG8<NH, FMT>;
+  constexpr int NR = 2 * NH;  // 32-channel rounds (tile_ref geometry)
+  constexpr bool NAT = FmtT<FMT>::NATURAL;
+  constexpr int D = Q::D;
+  extern __shared__ uint4 lds4[];
+  const Geo& G = a.G;
+  const int esc_room = (max(G.esc_cap, 16) + 15) / 16 * 16;
+  uint8_t* klds = reinterpret_cast<uint8_t*>(lds4);                         // [64][D] bf16, swizzled
+  uint8_t* esc_lds = klds + kSB * D * 2;                                      // esc_room + 16 bytes
+  uint4* qlds = reinterpret_cast<uint4*>(esc_lds + esc_room + 16);            // [g][D/8]
+  uint32_t* blds = reinterpret_cast<uint32_t*>(qlds + G.g * (D / 8));         // [version][K|V][NH][16][2]
+  const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int4 z = a.zrow[blockIdx.z];
+  const int si = z.x, seq = z.y, L = z.z;
+  const SbOrder ord(L, a.n_splits, split);
+  uint32_t flags = 0, bad = 0;
+  init_esc_lut<FMT>();
+
+  uint32_t eK = kUnallocated, eV = kUnallocated;
+  if (ord.cnt > 0) {
+    eK = load_entry<kSB>(a, seq, L, ord.at(0) * kSB, 0, h);
+    eV = load_entry<kSB>(a, seq, L, ord.at(0) * kSB, 1, h);
+  }
+  uint4 qr[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int k = lane + kWave * u;
+    qr[u] = k < G.g * (D / 8) ? ld128(a.q + ((size_t)si * G.Hq + h * G.g) * D + 8 * k) : make_uint4(0, 0, 0, 0);
+  }
+  constexpr int BU = 64 * NH / kWave;  // packed base words per lane and version
+  uint32_t br[BU];
+#pragma unroll
+  for (int u = 0; u < BU; ++u) br[u] = g8_packed_bases<NH, FMT>(G, a.B.bases, 0, lane + kWave * u, h);
+
+  float m = -INFINITY, l = 0.0f;
+  f32x4_t acc[NH * 4];  // accumulator r * 4 + gi: MFMA column n = channel 64r + 4n + gi
+#pragma unroll
+  for (int i = 0; i < NH * 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  C8Regs<NH, FMT> cK, cV;
+  TileRef rK, rV;
+  if (ord.cnt > 0) {
+    rK = tile_ref<NR, kSB, FMT>(a, seq, L, ord.at(0) * kSB, 0, h, eK);
+    flags |= missing_flag(L, ord.at(0) * kSB, eK);
+    g8_load_tile<NH, FMT, true>(rK, lane, cK);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (lane + kWave * u < G.g * (D / 8)) qlds[lane + kWave * u] = qr[u];
+#pragma unroll
+  for (int u = 0; u < BU; ++u) blds[lane + kWave * u] = br[u];
+  for (int v = 1; v < G.n_versions; ++v)
+#pragma unroll
+    for (int u = 0; u < BU; ++u) blds[v * 64 * NH + lane + kWave * u] = g8_packed_bases<NH, FMT>(G, a.B.bases, v, lane + kWave * u, h);
+
+  for (int it = 0; it < ord.cnt; ++it) {
+    phase_priority(2 * (ord.cnt - it));
+    const int sb = ord.at(it);
+    rV = tile_ref<NR, kSB, FMT>(a, seq, L, sb * kSB, 1, h, eV);
+    flags |= missing_flag(L, sb * kSB, eV);
+    g8_load_tile<NH, FMT, false>(rV, lane, cV);
+    if (it + 1 < ord.cnt) {
+      eK = load_entry<kSB>(a, seq, L, ord.at(it + 1) * kSB, 0, h);
+      eV = load_entry<kSB>(a, seq, L, ord.at(it + 1) * kSB, 1, h);
+    }
+
+    // ---- K: rebuild into the LDS tile ----
+    __syncthreads();
+    const uint32_t pfxK = g8_stage_escape<NH, FMT>(cK, rK, lane, esc_lds, bad);
+    __syncthreads();
+    const int kind = __builtin_amdgcn_readfirstlane(rK.kind);
+    if ((kind & 3) == SRC_COMP) {
+      const int boK = kind >> 2;
+#pragma unroll
+      for (int s = 0; s < Q::US; ++s) {
+        uint32_t tw[3];
+        g8_fetch_tags<NH, FMT, true>(cK, s, j, n, pfxK, tw);
+        int tg, r;
+        g8_unit<NH, true>(s, j, tg, r);
+        const uint2 bw = *reinterpret_cast<const uint2*>(blds + boK + ((0 * NH + r) * 16 + n) * 2);
+        uint32_t o[4][2][2];
+        g8_rebuild_unit<NH, FMT>(cK, s, n, tw, bw, esc_lds, bad, o);
+        // token 8tg + 4qq + k: channels 64r + 4n .. +3 as one 8-byte store (BF16: word k & 1,
+        // half k >> 1; FP8: word k >> 1, half k & 1)
+        const int chunk = 8 * r + (n >> 1), off = 8 * (n & 1);
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int row = 16 * (tg & 3) + 8 * (tg >> 2) + 4 * qq + k;
+            const int wi = NAT ? (k >> 1) : (k & 1);
+            const uint32_t sel = (NAT ? (k & 1) : (k >> 1)) ? 0x07060302u : 0x05040100u;
+            const uint32_t w01 = perm_b32(o[1][wi][qq], o[0][wi][qq], sel);
+            const uint32_t w23 = perm_b32(o[3][wi][qq], o[2][wi][qq], sel);
+            *reinterpret_cast<uint2*>(klds + row * 2 * D + ((chunk ^ swz(row)) << 4) + off) = make_uint2(w01, w23);
+          }
+      }
+    } else if ((kind & 3) == SRC_RAW) {
+      // a raw tile: token rows straight into their LDS rows (BF16 by LDS-DMA, FP8 through
+      // registers, converted to BF16)
+      const uint64_t rp = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)((uintptr_t)rK.p >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)rK.p);
+      if constexpr (FMT == 0) {
+        constexpr int RPI = 512 / D;  // rows per instruction
+        constexpr int LPR = D / 8;    // lanes (16-byte pieces) per row
+        const uint16_t* raw = reinterpret_cast<const uint16_t*>(rp);
+#pragma unroll 1
+        for (int i = 0; i < kSB / RPI; ++i) {
+          const int row = RPI * i + lane / LPR, pos = lane % LPR;
+          const int tok = 32 * ((row & 15) >> 3) + 8 * (row >> 4) + (row & 7);  // the token of LDS row `row`
+          __builtin_amdgcn_global_load_lds(raw + (size_t)tok * D + 8 * (pos ^ swz(row)),
+                                           (__attribute__((address_space(3))) void*)(klds + RPI * i * 2 * D), 16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the DMA has landed in LDS
+      } else {
+        const uint8_t* raw = reinterpret_cast<const uint8_t*>(rp);
+        constexpr int NCH = D / 8;  // 8-element pieces per row; lane group j fills LDS rows 16j .. 16j+15
+#pragma unroll
+        for (int m0 = 0; m0 < NCH; m0 += 4) {
+          uint2 v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int k = n + 16 * (m0 + u), row = 16 * j + k / NCH, chunk = k % NCH;
+            const int tok = 32 * ((row & 15) >> 3) + 8 * (row >> 4) + (row & 7);
+            v[u] = ld64(raw + (size_t)tok * D + 8 * chunk);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int k = n + 16 * (m0 + u), row = 16 * j + k / NCH, chunk = k % NCH;
+            *reinterpret_cast<uint4*>(klds + row * 2 * D + ((chunk ^ swz(row)) << 4)) = fp8x8_to_operand<FMT>(v[u]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- QK and softmax: s[8h + u] = head n, token 32h + 8j + u ----
+    const int valid = min(rK.valid(), rV.valid());
+    f32x4_t cc[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) cc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NR; ++ks) {
+      uint4 qv = qlds[min(n, G.g - 1) * (D / 8) + 4 * ks + j];
+      if (n >= G.g) qv = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int row = 16 * (n >> 2) + 4 * rb + (n & 3);
+        const uint4 av = *reinterpret_cast<const uint4*>(klds + row * 2 * D + (((4 * ks + j) ^ swz(row)) << 4));
+        cc[rb] = mfma16(av, qv, cc[rb]);
+      }
+    }
+    float s[16];
+    if (__builtin_amdgcn_ballot_w64(valid == 0)) {  // a block missing from the table (status bit 4)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) s[k] = -INFINITY;
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[4 * rb + r] = cc[rb][r] * a.sl2;
+    }
+    const float alpha = softmax_update(s, m, l);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) rescale_rows<NH * 4>(acc, alpha);
+    uint4 phi[2], plo[2];
+    pack_p<!NAT>(s, phi, plo);
+
+    if (it + 1 < ord.cnt) {
+      rK = tile_ref<NR, kSB, FMT>(a, seq, L, ord.at(it + 1) * kSB, 0, h, eK);
+      flags |= missing_flag(L, ord.at(it + 1) * kSB, eK);
+      g8_load_tile<NH, FMT, true>(rK, lane, cK);
+    }
+
+    phase_priority(2 * (ord.cnt - it) - 1);
+    // ---- V: rebuild straight into B operands ----
+    __syncthreads();
+    const uint32_t pfxV = g8_stage_escape<NH, FMT>(cV, rV, lane, esc_lds, bad);
+    __syncthreads();
+    const int kindV = __builtin_amdgcn_readfirstlane(rV.kind);
+    const int boV = kindV >> 2;
+#pragma unroll
+    for (int s = 0; s < Q::US; ++s) {
+      int tg, r;
+      g8_unit<NH, false>(s, j, tg, r);
+      const int hh = s / NH;  // the 32-token half
+      uint4 bv[4];
+      if ((kindV & 3) == SRC_COMP) {
+        uint32_t tw[3];
+        g8_fetch_tags<NH, FMT, false>(cV, s, j, n, pfxV, tw);
+        const uint2 bw = *reinterpret_cast<const uint2*>(blds + boV + ((NH + r) * 16 + n) * 2);
+        uint32_t o[4][2][2];
+        g8_rebuild_unit<NH, FMT>(cV, s, n, tw, bw, esc_lds, bad, o);
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) bv[gi] = make_uint4(o[gi][0][0], o[gi][1][0], o[gi][0][1], o[gi][1][1]);
+      } else if ((kindV & 3) == SRC_RAW) {
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          const size_t off = (size_t)(64 * r + 4 * n + gi) * kSB + 32 * hh + 8 * j;  // elements
+          if constexpr (FMT == 0) {  // natural order -> the interleaved order of P
+            const uint4 v = ld128(reinterpret_cast<const uint16_t*>(rV.p) + off);
+            bv[gi] = make_uint4(perm_b32(v.y, v.x, 0x05040100u), perm_b32(v.y, v.x, 0x07060302u),
+                                perm_b32(v.w, v.z, 0x05040100u), perm_b32(v.w, v.z, 0x07060302u));
+          } else {
+            bv[gi] = fp8x8_to_operand<FMT>(ld64(rV.p + off));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) bv[gi] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        acc[4 * r + gi] = mfma16(phi[hh], bv[gi], acc[4 * r + gi]);
+        acc[4 * r + gi] = mfma16(plo[hh], bv[gi], acc[4 * r + gi]);
+      }
+    }
+  }
+  if (bad) flags |= 8u;
+  if (flags) atomicOr(&a.B.counters->status, flags);
+  // partials: head 4j + i, channels 64r + 4n .. +3 from accumulators 4r .. 4r+3
+  {
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    const int S = a.n_splits;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int head = 4 * j + i;
+      if (head < G.g) {
+        float* dst = a.ws_acc + (((size_t)si * G.Hq + h * G.g + head) * S + split) * D;
+#pragma unroll
+        for (int r = 0; r < NH; ++r)
+          *reinterpret_cast<float4*>(dst + 64 * r + 4 * n) =
+              make_float4(acc[4 * r][i], acc[4 * r + 1][i], acc[4 * r + 2][i], acc[4 * r + 3][i]);
+      }
+    }
+    if (j == 0 && n < G.g) {
+      float* ml = a.ws_ml + (((size_t)si * G.Hq + h * G.g + n) * S + split) * 2;
+      ml[0] = m;
+      ml[1] = lt;
+    }
+  }
+  if (a.k_new != nullptr && split == 0) store_new_token<FMT>(a, si, seq, z.w, h);
+}
+
+// ------------------------------------------------------------------------------------------
 // Uncompressed cache (every tile raw): the speedup baseline.  K rows are loaded straight into
 // QK A operands and V straight into PV B operands (no LDS), with the same K/V phase pipelining.
 // Operand pieces as loaded: eight BF16 (uint4) or eight FP8 (uint2, converted at use).
@@ -1168,8 +1678,27 @@ int launch_attn_t(const AttnArgs& a, int n_seqs, void* stream) {
   }
 }
 
+// 8-token groups: 64-token blocks only, and the tile offsets this kernel is compiled for.
+template <int NH, int FMT>
+int launch_attn_g8(const AttnArgs& a, int n_seqs, void* stream) {
+  using Q = TG8<NH, FMT>;
+  const Geo& G = a.G;
+  if (G.T != kSB || G.GT != 8 || G.mode_set != 0 || G.code_off != Q::CODE_OFF || G.sm_off != Q::SM_OFF ||
+      G.esc_off != Q::ESC_OFF || G.PW != Q::PW || G.esc_cap > 512)
+    return (int)hipErrorInvalidValue;
+  const dim3 grid(a.n_splits, G.Hkv, n_seqs);
+  // K tile, escape staging (+16 bytes that the byte reads may touch past the last piece), query,
+  // bases per version
+  const size_t lds = (size_t)kSB * Q::D * 2 + (size_t)((max(G.esc_cap, 16) + 15) / 16 * 16 + 16) +
+                     (size_t)G.g * Q::D * 2 + (size_t)G.n_versions * 64 * NH * 4;
+  hipLaunchKernelGGL((attn_g8_kernel<NH, FMT>), grid, dim3(kWave), lds, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
 template <int FMT>
 int launch_attn_f(const AttnArgs& a, int n_seqs, void* stream) {
+  if (a.G.compressed && a.G.GT == 8)
+    return (a.G.D == 128) ? launch_attn_g8<2, FMT>(a, n_seqs, stream) : launch_attn_g8<1, FMT>(a, n_seqs, stream);
   return (a.G.D == 128) ? launch_attn_t<4, FMT>(a, n_seqs, stream) : launch_attn_t<2, FMT>(a, n_seqs, stream);
 }
 

@@ -40,6 +40,7 @@ __device__ __forceinline__ uint32_t code_slot(uint32_t W0, uint32_t W1, uint32_t
 
 // (a & mask) | (b & ~mask) as one v_bfi_b32.  Written as asm: given chains of constant-mask
 // selects the compiler splits them into separate ANDs and an OR3 (two more instructions each).
+// The mask goes in a scalar register: it must be the same for every lane (a constant).
 __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
   uint32_t r;
   asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(b));
@@ -70,7 +71,8 @@ __device__ __forceinline__ uint32_t e5m2_sign_mant(uint32_t W0, uint32_t W1, uin
 // in place in y.
 __device__ __forceinline__ uint32_t e4m3_sign_mant(uint32_t y) { return bfi(0x07800780u, y >> 4, y); }
 
-// 24-bit multiply (v_mul_u32_u24, full rate).  Written as asm so that the compiler cannot fold a
+// 24-bit multiply (v_mul_u32_u24, full rate): the low 32 bits of the product of the operands' low
+// 24 bits, so both operands must be below 2^24.  Written as asm so that the compiler cannot fold a
 // following shift into the constant and fall back to the quarter-rate 32-bit multiply.
 __device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) {
   uint32_t r;

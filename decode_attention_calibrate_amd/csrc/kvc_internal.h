@@ -149,8 +149,10 @@ int launch_decode_blocks(const Geo& G, const DevBufs& B, int seq, int first, int
 int launch_attention_partials(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale,
                               int n_splits, float* ws_acc, float* ws_ml, const void* k_new, const void* v_new,
                               const int* new_pos, void* stream);
-// The same partials for compressed caches with 8-token groups (any format), from blocks rebuilt
-// into LDS; same workspace layout and decode-step tail store.
+// (Compressed caches with 8-token groups in 64-token blocks take a register-rebuild kernel of
+// their own.)  The same partials for compressed caches with 8-token groups in other block sizes
+// and for FORMAT v2 (any format), from blocks rebuilt into LDS; same workspace layout and
+// decode-step tail store.
 int launch_attention_any(const Geo& G, const DevBufs& B, const SeqList& seqs, const uint16_t* q, float scale,
                          int n_splits, float* ws_acc, float* ws_ml, const void* k_new, const void* v_new,
                          const int* new_pos, void* stream);
