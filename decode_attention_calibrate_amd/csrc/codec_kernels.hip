@@ -122,6 +122,14 @@ __global__ void calibrate_kernel(Geo G, DevBufs B, const void* __restrict__ k, c
   }
 }
 
+// Element format constants (kvc_dtype: 0 BF16, 1 FP8 E5M2, 2 FP8 E4M3).
+template <int FMT>
+struct EncFmt {
+  static constexpr int F = FMT == 0 ? 8 : (FMT == 1 ? 5 : 4);
+  static constexpr int MB = FMT == 0 ? 7 : (FMT == 1 ? 2 : 3);
+  static constexpr int EB = FMT == 0 ? 2 : 1;
+};
+
 // Mode of a group from its exponent range and the channel's bases: 0 narrow, 1 wide, 2 raw.
 __device__ __forceinline__ int choose_mode(uint32_t mn, uint32_t mx, uint32_t b3, uint32_t b4, bool has_wide) {
   if (b3 <= mn && mx <= b3 + 7) return 0;
@@ -134,20 +142,28 @@ struct PairInfo {
   uint32_t base[2];
 };
 
-__device__ __forceinline__ PairInfo pair_info(const Geo& G, const uint16_t* tile, const uint8_t* b3, const uint8_t* b4,
-                                              int pr) {
+// Modes and bases of a pair of groups (channels c0, c0 + 1 of one token group) from its 16 words
+// held in registers (token tau: channel c0 in the low half, c0 + 1 in the high half) and the two
+// channels' bases.
+template <int FMT>
+__device__ __forceinline__ PairInfo pair_info_regs(const uint32_t pw[kGroup], uint32_t b3a, uint32_t b3b,
+                                                   uint32_t b4a, uint32_t b4b) {
+  using EF = EncFmt<FMT>;
+  uint32_t mn[2] = {255u, 255u}, mx[2] = {0u, 0u};
+#pragma unroll
+  for (int tau = 0; tau < kGroup; ++tau)
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const uint32_t e = (pw[tau] >> (16 * gi + EF::MB)) & ((1u << EF::F) - 1u);
+      mn[gi] = min(mn[gi], e);
+      mx[gi] = max(mx[gi], e);
+    }
   PairInfo P;
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
-    const int q = 2 * pr + gi, tg = q / G.D, c = q % G.D;
-    uint32_t mn = 255, mx = 0;
-    for (int tau = 0; tau < kGroup; ++tau) {
-      const uint32_t e = exp_of(G, tile[(tg * kGroup + tau) * G.D + c]);
-      mn = min(mn, e);
-      mx = max(mx, e);
-    }
-    P.mode[gi] = choose_mode(mn, mx, b3[c], b4[c], G.F > 4);
-    P.base[gi] = P.mode[gi] == 0 ? b3[c] : (P.mode[gi] == 1 ? b4[c] : 0u);
+    const uint32_t b3 = gi ? b3b : b3a, b4 = gi ? b4b : b4a;
+    P.mode[gi] = choose_mode(mn[gi], mx[gi], b3, b4, EF::F > 4);
+    P.base[gi] = P.mode[gi] == 0 ? b3 : (P.mode[gi] == 1 ? b4 : 0u);
   }
   return P;
 }
@@ -155,6 +171,25 @@ __device__ __forceinline__ PairInfo pair_info(const Geo& G, const uint16_t* tile
 // GT-bit escape units of a group: none (narrow), one plane (wide), F - 3 units (raw: bit 3,
 // then BF16 bits 4..7 as four units of nibbles, E5M2 bit 4 as one more plane).
 __device__ __forceinline__ int mode_planes(const Geo& G, int m) { return m == 0 ? 0 : (m == 1 ? 1 : G.F - 3); }
+
+// The 16 bytes x (8 BF16 or 16 FP8 elements, in order) as consecutive 16-bit LDS elements at
+// dst (16-byte aligned): one or two 16-byte stores.
+template <int EB>
+__device__ __forceinline__ void store_elems(uint16_t* dst, uint4 x) {
+  if constexpr (EB == 2) {
+    *reinterpret_cast<uint4*>(dst) = x;
+  } else {  // FP8 bytes widened to 16 bits: bytes (b0, b1) of a word -> (b0, 0, b1, 0)
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t y[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      y[2 * k] = perm_b32(0u, w[k], 0x0C010C00u);
+      y[2 * k + 1] = perm_b32(0u, w[k], 0x0C030C02u);
+    }
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(y[0], y[1], y[2], y[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(y[4], y[5], y[6], y[7]);
+  }
+}
 
 // Gathers block b's T tokens into the LDS tile [T][D] with 16-byte loads along each source's
 // contiguous axis: tokens still in the old tail (K token-major, V channel-major), then the
@@ -186,6 +221,10 @@ __device__ __forceinline__ void gather_block(const Geo& G, const uint8_t* tail, 
         w4[e / (4 / EB)] |= elem_at(src, e, EB) << (8 * EB * (e % (4 / EB)));
       x = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
+    if (!kv) {  // K: the vector is VE consecutive channels of one token, whole
+      store_elems<EB>(tile + t * D + c, x);
+      continue;
+    }
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
@@ -198,13 +237,7 @@ __device__ __forceinline__ void gather_block(const Geo& G, const uint8_t* tail, 
     const int t = n_tail + v / (D / VE), c = (v % (D / VE)) * VE, p = b * T + t;
     const uint8_t* src = reinterpret_cast<const uint8_t*>(in) +
                          ((((size_t)si * n_tok + (p - L0)) * G.Hkv + h) * D + c) * EB;
-    const uint4 x = *reinterpret_cast<const uint4*>(src);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int e = 0; e < VE; ++e) {
-      const uint32_t val = EB == 2 ? (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu : (w[e >> 2] >> (8 * (e & 3))) & 0xFFu;
-      tile[t * D + c + e] = (uint16_t)val;
-    }
+    store_elems<EB>(tile + t * D + c, *reinterpret_cast<const uint4*>(src));
   }
 }
 
@@ -271,13 +304,6 @@ __device__ void store_raw_tile(const Geo& G, const DevBufs& B, int slot, int kv,
 // One block per newly full block of one (sequence, K|V, head): gathers its T tokens from the
 // old tail and the appended tokens, encodes it (or stores it raw), pops a slot and writes the
 // block-table entry.
-// Element format constants (kvc_dtype: 0 BF16, 1 FP8 E5M2, 2 FP8 E4M3).
-template <int FMT>
-struct EncFmt {
-  static constexpr int F = FMT == 0 ? 8 : (FMT == 1 ? 5 : 4);
-  static constexpr int MB = FMT == 0 ? 7 : (FMT == 1 ? 2 : 3);
-  static constexpr int EB = FMT == 0 ? 2 : 1;
-};
 
 // Place the four 3-bit fields of slot s (one per byte lane, bits 0..2) at bits 3s..3s+2 of
 // the byte lanes' 24-bit streams held in W[0..2] (byte lane k of word w = stream bits 8w..8w+7).
@@ -296,7 +322,8 @@ template <int FMT>
 __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqList S, const void* __restrict__ kin,
                                                           const void* __restrict__ vin, int n_tok) {
   using EF = EncFmt<FMT>;
-  extern __shared__ uint32_t smem[];
+  extern __shared__ uint4 smem4[];                                      // 16-byte aligned
+  uint32_t* smem = reinterpret_cast<uint32_t*>(smem4);
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);                  // [T][D] logical
   uint32_t* tagw = smem + (G.raw_elems / 2);                            // [2][PW]
   __shared__ int red[8];
@@ -322,19 +349,24 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
   int is_raw = 1, total = 0;
   const uint8_t* b3 = bases_of(G, B.bases, G.cur_ver, 3, kv, h);  // blocks are encoded with the current bases
   const uint8_t* b4 = bases_of(G, B.bases, G.cur_ver, 4, kv, h);
-  const int ppt = (G.NP + kThreads - 1) / kThreads;  // pairs per thread (consecutive)
-  const int pr0 = tid * ppt;
+  // One pair of groups per thread (G.NP <= 256 for T <= 64, D <= 128): channels c0, c0 + 1 of
+  // token group tg, read from LDS once as 16 words (token tau: channel c0 in the low half).
+  const int pr = tid, q0 = 2 * pr, tg = q0 / D, c0 = q0 % D;
+  const bool has_pair = pr < G.NP;
+  uint32_t pw[kGroup];
+#pragma unroll
+  for (int tau = 0; tau < kGroup; ++tau)
+    pw[tau] = has_pair ? *reinterpret_cast<const uint32_t*>(tile + (tg * kGroup + tau) * D + c0) : 0u;
+  PairInfo PI = {{0, 0}, {0u, 0u}};
   int my_before = 0;
   if (G.compressed) {
     int my_planes = 0;
     int cnt[3] = {0, 0, 0};
-    for (int k = 0; k < ppt; ++k) {
-      const int pr = pr0 + k;
-      if (pr >= G.NP) break;
-      const PairInfo P = pair_info(G, tile, b3, b4, pr);
-      my_planes += mode_planes(G, P.mode[0]) + mode_planes(G, P.mode[1]);
-      cnt[P.mode[0]]++;
-      cnt[P.mode[1]]++;
+    if (has_pair) {
+      PI = pair_info_regs<FMT>(pw, b3[c0], b3[c0 + 1], b4[c0], b4[c0 + 1]);
+      my_planes = mode_planes(G, PI.mode[0]) + mode_planes(G, PI.mode[1]);
+      cnt[PI.mode[0]]++;
+      cnt[PI.mode[1]]++;
     }
     my_before = block_exclusive_scan(my_planes, red, &total);
     is_raw = (2 * total > G.esc_cap) ? 1 : 0;
@@ -360,16 +392,13 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
 
   uint8_t* dst = B.comp_pool + (size_t)slot * G.stride;
   int P = my_before;
-  for (int k = 0; k < ppt; ++k) {
-    const int pr = pr0 + k;
-    if (pr >= G.NP) break;
-    const PairInfo PI = pair_info(G, tile, b3, b4, pr);
+  if (has_pair) {
     uint32_t W[3] = {0u, 0u, 0u};
     uint32_t SM[4] = {0u, 0u, 0u, 0u};  // E5M2: 3 words in the CODE unit layout; E4M3: 4 words of nibbles
     uint32_t smb[8];                      // BF16: the 8 SM words (one byte per element)
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
-      const int q = 2 * pr + gi, tg = q / D, c = q % D;
+      const int q = q0 + gi;
       const uint32_t base = PI.base[gi];
       // escape units: [0] = plane of offset bit 3; a raw BF16 group adds [1..4] = 4-bit fields
       // of offset bits 4..7 (token tau at bits 4*(tau%4) of unit 1 + tau/4), a raw E5M2 group
@@ -381,7 +410,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
 #pragma unroll
         for (int lk = 0; lk < 4; ++lk) {
           const int tau = 4 * t4 + lk;
-          const uint32_t x = tile[(tg * kGroup + tau) * D + c];
+          const uint32_t x = (pw[tau] >> (16 * gi)) & 0xFFFFu;
           const uint32_t o = ((x >> EF::MB) & ((1u << EF::F) - 1u)) - base;
           const uint32_t f = ((x >> (EF::MB + EF::F)) << EF::MB) | (x & ((1u << EF::MB) - 1u));
           cf |= (o & 7u) << (8 * lk);
