@@ -137,6 +137,8 @@ __device__ __forceinline__ int choose_mode(uint32_t mn, uint32_t mx, uint32_t b3
   return 2;
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 struct PairInfo {
   int mode[2];
   uint32_t base[2];
@@ -149,15 +151,15 @@ template <int FMT>
 __device__ __forceinline__ PairInfo pair_info_regs(const uint32_t pw[kGroup], uint32_t b3a, uint32_t b3b,
                                                    uint32_t b4a, uint32_t b4b) {
   using EF = EncFmt<FMT>;
-  uint32_t mn[2] = {255u, 255u}, mx[2] = {0u, 0u};
+  // both channels' exponents in 16-bit lanes, packed 16-bit min and max over the 16 tokens
+  u16x2 lo = {0xFFFFu, 0xFFFFu}, hi = {0u, 0u};
 #pragma unroll
-  for (int tau = 0; tau < kGroup; ++tau)
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const uint32_t e = (pw[tau] >> (16 * gi + EF::MB)) & ((1u << EF::F) - 1u);
-      mn[gi] = min(mn[gi], e);
-      mx[gi] = max(mx[gi], e);
-    }
+  for (int tau = 0; tau < kGroup; ++tau) {
+    const u16x2 e = __builtin_bit_cast(u16x2, (pw[tau] >> EF::MB) & (((1u << EF::F) - 1u) * 0x00010001u));
+    lo = __builtin_elementwise_min(lo, e);
+    hi = __builtin_elementwise_max(hi, e);
+  }
+  const uint32_t mn[2] = {lo.x, lo.y}, mx[2] = {hi.x, hi.y};
   PairInfo P;
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
@@ -392,7 +394,65 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
 
   uint8_t* dst = B.comp_pool + (size_t)slot * G.stride;
   int P = my_before;
-  if (has_pair) {
+  if (has_pair && FMT == 0) {
+    // BF16, four tokens per word for both channels at once: word k of a quad holds channel c0 in
+    // its low half; shifted right by 7 its bytes 0 and 2 are the two exponents, and one bit-select
+    // puts each channel's sign/mantissa byte (sign << 7 | mantissa) in the same bytes.  v_perm then
+    // gathers each channel's four bytes into one word (token 4 t4 + k in byte lane k).
+    uint32_t W[3] = {0u, 0u, 0u}, smb[8], units[2][5] = {{0u, 0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u, 0u}};
+    const uint32_t base2 = PI.base[0] | (PI.base[1] << 16);
+    const uint32_t B0 = PI.base[0] * 0x01010101u, B1 = PI.base[1] * 0x01010101u;
+    const bool any_raw = PI.mode[0] == 2 || PI.mode[1] == 2;
+    uint32_t pl = 0;  // offset bit 3 of token tau at bit tau of each 16-bit half (the escape planes)
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      uint32_t ex[4], sx[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = pw[4 * t4 + k];
+        ex[k] = w >> 7;
+        sx[k] = bfi(0x00800080u, w >> 8, w);
+        pl |= ((((ex[k] & 0x00FF00FFu) - base2) >> 3) & 0x00010001u) << (4 * t4 + k);
+      }
+      const uint32_t A = perm_b32(ex[1], ex[0], 0x06020400u), Bq = perm_b32(ex[3], ex[2], 0x06020400u);
+      const uint32_t o0 = perm_b32(Bq, A, 0x05040100u) - B0, o1 = perm_b32(Bq, A, 0x07060302u) - B1;
+      const uint32_t SA = perm_b32(sx[1], sx[0], 0x06020400u), SB = perm_b32(sx[3], sx[2], 0x06020400u);
+      smb[t4] = perm_b32(SB, SA, 0x05040100u);
+      smb[4 + t4] = perm_b32(SB, SA, 0x07060302u);
+      switch (t4) {
+        case 0: place_slot<0>(W, o0 & 0x07070707u); place_slot<4>(W, o1 & 0x07070707u); break;
+        case 1: place_slot<1>(W, o0 & 0x07070707u); place_slot<5>(W, o1 & 0x07070707u); break;
+        case 2: place_slot<2>(W, o0 & 0x07070707u); place_slot<6>(W, o1 & 0x07070707u); break;
+        default: place_slot<3>(W, o0 & 0x07070707u); place_slot<7>(W, o1 & 0x07070707u); break;
+      }
+      if (any_raw) {  // offset bits 4..7, token 4 t4 + k at bits 4k of unit 1 + t4
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          const uint32_t t = ((gi ? o1 : o0) >> 4) & 0x0F0F0F0Fu;
+          const uint32_t u = t | (t >> 4);
+          units[gi][1 + t4] = (u & 0xFFu) | ((u >> 8) & 0xFF00u);
+        }
+      }
+    }
+    units[0][0] = pl & 0xFFFFu;
+    units[1][0] = pl >> 16;
+    uint16_t* esc16 = reinterpret_cast<uint16_t*>(dst + G.esc_off);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int q = q0 + gi, np = mode_planes(G, PI.mode[gi]);
+      for (int p = 0; p < np; ++p) esc16[P + p] = (uint16_t)units[gi][p];
+      P += np;
+      if (PI.mode[gi] >= 1) atomicOr(&tagw[q >> 5], 1u << (q & 31));
+      if (PI.mode[gi] == 2) atomicOr(&tagw[G.PW + (q >> 5)], 1u << (q & 31));
+    }
+    uint32_t* code = reinterpret_cast<uint32_t*>(dst + G.code_off + 12 * pr);
+    code[0] = W[0];
+    code[1] = W[1];
+    code[2] = W[2];
+    uint4* smd = reinterpret_cast<uint4*>(dst + G.sm_off + 32 * pr);
+    smd[0] = make_uint4(smb[0], smb[1], smb[2], smb[3]);
+    smd[1] = make_uint4(smb[4], smb[5], smb[6], smb[7]);
+  } else if (has_pair) {  // FP8: element by element
     uint32_t W[3] = {0u, 0u, 0u};
     uint32_t SM[4] = {0u, 0u, 0u, 0u};  // E5M2: 3 words in the CODE unit layout; E4M3: 4 words of nibbles
     uint32_t smb[8];                      // BF16: the 8 SM words (one byte per element)
