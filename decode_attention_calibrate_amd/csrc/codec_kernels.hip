@@ -362,21 +362,25 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
   PairInfo PI = {{0, 0}, {0u, 0u}};
   int my_before = 0;
   if (G.compressed) {
-    int my_planes = 0;
-    int cnt[3] = {0, 0, 0};
+    // one block scan of three packed counts: escape units (bits 0..11; at most 256 pairs x 10),
+    // wide groups (12..21) and raw groups (22..31; at most 512 each)
+    int packed = 0;
     if (has_pair) {
       PI = pair_info_regs<FMT>(pw, b3[c0], b3[c0 + 1], b4[c0], b4[c0 + 1]);
-      my_planes = mode_planes(G, PI.mode[0]) + mode_planes(G, PI.mode[1]);
-      cnt[PI.mode[0]]++;
-      cnt[PI.mode[1]]++;
+      packed = mode_planes(G, PI.mode[0]) + mode_planes(G, PI.mode[1]) + ((PI.mode[0] == 1) + (PI.mode[1] == 1)) * (1 << 12) +
+               ((PI.mode[0] == 2) + (PI.mode[1] == 2)) * (1 << 22);
     }
-    my_before = block_exclusive_scan(my_planes, red, &total);
+    int all = 0;
+    my_before = block_exclusive_scan(packed, red, &all) & 0xFFF;
+    total = all & 0xFFF;
     is_raw = (2 * total > G.esc_cap) ? 1 : 0;
-    for (int m = 0; m < 3; ++m) {
-      const int s = block_sum(cnt[m], red);
-      if (tid == 0) sh_modes[m] = (unsigned long long)s;
+    if (tid == 0) {
+      const int wide = (all >> 12) & 0x3FF, rawg = (int)((unsigned)all >> 22);
+      sh_modes[0] = (unsigned long long)(2 * G.NP - wide - rawg);
+      sh_modes[1] = (unsigned long long)wide;
+      sh_modes[2] = (unsigned long long)rawg;
+      sh_modes[3] = 0;
     }
-    if (tid == 0) sh_modes[3] = 0;
   }
 
   if (tid == 0) sh_slot = pop_slot(B, is_raw, sh_modes, 2 * total, &sh_raw);
