@@ -383,27 +383,15 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
     }
   }
 
-  if (tid == 0) sh_slot = pop_slot(B, is_raw, sh_modes, 2 * total, &sh_raw);
-  __syncthreads();
-  const int slot = sh_slot, raw = sh_raw;
-  if (slot < 0) {
-    if (tid == 0) B.table[entry_idx] = kUnallocated;
-    return;
-  }
-
-  if (raw) {
-    store_raw_tile(G, B, slot, kv, tile, entry_idx);
-    return;
-  }
-
-  uint8_t* dst = B.comp_pool + (size_t)slot * G.stride;
-  int P = my_before;
-  if (has_pair && FMT == 0) {
+  // BF16: the pair's fields are packed in registers while thread 0 pops the slot (its atomics'
+  // round trips overlap the other waves' packing); stored once the slot is known.
+  uint32_t W[3] = {0u, 0u, 0u}, smb[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  uint32_t units[2][5] = {{0u, 0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u, 0u}};
+  if (FMT == 0 && has_pair && !is_raw) {
     // BF16, four tokens per word for both channels at once: word k of a quad holds channel c0 in
     // its low half; shifted right by 7 its bytes 0 and 2 are the two exponents, and one bit-select
     // puts each channel's sign/mantissa byte (sign << 7 | mantissa) in the same bytes.  v_perm then
     // gathers each channel's four bytes into one word (token 4 t4 + k in byte lane k).
-    uint32_t W[3] = {0u, 0u, 0u}, smb[8], units[2][5] = {{0u, 0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u, 0u}};
     const uint32_t base2 = PI.base[0] | (PI.base[1] << 16);
     const uint32_t B0 = PI.base[0] * 0x01010101u, B1 = PI.base[1] * 0x01010101u;
     const bool any_raw = PI.mode[0] == 2 || PI.mode[1] == 2;
@@ -440,14 +428,36 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
     }
     units[0][0] = pl & 0xFFFFu;
     units[1][0] = pl >> 16;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int q = q0 + gi;
+      if (PI.mode[gi] >= 1) atomicOr(&tagw[q >> 5], 1u << (q & 31));
+      if (PI.mode[gi] == 2) atomicOr(&tagw[G.PW + (q >> 5)], 1u << (q & 31));
+    }
+  }
+
+  if (tid == 0) sh_slot = pop_slot(B, is_raw, sh_modes, 2 * total, &sh_raw);
+  __syncthreads();
+  const int slot = sh_slot, raw = sh_raw;
+  if (slot < 0) {
+    if (tid == 0) B.table[entry_idx] = kUnallocated;
+    return;
+  }
+
+  if (raw) {
+    store_raw_tile(G, B, slot, kv, tile, entry_idx);
+    return;
+  }
+
+  uint8_t* dst = B.comp_pool + (size_t)slot * G.stride;
+  int P = my_before;
+  if (has_pair && FMT == 0) {
     uint16_t* esc16 = reinterpret_cast<uint16_t*>(dst + G.esc_off);
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
-      const int q = q0 + gi, np = mode_planes(G, PI.mode[gi]);
+      const int np = mode_planes(G, PI.mode[gi]);
       for (int p = 0; p < np; ++p) esc16[P + p] = (uint16_t)units[gi][p];
       P += np;
-      if (PI.mode[gi] >= 1) atomicOr(&tagw[q >> 5], 1u << (q & 31));
-      if (PI.mode[gi] == 2) atomicOr(&tagw[G.PW + (q >> 5)], 1u << (q & 31));
     }
     uint32_t* code = reinterpret_cast<uint32_t*>(dst + G.code_off + 12 * pr);
     code[0] = W[0];
