@@ -548,6 +548,185 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(Geo G, DevBufs B, SeqL
   }
 }
 
+// BF16 tiles with 8-token groups (FORMAT v1): one thread per CODE unit (channels c0 .. c0+3 of one
+// token group, 8 tokens each, read from LDS as 8 words of channels c0, c0+1 and 8 of c0+2, c0+3),
+// fields packed four tokens per word as in encode_kernel.  Escape units are single bytes: an 8-bit
+// plane per escaped group, then four bytes of 4-bit fields for a raw group.
+__global__ void __launch_bounds__(kThreads) encode_g8_kernel(Geo G, DevBufs B, SeqList S, const void* __restrict__ kin,
+                                                             const void* __restrict__ vin, int n_tok) {
+  extern __shared__ uint4 smem4[];                                      // 16-byte aligned
+  uint32_t* smem = reinterpret_cast<uint32_t*>(smem4);
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);                  // [T][D] logical
+  uint32_t* tagw = smem + (G.raw_elems / 2);                            // [2][PW]
+  __shared__ int red[8];
+  __shared__ int sh_slot, sh_raw;
+  __shared__ unsigned long long sh_modes[4];
+
+  const int si = blockIdx.y, kv = blockIdx.z / G.Hkv, h = blockIdx.z % G.Hkv;
+  const int seq = S.ids[si], L0 = S.lens[si];
+  const int first_blk = L0 / G.T, last_full = (L0 + n_tok) / G.T;
+  const int b = first_blk + blockIdx.x;
+  if (b >= last_full) return;
+  const int tid = threadIdx.x, D = G.D;
+  const uint8_t* tail = reinterpret_cast<const uint8_t*>(B.tail) + tail_offset(G, seq, kv, h) * 2;
+  gather_block<2>(G, tail, kv ? vin : kin, si, h, kv, b, L0, n_tok, first_blk * G.T, tile);
+  for (int i = tid; i < 2 * G.PW; i += kThreads) tagw[i] = 0;
+  if (tid < 4) sh_modes[tid] = 0;
+  __syncthreads();
+
+  const size_t entry_idx = table_index(G, seq, b, kv, h);
+  const uint8_t* b3 = bases_of(G, B.bases, G.cur_ver, 3, kv, h);  // blocks are encoded with the current bases
+  const uint8_t* b4 = bases_of(G, B.bases, G.cur_ver, 4, kv, h);
+  // one CODE unit per thread (T * D / 32 <= 256 units for T <= 64, D <= 128)
+  const int u = tid, q0 = 4 * u, tg = q0 / D, c0 = q0 % D;
+  const bool has_unit = u < G.raw_elems / 32;
+  uint32_t A[8], Bw[8];  // token tau: channels c0 (low half), c0+1 / c0+2 (low half), c0+3
+#pragma unroll
+  for (int tau = 0; tau < 8; ++tau) {
+    const uint2 x = has_unit ? *reinterpret_cast<const uint2*>(tile + (tg * 8 + tau) * D + c0) : make_uint2(0u, 0u);
+    A[tau] = x.x;
+    Bw[tau] = x.y;
+  }
+  int mode[4] = {0, 0, 0, 0};
+  uint32_t base[4] = {0u, 0u, 0u, 0u};
+  int packed = 0;  // escape bytes of the unit (bits 0..15), escaped groups (16..)
+  if (G.compressed && has_unit) {
+    u16x2 loA = {0xFFFFu, 0xFFFFu}, hiA = {0u, 0u}, loB = {0xFFFFu, 0xFFFFu}, hiB = {0u, 0u};
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) {
+      const u16x2 ea = __builtin_bit_cast(u16x2, (A[tau] >> 7) & 0x00FF00FFu);
+      const u16x2 eb = __builtin_bit_cast(u16x2, (Bw[tau] >> 7) & 0x00FF00FFu);
+      loA = __builtin_elementwise_min(loA, ea);
+      hiA = __builtin_elementwise_max(hiA, ea);
+      loB = __builtin_elementwise_min(loB, eb);
+      hiB = __builtin_elementwise_max(hiB, eb);
+    }
+    const uint32_t mn[4] = {loA.x, loA.y, loB.x, loB.y}, mx[4] = {hiA.x, hiA.y, hiB.x, hiB.y};
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      mode[gi] = choose_mode(mn[gi], mx[gi], b3[c0 + gi], b4[c0 + gi], true);
+      base[gi] = mode[gi] == 0 ? b3[c0 + gi] : (mode[gi] == 1 ? b4[c0 + gi] : 0u);
+      packed += mode[gi] == 0 ? 0 : (mode[gi] == 1 ? 1 + (1 << 16) : 5 + (1 << 16));
+    }
+  }
+  int all = 0;
+  const int my_before = block_exclusive_scan(packed, red, &all) & 0xFFFF;
+  const int used = all & 0xFFFF, n_esc = all >> 16;  // escape bytes; wide + raw groups
+  const int is_raw = (!G.compressed || used > G.esc_cap) ? 1 : 0;
+  if (tid == 0 && G.compressed) {
+    const int rawg = (used - n_esc) / 4;  // a raw group's escape is 5 bytes, a wide group's 1
+    sh_modes[0] = (unsigned long long)(G.NG - n_esc);
+    sh_modes[1] = (unsigned long long)(n_esc - rawg);
+    sh_modes[2] = (unsigned long long)rawg;
+  }
+
+  // the unit's fields, packed in registers while thread 0 pops the slot
+  uint32_t W[3] = {0u, 0u, 0u}, smb[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u}, plane[4] = {0u, 0u, 0u, 0u};
+  uint32_t hin[4] = {0u, 0u, 0u, 0u};  // raw groups: token tau's offset bits 4..7 at bits 4 tau
+  if (has_unit && !is_raw) {
+    const uint32_t base2A = base[0] | (base[1] << 16), base2B = base[2] | (base[3] << 16);
+    const bool any_raw = (mode[0] | mode[1] | mode[2] | mode[3]) & 2;
+    uint32_t plA = 0, plB = 0;  // offset bit 3 of token tau at bit tau of each 16-bit half
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      uint32_t exA[4], exB[4], sxA[4], sxB[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t wa = A[4 * qq + k], wb = Bw[4 * qq + k];
+        exA[k] = wa >> 7;
+        exB[k] = wb >> 7;
+        sxA[k] = bfi(0x00800080u, wa >> 8, wa);
+        sxB[k] = bfi(0x00800080u, wb >> 8, wb);
+        plA |= ((((exA[k] & 0x00FF00FFu) - base2A) >> 3) & 0x00010001u) << (4 * qq + k);
+        plB |= ((((exB[k] & 0x00FF00FFu) - base2B) >> 3) & 0x00010001u) << (4 * qq + k);
+      }
+      const uint32_t aA = perm_b32(exA[1], exA[0], 0x06020400u), bA = perm_b32(exA[3], exA[2], 0x06020400u);
+      const uint32_t aB = perm_b32(exB[1], exB[0], 0x06020400u), bB = perm_b32(exB[3], exB[2], 0x06020400u);
+      const uint32_t o[4] = {perm_b32(bA, aA, 0x05040100u) - base[0] * 0x01010101u,
+                             perm_b32(bA, aA, 0x07060302u) - base[1] * 0x01010101u,
+                             perm_b32(bB, aB, 0x05040100u) - base[2] * 0x01010101u,
+                             perm_b32(bB, aB, 0x07060302u) - base[3] * 0x01010101u};
+      const uint32_t sA = perm_b32(sxA[1], sxA[0], 0x06020400u), tA = perm_b32(sxA[3], sxA[2], 0x06020400u);
+      const uint32_t sB = perm_b32(sxB[1], sxB[0], 0x06020400u), tB = perm_b32(sxB[3], sxB[2], 0x06020400u);
+      smb[0 + qq] = perm_b32(tA, sA, 0x05040100u);  // element 8 gi + 4 qq + k: word 2 gi + qq
+      smb[2 + qq] = perm_b32(tA, sA, 0x07060302u);
+      smb[4 + qq] = perm_b32(tB, sB, 0x05040100u);
+      smb[6 + qq] = perm_b32(tB, sB, 0x07060302u);
+      if (qq == 0) {
+        place_slot<0>(W, o[0] & 0x07070707u); place_slot<2>(W, o[1] & 0x07070707u);
+        place_slot<4>(W, o[2] & 0x07070707u); place_slot<6>(W, o[3] & 0x07070707u);
+      } else {
+        place_slot<1>(W, o[0] & 0x07070707u); place_slot<3>(W, o[1] & 0x07070707u);
+        place_slot<5>(W, o[2] & 0x07070707u); place_slot<7>(W, o[3] & 0x07070707u);
+      }
+      if (any_raw) {
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          const uint32_t t = (o[gi] >> 4) & 0x0F0F0F0Fu;
+          const uint32_t v = t | (t >> 4);
+          hin[gi] |= ((v & 0xFFu) | ((v >> 8) & 0xFF00u)) << (16 * qq);
+        }
+      }
+    }
+    plane[0] = plA & 0xFFu;
+    plane[1] = (plA >> 16) & 0xFFu;
+    plane[2] = plB & 0xFFu;
+    plane[3] = (plB >> 16) & 0xFFu;
+    uint32_t e4 = 0, r4 = 0;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      e4 |= (mode[gi] >= 1 ? 1u : 0u) << gi;
+      r4 |= (mode[gi] == 2 ? 1u : 0u) << gi;
+    }
+    if (e4) atomicOr(&tagw[q0 >> 5], e4 << (q0 & 31));
+    if (r4) atomicOr(&tagw[G.PW + (q0 >> 5)], r4 << (q0 & 31));
+  }
+
+  if (tid == 0) sh_slot = pop_slot(B, is_raw, sh_modes, used, &sh_raw);
+  __syncthreads();
+  const int slot = sh_slot, raw = sh_raw;
+  if (slot < 0) {
+    if (tid == 0) B.table[entry_idx] = kUnallocated;
+    return;
+  }
+  if (raw) {
+    store_raw_tile(G, B, slot, kv, tile, entry_idx);
+    return;
+  }
+  uint8_t* dst = B.comp_pool + (size_t)slot * G.stride;
+  if (has_unit) {
+    uint8_t* esc = dst + G.esc_off;
+    int P = my_before;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      if (mode[gi] >= 1) esc[P++] = (uint8_t)plane[gi];
+      if (mode[gi] == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) esc[P + k] = (uint8_t)(hin[gi] >> (8 * k));
+        P += 4;
+      }
+    }
+    uint32_t* code = reinterpret_cast<uint32_t*>(dst + G.code_off + 12 * u);
+    code[0] = W[0];
+    code[1] = W[1];
+    code[2] = W[2];
+    uint4* smd = reinterpret_cast<uint4*>(dst + G.sm_off + 32 * u);
+    smd[0] = make_uint4(smb[0], smb[1], smb[2], smb[3]);
+    smd[1] = make_uint4(smb[4], smb[5], smb[6], smb[7]);
+  }
+  // zero the unused escape bytes [used, esc_cap)
+  {
+    uint8_t* esc = dst + G.esc_off;
+    if (tid < ((4 - (used & 3)) & 3)) esc[used + tid] = 0;
+    const int w0 = (used + 3) >> 2;
+    uint32_t* esc32 = reinterpret_cast<uint32_t*>(esc);
+    for (int i = w0 + tid; i < (G.esc_cap >> 2); i += kThreads) esc32[i] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < 2 * G.PW; i += kThreads) reinterpret_cast<uint32_t*>(dst + G.tag_off)[i] = tagw[i];
+  if (tid == 0) B.table[entry_idx] = comp_entry((uint32_t)slot, (uint32_t)((used + 15) >> 4), G.cur_ver);
+}
+
 // Any group size (8-token groups; 16 works too): the slot is assembled in LDS by OR-ing every
 // field into zeroed words at the bit positions FORMAT v1 gives it, then copied out whole.
 // One 256-thread workgroup per new tile, as encode_kernel.
@@ -2146,12 +2325,14 @@ int launch_append(const Geo& G, const DevBufs& B, const SeqList& S, const void* 
     const int err = (int)hipGetLastError();
     if (err) return err;
   } else if (max_new_blocks > 0) {
-    const bool any = G.GT != kGroup;  // 8-token groups: the bit-assembling encoder
+    // 8-token groups: BF16 by the unit-per-thread encoder, FP8 by the bit-assembling one
+    const bool any = G.GT != kGroup && G.fmt != 0;
     const size_t lds = any ? (size_t)G.raw_elems * 2 + (size_t)G.stride + (size_t)(3 * G.NG + 3) / 4 * 4
                            : (size_t)G.raw_elems * 2 + (size_t)2 * G.PW * 4;
     void (*kern)(Geo, DevBufs, SeqList, const void*, const void*, int) =
-        any ? (G.fmt == 0 ? encode_any_kernel<0> : (G.fmt == 1 ? encode_any_kernel<1> : encode_any_kernel<2>))
-            : (G.fmt == 0 ? encode_kernel<0> : (G.fmt == 1 ? encode_kernel<1> : encode_kernel<2>));
+        any ? (G.fmt == 1 ? encode_any_kernel<1> : encode_any_kernel<2>)
+            : G.GT != kGroup ? encode_g8_kernel
+                             : (G.fmt == 0 ? encode_kernel<0> : (G.fmt == 1 ? encode_kernel<1> : encode_kernel<2>));
     hipLaunchKernelGGL(kern, dim3(max_new_blocks, S.n, 2 * G.Hkv), dim3(kThreads), lds, (hipStream_t)stream, G, B,
                        S, k, v, n_tokens);
     const int err = (int)hipGetLastError();
