@@ -74,10 +74,11 @@ typedef struct {
                                  build implements 16, 32 and 64 (others: KVC_EUNSUPPORTED)   */
   int32_t group_tokens;       /* G: tokens per exponent group, 16 or 8 in this build (GAAC
                                  page §3.1 groups the exponents of a few tokens of one
-                                 channel).  Decode attention over a compressed G = 16 cache
-                                 rebuilds tiles in registers (the tuned path); over a
-                                 compressed G = 8 cache it rebuilds each block's tiles into
-                                 LDS (correct for every format, not tuned)                   */
+                                 channel).  Decode attention over a compressed cache
+                                 rebuilds tiles in registers: a kernel for G = 16 (the tuned
+                                 path) and one for G = 8 in 64-token blocks; a G = 8 cache in
+                                 16- or 32-token blocks is attended by rebuilding each block's
+                                 tiles into LDS (correct for every format, not tuned)        */
   int32_t esc_cap_bytes;      /* escape capacity per tile, multiple of 16, <= 2032 (this
                                  build implements <= 512); < 0 selects T*D/16                */
   int32_t compressed;         /* 1: blocks are encoded; 0: every block is stored raw (the
@@ -214,7 +215,8 @@ size_t kv_attention_workspace_bytes(const kvc_params* params, int32_t n_seqs, in
  * [n_seqs][Hq][D] BF16 (round-to-nearest-even of an fp32 result); q, out and the workspace
  * 16-byte aligned (KVC_EINVAL otherwise).  The finished blocks of each
  * sequence are split into n_splits contiguous ranges (of 64-token super-blocks; of blocks for
- * a compressed cache with 8-token groups) processed in parallel (1 <= n_splits <= 1024); their
+ * a compressed cache with 8-token groups in 16- or 32-token blocks) processed in parallel
+ * (1 <= n_splits <= 1024); their
  * partial results and the tail are merged by log-sum-exp.  Every listed sequence must hold at
  * least one token (KVC_EINVAL otherwise).  With head_dim 256 the split kernel's last split
  * attends the tail and the merge kernel merges the splits only; kv_decode_step then runs as
