@@ -954,15 +954,24 @@ __device__ __forceinline__ uint32_t e5m2_sign_mant_of(int S, uint32_t W0, uint32
   }
 }
 
-// The E and R words holding unit s of the lane and the escape bytes before them (cross-lane reads).
+// Unit s of lane n as one word: bits 0..3 its groups' E bits, 4..7 their R bits, 8.. the escape
+// bytes before its first group, from the tag words and escape prefix of the lane holding its tag
+// word (cross-lane reads).  A raw group without an E bit is flagged (bad).
 template <int NH, int FMT, bool ISK>
-__device__ __forceinline__ void g8_fetch_tags(const C8Regs<NH, FMT>& c, int s, int j, int n, uint32_t pfx, uint32_t tw[3]) {
+__device__ __forceinline__ uint32_t g8_unit_tags(const C8Regs<NH, FMT>& c, int s, int j, int n, uint32_t pfx,
+                                                 uint32_t& bad) {
+  constexpr int RU = FmtT<FMT>::F - 3;  // escape bytes of a raw group
   int tg, r;
   g8_unit<NH, ISK>(s, j, tg, r);
   const int w = tg * (TG8<NH, FMT>::D / 32) + 2 * r + (n >> 3);  // unit tg * D/4 + 16r + n, 8 units a word
-  tw[0] = (uint32_t)__shfl((int)c.tE, w);
-  tw[1] = (uint32_t)__shfl((int)c.tR, w);
-  tw[2] = (uint32_t)__shfl((int)pfx, w);
+  const uint32_t Ew = (uint32_t)__shfl((int)c.tE, w), Rw = (uint32_t)__shfl((int)c.tR, w), Pw = (uint32_t)__shfl((int)pfx, w);
+  const int bit = 4 * (n & 7);
+  const uint32_t e4 = __builtin_amdgcn_ubfe(Ew, bit, 4), r4 = __builtin_amdgcn_ubfe(Rw, bit, 4);
+  bad |= r4 & ~e4;
+  if constexpr (FMT == 2) bad |= e4 & ~r4;  // no wide mode in a 4-bit exponent field
+  const uint32_t below = (1u << bit) - 1u;
+  const uint32_t P = Pw + __popc(Ew & below) + (uint32_t)(RU - 1) * __popc(Rw & below);
+  return e4 | (r4 << 4) | (P << 8);
 }
 
 // Element words of quad qq of group gi of unit s from its rebuilt exponents Ev (four byte lanes) and
@@ -989,23 +998,18 @@ __device__ __forceinline__ void g8_assemble(const C8Regs<NH, FMT>& c, int s, int
   }
 }
 
-// Rebuild unit s of lane n: channels gi = 0..3 x 8 tokens.  tw = the E and R words holding the
-// unit's four groups and the escape bytes before them; bw = b3 (x) and b4 (y) of the four
+// Rebuild unit s of lane n: channels gi = 0..3 x 8 tokens.  ut = the unit's tags and escape
+// offset (g8_unit_tags); bw = b3 (x) and b4 (y) of the four
 // channels, one byte each (FP8: pre-shifted to the exponent position).  Output, low half first:
 // BF16 o[gi][0][qq] = tokens (4qq, 4qq+2), o[gi][1][qq] = (4qq+1, 4qq+3); FP8 (converted exactly
 // to BF16) o[gi][0][qq] = (4qq, 4qq+1), o[gi][1][qq] = (4qq+2, 4qq+3).
 template <int NH, int FMT>
-__device__ __forceinline__ void g8_rebuild_unit(const C8Regs<NH, FMT>& c, int s, int n, const uint32_t tw[3], uint2 bw,
-                                                const uint8_t* esc8, uint32_t& bad, uint32_t o[4][2][2]) {
+__device__ __forceinline__ void g8_rebuild_unit(const C8Regs<NH, FMT>& c, int s, uint32_t ut, uint2 bw,
+                                                const uint8_t* esc8, uint32_t o[4][2][2]) {
   constexpr int RU = FmtT<FMT>::F - 3;  // escape bytes of a raw group
   constexpr int XS = FmtT<FMT>::XS;
-  const int bit = 4 * (n & 7);
-  const uint32_t Ew = tw[0], Rw = tw[1];
-  const uint32_t e4 = __builtin_amdgcn_ubfe(Ew, bit, 4), r4 = __builtin_amdgcn_ubfe(Rw, bit, 4);
-  bad |= r4 & ~e4;
-  if constexpr (FMT == 2) bad |= e4 & ~r4;  // no wide mode in a 4-bit exponent field
-  const uint32_t below = (1u << bit) - 1u;
-  uint32_t P = tw[2] + __popc(Ew & below) + (uint32_t)(RU - 1) * __popc(Rw & below);
+  const uint32_t e4 = ut & 0xFu, r4 = (ut >> 4) & 0xFu;
+  uint32_t P = ut >> 8;
   const uint32_t W0 = c.cd[s][0], W1 = c.cd[s][1], W2 = c.cd[s][2];
   // byte g of Hw: the base of group g's mode, b4 where the group escapes (wide or raw), else b3;
   // a raw group's base is 0, which its rare path below restores by taking b4 back off
@@ -1156,15 +1160,16 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
     const int kind = __builtin_amdgcn_readfirstlane(rK.kind);
     if ((kind & 3) == SRC_COMP) {
       const int boK = kind >> 2;
+      uint32_t ut[Q::US];  // every unit's tags first: their cross-lane reads are in flight together
+#pragma unroll
+      for (int s = 0; s < Q::US; ++s) ut[s] = g8_unit_tags<NH, FMT, true>(cK, s, j, n, pfxK, bad);
 #pragma unroll
       for (int s = 0; s < Q::US; ++s) {
-        uint32_t tw[3];
-        g8_fetch_tags<NH, FMT, true>(cK, s, j, n, pfxK, tw);
         int tg, r;
         g8_unit<NH, true>(s, j, tg, r);
         const uint2 bw = *reinterpret_cast<const uint2*>(blds + boK + ((0 * NH + r) * 16 + n) * 2);
         uint32_t o[4][2][2];
-        g8_rebuild_unit<NH, FMT>(cK, s, n, tw, bw, esc_lds, bad, o);
+        g8_rebuild_unit<NH, FMT>(cK, s, ut[s], bw, esc_lds, o);
         // token 8tg + 4qq + k: channels 64r + 4n .. +3 as one 8-byte store (BF16: word k & 1,
         // half k >> 1; FP8: word k >> 1, half k & 1)
         const int chunk = 8 * r + (n >> 1), off = 8 * (n & 1);
@@ -1263,6 +1268,11 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
     __syncthreads();
     const int kindV = __builtin_amdgcn_readfirstlane(rV.kind);
     const int boV = kindV >> 2;
+    uint32_t utV[Q::US];
+    if ((kindV & 3) == SRC_COMP) {
+#pragma unroll
+      for (int s = 0; s < Q::US; ++s) utV[s] = g8_unit_tags<NH, FMT, false>(cV, s, j, n, pfxV, bad);
+    }
 #pragma unroll
     for (int s = 0; s < Q::US; ++s) {
       int tg, r;
@@ -1270,11 +1280,9 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
       const int hh = s / NH;  // the 32-token half
       uint4 bv[4];
       if ((kindV & 3) == SRC_COMP) {
-        uint32_t tw[3];
-        g8_fetch_tags<NH, FMT, false>(cV, s, j, n, pfxV, tw);
         const uint2 bw = *reinterpret_cast<const uint2*>(blds + boV + ((NH + r) * 16 + n) * 2);
         uint32_t o[4][2][2];
-        g8_rebuild_unit<NH, FMT>(cV, s, n, tw, bw, esc_lds, bad, o);
+        g8_rebuild_unit<NH, FMT>(cV, s, utV[s], bw, esc_lds, o);
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) bv[gi] = make_uint4(o[gi][0][0], o[gi][1][0], o[gi][0][1], o[gi][1][1]);
       } else if ((kindV & 3) == SRC_RAW) {
