@@ -919,7 +919,7 @@ __device__ __forceinline__ uint32_t g8_stage_escape(C8Regs<NH, FMT>& c, const Ti
   uint32_t incl = row_scan16(cnt);
   if constexpr (TG8<NH, FMT>::PW > 16)
     incl += lane >= 16 ? (uint32_t)__builtin_amdgcn_readlane((int)incl, 15) : 0u;
-  if (rf.src() == SRC_COMP && incl > 16u * (uint32_t)rf.escu) {
+  if (rf.src() == SRC_COMP && !esc_bytes_fit(incl, (uint32_t)rf.escu)) {
     bad |= 1u;
     c.tE = c.tR = 0u;
     return 0u;
@@ -969,9 +969,7 @@ __device__ __forceinline__ uint32_t g8_unit_tags(const C8Regs<NH, FMT>& c, int s
   const uint32_t e4 = __builtin_amdgcn_ubfe(Ew, bit, 4), r4 = __builtin_amdgcn_ubfe(Rw, bit, 4);
   bad |= r4 & ~e4;
   if constexpr (FMT == 2) bad |= e4 & ~r4;  // no wide mode in a 4-bit exponent field
-  const uint32_t below = (1u << bit) - 1u;
-  const uint32_t P = Pw + __popc(Ew & below) + (uint32_t)(RU - 1) * __popc(Rw & below);
-  return e4 | (r4 << 4) | (P << 8);
+  return e4 | (r4 << 4) | (g8_unit_escape(Ew, Rw, Pw, n & 7, RU) << 8);
 }
 
 // Element words of quad qq of group gi of unit s from its rebuilt exponents Ev (four byte lanes) and

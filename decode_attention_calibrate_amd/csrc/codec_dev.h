@@ -144,6 +144,21 @@ __host__ __device__ inline bool esc_tags_fit(uint32_t units_through, uint32_t es
   return units_through <= 8u * esc_pieces;
 }
 
+// 8-token groups (escape units are bytes).  Whether the groups of a tag word may read their
+// escape: bytes_through = escape bytes of this word and every earlier word, esc_pieces = the
+// 16-byte pieces staged.
+__host__ __device__ inline bool esc_bytes_fit(uint32_t bytes_through, uint32_t esc_pieces) {
+  return bytes_through <= 16u * esc_pieces;
+}
+
+// 8-token groups: escape byte where the first group of the four-group CODE unit at nibble k
+// (0..7) of a tag word starts (E, R planes Ew, Rw; Pw = escape bytes of the earlier words; a
+// wide group holds 1 byte, a raw group RU).
+__host__ __device__ inline uint32_t g8_unit_escape(uint32_t Ew, uint32_t Rw, uint32_t Pw, int k, int RU) {
+  const uint32_t below = (1u << (4 * k)) - 1u;
+  return Pw + (uint32_t)__builtin_popcount(Ew & below) + (uint32_t)(RU - 1) * (uint32_t)__builtin_popcount(Rw & below);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN

@@ -1,7 +1,8 @@
 """Host check of the split attention's escape indexing (no GPU): tests/escape_bounds.cpp is built
-host-only from the kernel's own helpers in csrc/codec_dev.h and walks the rebuild's per-lane
+host-only from the kernels' own helpers in csrc/codec_dev.h and walks the rebuild's per-lane
 steps for random, dense, all-raw, all-wide and corrupt tag words against every count of stored
-escape pieces.  A corrupt tile's escape reads stay inside its staged escape bytes (or, for the
+escape pieces, for 16-token groups (escape units of two bytes) and 8-token groups (units of one
+byte, four groups per CODE unit).  A corrupt tile's escape reads stay inside its staged escape bytes (or, for the
 always-issued plane read, at most one unused unit past them, inside the workgroup's LDS)."""
 import os
 import subprocess

@@ -144,3 +144,21 @@ def test_g8_decode_step_equals_append_then_attention(fmt):
         ref = oracle.attention(fmt, qh[0], toks[s][0][:L], toks[s][1][:L], cfg.scale)
         assert row_rel_err(out[row], ref) <= TOL, s
     assert step_cache.status()[0] == 0
+
+
+@pytest.mark.parametrize("fmt", [oracle.BF16, oracle.E5M2])
+def test_g8_gqa_group_of_16(fmt):
+    """Sixteen query heads per KV head (every row of the 16-row MFMA tiles a real head), 128
+    channels, a ragged length with a tail, split counts 1 and 7; against the oracle."""
+    cfg = dataclasses.replace(synth.config(0), fmt=fmt, G=8, T=64, Hkv=1, Hq=16, D=128)
+    print(f"[g8 gqa16] fmt={fmt}", flush=True)
+    g, toks = synth.sequence_tokens(cfg)
+    k, v = toks[0]
+    L = 1000
+    c = _filled(cfg, k, v, L, fmt=fmt)
+    q = synth.queries(cfg, step=L)
+    ref = oracle.attention(fmt, q[0], k[:L], v[:L], cfg.scale)
+    for S in (1, 7):
+        out = host(c.attention([0], dev(q), cfg.scale, S))
+        assert row_rel_err(out[0], ref) <= TOL, S
+    assert c.status()[0] == 0
