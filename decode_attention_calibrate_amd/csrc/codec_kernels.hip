@@ -2338,6 +2338,11 @@ int launch_append(const Geo& G, const DevBufs& B, const SeqList& S, const void* 
     const int err = (int)hipGetLastError();
     if (err) return err;
   }
+  // the tokens past the last finished block go to the tail; when every sequence's appended tokens
+  // end exactly on a block boundary (a decode step's block-completing token) there are none
+  bool any_tail = false;
+  for (int i = 0; i < S.n; ++i) any_tail |= (S.lens[i] + n_tokens) % G.T != 0;
+  if (!any_tail) return (int)hipGetLastError();
   hipLaunchKernelGGL(tail_kernel, dim3(S.n, 2 * G.Hkv), dim3(256), 0, (hipStream_t)stream, G, B, S, k, v, n_tokens);
   return (int)hipGetLastError();
 }
