@@ -818,7 +818,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 2
 }
 
 // ------------------------------------------------------------------------------------------
-// Compressed caches with 8-token groups (FORMAT v1, 64-token blocks): the same split-K structure,
+// Compressed caches with 8-token groups (FORMAT v1, 64-token blocks; GAAC page §3.1 codes the
+// exponents of small groups of eight values of one channel): the same split-K structure,
 // phase pipelining and rebuild-in-registers as attn_comp_kernel, with a lane layout made for
 // 8-token groups.  A CODE unit of an 8-token-group tile is 4 consecutive channels x the 8 tokens
 // of one token group (one group per channel), so each lane rebuilds whole units, four tokens per
