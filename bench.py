@@ -311,6 +311,8 @@ def main():
     bytes_r = raw_kv_bytes + q_bytes + table_bytes
     achieved = bytes_c / (attn_c * 1e-6) / 1e9
     attain = attainable_read(torch, K, stream, bytes_c)
+    attain_r = attainable_read(torch, K, stream, bytes_r)
+    bound_r = bytes_r / (attain_r["GBps"] * 1e9) * 1e6
     digest = kernel_source_digest()
     traffic = counter_traffic(digest, S, n_layers)
     value_us = c_total * 1e3 / args.steps
@@ -354,6 +356,11 @@ def main():
         "effective_GBps": round(achieved, 1),
         "logical_GBps": round(bytes_r / (attn_c * 1e-6) / 1e9, 1),
         "uncompressed_GBps": round(bytes_r / (attn_r * 1e-6) / 1e9, 1),
+        "uncompressed_streaming_bound": {
+            "us": round(bound_r, 3), "GBps": attain_r["GBps"], "speedup_attention": round(bound_r / attn_c, 4),
+            "note": "the uncompressed bytes read at the streaming probe's rate at the same launch shape and bytes "
+                    "per wave: the time no uncompressed kernel of this launch shape beats, and the compressed "
+                    "kernel's speedup against it"},
         "codec_ratio": round(codec_ratio, 4),
         "resident_ratio": round(resident_ratio, 4),
         "exponent_coverage": coverage,
@@ -873,8 +880,11 @@ def attainable_read(torch, K, stream, nbytes, waves=2048, n_buf=8, reps=48):
     """The library's streaming-read kernel (kv_read_probe) at the split attention kernel's launch
     shape -- `waves` workgroups of one wave, here one per wave slot of the chip -- reading about
     nbytes per launch, rotated over n_buf buffers so every launch reads from HBM: the read rate
-    this launch shape attains on the GPU at hand, beside the 8 TB/s peak."""
-    per = max(8192, int(round(nbytes / waves / 8192)) * 8192)
+    this launch shape attains on the GPU at hand, beside the 8 TB/s peak.  Each wave reads an odd
+    number of 8 KiB pieces, so the waves' start addresses do not all share one power-of-two
+    alignment (and with it one memory channel)."""
+    k = max(1, int(round(nbytes / waves / 8192)))
+    per = 8192 * (k + 1 - k % 2)
     bufs = [torch.zeros(waves * per // 4, dtype=torch.int32, device="cuda") for _ in range(n_buf)]
     sink = torch.empty((waves, 64), dtype=torch.int32, device="cuda")
     for i in range(2 * n_buf):
