@@ -2,6 +2,8 @@
 and the uncompressed tail in one softmax).  The bar: per (sequence, query head) row,
 max_c |o - r| / max_c |r| <= 4e-3 against the oracle's exact fp64 attention, with the GPU
 accumulating in fp32 and rounding the output to BF16."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -193,7 +195,6 @@ def test_gqa_group_sizes(cfg_i, g):
     """Query heads per KV head from 1 (plain multi-head) to 16 (every column of the QK MFMA
     used), D = 64 and 128, compressed and uncompressed caches, and the 8-token-group kernel;
     against the oracle (query head hq reads KV head hq // g)."""
-    import dataclasses
     cfg = dataclasses.replace(synth.config(cfg_i), Hq=synth.config(cfg_i).Hkv * g)
     g_, toks = synth.sequence_tokens(cfg)
     k, v = toks[0]
@@ -326,6 +327,33 @@ def test_cfg2_full_context_all_heads():
         torch.cuda.empty_cache()
 
 
+def test_context_128k_all_heads():
+    """The same layer at 131,072 tokens (2,048 finished blocks, eight 64-token super-blocks per
+    split at 256 splits: the longest split loop the benchmark's context sweep times), all 32
+    query heads against the oracle on compressed and uncompressed caches; kv_decode_blocks gives
+    back the stored tokens bit for bit (GAAC page §3.1: the codec is lossless) on 64 blocks spread
+    over the whole sequence."""
+    cfg = dataclasses.replace(synth.config(2), context=(131072,))
+    print("[attention 128k] all heads", flush=True)
+    g, toks = synth.sequence_tokens(cfg)
+    k, v = toks[0]
+    q = synth.queries(cfg)
+    ref = _oracle(cfg, toks, q)
+    for compressed in (True, False):
+        cache = _fill(cfg, toks, compressed)
+        out = host(cache.attention([0], dev(q), cfg.scale, 256))
+        assert row_rel_err(out, ref) <= TOL, compressed
+        assert cache.status()[0] == 0
+        if compressed:
+            for b in range(0, 2048, 32):
+                kd, vd = cache.decode_blocks(0, b, 1)
+                t0 = b * cfg.T
+                assert np.array_equal(host(kd).view(np.uint16), k[t0:t0 + cfg.T].view(np.uint16)), b
+                assert np.array_equal(host(vd).view(np.uint16), v[t0:t0 + cfg.T].view(np.uint16)), b
+        del cache
+        torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("compressed", [True, False])
 @pytest.mark.parametrize("T", [16, 64])
 def test_decode_step_equals_append_then_attention(compressed, T):
@@ -398,7 +426,6 @@ def test_more_sequences_than_one_launch():
     """70 sequences of mixed lengths (two launches of at most 64, each dispatched longest first),
     listed in a shuffled order: attention and a decode step (no block completed, so the split
     kernel stores every new token) match the oracle for every sequence."""
-    import dataclasses
     cfg = synth.config(0)
     g = synth.LayerGen(cfg)
     rng = np.random.default_rng(5)
