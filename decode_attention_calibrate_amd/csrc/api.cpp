@@ -71,7 +71,7 @@ int check_params(const kvc_params* p) {
   if (p->base_versions < 0 || p->base_versions > kvc::kMaxVersions) return fail(KVC_EINVAL, "base_versions must be 0 .. 4");
   if (p->compressed && p->num_comp_slots < 1) return fail(KVC_EINVAL, "a compressed cache needs compressed slots");
   if (!p->compressed && p->num_raw_slots < 1) return fail(KVC_EINVAL, "an uncompressed cache needs raw slots");
-  // valid requests the kernels of this build do not implement
+  // valid requests the library's kernels do not implement
   if (p->group_tokens != 16 && p->group_tokens != 8)
     return fail(KVC_EUNSUPPORTED, "these kernels implement 16- and 8-token groups");
   if (p->block_tokens != 16 && p->block_tokens != 32 && p->block_tokens != 64)

@@ -43,7 +43,7 @@ enum {
   KVC_OK = 0,
   KVC_EINVAL = -1,        /* bad argument                                               */
   KVC_ENOSLOT = -2,       /* not enough free slots / table room for the request         */
-  KVC_EUNSUPPORTED = -3,  /* valid request this build's kernels do not implement        */
+  KVC_EUNSUPPORTED = -3,  /* valid request the library's kernels do not implement      */
   KVC_EHIP = -4,          /* a HIP runtime call failed                                  */
   KVC_ECORRUPT = -5,      /* corrupt stored data (reserved tag, escape overrun)         */
   KVC_ESTATE = -6,        /* call not valid in the cache's current state                */
@@ -70,17 +70,17 @@ typedef struct {
                                  slots); calibration, encode, decode, statistics and decode
                                  attention (both halves of a head in one softmax, through a
                                  simpler LDS-rebuild kernel) work on it                      */
-  int32_t block_tokens;       /* T: tokens per block/tile: a multiple of 16 is valid; this
-                                 build implements 16, 32 and 64 (others: KVC_EUNSUPPORTED)   */
-  int32_t group_tokens;       /* G: tokens per exponent group, 16 or 8 in this build (GAAC
+  int32_t block_tokens;       /* T: tokens per block/tile: a multiple of 16 is valid; the
+                                 kernels implement 16, 32 and 64 (others: KVC_EUNSUPPORTED)  */
+  int32_t group_tokens;       /* G: tokens per exponent group, 16 or 8 (GAAC
                                  page §3.1 groups the exponents of a few tokens of one
                                  channel).  Decode attention over a compressed cache
                                  rebuilds tiles in registers: a kernel for G = 16 (the tuned
                                  path) and one for G = 8 in 64-token blocks; a G = 8 cache in
                                  16- or 32-token blocks is attended by rebuilding each block's
                                  tiles into LDS (correct for every format, not tuned)        */
-  int32_t esc_cap_bytes;      /* escape capacity per tile, multiple of 16, <= 2032 (this
-                                 build implements <= 512); < 0 selects T*D/16                */
+  int32_t esc_cap_bytes;      /* escape capacity per tile, multiple of 16, <= 2032 (the
+                                 kernels implement <= 512); < 0 selects T*D/16               */
   int32_t compressed;         /* 1: blocks are encoded; 0: every block is stored raw (the
                                  uncompressed baseline cache, same table and layout)         */
   int32_t max_seqs;           /* sequence ids are 0 .. max_seqs-1                            */
