@@ -422,6 +422,29 @@ def test_misaligned_buffers_rejected():
     assert row_rel_err(out, _oracle(cfg, [(k, v)], host(q))) <= TOL
 
 
+def test_empty_sequence_rejected():
+    """A listed sequence that holds no token has no softmax to take: attention and the split
+    kernel's entry point reject it with an argument error before any launch, and a batch that
+    lists it beside a filled sequence is rejected whole.  A decode step on it is valid (its new
+    token is the only one) and matches the oracle."""
+    from decode_attention_calibrate_amd._lib import KVCError
+    cfg = synth.config(0)
+    g, toks = synth.sequence_tokens(cfg)
+    k, v = toks[0]
+    cache = new_cache(Hkv=cfg.Hkv, Hq=cfg.Hq, D=cfg.D, T=cfg.T, max_seqs=2, max_blocks=20)
+    cache.calibrate(dev(k[:cfg.n_cal]), dev(v[:cfg.n_cal]))
+    cache.append([0], dev(k[None, :300]), dev(v[None, :300]))
+    q1 = dev(synth.queries(cfg))
+    q2 = dev(synth.queries(cfg)[:1].repeat(2, axis=0))
+    with pytest.raises(KVCError):
+        cache.attention([1], q1, cfg.scale, 2)
+    with pytest.raises(KVCError):
+        cache.attention([0, 1], q2, cfg.scale, 2)
+    assert cache.seq_length(1) == 0 and cache.status()[0] == 0
+    out = host(cache.decode_step([1], dev(k[None, :1]), dev(v[None, :1]), q1, cfg.scale, 2))
+    assert row_rel_err(out, _oracle(cfg, [(k[:1], v[:1])], host(q1))) <= TOL
+
+
 def test_more_sequences_than_one_launch():
     """70 sequences of mixed lengths (two launches of at most 64, each dispatched longest first),
     listed in a shuffled order: attention and a decode step (no block completed, so the split
