@@ -1497,11 +1497,39 @@ struct CombineArgs {
   int n_splits;
 };
 
+// Cross-lane moves inside a 16-lane row by DPP, without an LDS round trip: xor 1 and xor 2 as
+// quad permutations, the half-row and row mirrors (lane i with 7 - i and with 15 - i) and row
+// rotations by 4 and 8.  Once every lane of a quad holds the quad's total, the half-row mirror
+// pairs whole quads and the row mirror whole half-rows, so four steps reduce a row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kDppRor4 = 0x124, kDppRor8 = 0x128;
+
+// every lane of each aligned group of N lanes (N a power of two <= 16) gets the group's sum
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N >= 1 && N <= 16 && (N & (N - 1)) == 0, "group of 1 to 16 lanes");
+  if constexpr (N >= 2) v += dpp<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp<kDppMirror>(v);
+  return v;
+}
+
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
-  for (int o = 32; o > 0; o >>= 1) {
-    const float t = __shfl_xor(v, o);
-    v = is_max ? fmaxf(v, t) : v + t;
-  }
+  // the wave: each row by DPP, then the four rows' results (read as scalars)
+  v = is_max ? fmaxf(v, dpp<kDppXor1>(v)) : v + dpp<kDppXor1>(v);
+  v = is_max ? fmaxf(v, dpp<kDppXor2>(v)) : v + dpp<kDppXor2>(v);
+  v = is_max ? fmaxf(v, dpp<kDppHalfMirror>(v)) : v + dpp<kDppHalfMirror>(v);
+  v = is_max ? fmaxf(v, dpp<kDppMirror>(v)) : v + dpp<kDppMirror>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  v = is_max ? fmaxf(fmaxf(r0, r1), fmaxf(r2, r3)) : (r0 + r1) + (r2 + r3);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) red[w] = v;
@@ -1594,8 +1622,7 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
   float dot = 0.0f;
 #pragma unroll
   for (int p = 0; p < KPL / 8; ++p) dot += dot8(kk[p], qq[p]);
-  dot += __shfl_xor(dot, 1);
-  dot += __shfl_xor(dot, 2);
+  dot = group_sum<4>(dot);
   const bool kok = tk < ntail;
   const float st = kok ? dot * a.sl2 : -INFINITY;
   float mx = st;
@@ -1632,7 +1659,15 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
     sum.z += s < S ? ws * av[u].z : 0.0f;
     sum.w += s < S ? ws * av[u].w : 0.0f;
   }
-  for (int o = NQ; o < 64; o <<= 1) {  // add the slices of this wave
+  int o0 = NQ;  // add the slices of this wave
+  if constexpr (NQ == 4) {  // the four lanes of a row with this lane's quad: two rotations
+    sum.x += dpp<kDppRor4>(sum.x); sum.y += dpp<kDppRor4>(sum.y);
+    sum.z += dpp<kDppRor4>(sum.z); sum.w += dpp<kDppRor4>(sum.w);
+    sum.x += dpp<kDppRor8>(sum.x); sum.y += dpp<kDppRor8>(sum.y);
+    sum.z += dpp<kDppRor8>(sum.z); sum.w += dpp<kDppRor8>(sum.w);
+    o0 = 16;
+  }
+  for (int o = o0; o < 64; o <<= 1) {
     sum.x += __shfl_xor(sum.x, o);
     sum.y += __shfl_xor(sum.y, o);
     sum.z += __shfl_xor(sum.z, o);
@@ -1648,7 +1683,7 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(CombineArgs a)
       tv += (t0 + k < ntail) ? pt[min(t0 + k, kTailTok - 1)] * v4[k] : 0.0f;
     }
   }
-  for (int o = 1; o < TPC; o <<= 1) tv += __shfl_xor(tv, o);
+  tv = group_sum<TPC>(tv);
   const int lane = tid & 63, wv = tid >> 6;
   if (lane < NQ) *reinterpret_cast<float4*>(part + wv * CH + 4 * lane) = sum;
   if (tid % TPC == 0) tsum[cv] = tv;
